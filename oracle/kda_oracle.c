@@ -1,0 +1,216 @@
+/*
+ * kda_oracle.c -- plain fp64 CPU oracle for the KDA / CKDA gated delta rule.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the parity reference: only the test
+ * suite, the smoke check and the CPU-baseline leg of the benchmark may load
+ * it.  It shares no code, header or table with the HIP library.
+ *
+ * What it computes (one (batch, head) pair at a time, one token at a time):
+ *
+ *   S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *   o_t = S_t^T q_t
+ *
+ * with S a d_k x d_v matrix (rows = key channels, columns = value channels).
+ *   - The recurrence is the real-coordinate form of the update printed on
+ *     "Resumen Tecnico: Atencion Delta de Fourier Semidirecta (SFDA)",
+ *     section "Arquitectura Central" (phases theta = 0, which the same page's
+ *     "Principales Contribuciones" item 1 says recovers KDA), and of the
+ *     Gated DeltaNet-2 update on "ملخص تقني: Gated DeltaNet-2", section 1,
+ *     with the erase and write gates tied to one scalar beta (the KDA case
+ *     stated right after that equation).  The conjugate transposes of the
+ *     complex form are plain transposes for real data.
+ *   - The decay Diag(alpha_t) acts on the key dimension (rows of S) and is
+ *     applied before the erase/write, as D_t is placed in the Gated
+ *     DeltaNet-2 equation.
+ *   - CKDA allows alpha in [-1, 1] per channel and beta in [0, 2]
+ *     ("Complex KDA: ..." page, section "Complex KDA (CKDA) Mimarisi").
+ *     Nothing here depends on the range: the oracle is the definition.
+ *   - The readout o_t = S_t^T q_t (after the update) is not printed on the
+ *     pages; this is the plainest reading (a linear-attention read of the
+ *     fixed-size state with the query) and it is the one used throughout.
+ *
+ * Step order inside one token, written out literally:
+ *   1. S <- Diag(alpha) S                       (row i scaled by alpha_i)
+ *   2. u <- S^T k                               (read of the old content)
+ *   3. S <- S + beta k (v - u)^T                (= (I - beta k k^T) S + beta k v^T)
+ *   4. o <- S^T q
+ *
+ * Columns of S evolve independently (every step above acts on one column at
+ * a time), so the work is split over (head, column block) for OpenMP; each
+ * column still runs the full serial recurrence over t.
+ *
+ * Inputs are the exact bytes given to the GPU (bf16 bit patterns or fp32),
+ * widened exactly to fp64.  Nothing is normalised or rescaled here.
+ *
+ * Parity pins: the recurrence (fwd and decode) is pinned by the CPU tests
+ * against explicit transition-matrix products, the plain delta rule, pure
+ * decay, non-expansiveness, norm preservation and the d=2 rotation.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORC_BF16 = 0, ORC_F32 = 1, ORC_F64 = 2 };
+
+static double load_elem(const void* base, int dtype, size_t idx) {
+    if (dtype == ORC_BF16) {
+        uint32_t bits = ((uint32_t)((const uint16_t*)base)[idx]) << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        return (double)f;
+    }
+    if (dtype == ORC_F32) return (double)((const float*)base)[idx];
+    return ((const double*)base)[idx];
+}
+
+/* One token of the recurrence on columns [j0, j1) of a d_k x d_v state. */
+static void kda_token(double* S, int dk, int dv, int j0, int j1,
+                      const double* q, const double* k, const double* v,
+                      const double* a, double beta, double* u, double* o) {
+    /* 1. decay: S <- Diag(alpha) S */
+    for (int i = 0; i < dk; ++i)
+        for (int j = j0; j < j1; ++j) S[(size_t)i * dv + j] *= a[i];
+    /* 2. read: u = S^T k */
+    for (int j = j0; j < j1; ++j) u[j] = 0.0;
+    for (int i = 0; i < dk; ++i)
+        for (int j = j0; j < j1; ++j) u[j] += k[i] * S[(size_t)i * dv + j];
+    /* 3. erase + write: S <- S + beta k (v - u)^T */
+    for (int i = 0; i < dk; ++i)
+        for (int j = j0; j < j1; ++j)
+            S[(size_t)i * dv + j] += beta * k[i] * (v[j] - u[j]);
+    /* 4. readout: o = S^T q */
+    if (o) {
+        for (int j = j0; j < j1; ++j) o[j] = 0.0;
+        for (int i = 0; i < dk; ++i)
+            for (int j = j0; j < j1; ++j) o[j] += q[i] * S[(size_t)i * dv + j];
+    }
+}
+
+static int pick_threads(int nthreads) {
+#ifdef _OPENMP
+    return nthreads > 0 ? nthreads : omp_get_max_threads();
+#else
+    (void)nthreads;
+    return 1;
+#endif
+}
+
+/*
+ * Forward over whole sequences.
+ *   q, k, alpha : [B, T, H, dk]   (dtype)
+ *   v           : [B, T, H, dv]   (dtype)
+ *   beta        : [B, T, H]       (dtype)
+ *   S0          : [n_sel, dk, dv] fp64, or NULL for zeros
+ *   o_out       : [n_sel, T, dv]  fp64, or NULL
+ *   S_out       : [n_sel, dk, dv] fp64, or NULL
+ *   sel         : n_sel flat head indices b*H + h, or NULL (then n_sel = B*H)
+ *   col_block   : width of the column blocks handed to threads (<= 0: dv)
+ * Returns 0, or -1 on bad arguments / allocation failure.
+ */
+int kda_oracle_fwd(int B, int T, int H, int dk, int dv, int dtype,
+                   const void* q, const void* k, const void* v,
+                   const void* alpha, const void* beta, const double* S0,
+                   double* o_out, double* S_out, const int* sel, int n_sel,
+                   int col_block, int nthreads) {
+    if (B < 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+    if (dtype < ORC_BF16 || dtype > ORC_F64) return -1;
+    if (!sel) n_sel = B * H;
+    if (n_sel < 0) return -1;
+    if (col_block <= 0 || col_block > dv) col_block = dv;
+    const int nblk = (dv + col_block - 1) / col_block;
+    const long n_items = (long)n_sel * nblk;
+    int err = 0;
+
+#pragma omp parallel num_threads(pick_threads(nthreads))
+    {
+        double* S = (double*)malloc(sizeof(double) * (size_t)dk * dv);
+        double* buf = (double*)malloc(sizeof(double) * (size_t)(3 * dk + 3 * dv));
+        if (!S || !buf) {
+#pragma omp atomic write
+            err = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (long it = 0; it < n_items; ++it) {
+            if (!S || !buf) continue;
+            const int s = (int)(it / nblk);
+            const int j0 = (int)(it % nblk) * col_block;
+            const int j1 = j0 + col_block < dv ? j0 + col_block : dv;
+            const int bh = sel ? sel[s] : s;
+            const int b = bh / H, h = bh % H;
+            double *qq = buf, *kk = buf + dk, *aa = buf + 2 * dk;
+            double *vv = buf + 3 * dk, *u = vv + dv, *oo = u + dv;
+            for (int i = 0; i < dk; ++i)
+                for (int j = j0; j < j1; ++j)
+                    S[(size_t)i * dv + j] = S0 ? S0[((size_t)s * dk + i) * dv + j] : 0.0;
+            for (int t = 0; t < T; ++t) {
+                const size_t row = ((size_t)b * T + t) * H + h;
+                for (int i = 0; i < dk; ++i) {
+                    qq[i] = load_elem(q, dtype, row * dk + i);
+                    kk[i] = load_elem(k, dtype, row * dk + i);
+                    aa[i] = load_elem(alpha, dtype, row * dk + i);
+                }
+                for (int j = j0; j < j1; ++j) vv[j] = load_elem(v, dtype, row * dv + j);
+                const double bt = load_elem(beta, dtype, row);
+                kda_token(S, dk, dv, j0, j1, qq, kk, vv, aa, bt, u, o_out ? oo : NULL);
+                if (o_out)
+                    for (int j = j0; j < j1; ++j)
+                        o_out[((size_t)s * T + t) * dv + j] = oo[j];
+            }
+            if (S_out)
+                for (int i = 0; i < dk; ++i)
+                    for (int j = j0; j < j1; ++j)
+                        S_out[((size_t)s * dk + i) * dv + j] = S[(size_t)i * dv + j];
+        }
+        free(S);
+        free(buf);
+    }
+    return err ? -1 : 0;
+}
+
+/*
+ * One recurrent decode step (the same token body), state carried by caller.
+ *   q, k, alpha : [B, H, dk]; v : [B, H, dv]; beta : [B, H]   (dtype)
+ *   state       : [n_sel, dk, dv] fp64, updated in place
+ *   o_out       : [n_sel, dv] fp64, or NULL
+ */
+int kda_oracle_decode(int B, int H, int dk, int dv, int dtype,
+                      const void* q, const void* k, const void* v,
+                      const void* alpha, const void* beta, double* state,
+                      double* o_out, const int* sel, int n_sel, int nthreads) {
+    if (B < 0 || H <= 0 || dk <= 0 || dv <= 0 || !state) return -1;
+    if (dtype < ORC_BF16 || dtype > ORC_F64) return -1;
+    if (!sel) n_sel = B * H;
+    if (n_sel < 0) return -1;
+    int err = 0;
+#pragma omp parallel num_threads(pick_threads(nthreads))
+    {
+        double* buf = (double*)malloc(sizeof(double) * (size_t)(3 * dk + 3 * dv));
+        if (!buf) {
+#pragma omp atomic write
+            err = 1;
+        }
+#pragma omp for schedule(dynamic, 4)
+        for (int s = 0; s < n_sel; ++s) {
+            if (!buf) continue;
+            const int bh = sel ? sel[s] : s;
+            double *qq = buf, *kk = buf + dk, *aa = buf + 2 * dk;
+            double *vv = buf + 3 * dk, *u = vv + dv, *oo = u + dv;
+            for (int i = 0; i < dk; ++i) {
+                qq[i] = load_elem(q, dtype, (size_t)bh * dk + i);
+                kk[i] = load_elem(k, dtype, (size_t)bh * dk + i);
+                aa[i] = load_elem(alpha, dtype, (size_t)bh * dk + i);
+            }
+            for (int j = 0; j < dv; ++j) vv[j] = load_elem(v, dtype, (size_t)bh * dv + j);
+            const double bt = load_elem(beta, dtype, (size_t)bh);
+            kda_token(state + (size_t)s * dk * dv, dk, dv, 0, dv, qq, kk, vv, aa, bt, u,
+                      o_out ? oo : NULL);
+            if (o_out)
+                for (int j = 0; j < dv; ++j) o_out[(size_t)s * dv + j] = oo[j];
+        }
+        free(buf);
+    }
+    return err ? -1 : 0;
+}

@@ -1,0 +1,73 @@
+"""The chunk-WY algebra (as the kernel computes it) against the fp64 oracle (CPU only).
+
+The SFDA page reports its chunk-WY recursion and affine block transfer agreeing
+with brute force to residuals between 1e-10 and 1e-15 ("Resultados",
+numerical verification); the fp64 model here is held to 1e-10.
+"""
+import numpy as np
+import pytest
+
+import chunk_model as cm
+import oracle
+from test_oracle import _rand_case
+
+
+def _run(T, dk, dv, seed, ckda=True, zero_frac=0.15):
+    rng = np.random.default_rng(seed)
+    q, k, v, a, b = _rand_case(rng, 1, T, 1, dk, dv, ckda=ckda)
+    S0 = rng.standard_normal((dk, dv))
+    o, S = oracle.fwd(q, k, v, a, b, S0=S0[None])
+    dbg = []
+    om, Sm = cm.chunk_forward(q[0, :, 0], k[0, :, 0], v[0, :, 0], a[0, :, 0], b[0, :, 0], S0, debug=dbg)
+    return o[0], S[0], om, Sm, dbg, b[0, :, 0]
+
+
+@pytest.mark.parametrize("T,dk,dv,seed", [(64, 8, 8, 1), (150, 8, 6, 2), (257, 16, 4, 3),
+                                          (1, 4, 4, 4), (63, 5, 7, 5), (200, 32, 32, 6)])
+def test_chunk_model_matches_oracle(T, dk, dv, seed):
+    o, S, om, Sm, _, _ = _run(T, dk, dv, seed)
+    scale = max(1.0, np.abs(o).max())
+    assert np.abs(om - o).max() <= 1e-10 * scale
+    assert np.abs(Sm - S).max() <= 1e-10 * max(1.0, np.abs(S).max())
+
+
+def test_chunk_model_kda_gates():
+    o, S, om, Sm, _, _ = _run(300, 16, 16, 7, ckda=False)
+    assert np.abs(om - o).max() <= 1e-10 * max(1.0, np.abs(o).max())
+
+
+def test_all_zero_and_sign_gates():
+    """Gates only in {-1, 0, 1}: every decay factor is exactly a signed 0/1 pattern."""
+    rng = np.random.default_rng(8)
+    T, dk, dv = 192, 8, 8
+    q, k, v, _, b = _rand_case(rng, 1, T, 1, dk, dv)
+    a = rng.choice([-1.0, 0.0, 1.0], size=(1, T, 1, dk))
+    S0 = rng.standard_normal((dk, dv))
+    o, S = oracle.fwd(q, k, v, a, b, S0=S0[None])
+    om, Sm = cm.chunk_forward(q[0, :, 0], k[0, :, 0], v[0, :, 0], a[0, :, 0], b[0, :, 0], S0)
+    assert np.abs(om - o[0]).max() <= 1e-10 * max(1.0, np.abs(o).max())
+    assert np.abs(Sm - S[0]).max() <= 1e-10
+
+
+def test_inverse_entries_bounded_by_beta():
+    """|((I+T)^-1)_ij| <= max beta for i != j: the entry is -beta_i k_i^T D_i A_{i-1}..A_{j+1} k_j,
+    a product of non-expansive factors (unit k, |alpha| <= 1, beta in [0, 2])."""
+    _, _, _, _, dbg, b = _run(256, 16, 8, 9)
+    for d in dbg:
+        M = d["M"].copy()
+        np.fill_diagonal(M, 0.0)
+        assert np.abs(M).max() <= b.max() + 1e-12
+        np.testing.assert_allclose(M + np.eye(M.shape[0]), np.linalg.inv(np.eye(M.shape[0]) + d["T"]),
+                                   atol=1e-12)
+
+
+def test_bf16_emulation_within_tolerance():
+    """bf16 operands with fp32 accumulation stay well inside the 2e-2 parity gate."""
+    from gated_delta_rule_78_amd.inputs import make, bf16_to_f32
+    inp = make(1, 640, 1, 128, 128, "bf16", "ckda", False, seed=21)
+    o, S = oracle.fwd(inp.q, inp.k, inp.v, inp.alpha, inp.beta, S0=inp.S0.reshape(1, 128, 128))
+    f = lambda x: bf16_to_f32(x[0, :, 0])
+    om, Sm = cm.chunk_forward(f(inp.q), f(inp.k), f(inp.v), f(inp.alpha), bf16_to_f32(inp.beta[0, :, 0]),
+                              inp.S0[0, 0], emulate="bf16")
+    assert np.abs(om - o[0]).max() / np.abs(o[0]).max() < 1e-2
+    assert np.abs(Sm - S[0]).max() / np.abs(S[0]).max() < 1e-2

@@ -1,0 +1,111 @@
+"""Mutation check of the oracle's pins (CPU only).
+
+Each mutant plants one plausible mistake in a copy of ``oracle/kda_oracle.c``
+(a dropped term, a wrong sign, a wrong index or operand, a transposed role),
+compiles it to a temporary library and runs the pin suite against it.  Every
+mutant must be caught by at least one pin; the unmodified source must pass.
+"""
+import os
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+import oracle
+import test_oracle as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "kda_oracle.c")
+
+MUTANTS = {
+    "drop_decay": ("S[(size_t)i * dv + j] *= a[i];", "(void)a;"),
+    "decay_wrong_index": ("*= a[i];", "*= a[j % dk];"),
+    "erase_sign": ("(v[j] - u[j])", "(v[j] + u[j])"),
+    "drop_erase": ("(v[j] - u[j])", "(v[j] - 0.0 * u[j])"),
+    "drop_beta": ("+= beta * k[i] * (v[j] - u[j])", "+= k[i] * (v[j] - u[j])"),
+    "beta_squared": ("+= beta * k[i] * (v[j] - u[j])", "+= beta * beta * k[i] * (v[j] - u[j])"),
+    "read_with_q": ("u[j] += k[i] *", "u[j] += q[i] *"),
+    "readout_with_k": ("o[j] += q[i] *", "o[j] += k[i] *"),
+    "write_key_is_query": ("+= beta * k[i] *", "+= beta * q[i] *"),
+    "alpha_shifted_channel": ("aa[i] = load_elem(alpha, dtype, row * dk + i);",
+                              "aa[i] = load_elem(alpha, dtype, row * dk + (i + 1) % dk);"),
+    "beta_from_first_head": ("const double bt = load_elem(beta, dtype, row);",
+                             "const double bt = load_elem(beta, dtype, row - h);"),
+    "head_stride_ignored": ("const size_t row = ((size_t)b * T + t) * H + h;",
+                            "const size_t row = ((size_t)b * T + t) * H + 0 * h;"),
+    "time_reversed": ("const size_t row = ((size_t)b * T + t) * H + h;",
+                      "const size_t row = ((size_t)b * T + (T - 1 - t)) * H + h;"),
+    "readout_before_update": (
+        "    /* 3. erase + write: S <- S + beta k (v - u)^T */",
+        "    if (o) { for (int j = j0; j < j1; ++j) { o[j] = 0.0; for (int i = 0; i < dk; ++i) "
+        "o[j] += q[i] * S[(size_t)i * dv + j]; } o = NULL; }\n"
+        "    /* 3. erase + write: S <- S + beta k (v - u)^T */"),
+    "decay_after_write": (
+        "    /* 1. decay: S <- Diag(alpha) S */\n"
+        "    for (int i = 0; i < dk; ++i)\n"
+        "        for (int j = j0; j < j1; ++j) S[(size_t)i * dv + j] *= a[i];\n",
+        ""),
+}
+# decay_after_write removes the first decay and re-inserts it after the write:
+_DECAY_AFTER_WRITE_TAIL = (
+    "    /* 4. readout: o = S^T q */",
+    "    for (int i = 0; i < dk; ++i) for (int j = j0; j < j1; ++j) S[(size_t)i * dv + j] *= a[i];\n"
+    "    /* 4. readout: o = S^T q */")
+
+PIN_TESTS = [
+    ("hand", lambda: pins.test_hand_derived_two_tokens()),
+    ("explicit", lambda: pins.test_explicit_transition_products(3, 2, 32)),
+    ("layout", lambda: pins.test_multi_head_layout_matches_single_heads()),
+    ("delta", lambda: pins.test_alpha_one_is_the_delta_rule()),
+    ("decay", lambda: pins.test_beta_zero_is_pure_decay()),
+    ("rotation", lambda: pins.test_d2_reflection_pair_is_rotation(0.3)),
+    ("affine", lambda: pins.test_affine_block_transfer()),
+]
+
+
+def _build_variant(src_text, tmpdir, name):
+    path = os.path.join(tmpdir, f"{name}.c")
+    with open(path, "w") as f:
+        f.write(src_text)
+    out = os.path.join(tmpdir, f"{name}.so")
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-std=c11", path, "-o", out],
+                   check=True, capture_output=True)
+    return oracle.load(out)
+
+
+def _caught(lib, monkeypatch):
+    failed = []
+    with monkeypatch.context() as m:
+        real_fwd, real_dec = oracle.fwd, oracle.decode
+        m.setattr(oracle, "fwd", lambda *a, **kw: real_fwd(*a, lib=lib, **kw))
+        m.setattr(oracle, "decode", lambda *a, **kw: real_dec(*a, lib=lib, **kw))
+        for name, fn in PIN_TESTS:
+            try:
+                with np.errstate(all="ignore"):
+                    fn()
+            except AssertionError:
+                failed.append(name)
+    return failed
+
+
+@pytest.fixture(scope="module")
+def src_text():
+    with open(SRC) as f:
+        return f.read()
+
+
+def test_unmodified_source_passes(src_text, monkeypatch, tmp_path):
+    lib = _build_variant(src_text, str(tmp_path), "clean")
+    assert _caught(lib, monkeypatch) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, src_text, monkeypatch, tmp_path):
+    old, new = MUTANTS[name]
+    assert src_text.count(old) >= 1, f"mutation anchor for {name} not found"
+    text = src_text.replace(old, new, 1)
+    if name == "decay_after_write":
+        text = text.replace(*_DECAY_AFTER_WRITE_TAIL, 1)
+    lib = _build_variant(text, str(tmp_path), name)
+    caught = _caught(lib, monkeypatch)
+    assert caught, f"mutant {name} passed every pin"
