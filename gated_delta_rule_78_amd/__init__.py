@@ -1,0 +1,171 @@
+"""MI355X (gfx950) KDA / CKDA gated delta rule: thin Python binding of ``libkda.so``.
+
+The arithmetic runs in the HIP library (``csrc/``); this module only checks
+tensors, passes raw device pointers and the current HIP stream through the C
+ABI declared in ``include/kda.h``, and raises on a non-zero status.  PyTorch
+supplies device memory and streams.  There is no CPU fallback: without the
+built library every call raises.
+
+    o, S_T = chunk_fwd(q, k, v, alpha, beta, initial_state=None)   # prefill
+    o      = decode_step(q, k, v, alpha, beta, state)               # state in place
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["chunk_fwd", "chunk_fwd_debug", "decode_step", "lib", "version", "status_string",
+           "LIB_PATH", "KdaError", "Shape", "BF16", "F32"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+BF16, F32 = 0, 1
+_lib = None
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: status {status} ({status_string(status)})")
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int), ("dk", ctypes.c_int),
+                ("dv", ctypes.c_int), ("chunk", ctypes.c_int), ("dtype", ctypes.c_int)]
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m gated_delta_rule_78_amd.build` "
+                               "(there is no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        SP = ctypes.POINTER(Shape)
+        L.kda_chunk_fwd.argtypes = [SP, P, P, P, P, P, P, P, P, P]
+        L.kda_chunk_fwd.restype = ctypes.c_int
+        L.kda_chunk_fwd_debug.argtypes = [SP, P, P, P, P, P, P, P, P, P, P]
+        L.kda_chunk_fwd_debug.restype = ctypes.c_int
+        L.kda_decode_step.argtypes = [SP, P, P, P, P, P, P, P, P]
+        L.kda_decode_step.restype = ctypes.c_int
+        L.kda_status_string.argtypes = [ctypes.c_int]
+        L.kda_status_string.restype = ctypes.c_char_p
+        L.kda_version.argtypes = []
+        L.kda_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def version() -> int:
+    return lib().kda_version()
+
+
+def status_string(status: int) -> str:
+    return lib().kda_status_string(int(status)).decode()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"q/k/v/alpha/beta must be bfloat16 or float32, got {t.dtype}")
+
+
+def _check(ts, names, dev):
+    for t, nm in zip(ts, names):
+        if t is None:
+            continue
+        if not t.is_cuda or t.device != dev:
+            raise ValueError(f"{nm} must be on {dev}")
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _chunk_call(debug, q, k, v, alpha, beta, initial_state, out, final_state, want_final):
+    torch = _torch()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    code = _dtype_code(q)
+    for t, nm in ((k, "k"), (alpha, "alpha"), (v, "v"), (beta, "beta")):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{nm} must have the dtype of q")
+    if k.shape != q.shape or alpha.shape != q.shape or v.shape != (B, T, H, dv) or beta.shape != (B, T, H):
+        raise ValueError("shapes: q, k, alpha [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H]")
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    if final_state is None and want_final:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    for t, nm in ((initial_state, "initial_state"), (final_state, "final_state")):
+        if t is not None and (t.dtype != torch.float32 or t.shape != (B, H, dk, dv)):
+            raise ValueError(f"{nm} must be float32 [B,H,dk,dv]")
+    _check((q, k, v, alpha, beta, initial_state, out, final_state),
+           ("q", "k", "v", "alpha", "beta", "initial_state", "out", "final_state"), dev)
+    shape = Shape(B, T, H, dk, dv, 64, code)
+    args = [ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state),
+            _ptr(out), _ptr(final_state)]
+    dbg = None
+    if debug:
+        nch = (T + 63) // 64
+        dbg = torch.zeros((B * H, nch, 4, 64, 64), dtype=torch.float32, device=dev)
+        rc = lib().kda_chunk_fwd_debug(*args, _ptr(dbg), _stream(dev))
+    else:
+        rc = lib().kda_chunk_fwd(*args, _stream(dev))
+    if rc != 0:
+        raise KdaError(rc, "kda_chunk_fwd")
+    return out, final_state, dbg
+
+
+def chunk_fwd(q, k, v, alpha, beta, initial_state=None, out=None, final_state=None, want_final=True):
+    """Chunkwise WY forward.  q, k, alpha [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H]
+    (all bf16 or all fp32, contiguous, on one GPU); initial_state fp32 [B,H,dk,dv]
+    or None.  Returns (o [B,T,H,dv], final_state fp32 [B,H,dk,dv] or None)."""
+    o, s, _ = _chunk_call(False, q, k, v, alpha, beta, initial_state, out, final_state, want_final)
+    return o, s
+
+
+def chunk_fwd_debug(q, k, v, alpha, beta, initial_state=None):
+    """As chunk_fwd, also returning per-chunk intermediates [B*H, n_chunks, 4, 64, 64]
+    (T, A, (I+T)^-1, W[:, :64]) for diagnosing parity failures."""
+    return _chunk_call(True, q, k, v, alpha, beta, initial_state, None, None, True)
+
+
+def decode_step(q, k, v, alpha, beta, state, out=None):
+    """One recurrent token for every (b, h).  q, k, alpha [B,H,dk]; v [B,H,dv];
+    beta [B,H]; state fp32 [B,H,dk,dv] updated in place.  Returns o [B,H,dv]."""
+    torch = _torch()
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    code = _dtype_code(q)
+    if k.shape != q.shape or alpha.shape != q.shape or v.shape != (B, H, dv) or beta.shape != (B, H):
+        raise ValueError("shapes: q, k, alpha [B,H,dk]; v [B,H,dv]; beta [B,H]")
+    if state.dtype != torch.float32 or state.shape != (B, H, dk, dv):
+        raise ValueError("state must be float32 [B,H,dk,dv]")
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
+    _check((q, k, v, alpha, beta, state, out), ("q", "k", "v", "alpha", "beta", "state", "out"), dev)
+    shape = Shape(B, 1, H, dk, dv, 0, code)
+    rc = lib().kda_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                               _ptr(state), _ptr(out), _stream(dev))
+    if rc != 0:
+        raise KdaError(rc, "kda_decode_step")
+    return out

@@ -1,0 +1,137 @@
+// kda_decode.hip -- one recurrent KDA / CKDA token per (batch, head), state in place.
+//
+//   S' = Diag(alpha) S ;  u = S'^T k ;  p = S'^T q ;  delta = beta (v - u)
+//   S  <- S' + k delta^T ;  o = S^T q = p + (q . k) delta
+//
+// This is one step of the recurrence on the SFDA page ("Arquitectura
+// Central", phases zero) in its constant-memory inference use ("Complex KDA"
+// summary, practical implications: O(1) inference memory).
+//
+// Bandwidth bound: every step streams the fp32 d_k x d_v state from HBM once
+// and back once.  One workgroup of 256 threads owns one (b, h) tile; a thread
+// keeps DK / (256 * 4 / DV) rows x 4 columns of the tile in registers (one
+// 16-byte load and one 16-byte store per row), so the tile is read and written
+// exactly once.  The two column reductions over d_k (u and p) go through lane
+// shuffles inside a wave and a small LDS exchange across the four waves.
+#include "kda_common.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ q,
+                                                     const void* __restrict__ k,
+                                                     const void* __restrict__ v,
+                                                     const void* __restrict__ alpha,
+                                                     const void* __restrict__ beta,
+                                                     float* __restrict__ state,
+                                                     void* __restrict__ o) {
+  constexpr int NT = 256;
+  constexpr int TPR = DV / 4;      // threads covering one state row (4 columns each)
+  constexpr int RG = NT / TPR;     // row groups
+  constexpr int RPT = DK / RG;     // rows per thread
+  static_assert(RPT * RG == DK && TPR * 4 == DV, "tile split");
+
+  __shared__ float s_q[DK], s_k[DK], s_a[DK], s_v[DV];
+  __shared__ float s_red[4][2][DV];
+  __shared__ float s_qk;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const size_t bh = blockIdx.x;
+  const int cq = tid % TPR;        // column quad
+  const int rg = tid / TPR;        // row group
+
+  float4* S = reinterpret_cast<float4*>(state + bh * (size_t)DK * DV);
+  float4 s[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) s[i] = S[(size_t)(rg + RG * i) * TPR + cq];
+
+  float qk_part = 0.f;
+  if (tid < DK) {
+    const float qq = Elem<T>::load(q, bh * DK + tid);
+    const float kk = Elem<T>::load(k, bh * DK + tid);
+    s_q[tid] = qq;
+    s_k[tid] = kk;
+    s_a[tid] = Elem<T>::load(alpha, bh * DK + tid);
+    qk_part = qq * kk;
+  }
+  if (tid < DV) s_v[tid] = Elem<T>::load(v, bh * DV + tid);
+  const float bt = Elem<T>::load(beta, bh);
+  // q . k: one product per thread (zero beyond DK), reduced per wave, then across waves
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) qk_part += __shfl_xor(qk_part, off);
+  if (lane == 0) s_red[wave][0][0] = qk_part;
+  __syncthreads();
+  if (tid == 0) s_qk = s_red[0][0][0] + s_red[1][0][0] + s_red[2][0][0] + s_red[3][0][0];
+
+  float u[4] = {0.f, 0.f, 0.f, 0.f}, p[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r = rg + RG * i;
+    const float a = s_a[r], kk = s_k[r], qq = s_q[r];
+    s[i].x *= a; s[i].y *= a; s[i].z *= a; s[i].w *= a;
+    u[0] += kk * s[i].x; u[1] += kk * s[i].y; u[2] += kk * s[i].z; u[3] += kk * s[i].w;
+    p[0] += qq * s[i].x; p[1] += qq * s[i].y; p[2] += qq * s[i].z; p[3] += qq * s[i].w;
+  }
+  // reduce the row groups that share a wave
+#pragma unroll
+  for (int off = TPR; off < 64; off <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u[j] += __shfl_xor(u[j], off);
+      p[j] += __shfl_xor(p[j], off);
+    }
+  }
+  __syncthreads();  // s_red reuse (q.k partials consumed by thread 0 above)
+  if (lane < TPR) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s_red[wave][0][4 * cq + j] = u[j];
+      s_red[wave][1][4 * cq + j] = p[j];
+    }
+  }
+  __syncthreads();
+  float d[4];
+  const float qk = s_qk;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = 4 * cq + j;
+    const float uu = s_red[0][0][c] + s_red[1][0][c] + s_red[2][0][c] + s_red[3][0][c];
+    d[j] = bt * (s_v[c] - uu);
+    p[j] = s_red[0][1][c] + s_red[1][1][c] + s_red[2][1][c] + s_red[3][1][c];
+  }
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const float kk = s_k[rg + RG * i];
+    s[i].x += kk * d[0]; s[i].y += kk * d[1]; s[i].z += kk * d[2]; s[i].w += kk * d[3];
+    S[(size_t)(rg + RG * i) * TPR + cq] = s[i];
+  }
+  if (rg == 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) Elem<T>::store(o, bh * DV + 4 * cq + j, p[j] + qk * d[j]);
+  }
+}
+
+template <typename T, int DK, int DV>
+static hipError_t launch_decode_t(const DecodeArgs& a) {
+  hipLaunchKernelGGL((decode_kernel<T, DK, DV>), dim3(a.BH), dim3(256), 0, (hipStream_t)a.stream,
+                     a.q, a.k, a.v, a.alpha, a.beta, a.state, a.o);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_decode_d(const DecodeArgs& a) {
+  if (a.dk == 64 && a.dv == 64) return launch_decode_t<T, 64, 64>(a);
+  if (a.dk == 64 && a.dv == 128) return launch_decode_t<T, 64, 128>(a);
+  if (a.dk == 128 && a.dv == 64) return launch_decode_t<T, 128, 64>(a);
+  return launch_decode_t<T, 128, 128>(a);
+}
+
+hipError_t launch_decode(const DecodeArgs& a) {
+  if (a.BH == 0) return hipSuccess;
+  return a.bf16 ? launch_decode_d<bf16_t>(a) : launch_decode_d<float>(a);
+}
+
+}  // namespace kda

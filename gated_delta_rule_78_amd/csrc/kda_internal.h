@@ -1,0 +1,31 @@
+// kda_internal.h -- launch descriptors shared by the C ABI layer and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace kda {
+
+struct DecodeArgs {
+  const void *q, *k, *v, *alpha, *beta;
+  float* state;
+  void* o;
+  int BH, dk, dv;
+  bool bf16;
+  void* stream;
+};
+
+struct ChunkArgs {
+  const void *q, *k, *v, *alpha, *beta;
+  const float* s0;  // may be NULL
+  void* o;
+  float* sT;        // may be NULL
+  float* dbg;       // may be NULL (diagnostic dumps)
+  int B, T, H, dk, dv;
+  bool bf16;
+  void* stream;
+};
+
+hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_chunk(const ChunkArgs& a);
+
+}  // namespace kda

@@ -1,0 +1,137 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) KDA / CKDA gated delta-rule library.
+ *
+ * The operation (per batch b and head h, state S of d_k x d_v, fp32):
+ *
+ *   S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *   o_t = S_t^T q_t
+ *
+ * The update is the real form of the recurrence on the SFDA page ("Resumen
+ * Tecnico: Atencion Delta de Fourier Semidirecta (SFDA)", section
+ * "Arquitectura Central", with the phases at zero, which recovers KDA) and of
+ * the Gated DeltaNet-2 page (section 1, erase and write gates tied to the
+ * scalar beta).  Complex KDA ("Complex KDA" summary, section "Complex KDA
+ * (CKDA) Mimarisi") widens the ranges to alpha in [-1, 1] per key channel and
+ * beta in [0, 2]; both ranges are supported, including exact zero and
+ * negative gates.  The readout after the update is the reading this library
+ * implements (the pages print no readout).
+ *
+ * Two entry points:
+ *   kda_chunk_fwd   -- chunkwise-parallel WY forward over whole sequences
+ *                      (prefill), the chunk-WY form of the SFDA page ("El
+ *                      Teorema de Chunk-WY Constructivo") with the decay-
+ *                      absorbed triangular solve of the Gated DeltaNet-2 page
+ *                      (section 3), chunk C = 64;
+ *   kda_decode_step -- one recurrent token with the state updated in place
+ *                      (constant-memory inference, "Complex KDA" summary,
+ *                      section on practical implications).
+ *
+ * Conventions shared by all entry points
+ *   - Every pointer except `shape` is a DEVICE pointer on the current HIP
+ *     device; the caller owns every buffer.  The library allocates nothing.
+ *   - Layouts are dense, row-major, contiguous:
+ *       q, k, alpha : [B, T, H, dk]      (decode: [B, H, dk])
+ *       v           : [B, T, H, dv]      (decode: [B, H, dv])
+ *       beta        : [B, T, H]          (decode: [B, H])
+ *       o           : [B, T, H, dv]      (decode: [B, H, dv]), same dtype as q
+ *       states      : [B, H, dk, dv] fp32 (row = key channel, column = value channel)
+ *     q, k, v, alpha, beta and o share one dtype (kda_dtype).
+ *   - Alignment: states must be 16-byte aligned; kda_chunk_fwd also needs
+ *     16-byte aligned q, k, v, alpha and o (they move in 16-byte vectors).
+ *     Every other pointer needs only the alignment of its element type.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = default
+ *     stream).  The library keeps no mutable global state; concurrent calls
+ *     on different streams with disjoint outputs are safe.
+ *   - Return value: KDA_OK (0), or a negative kda_status.  Argument errors are
+ *     detected on the host before anything is launched; KDA_ERR_HIP reports a
+ *     launch failure (hipGetLastError).  No C++ exception crosses the ABI.
+ *   - Preconditions that are documented but not checked on the device:
+ *     |alpha| <= 1, 0 <= beta <= 2, k L2-normalised (these make every
+ *     transition non-expansive).  Nothing is normalised or scaled inside.
+ *     Gates with |alpha| below the smallest normal fp32 (~1.2e-38) may act
+ *     as exact zeros.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_BF16 = 0, /* q, k, v, alpha, beta, o are bfloat16; state fp32 */
+    KDA_F32 = 1   /* q, k, v, alpha, beta, o are float32; state fp32 */
+} kda_dtype;
+
+typedef struct {
+    int B;          /* batch size, >= 0 */
+    int T;          /* sequence length, >= 0 (ignored by kda_decode_step) */
+    int H;          /* heads, >= 1 */
+    int dk;         /* key channels: 64 or 128 */
+    int dv;         /* value channels: 64 or 128 */
+    int chunk;      /* chunk length; 0 or 64 (the only supported value) */
+    kda_dtype dtype;
+} kda_shape;
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL = -1,        /* a required pointer is NULL */
+    KDA_ERR_SHAPE = -2,       /* negative / zero sizes, or sizes overflow */
+    KDA_ERR_DTYPE = -3,       /* unknown kda_dtype */
+    KDA_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
+    KDA_ERR_ALIAS = -5,       /* the output overlaps an input it must not alias */
+    KDA_ERR_UNSUPPORTED = -6, /* valid but unsupported (dk/dv, chunk, dtype x dk) */
+    KDA_ERR_HIP = -7          /* the HIP runtime reported an error on launch */
+} kda_status;
+
+/*
+ * Chunkwise WY forward over whole sequences.
+ *   initial_state : [B, H, dk, dv] fp32, or NULL for a zero start state.
+ *   o             : [B, T, H, dv] output, must not overlap any input.
+ *   final_state   : [B, H, dk, dv] fp32, or NULL (not written).  It may be
+ *                   the same pointer as initial_state (each (b, h) tile is
+ *                   read before it is written); any other overlap with an
+ *                   input is KDA_ERR_ALIAS.
+ * Supported: dk in {64, 128}, dv in {64, 128}; KDA_F32 requires dk == dv == 64.
+ * T need not be a multiple of 64 (the last chunk is masked); B*T == 0 only
+ * copies initial_state to final_state (or zeroes it).
+ */
+int kda_chunk_fwd(const kda_shape* shape, const void* q, const void* k, const void* v,
+                  const void* alpha, const void* beta, const float* initial_state,
+                  void* o, float* final_state, void* stream);
+
+/*
+ * One recurrent decode step for every (b, h), state updated in place:
+ *   S <- (I - beta k k^T) Diag(alpha) S + beta k v^T ;  o <- S^T q.
+ *   state : [B, H, dk, dv] fp32, read and written in place.
+ *   o     : [B, H, dv], must not overlap any input or the state.
+ * shape->T and shape->chunk are ignored.  Supported: dk, dv in {64, 128}.
+ */
+int kda_decode_step(const kda_shape* shape, const void* q, const void* k, const void* v,
+                    const void* alpha, const void* beta, float* state, void* o,
+                    void* stream);
+
+/* Human-readable text for a kda_status value (static storage). */
+const char* kda_status_string(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int kda_version(void);
+
+/*
+ * Diagnostic: run the chunk forward like kda_chunk_fwd and also dump, for
+ * every (b, h) and chunk, the chunk-local intermediates in fp32:
+ *   dbg : [B*H, n_chunks, 4, 64, 64]  -> T (beta-scaled strictly lower),
+ *                                        A (decay-weighted q.k, lower incl. diagonal),
+ *                                        M = (I + T)^-1, and (I + T) M - I
+ *                                        is not stored; slot 3 holds W[:, :64]
+ * Used only by the test suite to localise a parity failure; slower than
+ * kda_chunk_fwd.  Same arguments and errors as kda_chunk_fwd.
+ */
+int kda_chunk_fwd_debug(const kda_shape* shape, const void* q, const void* k, const void* v,
+                        const void* alpha, const void* beta, const float* initial_state,
+                        void* o, float* final_state, float* dbg, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H */

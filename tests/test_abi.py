@@ -1,0 +1,124 @@
+"""The C ABI library loads, exports what include/kda.h declares, and rejects bad
+arguments on the host (CPU only: no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import gated_delta_rule_78_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, UNSUP = 0, -1, -2, -3, -4, -5, -6
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(kda.LIB_PATH):
+        pytest.skip("libkda.so not built")
+    return kda.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert {"kda_chunk_fwd", "kda_decode_step", "kda_status_string", "kda_version"} <= set(names)
+    nm = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (kda_\w+)", nm))
+    for n in names:
+        assert n in exported, f"{n} declared in kda.h but not exported"
+        getattr(L, n)
+
+
+def test_version_and_status_strings(L):
+    assert kda.version() == 100
+    for st in range(-7, 1):
+        assert kda.status_string(st) and kda.status_string(st) != "unknown status"
+    assert kda.status_string(-99) == "unknown status"
+
+
+# Fake, never-dereferenced "device" addresses: every case below is rejected on the host.
+BASE = 1 << 40
+MB = 1 << 20
+
+
+def _p(i, off=0):
+    return ctypes.c_void_p(BASE + i * 64 * MB + off)
+
+
+def _chunk(L, B=1, T=64, H=2, dk=64, dv=64, chunk=64, dtype=0, ptrs=None, s0=None, sT=None):
+    shape = kda.Shape(B, T, H, dk, dv, chunk, dtype)
+    p = ptrs or [_p(i) for i in range(6)]
+    return L.kda_chunk_fwd(ctypes.byref(shape), p[0], p[1], p[2], p[3], p[4], s0, p[5], sT, None)
+
+
+def _decode(L, B=2, H=2, dk=64, dv=64, dtype=0, ptrs=None):
+    shape = kda.Shape(B, 1, H, dk, dv, 0, dtype)
+    p = ptrs or [_p(i) for i in range(7)]
+    return L.kda_decode_step(ctypes.byref(shape), p[0], p[1], p[2], p[3], p[4], p[5], p[6], None)
+
+
+def test_chunk_argument_errors(L):
+    assert L.kda_chunk_fwd(None, *([None] * 9)) == NULL
+    assert _chunk(L, dtype=7) == DTYPE
+    assert _chunk(L, B=-1) == SHAPE
+    assert _chunk(L, H=0) == SHAPE
+    assert _chunk(L, T=-5) == SHAPE
+    assert _chunk(L, dk=96) == UNSUP
+    assert _chunk(L, dv=256) == UNSUP
+    assert _chunk(L, chunk=32) == UNSUP
+    assert _chunk(L, dtype=1, dk=128, dv=128) == UNSUP
+    assert _chunk(L, dtype=1, dk=64, dv=128) == UNSUP
+    p = [_p(i) for i in range(6)]
+    p[0] = None
+    assert _chunk(L, ptrs=p) == NULL
+    p = [_p(i) for i in range(6)]
+    p[2] = _p(2, off=8)
+    assert _chunk(L, ptrs=p) == ALIGN
+    p = [_p(i) for i in range(6)]
+    p[4] = _p(4, off=3)            # beta: element alignment only, and 3 is not
+    assert _chunk(L, ptrs=p) == ALIGN
+    p = [_p(i) for i in range(6)]
+    p[5] = _p(0, off=64)           # o inside q
+    assert _chunk(L, ptrs=p) == ALIAS
+    # (s0 == sT in place is allowed; that case would launch, so it is covered by the GPU tests)
+    assert _chunk(L, s0=_p(7), sT=_p(7, off=16)) == ALIAS  # partial overlap is not allowed
+    assert _chunk(L, sT=_p(1)) == ALIAS
+    assert _chunk(L, sT=_p(5)) == ALIAS                 # final state over the output
+
+
+def test_decode_argument_errors(L):
+    assert L.kda_decode_step(None, *([None] * 8)) == NULL
+    assert _decode(L, dtype=3) == DTYPE
+    assert _decode(L, dk=32) == UNSUP
+    assert _decode(L, B=-2) == SHAPE
+    p = [_p(i) for i in range(7)]
+    p[5] = None
+    assert _decode(L, ptrs=p) == NULL
+    p = [_p(i) for i in range(7)]
+    p[6] = _p(5, off=32)           # o inside the state
+    assert _decode(L, ptrs=p) == ALIAS
+    p = [_p(i) for i in range(7)]
+    p[5] = _p(1)                   # state over k
+    assert _decode(L, ptrs=p) == ALIAS
+    p = [_p(i) for i in range(7)]
+    p[0] = _p(0, off=1)            # not even element-aligned
+    assert _decode(L, ptrs=p) == ALIGN
+    p = [_p(i) for i in range(7)]
+    p[5] = _p(5, off=4)            # the state needs 16 bytes
+    assert _decode(L, ptrs=p) == ALIGN
+
+
+def test_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises((ValueError, RuntimeError)):
+        kda.chunk_fwd(x, x, x, x, torch.zeros(1, 4, 1, dtype=torch.bfloat16))

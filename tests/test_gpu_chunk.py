@@ -1,0 +1,193 @@
+"""Chunkwise WY forward on the GPU against the fp64 oracle (gpu).
+
+Small cases are compared element by element on every (b, h); the full-size
+workloads run on the GPU in the configuration the benchmark times and are
+compared on sampled heads that the oracle follows through the whole sequence.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gated_delta_rule_78_amd.inputs import make, make_workload, as_float
+from kda_testutil import TOL, heads_of, inputs_to_dev, rel_err_slices, state_to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu(inp, S0=None, in_place=False):
+    import gated_delta_rule_78_amd as kda
+    import torch
+    q, k, v, a, b = inputs_to_dev(inp)
+    s0 = None if S0 is None else state_to_dev(S0)
+    if in_place:
+        o, sT = kda.chunk_fwd(q, k, v, a, b, initial_state=s0, final_state=s0)
+        assert sT.data_ptr() == s0.data_ptr()
+    else:
+        o, sT = kda.chunk_fwd(q, k, v, a, b, initial_state=s0)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), sT.cpu().numpy()
+
+
+def _check(inp, S0, heads=None, tol=None, in_place=False, label=""):
+    m = inp.meta
+    B, T, H, dk, dv = m["B"], m["T"], m["H"], m["dk"], m["dv"]
+    print(f"chunk {label} B={B} T={T} H={H} dk={dk} dv={dv} {inp.dtype}", flush=True)
+    o_gpu, s_gpu = _gpu(inp, S0, in_place)
+    sel = list(range(B * H)) if heads is None else list(heads)
+    s0_ref = None if S0 is None else S0.reshape(B * H, dk, dv)[sel]
+    o_ref, s_ref = oracle.fwd(inp.q, inp.k, inp.v, inp.alpha, inp.beta, S0=s0_ref, heads=sel,
+                              col_block=16)
+    tol = tol or TOL[inp.dtype]
+    eo = rel_err_slices(heads_of(o_gpu, sel, H), o_ref, len(sel))
+    es = rel_err_slices(s_gpu.reshape(B * H, dk, dv)[sel], s_ref, len(sel))
+    print(f"   err o {eo:.3e}  state {es:.3e}", flush=True)
+    assert eo <= tol, (label, eo)
+    assert es <= tol, (label, es)
+    return eo, es
+
+
+def test_tiny_fp32_kda():
+    """fp32 inputs, B=1 H=2 T=256 d=64, zero start state: gate 1e-4."""
+    inp = make_workload("kda_tiny_f32")
+    _check(inp, None, label="tiny-f32")
+
+
+@pytest.mark.parametrize("gates", ["kda", "ckda"])
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 200, 257])
+def test_bf16_lengths(gates, T):
+    inp = make(1, T, 2, 128, 128, "bf16", gates, False, seed=100 + T)
+    _check(inp, inp.S0, label=f"{gates}-T{T}")
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64)])
+def test_bf16_head_widths(dk, dv):
+    inp = make(2, 150, 3, dk, dv, "bf16", "ckda", False, seed=7 + dk + dv)
+    _check(inp, inp.S0, label=f"d{dk}x{dv}")
+
+
+def test_fp32_ckda_edges():
+    inp = make(1, 192, 2, 64, 64, "f32", "ckda", False, seed=9)
+    _check(inp, inp.S0, label="f32-ckda")
+
+
+def test_gates_only_signs_and_zeros():
+    """alpha entirely in {-1, 0, +1} and beta in {0, 2}: exact zero / sign handling."""
+    inp = make(1, 256, 2, 128, 128, "bf16", "ckda", False, seed=11)
+    rng = np.random.default_rng(11)
+    from gated_delta_rule_78_amd.inputs import bf16_bits
+    inp.alpha = bf16_bits(rng.choice([-1.0, 0.0, 1.0], size=inp.alpha.shape).astype(np.float32))
+    inp.beta = bf16_bits(rng.choice([0.0, 2.0], size=inp.beta.shape).astype(np.float32))
+    _check(inp, inp.S0, label="signs-zeros")
+
+
+def test_zero_gate_resets_history():
+    """A zero gate on every channel at t0 erases everything before it: outputs from
+    t0 on do not depend on the start state or on earlier tokens."""
+    import gated_delta_rule_78_amd as kda
+    import torch
+    from gated_delta_rule_78_amd.inputs import bf16_bits
+    inp = make(1, 192, 2, 128, 128, "bf16", "kda", False, seed=12)
+    t0 = 77
+    a = as_float(inp.alpha, "bf16").copy()
+    a[:, t0] = 0.0
+    inp.alpha = bf16_bits(a)
+    o1, s1 = _gpu(inp, inp.S0)
+    inp2 = make(1, 192, 2, 128, 128, "bf16", "kda", False, seed=13)   # different history
+    for name in ("q", "k", "v", "alpha", "beta"):
+        x = getattr(inp2, name).copy()
+        x[:, t0:] = getattr(inp, name)[:, t0:]
+        setattr(inp2, name, x)
+    o2, s2 = _gpu(inp2, inp2.S0)
+    np.testing.assert_array_equal(o1[:, t0:], o2[:, t0:])
+    np.testing.assert_array_equal(s1, s2)
+
+
+def test_zero_start_state_and_in_place_final_state():
+    inp = make(2, 130, 2, 128, 128, "bf16", "ckda", False, seed=14)
+    _check(inp, None, label="s0-none")
+    _check(inp, inp.S0, in_place=True, label="in-place")
+
+
+def test_split_invariance_on_gpu():
+    """chunk_fwd(T1 + T2) == chunk_fwd(T2, S0 = final(T1)) for T1 a multiple of 64:
+    the affine block transfer applied at a chunk boundary."""
+    import gated_delta_rule_78_amd as kda
+    import torch
+    inp = make(1, 320, 2, 128, 128, "bf16", "ckda", False, seed=15)
+    q, k, v, a, b = inputs_to_dev(inp)
+    s0 = state_to_dev(inp.S0)
+    o, sT = kda.chunk_fwd(q, k, v, a, b, initial_state=s0)
+    t1 = 128
+    o1, s1 = kda.chunk_fwd(*(x[:, :t1].contiguous() for x in (q, k, v, a, b)), initial_state=s0)
+    o2, s2 = kda.chunk_fwd(*(x[:, t1:].contiguous() for x in (q, k, v, a, b)), initial_state=s1)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([o1, o2], dim=1), o)
+    assert torch.equal(s2, sT)
+
+
+def test_decode_steps_match_chunk_forward():
+    import gated_delta_rule_78_amd as kda
+    import torch
+    inp = make(2, 40, 3, 128, 128, "bf16", "ckda", False, seed=16)
+    q, k, v, a, b = inputs_to_dev(inp)
+    s0 = state_to_dev(inp.S0)
+    o, sT = kda.chunk_fwd(q, k, v, a, b, initial_state=s0)
+    S = s0.clone()
+    outs = [kda.decode_step(q[:, t].contiguous(), k[:, t].contiguous(), v[:, t].contiguous(),
+                            a[:, t].contiguous(), b[:, t].contiguous(), S) for t in range(40)]
+    od = torch.stack(outs, dim=1)
+    torch.cuda.synchronize()
+    e_o = rel_err_slices(od.float().cpu().numpy().transpose(0, 2, 1, 3).reshape(6, -1),
+                         o.float().cpu().numpy().transpose(0, 2, 1, 3).reshape(6, -1), 6)
+    e_s = rel_err_slices(S.cpu().numpy().reshape(6, -1), sT.cpu().numpy().reshape(6, -1), 6)
+    assert e_o <= TOL["bf16"] and e_s <= TOL["bf16"], (e_o, e_s)
+
+
+def test_intermediates_match_chunk_model():
+    """Per-chunk T, A, (I+T)^-1 and W from the debug entry point against the numpy
+    model of the chunk algebra, run on the same bf16-rounded inputs in fp64."""
+    import chunk_model as cm
+    import gated_delta_rule_78_amd as kda
+    import torch
+    inp = make(1, 150, 2, 128, 128, "bf16", "ckda", False, seed=17)
+    q, k, v, a, b = inputs_to_dev(inp)
+    _, _, dbg = kda.chunk_fwd_debug(q, k, v, a, b, initial_state=state_to_dev(inp.S0))
+    torch.cuda.synchronize()
+    dbg = dbg.cpu().numpy()
+    f = lambda x, h: as_float(x, "bf16")[0, :, h].astype(np.float64)
+    for h in range(2):
+        ref = []
+        cm.chunk_forward(f(inp.q, h), f(inp.k, h), f(inp.v, h), f(inp.alpha, h),
+                         as_float(inp.beta, "bf16")[0, :, h].astype(np.float64), inp.S0[0, h], debug=ref)
+        for c, d in enumerate(ref):
+            low = np.tril(np.ones((64, 64)), -1)
+            lowd = np.tril(np.ones((64, 64)))
+            for name, got, want, mask in (("T", dbg[h, c, 0], d["T"], low), ("A", dbg[h, c, 1], d["A"], lowd),
+                                          ("M", dbg[h, c, 2], d["M"], lowd),
+                                          ("W", dbg[h, c, 3], d["W"][:, :64], np.ones((64, 64)))):
+                err = np.abs(got * mask - want * mask).max() / max(np.abs(want * mask).max(), 1e-30)
+                assert err < 2e-2, (h, c, name, err)
+
+
+def _full(name, nheads, seed=0):
+    w = make_workload(name)
+    m = w.meta
+    rng = np.random.default_rng(seed)
+    BH = m["B"] * m["H"]
+    heads = sorted(set(rng.choice(BH, size=nheads, replace=False).tolist()) | {0, BH - 1})
+    return w, heads
+
+
+def test_full_kda_prefill_8k_sampled():
+    inp, heads = _full("kda_prefill_8k", 6)
+    _check(inp, inp.S0, heads=heads, label="kda-8k")
+
+
+def test_full_ckda_prefill_8k_sampled():
+    inp, heads = _full("ckda_prefill_8k", 6, seed=1)
+    _check(inp, inp.S0, heads=heads, label="ckda-8k")
+
+
+def test_full_ckda_prefill_128k_sampled():
+    inp, heads = _full("ckda_prefill_128k", 1, seed=2)
+    _check(inp, inp.S0, heads=heads[:2], label="ckda-128k")
