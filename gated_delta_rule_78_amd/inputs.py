@@ -146,3 +146,17 @@ def make_workload(name: str, T: int | None = None, B: int | None = None, H: int 
 def as_float(x: np.ndarray, dtype: str) -> np.ndarray:
     """The exact fp32 values behind an input array (bf16 bits widened)."""
     return bf16_to_f32(x) if dtype == "bf16" else np.asarray(x, np.float32)
+
+
+def to_torch(inp: Inputs, device="cuda"):
+    """Upload the exact input bytes: returns (q, k, v, alpha, beta, S0) torch tensors
+    (bf16 inputs keep their bit patterns; S0 is fp32, or None)."""
+    import torch
+
+    def up(x):
+        if inp.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(device).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+
+    s0 = None if inp.S0 is None else torch.from_numpy(np.ascontiguousarray(inp.S0, np.float32)).to(device)
+    return (*[up(x) for x in (inp.q, inp.k, inp.v, inp.alpha, inp.beta)], s0)
