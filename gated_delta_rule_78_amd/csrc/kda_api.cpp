@@ -5,6 +5,7 @@
 #include "../../include/kda.h"
 
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "kda_internal.h"
 
@@ -26,6 +27,15 @@ bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.l
 bool misaligned(const void* p, unsigned bytes = 16) { return ((uintptr_t)p & (bytes - 1)) != 0; }
 
 bool supported_width(int d) { return d == 64 || d == 128; }
+
+// KDA_VALUE_TILE=64|128 pins the chunk kernel's value-tile width (tuning aid).
+int value_tile_override() {
+  static const int v = [] {
+    const char* e = getenv("KDA_VALUE_TILE");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
+}
 
 // Checks common to both entry points; fills element size.
 int check_shape(const kda_shape* s, bool decode, int* es) {
@@ -91,7 +101,7 @@ static int chunk_fwd_impl(const kda_shape* shape, const void* q, const void* k, 
     if (overlap(rs, ro)) return KDA_ERR_ALIAS;
   }
   kda::ChunkArgs a{q, k, v, alpha, beta, s0, o, sT, dbg, s.B, s.T, s.H, s.dk, s.dv,
-                   s.dtype == KDA_BF16, stream};
+                   s.dtype == KDA_BF16, stream, value_tile_override()};
   return kda::launch_chunk(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -32,12 +32,20 @@
 //     prefix / suffix products inside aligned lam-segments; one matrix-core
 //     pass per level, the level picked per element.
 //
-// Layout of the work: one workgroup per (b, h) with DV / 16 waves; wave w owns
-// value columns [16 w, 16 w + 16).  The fp32 state stays in registers for the
-// whole sequence in accumulator layout (8 tiles of 16x16 at d_k = 128), and an
-// accumulator pair is directly a matrix-core B fragment (the k-slot order is
-// permuted to match).  q, k, alpha, beta, v of the next chunk are prefetched
-// into registers while the current chunk computes.
+// (I + T)^-1: the four diagonal 16x16 blocks by forward substitution held in
+// registers (one lane per column; the rows of T are broadcast across the
+// 16-lane DPP row), the off-diagonal blocks by fp32 matrix-core products in
+// three dependency stages, M_IJ = -N_II sum_{K=J}^{I-1} T_IK M_KJ.
+//
+// Layout of the work: one workgroup per (b, h, value tile of VT columns) with
+// VT / 16 waves; wave w owns value columns [16 w, 16 w + 16) of the tile.  A
+// head's tiles are placed on one XCD (shared L2 for the re-read q, k, alpha).
+// The fp32 state stays in registers for the whole sequence in accumulator
+// layout, and an accumulator pair is directly a matrix-core B fragment (the
+// k-slot order is permuted to match).  q, k, alpha, beta, v of the next chunk
+// are prefetched into registers while the current chunk computes.
+#include <type_traits>
+
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -49,26 +57,30 @@ constexpr int C = 64;
 constexpr int SUB = 16;
 constexpr int NB = C / SUB;
 
-// Off-diagonal tile jobs (I, J) and which block-product Pi they need
+// Off-diagonal tile jobs (I, J) and the block-product Pi they need
 // (-1: adjacent, none; 0: g1; 1: g1 g2; 2: g2).
 __constant__ int kOffI[6] = {1, 2, 3, 2, 3, 3};
 __constant__ int kOffJ[6] = {0, 1, 2, 0, 1, 0};
 __constant__ int kOffPi[6] = {-1, -1, -1, 0, 2, 1};
+// Upper 16x16 tiles of A~ that must read as zero.
+__constant__ int kUpI[6] = {0, 0, 0, 1, 1, 2};
+__constant__ int kUpJ[6] = {1, 2, 3, 2, 3, 3};
 
-template <typename T, int DK, int DV>
+template <typename T, int DK, int VT>
 struct Cfg {
   static constexpr int ES = Elem<T>::kBytes;
-  static constexpr int NW = DV / 16;
+  static constexpr int NW = VT / 16;
   static constexpr int NT = NW * 64;
-  static constexpr int KS = DK / 32;  // k-steps over key channels
+  static constexpr int KS = DK / 32;          // k-steps over key channels
   static constexpr int RS_DK = DK * ES + 16;  // [pos][channel] rows (padded)
   static constexpr int RS_C = C * ES + 16;    // [channel][pos] and [pos][pos] rows of T type
-  static constexpr int RS_DV = DV * ES + 16;  // [pos][value col]
+  static constexpr int RS_VT = VT * ES + 16;  // [pos][value col]
   static constexpr int RS_F = C * 4 + 16;     // fp32 [pos][pos]
-  // region R_IN: q, k, alpha -> later v (VV), M (MM, fp32), M~ (MT)
+  static constexpr int RS_MB = SUB * 4 + 16;  // fp32 transposed 16x16 blocks
+  // region R_IN: q, k, alpha -> later v tile (VV), M (MM, fp32), M~ (MT); O staging over VV
   static constexpr int SZ_IN_A = 3 * C * RS_DK;
   static constexpr int OFF_VV = 0;
-  static constexpr int OFF_MM = OFF_VV + C * RS_DV;
+  static constexpr int OFF_MM = OFF_VV + C * RS_VT;
   static constexpr int OFF_MT = OFF_MM + C * RS_F;
   static constexpr int SZ_IN_B = OFF_MT + C * RS_C;
   static constexpr int SZ_IN = SZ_IN_A > SZ_IN_B ? SZ_IN_A : SZ_IN_B;
@@ -79,78 +91,115 @@ struct Cfg {
   static constexpr int OFF_KRT = OFF_KGT + DK * RS_C;
   static constexpr int SZ_OP_B = OFF_KRT + DK * RS_C;
   static constexpr int SZ_OP = SZ_OP_A > SZ_OP_B ? SZ_OP_A : SZ_OP_B;
-  // region R_L: level operands (2 levels x 4 blocks x (16 A rows + 8 B rows)) -> later T, A (fp32), A~ (AT)
+  // region R_L: level operands (2 levels x 4 blocks x (16 A rows + 8 B rows))
+  //   -> later D (fp32: T before its beta row scale), A~ (AT), transposed inverse blocks (MB);
+  //      W over D once the inverse is done
   static constexpr int LVL_ROWS = 24;
   static constexpr int SZ_L_A = 2 * NB * LVL_ROWS * RS_DK;
-  static constexpr int OFF_TT = 0;          // later also W (WW) once T is consumed
-  static constexpr int OFF_AA = OFF_TT + C * RS_F;  // later E = N_II T_IK blocks
-  static constexpr int OFF_AT = OFF_AA + C * RS_F;
-  static constexpr int SZ_L_B = OFF_AT + C * RS_C;
+  static constexpr int OFF_TT = 0;
+  static constexpr int OFF_AT = OFF_TT + C * RS_F;
+  static constexpr int OFF_MB = OFF_AT + C * RS_C;
+  static constexpr int NMB = 5;  // N00, N11, N22, M10, M20, each stored transposed
+  static constexpr int SZ_L_B = OFF_MB + NMB * SUB * RS_MB;
   static constexpr int SZ_L = SZ_L_A > SZ_L_B ? SZ_L_A : SZ_L_B;
   // small fp32 tables
   static constexpr int BASE_IN = 0;
   static constexpr int BASE_OP = BASE_IN + SZ_IN;
   static constexpr int BASE_L = BASE_OP + SZ_OP;
-  static constexpr int BASE_GT = BASE_L + SZ_L;       // block totals g[4][DK]
+  static constexpr int BASE_GT = BASE_L + SZ_L;         // block totals g[4][DK]
   static constexpr int BASE_PI = BASE_GT + 4 * DK * 4;  // Pi tables [3][DK]
   static constexpr int BASE_GC = BASE_PI + 3 * DK * 4;  // gamma of the last row [DK]
   static constexpr int BASE_BETA = BASE_GC + DK * 4;    // beta [C]
   static constexpr int LDS = BASE_BETA + C * 4;
   static_assert(LDS <= 160 * 1024, "LDS budget");
-  static_assert(C * RS_DK <= C * RS_F, "W fits over T");
+  static_assert(C * RS_DK <= C * RS_F, "W fits over D");
   // prefetch vectors (16 B) per thread
   static constexpr int VROW_K = DK * ES / 16;  // 16-byte vectors per q/k/alpha row
-  static constexpr int VROW_V = DV * ES / 16;
+  static constexpr int VROW_V = VT * ES / 16;  // 16-byte vectors per row of the v tile
   static constexpr int VPT = C * VROW_K / NT;
   static constexpr int VPT_V = C * VROW_V / NT;
   static_assert(VPT * NT == C * VROW_K && VPT_V * NT == C * VROW_V, "prefetch split");
-  static constexpr int NITEM = NB * DK / 2;  // (block, channel pair) items of the gate passes
+  // gate passes: (block, channel pair) items; with enough threads two roles split the work
+  static constexpr int NITEM = NB * DK / 2;
+  static constexpr bool SPLIT = NT >= 2 * NITEM;
   static_assert(NITEM <= NT, "one gate item per thread");
 };
 
+// Two adjacent channels of one row, kept packed until used.
 template <typename T>
-struct Pair;  // two adjacent channels of one row
+struct Raw;
 template <>
-struct Pair<bf16_t> {
-  __device__ __forceinline__ static void load(const char* p, float& a, float& b) {
-    uint32_t w = *(const uint32_t*)p;
+struct Raw<bf16_t> {
+  typedef uint32_t type;
+  __device__ __forceinline__ static type ld(const char* p) { return *(const uint32_t*)p; }
+  __device__ __forceinline__ static void unpack(type w, float& a, float& b) {
     a = __uint_as_float(w << 16);
     b = __uint_as_float(w & 0xFFFF0000u);
   }
-  __device__ __forceinline__ static void store(char* p, float a, float b) {
-    *(uint32_t*)p = pack_bf16x2(a, b);
-  }
+  __device__ __forceinline__ static void st(char* p, float a, float b) { *(uint32_t*)p = pack_bf16x2(a, b); }
+  static constexpr uint32_t kOneWord = 0x3F803F80u;  // two bf16 ones
 };
 template <>
-struct Pair<float> {
-  __device__ __forceinline__ static void load(const char* p, float& a, float& b) {
-    float2 w = *(const float2*)p;
+struct Raw<float> {
+  typedef float2 type;
+  __device__ __forceinline__ static type ld(const char* p) { return *(const float2*)p; }
+  __device__ __forceinline__ static void unpack(type w, float& a, float& b) {
     a = w.x;
     b = w.y;
   }
-  __device__ __forceinline__ static void store(char* p, float a, float b) {
-    *(float2*)p = make_float2(a, b);
-  }
+  __device__ __forceinline__ static void st(char* p, float a, float b) { *(float2*)p = make_float2(a, b); }
+  static constexpr uint32_t kOneWord = 0x3F800000u;
 };
 
-__device__ __forceinline__ void st_elem_bf16_or_f32(char* p, float x, int es) {
+__device__ __forceinline__ void st_elem(char* p, float x, int es) {
   if (es == 2)
     *(uint16_t*)p = f32_to_bf16(x);
   else
     *(float*)p = x;
 }
 
+// eight consecutive elements of one row (16-byte aligned for bf16, 32-byte for fp32)
+template <typename T>
+__device__ __forceinline__ void st_row8(char* p, const float (&v)[8]);
+template <>
+__device__ __forceinline__ void st_row8<bf16_t>(char* p, const float (&v)[8]) {
+  *(uint4*)p = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                          pack_bf16x2(v[6], v[7]));
+}
+template <>
+__device__ __forceinline__ void st_row8<float>(char* p, const float (&v)[8]) {
+  ((float4*)p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+  ((float4*)p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+// value of `x` held by lane `src` (0..15) of this lane's 16-lane DPP row
+template <int src>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + src, 0xF,
+                                                               0xF, true));
+}
+
+// 16x16 fp32 product step: acc += A B with A[row n][k-slot 4 g + s], B[k-slot 4 g + s][col n]
+__device__ __forceinline__ void mm4(f32x4_t& acc, const float (&a)[4], const float (&b)[4]) {
+#ifndef KDA_HOST_PASS
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
+#endif
+}
+
 }  // namespace
 
-template <typename T, int DK, int DV>
-__global__ __launch_bounds__((DV / 16) * 64) void chunk_fwd_kernel(
+template <typename T, int DK, int VT>
+__global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
     const void* __restrict__ gq, const void* __restrict__ gk, const void* __restrict__ gv,
     const void* __restrict__ galpha, const void* __restrict__ gbeta, const float* s0,
-    void* __restrict__ go, float* sT, float* __restrict__ dbg, int Tlen, int H) {
-  using K = Cfg<T, DK, DV>;
+    void* __restrict__ go, float* sT, float* __restrict__ dbg, int Tlen, int H, int DV, int BH) {
+  using K = Cfg<T, DK, VT>;
+  using R = Raw<T>;
   constexpr int ES = K::ES;
   constexpr int NT = K::NT;
   constexpr int NW = K::NW;
+  constexpr int LDF = K::RS_F / 4;
   extern __shared__ __align__(16) char smem[];
   char* const R_IN = smem + K::BASE_IN;
   char* const R_OP = smem + K::BASE_OP;
@@ -162,46 +211,59 @@ __global__ __launch_bounds__((DV / 16) * 64) void chunk_fwd_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int g = lane >> 4;
   const int n = lane & 15;
-  const int bh = blockIdx.x;
+  // block -> (head, value tile); a head's tiles land on one XCD when the grid allows it
+  const int NVT = DV / VT;
+  int bh, vt;
+  {
+    const int bid = blockIdx.x;
+    if (NVT > 1 && (BH & 7) == 0) {
+      const int r = bid >> 3;
+      vt = r % NVT;
+      bh = (r / NVT) * 8 + (bid & 7);
+    } else {
+      bh = bid / NVT;
+      vt = bid % NVT;
+    }
+  }
   const int b = bh / H, h = bh % H;
+  const int v0 = vt * VT;
   const int nchunks = (Tlen + C - 1) / C;
+  auto row_base = [&](int t) -> size_t { return ((size_t)b * Tlen + t) * H + h; };
 
-  // ---------------- state tiles (rows 16 r .. of key channels, columns 16 wave + n)
+  // ---------------- state tiles: rows 16 r + 4 g + e (key channels), column v0 + 16 wave + n
   f32x4_t S[DK / 16];
 #pragma unroll
-  for (int r = 0; r < DK / 16; ++r) {
+  for (int r = 0; r < DK / 16; ++r) S[r] = zero4();
+  if (s0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      S[r][e] = s0 ? s0[((size_t)bh * DK + 16 * r + 4 * g + e) * DV + 16 * wave + n] : 0.f;
+    for (int r = 0; r < DK / 16; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[r][e] = s0[((size_t)bh * DK + 16 * r + 4 * g + e) * DV + v0 + 16 * wave + n];
   }
 
-  // ---------------- prefetch registers
+  // ---------------- prefetch registers.  Loads are unconditional (rows past the end
+  // are clamped to the last row and replaced when staged) so that no wait is forced
+  // at issue time.
   uint4 pq[K::VPT], pk[K::VPT], pa[K::VPT], pv[K::VPT_V];
-  float pb = 0.f;
-  auto row_base = [&](int t) -> size_t { return ((size_t)b * Tlen + t) * H + h; };
+  uint32_t pb = 0u;  // raw beta bits, converted when staged
   auto issue_qka = [&](int c) {
     const int t0 = c * C;
 #pragma unroll
     for (int i = 0; i < K::VPT; ++i) {
       const int j = tid + NT * i;
       const int row = j / K::VROW_K, c16 = j % K::VROW_K;
-      if (t0 + row < Tlen) {
-        const size_t off = row_base(t0 + row) * DK * ES + (size_t)c16 * 16;
-        pq[i] = *(const uint4*)((const char*)gq + off);
-        pk[i] = *(const uint4*)((const char*)gk + off);
-        pa[i] = *(const uint4*)((const char*)galpha + off);
-      } else {
-        pq[i] = make_uint4(0, 0, 0, 0);
-        pk[i] = make_uint4(0, 0, 0, 0);
-        // alpha = 1 on padded rows: identity transitions
-        const uint32_t one = ES == 2 ? 0x3F803F80u : 0x3F800000u;
-        pa[i] = make_uint4(one, one, one, one);
-      }
+      const size_t off = row_base(min(t0 + row, Tlen - 1)) * DK * ES + (size_t)c16 * 16;
+      pq[i] = *(const uint4*)((const char*)gq + off);
+      pk[i] = *(const uint4*)((const char*)gk + off);
+      pa[i] = *(const uint4*)((const char*)galpha + off);
     }
-    if (tid < C) pb = (t0 + tid < Tlen) ? Elem<T>::load(gbeta, row_base(t0 + tid)) : 0.f;
+    {
+      const size_t ib = row_base(min(t0 + (tid & (C - 1)), Tlen - 1));
+      pb = ES == 2 ? (uint32_t)((const uint16_t*)gbeta)[ib] : ((const uint32_t*)gbeta)[ib];
+    }
   };
   auto issue_v = [&](int c) {
     const int t0 = c * C;
@@ -209,9 +271,8 @@ __global__ __launch_bounds__((DV / 16) * 64) void chunk_fwd_kernel(
     for (int i = 0; i < K::VPT_V; ++i) {
       const int j = tid + NT * i;
       const int row = j / K::VROW_V, c16 = j % K::VROW_V;
-      pv[i] = (t0 + row < Tlen)
-                  ? *(const uint4*)((const char*)gv + row_base(t0 + row) * DV * ES + (size_t)c16 * 16)
-                  : make_uint4(0, 0, 0, 0);
+      pv[i] = *(const uint4*)((const char*)gv + row_base(min(t0 + row, Tlen - 1)) * DV * ES + (size_t)v0 * ES +
+                              (size_t)c16 * 16);
     }
   };
   if (nchunks > 0) {
@@ -219,26 +280,33 @@ __global__ __launch_bounds__((DV / 16) * 64) void chunk_fwd_kernel(
     issue_v(0);
   }
 
-  // gate-pass item: (block I, channel pair cp)
-  const bool has_item = tid < K::NITEM;
-  const int iI = tid / (DK / 2);
-  const int icp = tid % (DK / 2);
+  // gate-pass item: (block iI, channels 2 icp, 2 icp + 1); roles 0 / 1 split the passes
+  const int item = K::SPLIT ? tid % K::NITEM : tid;
+  const int role = K::SPLIT ? tid / K::NITEM : 2;  // 2: this thread takes both roles
+  const bool has_item = K::SPLIT ? (tid < 2 * K::NITEM) : (tid < K::NITEM);
+  const bool r0 = has_item && role != 1;
+  const bool r1 = has_item && role != 0;
+  const int iI = item / (DK / 2);
+  const int icp = item % (DK / 2);
+  const int item_off = (SUB * iI) * K::RS_DK + 2 * icp * ES;
 
   for (int chunk = 0; chunk < nchunks; ++chunk) {
     const int t0 = chunk * C;
     const int nv = min(C, Tlen - t0);
-    // ================= phase 0: staged inputs -> LDS
+    // ================= phase 0: staged inputs -> LDS (padded rows: q = k = 0, alpha = 1, beta = 0)
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < K::VPT; ++i) {
       const int j = tid + NT * i;
       const int row = j / K::VROW_K, c16 = j % K::VROW_K;
+      const bool ok = t0 + row < Tlen;
+      const uint32_t one = R::kOneWord;
       const int off = row * K::RS_DK + c16 * 16;
-      *(uint4*)(R_IN + 0 * C * K::RS_DK + off) = pq[i];
-      *(uint4*)(R_IN + 1 * C * K::RS_DK + off) = pk[i];
-      *(uint4*)(R_IN + 2 * C * K::RS_DK + off) = pa[i];
+      *(uint4*)(R_IN + 0 * C * K::RS_DK + off) = ok ? pq[i] : make_uint4(0, 0, 0, 0);
+      *(uint4*)(R_IN + 1 * C * K::RS_DK + off) = ok ? pk[i] : make_uint4(0, 0, 0, 0);
+      *(uint4*)(R_IN + 2 * C * K::RS_DK + off) = ok ? pa[i] : make_uint4(one, one, one, one);
     }
-    if (tid < C) BETA[tid] = pb;
+    if (tid < C) BETA[tid] = (t0 + tid < Tlen) ? __uint_as_float(ES == 2 ? pb << 16 : pb) : 0.f;
     __syncthreads();
     if (chunk + 1 < nchunks) issue_qka(chunk + 1);
 
@@ -246,51 +314,36 @@ __global__ __launch_bounds__((DV / 16) * 64) void chunk_fwd_kernel(
     const char* const Ks = R_IN + C * K::RS_DK;
     const char* const As = R_IN + 2 * C * K::RS_DK;
 
-    // ================= phase A: block totals of the gates
-    // gate-pass item (block iI, channels 2 icp, 2 icp + 1); alpha / q / k are
-    // re-read from LDS in every gate phase rather than held across barriers.
-    const int item_off = (SUB * iI) * K::RS_DK + 2 * icp * ES;
-    auto ld_alpha = [&](float (&al)[SUB][2]) {
+    // item registers: alpha (fp32), q and k (packed), loaded in one batch per phase
+    typename R::type qr[SUB], kr_raw[SUB];
+    float al[SUB][2];
+    auto ld_item = [&](bool with_qk) {
 #pragma unroll
-      for (int m = 0; m < SUB; ++m) Pair<T>::load(As + item_off + m * K::RS_DK, al[m][0], al[m][1]);
+      for (int m = 0; m < SUB; ++m) {
+        R::unpack(R::ld(As + item_off + m * K::RS_DK), al[m][0], al[m][1]);
+        if (with_qk) {
+          qr[m] = R::ld(Qs + item_off + m * K::RS_DK);
+          kr_raw[m] = R::ld(Ks + item_off + m * K::RS_DK);
+        }
+      }
     };
-    auto ld_q = [&](int m, float& a, float& b) { Pair<T>::load(Qs + item_off + m * K::RS_DK, a, b); };
-    auto ld_k = [&](int m, float& a, float& b) { Pair<T>::load(Ks + item_off + m * K::RS_DK, a, b); };
-    if (has_item) {
-      float al[SUB][2];
-      ld_alpha(al);
+
+    // ================= phase A: block totals of the gates
+    if (r0) {
+      ld_item(false);
       float g0 = 1.f, g1 = 1.f;
 #pragma unroll
       for (int m = 0; m < SUB; ++m) {
         g0 *= al[m][0];
         g1 *= al[m][1];
       }
-      GT[iI * DK + 2 * icp] = g0;
-      GT[iI * DK + 2 * icp + 1] = g1;
+      *(float2*)(GT + iI * DK + 2 * icp) = make_float2(g0, g1);
     }
     __syncthreads();
 
-    // chunk-level products for the item's channels
-    float Gp[2] = {1.f, 1.f}, Rp[2] = {1.f, 1.f};
-    if (has_item) {
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int c = 2 * icp + e;
-        const float t0v = GT[c], t1v = GT[DK + c], t2v = GT[2 * DK + c], t3v = GT[3 * DK + c];
-        Gp[e] = iI == 0 ? 1.f : iI == 1 ? t0v : iI == 2 ? t0v * t1v : t0v * t1v * t2v;
-        Rp[e] = iI == 3 ? 1.f : iI == 2 ? t3v : iI == 1 ? t2v * t3v : t1v * t2v * t3v;
-        if (iI == 0) {
-          PI[0 * DK + c] = t1v;
-          PI[1 * DK + c] = t1v * t2v;
-          PI[2 * DK + c] = t2v;
-          GC[c] = t0v * t1v * t2v * t3v;
-        }
-      }
-    }
-
-    // level operand writer: slot ls (0/1), block I, level lam
-    auto write_levels = [&](const float (&al)[SUB][2], int ls, int lam) {
-      char* LA = R_L + (size_t)(ls * NB + iI) * K::LVL_ROWS * K::RS_DK;
+    // level operand writer: slot ls (0/1), level lam, for the item's block
+    auto write_levels = [&](int ls, int lam) {
+      char* LA = R_L + (size_t)(ls * NB + iI) * K::LVL_ROWS * K::RS_DK + 2 * icp * ES;
       char* LB = LA + 16 * K::RS_DK;
       float f0 = 1.f, f1 = 1.f;
 #pragma unroll
@@ -305,10 +358,10 @@ __global__ __launch_bounds__((DV / 16) * 64) void chunk_fwd_kernel(
           }
           const int u = (m / (2 * lam)) * lam + (m & (lam - 1));
           float q0, q1, k0, k1;
-          ld_q(m, q0, q1);
-          ld_k(m, k0, k1);
-          Pair<T>::store(LA + u * K::RS_DK + 2 * icp * ES, q0 * f0, q1 * f1);
-          Pair<T>::store(LA + (8 + u) * K::RS_DK + 2 * icp * ES, k0 * f0, k1 * f1);
+          R::unpack(qr[m], q0, q1);
+          R::unpack(kr_raw[m], k0, k1);
+          R::st(LA + u * K::RS_DK, q0 * f0, q1 * f1);
+          R::st(LA + (8 + u) * K::RS_DK, k0 * f0, k1 * f1);
         }
       }
       float b0 = 1.f, b1 = 1.f;
@@ -324,41 +377,53 @@ __global__ __launch_bounds__((DV / 16) * 64) void chunk_fwd_kernel(
           }
           const int v = (m / (2 * lam)) * lam + (m & (lam - 1));
           float k0, k1;
-          ld_k(m, k0, k1);
-          Pair<T>::store(LB + v * K::RS_DK + 2 * icp * ES, k0 * b0, k1 * b1);
+          R::unpack(kr_raw[m], k0, k1);
+          R::st(LB + v * K::RS_DK, k0 * b0, k1 * b1);
         }
       }
     };
 
-    // ================= phase B: 16-block anchored operands + level 8 / 4 operands
+    // ================= phase B: 16-block anchored operands (role 0) + level 8 / 4 operands (role 1)
     if (has_item) {
-      float al[SUB][2];
-      ld_alpha(al);
-      char* Xq = R_OP;
-      char* Xk = R_OP + C * K::RS_DK;
-      char* Y = R_OP + 2 * C * K::RS_DK;
-      float f0 = 1.f, f1 = 1.f;
+      ld_item(true);
+      if (r0) {
+        char* Xq = R_OP + item_off;
+        char* Xk = R_OP + C * K::RS_DK + item_off;
+        char* Y = R_OP + 2 * C * K::RS_DK + item_off;
+        float f0 = 1.f, f1 = 1.f;
 #pragma unroll
-      for (int m = 0; m < SUB; ++m) {
-        f0 *= al[m][0];
-        f1 *= al[m][1];
-        float q0, q1, k0, k1;
-        ld_q(m, q0, q1);
-        ld_k(m, k0, k1);
-        Pair<T>::store(Xq + item_off + m * K::RS_DK, q0 * f0, q1 * f1);
-        Pair<T>::store(Xk + item_off + m * K::RS_DK, k0 * f0, k1 * f1);
-      }
-      float b0 = 1.f, b1 = 1.f;
+        for (int m = 0; m < SUB; ++m) {
+          f0 *= al[m][0];
+          f1 *= al[m][1];
+          float q0, q1, k0, k1;
+          R::unpack(qr[m], q0, q1);
+          R::unpack(kr_raw[m], k0, k1);
+          R::st(Xq + m * K::RS_DK, q0 * f0, q1 * f1);
+          R::st(Xk + m * K::RS_DK, k0 * f0, k1 * f1);
+        }
+        float b0 = 1.f, b1 = 1.f;
 #pragma unroll
-      for (int m = SUB - 1; m >= 0; --m) {
-        float k0, k1;
-        ld_k(m, k0, k1);
-        Pair<T>::store(Y + item_off + m * K::RS_DK, k0 * b0, k1 * b1);
-        b0 *= al[m][0];
-        b1 *= al[m][1];
+        for (int m = SUB - 1; m >= 0; --m) {
+          float k0, k1;
+          R::unpack(kr_raw[m], k0, k1);
+          R::st(Y + m * K::RS_DK, k0 * b0, k1 * b1);
+          b0 *= al[m][0];
+          b1 *= al[m][1];
+        }
+        if (iI == 0) {
+          const float2 t0v = *(const float2*)(GT + 2 * icp), t1v = *(const float2*)(GT + DK + 2 * icp);
+          const float2 t2v = *(const float2*)(GT + 2 * DK + 2 * icp), t3v = *(const float2*)(GT + 3 * DK + 2 * icp);
+          *(float2*)(PI + 0 * DK + 2 * icp) = t1v;
+          *(float2*)(PI + 1 * DK + 2 * icp) = make_float2(t1v.x * t2v.x, t1v.y * t2v.y);
+          *(float2*)(PI + 2 * DK + 2 * icp) = t2v;
+          *(float2*)(GC + 2 * icp) =
+              make_float2(t0v.x * t1v.x * t2v.x * t3v.x, t0v.y * t1v.y * t2v.y * t3v.y);
+        }
       }
-      write_levels(al, 0, 8);
-      write_levels(al, 1, 4);
+      if (r1) {
+        write_levels(0, 8);
+        write_levels(1, 4);
+      }
     }
     __syncthreads();
 
@@ -376,85 +441,103 @@ __global__ __launch_bounds__((DV / 16) * 64) void chunk_fwd_kernel(
         const char* Xq = R_OP + (16 * I + n) * K::RS_DK;
         const char* Xk = R_OP + C * K::RS_DK + (16 * I + n) * K::RS_DK;
         const char* Y = R_OP + 2 * C * K::RS_DK + (16 * J + n) * K::RS_DK;
+        Frag<T> fa[K::KS], fk[K::KS], fb[K::KS];
 #pragma unroll
         for (int ks = 0; ks < K::KS; ++ks) {
           const int c0 = 32 * ks + 8 * g;
-          Frag<T> fa, fk, fb;
-          fb.load8(Y + c0 * ES);
-          if (pi >= 0) {
+          fb[ks].load8(Y + c0 * ES);
+          fa[ks].load8(Xq + c0 * ES);
+          fk[ks].load8(Xk + c0 * ES);
+        }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) fb.set(e, fb.get(e) * PI[pi * DK + c0 + e]);
+        for (int ks = 0; ks < K::KS; ++ks) {
+          if (pi >= 0) {
+            const int c0 = 32 * ks + 8 * g;
+            const float4 p0 = *(const float4*)(PI + pi * DK + c0);
+            const float4 p1 = *(const float4*)(PI + pi * DK + c0 + 4);
+            const float pv8[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+            fb[ks].scale(pv8);
           }
-          fa.load8(Xq + c0 * ES);
-          fk.load8(Xk + c0 * ES);
-          mma(r1a[s], fa, fb);
-          mma(r1t[s], fk, fb);
+          mma(r1a[s], fa[ks], fb[ks]);
+          mma(r1t[s], fk[ks], fb[ks]);
         }
       } else if (j < NJ1) {
         const int ls = (j - 6) / NB, I = (j - 6) % NB;
         const char* LA = R_L + (size_t)(ls * NB + I) * K::LVL_ROWS * K::RS_DK;
         const char* LB = LA + 16 * K::RS_DK;
+        Frag<T> fa[K::KS], fb[K::KS];
 #pragma unroll
         for (int ks = 0; ks < K::KS; ++ks) {
           const int c0 = 32 * ks + 8 * g;
-          Frag<T> fa, fb;
-          fa.load8(LA + n * K::RS_DK + c0 * ES);
+          fa[ks].load8(LA + n * K::RS_DK + c0 * ES);
           if (n < 8)
-            fb.load8(LB + n * K::RS_DK + c0 * ES);
+            fb[ks].load8(LB + n * K::RS_DK + c0 * ES);
           else
-            fb.zero();
-          mma(r1a[s], fa, fb);
+            fb[ks].zero();
         }
+#pragma unroll
+        for (int ks = 0; ks < K::KS; ++ks) mma(r1a[s], fa[ks], fb[ks]);
       }
     }
     __syncthreads();
 
-    // ================= phase C: gamma / rho operands + level 2 / 1 operands
+    // ================= phase C: gamma / rho operands (role 0) + level 2 / 1 operands (role 1)
     if (has_item) {
-      float al[SUB][2];
-      ld_alpha(al);
-      char* QG = R_OP + K::OFF_QG;
-      char* KGT = R_OP + K::OFF_KGT;
-      char* KRT = R_OP + K::OFF_KRT;
-      char* kg_row0 = KGT + (2 * icp) * K::RS_C + (SUB * iI) * ES;
-      char* kg_row1 = kg_row0 + K::RS_C;
-      char* kr_row0 = KRT + (2 * icp) * K::RS_C + (SUB * iI) * ES;
-      char* kr_row1 = kr_row0 + K::RS_C;
-      float f0 = Gp[0], f1 = Gp[1];
-      float p0 = 0.f, p1 = 0.f;  // previous position's values (pairs of positions per store)
+      ld_item(true);
+      if (r0) {
+        const float2 t0v = *(const float2*)(GT + 2 * icp), t1v = *(const float2*)(GT + DK + 2 * icp);
+        const float2 t2v = *(const float2*)(GT + 2 * DK + 2 * icp), t3v = *(const float2*)(GT + 3 * DK + 2 * icp);
+        float Gp[2], Rp[2];
+        Gp[0] = iI == 0 ? 1.f : iI == 1 ? t0v.x : iI == 2 ? t0v.x * t1v.x : t0v.x * t1v.x * t2v.x;
+        Gp[1] = iI == 0 ? 1.f : iI == 1 ? t0v.y : iI == 2 ? t0v.y * t1v.y : t0v.y * t1v.y * t2v.y;
+        Rp[0] = iI == 3 ? 1.f : iI == 2 ? t3v.x : iI == 1 ? t2v.x * t3v.x : t1v.x * t2v.x * t3v.x;
+        Rp[1] = iI == 3 ? 1.f : iI == 2 ? t3v.y : iI == 1 ? t2v.y * t3v.y : t1v.y * t2v.y * t3v.y;
+        char* QG = R_OP + K::OFF_QG + item_off;
+        // (K o gamma)^T and (K o rho)^T rows of the item's two channels, positions 16 iI ..
+        // 16 iI + 15: written as 8-position row segments
+        char* pg0 = R_OP + K::OFF_KGT + (2 * icp) * K::RS_C + (SUB * iI) * ES;
+        char* pr0 = R_OP + K::OFF_KRT + (2 * icp) * K::RS_C + (SUB * iI) * ES;
+        float f0 = Gp[0], f1 = Gp[1];
 #pragma unroll
-      for (int m = 0; m < SUB; ++m) {
-        f0 *= al[m][0];
-        f1 *= al[m][1];
-        float q0, q1, k0, k1;
-        ld_q(m, q0, q1);
-        ld_k(m, k0, k1);
-        Pair<T>::store(QG + item_off + m * K::RS_DK, q0 * f0, q1 * f1);
-        if (m & 1) {
-          Pair<T>::store(kg_row0 + (m - 1) * ES, p0, k0 * f0);
-          Pair<T>::store(kg_row1 + (m - 1) * ES, p1, k1 * f1);
-        } else {
-          p0 = k0 * f0;
-          p1 = k1 * f1;
+        for (int h8 = 0; h8 < SUB; h8 += 8) {
+          float g8a[8], g8b[8];
+#pragma unroll
+          for (int mm = 0; mm < 8; ++mm) {
+            const int m = h8 + mm;
+            f0 *= al[m][0];
+            f1 *= al[m][1];
+            float q0, q1, k0, k1;
+            R::unpack(qr[m], q0, q1);
+            R::unpack(kr_raw[m], k0, k1);
+            R::st(QG + m * K::RS_DK, q0 * f0, q1 * f1);
+            g8a[mm] = k0 * f0;
+            g8b[mm] = k1 * f1;
+          }
+          st_row8<T>(pg0 + h8 * ES, g8a);
+          st_row8<T>(pg0 + K::RS_C + h8 * ES, g8b);
+        }
+        float b0 = Rp[0], b1 = Rp[1];
+#pragma unroll
+        for (int h8 = SUB - 8; h8 >= 0; h8 -= 8) {
+          float r8a[8], r8b[8];
+#pragma unroll
+          for (int mm = 7; mm >= 0; --mm) {
+            const int m = h8 + mm;
+            float k0, k1;
+            R::unpack(kr_raw[m], k0, k1);
+            r8a[mm] = k0 * b0;
+            r8b[mm] = k1 * b1;
+            b0 *= al[m][0];
+            b1 *= al[m][1];
+          }
+          st_row8<T>(pr0 + h8 * ES, r8a);
+          st_row8<T>(pr0 + K::RS_C + h8 * ES, r8b);
         }
       }
-      float b0 = Rp[0], b1 = Rp[1];
-#pragma unroll
-      for (int m = SUB - 1; m >= 0; --m) {
-        float k0, k1;
-        ld_k(m, k0, k1);
-        if (m & 1) {
-          p0 = k0 * b0;
-          p1 = k1 * b1;
-        } else {
-          Pair<T>::store(kr_row0 + m * ES, k0 * b0, p0);
-          Pair<T>::store(kr_row1 + m * ES, k1 * b1, p1);
-        }
-        b0 *= al[m][0];
-        b1 *= al[m][1];
+      if (r1) {
+        write_levels(0, 2);
+        write_levels(1, 1);
       }
-      write_levels(al, 0, 2);
-      write_levels(al, 1, 1);
     }
     __syncthreads();
 
@@ -466,57 +549,70 @@ __global__ __launch_bounds__((DV / 16) * 64) void chunk_fwd_kernel(
     for (int s = 0; s < MJ2; ++s) {
       const int j = wave + s * NW;
       r2[s] = zero4();
-      if (j < 8) {
-        const int ls = j / NB, I = j % NB;
-        const char* LA = R_L + (size_t)(ls * NB + I) * K::LVL_ROWS * K::RS_DK;
-        const char* LB = LA + 16 * K::RS_DK;
+      if (j < NJ2) {
+        const char* pa_;
+        const char* pb_;
+        bool use_b = true;
+        if (j < 8) {
+          const int ls = j / NB, I = j % NB;
+          pa_ = R_L + (size_t)(ls * NB + I) * K::LVL_ROWS * K::RS_DK + n * K::RS_DK;
+          pb_ = R_L + (size_t)(ls * NB + I) * K::LVL_ROWS * K::RS_DK + (16 + n) * K::RS_DK;
+          use_b = n < 8;
+        } else {
+          const int I = j - 8;
+          pa_ = Qs + (16 * I + n) * K::RS_DK;
+          pb_ = Ks + (16 * I + n) * K::RS_DK;
+        }
+        Frag<T> fa[K::KS], fb[K::KS];
 #pragma unroll
         for (int ks = 0; ks < K::KS; ++ks) {
           const int c0 = 32 * ks + 8 * g;
-          Frag<T> fa, fb;
-          fa.load8(LA + n * K::RS_DK + c0 * ES);
-          if (n < 8)
-            fb.load8(LB + n * K::RS_DK + c0 * ES);
+          fa[ks].load8(pa_ + c0 * ES);
+          if (use_b)
+            fb[ks].load8(pb_ + c0 * ES);
           else
-            fb.zero();
-          mma(r2[s], fa, fb);
+            fb[ks].zero();
         }
-      } else if (j < NJ2) {
-        const int I = j - 8;
 #pragma unroll
-        for (int ks = 0; ks < K::KS; ++ks) {
-          const int c0 = 32 * ks + 8 * g;
-          Frag<T> fa, fb;
-          fa.load8(Qs + (16 * I + n) * K::RS_DK + c0 * ES);
-          fb.load8(Ks + (16 * I + n) * K::RS_DK + c0 * ES);
-          mma(r2[s], fa, fb);
-        }
+        for (int ks = 0; ks < K::KS; ++ks) mma(r2[s], fa[ks], fb[ks]);
       }
     }
     __syncthreads();
 
-    // ================= phase D: scatter T and A (fp32) and stage v
+    // ================= phase D: scatter D (fp32, T before its beta row scale) and A~
     float* TT = (float*)(R_L + K::OFF_TT);
-    float* AA = (float*)(R_L + K::OFF_AA);
-    constexpr int LDF = K::RS_F / 4;
-    auto put_level = [&](const f32x4_t& acc, int lam, int I) {
+    char* AT = R_L + K::OFF_AT;
+    // level results: D[u][v] holds the A entry (u < 8) or D entry (u >= 8) of upper row
+    // rank u & 7 and lower row rank v, valid when both lie in one 2 lam block
+    auto put_level_t = [&](auto lam_c, const f32x4_t& acc, int I) {
+      constexpr int lam = decltype(lam_c)::value;
       if (n < 8) {
         const int v = n;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int row = 4 * g + e;
           const int u = row & 7;
-          if (u / lam == v / lam) {
+          if ((u / lam) == (v / lam)) {
             const int mu = (u / lam) * 2 * lam + lam + (u % lam);
             const int ml = (v / lam) * 2 * lam + (v % lam);
             const int gi = 16 * I + mu, gj = 16 * I + ml;
             if (row < 8)
-              AA[gi * LDF + gj] = acc[e];
+              st_elem(AT + gi * K::RS_C + gj * ES, acc[e], ES);
             else
-              TT[gi * LDF + gj] = BETA[gi] * acc[e];
+              TT[gi * LDF + gj] = acc[e];
           }
         }
       }
+    };
+    auto put_level = [&](const f32x4_t& acc, int lam, int I) {
+      if (lam == 8)
+        put_level_t(std::integral_constant<int, 8>(), acc, I);
+      else if (lam == 4)
+        put_level_t(std::integral_constant<int, 4>(), acc, I);
+      else if (lam == 2)
+        put_level_t(std::integral_constant<int, 2>(), acc, I);
+      else
+        put_level_t(std::integral_constant<int, 1>(), acc, I);
     };
 #pragma unroll
     for (int s = 0; s < MJ1; ++s) {
@@ -526,8 +622,8 @@ __global__ __launch_bounds__((DV / 16) * 64) void chunk_fwd_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int gi = 16 * I + 4 * g + e, gj = 16 * J + n;
-          AA[gi * LDF + gj] = r1a[s][e];
-          TT[gi * LDF + gj] = BETA[gi] * r1t[s][e];
+          st_elem(AT + gi * K::RS_C + gj * ES, r1a[s][e], ES);
+          TT[gi * LDF + gj] = r1t[s][e];
         }
       } else if (j < NJ1) {
         const int ls = (j - 6) / NB, I = (j - 6) % NB;
@@ -543,134 +639,260 @@ __global__ __launch_bounds__((DV / 16) * 64) void chunk_fwd_kernel(
       } else if (j < NJ2) {
         const int I = j - 8;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (4 * g + e == n) AA[(16 * I + n) * LDF + 16 * I + n] = r2[s][e];
+        for (int e = 0; e < 4; ++e) {
+          const int row = 4 * g + e;
+          if (row <= n) st_elem(AT + (16 * I + row) * K::RS_C + (16 * I + n) * ES, row == n ? r2[s][e] : 0.f, ES);
+        }
       }
     }
-    // v of this chunk -> LDS, then prefetch the next chunk's v
+    for (int x = tid; x < 6 * 16 * 2; x += NT) {  // 6 tiles x 16 rows x 2 segments of 8
+      const int t = x >> 5, i = (x >> 1) & 15, j0 = 8 * (x & 1);
+      const float z8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      st_row8<T>(AT + (16 * kUpI[t] + i) * K::RS_C + (16 * kUpJ[t] + j0) * ES, z8);
+    }
+    // v tile of this chunk -> LDS, then prefetch the next chunk's
 #pragma unroll
     for (int i = 0; i < K::VPT_V; ++i) {
       const int j = tid + NT * i;
       const int row = j / K::VROW_V, c16 = j % K::VROW_V;
-      *(uint4*)(R_IN + K::OFF_VV + row * K::RS_DV + c16 * 16) = pv[i];
+      *(uint4*)(R_IN + K::OFF_VV + row * K::RS_VT + c16 * 16) = (t0 + row < Tlen) ? pv[i] : make_uint4(0, 0, 0, 0);
     }
     if (chunk + 1 < nchunks) issue_v(chunk + 1);
     __syncthreads();
 
-    if (dbg) {
-      float* D = dbg + ((size_t)bh * nchunks + chunk) * 4 * C * C;
+    if (dbg && vt == 0) {
+      float* Dp = dbg + ((size_t)bh * nchunks + chunk) * 4 * C * C;
       for (int x = tid; x < C * C; x += NT) {
         const int i = x / C, j = x % C;
-        D[x] = j < i ? TT[i * LDF + j] : 0.f;
-        D[C * C + x] = j <= i ? AA[i * LDF + j] : 0.f;
+        Dp[x] = j < i ? BETA[i] * TT[i * LDF + j] : 0.f;
+        Dp[C * C + x] = j <= i ? Elem<T>::load(AT + i * K::RS_C, j) : 0.f;
       }
     }
 
-    // ================= phase I: M = (I + T)^-1
-    float* MM = (float*)(R_IN + K::OFF_MM);
-    char* MT = R_IN + K::OFF_MT;
-    char* AT = R_L + K::OFF_AT;
-    if (wave == 0) {
-      // diagonal blocks by forward substitution: lane = (block, column)
-      const int I = lane >> 4, col = lane & 15;
-      float x[SUB];
+    // O = (Q o gamma) S does not depend on the inverse: waves 1.. do it while wave 0
+    // runs the diagonal-block substitution, wave 0 in the second off-diagonal stage.
+    f32x4_t Ot[NB];
+    auto q_times_S = [&]() {
+      Frag<T> bs[K::KS];
 #pragma unroll
-      for (int i = 0; i < SUB; ++i) {
-        const float* trow = TT + (16 * I + i) * LDF + 16 * I;
-        float acc = (i == col) ? 1.f : 0.f;
+      for (int ks = 0; ks < K::KS; ++ks) bs[ks].from_acc(S[2 * ks], S[2 * ks + 1]);
 #pragma unroll
-        for (int p = 0; p < i; ++p) acc -= trow[p] * x[p];
-        x[i] = acc;
+      for (int I = 0; I < NB; ++I) {
+        Ot[I] = zero4();
+        const char* qrow = R_OP + K::OFF_QG + (16 * I + n) * K::RS_DK;
+        Frag<T> fq[K::KS];
+#pragma unroll
+        for (int ks = 0; ks < K::KS; ++ks) {
+          const int c0 = 32 * ks + 4 * g;
+          fq[ks].load4x2(qrow + c0 * ES, qrow + (c0 + 16) * ES);
+        }
+#pragma unroll
+        for (int ks = 0; ks < K::KS; ++ks) mma(Ot[I], fq[ks], bs[ks]);
       }
+    };
+    if (wave != 0) q_times_S();
+
+    // ================= phase I: M = (I + T)^-1 with T = diag(beta) D
+    float* MM = (float*)(R_IN + K::OFF_MM);
+    char* MB = R_L + K::OFF_MB;  // transposed 16x16 blocks: 0 N00, 1 N11, 2 N22, 3 M10, 4 M20
+    auto mb_row = [&](int blk, int r) -> float* { return (float*)(MB + (blk * SUB + r) * K::RS_MB); };
+    if (wave == 0) {
+      // diagonal blocks: lane = (block I, column col); it also holds row `col` of T_II
+      const int I = lane >> 4, col = lane & 15;
+      const float* drow = TT + (16 * I + col) * LDF + 16 * I;
+      const float bcol = BETA[16 * I + col];
+      float tr[SUB];
+#pragma unroll
+      for (int p4 = 0; p4 < SUB; p4 += 4) {
+        const float4 w4 = *(const float4*)(drow + p4);
+        tr[p4] = w4.x;
+        tr[p4 + 1] = w4.y;
+        tr[p4 + 2] = w4.z;
+        tr[p4 + 3] = w4.w;
+      }
+#pragma unroll
+      for (int p = 0; p < SUB; ++p) tr[p] = p < col ? bcol * tr[p] : 0.f;
+      float x[SUB], nx[SUB];  // column of N_II and its negation (accumulated with fmac)
+#define KDA_FS_ROW(i)                                                                        \
+  {                                                                                          \
+    float acc = (col == i) ? 1.f : 0.f;                                                      \
+    _Pragma("unroll") for (int p = 0; p < i; ++p) acc = fmaf(row_bcast<i>(tr[p]), nx[p], acc); \
+    x[i] = acc;                                                                              \
+    nx[i] = -acc;                                                                            \
+  }
+      KDA_FS_ROW(0) KDA_FS_ROW(1) KDA_FS_ROW(2) KDA_FS_ROW(3) KDA_FS_ROW(4) KDA_FS_ROW(5) KDA_FS_ROW(6)
+      KDA_FS_ROW(7) KDA_FS_ROW(8) KDA_FS_ROW(9) KDA_FS_ROW(10) KDA_FS_ROW(11) KDA_FS_ROW(12) KDA_FS_ROW(13)
+      KDA_FS_ROW(14) KDA_FS_ROW(15)
+#undef KDA_FS_ROW
 #pragma unroll
       for (int i = 0; i < SUB; ++i) MM[(16 * I + i) * LDF + 16 * I + col] = x[i];
-    } else {
-      // A~ = A (lower incl. diagonal) as matrix-core operand
-      for (int x = tid - 64; x < C * C; x += NT - 64) {
-        const int i = x / C, j = x % C;
-        st_elem_bf16_or_f32(AT + i * K::RS_C + j * ES, j <= i ? AA[i * LDF + j] : 0.f, ES);
+      if (I < 3) {
+        float* dst = mb_row(I, col);
+#pragma unroll
+        for (int p4 = 0; p4 < SUB; p4 += 4) *(float4*)(dst + p4) = make_float4(x[p4], x[p4 + 1], x[p4 + 2], x[p4 + 3]);
       }
     }
     __syncthreads();
-    // E_IK = N_II T_IK for K < I, into the A buffer (A~ already formed)
-    float* EE = AA;
-    for (int x = tid; x < 6 * 256; x += NT) {
-      const int blk = x >> 8, i = (x >> 4) & 15, r = x & 15;
-      const int I = kOffI[blk], Kb = kOffJ[blk];
-      float acc = 0.f;
+    // off-diagonal blocks.  In product instruction s the k-slot is 4 g + s, so an
+    // accumulator tile is directly the B operand of the next product.
+    auto a_T = [&](int I, int Kb, float (&a)[4]) {  // row n of T_IK = beta_i D_IK
+      const float4 w4 = *(const float4*)(TT + (16 * I + n) * LDF + 16 * Kb + 4 * g);
+      const float bi = BETA[16 * I + n];
+      a[0] = bi * w4.x;
+      a[1] = bi * w4.y;
+      a[2] = bi * w4.z;
+      a[3] = bi * w4.w;
+    };
+    auto b_MB = [&](int blk, float (&bb)[4]) {  // B = a block whose transpose is stored in MB
+      const float4 w4 = *(const float4*)(mb_row(blk, n) + 4 * g);
+      bb[0] = w4.x;
+      bb[1] = w4.y;
+      bb[2] = w4.z;
+      bb[3] = w4.w;
+    };
+    auto mm4_acc = [&](f32x4_t& acc, const float (&a)[4], const f32x4_t& bacc) {
+      const float bb[4] = {bacc[0], bacc[1], bacc[2], bacc[3]};
+      mm4(acc, a, bb);
+    };
+    auto neg_N_times = [&](int I, const f32x4_t& z) -> f32x4_t {  // -N_II z
+      const float4 w4 = *(const float4*)(MM + (16 * I + n) * LDF + 16 * I + 4 * g);
+      const float a[4] = {w4.x, w4.y, w4.z, w4.w};
+      f32x4_t r = zero4();
+      mm4_acc(r, a, z);
+      return -r;
+    };
+    auto put_M = [&](int I, int J, const f32x4_t& m, int blk) {
 #pragma unroll
-      for (int p = 0; p < SUB; ++p) acc += MM[(16 * I + i) * LDF + 16 * I + p] * TT[(16 * I + p) * LDF + 16 * Kb + r];
-      EE[(16 * I + i) * LDF + 16 * Kb + r] = acc;
+      for (int e = 0; e < 4; ++e) MM[(16 * I + 4 * g + e) * LDF + 16 * J + n] = m[e];
+      if (blk >= 0) *(float4*)(mb_row(blk, n) + 4 * g) = make_float4(m[0], m[1], m[2], m[3]);
+    };
+    f32x4_t keep = zero4();  // partial sum carried across the stages (waves 0 and 3)
+    {
+      float a[4], bb[4];
+      if (wave == 0) {  // M10, then P30 = T30 N00 + T31 M10
+        f32x4_t z = zero4();
+        a_T(1, 0, a);
+        b_MB(0, bb);
+        mm4(z, a, bb);
+        const f32x4_t m10 = neg_N_times(1, z);
+        put_M(1, 0, m10, 3);
+        a_T(3, 0, a);
+        b_MB(0, bb);
+        mm4(keep, a, bb);
+        a_T(3, 1, a);
+        mm4_acc(keep, a, m10);
+      } else if (wave == 1) {  // M21, then M31 = -N33 (T31 N11 + T32 M21)
+        f32x4_t z = zero4();
+        a_T(2, 1, a);
+        b_MB(1, bb);
+        mm4(z, a, bb);
+        const f32x4_t m21 = neg_N_times(2, z);
+        put_M(2, 1, m21, -1);
+        f32x4_t p = zero4();
+        a_T(3, 1, a);
+        b_MB(1, bb);
+        mm4(p, a, bb);
+        a_T(3, 2, a);
+        mm4_acc(p, a, m21);
+        put_M(3, 1, neg_N_times(3, p), -1);
+      } else if (wave == 2) {  // M32
+        f32x4_t z = zero4();
+        a_T(3, 2, a);
+        b_MB(2, bb);
+        mm4(z, a, bb);
+        put_M(3, 2, neg_N_times(3, z), -1);
+      } else if (wave == 3) {  // P20 = T20 N00
+        a_T(2, 0, a);
+        b_MB(0, bb);
+        mm4(keep, a, bb);
+      }
     }
     __syncthreads();
-    // block rows: M_IJ = -sum_{K=J}^{I-1} E_IK M_KJ
-#pragma unroll
-    for (int I = 1; I < NB; ++I) {
-      for (int x = tid; x < I * 256; x += NT) {
-        const int J = x >> 8, i = (x >> 4) & 15, j = x & 15;
-        float acc = 0.f;
-        for (int Kb = J; Kb < I; ++Kb) {
-#pragma unroll
-          for (int r = 0; r < SUB; ++r)
-            acc += EE[(16 * I + i) * LDF + 16 * Kb + r] * MM[(16 * Kb + r) * LDF + 16 * J + j];
-        }
-        MM[(16 * I + i) * LDF + 16 * J + j] = -acc;
-      }
-      __syncthreads();
+    if (wave == 0) q_times_S();  // wave 0's share, in the stage where it is otherwise idle
+    if (wave == 3) {  // M20 = -N22 (P20 + T21 M10)
+      float a[4], bb[4];
+      a_T(2, 1, a);
+      b_MB(3, bb);
+      mm4(keep, a, bb);
+      put_M(2, 0, neg_N_times(2, keep), 4);
     }
-    // M~ = M diag(beta), lower incl. diagonal, as matrix-core operand
-    for (int x = tid; x < C * C; x += NT) {
-      const int i = x / C, j = x % C;
-      st_elem_bf16_or_f32(MT + i * K::RS_C + j * ES, j <= i ? MM[i * LDF + j] * BETA[j] : 0.f, ES);
+    __syncthreads();
+    if (wave == 0) {  // M30 = -N33 (P30 + T32 M20)
+      float a[4], bb[4];
+      a_T(3, 2, a);
+      b_MB(4, bb);
+      mm4(keep, a, bb);
+      put_M(3, 0, neg_N_times(3, keep), -1);
     }
-    if (dbg) {
-      float* D = dbg + ((size_t)bh * nchunks + chunk) * 4 * C * C + 2 * C * C;
+    __syncthreads();
+    // M~ = M diag(beta), lower incl. diagonal, as matrix-core operand (8 columns per step)
+    char* MT = R_IN + K::OFF_MT;
+#pragma unroll
+    for (int x = tid; x < C * C / 8; x += NT) {
+      const int i = x / (C / 8), j0 = 8 * (x % (C / 8));
+      const float4 m0 = *(const float4*)(MM + i * LDF + j0), m1 = *(const float4*)(MM + i * LDF + j0 + 4);
+      const float4 b0 = *(const float4*)(BETA + j0), b1 = *(const float4*)(BETA + j0 + 4);
+      float v8[8] = {m0.x * b0.x, m0.y * b0.y, m0.z * b0.z, m0.w * b0.w,
+                     m1.x * b1.x, m1.y * b1.y, m1.z * b1.z, m1.w * b1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (j0 + e > i) v8[e] = 0.f;
+      st_row8<T>(MT + i * K::RS_C + j0 * ES, v8);
+    }
+    if (dbg && vt == 0) {
+      float* Dp = dbg + ((size_t)bh * nchunks + chunk) * 4 * C * C + 2 * C * C;
       for (int x = tid; x < C * C; x += NT) {
         const int i = x / C, j = x % C;
-        D[x] = j <= i ? MM[i * LDF + j] : 0.f;
+        Dp[x] = j <= i ? MM[i * LDF + j] : 0.f;
       }
     }
     __syncthreads();
 
     // ================= phase W: W = M~ (K o gamma) -> -W in LDS;  U_w = M~ V[:, w] in registers
     char* WW = R_L + K::OFF_TT;
+    f32x4_t Dl[NB];
     {
-      constexpr int NCT = DK / 16;
-      for (int t = wave; t < NB * NCT; t += NW) {
-        const int I = t / NCT, cn = t % NCT;
-        f32x4_t acc = zero4();
-        const int nks = I < 2 ? 1 : 2;
-        for (int ks = 0; ks < nks; ++ks) {
-          Frag<T> fa, fb;
-          fa.load8(MT + (16 * I + n) * K::RS_C + (32 * ks + 8 * g) * ES);
-          fb.load8(R_OP + K::OFF_KGT + (16 * cn + n) * K::RS_C + (32 * ks + 8 * g) * ES);
-          mma(acc, fa, fb);
+      Frag<T> am[NB][2];
+#pragma unroll
+      for (int I = 0; I < NB; ++I)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          if (ks == 0 || I >= 2)
+            am[I][ks].load8(MT + (16 * I + n) * K::RS_C + (32 * ks + 8 * g) * ES);
+          else
+            am[I][ks].zero();
         }
+      constexpr int NCT = DK / 16;
+      for (int cn = wave; cn < NCT; cn += NW) {
+        Frag<T> bk[2];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          st_elem_bf16_or_f32(WW + (16 * I + 4 * g + e) * K::RS_DK + (16 * cn + n) * ES, -acc[e], ES);
-        if (dbg && cn < 4) {
-          float* D = dbg + ((size_t)bh * nchunks + chunk) * 4 * C * C + 3 * C * C;
+        for (int ks = 0; ks < 2; ++ks)
+          bk[ks].load8(R_OP + K::OFF_KGT + (16 * cn + n) * K::RS_C + (32 * ks + 8 * g) * ES);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) D[(16 * I + 4 * g + e) * C + 16 * cn + n] = acc[e];
+        for (int I = 0; I < NB; ++I) {
+          f32x4_t acc = zero4();
+          mma(acc, am[I][0], bk[0]);
+          if (I >= 2) mma(acc, am[I][1], bk[1]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            st_elem(WW + (16 * I + 4 * g + e) * K::RS_DK + (16 * cn + n) * ES, -acc[e], ES);
+          if (dbg && vt == 0 && cn < 4) {
+            float* Dp = dbg + ((size_t)bh * nchunks + chunk) * 4 * C * C + 3 * C * C;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Dp[(16 * I + 4 * g + e) * C + 16 * cn + n] = acc[e];
+          }
         }
       }
-    }
-    f32x4_t Dl[NB];
+      // U for this wave's value columns
+      Frag<T> bv[2];
 #pragma unroll
-    for (int I = 0; I < NB; ++I) {
-      Dl[I] = zero4();
-      const int nks = I < 2 ? 1 : 2;
+      for (int ks = 0; ks < 2; ++ks)
+        bv[ks].load_col8(R_IN + K::OFF_VV + (32 * ks + 8 * g) * K::RS_VT + (16 * wave + n) * ES, K::RS_VT);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        if (ks < nks) {
-          Frag<T> fa, fb;
-          fa.load8(MT + (16 * I + n) * K::RS_C + (32 * ks + 8 * g) * ES);
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            fb.set(e, Elem<T>::load(R_IN + K::OFF_VV + (32 * ks + 8 * g + e) * K::RS_DV, 16 * wave + n));
-          mma(Dl[I], fa, fb);
-        }
+      for (int I = 0; I < NB; ++I) {
+        Dl[I] = zero4();
+        mma(Dl[I], am[I][0], bv[0]);
+        if (I >= 2) mma(Dl[I], am[I][1], bv[1]);
       }
     }
     __syncthreads();
@@ -680,21 +902,17 @@ __global__ __launch_bounds__((DV / 16) * 64) void chunk_fwd_kernel(
       Frag<T> bs[K::KS];
 #pragma unroll
       for (int ks = 0; ks < K::KS; ++ks) bs[ks].from_acc(S[2 * ks], S[2 * ks + 1]);
-      f32x4_t Ot[NB];
 #pragma unroll
       for (int I = 0; I < NB; ++I) {
-        Ot[I] = zero4();
         const char* wrow = WW + (16 * I + n) * K::RS_DK;
-        const char* qrow = R_OP + K::OFF_QG + (16 * I + n) * K::RS_DK;
+        Frag<T> fw[K::KS];
 #pragma unroll
         for (int ks = 0; ks < K::KS; ++ks) {
           const int c0 = 32 * ks + 4 * g;
-          Frag<T> fw, fq;
-          fw.load4x2(wrow + c0 * ES, wrow + (c0 + 16) * ES);
-          fq.load4x2(qrow + c0 * ES, qrow + (c0 + 16) * ES);
-          mma(Dl[I], fw, bs[ks]);
-          mma(Ot[I], fq, bs[ks]);
+          fw[ks].load4x2(wrow + c0 * ES, wrow + (c0 + 16) * ES);
         }
+#pragma unroll
+        for (int ks = 0; ks < K::KS; ++ks) mma(Dl[I], fw[ks], bs[ks]);
       }
       Frag<T> bd[2];
       bd[0].from_acc(Dl[0], Dl[1]);
@@ -714,32 +932,35 @@ __global__ __launch_bounds__((DV / 16) * 64) void chunk_fwd_kernel(
       }
 #pragma unroll
       for (int r = 0; r < DK / 16; ++r) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) S[r][e] *= GC[16 * r + 4 * g + e];
+        const float4 gc = *(const float4*)(GC + 16 * r + 4 * g);
+        S[r][0] *= gc.x;
+        S[r][1] *= gc.y;
+        S[r][2] *= gc.z;
+        S[r][3] *= gc.w;
         const char* krow = R_OP + K::OFF_KRT + (16 * r + n) * K::RS_C;
+        Frag<T> fa[2];
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           const int p0 = 32 * s2 + 4 * g;
-          Frag<T> fa;
-          fa.load4x2(krow + p0 * ES, krow + (p0 + 16) * ES);
-          mma(S[r], fa, bd[s2]);
+          fa[s2].load4x2(krow + p0 * ES, krow + (p0 + 16) * ES);
         }
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) mma(S[r], fa[s2], bd[s2]);
       }
-      // stage O (reuses the v slot of R_IN: v is consumed)
+      // stage O (over the consumed v tile)
 #pragma unroll
       for (int I = 0; I < NB; ++I)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          st_elem_bf16_or_f32(R_IN + K::OFF_VV + (16 * I + 4 * g + e) * K::RS_DV + (16 * wave + n) * ES,
-                              Ot[I][e], ES);
+          st_elem(R_IN + K::OFF_VV + (16 * I + 4 * g + e) * K::RS_VT + (16 * wave + n) * ES, Ot[I][e], ES);
     }
     __syncthreads();
     // ================= phase O: coalesced store of the chunk's outputs
     for (int j = tid; j < C * K::VROW_V; j += NT) {
       const int row = j / K::VROW_V, c16 = j % K::VROW_V;
       if (row < nv)
-        *(uint4*)((char*)go + row_base(t0 + row) * DV * ES + (size_t)c16 * 16) =
-            *(const uint4*)(R_IN + K::OFF_VV + row * K::RS_DV + c16 * 16);
+        *(uint4*)((char*)go + row_base(t0 + row) * DV * ES + (size_t)v0 * ES + (size_t)c16 * 16) =
+            *(const uint4*)(R_IN + K::OFF_VV + row * K::RS_VT + c16 * 16);
     }
   }
 
@@ -747,36 +968,45 @@ __global__ __launch_bounds__((DV / 16) * 64) void chunk_fwd_kernel(
 #pragma unroll
     for (int r = 0; r < DK / 16; ++r)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sT[((size_t)bh * DK + 16 * r + 4 * g + e) * DV + 16 * wave + n] = S[r][e];
+      for (int e = 0; e < 4; ++e)
+        sT[((size_t)bh * DK + 16 * r + 4 * g + e) * DV + v0 + 16 * wave + n] = S[r][e];
   }
 }
 
-template <typename T, int DK, int DV>
+template <typename T, int DK, int VT>
 static hipError_t launch_chunk_t(const ChunkArgs& a) {
-  using K = Cfg<T, DK, DV>;
-  auto kern = chunk_fwd_kernel<T, DK, DV>;
+  using K = Cfg<T, DK, VT>;
+  auto kern = chunk_fwd_kernel<T, DK, VT>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, K::LDS);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3(a.B * a.H), dim3(K::NT), K::LDS, (hipStream_t)a.stream, a.q, a.k, a.v,
-                     a.alpha, a.beta, a.s0, a.o, a.sT, a.dbg, a.T, a.H);
+  const int BH = a.B * a.H;
+  hipLaunchKernelGGL(kern, dim3(BH * (a.dv / VT)), dim3(K::NT), K::LDS, (hipStream_t)a.stream, a.q, a.k, a.v,
+                     a.alpha, a.beta, a.s0, a.o, a.sT, a.dbg, a.T, a.H, a.dv, BH);
   return hipGetLastError();
+}
+
+// Value-tile width: narrow tiles (more workgroups; the gate work is repeated per
+// tile) when the (b, h) count alone cannot fill the chip's 256 compute units.
+static int pick_vt(const ChunkArgs& a) {
+  if (a.vt_override == 64 || a.vt_override == 128) return a.vt_override <= a.dv ? a.vt_override : a.dv;
+  if (a.dv == 64) return 64;
+  return (long)a.B * a.H >= 256 ? 128 : 64;
 }
 
 hipError_t launch_chunk(const ChunkArgs& a) {
   if (a.B * a.H == 0) return hipSuccess;
+  const int vt = pick_vt(a);
   if (!a.bf16) {
     // fp32 operands double every LDS buffer: only d_k = d_v = 64 fits
     if (a.dk == 64 && a.dv == 64) return launch_chunk_t<float, 64, 64>(a);
     return hipErrorInvalidValue;
   }
-  if (a.dk == 64 && a.dv == 64) return launch_chunk_t<bf16_t, 64, 64>(a);
-  if (a.dk == 64 && a.dv == 128) return launch_chunk_t<bf16_t, 64, 128>(a);
-  if (a.dk == 128 && a.dv == 64) return launch_chunk_t<bf16_t, 128, 64>(a);
-  return launch_chunk_t<bf16_t, 128, 128>(a);
+  if (a.dk == 64) return vt == 64 ? launch_chunk_t<bf16_t, 64, 64>(a) : launch_chunk_t<bf16_t, 64, 128>(a);
+  return vt == 64 ? launch_chunk_t<bf16_t, 128, 64>(a) : launch_chunk_t<bf16_t, 128, 128>(a);
 }
 
 }  // namespace kda

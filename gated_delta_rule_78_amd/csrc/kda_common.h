@@ -24,16 +24,16 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
 
-// Round to nearest even; inputs here are finite (NaN payloads are not kept).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 pair -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
-}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)(pack_bf16x2(f, 0.f) & 0xFFFFu); }
 
 // Element type policy: storage / operand type of q, k, v, alpha, beta, o and of
 // the matrix-core operands.
@@ -84,6 +84,23 @@ struct Frag<bf16_t> {
     return __uint_as_float((e & 1) ? (x & 0xFFFF0000u) : (x << 16));
   }
   __device__ __forceinline__ void zero() { w[0] = w[1] = w[2] = w[3] = 0u; }
+  __device__ __forceinline__ void scale(const float (&s)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = pack_bf16x2(__uint_as_float(w[i] << 16) * s[2 * i], __uint_as_float(w[i] & 0xFFFF0000u) * s[2 * i + 1]);
+  }
+  // slots from eight raw bf16 values
+  __device__ __forceinline__ void from_raw(const uint16_t (&v)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)v[2 * i] | ((uint32_t)v[2 * i + 1] << 16);
+  }
+  // slot e from the element at p + e * stride (bytes): a column segment of a row-major tile
+  __device__ __forceinline__ void load_col8(const char* p, int stride) {
+    uint16_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = *(const uint16_t*)(p + e * stride);
+    from_raw(v);
+  }
   // slots 0..7 from 8 consecutive elements at p (16-byte aligned)
   __device__ __forceinline__ void load8(const void* p) {
     uint4 v = *(const uint4*)p;
@@ -110,6 +127,14 @@ struct Frag<float> {
   __device__ __forceinline__ void zero() {
 #pragma unroll
     for (int e = 0; e < 8; ++e) w[e] = 0.f;
+  }
+  __device__ __forceinline__ void scale(const float (&s)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] *= s[e];
+  }
+  __device__ __forceinline__ void load_col8(const char* p, int stride) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] = *(const float*)(p + e * stride);
   }
   __device__ __forceinline__ void load8(const void* p) {
     float4 a = ((const float4*)p)[0], b = ((const float4*)p)[1];

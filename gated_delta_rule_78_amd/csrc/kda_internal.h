@@ -23,6 +23,7 @@ struct ChunkArgs {
   int B, T, H, dk, dv;
   bool bf16;
   void* stream;
+  int vt_override;  // value-tile width (64 / 128) chosen by the caller; 0 = heuristic
 };
 
 hipError_t launch_decode(const DecodeArgs& a);
