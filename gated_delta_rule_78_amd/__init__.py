@@ -14,7 +14,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["chunk_fwd", "chunk_fwd_debug", "decode_step", "lib", "version", "status_string",
+__all__ = ["chunk_fwd", "chunk_fwd_debug", "decode_step", "workspace_size", "pick_path", "lib", "version",
+           "status_string",
            "LIB_PATH", "KdaError", "Shape", "BF16", "F32"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -48,6 +49,10 @@ def lib() -> ctypes.CDLL:
         L.kda_chunk_fwd.restype = ctypes.c_int
         L.kda_chunk_fwd_debug.argtypes = [SP, P, P, P, P, P, P, P, P, P, P]
         L.kda_chunk_fwd_debug.restype = ctypes.c_int
+        L.kda_chunk_fwd_ws.argtypes = [SP, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.kda_chunk_fwd_ws.restype = ctypes.c_int
+        L.kda_chunk_fwd_workspace_size.argtypes = [SP]
+        L.kda_chunk_fwd_workspace_size.restype = ctypes.c_size_t
         L.kda_decode_step.argtypes = [SP, P, P, P, P, P, P, P, P]
         L.kda_decode_step.restype = ctypes.c_int
         L.kda_status_string.argtypes = [ctypes.c_int]
@@ -99,7 +104,21 @@ def _stream(dev):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
-def _chunk_call(debug, q, k, v, alpha, beta, initial_state, out, final_state, want_final):
+def workspace_size(B, T, H, dk, dv, dtype="bf16") -> int:
+    """Bytes of device workspace the two-pass chunk forward needs for this shape."""
+    shape = Shape(B, T, H, dk, dv, 64, BF16 if dtype == "bf16" else F32)
+    return int(lib().kda_chunk_fwd_workspace_size(ctypes.byref(shape)))
+
+
+def pick_path(B, T, H, dk, dv):
+    """The faster chunk-forward path for a shape on MI355X (measured): the two-pass
+    path once the single-pass kernel has too few (b, h, value-tile) workgroups to
+    hide its per-chunk latency; the fused single pass otherwise."""
+    return "twopass" if B * H * max(1, dv // 64) < 512 and T > 64 else "fused"
+
+
+def _chunk_call(debug, q, k, v, alpha, beta, initial_state, out, final_state, want_final, path="fused",
+                workspace=None):
     torch = _torch()
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -123,6 +142,21 @@ def _chunk_call(debug, q, k, v, alpha, beta, initial_state, out, final_state, wa
     args = [ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state),
             _ptr(out), _ptr(final_state)]
     dbg = None
+    if path == "auto":
+        path = pick_path(B, T, H, dk, dv)
+    if path == "twopass" and not debug:
+        need = int(lib().kda_chunk_fwd_workspace_size(ctypes.byref(shape)))
+        if workspace is None:
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        if workspace.numel() * workspace.element_size() < need:
+            raise ValueError(f"workspace needs {need} bytes")
+        _check((workspace,), ("workspace",), dev)
+        rc = lib().kda_chunk_fwd_ws(*args, _ptr(workspace), ctypes.c_size_t(need), _stream(dev))
+        if rc != 0:
+            raise KdaError(rc, "kda_chunk_fwd_ws")
+        return out, final_state, None
+    if path not in ("fused", "twopass"):
+        raise ValueError(f"unknown path {path!r}")
     if debug:
         nch = (T + 63) // 64
         dbg = torch.zeros((B * H, nch, 4, 64, 64), dtype=torch.float32, device=dev)
@@ -134,11 +168,16 @@ def _chunk_call(debug, q, k, v, alpha, beta, initial_state, out, final_state, wa
     return out, final_state, dbg
 
 
-def chunk_fwd(q, k, v, alpha, beta, initial_state=None, out=None, final_state=None, want_final=True):
+def chunk_fwd(q, k, v, alpha, beta, initial_state=None, out=None, final_state=None, want_final=True,
+              path="auto", workspace=None):
     """Chunkwise WY forward.  q, k, alpha [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H]
     (all bf16 or all fp32, contiguous, on one GPU); initial_state fp32 [B,H,dk,dv]
-    or None.  Returns (o [B,T,H,dv], final_state fp32 [B,H,dk,dv] or None)."""
-    o, s, _ = _chunk_call(False, q, k, v, alpha, beta, initial_state, out, final_state, want_final)
+    or None.  path: "fused" (single pass), "twopass" (parallel per-chunk records in a
+    workspace, then the state pass) or "auto".  workspace: optional uint8 device
+    tensor of at least workspace_size(...) bytes for the two-pass path (allocated
+    here when omitted).  Returns (o [B,T,H,dv], final_state fp32 [B,H,dk,dv] or None)."""
+    o, s, _ = _chunk_call(False, q, k, v, alpha, beta, initial_state, out, final_state, want_final, path,
+                          workspace)
     return o, s
 
 

@@ -65,15 +65,30 @@ const char* kda_status_string(int status) {
     case KDA_ERR_ALIAS: return "an output overlaps an input it must not alias";
     case KDA_ERR_UNSUPPORTED: return "unsupported configuration (dk/dv, chunk or dtype)";
     case KDA_ERR_HIP: return "HIP runtime error on launch";
+    case KDA_ERR_WORKSPACE: return "workspace smaller than kda_chunk_fwd_workspace_size()";
     default: return "unknown status";
   }
 }
 
 int kda_version(void) { return kVersion; }
 
+// KDA_PREP_CPW=n pins the chunks per workgroup of the two-pass first pass (tuning aid).
+int prep_cpw_override() {
+  static const int v = [] {
+    const char* e = getenv("KDA_PREP_CPW");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
+}
+
+size_t workspace_bytes_for(const kda_shape& s) {
+  const size_t nchunks = ((size_t)s.T + 63) / 64;
+  return (size_t)s.B * s.H * nchunks * kda::record_bytes(s.dtype == KDA_BF16, s.dk);
+}
+
 static int chunk_fwd_impl(const kda_shape* shape, const void* q, const void* k, const void* v,
                           const void* alpha, const void* beta, const float* s0, void* o, float* sT,
-                          float* dbg, void* stream) {
+                          float* dbg, void* ws, size_t ws_bytes, void* stream) {
   int es = 0;
   int rc = check_shape(shape, false, &es);
   if (rc) return rc;
@@ -102,20 +117,51 @@ static int chunk_fwd_impl(const kda_shape* shape, const void* q, const void* k, 
   }
   kda::ChunkArgs a{q, k, v, alpha, beta, s0, o, sT, dbg, s.B, s.T, s.H, s.dk, s.dv,
                    s.dtype == KDA_BF16, stream, value_tile_override()};
-  return kda::launch_chunk(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  if (!ws) return kda::launch_chunk(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  // two-pass path: the workspace holds one record per (b, h, chunk)
+  const size_t need = workspace_bytes_for(s);
+  if (ws_bytes < need) return KDA_ERR_WORKSPACE;
+  if (((uintptr_t)ws & 255u) != 0) return KDA_ERR_ALIGN;
+  const Range rw = range_of(ws, (int64_t)need);
+  for (const Range& r : in)
+    if (overlap(rw, r)) return KDA_ERR_ALIAS;
+  if (overlap(rw, ro) || (sT && overlap(rw, range_of(sT, st_bytes)))) return KDA_ERR_ALIAS;
+  if (rows == 0) return kda::launch_state(a, ws) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  const int64_t nchunks = ((int64_t)s.T + 63) / 64;
+  const int64_t total = (int64_t)s.B * s.H * nchunks;
+  int cpw = prep_cpw_override();
+  if (cpw <= 0) cpw = (int)((total + 1535) / 1536);  // aim at ~1.5K workgroups (6 per CU)
+  if (cpw < 1) cpw = 1;
+  if (cpw > nchunks) cpw = (int)nchunks;
+  if (kda::launch_prep(a, ws, cpw) != hipSuccess) return KDA_ERR_HIP;
+  return kda::launch_state(a, ws) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 int kda_chunk_fwd(const kda_shape* shape, const void* q, const void* k, const void* v,
                   const void* alpha, const void* beta, const float* initial_state, void* o,
                   float* final_state, void* stream) {
-  return chunk_fwd_impl(shape, q, k, v, alpha, beta, initial_state, o, final_state, nullptr, stream);
+  return chunk_fwd_impl(shape, q, k, v, alpha, beta, initial_state, o, final_state, nullptr, nullptr, 0, stream);
+}
+
+size_t kda_chunk_fwd_workspace_size(const kda_shape* shape) {
+  int es = 0;
+  if (check_shape(shape, false, &es) != KDA_OK) return 0;
+  if (shape->dtype == KDA_F32 && (shape->dk != 64 || shape->dv != 64)) return 0;
+  return workspace_bytes_for(*shape);
+}
+
+int kda_chunk_fwd_ws(const kda_shape* shape, const void* q, const void* k, const void* v, const void* alpha,
+                     const void* beta, const float* initial_state, void* o, float* final_state, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  return chunk_fwd_impl(shape, q, k, v, alpha, beta, initial_state, o, final_state, nullptr, workspace,
+                        workspace_bytes, stream);
 }
 
 int kda_chunk_fwd_debug(const kda_shape* shape, const void* q, const void* k, const void* v,
                         const void* alpha, const void* beta, const float* initial_state, void* o,
                         float* final_state, float* dbg, void* stream) {
   if (!dbg) return KDA_ERR_NULL;
-  return chunk_fwd_impl(shape, q, k, v, alpha, beta, initial_state, o, final_state, dbg, stream);
+  return chunk_fwd_impl(shape, q, k, v, alpha, beta, initial_state, o, final_state, dbg, nullptr, 0, stream);
 }
 
 int kda_decode_step(const kda_shape* shape, const void* q, const void* k, const void* v,

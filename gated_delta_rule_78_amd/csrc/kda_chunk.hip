@@ -48,6 +48,7 @@
 
 #include "kda_common.h"
 #include "kda_internal.h"
+#include "kda_record.h"
 
 namespace kda {
 
@@ -172,6 +173,12 @@ __device__ __forceinline__ void st_row8<float>(char* p, const float (&v)[8]) {
   ((float4*)p)[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
+// `bytes` (a multiple of 16) from LDS to global memory, 16 bytes per thread and step
+template <int NT>
+__device__ __forceinline__ void copy_flat(char* dst, const char* src, int bytes, int tid) {
+  for (int j = tid; j < bytes / 16; j += NT) *(uint4*)(dst + j * 16) = *(const uint4*)(src + j * 16);
+}
+
 // value of `x` held by lane `src` (0..15) of this lane's 16-lane DPP row
 template <int src>
 __device__ __forceinline__ float row_bcast(float x) {
@@ -189,11 +196,16 @@ __device__ __forceinline__ void mm4(f32x4_t& acc, const float (&a)[4], const flo
 
 }  // namespace
 
-template <typename T, int DK, int VT>
+// PREP = false: the fused single-pass forward (state in registers, outputs written).
+// PREP = true : the parallel first pass of the two-pass forward: every workgroup takes a
+//               run of `cpw` chunks of one head and writes each chunk's record (-W, Q o gamma,
+//               (K o rho)^T, A~, M~, gamma_last) to `ws` for the state pass.
+template <typename T, int DK, int VT, bool PREP>
 __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
     const void* __restrict__ gq, const void* __restrict__ gk, const void* __restrict__ gv,
     const void* __restrict__ galpha, const void* __restrict__ gbeta, const float* s0,
-    void* __restrict__ go, float* sT, float* __restrict__ dbg, int Tlen, int H, int DV, int BH) {
+    void* __restrict__ go, float* sT, float* __restrict__ dbg, int Tlen, int H, int DV, int BH,
+    char* __restrict__ ws, int cpw) {
   using K = Cfg<T, DK, VT>;
   using R = Raw<T>;
   constexpr int ES = K::ES;
@@ -215,29 +227,39 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
   const int g = lane >> 4;
   const int n = lane & 15;
   // block -> (head, value tile); a head's tiles land on one XCD when the grid allows it
-  const int NVT = DV / VT;
-  int bh, vt;
+  const int NVT = PREP ? 1 : DV / VT;
+  const int nchunks = (Tlen + C - 1) / C;
+  int bh, vt, c_begin, c_end;
   {
     const int bid = blockIdx.x;
-    if (NVT > 1 && (BH & 7) == 0) {
-      const int r = bid >> 3;
-      vt = r % NVT;
-      bh = (r / NVT) * 8 + (bid & 7);
+    if (PREP) {
+      const int nseg = (nchunks + cpw - 1) / cpw;
+      bh = bid / nseg;
+      vt = 0;
+      c_begin = (bid % nseg) * cpw;
+      c_end = min(nchunks, c_begin + cpw);
     } else {
-      bh = bid / NVT;
-      vt = bid % NVT;
+      if (NVT > 1 && (BH & 7) == 0) {
+        const int r = bid >> 3;
+        vt = r % NVT;
+        bh = (r / NVT) * 8 + (bid & 7);
+      } else {
+        bh = bid / NVT;
+        vt = bid % NVT;
+      }
+      c_begin = 0;
+      c_end = nchunks;
     }
   }
   const int b = bh / H, h = bh % H;
   const int v0 = vt * VT;
-  const int nchunks = (Tlen + C - 1) / C;
   auto row_base = [&](int t) -> size_t { return ((size_t)b * Tlen + t) * H + h; };
 
   // ---------------- state tiles: rows 16 r + 4 g + e (key channels), column v0 + 16 wave + n
   f32x4_t S[DK / 16];
 #pragma unroll
   for (int r = 0; r < DK / 16; ++r) S[r] = zero4();
-  if (s0) {
+  if (!PREP && s0) {
 #pragma unroll
     for (int r = 0; r < DK / 16; ++r)
 #pragma unroll
@@ -275,9 +297,9 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
                               (size_t)c16 * 16);
     }
   };
-  if (nchunks > 0) {
-    issue_qka(0);
-    issue_v(0);
+  if (c_begin < c_end) {
+    issue_qka(c_begin);
+    if (!PREP) issue_v(c_begin);
   }
 
   // gate-pass item: (block iI, channels 2 icp, 2 icp + 1); roles 0 / 1 split the passes
@@ -290,7 +312,7 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
   const int icp = item % (DK / 2);
   const int item_off = (SUB * iI) * K::RS_DK + 2 * icp * ES;
 
-  for (int chunk = 0; chunk < nchunks; ++chunk) {
+  for (int chunk = c_begin; chunk < c_end; ++chunk) {
     const int t0 = chunk * C;
     const int nv = min(C, Tlen - t0);
     // ================= phase 0: staged inputs -> LDS (padded rows: q = k = 0, alpha = 1, beta = 0)
@@ -308,7 +330,7 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
     }
     if (tid < C) BETA[tid] = (t0 + tid < Tlen) ? __uint_as_float(ES == 2 ? pb << 16 : pb) : 0.f;
     __syncthreads();
-    if (chunk + 1 < nchunks) issue_qka(chunk + 1);
+    if (chunk + 1 < c_end) issue_qka(chunk + 1);
 
     const char* const Qs = R_IN;
     const char* const Ks = R_IN + C * K::RS_DK;
@@ -651,16 +673,19 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
       st_row8<T>(AT + (16 * kUpI[t] + i) * K::RS_C + (16 * kUpJ[t] + j0) * ES, z8);
     }
     // v tile of this chunk -> LDS, then prefetch the next chunk's
+    if (!PREP) {
 #pragma unroll
-    for (int i = 0; i < K::VPT_V; ++i) {
-      const int j = tid + NT * i;
-      const int row = j / K::VROW_V, c16 = j % K::VROW_V;
-      *(uint4*)(R_IN + K::OFF_VV + row * K::RS_VT + c16 * 16) = (t0 + row < Tlen) ? pv[i] : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < K::VPT_V; ++i) {
+        const int j = tid + NT * i;
+        const int row = j / K::VROW_V, c16 = j % K::VROW_V;
+        *(uint4*)(R_IN + K::OFF_VV + row * K::RS_VT + c16 * 16) =
+            (t0 + row < Tlen) ? pv[i] : make_uint4(0, 0, 0, 0);
+      }
+      if (chunk + 1 < c_end) issue_v(chunk + 1);
     }
-    if (chunk + 1 < nchunks) issue_v(chunk + 1);
     __syncthreads();
 
-    if (dbg && vt == 0) {
+    if (!PREP && dbg && vt == 0) {
       float* Dp = dbg + ((size_t)bh * nchunks + chunk) * 4 * C * C;
       for (int x = tid; x < C * C; x += NT) {
         const int i = x / C, j = x % C;
@@ -690,7 +715,7 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
         for (int ks = 0; ks < K::KS; ++ks) mma(Ot[I], fq[ks], bs[ks]);
       }
     };
-    if (wave != 0) q_times_S();
+    if (!PREP && wave != 0) q_times_S();
 
     // ================= phase I: M = (I + T)^-1 with T = diag(beta) D
     float* MM = (float*)(R_IN + K::OFF_MM);
@@ -808,7 +833,7 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
       }
     }
     __syncthreads();
-    if (wave == 0) q_times_S();  // wave 0's share, in the stage where it is otherwise idle
+    if (!PREP && wave == 0) q_times_S();  // wave 0's share, in the stage where it is otherwise idle
     if (wave == 3) {  // M20 = -N22 (P20 + T21 M10)
       float a[4], bb[4];
       a_T(2, 1, a);
@@ -839,7 +864,7 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
         if (j0 + e > i) v8[e] = 0.f;
       st_row8<T>(MT + i * K::RS_C + j0 * ES, v8);
     }
-    if (dbg && vt == 0) {
+    if (!PREP && dbg && vt == 0) {
       float* Dp = dbg + ((size_t)bh * nchunks + chunk) * 4 * C * C + 2 * C * C;
       for (int x = tid; x < C * C; x += NT) {
         const int i = x / C, j = x % C;
@@ -876,26 +901,42 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             st_elem(WW + (16 * I + 4 * g + e) * K::RS_DK + (16 * cn + n) * ES, -acc[e], ES);
-          if (dbg && vt == 0 && cn < 4) {
+          if (!PREP && dbg && vt == 0 && cn < 4) {
             float* Dp = dbg + ((size_t)bh * nchunks + chunk) * 4 * C * C + 3 * C * C;
 #pragma unroll
             for (int e = 0; e < 4; ++e) Dp[(16 * I + 4 * g + e) * C + 16 * cn + n] = acc[e];
           }
         }
       }
-      // U for this wave's value columns
-      Frag<T> bv[2];
+      if constexpr (!PREP) {
+        // U for this wave's value columns
+        Frag<T> bv[2];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        bv[ks].load_col8(R_IN + K::OFF_VV + (32 * ks + 8 * g) * K::RS_VT + (16 * wave + n) * ES, K::RS_VT);
+        for (int ks = 0; ks < 2; ++ks)
+          bv[ks].load_col8(R_IN + K::OFF_VV + (32 * ks + 8 * g) * K::RS_VT + (16 * wave + n) * ES, K::RS_VT);
 #pragma unroll
-      for (int I = 0; I < NB; ++I) {
-        Dl[I] = zero4();
-        mma(Dl[I], am[I][0], bv[0]);
-        if (I >= 2) mma(Dl[I], am[I][1], bv[1]);
+        for (int I = 0; I < NB; ++I) {
+          Dl[I] = zero4();
+          mma(Dl[I], am[I][0], bv[0]);
+          if (I >= 2) mma(Dl[I], am[I][1], bv[1]);
+        }
       }
     }
     __syncthreads();
+    if constexpr (PREP) {
+      // the chunk's record for the state pass: -W, Q o gamma, (K o rho)^T, A~, M~, gamma_last
+      // (the LDS tiles are copied whole, padded rows and all: the record is their image)
+      using RL = RecordLayout<T, DK>;
+      static_assert(RL::RS_DK == K::RS_DK && RL::RS_C == K::RS_C, "record rows match the LDS tiles");
+      char* rec = ws + ((size_t)bh * nchunks + chunk) * RL::BYTES;
+      copy_flat<NT>(rec + RL::WW, WW, RL::QG - RL::WW, tid);
+      copy_flat<NT>(rec + RL::QG, R_OP + K::OFF_QG, RL::KRT - RL::QG, tid);
+      copy_flat<NT>(rec + RL::KRT, R_OP + K::OFF_KRT, RL::AT - RL::KRT, tid);
+      copy_flat<NT>(rec + RL::AT, AT, RL::MT - RL::AT, tid);
+      copy_flat<NT>(rec + RL::MT, MT, RL::GC - RL::MT, tid);
+      copy_flat<NT>(rec + RL::GC, (const char*)GC, RL::IMG - RL::GC, tid);
+      continue;
+    }
 
     // ================= phase S: Delta = U - W S ; O = (Q o gamma) S + A Delta ; S update
     {
@@ -964,7 +1005,7 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
     }
   }
 
-  if (sT) {
+  if (!PREP && sT) {
 #pragma unroll
     for (int r = 0; r < DK / 16; ++r)
 #pragma unroll
@@ -976,7 +1017,7 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
 template <typename T, int DK, int VT>
 static hipError_t launch_chunk_t(const ChunkArgs& a) {
   using K = Cfg<T, DK, VT>;
-  auto kern = chunk_fwd_kernel<T, DK, VT>;
+  auto kern = chunk_fwd_kernel<T, DK, VT, false>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, K::LDS);
@@ -985,7 +1026,7 @@ static hipError_t launch_chunk_t(const ChunkArgs& a) {
   }
   const int BH = a.B * a.H;
   hipLaunchKernelGGL(kern, dim3(BH * (a.dv / VT)), dim3(K::NT), K::LDS, (hipStream_t)a.stream, a.q, a.k, a.v,
-                     a.alpha, a.beta, a.s0, a.o, a.sT, a.dbg, a.T, a.H, a.dv, BH);
+                     a.alpha, a.beta, a.s0, a.o, a.sT, a.dbg, a.T, a.H, a.dv, BH, (char*)nullptr, 0);
   return hipGetLastError();
 }
 
@@ -1007,6 +1048,37 @@ hipError_t launch_chunk(const ChunkArgs& a) {
   }
   if (a.dk == 64) return vt == 64 ? launch_chunk_t<bf16_t, 64, 64>(a) : launch_chunk_t<bf16_t, 64, 128>(a);
   return vt == 64 ? launch_chunk_t<bf16_t, 128, 64>(a) : launch_chunk_t<bf16_t, 128, 128>(a);
+}
+
+// ---------------------------------------------------------------------------
+// Two-pass forward, first pass: records of every chunk of every head, in parallel.
+template <typename T, int DK>
+static hipError_t launch_prep_t(const ChunkArgs& a, char* ws, int cpw) {
+  using K = Cfg<T, DK, 64>;
+  auto kern = chunk_fwd_kernel<T, DK, 64, true>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, K::LDS);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int BH = a.B * a.H;
+  const int nchunks = (a.T + C - 1) / C;
+  const int nseg = (nchunks + cpw - 1) / cpw;
+  if ((long)BH * nseg == 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3(BH * nseg), dim3(K::NT), K::LDS, (hipStream_t)a.stream, a.q, a.k, a.v, a.alpha,
+                     a.beta, a.s0, a.o, a.sT, (float*)nullptr, a.T, a.H, a.dv, BH, ws, cpw);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep(const ChunkArgs& a, void* ws, int cpw) {
+  if (!a.bf16) return a.dk == 64 ? launch_prep_t<float, 64>(a, (char*)ws, cpw) : hipErrorInvalidValue;
+  return a.dk == 64 ? launch_prep_t<bf16_t, 64>(a, (char*)ws, cpw) : launch_prep_t<bf16_t, 128>(a, (char*)ws, cpw);
+}
+
+size_t record_bytes(bool bf16, int dk) {
+  if (!bf16) return RecordLayout<float, 64>::BYTES;
+  return dk == 64 ? RecordLayout<bf16_t, 64>::BYTES : RecordLayout<bf16_t, 128>::BYTES;
 }
 
 }  // namespace kda

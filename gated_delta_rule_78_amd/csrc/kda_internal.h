@@ -28,5 +28,9 @@ struct ChunkArgs {
 
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_chunk(const ChunkArgs& a);
+// two-pass forward: per-chunk records into ws (cpw chunks per workgroup), then the state pass
+hipError_t launch_prep(const ChunkArgs& a, void* ws, int cpw);
+hipError_t launch_state(const ChunkArgs& a, const void* ws);
+size_t record_bytes(bool bf16, int dk);
 
 }  // namespace kda

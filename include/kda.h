@@ -81,7 +81,8 @@ typedef enum {
     KDA_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
     KDA_ERR_ALIAS = -5,       /* the output overlaps an input it must not alias */
     KDA_ERR_UNSUPPORTED = -6, /* valid but unsupported (dk/dv, chunk, dtype x dk) */
-    KDA_ERR_HIP = -7          /* the HIP runtime reported an error on launch */
+    KDA_ERR_HIP = -7,         /* the HIP runtime reported an error on launch */
+    KDA_ERR_WORKSPACE = -8    /* workspace smaller than kda_chunk_fwd_workspace_size() */
 } kda_status;
 
 /*
@@ -99,6 +100,27 @@ typedef enum {
 int kda_chunk_fwd(const kda_shape* shape, const void* q, const void* k, const void* v,
                   const void* alpha, const void* beta, const float* initial_state,
                   void* o, float* final_state, void* stream);
+
+/*
+ * Two-pass chunk forward.  Same operation, arguments and errors as kda_chunk_fwd,
+ * plus a caller-owned device workspace:
+ *   pass 1 computes, for every (b, h, chunk) in parallel, the chunk's WY record
+ *          (-W, Q o gamma, (K o rho)^T, A, (I + T)^-1 diag(beta), gamma of the last
+ *          row: the data of the chunk's affine block transfer) into the workspace;
+ *   pass 2 walks the chunks of each (b, h) in order and carries the fp32 state.
+ * This trades extra HBM traffic (each record is written once and read once) for
+ * parallelism over chunks, which pays off when B*H is small and T is long.
+ *   workspace       : device memory, 256-byte aligned, not overlapping any argument;
+ *                     NULL selects the single-pass kernel (same as kda_chunk_fwd).
+ *   workspace_bytes : at least kda_chunk_fwd_workspace_size(shape), else
+ *                     KDA_ERR_WORKSPACE.
+ * The workspace contents on return are unspecified.
+ */
+size_t kda_chunk_fwd_workspace_size(const kda_shape* shape);  /* 0 if the shape is invalid */
+int kda_chunk_fwd_ws(const kda_shape* shape, const void* q, const void* k, const void* v,
+                     const void* alpha, const void* beta, const float* initial_state,
+                     void* o, float* final_state, void* workspace, size_t workspace_bytes,
+                     void* stream);
 
 /*
  * One recurrent decode step for every (b, h), state updated in place:

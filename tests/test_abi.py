@@ -12,7 +12,7 @@ import gated_delta_rule_78_amd as kda
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
 
-OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, UNSUP = 0, -1, -2, -3, -4, -5, -6
+OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, UNSUP, WORKSPACE = 0, -1, -2, -3, -4, -5, -6, -8
 
 
 def _declared():
@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(L):
 
 def test_version_and_status_strings(L):
     assert kda.version() == 100
-    for st in range(-7, 1):
+    for st in range(-8, 1):
         assert kda.status_string(st) and kda.status_string(st) != "unknown status"
     assert kda.status_string(-99) == "unknown status"
 
@@ -93,6 +93,36 @@ def test_chunk_argument_errors(L):
     assert _chunk(L, s0=_p(7), sT=_p(7, off=16)) == ALIAS  # partial overlap is not allowed
     assert _chunk(L, sT=_p(1)) == ALIAS
     assert _chunk(L, sT=_p(5)) == ALIAS                 # final state over the output
+
+
+def _chunk_ws(L, ws, ws_bytes, B=1, T=64, H=2, dk=64, dv=64, dtype=0):
+    shape = kda.Shape(B, T, H, dk, dv, 64, dtype)
+    p = [_p(i) for i in range(6)]
+    return L.kda_chunk_fwd_ws(ctypes.byref(shape), p[0], p[1], p[2], p[3], p[4], None, p[5], None, ws,
+                              ctypes.c_size_t(ws_bytes), None)
+
+
+def test_workspace_size_and_errors(L):
+    def size(B, T, H, dk, dv, dtype=0):
+        return L.kda_chunk_fwd_workspace_size(ctypes.byref(kda.Shape(B, T, H, dk, dv, 64, dtype)))
+    # one fixed-size record per (b, h, chunk), a multiple of 256 bytes
+    one = size(1, 64, 1, 128, 128)
+    assert one > 0 and one % 256 == 0
+    assert size(4, 8192, 32, 128, 128) == 4 * 32 * 128 * one
+    assert size(1, 65, 1, 128, 128) == 2 * one
+    assert size(1, 64, 1, 128, 64) == one            # the record does not depend on dv
+    assert size(1, 64, 1, 64, 64) < one
+    assert size(1, 64, 1, 64, 64, dtype=1) > size(1, 64, 1, 64, 64)
+    assert size(1, 0, 3, 128, 128) == 0
+    assert size(1, 64, 1, 96, 128) == 0               # unsupported shape
+    assert size(1, 64, 1, 128, 128, dtype=1) == 0
+    assert L.kda_chunk_fwd_workspace_size(None) == 0
+    need = size(1, 64, 2, 64, 64)
+    assert _chunk_ws(L, _p(9), need - 1) == WORKSPACE
+    assert _chunk_ws(L, _p(9, off=128), need) == ALIGN
+    assert _chunk_ws(L, _p(0, off=256), need) == ALIAS     # workspace over q
+    assert _chunk_ws(L, _p(5), need) == ALIAS               # workspace over o
+    assert _chunk_ws(L, _p(9), need, dk=96) == UNSUP
 
 
 def test_decode_argument_errors(L):

@@ -14,25 +14,28 @@ from kda_testutil import TOL, heads_of, inputs_to_dev, rel_err_slices, state_to_
 pytestmark = pytest.mark.gpu
 
 
-def _gpu(inp, S0=None, in_place=False):
+PATHS = ["fused", "twopass"]
+
+
+def _gpu(inp, S0=None, in_place=False, path="fused"):
     import gated_delta_rule_78_amd as kda
     import torch
     q, k, v, a, b = inputs_to_dev(inp)
     s0 = None if S0 is None else state_to_dev(S0)
     if in_place:
-        o, sT = kda.chunk_fwd(q, k, v, a, b, initial_state=s0, final_state=s0)
+        o, sT = kda.chunk_fwd(q, k, v, a, b, initial_state=s0, final_state=s0, path=path)
         assert sT.data_ptr() == s0.data_ptr()
     else:
-        o, sT = kda.chunk_fwd(q, k, v, a, b, initial_state=s0)
+        o, sT = kda.chunk_fwd(q, k, v, a, b, initial_state=s0, path=path)
     torch.cuda.synchronize()
     return o.float().cpu().numpy(), sT.cpu().numpy()
 
 
-def _check(inp, S0, heads=None, tol=None, in_place=False, label=""):
+def _check(inp, S0, heads=None, tol=None, in_place=False, label="", path="fused"):
     m = inp.meta
     B, T, H, dk, dv = m["B"], m["T"], m["H"], m["dk"], m["dv"]
-    print(f"chunk {label} B={B} T={T} H={H} dk={dk} dv={dv} {inp.dtype}", flush=True)
-    o_gpu, s_gpu = _gpu(inp, S0, in_place)
+    print(f"chunk {label} [{path}] B={B} T={T} H={H} dk={dk} dv={dv} {inp.dtype}", flush=True)
+    o_gpu, s_gpu = _gpu(inp, S0, in_place, path)
     sel = list(range(B * H)) if heads is None else list(heads)
     s0_ref = None if S0 is None else S0.reshape(B * H, dk, dv)[sel]
     o_ref, s_ref = oracle.fwd(inp.q, inp.k, inp.v, inp.alpha, inp.beta, S0=s0_ref, heads=sel,
@@ -46,28 +49,32 @@ def _check(inp, S0, heads=None, tol=None, in_place=False, label=""):
     return eo, es
 
 
-def test_tiny_fp32_kda():
+@pytest.mark.parametrize("path", PATHS)
+def test_tiny_fp32_kda(path):
     """fp32 inputs, B=1 H=2 T=256 d=64, zero start state: gate 1e-4."""
     inp = make_workload("kda_tiny_f32")
-    _check(inp, None, label="tiny-f32")
+    _check(inp, None, label="tiny-f32", path=path)
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("gates", ["kda", "ckda"])
 @pytest.mark.parametrize("T", [1, 63, 64, 65, 200, 257])
-def test_bf16_lengths(gates, T):
+def test_bf16_lengths(gates, T, path):
     inp = make(1, T, 2, 128, 128, "bf16", gates, False, seed=100 + T)
-    _check(inp, inp.S0, label=f"{gates}-T{T}")
+    _check(inp, inp.S0, label=f"{gates}-T{T}", path=path)
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64)])
-def test_bf16_head_widths(dk, dv):
+def test_bf16_head_widths(dk, dv, path):
     inp = make(2, 150, 3, dk, dv, "bf16", "ckda", False, seed=7 + dk + dv)
-    _check(inp, inp.S0, label=f"d{dk}x{dv}")
+    _check(inp, inp.S0, label=f"d{dk}x{dv}", path=path)
 
 
-def test_fp32_ckda_edges():
+@pytest.mark.parametrize("path", PATHS)
+def test_fp32_ckda_edges(path):
     inp = make(1, 192, 2, 64, 64, "f32", "ckda", False, seed=9)
-    _check(inp, inp.S0, label="f32-ckda")
+    _check(inp, inp.S0, label="f32-ckda", path=path)
 
 
 def test_gates_only_signs_and_zeros():
@@ -102,10 +109,20 @@ def test_zero_gate_resets_history():
     np.testing.assert_array_equal(s1, s2)
 
 
-def test_zero_start_state_and_in_place_final_state():
+@pytest.mark.parametrize("path", PATHS)
+def test_zero_start_state_and_in_place_final_state(path):
     inp = make(2, 130, 2, 128, 128, "bf16", "ckda", False, seed=14)
-    _check(inp, None, label="s0-none")
-    _check(inp, inp.S0, in_place=True, label="in-place")
+    _check(inp, None, label="s0-none", path=path)
+    _check(inp, inp.S0, in_place=True, label="in-place", path=path)
+
+
+def test_two_pass_agrees_with_single_pass():
+    """Both paths compute the same chunk algebra; their outputs agree to bf16 rounding."""
+    inp = make(2, 300, 4, 128, 128, "bf16", "ckda", False, seed=41)
+    o1, s1 = _gpu(inp, inp.S0, path="fused")
+    o2, s2 = _gpu(inp, inp.S0, path="twopass")
+    assert rel_err_slices(o1.transpose(0, 2, 1, 3).reshape(8, -1), o2.transpose(0, 2, 1, 3).reshape(8, -1), 8) < 1e-2
+    assert rel_err_slices(s1.reshape(8, -1), s2.reshape(8, -1), 8) < 1e-2
 
 
 def test_split_invariance_on_gpu():
@@ -178,16 +195,21 @@ def _full(name, nheads, seed=0):
     return w, heads
 
 
-def test_full_kda_prefill_8k_sampled():
+@pytest.mark.parametrize("path", PATHS)
+def test_full_kda_prefill_8k_sampled(path):
     inp, heads = _full("kda_prefill_8k", 6)
-    _check(inp, inp.S0, heads=heads, label="kda-8k")
+    _check(inp, inp.S0, heads=heads, label="kda-8k", path=path)
 
 
-def test_full_ckda_prefill_8k_sampled():
+@pytest.mark.parametrize("path", PATHS)
+def test_full_ckda_prefill_8k_sampled(path):
     inp, heads = _full("ckda_prefill_8k", 6, seed=1)
-    _check(inp, inp.S0, heads=heads, label="ckda-8k")
+    _check(inp, inp.S0, heads=heads, label="ckda-8k", path=path)
 
 
 def test_full_ckda_prefill_128k_sampled():
+    """The long-context workload, through the path chunk_fwd picks for it (two-pass)."""
+    import gated_delta_rule_78_amd as kda
     inp, heads = _full("ckda_prefill_128k", 1, seed=2)
-    _check(inp, inp.S0, heads=heads[:2], label="ckda-128k")
+    m = inp.meta
+    _check(inp, inp.S0, heads=heads[:2], label="ckda-128k", path=kda.pick_path(m["B"], m["T"], m["H"], 128, 128))
