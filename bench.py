@@ -1,19 +1,24 @@
 #!/usr/bin/env python3
 """Benchmark of the KDA / CKDA hot path on one MI355X.
 
-One "step" is one chunkwise WY forward (kda_chunk_fwd) over the prefill batch
-B=4, H=32, T=8192, d_k=d_v=128, bf16 inputs, fp32 state (the KDA workload,
-seeded synthetic inputs already resident in HBM).  ``value`` is whole-job
-prefill throughput in tokens/s (a token is one position across all H heads).
-The same run also measures, outside the timed steps:
+One "step" is one chunkwise WY forward over the prefill batch B=4, H=32,
+T=8192, d_k=d_v=128, bf16 inputs, fp32 state (the KDA workload, seeded
+synthetic inputs already resident in HBM), through the path the library picks
+for the shape (``pick_path``: the two-pass forward here, i.e. kda_chunk_records
+then kda_chunk_apply_records on a preallocated workspace).  ``value`` is
+whole-job prefill throughput in tokens/s (a token is one position across all H
+heads).  The same run also measures, outside the timed steps:
   * the CKDA prefill (same shape, gates in [-1, 1] and beta in [0, 2]);
+  * the long-context CKDA prefill (B=1, H=16, T=131072);
   * the batched decode step (B=256, H=32, d=128, 64 consecutive steps on a
     512 MiB fp32 state), reported as state GB/s against the HBM peak;
   * the fp64 CPU oracle on a bounded sample of the prefill workload.
 
 Prints ONE JSON line.  Timing: W untimed warm-up steps, then exactly K steps
-between synchronisations, with HIP events recorded on the stream the kernel
-is launched on (torch's current stream, which the binding launches on).
+between synchronisations, with HIP events recorded on the stream the kernels
+are launched on (torch's current stream, which the binding passes to the
+library); an event between the two launches of a step gives each kernel's own
+average duration for the roofline entry.
 """
 from __future__ import annotations
 
@@ -32,8 +37,18 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix cores
-PMC_FILE = os.path.join(ROOT, "profiles", "chunk_fwd_kda_prefill_8k_counters.md")
-KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_78_amd", "csrc", "kda_chunk.hip")
+CSRC = os.path.join(ROOT, "gated_delta_rule_78_amd", "csrc")
+# the rocprofv3 counter summary of each kernel, and the sources that kernel is built from
+PMC_FILES = {
+    "chunk_records": (os.path.join(ROOT, "profiles", "chunk_records_kda_prefill_8k_counters.md"),
+                      ["kda_chunk.hip", "kda_record.h", "kda_common.h"]),
+    "chunk_state": (os.path.join(ROOT, "profiles", "chunk_state_kda_prefill_8k_counters.md"),
+                    ["kda_state.hip", "kda_record.h", "kda_common.h"]),
+    "chunk_fused": (os.path.join(ROOT, "profiles", "chunk_fused_kda_prefill_8k_counters.md"),
+                    ["kda_chunk.hip", "kda_common.h"]),
+}
+RECORD_PAYLOAD = {128: 3 * 64 * 128 * 2 + 2 * 64 * 64 * 2 + 128 * 4,   # -W, QG, KRT, A, M~ (bf16), gamma (fp32)
+                  64: 3 * 64 * 64 * 2 + 2 * 64 * 64 * 2 + 64 * 4}
 
 
 def chunk_bytes(B, T, H, dk, dv, es=2):
@@ -50,24 +65,43 @@ def chunk_flops(B, T, H, dk, dv, C=64):
     return B * T * H * per
 
 
+def records_bytes(B, T, H, dk, es=2):
+    """Algorithmic bytes of one kda_chunk_records launch: q, k, alpha, beta read once,
+    one record per (b, h, chunk) written (its data: the padding of the LDS-image rows
+    is not counted)."""
+    nch = (T + 63) // 64
+    return B * T * H * es * (3 * dk + 1) + B * H * nch * RECORD_PAYLOAD[dk]
+
+
+def state_bytes(B, T, H, dk, dv, es=2):
+    """Algorithmic bytes of one kda_chunk_apply_records launch: every record read once,
+    v read and o written once, start state read and final state written."""
+    nch = (T + 63) // 64
+    return B * H * nch * RECORD_PAYLOAD[dk] + B * T * H * es * 2 * dv + 2 * B * H * dk * dv * 4
+
+
 def decode_bytes(B, H, dk, dv, es=2):
     return 2 * B * H * dk * dv * 4 + B * H * (es * (3 * dk + dv + 1) + es * dv)
 
 
-def kernel_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
-def stored_traffic():
+def stored_traffic(kernel):
     """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by
-    a copy-kernel calibration), if the counters were taken on the current kernel."""
-    if not os.path.exists(PMC_FILE):
+    a copy-kernel calibration), if the counters were taken on the current sources."""
+    path, files = PMC_FILES[kernel]
+    if not os.path.exists(path):
         return None
-    txt = open(PMC_FILE).read()
+    txt = open(path).read()
     mh = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", txt)
     mt = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
-    if not mh or not mt or mh.group(1) != kernel_hash():
+    if not mh or not mt or mh.group(1) != kernel_hash(files):
         return None
     return float(mt.group(1))
 
@@ -87,7 +121,30 @@ def timed(fn, steps, warmup, stream):
     return e0.elapsed_time(e1) / steps  # ms per step
 
 
+def timed_split(first, second, steps, warmup, stream):
+    """K steps of first(); second(), events around each launch.  Returns (ms per step,
+    mean ms of first, mean ms of second)."""
+    import torch
+    for _ in range(warmup):
+        first()
+        second()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps + 1)]
+    for i in range(steps):
+        ev[2 * i].record(stream)
+        first()
+        ev[2 * i + 1].record(stream)
+        second()
+    ev[2 * steps].record(stream)
+    torch.cuda.synchronize()
+    t1 = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)) / steps
+    t2 = sum(ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(steps)) / steps
+    return ev[0].elapsed_time(ev[2 * steps]) / steps, t1, t2
+
+
 def bench_prefill(name, steps, warmup, log):
+    """Times the chunk forward of workload `name` on the path the library picks.
+    Returns (workload, result dict, host inputs)."""
     import torch
     import gated_delta_rule_78_amd as kda
     from gated_delta_rule_78_amd.inputs import make_workload, WORKLOADS, to_torch
@@ -99,11 +156,31 @@ def bench_prefill(name, steps, warmup, log):
     o = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.bfloat16, device="cuda")
     sT = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
-    ms = timed(lambda: kda.chunk_fwd(q, k, v, a, b, initial_state=s0, out=o, final_state=sT),
-               steps, warmup, stream)
+    path = kda.pick_path(w.B, w.T, w.H, w.dk, w.dv)
+    res = {"path": path}
+    if path == "twopass":
+        ws = torch.empty(kda.workspace_size(w.B, w.T, w.H, w.dk, w.dv), dtype=torch.uint8, device="cuda")
+        ms, t1, t2 = timed_split(lambda: kda.chunk_records(q, k, a, b, workspace=ws, dv=w.dv),
+                                 lambda: kda.chunk_apply_records(ws, v, s0, out=o, final_state=sT, dk=w.dk),
+                                 steps, warmup, stream)
+        res.update(ms=ms, kernels={"chunk_records": t1, "chunk_state": t2},
+                   workspace_bytes=ws.numel())
+        del ws
+    else:
+        ms = timed(lambda: kda.chunk_fwd(q, k, v, a, b, initial_state=s0, out=o, final_state=sT, path="fused"),
+                   steps, warmup, stream)
+        res.update(ms=ms, kernels={"chunk_fused": ms})
     del q, k, v, a, b, s0, o, sT
     torch.cuda.empty_cache()
-    return w, ms, inp
+    return w, res, inp
+
+
+def kernel_bytes(kernel, w):
+    if kernel == "chunk_records":
+        return records_bytes(w.B, w.T, w.H, w.dk)
+    if kernel == "chunk_state":
+        return state_bytes(w.B, w.T, w.H, w.dk, w.dv)
+    return chunk_bytes(w.B, w.T, w.H, w.dk, w.dv)
 
 
 def bench_decode(steps_rep, log):
@@ -196,12 +273,18 @@ def main():
         log("[bench] calibration copy: 1 GiB read, 1 GiB written")
         del src, dst
 
-    w, ms, inp = bench_prefill("kda_prefill_8k", args.steps, args.warmup, log)
+    w, res, inp = bench_prefill("kda_prefill_8k", args.steps, args.warmup, log)
+    ms = res["ms"]
     tokens = w.B * w.T
     value = tokens / (ms * 1e-3)
     nbytes = chunk_bytes(w.B, w.T, w.H, w.dk, w.dv)
-    achieved = nbytes / (ms * 1e-3) / 1e9
+    path_gbs = nbytes / (ms * 1e-3) / 1e9
     flops = chunk_flops(w.B, w.T, w.H, w.dk, w.dv)
+    # roofline of the dominant kernel: its algorithmic bytes over its own mean duration
+    dom = max(res["kernels"], key=res["kernels"].get)
+    dom_ms = res["kernels"][dom]
+    dom_bytes = kernel_bytes(dom, w)
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     out = {
         "metric": "chunk-fwd tokens/s (H=32,d=128,T=8K bf16) + decode state GB/s, % of roofline",
         "value": value,
@@ -217,20 +300,27 @@ def main():
         "data": "synthetic (seeded numpy; q,k L2-normalised N(0,1), v N(0,1), "
                 "alpha=exp(-0.1 softplus(N)), beta=sigmoid(N), S0 N(0,0.02))",
         "config": {"workload": "kda_prefill_8k", "B": w.B, "T": w.T, "H": w.H, "dk": w.dk, "dv": w.dv,
-                   "chunk": 64, "state": "fp32", "tokens_per_step": tokens},
+                   "chunk": 64, "state": "fp32", "tokens_per_step": tokens, "path": res["path"]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": stored_traffic(),
-                     "kernel": "chunk_fwd_kernel<bf16,128,128>", "algorithmic_bytes_per_launch": nbytes,
-                     "mfma_tflops_algorithmic": flops / (ms * 1e-3) / 1e12,
-                     "mfma_frac_algorithmic": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": stored_traffic(dom),
+                     "kernel": dom, "kernel_ms": dom_ms, "algorithmic_bytes_per_launch": dom_bytes,
+                     "kernels_ms": res["kernels"],
+                     "path": {"algorithmic_bytes_per_step": nbytes, "achieved_gbs": path_gbs,
+                              "frac_hbm": path_gbs / HBM_PEAK_GBS,
+                              "mfma_tflops_algorithmic": flops / (ms * 1e-3) / 1e12,
+                              "mfma_frac_algorithmic": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}},
     }
-    log(f"[bench] kda prefill: {ms:.3f} ms/step, {value:.4g} tokens/s, {achieved:.1f} GB/s")
+    log(f"[bench] kda prefill ({res['path']}): {ms:.3f} ms/step, {value:.4g} tokens/s; "
+        + ", ".join(f"{k2} {v2:.3f} ms" for k2, v2 in res["kernels"].items()))
     if not args.no_extras:
-        w3, ms3, _ = bench_prefill("ckda_prefill_8k", args.steps, args.warmup, log)
-        out["ckda_prefill_8k"] = {"value": w3.B * w3.T / (ms3 * 1e-3), "unit": "tokens/s", "ms_per_step": ms3,
-                                  "frac_hbm": chunk_bytes(w3.B, w3.T, w3.H, w3.dk, w3.dv) / (ms3 * 1e-3) / 1e9
-                                  / HBM_PEAK_GBS}
-        log(f"[bench] ckda prefill: {ms3:.3f} ms/step")
+        for name, steps in (("ckda_prefill_8k", args.steps), ("ckda_prefill_128k", max(2, args.steps // 4))):
+            w3, r3, _ = bench_prefill(name, steps, min(args.warmup, 2), log)
+            ms3 = r3["ms"]
+            out[name] = {"value": w3.B * w3.T / (ms3 * 1e-3), "unit": "tokens/s", "ms_per_step": ms3,
+                         "steps": steps, "path": r3["path"], "kernels_ms": r3["kernels"],
+                         "frac_hbm": chunk_bytes(w3.B, w3.T, w3.H, w3.dk, w3.dv) / (ms3 * 1e-3) / 1e9
+                         / HBM_PEAK_GBS}
+            log(f"[bench] {name} ({r3['path']}): {ms3:.3f} ms/step")
         wd, msd = bench_decode(3, log)
         db = decode_bytes(wd.B, wd.H, wd.dk, wd.dv)
         gbs = db / (msd * 1e-3) / 1e9

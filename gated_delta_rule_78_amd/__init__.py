@@ -14,8 +14,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["chunk_fwd", "chunk_fwd_debug", "decode_step", "workspace_size", "pick_path", "lib", "version",
-           "status_string",
+__all__ = ["chunk_fwd", "chunk_records", "chunk_apply_records", "chunk_fwd_debug", "decode_step",
+           "workspace_size", "pick_path", "lib", "version", "status_string",
            "LIB_PATH", "KdaError", "Shape", "BF16", "F32"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -53,6 +53,10 @@ def lib() -> ctypes.CDLL:
         L.kda_chunk_fwd_ws.restype = ctypes.c_int
         L.kda_chunk_fwd_workspace_size.argtypes = [SP]
         L.kda_chunk_fwd_workspace_size.restype = ctypes.c_size_t
+        L.kda_chunk_records.argtypes = [SP, P, P, P, P, P, ctypes.c_size_t, P]
+        L.kda_chunk_records.restype = ctypes.c_int
+        L.kda_chunk_apply_records.argtypes = [SP, P, ctypes.c_size_t, P, P, P, P, P]
+        L.kda_chunk_apply_records.restype = ctypes.c_int
         L.kda_decode_step.argtypes = [SP, P, P, P, P, P, P, P, P]
         L.kda_decode_step.restype = ctypes.c_int
         L.kda_status_string.argtypes = [ctypes.c_int]
@@ -179,6 +183,60 @@ def chunk_fwd(q, k, v, alpha, beta, initial_state=None, out=None, final_state=No
     o, s, _ = _chunk_call(False, q, k, v, alpha, beta, initial_state, out, final_state, want_final, path,
                           workspace)
     return o, s
+
+
+def chunk_records(q, k, alpha, beta, workspace=None, dv=None):
+    """First pass of the two-pass forward alone: the per-chunk records of q, k, alpha,
+    beta (layouts as chunk_fwd) into `workspace` (uint8 device tensor of at least
+    workspace_size(...) bytes; allocated when None).  Returns the workspace."""
+    torch = _torch()
+    B, T, H, dk = q.shape
+    dv = dk if dv is None else dv
+    code = _dtype_code(q)
+    for t, nm in ((k, "k"), (alpha, "alpha"), (beta, "beta")):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{nm} must have the dtype of q")
+    if k.shape != q.shape or alpha.shape != q.shape or beta.shape != (B, T, H):
+        raise ValueError("shapes: q, k, alpha [B,T,H,dk]; beta [B,T,H]")
+    dev = q.device
+    shape = Shape(B, T, H, dk, dv, 64, code)
+    need = int(lib().kda_chunk_fwd_workspace_size(ctypes.byref(shape)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check((q, k, alpha, beta, workspace), ("q", "k", "alpha", "beta", "workspace"), dev)
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = lib().kda_chunk_records(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(alpha), _ptr(beta), _ptr(workspace),
+                                 ctypes.c_size_t(nbytes), _stream(dev))
+    if rc != 0:
+        raise KdaError(rc, "kda_chunk_records")
+    return workspace
+
+
+def chunk_apply_records(workspace, v, initial_state=None, out=None, final_state=None, want_final=True, dk=128,
+                        dtype=None):
+    """Second pass alone: applies the records in `workspace` to v [B,T,H,dv] and the
+    start state.  dk is the key width the records were made with.  Returns
+    (o [B,T,H,dv], final_state or None)."""
+    torch = _torch()
+    B, T, H, dv = v.shape
+    code = _dtype_code(v)
+    dev = v.device
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=v.dtype, device=dev)
+    if final_state is None and want_final:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    for t, nm in ((initial_state, "initial_state"), (final_state, "final_state")):
+        if t is not None and (t.dtype != torch.float32 or t.shape != (B, H, dk, dv)):
+            raise ValueError(f"{nm} must be float32 [B,H,dk,dv]")
+    _check((workspace, v, initial_state, out, final_state),
+           ("workspace", "v", "initial_state", "out", "final_state"), dev)
+    shape = Shape(B, T, H, dk, dv, 64, code)
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = lib().kda_chunk_apply_records(ctypes.byref(shape), _ptr(workspace), ctypes.c_size_t(nbytes), _ptr(v),
+                                       _ptr(initial_state), _ptr(out), _ptr(final_state), _stream(dev))
+    if rc != 0:
+        raise KdaError(rc, "kda_chunk_apply_records")
+    return out, final_state
 
 
 def chunk_fwd_debug(q, k, v, alpha, beta, initial_state=None):

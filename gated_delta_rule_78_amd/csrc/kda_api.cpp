@@ -51,6 +51,97 @@ int check_shape(const kda_shape* s, bool decode, int* es) {
   return KDA_OK;
 }
 
+// KDA_PREP_CPW=n pins the chunks per workgroup of the two-pass first pass (tuning aid).
+int prep_cpw_override() {
+  static const int v = [] {
+    const char* e = getenv("KDA_PREP_CPW");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
+}
+
+size_t workspace_bytes_for(const kda_shape& s) {
+  const size_t nchunks = ((size_t)s.T + 63) / 64;
+  return (size_t)s.B * s.H * nchunks * kda::record_bytes(s.dtype == KDA_BF16, s.dk);
+}
+
+// Pointers of one chunk-forward call; the members a given entry point does not take are NULL.
+struct ChunkPtrs {
+  const void *q, *k, *v, *alpha, *beta;
+  const float* s0;
+  void* o;
+  float* sT;
+  float* dbg;
+  void* ws;
+  size_t ws_bytes;
+};
+
+enum : int { kNeedQKAB = 1, kNeedVO = 2, kNeedWS = 4 };
+
+// Host-side checks shared by the chunk entry points (nothing touches the device).
+int validate_chunk(const kda_shape* shape, const ChunkPtrs& p, int need) {
+  int es = 0;
+  int rc = check_shape(shape, false, &es);
+  if (rc) return rc;
+  const kda_shape& s = *shape;
+  if (s.dtype == KDA_F32 && (s.dk != 64 || s.dv != 64)) return KDA_ERR_UNSUPPORTED;
+  const int64_t rows = (int64_t)s.B * s.T * s.H;
+  const int64_t st_bytes = (int64_t)s.B * s.H * s.dk * s.dv * 4;
+  if (rows > 0) {
+    if ((need & kNeedQKAB) && (!p.q || !p.k || !p.alpha || !p.beta)) return KDA_ERR_NULL;
+    if ((need & kNeedVO) && (!p.v || !p.o)) return KDA_ERR_NULL;
+  }
+  // q, k, v, alpha, o and the states move in 16-byte vectors; beta is read per element
+  const void* vec[] = {p.q, p.k, p.v, p.alpha, p.o, p.s0, p.sT, p.dbg};
+  for (const void* x : vec)
+    if (x && misaligned(x)) return KDA_ERR_ALIGN;
+  if (p.beta && misaligned(p.beta, es)) return KDA_ERR_ALIGN;
+  const Range in[] = {range_of(p.q, p.q ? rows * s.dk * es : 0),         range_of(p.k, p.k ? rows * s.dk * es : 0),
+                      range_of(p.v, p.v ? rows * s.dv * es : 0),         range_of(p.alpha, p.alpha ? rows * s.dk * es : 0),
+                      range_of(p.beta, p.beta ? rows * es : 0),          range_of(p.s0, p.s0 ? st_bytes : 0)};
+  const Range ro = range_of(p.o, p.o ? rows * s.dv * es : 0);
+  const Range rs = range_of(p.sT, p.sT ? st_bytes : 0);
+  for (const Range& r : in)
+    if (overlap(ro, r)) return KDA_ERR_ALIAS;
+  for (int i = 0; i < 5; ++i)
+    if (overlap(rs, in[i])) return KDA_ERR_ALIAS;
+  if (p.s0 != p.sT && overlap(rs, in[5])) return KDA_ERR_ALIAS;  // in place is allowed
+  if (overlap(rs, ro)) return KDA_ERR_ALIAS;
+  if (need & kNeedWS) {
+    const size_t ws_need = workspace_bytes_for(s);
+    if (ws_need > 0 && !p.ws) return KDA_ERR_NULL;
+    if (p.ws_bytes < ws_need) return KDA_ERR_WORKSPACE;
+    if (((uintptr_t)p.ws & 255u) != 0) return KDA_ERR_ALIGN;
+    const Range rw = range_of(p.ws, (int64_t)ws_need);
+    for (const Range& r : in)
+      if (overlap(rw, r)) return KDA_ERR_ALIAS;
+    if (overlap(rw, ro) || overlap(rw, rs)) return KDA_ERR_ALIAS;
+  }
+  return KDA_OK;
+}
+
+kda::ChunkArgs chunk_args(const kda_shape& s, const ChunkPtrs& p, void* stream) {
+  return kda::ChunkArgs{p.q, p.k, p.v, p.alpha, p.beta, p.s0, p.o, p.sT, p.dbg, s.B, s.T, s.H, s.dk, s.dv,
+                        s.dtype == KDA_BF16, stream, value_tile_override()};
+}
+
+// pass 1 of the two-pass forward: every chunk's record, in parallel
+int run_records(const kda_shape& s, const ChunkPtrs& p, void* stream) {
+  const int64_t nchunks = ((int64_t)s.T + 63) / 64;
+  const int64_t total = (int64_t)s.B * s.H * nchunks;
+  if (total == 0) return KDA_OK;
+  int cpw = prep_cpw_override();
+  if (cpw <= 0) cpw = (int)((total + 1535) / 1536);  // aim at ~1.5K workgroups (6 per CU)
+  if (cpw < 1) cpw = 1;
+  if (cpw > nchunks) cpw = (int)nchunks;
+  return kda::launch_prep(chunk_args(s, p, stream), p.ws, cpw) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+// pass 2: the state walk over the records
+int run_apply(const kda_shape& s, const ChunkPtrs& p, void* stream) {
+  return kda::launch_state(chunk_args(s, p, stream), p.ws) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -72,75 +163,14 @@ const char* kda_status_string(int status) {
 
 int kda_version(void) { return kVersion; }
 
-// KDA_PREP_CPW=n pins the chunks per workgroup of the two-pass first pass (tuning aid).
-int prep_cpw_override() {
-  static const int v = [] {
-    const char* e = getenv("KDA_PREP_CPW");
-    return e ? atoi(e) : 0;
-  }();
-  return v;
-}
-
-size_t workspace_bytes_for(const kda_shape& s) {
-  const size_t nchunks = ((size_t)s.T + 63) / 64;
-  return (size_t)s.B * s.H * nchunks * kda::record_bytes(s.dtype == KDA_BF16, s.dk);
-}
-
-static int chunk_fwd_impl(const kda_shape* shape, const void* q, const void* k, const void* v,
-                          const void* alpha, const void* beta, const float* s0, void* o, float* sT,
-                          float* dbg, void* ws, size_t ws_bytes, void* stream) {
-  int es = 0;
-  int rc = check_shape(shape, false, &es);
-  if (rc) return rc;
-  const kda_shape& s = *shape;
-  if (s.dtype == KDA_F32 && (s.dk != 64 || s.dv != 64)) return KDA_ERR_UNSUPPORTED;
-  const int64_t rows = (int64_t)s.B * s.T * s.H;
-  const int64_t st_bytes = (int64_t)s.B * s.H * s.dk * s.dv * 4;
-  if (rows > 0 && (!q || !k || !v || !alpha || !beta || !o)) return KDA_ERR_NULL;
-  // q, k, v, alpha, o and the states move in 16-byte vectors; beta is read per element
-  const void* ptrs[] = {q, k, v, alpha, o, s0, sT, dbg};
-  for (const void* p : ptrs)
-    if (p && misaligned(p)) return KDA_ERR_ALIGN;
-  if (beta && misaligned(beta, es)) return KDA_ERR_ALIGN;
-  const Range in[] = {range_of(q, rows * s.dk * es), range_of(k, rows * s.dk * es),
-                      range_of(v, rows * s.dv * es), range_of(alpha, rows * s.dk * es),
-                      range_of(beta, rows * es), range_of(s0, s0 ? st_bytes : 0)};
-  const Range ro = range_of(o, rows * s.dv * es);
-  for (const Range& r : in)
-    if (overlap(ro, r)) return KDA_ERR_ALIAS;
-  if (sT) {
-    const Range rs = range_of(sT, st_bytes);
-    for (int i = 0; i < 5; ++i)
-      if (overlap(rs, in[i])) return KDA_ERR_ALIAS;
-    if (s0 && s0 != sT && overlap(rs, in[5])) return KDA_ERR_ALIAS;
-    if (overlap(rs, ro)) return KDA_ERR_ALIAS;
-  }
-  kda::ChunkArgs a{q, k, v, alpha, beta, s0, o, sT, dbg, s.B, s.T, s.H, s.dk, s.dv,
-                   s.dtype == KDA_BF16, stream, value_tile_override()};
-  if (!ws) return kda::launch_chunk(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
-  // two-pass path: the workspace holds one record per (b, h, chunk)
-  const size_t need = workspace_bytes_for(s);
-  if (ws_bytes < need) return KDA_ERR_WORKSPACE;
-  if (((uintptr_t)ws & 255u) != 0) return KDA_ERR_ALIGN;
-  const Range rw = range_of(ws, (int64_t)need);
-  for (const Range& r : in)
-    if (overlap(rw, r)) return KDA_ERR_ALIAS;
-  if (overlap(rw, ro) || (sT && overlap(rw, range_of(sT, st_bytes)))) return KDA_ERR_ALIAS;
-  if (rows == 0) return kda::launch_state(a, ws) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
-  const int64_t nchunks = ((int64_t)s.T + 63) / 64;
-  const int64_t total = (int64_t)s.B * s.H * nchunks;
-  int cpw = prep_cpw_override();
-  if (cpw <= 0) cpw = (int)((total + 1535) / 1536);  // aim at ~1.5K workgroups (6 per CU)
-  if (cpw < 1) cpw = 1;
-  if (cpw > nchunks) cpw = (int)nchunks;
-  if (kda::launch_prep(a, ws, cpw) != hipSuccess) return KDA_ERR_HIP;
-  return kda::launch_state(a, ws) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
-}
 
 int kda_chunk_fwd(const kda_shape* shape, const void* q, const void* k, const void* v,
                   const void* alpha, const void* beta, const float* initial_state, void* o,
                   float* final_state, void* stream) {
-  return chunk_fwd_impl(shape, q, k, v, alpha, beta, initial_state, o, final_state, nullptr, nullptr, 0, stream);
+  const ChunkPtrs p{q, k, v, alpha, beta, initial_state, o, final_state, nullptr, nullptr, 0};
+  int rc = validate_chunk(shape, p, kNeedQKAB | kNeedVO);
+  if (rc) return rc;
+  return kda::launch_chunk(chunk_args(*shape, p, stream)) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 size_t kda_chunk_fwd_workspace_size(const kda_shape* shape) {
@@ -153,15 +183,37 @@ size_t kda_chunk_fwd_workspace_size(const kda_shape* shape) {
 int kda_chunk_fwd_ws(const kda_shape* shape, const void* q, const void* k, const void* v, const void* alpha,
                      const void* beta, const float* initial_state, void* o, float* final_state, void* workspace,
                      size_t workspace_bytes, void* stream) {
-  return chunk_fwd_impl(shape, q, k, v, alpha, beta, initial_state, o, final_state, nullptr, workspace,
-                        workspace_bytes, stream);
+  if (!workspace) return kda_chunk_fwd(shape, q, k, v, alpha, beta, initial_state, o, final_state, stream);
+  const ChunkPtrs p{q, k, v, alpha, beta, initial_state, o, final_state, nullptr, workspace, workspace_bytes};
+  int rc = validate_chunk(shape, p, kNeedQKAB | kNeedVO | kNeedWS);
+  if (rc) return rc;
+  rc = run_records(*shape, p, stream);
+  return rc ? rc : run_apply(*shape, p, stream);
+}
+
+int kda_chunk_records(const kda_shape* shape, const void* q, const void* k, const void* alpha, const void* beta,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  const ChunkPtrs p{q, k, nullptr, alpha, beta, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes};
+  int rc = validate_chunk(shape, p, kNeedQKAB | kNeedWS);
+  return rc ? rc : run_records(*shape, p, stream);
+}
+
+int kda_chunk_apply_records(const kda_shape* shape, const void* workspace, size_t workspace_bytes, const void* v,
+                            const float* initial_state, void* o, float* final_state, void* stream) {
+  const ChunkPtrs p{nullptr, nullptr, v, nullptr, nullptr, initial_state, o, final_state, nullptr,
+                    const_cast<void*>(workspace), workspace_bytes};
+  int rc = validate_chunk(shape, p, kNeedVO | kNeedWS);
+  return rc ? rc : run_apply(*shape, p, stream);
 }
 
 int kda_chunk_fwd_debug(const kda_shape* shape, const void* q, const void* k, const void* v,
                         const void* alpha, const void* beta, const float* initial_state, void* o,
                         float* final_state, float* dbg, void* stream) {
   if (!dbg) return KDA_ERR_NULL;
-  return chunk_fwd_impl(shape, q, k, v, alpha, beta, initial_state, o, final_state, dbg, nullptr, 0, stream);
+  const ChunkPtrs p{q, k, v, alpha, beta, initial_state, o, final_state, dbg, nullptr, 0};
+  int rc = validate_chunk(shape, p, kNeedQKAB | kNeedVO);
+  if (rc) return rc;
+  return kda::launch_chunk(chunk_args(*shape, p, stream)) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 int kda_decode_step(const kda_shape* shape, const void* q, const void* k, const void* v,

@@ -123,6 +123,26 @@ int kda_chunk_fwd_ws(const kda_shape* shape, const void* q, const void* k, const
                      void* stream);
 
 /*
+ * The two passes of kda_chunk_fwd_ws as separate calls (same workspace rules).
+ * A chunk's record depends only on q, k, alpha and beta: it is the chunk's exact
+ * affine block transfer (SFDA page, "Principales Contribuciones" item 3) less the
+ * part that v and the state enter linearly, so one set of records can be applied
+ * to several v / start-state pairs of the same shape.
+ *   kda_chunk_records       : reads q, k, alpha, beta [layouts as kda_chunk_fwd];
+ *                             writes the records of every (b, h, chunk).
+ *   kda_chunk_apply_records : reads the records, v and initial_state (NULL = zero);
+ *                             writes o and final_state (NULL = not written; may equal
+ *                             initial_state).  The workspace is only read.
+ * shape->dv is checked but does not change the records.  Errors as kda_chunk_fwd_ws;
+ * a NULL workspace is KDA_ERR_NULL unless the shape needs none (B*T == 0).
+ */
+int kda_chunk_records(const kda_shape* shape, const void* q, const void* k, const void* alpha,
+                      const void* beta, void* workspace, size_t workspace_bytes, void* stream);
+int kda_chunk_apply_records(const kda_shape* shape, const void* workspace, size_t workspace_bytes,
+                            const void* v, const float* initial_state, void* o, float* final_state,
+                            void* stream);
+
+/*
  * One recurrent decode step for every (b, h), state updated in place:
  *   S <- (I - beta k k^T) Diag(alpha) S + beta k v^T ;  o <- S^T q.
  *   state : [B, H, dk, dv] fp32, read and written in place.

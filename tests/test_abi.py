@@ -125,6 +125,34 @@ def test_workspace_size_and_errors(L):
     assert _chunk_ws(L, _p(9), need, dk=96) == UNSUP
 
 
+def test_records_and_apply_argument_errors(L):
+    shape = kda.Shape(1, 64, 2, 64, 64, 64, 0)
+    need = L.kda_chunk_fwd_workspace_size(ctypes.byref(shape))
+    sz = ctypes.c_size_t
+
+    def rec(q=_p(0), k=_p(1), a=_p(3), b=_p(4), ws=_p(9), n=need, sh=shape):
+        return L.kda_chunk_records(ctypes.byref(sh), q, k, a, b, ws, sz(n), None)
+
+    def app(ws=_p(9), n=need, v=_p(2), s0=None, o=_p(5), sT=None):
+        return L.kda_chunk_apply_records(ctypes.byref(shape), ws, sz(n), v, s0, o, sT, None)
+
+    assert rec(q=None) == NULL
+    assert rec(b=None) == NULL
+    assert rec(ws=None) == NULL
+    assert rec(n=need - 16) == WORKSPACE
+    assert rec(ws=_p(9, off=64)) == ALIGN
+    assert rec(ws=_p(3)) == ALIAS                        # workspace over alpha
+    assert rec(sh=kda.Shape(1, 64, 2, 64, 64, 64, 1), n=need) == WORKSPACE   # fp32 records are larger
+    assert app(v=None) == NULL
+    assert app(o=None) == NULL
+    assert app(ws=None) == NULL
+    assert app(n=0) == WORKSPACE
+    assert app(o=_p(9, off=256)) == ALIAS                # output over the records
+    assert app(sT=_p(2)) == ALIAS                        # final state over v
+    assert app(s0=_p(7), sT=_p(7, off=16)) == ALIAS
+    assert app(v=_p(2, off=4)) == ALIGN
+
+
 def test_decode_argument_errors(L):
     assert L.kda_decode_step(None, *([None] * 8)) == NULL
     assert _decode(L, dtype=3) == DTYPE

@@ -125,6 +125,29 @@ def test_two_pass_agrees_with_single_pass():
     assert rel_err_slices(s1.reshape(8, -1), s2.reshape(8, -1), 8) < 1e-2
 
 
+def test_records_applied_to_two_value_sets():
+    """Records depend on q, k, alpha, beta only: one set of records applied to two
+    different (v, start state) pairs gives each pair's own forward."""
+    import gated_delta_rule_78_amd as kda
+    import torch
+    inp = make(2, 200, 3, 128, 128, "bf16", "ckda", False, seed=43)
+    other = make(2, 200, 3, 128, 128, "bf16", "ckda", False, seed=44)
+    q, k, v, a, b = inputs_to_dev(inp)
+    v2 = inputs_to_dev(other)[2]
+    s0, s02 = state_to_dev(inp.S0), state_to_dev(other.S0)
+    ws = kda.chunk_records(q, k, a, b)
+    o1, f1 = kda.chunk_apply_records(ws, v, s0)
+    o2, f2 = kda.chunk_apply_records(ws, v2, s02)
+    r1 = kda.chunk_fwd(q, k, v, a, b, initial_state=s0, path="fused")
+    r2 = kda.chunk_fwd(q, k, v2, a, b, initial_state=s02, path="fused")
+    torch.cuda.synchronize()
+    for got, want in ((o1, r1[0]), (f1, r1[1]), (o2, r2[0]), (f2, r2[1])):
+        assert torch.equal(got, want)
+    # and against the oracle for the second pair
+    inp.v, inp.S0 = other.v, other.S0
+    _check(inp, inp.S0, label="records-reuse", path="twopass")
+
+
 def test_split_invariance_on_gpu():
     """chunk_fwd(T1 + T2) == chunk_fwd(T2, S0 = final(T1)) for T1 a multiple of 64:
     the affine block transfer applied at a chunk boundary."""
