@@ -1052,10 +1052,10 @@ hipError_t launch_chunk(const ChunkArgs& a) {
 
 // ---------------------------------------------------------------------------
 // Two-pass forward, first pass: records of every chunk of every head, in parallel.
-template <typename T, int DK>
+template <typename T, int DK, int NWV>
 static hipError_t launch_prep_t(const ChunkArgs& a, char* ws, int cpw) {
-  using K = Cfg<T, DK, 64>;
-  auto kern = chunk_fwd_kernel<T, DK, 64, true>;
+  using K = Cfg<T, DK, NWV>;
+  auto kern = chunk_fwd_kernel<T, DK, NWV, true>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, K::LDS);
@@ -1072,8 +1072,9 @@ static hipError_t launch_prep_t(const ChunkArgs& a, char* ws, int cpw) {
 }
 
 hipError_t launch_prep(const ChunkArgs& a, void* ws, int cpw) {
-  if (!a.bf16) return a.dk == 64 ? launch_prep_t<float, 64>(a, (char*)ws, cpw) : hipErrorInvalidValue;
-  return a.dk == 64 ? launch_prep_t<bf16_t, 64>(a, (char*)ws, cpw) : launch_prep_t<bf16_t, 128>(a, (char*)ws, cpw);
+  if (!a.bf16) return a.dk == 64 ? launch_prep_t<float, 64, 64>(a, (char*)ws, cpw) : hipErrorInvalidValue;
+  return a.dk == 64 ? launch_prep_t<bf16_t, 64, 64>(a, (char*)ws, cpw)
+                    : launch_prep_t<bf16_t, 128, 64>(a, (char*)ws, cpw);
 }
 
 size_t record_bytes(bool bf16, int dk) {

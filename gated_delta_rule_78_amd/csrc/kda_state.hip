@@ -34,18 +34,39 @@ __device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
 #endif
 }
 
-__device__ __forceinline__ void wait_vmem() {
+// Workgroup barriers without a memory fence (a fence would also wait for the DMA still
+// streaming the next chunk).  The empty asm statements keep the compiler from moving
+// memory accesses across them; the explicit waits make this wave's LDS writes (and, for
+// full_barrier, its DMA and global accesses) complete before the barrier.
+__device__ __forceinline__ void lds_barrier() {
 #ifndef KDA_HOST_PASS
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt left at their maxima
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 #endif
 }
 
+__device__ __forceinline__ void full_barrier() {
+#ifndef KDA_HOST_PASS
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+#endif
+}
+
+// NW compute waves (16 value columns each) and NP producer waves that only move each
+// chunk's record and v tile global -> LDS with 16-byte DMA.  A wave stalled issuing
+// DMA cannot issue matrix work, and one wave's DMA issue rate is well below a CU's
+// share of HBM bandwidth, hence several producers beside the compute waves.
 template <typename T, int DK, int VT>
 struct SCfg {
   using RL = RecordLayout<T, DK>;
   static constexpr int ES = Elem<T>::kBytes;
   static constexpr int NW = VT / 16;
-  static constexpr int NT = NW * 64;
+  static constexpr int NP = 4;
+  static constexpr int NT = (NW + NP) * 64;
   static constexpr int KS = DK / 32;
   static constexpr int RS_V = VT * ES;        // v tile rows (dense: filled by DMA), reused for O
   static constexpr int UPR = RS_V / 16;        // 16-byte units per v row
@@ -60,14 +81,27 @@ struct SCfg {
 
 }  // namespace
 
+// Keeps the compiler's scheduler from moving instructions across this point: the
+// fragment loads issued before it stay ahead of the matrix-core work after it.
+__device__ __forceinline__ void fence_sched() {
+#ifndef KDA_HOST_PASS
+  __builtin_amdgcn_sched_barrier(0);
+#endif
+}
+
 // One chunk of the state pass: record `rec` and v tile `vv` are in LDS; S advances one
 // chunk and the chunk's outputs are staged into this wave's own columns of `vv`.
+//   U = M~ V ;  Delta = U - W S ;  O = (Q o gamma) S + A Delta ;
+//   S <- diag(gamma_last) S + (K o rho)^T Delta
+// With one compute wave per SIMD little else hides LDS latency, so the operand
+// fragments of each group of products are loaded one group ahead (software pipelining).
 template <typename T, int DK, int VT>
 __device__ __forceinline__ void state_chunk(const char* rec, char* vv, f32x4_t (&S)[DK / 16], int wave, int g,
                                             int n) {
   using K = SCfg<T, DK, VT>;
   using RL = typename K::RL;
   constexpr int ES = K::ES;
+  constexpr int KS = K::KS;
   const char* WW = rec + RL::WW;
   const char* QG = rec + RL::QG;
   const char* KRT = rec + RL::KRT;
@@ -75,81 +109,106 @@ __device__ __forceinline__ void state_chunk(const char* rec, char* vv, f32x4_t (
   const char* MT = rec + RL::MT;
   const float* GC = (const float*)(rec + RL::GC);
 
-  // U = M~ V for this wave's 16 value columns
-  f32x4_t Dl[NB];
-  {
-    Frag<T> bv[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) bv[ks].load_col8(vv + (32 * ks + 8 * g) * K::RS_V + (16 * wave + n) * ES, K::RS_V);
-#pragma unroll
-    for (int I = 0; I < NB; ++I) {
-      Dl[I] = zero4();
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        if (ks == 0 || I >= 2) {
-          Frag<T> fa;
-          fa.load8(MT + (16 * I + n) * RL::RS_C + (32 * ks + 8 * g) * ES);
-          mma(Dl[I], fa, bv[ks]);
-        }
-      }
-    }
-  }
-  // Delta = U - W S ; O = (Q o gamma) S + A Delta ; S <- diag(gamma_last) S + (K o rho)^T Delta
-  Frag<T> bs[K::KS];
-#pragma unroll
-  for (int ks = 0; ks < K::KS; ++ks) bs[ks].from_acc(S[2 * ks], S[2 * ks + 1]);
-  f32x4_t Ot[NB];
-#pragma unroll
-  for (int I = 0; I < NB; ++I) {
-    Ot[I] = zero4();
+  // -W and Q o gamma rows of block I, key steps ks: A fragments (slots 4g.. and 16 + 4g..)
+  auto load_wq = [&](Frag<T> (&fw)[KS], Frag<T> (&fq)[KS], int I) {
     const char* wrow = WW + (16 * I + n) * RL::RS_DK;
     const char* qrow = QG + (16 * I + n) * RL::RS_DK;
-    Frag<T> fw[K::KS], fq[K::KS];
 #pragma unroll
-    for (int ks = 0; ks < K::KS; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       const int c0 = 32 * ks + 4 * g;
       fw[ks].load4x2(wrow + c0 * ES, wrow + (c0 + 16) * ES);
       fq[ks].load4x2(qrow + c0 * ES, qrow + (c0 + 16) * ES);
     }
+  };
+
+  // group 0 operands: M~ (lower blocks only), the v tile columns of this wave, block 0 of W, Q
+  Frag<T> fm[6], bv[2];
+  Frag<T> fw[2][KS], fq[2][KS];
 #pragma unroll
-    for (int ks = 0; ks < K::KS; ++ks) {
-      mma(Dl[I], fw[ks], bs[ks]);
-      mma(Ot[I], fq[ks], bs[ks]);
-    }
+  for (int ks = 0; ks < 2; ++ks) bv[ks].load_col8(vv + (32 * ks + 8 * g) * K::RS_V + (16 * wave + n) * ES, K::RS_V);
+#pragma unroll
+  for (int j = 0; j < 6; ++j) {
+    const int I = j < 2 ? j : 2 + (j - 2) / 2, ks = j < 2 ? 0 : (j - 2) % 2;
+    fm[j].load8(MT + (16 * I + n) * RL::RS_C + (32 * ks + 8 * g) * ES);
   }
+  load_wq(fw[0], fq[0], 0);
+  Frag<T> bs[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) bs[ks].from_acc(S[2 * ks], S[2 * ks + 1]);
+  fence_sched();
+
+  // U = M~ V, then per block I: Delta_I = U_I - W_I S, O_I = Q_I S (operands of I + 1 in flight)
+  f32x4_t Dl[NB], Ot[NB];
+#pragma unroll
+  for (int j = 0; j < 6; ++j) {
+    const int I = j < 2 ? j : 2 + (j - 2) / 2, ks = j < 2 ? 0 : (j - 2) % 2;
+    if (ks == 0) Dl[I] = zero4();
+    mma(Dl[I], fm[j], bv[ks]);
+  }
+#pragma unroll
+  for (int I = 0; I < NB; ++I) {
+    if (I + 1 < NB) load_wq(fw[(I + 1) & 1], fq[(I + 1) & 1], I + 1);
+    fence_sched();
+    Ot[I] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      mma(Dl[I], fw[I & 1][ks], bs[ks]);
+      mma(Ot[I], fq[I & 1][ks], bs[ks]);
+    }
+    fence_sched();
+  }
+
+  // A Delta (A lower blocks) and the first half of (K o rho)^T, loaded while the
+  // last products retire
+  Frag<T> fa[6];
+#pragma unroll
+  for (int j = 0; j < 6; ++j) {
+    const int I = j < 2 ? j : 2 + (j - 2) / 2, s2 = j < 2 ? 0 : (j - 2) % 2;
+    const char* arow = AT + (16 * I + n) * RL::RS_C;
+    const int p0 = 32 * s2 + 4 * g;
+    fa[j].load4x2(arow + p0 * ES, arow + (p0 + 16) * ES);
+  }
+  constexpr int RH = DK / 32;  // S row blocks per half
+  Frag<T> fk[2][RH][2];
+  float4 gc[2][RH];
+  auto load_k = [&](int half) {
+#pragma unroll
+    for (int rr = 0; rr < RH; ++rr) {
+      const int r = half * RH + rr;
+      const char* krow = KRT + (16 * r + n) * RL::RS_C;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int p0 = 32 * s2 + 4 * g;
+        fk[half][rr][s2].load4x2(krow + p0 * ES, krow + (p0 + 16) * ES);
+      }
+      gc[half][rr] = *(const float4*)(GC + 16 * r + 4 * g);
+    }
+  };
+  load_k(0);
+  fence_sched();
   Frag<T> bd[2];
   bd[0].from_acc(Dl[0], Dl[1]);
   bd[1].from_acc(Dl[2], Dl[3]);
 #pragma unroll
-  for (int I = 0; I < NB; ++I) {
-    const char* arow = AT + (16 * I + n) * RL::RS_C;
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      if (s2 == 0 || I >= 2) {
-        const int p0 = 32 * s2 + 4 * g;
-        Frag<T> fa;
-        fa.load4x2(arow + p0 * ES, arow + (p0 + 16) * ES);
-        mma(Ot[I], fa, bd[s2]);
-      }
-    }
+  for (int j = 0; j < 6; ++j) {
+    const int I = j < 2 ? j : 2 + (j - 2) / 2, s2 = j < 2 ? 0 : (j - 2) % 2;
+    mma(Ot[I], fa[j], bd[s2]);
   }
+  load_k(1);
+  fence_sched();
+  // S <- diag(gamma_last) S + (K o rho)^T Delta
 #pragma unroll
-  for (int r = 0; r < DK / 16; ++r) {
-    const float4 gc = *(const float4*)(GC + 16 * r + 4 * g);
-    S[r][0] *= gc.x;
-    S[r][1] *= gc.y;
-    S[r][2] *= gc.z;
-    S[r][3] *= gc.w;
-    const char* krow = KRT + (16 * r + n) * RL::RS_C;
-    Frag<T> fa[2];
+  for (int half = 0; half < 2; ++half)
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const int p0 = 32 * s2 + 4 * g;
-      fa[s2].load4x2(krow + p0 * ES, krow + (p0 + 16) * ES);
+    for (int rr = 0; rr < RH; ++rr) {
+      const int r = half * RH + rr;
+      S[r][0] *= gc[half][rr].x;
+      S[r][1] *= gc[half][rr].y;
+      S[r][2] *= gc[half][rr].z;
+      S[r][3] *= gc[half][rr].w;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) mma(S[r], fk[half][rr][s2], bd[s2]);
     }
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) mma(S[r], fa[s2], bd[s2]);
-  }
   // O over this wave's own (already consumed) v columns
 #pragma unroll
   for (int I = 0; I < NB; ++I)
@@ -164,11 +223,12 @@ __device__ __forceinline__ void state_chunk(const char* rec, char* vv, f32x4_t (
 }
 
 template <typename T, int DK, int VT>
-__global__ __launch_bounds__((VT / 16) * 64) void chunk_state_kernel(const char* __restrict__ ws,
-                                                                     const void* __restrict__ gv, const float* s0,
-                                                                     void* __restrict__ go, float* sT, int Tlen, int H,
-                                                                     int DV, int BH) {
+__global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const char* __restrict__ ws,
+                                                                         const void* __restrict__ gv,
+                                                                         const float* s0, void* __restrict__ go,
+                                                                         float* sT, int Tlen, int H, int DV, int BH) {
   using K = SCfg<T, DK, VT>;
+  constexpr int NP = K::NP;
   using RL = typename K::RL;
   constexpr int ES = K::ES;
   constexpr int NT = K::NT;
@@ -182,6 +242,8 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_state_kernel(const char*
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool producer = wave >= NW;  // move the data; the other waves only compute
+  const int pw = wave - NW;          // producer index
   const int g = lane >> 4;
   const int n = lane & 15;
   const int NVT = DV / VT;
@@ -205,33 +267,35 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_state_kernel(const char*
   f32x4_t S[DK / 16];
 #pragma unroll
   for (int r = 0; r < DK / 16; ++r) S[r] = zero4();
-  if (s0) {
+  if (s0 && !producer) {
 #pragma unroll
     for (int r = 0; r < DK / 16; ++r)
 #pragma unroll
       for (int e = 0; e < 4; ++e) S[r][e] = s0[((size_t)bh * DK + 16 * r + 4 * g + e) * DV + v0 + 16 * wave + n];
   }
 
-  // chunk c's record and v tile (rows past the end clamped to the last row) -> LDS
+  // (producer waves) chunk c's record and v tile -> LDS; v rows past the end are clamped
+  // to the last row here and zeroed once they have landed
   auto issue = [&](int c, char* rec_dst, char* v_dst) {
     const char* rec = rec0 + (size_t)c * RL::BYTES;
-    for (int x = wave; x < K::N_DMA_REC; x += NW) {
-      const int off = x * 1024 + lane * 16;
-      if (off < RL::IMG) dma16(rec + off, rec_dst + x * 1024);
-    }
     const int t0 = c * C;
-    for (int x = wave; x < K::N_DMA_V; x += NW) {
+#pragma nounroll
+    for (int x = pw; x < K::N_DMA_V; x += NP) {
       const int sl = x * 64 + lane;
       const int row = sl / K::UPR, u = sl % K::UPR;
       const size_t gr = ((size_t)b * Tlen + min(t0 + row, Tlen - 1)) * H + h;
       dma16((const char*)gv + (gr * DV + v0) * ES + (size_t)u * 16, v_dst + x * 1024);
     }
+#pragma nounroll
+    for (int x = pw; x < K::N_DMA_REC; x += NP) {
+      const int off = x * 1024 + lane * 16;
+      if (off < RL::IMG) dma16(rec + off, rec_dst + x * 1024);
+    }
   };
-  // after the wait: zero the v rows past the end, then store the staged outputs
-  auto finish = [&](int c, char* vv) {
+  // the staged outputs of chunk c (in the consumed v tile `vv`) -> o
+  auto store_o = [&](int c, const char* vv) {
     const int t0 = c * C;
     const int nv = min(C, Tlen - t0);
-    __syncthreads();
     for (int j = tid; j < C * K::UPR; j += NT) {
       const int row = j / K::UPR, u = j % K::UPR;
       if (row < nv)
@@ -239,46 +303,56 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_state_kernel(const char*
             *(const uint4*)(vv + row * K::RS_V + u * 16);
     }
   };
+  // v rows past the end of the sequence read as zero
   auto pad_rows = [&](int c, char* vv) {
     const int nv = Tlen - c * C;
     if (nv < C) {
       for (int j = nv * K::UPR + tid; j < C * K::UPR; j += NT) *(uint4*)(vv + j * 16) = make_uint4(0, 0, 0, 0);
-      __syncthreads();
+      lds_barrier();
     }
   };
 
-  if (nchunks > 0) issue(0, rec_a, v_a);
+  if (nchunks > 0 && producer) issue(0, rec_a, v_a);
   if constexpr (K::NBUF == 2) {
+    // chunk c computes from buffers P while the producer streams chunk c + 1 into
+    // buffers Q; the outputs of chunk c - 1, staged in Q's v tile, are stored first
+    auto step = [&](int c, const char* recP, char* vP, char* recQ, char* vQ) {
+      full_barrier();  // chunk c landed; chunk c - 1 finished everywhere
+      if (c > 0) {
+        store_o(c - 1, vQ);
+        lds_barrier();  // vQ read out before the next v tile lands there
+      }
+      pad_rows(c, vP);
+      if (producer) {
+        if (c + 1 < nchunks) issue(c + 1, recQ, vQ);
+      } else {
+        state_chunk<T, DK, VT>(recP, vP, S, wave, g, n);
+      }
+    };
     for (int chunk = 0; chunk < nchunks; chunk += 2) {
-      wait_vmem();
-      __syncthreads();
-      pad_rows(chunk, v_a);
-      if (chunk + 1 < nchunks) issue(chunk + 1, rec_b, v_b);
-      state_chunk<T, DK, VT>(rec_a, v_a, S, wave, g, n);
-      finish(chunk, v_a);
+      step(chunk, rec_a, v_a, rec_b, v_b);
       if (chunk + 1 >= nchunks) break;
-      wait_vmem();
-      __syncthreads();
-      pad_rows(chunk + 1, v_b);
-      if (chunk + 2 < nchunks) issue(chunk + 2, rec_a, v_a);
-      state_chunk<T, DK, VT>(rec_b, v_b, S, wave, g, n);
-      finish(chunk + 1, v_b);
+      step(chunk + 1, rec_b, v_b, rec_a, v_a);
+    }
+    if (nchunks > 0) {
+      lds_barrier();
+      store_o(nchunks - 1, ((nchunks - 1) & 1) ? v_b : v_a);
     }
   } else {
     for (int chunk = 0; chunk < nchunks; ++chunk) {
-      wait_vmem();
-      __syncthreads();
+      full_barrier();
       pad_rows(chunk, v_a);
-      state_chunk<T, DK, VT>(rec_a, v_a, S, wave, g, n);
-      finish(chunk, v_a);
+      if (!producer) state_chunk<T, DK, VT>(rec_a, v_a, S, wave, g, n);
+      lds_barrier();
+      store_o(chunk, v_a);
       if (chunk + 1 < nchunks) {
-        __syncthreads();  // every output read out of v_a before the next chunk lands there
-        issue(chunk + 1, rec_a, v_a);
+        lds_barrier();  // every output read out of v_a before the next chunk lands there
+        if (producer) issue(chunk + 1, rec_a, v_a);
       }
     }
   }
 
-  if (sT) {
+  if (sT && !producer) {
 #pragma unroll
     for (int r = 0; r < DK / 16; ++r)
 #pragma unroll
@@ -292,8 +366,8 @@ static hipError_t launch_state_t(const ChunkArgs& a, const void* ws) {
   using K = SCfg<T, DK, VT>;
   const int BH = a.B * a.H;
   auto kern = chunk_state_kernel<T, DK, VT>;
-  hipLaunchKernelGGL(kern, dim3(BH * (a.dv / VT)), dim3(K::NT), 0, (hipStream_t)a.stream,
-                     (const char*)ws, a.v, a.s0, a.o, a.sT, a.T, a.H, a.dv, BH);
+  hipLaunchKernelGGL(kern, dim3(BH * (a.dv / VT)), dim3(K::NT), 0, (hipStream_t)a.stream, (const char*)ws, a.v,
+                     a.s0, a.o, a.sT, a.T, a.H, a.dv, BH);
   return hipGetLastError();
 }
 
