@@ -108,8 +108,7 @@ struct Cfg {
   static constexpr int BASE_OP = BASE_IN + SZ_IN;
   static constexpr int BASE_L = BASE_OP + SZ_OP;
   static constexpr int BASE_GT = BASE_L + SZ_L;         // block totals g[4][DK]
-  static constexpr int BASE_PI = BASE_GT + 4 * DK * 4;  // Pi tables [3][DK]
-  static constexpr int BASE_GC = BASE_PI + 3 * DK * 4;  // gamma of the last row [DK]
+  static constexpr int BASE_GC = BASE_GT + 4 * DK * 4;  // gamma of the last row [DK]
   static constexpr int BASE_BETA = BASE_GC + DK * 4;    // beta [C]
   static constexpr int LDS = BASE_BETA + C * 4;
   static_assert(LDS <= 160 * 1024, "LDS budget");
@@ -217,7 +216,6 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
   char* const R_OP = smem + K::BASE_OP;
   char* const R_L = smem + K::BASE_L;
   float* const GT = (float*)(smem + K::BASE_GT);
-  float* const PI = (float*)(smem + K::BASE_PI);
   float* const GC = (float*)(smem + K::BASE_GC);
   float* const BETA = (float*)(smem + K::BASE_BETA);
 
@@ -350,19 +348,6 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
       }
     };
 
-    // ================= phase A: block totals of the gates
-    if (r0) {
-      ld_item(false);
-      float g0 = 1.f, g1 = 1.f;
-#pragma unroll
-      for (int m = 0; m < SUB; ++m) {
-        g0 *= al[m][0];
-        g1 *= al[m][1];
-      }
-      *(float2*)(GT + iI * DK + 2 * icp) = make_float2(g0, g1);
-    }
-    __syncthreads();
-
     // level operand writer: slot ls (0/1), level lam, for the item's block
     auto write_levels = [&](int ls, int lam) {
       char* LA = R_L + (size_t)(ls * NB + iI) * K::LVL_ROWS * K::RS_DK + 2 * icp * ES;
@@ -423,6 +408,7 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
           R::st(Xq + m * K::RS_DK, q0 * f0, q1 * f1);
           R::st(Xk + m * K::RS_DK, k0 * f0, k1 * f1);
         }
+        *(float2*)(GT + iI * DK + 2 * icp) = make_float2(f0, f1);  // the block's gate total
         float b0 = 1.f, b1 = 1.f;
 #pragma unroll
         for (int m = SUB - 1; m >= 0; --m) {
@@ -431,15 +417,6 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
           R::st(Y + m * K::RS_DK, k0 * b0, k1 * b1);
           b0 *= al[m][0];
           b1 *= al[m][1];
-        }
-        if (iI == 0) {
-          const float2 t0v = *(const float2*)(GT + 2 * icp), t1v = *(const float2*)(GT + DK + 2 * icp);
-          const float2 t2v = *(const float2*)(GT + 2 * DK + 2 * icp), t3v = *(const float2*)(GT + 3 * DK + 2 * icp);
-          *(float2*)(PI + 0 * DK + 2 * icp) = t1v;
-          *(float2*)(PI + 1 * DK + 2 * icp) = make_float2(t1v.x * t2v.x, t1v.y * t2v.y);
-          *(float2*)(PI + 2 * DK + 2 * icp) = t2v;
-          *(float2*)(GC + 2 * icp) =
-              make_float2(t0v.x * t1v.x * t2v.x * t3v.x, t0v.y * t1v.y * t2v.y * t3v.y);
         }
       }
       if (r1) {
@@ -474,9 +451,15 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
 #pragma unroll
         for (int ks = 0; ks < K::KS; ++ks) {
           if (pi >= 0) {
+            // whole blocks between J and I: g1 (pi 0), g1 g2 (pi 1), g2 (pi 2)
             const int c0 = 32 * ks + 8 * g;
-            const float4 p0 = *(const float4*)(PI + pi * DK + c0);
-            const float4 p1 = *(const float4*)(PI + pi * DK + c0 + 4);
+            const float* G1 = GT + (pi == 2 ? 2 : 1) * DK + c0;
+            float4 p0 = *(const float4*)G1, p1 = *(const float4*)(G1 + 4);
+            if (pi == 1) {
+              const float4 e0 = *(const float4*)(GT + 2 * DK + c0), e1 = *(const float4*)(GT + 2 * DK + c0 + 4);
+              p0 = make_float4(p0.x * e0.x, p0.y * e0.y, p0.z * e0.z, p0.w * e0.w);
+              p1 = make_float4(p1.x * e1.x, p1.y * e1.y, p1.z * e1.z, p1.w * e1.w);
+            }
             const float pv8[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
             fb[ks].scale(pv8);
           }
@@ -514,6 +497,7 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
         Gp[1] = iI == 0 ? 1.f : iI == 1 ? t0v.y : iI == 2 ? t0v.y * t1v.y : t0v.y * t1v.y * t2v.y;
         Rp[0] = iI == 3 ? 1.f : iI == 2 ? t3v.x : iI == 1 ? t2v.x * t3v.x : t1v.x * t2v.x * t3v.x;
         Rp[1] = iI == 3 ? 1.f : iI == 2 ? t3v.y : iI == 1 ? t2v.y * t3v.y : t1v.y * t2v.y * t3v.y;
+        if (iI == 3) *(float2*)(GC + 2 * icp) = make_float2(Gp[0] * t3v.x, Gp[1] * t3v.y);  // gamma_last
         char* QG = R_OP + K::OFF_QG + item_off;
         // (K o gamma)^T and (K o rho)^T rows of the item's two channels, positions 16 iI ..
         // 16 iI + 15: written as 8-position row segments

@@ -43,10 +43,15 @@ __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ q,
   const int cq = tid % TPR;        // column quad
   const int rg = tid / TPR;        // row group
 
-  float4* S = reinterpret_cast<float4*>(state + bh * (size_t)DK * DV);
+  // the state streams through once per step: nontemporal loads and stores keep it from
+  // displacing cached lines it will not reuse
+  f32x4_t* S = reinterpret_cast<f32x4_t*>(state + bh * (size_t)DK * DV);
   float4 s[RPT];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) s[i] = S[(size_t)(rg + RG * i) * TPR + cq];
+  for (int i = 0; i < RPT; ++i) {
+    const f32x4_t t = __builtin_nontemporal_load(&S[(size_t)(rg + RG * i) * TPR + cq]);
+    s[i] = make_float4(t[0], t[1], t[2], t[3]);
+  }
 
   float qk_part = 0.f;
   if (tid < DK) {
@@ -106,7 +111,8 @@ __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ q,
   for (int i = 0; i < RPT; ++i) {
     const float kk = s_k[rg + RG * i];
     s[i].x += kk * d[0]; s[i].y += kk * d[1]; s[i].z += kk * d[2]; s[i].w += kk * d[3];
-    S[(size_t)(rg + RG * i) * TPR + cq] = s[i];
+    const f32x4_t t = {s[i].x, s[i].y, s[i].z, s[i].w};
+    __builtin_nontemporal_store(t, &S[(size_t)(rg + RG * i) * TPR + cq]);
   }
   if (rg == 0) {
 #pragma unroll
