@@ -10,6 +10,8 @@
 //   S    <- diag(gamma_last) S + (K o rho)^T Delta
 // Records and v tiles move from global memory straight into LDS (16-byte DMA per lane);
 // with two LDS buffers the next chunk streams in while the current one computes.
+#include <stdlib.h>
+
 #include "kda_common.h"
 #include "kda_internal.h"
 #include "kda_record.h"
@@ -371,10 +373,40 @@ static hipError_t launch_state_t(const ChunkArgs& a, const void* ws) {
   return hipGetLastError();
 }
 
+// KDA_STATE_VT=16|32|64 pins the state pass's value-tile width (tuning aid)
+static int state_vt_override() {
+  static const int v = [] {
+    const char* e = getenv("KDA_STATE_VT");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
+}
+
+// Value-tile width of the state pass: each workgroup walks the whole chunk chain of one
+// (b, h, tile), so with few (b, h) pairs narrower tiles put more compute units on the
+// chains (every tile reads the whole record; the extra reads hit in L2).
+static int pick_state_vt(const ChunkArgs& a) {
+  const int o = state_vt_override();
+  if (o == 16 || o == 32 || o == 64) return o <= a.dv ? o : a.dv;
+  const long bh = (long)a.B * a.H;
+  if (bh * (a.dv / 64) >= 256) return 64;
+  if (bh * (a.dv / 32) >= 256) return 32;
+  return 16;
+}
+
+template <typename T, int DK>
+static hipError_t launch_state_vt(const ChunkArgs& a, const void* ws) {
+  switch (pick_state_vt(a)) {
+    case 16: return launch_state_t<T, DK, 16>(a, ws);
+    case 32: return launch_state_t<T, DK, 32>(a, ws);
+    default: return launch_state_t<T, DK, 64>(a, ws);
+  }
+}
+
 hipError_t launch_state(const ChunkArgs& a, const void* ws) {
   if (a.B * a.H == 0) return hipSuccess;
-  if (!a.bf16) return a.dk == 64 && a.dv == 64 ? launch_state_t<float, 64, 64>(a, ws) : hipErrorInvalidValue;
-  return a.dk == 64 ? launch_state_t<bf16_t, 64, 64>(a, ws) : launch_state_t<bf16_t, 128, 64>(a, ws);
+  if (!a.bf16) return a.dk == 64 && a.dv == 64 ? launch_state_vt<float, 64>(a, ws) : hipErrorInvalidValue;
+  return a.dk == 64 ? launch_state_vt<bf16_t, 64>(a, ws) : launch_state_vt<bf16_t, 128>(a, ws);
 }
 
 }  // namespace kda

@@ -77,6 +77,14 @@ def test_fp32_ckda_edges(path):
     _check(inp, inp.S0, label="f32-ckda", path=path)
 
 
+@pytest.mark.parametrize("B,H", [(1, 2), (4, 25), (8, 16)])
+def test_two_pass_value_tile_widths(B, H):
+    """The state pass narrows its value tiles to 32 or 16 columns when B*H is small:
+    (1, 2) and (4, 25) and (8, 16) run 16-, 32- and 64-column tiles."""
+    inp = make(B, 130, H, 128, 128, "bf16", "ckda", False, seed=50 + B + H)
+    _check(inp, inp.S0, label=f"tiles-B{B}H{H}", path="twopass")
+
+
 def test_gates_only_signs_and_zeros():
     """alpha entirely in {-1, 0, +1} and beta in {0, 2}: exact zero / sign handling."""
     inp = make(1, 256, 2, 128, 128, "bf16", "ckda", False, seed=11)
