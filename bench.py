@@ -46,6 +46,8 @@ PMC_FILES = {
                     ["kda_state.hip", "kda_record.h", "kda_common.h"]),
     "chunk_fused": (os.path.join(ROOT, "profiles", "chunk_fused_kda_prefill_8k_counters.md"),
                     ["kda_chunk.hip", "kda_common.h"]),
+    "decode": (os.path.join(ROOT, "profiles", "decode_ckda_decode_b256_counters.md"),
+               ["kda_decode.hip", "kda_common.h"]),
 }
 RECORD_PAYLOAD = {128: 3 * 64 * 128 * 2 + 2 * 64 * 64 * 2 + 128 * 4,   # -W, QG, KRT, A, M~ (bf16), gamma (fp32)
                   64: 3 * 64 * 64 * 2 + 2 * 64 * 64 * 2 + 64 * 4}
@@ -250,6 +252,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the decode measurement (for profiling the decode kernel)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -273,6 +277,13 @@ def main():
         log("[bench] calibration copy: 1 GiB read, 1 GiB written")
         del src, dst
 
+    if args.decode_only:
+        wd, msd = bench_decode(max(1, args.steps // 10), log)
+        db = decode_bytes(wd.B, wd.H, wd.dk, wd.dv)
+        gbs = db / (msd * 1e-3) / 1e9
+        print(json.dumps({"workload": "ckda_decode_b256", "ms_per_step": msd, "value": gbs, "unit": "GB/s",
+                          "frac": gbs / HBM_PEAK_GBS, "bytes_per_step": db}), flush=True)
+        return
     w, res, inp = bench_prefill("kda_prefill_8k", args.steps, args.warmup, log)
     ms = res["ms"]
     tokens = w.B * w.T
@@ -327,7 +338,7 @@ def main():
         out["decode"] = {"workload": "ckda_decode_b256", "B": wd.B, "H": wd.H, "dk": wd.dk, "dv": wd.dv,
                          "steps": wd.decode_steps, "ms_per_step": msd, "value": gbs, "unit": "GB/s",
                          "tokens_per_s": wd.B / (msd * 1e-3), "frac": gbs / HBM_PEAK_GBS,
-                         "bytes_per_step": db}
+                         "bytes_per_step": db, "traffic": stored_traffic("decode")}
         log(f"[bench] decode: {msd * 1e3:.1f} us/step, {gbs:.1f} GB/s")
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, log)
