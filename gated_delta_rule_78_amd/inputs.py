@@ -15,6 +15,10 @@ patterns, which both sides widen exactly):
 * CKDA gates  : alpha = tanh(2x) in [-1, 1], beta = 2 * sigmoid(2x) in [0, 2];
   then a Bernoulli(0.05) mask over alpha entries sets each masked entry to a
   value drawn uniformly from {-1, 0, +1} (+0.0 for zero).
+* GDN-2 gates : alpha as KDA; an erase gate b = sigmoid(x) per key channel and a
+  write gate w = sigmoid(x) per value channel, x ~ N(0, 1) (two more streams,
+  children 7 and 8 of the same SeedSequence, so the other tensors do not change);
+  beta is drawn as for KDA and unused by GDN-2.
 * S0     ~ N(0, std 0.02) in fp32, or zeros.
 
 The five named workloads mirror the shapes the method is evaluated on: a tiny
@@ -54,6 +58,7 @@ WORKLOADS = {
     "ckda_prefill_128k": Workload("ckda_prefill_128k", 1, 131072, 16, 128, 128, "bf16", "ckda", False, index=3),
     "ckda_decode_b256": Workload("ckda_decode_b256", 256, 1, 32, 128, 128, "bf16", "ckda", False,
                                  decode_steps=64, index=4),
+    "gdn2_prefill_8k": Workload("gdn2_prefill_8k", 4, 8192, 32, 128, 128, "bf16", "gdn2", False, index=5),
 }
 
 
@@ -93,6 +98,8 @@ class Inputs:
     S0: np.ndarray | None       # fp32 [B, H, dk, dv] or None (zeros)
     dtype: str                  # "bf16" (uint16 bit arrays) or "f32"
     meta: dict = field(default_factory=dict)
+    erase: np.ndarray | None = None   # GDN-2 erase gate [.., dk]
+    write: np.ndarray | None = None   # GDN-2 write gate [.., dv]
 
 
 def make(B, T, H, dk, dv, dtype="bf16", gates="kda", zero_s0=False, seed=BASE_SEED,
@@ -102,8 +109,8 @@ def make(B, T, H, dk, dv, dtype="bf16", gates="kda", zero_s0=False, seed=BASE_SE
     ``lead`` (optional) is an extra leading dimension (decode steps): tensors are
     then [lead, B, H, d] and beta [lead, B, H]; otherwise [B, T, H, d], [B, T, H].
     """
-    ss = np.random.SeedSequence(seed).spawn(7)
-    rq, rk, rv, ra, rb, rs, rm = [np.random.default_rng(s) for s in ss]
+    ss = np.random.SeedSequence(seed).spawn(9)
+    rq, rk, rv, ra, rb, rs, rm, re, rw = [np.random.default_rng(s) for s in ss]
     shp = (lead, B, H) if lead else (B, T, H)
     f32 = np.float32
     q = _l2n(rq.standard_normal(shp + (dk,), dtype=f32))
@@ -111,9 +118,13 @@ def make(B, T, H, dk, dv, dtype="bf16", gates="kda", zero_s0=False, seed=BASE_SE
     v = rv.standard_normal(shp + (dv,), dtype=f32)
     xa = ra.standard_normal(shp + (dk,), dtype=f32)
     xb = rb.standard_normal(shp, dtype=f32)
-    if gates == "kda":
+    erase = write = None
+    if gates in ("kda", "gdn2"):
         alpha = np.exp(-0.1 * _softplus(xa)).astype(f32)
         beta = _sigmoid(xb)
+        if gates == "gdn2":
+            erase = _sigmoid(re.standard_normal(shp + (dk,), dtype=f32))
+            write = _sigmoid(rw.standard_normal(shp + (dv,), dtype=f32))
     elif gates == "ckda":
         alpha = np.tanh(2.0 * xa).astype(f32)
         beta = (2.0 * _sigmoid(2.0 * xb)).astype(f32)
@@ -126,10 +137,12 @@ def make(B, T, H, dk, dv, dtype="bf16", gates="kda", zero_s0=False, seed=BASE_SE
     S0 = None if zero_s0 else (0.02 * rs.standard_normal((B, H, dk, dv), dtype=f32)).astype(f32)
     if dtype == "bf16":
         q, k, v, alpha, beta = (bf16_bits(x) for x in (q, k, v, alpha, beta))
+        if erase is not None:
+            erase, write = bf16_bits(erase), bf16_bits(write)
     elif dtype != "f32":
         raise ValueError(dtype)
     return Inputs(q, k, v, alpha, beta, S0, dtype,
-                  dict(B=B, T=T, H=H, dk=dk, dv=dv, gates=gates, seed=seed, lead=lead))
+                  dict(B=B, T=T, H=H, dk=dk, dv=dv, gates=gates, seed=seed, lead=lead), erase, write)
 
 
 def make_workload(name: str, T: int | None = None, B: int | None = None, H: int | None = None,

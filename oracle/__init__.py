@@ -51,7 +51,7 @@ def load(path: str = _LIB_PATH):
     global _lib
     if path == _LIB_PATH and _lib is not None:
         return _lib
-    if not os.path.exists(path):
+    if not os.path.exists(path) or (path == _LIB_PATH and os.path.getmtime(path) < os.path.getmtime(_SRC)):
         build(out=path)
     lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
@@ -60,6 +60,10 @@ def load(path: str = _LIB_PATH):
     lib.kda_oracle_fwd.restype = I
     lib.kda_oracle_decode.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, I, I]
     lib.kda_oracle_decode.restype = I
+    lib.kda_oracle_fwd_gdn2.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, I, I, I]
+    lib.kda_oracle_fwd_gdn2.restype = I
+    lib.kda_oracle_decode_gdn2.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P, I, I]
+    lib.kda_oracle_decode_gdn2.restype = I
     if path == _LIB_PATH:
         _lib = lib
     return lib
@@ -128,4 +132,50 @@ def decode(q, k, v, alpha, beta, state, heads=None, nthreads=0, lib=None):
                                _ptr(sel), n_sel, int(nthreads))
     if rc != 0:
         raise RuntimeError("kda_oracle_decode failed")
+    return o
+
+
+def fwd_gdn2(q, k, v, alpha, erase, write, S0=None, heads=None, col_block=0, nthreads=0, lib=None,
+             want_o=True):
+    """Gated DeltaNet-2 recurrence over whole sequences: as fwd, with beta replaced by
+    the erase gate [B, T, H, dk] and the write gate [B, T, H, dv]."""
+    lib = lib or load()
+    arrs = [np.ascontiguousarray(x) for x in (q, k, v, alpha, erase, write)]
+    code = _dtype_code(arrs[0])
+    for a in arrs[1:]:
+        if _dtype_code(a) != code:
+            raise TypeError("all oracle inputs must share one dtype")
+    B, T, H, dk = arrs[0].shape
+    dv = arrs[2].shape[-1]
+    if arrs[4].shape != arrs[0].shape or arrs[5].shape != arrs[2].shape:
+        raise ValueError("erase gate [B,T,H,dk], write gate [B,T,H,dv]")
+    sel = None if heads is None else np.ascontiguousarray(np.asarray(heads, dtype=np.int32))
+    n_sel = B * H if sel is None else len(sel)
+    S0d = None if S0 is None else np.ascontiguousarray(np.asarray(S0, dtype=np.float64)).reshape(n_sel, dk, dv)
+    o = np.empty((n_sel, T, dv), np.float64) if want_o else None
+    S = np.empty((n_sel, dk, dv), np.float64)
+    rc = lib.kda_oracle_fwd_gdn2(B, T, H, dk, dv, code, *[_ptr(a) for a in arrs], _ptr(S0d),
+                                 _ptr(o), _ptr(S), _ptr(sel), n_sel, int(col_block), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_fwd_gdn2 failed")
+    return o, S
+
+
+def decode_gdn2(q, k, v, alpha, erase, write, state, heads=None, nthreads=0, lib=None):
+    """One Gated DeltaNet-2 decode step; ``state`` ([n_sel, dk, dv] fp64) in place.
+    erase [B, H, dk], write [B, H, dv].  Returns o [n_sel, dv]."""
+    lib = lib or load()
+    arrs = [np.ascontiguousarray(x) for x in (q, k, v, alpha, erase, write)]
+    code = _dtype_code(arrs[0])
+    B, H, dk = arrs[0].shape
+    dv = arrs[2].shape[-1]
+    sel = None if heads is None else np.ascontiguousarray(np.asarray(heads, dtype=np.int32))
+    n_sel = B * H if sel is None else len(sel)
+    if state.dtype != np.float64 or not state.flags.c_contiguous or state.shape != (n_sel, dk, dv):
+        raise TypeError("state must be a C-contiguous float64 array of shape [n_sel, dk, dv]")
+    o = np.empty((n_sel, dv), np.float64)
+    rc = lib.kda_oracle_decode_gdn2(B, H, dk, dv, code, *[_ptr(a) for a in arrs], _ptr(state), _ptr(o),
+                                    _ptr(sel), n_sel, int(nthreads))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_decode_gdn2 failed")
     return o

@@ -45,6 +45,19 @@
  * Parity pins: the recurrence (fwd and decode) is pinned by the CPU tests
  * against explicit transition-matrix products, the plain delta rule, pure
  * decay, non-expansiveness, norm preservation and the d=2 rotation.
+ *
+ * Gated DeltaNet-2 ("ملخص تقني: Gated DeltaNet-2", section 1) splits the scalar
+ * beta into an erase gate b_t per key channel and a write gate w_t per value
+ * channel:
+ *
+ *   S_t = (I - k_t (b_t o k_t)^T) D_t S_{t-1} + k_t (w_t o v_t)^T,  D_t = Diag(alpha_t)
+ *
+ * (o: elementwise product), with the same readout.  kda_oracle_fwd_gdn2 and
+ * kda_oracle_decode_gdn2 below run that update one token at a time; the CPU
+ * tests pin them against explicit transition-matrix products, against the KDA
+ * functions when b = w = beta (the reduction the page states), against the
+ * no-erase case (b = 0: a decayed sum of writes) and against a hand-worked
+ * two-token case.
  */
 #include <stdint.h>
 #include <stdlib.h>
@@ -207,6 +220,147 @@ int kda_oracle_decode(int B, int H, int dk, int dv, int dtype,
             const double bt = load_elem(beta, dtype, (size_t)bh);
             kda_token(state + (size_t)s * dk * dv, dk, dv, 0, dv, qq, kk, vv, aa, bt, u,
                       o_out ? oo : NULL);
+            if (o_out)
+                for (int j = 0; j < dv; ++j) o_out[(size_t)s * dv + j] = oo[j];
+        }
+        free(buf);
+    }
+    return err ? -1 : 0;
+}
+
+/* One Gated DeltaNet-2 token on columns [j0, j1): the read goes through the erase
+ * gate on the key side, the write through the write gate on the value side. */
+static void gdn2_token(double* S, int dk, int dv, int j0, int j1,
+                       const double* q, const double* k, const double* v,
+                       const double* a, const double* eg, const double* wg,
+                       double* u, double* o) {
+    /* 1. decay: S <- D S */
+    for (int i = 0; i < dk; ++i)
+        for (int j = j0; j < j1; ++j) S[(size_t)i * dv + j] *= a[i];
+    /* 2. read through the erase gate: u = S^T (b o k) */
+    for (int j = j0; j < j1; ++j) u[j] = 0.0;
+    for (int i = 0; i < dk; ++i) {
+        const double e = eg[i] * k[i];
+        for (int j = j0; j < j1; ++j) u[j] += e * S[(size_t)i * dv + j];
+    }
+    /* 3. erase + write: S <- S + k ((w o v) - u)^T
+     *    (= (I - k (b o k)^T) D S + k (w o v)^T with D S from step 1) */
+    for (int i = 0; i < dk; ++i)
+        for (int j = j0; j < j1; ++j)
+            S[(size_t)i * dv + j] += k[i] * (wg[j] * v[j] - u[j]);
+    /* 4. readout: o = S^T q */
+    if (o) {
+        for (int j = j0; j < j1; ++j) o[j] = 0.0;
+        for (int i = 0; i < dk; ++i)
+            for (int j = j0; j < j1; ++j) o[j] += q[i] * S[(size_t)i * dv + j];
+    }
+}
+
+/*
+ * Gated DeltaNet-2 forward over whole sequences.  As kda_oracle_fwd, with the
+ * scalar beta replaced by
+ *   erase : [B, T, H, dk]  erase gate b (dtype)
+ *   write : [B, T, H, dv]  write gate w (dtype)
+ */
+int kda_oracle_fwd_gdn2(int B, int T, int H, int dk, int dv, int dtype,
+                        const void* q, const void* k, const void* v,
+                        const void* alpha, const void* erase, const void* write,
+                        const double* S0, double* o_out, double* S_out,
+                        const int* sel, int n_sel, int col_block, int nthreads) {
+    if (B < 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+    if (dtype < ORC_BF16 || dtype > ORC_F64) return -1;
+    if (!sel) n_sel = B * H;
+    if (n_sel < 0) return -1;
+    if (col_block <= 0 || col_block > dv) col_block = dv;
+    const int nblk = (dv + col_block - 1) / col_block;
+    const long n_items = (long)n_sel * nblk;
+    int err = 0;
+
+#pragma omp parallel num_threads(pick_threads(nthreads))
+    {
+        double* S = (double*)malloc(sizeof(double) * (size_t)dk * dv);
+        double* buf = (double*)malloc(sizeof(double) * (size_t)(4 * dk + 4 * dv));
+        if (!S || !buf) {
+#pragma omp atomic write
+            err = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (long it = 0; it < n_items; ++it) {
+            if (!S || !buf) continue;
+            const int s = (int)(it / nblk);
+            const int j0 = (int)(it % nblk) * col_block;
+            const int j1 = j0 + col_block < dv ? j0 + col_block : dv;
+            const int bh = sel ? sel[s] : s;
+            const int b = bh / H, h = bh % H;
+            double *qq = buf, *kk = buf + dk, *aa = buf + 2 * dk, *ee = buf + 3 * dk;
+            double *vv = buf + 4 * dk, *ww = vv + dv, *u = ww + dv, *oo = u + dv;
+            for (int i = 0; i < dk; ++i)
+                for (int j = j0; j < j1; ++j)
+                    S[(size_t)i * dv + j] = S0 ? S0[((size_t)s * dk + i) * dv + j] : 0.0;
+            for (int t = 0; t < T; ++t) {
+                const size_t tok = ((size_t)b * T + t) * H + h;
+                for (int i = 0; i < dk; ++i) {
+                    qq[i] = load_elem(q, dtype, tok * dk + i);
+                    kk[i] = load_elem(k, dtype, tok * dk + i);
+                    aa[i] = load_elem(alpha, dtype, tok * dk + i);
+                    ee[i] = load_elem(erase, dtype, tok * dk + i);
+                }
+                for (int j = j0; j < j1; ++j) {
+                    vv[j] = load_elem(v, dtype, tok * dv + j);
+                    ww[j] = load_elem(write, dtype, tok * dv + j);
+                }
+                gdn2_token(S, dk, dv, j0, j1, qq, kk, vv, aa, ee, ww, u, o_out ? oo : NULL);
+                if (o_out)
+                    for (int j = j0; j < j1; ++j)
+                        o_out[((size_t)s * T + t) * dv + j] = oo[j];
+            }
+            if (S_out)
+                for (int i = 0; i < dk; ++i)
+                    for (int j = j0; j < j1; ++j)
+                        S_out[((size_t)s * dk + i) * dv + j] = S[(size_t)i * dv + j];
+        }
+        free(S);
+        free(buf);
+    }
+    return err ? -1 : 0;
+}
+
+/* One Gated DeltaNet-2 decode step: erase [B, H, dk], write [B, H, dv]. */
+int kda_oracle_decode_gdn2(int B, int H, int dk, int dv, int dtype,
+                           const void* q, const void* k, const void* v,
+                           const void* alpha, const void* erase, const void* write,
+                           double* state, double* o_out, const int* sel, int n_sel,
+                           int nthreads) {
+    if (B < 0 || H <= 0 || dk <= 0 || dv <= 0 || !state) return -1;
+    if (dtype < ORC_BF16 || dtype > ORC_F64) return -1;
+    if (!sel) n_sel = B * H;
+    if (n_sel < 0) return -1;
+    int err = 0;
+#pragma omp parallel num_threads(pick_threads(nthreads))
+    {
+        double* buf = (double*)malloc(sizeof(double) * (size_t)(4 * dk + 4 * dv));
+        if (!buf) {
+#pragma omp atomic write
+            err = 1;
+        }
+#pragma omp for schedule(dynamic, 4)
+        for (int s = 0; s < n_sel; ++s) {
+            if (!buf) continue;
+            const int bh = sel ? sel[s] : s;
+            double *qq = buf, *kk = buf + dk, *aa = buf + 2 * dk, *ee = buf + 3 * dk;
+            double *vv = buf + 4 * dk, *ww = vv + dv, *u = ww + dv, *oo = u + dv;
+            for (int i = 0; i < dk; ++i) {
+                qq[i] = load_elem(q, dtype, (size_t)bh * dk + i);
+                kk[i] = load_elem(k, dtype, (size_t)bh * dk + i);
+                aa[i] = load_elem(alpha, dtype, (size_t)bh * dk + i);
+                ee[i] = load_elem(erase, dtype, (size_t)bh * dk + i);
+            }
+            for (int j = 0; j < dv; ++j) {
+                vv[j] = load_elem(v, dtype, (size_t)bh * dv + j);
+                ww[j] = load_elem(write, dtype, (size_t)bh * dv + j);
+            }
+            gdn2_token(state + (size_t)s * dk * dv, dk, dv, 0, dv, qq, kk, vv, aa, ee, ww, u,
+                       o_out ? oo : NULL);
             if (o_out)
                 for (int j = 0; j < dv; ++j) o_out[(size_t)s * dv + j] = oo[j];
         }

@@ -109,3 +109,60 @@ def test_mutant_is_caught(name, src_text, monkeypatch, tmp_path):
     lib = _build_variant(text, str(tmp_path), name)
     caught = _caught(lib, monkeypatch)
     assert caught, f"mutant {name} passed every pin"
+
+
+# ---- the Gated DeltaNet-2 token code: plausible mistakes, each must fail a GDN-2 pin
+import test_oracle_gdn2 as gpins  # noqa: E402
+
+MUTANTS_GDN2 = {
+    "gdn2_erase_gate_dropped": ("const double e = eg[i] * k[i];", "const double e = k[i];"),
+    "gdn2_write_gate_dropped": ("(wg[j] * v[j] - u[j])", "(v[j] - u[j])"),
+    "gdn2_erase_sign": ("(wg[j] * v[j] - u[j])", "(wg[j] * v[j] + u[j])"),
+    "gdn2_gates_swapped_sides": ("+= k[i] * (wg[j] * v[j] - u[j]);", "+= eg[i] * k[i] * (v[j] - u[j]);"),
+    "gdn2_write_key_is_erase_key": ("+= k[i] * (wg[j] * v[j] - u[j]);", "+= eg[i] * k[i] * (wg[j] * v[j] - u[j]);"),
+    "gdn2_decay_dropped": ("    /* 1. decay: S <- D S */\n    for (int i = 0; i < dk; ++i)\n"
+                           "        for (int j = j0; j < j1; ++j) S[(size_t)i * dv + j] *= a[i];",
+                           "    /* 1. decay: S <- D S */"),
+    "gdn2_erase_channel_shifted": ("ee[i] = load_elem(erase, dtype, tok * dk + i);",
+                                   "ee[i] = load_elem(erase, dtype, tok * dk + (i + 1) % dk);"),
+    "gdn2_write_channel_shifted": ("ww[j] = load_elem(write, dtype, tok * dv + j);",
+                                   "ww[j] = load_elem(write, dtype, tok * dv + (j + 1) % dv);"),
+    "gdn2_readout_with_k": ("o[j] += q[i] * S[(size_t)i * dv + j];\n    }\n}\n\n/*\n * Gated DeltaNet-2 forward",
+                            "o[j] += k[i] * S[(size_t)i * dv + j];\n    }\n}\n\n/*\n * Gated DeltaNet-2 forward"),
+}
+
+PIN_TESTS_GDN2 = [
+    ("hand", lambda: gpins.test_gdn2_hand_derived_two_tokens()),
+    ("explicit", lambda: gpins.test_gdn2_explicit_transition_products(3, 2, 32)),
+    ("tied_kda", lambda: gpins.test_gdn2_with_tied_gates_is_kda()),
+    ("readback", lambda: gpins.test_gdn2_full_erase_reads_back_the_write()),
+    ("no_erase", lambda: gpins.test_gdn2_without_erase_is_a_decayed_sum_of_writes()),
+]
+
+
+def _caught_gdn2(lib, monkeypatch):
+    failed = []
+    with monkeypatch.context() as m:
+        real = {n: getattr(oracle, n) for n in ("fwd", "decode", "fwd_gdn2", "decode_gdn2")}
+        for n, f in real.items():
+            m.setattr(oracle, n, (lambda f: lambda *a, **kw: f(*a, lib=lib, **kw))(f))
+        for name, fn in PIN_TESTS_GDN2:
+            try:
+                with np.errstate(all="ignore"):
+                    fn()
+            except AssertionError:
+                failed.append(name)
+    return failed
+
+
+def test_unmodified_source_passes_gdn2_pins(src_text, monkeypatch, tmp_path):
+    lib = _build_variant(src_text, str(tmp_path), "clean_gdn2")
+    assert _caught_gdn2(lib, monkeypatch) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS_GDN2))
+def test_gdn2_mutant_is_caught(name, src_text, monkeypatch, tmp_path):
+    old, new = MUTANTS_GDN2[name]
+    assert src_text.count(old) == 1, f"mutation anchor for {name} not unique"
+    lib = _build_variant(src_text.replace(old, new), str(tmp_path), name)
+    assert _caught_gdn2(lib, monkeypatch), f"mutant {name} passed every GDN-2 pin"
