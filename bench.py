@@ -10,6 +10,7 @@ whole-job prefill throughput in tokens/s (a token is one position across all H
 heads).  The same run also measures, outside the timed steps:
   * the CKDA prefill (same shape, gates in [-1, 1] and beta in [0, 2]);
   * the long-context CKDA prefill (B=1, H=16, T=131072);
+  * the Gated DeltaNet-2 prefill (decoupled erase / write gates, B=4, H=32, T=8192);
   * the batched decode step (B=256, H=32, d=128, 64 consecutive steps on a
     512 MiB fp32 state), reported as state GB/s against the HBM peak;
   * the fp64 CPU oracle on a bounded sample of the prefill workload.
@@ -160,7 +161,17 @@ def bench_prefill(name, steps, warmup, log):
     stream = torch.cuda.current_stream()
     path = kda.pick_path(w.B, w.T, w.H, w.dk, w.dv)
     res = {"path": path}
-    if path == "twopass":
+    if w.gates == "gdn2":
+        # Gated DeltaNet-2: erase / write gates in place of beta, two-pass path
+        def dev(x):
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to("cuda").view(torch.bfloat16)
+        e, wg = dev(inp.erase), dev(inp.write)
+        ws = torch.empty(kda.workspace_size(w.B, w.T, w.H, w.dk, w.dv), dtype=torch.uint8, device="cuda")
+        ms = timed(lambda: kda.gdn2_chunk_fwd(q, k, v, a, e, wg, initial_state=s0, out=o, final_state=sT,
+                                              workspace=ws), steps, warmup, stream)
+        res.update(path="gdn2-twopass", ms=ms, kernels={"gdn2_chunk_fwd": ms})
+        del ws, e, wg
+    elif path == "twopass":
         ws = torch.empty(kda.workspace_size(w.B, w.T, w.H, w.dk, w.dv), dtype=torch.uint8, device="cuda")
         ms, t1, t2 = timed_split(lambda: kda.chunk_records(q, k, a, b, workspace=ws, dv=w.dv),
                                  lambda: kda.chunk_apply_records(ws, v, s0, out=o, final_state=sT, dk=w.dk),
@@ -324,7 +335,8 @@ def main():
     log(f"[bench] kda prefill ({res['path']}): {ms:.3f} ms/step, {value:.4g} tokens/s; "
         + ", ".join(f"{k2} {v2:.3f} ms" for k2, v2 in res["kernels"].items()))
     if not args.no_extras:
-        for name, steps in (("ckda_prefill_8k", args.steps), ("ckda_prefill_128k", max(2, args.steps // 4))):
+        for name, steps in (("ckda_prefill_8k", args.steps), ("ckda_prefill_128k", max(2, args.steps // 4)),
+                            ("gdn2_prefill_8k", args.steps)):
             w3, r3, _ = bench_prefill(name, steps, min(args.warmup, 2), log)
             ms3 = r3["ms"]
             out[name] = {"value": w3.B * w3.T / (ms3 * 1e-3), "unit": "tokens/s", "ms_per_step": ms3,

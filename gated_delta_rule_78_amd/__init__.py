@@ -15,6 +15,7 @@ import ctypes
 import os
 
 __all__ = ["chunk_fwd", "chunk_records", "chunk_apply_records", "chunk_fwd_debug", "decode_step",
+           "gdn2_chunk_fwd", "gdn2_decode_step",
            "workspace_size", "pick_path", "lib", "version", "status_string",
            "LIB_PATH", "KdaError", "Shape", "BF16", "F32"]
 
@@ -59,6 +60,10 @@ def lib() -> ctypes.CDLL:
         L.kda_chunk_apply_records.restype = ctypes.c_int
         L.kda_decode_step.argtypes = [SP, P, P, P, P, P, P, P, P]
         L.kda_decode_step.restype = ctypes.c_int
+        L.kda_gdn2_chunk_fwd.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.kda_gdn2_chunk_fwd.restype = ctypes.c_int
+        L.kda_gdn2_decode_step.argtypes = [SP, P, P, P, P, P, P, P, P, P]
+        L.kda_gdn2_decode_step.restype = ctypes.c_int
         L.kda_status_string.argtypes = [ctypes.c_int]
         L.kda_status_string.restype = ctypes.c_char_p
         L.kda_version.argtypes = []
@@ -265,4 +270,67 @@ def decode_step(q, k, v, alpha, beta, state, out=None):
                                _ptr(state), _ptr(out), _stream(dev))
     if rc != 0:
         raise KdaError(rc, "kda_decode_step")
+    return out
+
+
+def gdn2_chunk_fwd(q, k, v, alpha, erase, write, initial_state=None, out=None, final_state=None, want_final=True,
+                   workspace=None):
+    """Gated DeltaNet-2 chunk forward: as chunk_fwd with beta replaced by the erase gate
+    [B,T,H,dk] and the write gate [B,T,H,dv] (two-pass path; the workspace is allocated
+    here when omitted).  Returns (o, final_state or None)."""
+    torch = _torch()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    code = _dtype_code(q)
+    for t, nm in ((k, "k"), (alpha, "alpha"), (v, "v"), (erase, "erase"), (write, "write")):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{nm} must have the dtype of q")
+    if k.shape != q.shape or alpha.shape != q.shape or erase.shape != q.shape or v.shape != (B, T, H, dv) \
+            or write.shape != v.shape:
+        raise ValueError("shapes: q, k, alpha, erase [B,T,H,dk]; v, write [B,T,H,dv]")
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    if final_state is None and want_final:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    for t, nm in ((initial_state, "initial_state"), (final_state, "final_state")):
+        if t is not None and (t.dtype != torch.float32 or t.shape != (B, H, dk, dv)):
+            raise ValueError(f"{nm} must be float32 [B,H,dk,dv]")
+    shape = Shape(B, T, H, dk, dv, 64, code)
+    need = int(lib().kda_chunk_fwd_workspace_size(ctypes.byref(shape)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check((q, k, v, alpha, erase, write, initial_state, out, final_state, workspace),
+           ("q", "k", "v", "alpha", "erase", "write", "initial_state", "out", "final_state", "workspace"), dev)
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = lib().kda_gdn2_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase),
+                                  _ptr(write), _ptr(initial_state), _ptr(out), _ptr(final_state), _ptr(workspace),
+                                  ctypes.c_size_t(nbytes), _stream(dev))
+    if rc != 0:
+        raise KdaError(rc, "kda_gdn2_chunk_fwd")
+    return out, final_state
+
+
+def gdn2_decode_step(q, k, v, alpha, erase, write, state, out=None):
+    """One Gated DeltaNet-2 token for every (b, h): q, k, alpha, erase [B,H,dk]; v, write
+    [B,H,dv]; state fp32 [B,H,dk,dv] updated in place.  Returns o [B,H,dv]."""
+    torch = _torch()
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    code = _dtype_code(q)
+    if k.shape != q.shape or alpha.shape != q.shape or erase.shape != q.shape or v.shape != (B, H, dv) \
+            or write.shape != v.shape:
+        raise ValueError("shapes: q, k, alpha, erase [B,H,dk]; v, write [B,H,dv]")
+    if state.dtype != torch.float32 or state.shape != (B, H, dk, dv):
+        raise ValueError("state must be float32 [B,H,dk,dv]")
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
+    _check((q, k, v, alpha, erase, write, state, out), ("q", "k", "v", "alpha", "erase", "write", "state", "out"),
+           dev)
+    shape = Shape(B, 1, H, dk, dv, 0, code)
+    rc = lib().kda_gdn2_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase),
+                                    _ptr(write), _ptr(state), _ptr(out), _stream(dev))
+    if rc != 0:
+        raise KdaError(rc, "kda_gdn2_decode_step")
     return out

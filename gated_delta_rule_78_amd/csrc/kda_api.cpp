@@ -74,9 +74,12 @@ struct ChunkPtrs {
   float* dbg;
   void* ws;
   size_t ws_bytes;
+  const void* erase = nullptr;  // Gated DeltaNet-2 gates
+  const void* write = nullptr;
 };
 
-enum : int { kNeedQKAB = 1, kNeedVO = 2, kNeedWS = 4 };
+// kNeedQKAB: q, k, alpha and beta (or, with kNeedG2, the erase gate in beta's place)
+enum : int { kNeedQKAB = 1, kNeedVO = 2, kNeedWS = 4, kNeedG2 = 8 };
 
 // Host-side checks shared by the chunk entry points (nothing touches the device).
 int validate_chunk(const kda_shape* shape, const ChunkPtrs& p, int need) {
@@ -87,24 +90,28 @@ int validate_chunk(const kda_shape* shape, const ChunkPtrs& p, int need) {
   if (s.dtype == KDA_F32 && (s.dk != 64 || s.dv != 64)) return KDA_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)s.B * s.T * s.H;
   const int64_t st_bytes = (int64_t)s.B * s.H * s.dk * s.dv * 4;
+  const bool g2 = (need & kNeedG2) != 0;
   if (rows > 0) {
-    if ((need & kNeedQKAB) && (!p.q || !p.k || !p.alpha || !p.beta)) return KDA_ERR_NULL;
-    if ((need & kNeedVO) && (!p.v || !p.o)) return KDA_ERR_NULL;
+    if ((need & kNeedQKAB) && (!p.q || !p.k || !p.alpha || (g2 ? !p.erase : !p.beta))) return KDA_ERR_NULL;
+    if ((need & kNeedVO) && (!p.v || !p.o || (g2 && !p.write))) return KDA_ERR_NULL;
   }
-  // q, k, v, alpha, o and the states move in 16-byte vectors; beta is read per element
-  const void* vec[] = {p.q, p.k, p.v, p.alpha, p.o, p.s0, p.sT, p.dbg};
+  // q, k, v, alpha, o, the gate tiles and the states move in 16-byte vectors; beta is
+  // read per element
+  const void* vec[] = {p.q, p.k, p.v, p.alpha, p.o, p.s0, p.sT, p.dbg, p.erase, p.write};
   for (const void* x : vec)
     if (x && misaligned(x)) return KDA_ERR_ALIGN;
   if (p.beta && misaligned(p.beta, es)) return KDA_ERR_ALIGN;
+  // inputs: [0..4] and the gate tiles may not overlap any output; [5] is the start state
   const Range in[] = {range_of(p.q, p.q ? rows * s.dk * es : 0),         range_of(p.k, p.k ? rows * s.dk * es : 0),
                       range_of(p.v, p.v ? rows * s.dv * es : 0),         range_of(p.alpha, p.alpha ? rows * s.dk * es : 0),
-                      range_of(p.beta, p.beta ? rows * es : 0),          range_of(p.s0, p.s0 ? st_bytes : 0)};
+                      range_of(p.beta, p.beta ? rows * es : 0),          range_of(p.s0, p.s0 ? st_bytes : 0),
+                      range_of(p.erase, p.erase ? rows * s.dk * es : 0), range_of(p.write, p.write ? rows * s.dv * es : 0)};
   const Range ro = range_of(p.o, p.o ? rows * s.dv * es : 0);
   const Range rs = range_of(p.sT, p.sT ? st_bytes : 0);
   for (const Range& r : in)
     if (overlap(ro, r)) return KDA_ERR_ALIAS;
-  for (int i = 0; i < 5; ++i)
-    if (overlap(rs, in[i])) return KDA_ERR_ALIAS;
+  for (int i = 0; i < 8; ++i)
+    if (i != 5 && overlap(rs, in[i])) return KDA_ERR_ALIAS;
   if (p.s0 != p.sT && overlap(rs, in[5])) return KDA_ERR_ALIAS;  // in place is allowed
   if (overlap(rs, ro)) return KDA_ERR_ALIAS;
   if (need & kNeedWS) {
@@ -121,8 +128,11 @@ int validate_chunk(const kda_shape* shape, const ChunkPtrs& p, int need) {
 }
 
 kda::ChunkArgs chunk_args(const kda_shape& s, const ChunkPtrs& p, void* stream) {
-  return kda::ChunkArgs{p.q, p.k, p.v, p.alpha, p.beta, p.s0, p.o, p.sT, p.dbg, s.B, s.T, s.H, s.dk, s.dv,
-                        s.dtype == KDA_BF16, stream, value_tile_override()};
+  kda::ChunkArgs a{p.q, p.k, p.v, p.alpha, p.beta, p.s0, p.o, p.sT, p.dbg, s.B, s.T, s.H, s.dk, s.dv,
+                   s.dtype == KDA_BF16, stream, value_tile_override()};
+  a.erase = p.erase;
+  a.write = p.write;
+  return a;
 }
 
 // pass 1 of the two-pass forward: every chunk's record, in parallel
@@ -216,30 +226,64 @@ int kda_chunk_fwd_debug(const kda_shape* shape, const void* q, const void* k, co
   return kda::launch_chunk(chunk_args(*shape, p, stream)) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
-int kda_decode_step(const kda_shape* shape, const void* q, const void* k, const void* v,
-                    const void* alpha, const void* beta, float* state, void* o, void* stream) {
+int kda_gdn2_chunk_fwd(const kda_shape* shape, const void* q, const void* k, const void* v, const void* alpha,
+                       const void* erase_gate, const void* write_gate, const float* initial_state, void* o,
+                       float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+  ChunkPtrs p{q, k, v, alpha, nullptr, initial_state, o, final_state, nullptr, workspace, workspace_bytes};
+  p.erase = erase_gate;
+  p.write = write_gate;
+  int rc = validate_chunk(shape, p, kNeedQKAB | kNeedVO | kNeedWS | kNeedG2);
+  if (rc) return rc;
+  rc = run_records(*shape, p, stream);
+  return rc ? rc : run_apply(*shape, p, stream);
+}
+
+static int decode_impl(const kda_shape* shape, const void* q, const void* k, const void* v, const void* alpha,
+                       const void* beta, const void* erase, const void* write, float* state, void* o,
+                       void* stream) {
   int es = 0;
   int rc = check_shape(shape, true, &es);
   if (rc) return rc;
   const kda_shape& s = *shape;
   const int64_t rows = (int64_t)s.B * s.H;
   if (rows > 0x7FFFFFFF) return KDA_ERR_SHAPE;
-  if (rows > 0 && (!q || !k || !v || !alpha || !beta || !o || !state)) return KDA_ERR_NULL;
+  const bool g2 = erase || write;
+  if (rows > 0 && (!q || !k || !v || !alpha || !o || !state || (g2 ? (!erase || !write) : !beta)))
+    return KDA_ERR_NULL;
   // the state moves in 16-byte vectors; the per-token vectors are read per element
   if (state && misaligned(state)) return KDA_ERR_ALIGN;
-  const void* ptrs[] = {q, k, v, alpha, beta, o};
+  const void* ptrs[] = {q, k, v, alpha, beta, o, erase, write};
   for (const void* p : ptrs)
     if (p && misaligned(p, es)) return KDA_ERR_ALIGN;
-  const Range in[] = {range_of(q, rows * s.dk * es), range_of(k, rows * s.dk * es),
-                      range_of(v, rows * s.dv * es), range_of(alpha, rows * s.dk * es),
-                      range_of(beta, rows * es)};
+  const Range in[] = {range_of(q, rows * s.dk * es),     range_of(k, rows * s.dk * es),
+                      range_of(v, rows * s.dv * es),     range_of(alpha, rows * s.dk * es),
+                      range_of(beta, beta ? rows * es : 0), range_of(erase, erase ? rows * s.dk * es : 0),
+                      range_of(write, write ? rows * s.dv * es : 0)};
   const Range ro = range_of(o, rows * s.dv * es);
   const Range rs = range_of(state, rows * s.dk * s.dv * 4);
   for (const Range& r : in)
     if (overlap(ro, r) || overlap(rs, r)) return KDA_ERR_ALIAS;
   if (overlap(ro, rs)) return KDA_ERR_ALIAS;
   kda::DecodeArgs a{q, k, v, alpha, beta, state, o, (int)rows, s.dk, s.dv, s.dtype == KDA_BF16, stream};
+  a.erase = erase;
+  a.write = write;
   return kda::launch_decode(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_gdn2_decode_step(const kda_shape* shape, const void* q, const void* k, const void* v, const void* alpha,
+                         const void* erase_gate, const void* write_gate, float* state, void* o, void* stream) {
+  if (!erase_gate || !write_gate) {
+    int es = 0;
+    int rc = check_shape(shape, true, &es);
+    if (rc) return rc;
+    if ((int64_t)shape->B * shape->H > 0) return KDA_ERR_NULL;
+  }
+  return decode_impl(shape, q, k, v, alpha, nullptr, erase_gate, write_gate, state, o, stream);
+}
+
+int kda_decode_step(const kda_shape* shape, const void* q, const void* k, const void* v,
+                    const void* alpha, const void* beta, float* state, void* o, void* stream) {
+  return decode_impl(shape, q, k, v, alpha, beta, nullptr, nullptr, state, o, stream);
 }
 
 }  // extern "C"

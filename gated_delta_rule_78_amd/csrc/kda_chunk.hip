@@ -199,12 +199,16 @@ __device__ __forceinline__ void mm4(f32x4_t& acc, const float (&a)[4], const flo
 // PREP = true : the parallel first pass of the two-pass forward: every workgroup takes a
 //               run of `cpw` chunks of one head and writes each chunk's record (-W, Q o gamma,
 //               (K o rho)^T, A~, M~, gamma_last) to `ws` for the state pass.
-template <typename T, int DK, int VT, bool PREP>
+// G2 = true (with PREP): Gated DeltaNet-2 records.  The erase gate b scales the key on
+//               the read side only, e = b o k: T_ij = sum_c e_ic k_jc r_ijc and W = M (E o gamma),
+//               with no beta (M~ = M); the write side (K o rho, A) keeps k.
+template <typename T, int DK, int VT, bool PREP, bool G2 = false>
 __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
     const void* __restrict__ gq, const void* __restrict__ gk, const void* __restrict__ gv,
     const void* __restrict__ galpha, const void* __restrict__ gbeta, const float* s0,
     void* __restrict__ go, float* sT, float* __restrict__ dbg, int Tlen, int H, int DV, int BH,
-    char* __restrict__ ws, int cpw) {
+    char* __restrict__ ws, int cpw, const void* __restrict__ gerase) {
+  static_assert(PREP || !G2, "the Gated DeltaNet-2 gates run on the two-pass path");
   using K = Cfg<T, DK, VT>;
   using R = Raw<T>;
   constexpr int ES = K::ES;
@@ -269,6 +273,10 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
   // at issue time.
   uint4 pq[K::VPT], pk[K::VPT], pa[K::VPT], pv[K::VPT_V];
   uint32_t pb = 0u;  // raw beta bits, converted when staged
+  // (G2) erase gate of this thread's gate item (16 rows x 2 channels), one chunk ahead
+  typename Raw<T>::type pe[G2 ? SUB : 1], er_raw[G2 ? SUB : 1];
+  const int item_g = K::SPLIT ? tid % K::NITEM : tid;
+  const bool item_ok = K::SPLIT ? (tid < 2 * K::NITEM) : (tid < K::NITEM);
   auto issue_qka = [&](int c) {
     const int t0 = c * C;
 #pragma unroll
@@ -280,9 +288,14 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
       pk[i] = *(const uint4*)((const char*)gk + off);
       pa[i] = *(const uint4*)((const char*)galpha + off);
     }
-    {
+    if constexpr (!G2) {
       const size_t ib = row_base(min(t0 + (tid & (C - 1)), Tlen - 1));
       pb = ES == 2 ? (uint32_t)((const uint16_t*)gbeta)[ib] : ((const uint32_t*)gbeta)[ib];
+    } else if (item_ok) {
+      const int bI = item_g / (DK / 2), cp = item_g % (DK / 2);
+#pragma unroll
+      for (int m = 0; m < SUB; ++m)
+        pe[m] = R::ld((const char*)gerase + row_base(min(t0 + SUB * bI + m, Tlen - 1)) * DK * ES + 2 * cp * ES);
     }
   };
   auto issue_v = [&](int c) {
@@ -326,7 +339,11 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
       *(uint4*)(R_IN + 1 * C * K::RS_DK + off) = ok ? pk[i] : make_uint4(0, 0, 0, 0);
       *(uint4*)(R_IN + 2 * C * K::RS_DK + off) = ok ? pa[i] : make_uint4(one, one, one, one);
     }
-    if (tid < C) BETA[tid] = (t0 + tid < Tlen) ? __uint_as_float(ES == 2 ? pb << 16 : pb) : 0.f;
+    if (tid < C) BETA[tid] = (t0 + tid < Tlen) ? (G2 ? 1.f : __uint_as_float(ES == 2 ? pb << 16 : pb)) : 0.f;
+    if constexpr (G2) {
+#pragma unroll
+      for (int m = 0; m < SUB; ++m) er_raw[m] = pe[m];
+    }
     __syncthreads();
     if (chunk + 1 < c_end) issue_qka(chunk + 1);
 
@@ -337,6 +354,16 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
     // item registers: alpha (fp32), q and k (packed), loaded in one batch per phase
     typename R::type qr[SUB], kr_raw[SUB];
     float al[SUB][2];
+    // the key as the erase side reads it: k (KDA), b o k (Gated DeltaNet-2)
+    auto read_key = [&](int m, float& e0, float& e1) {
+      R::unpack(kr_raw[m], e0, e1);
+      if constexpr (G2) {
+        float b0, b1;
+        R::unpack(er_raw[m], b0, b1);
+        e0 *= b0;
+        e1 *= b1;
+      }
+    };
     auto ld_item = [&](bool with_qk) {
 #pragma unroll
       for (int m = 0; m < SUB; ++m) {
@@ -366,7 +393,7 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
           const int u = (m / (2 * lam)) * lam + (m & (lam - 1));
           float q0, q1, k0, k1;
           R::unpack(qr[m], q0, q1);
-          R::unpack(kr_raw[m], k0, k1);
+          read_key(m, k0, k1);
           R::st(LA + u * K::RS_DK, q0 * f0, q1 * f1);
           R::st(LA + (8 + u) * K::RS_DK, k0 * f0, k1 * f1);
         }
@@ -404,7 +431,7 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
           f1 *= al[m][1];
           float q0, q1, k0, k1;
           R::unpack(qr[m], q0, q1);
-          R::unpack(kr_raw[m], k0, k1);
+          read_key(m, k0, k1);
           R::st(Xq + m * K::RS_DK, q0 * f0, q1 * f1);
           R::st(Xk + m * K::RS_DK, k0 * f0, k1 * f1);
         }
@@ -514,7 +541,7 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
             f1 *= al[m][1];
             float q0, q1, k0, k1;
             R::unpack(qr[m], q0, q1);
-            R::unpack(kr_raw[m], k0, k1);
+            read_key(m, k0, k1);
             R::st(QG + m * K::RS_DK, q0 * f0, q1 * f1);
             g8a[mm] = k0 * f0;
             g8b[mm] = k1 * f1;
@@ -1010,7 +1037,8 @@ static hipError_t launch_chunk_t(const ChunkArgs& a) {
   }
   const int BH = a.B * a.H;
   hipLaunchKernelGGL(kern, dim3(BH * (a.dv / VT)), dim3(K::NT), K::LDS, (hipStream_t)a.stream, a.q, a.k, a.v,
-                     a.alpha, a.beta, a.s0, a.o, a.sT, a.dbg, a.T, a.H, a.dv, BH, (char*)nullptr, 0);
+                     a.alpha, a.beta, a.s0, a.o, a.sT, a.dbg, a.T, a.H, a.dv, BH, (char*)nullptr, 0,
+                     (const void*)nullptr);
   return hipGetLastError();
 }
 
@@ -1036,10 +1064,10 @@ hipError_t launch_chunk(const ChunkArgs& a) {
 
 // ---------------------------------------------------------------------------
 // Two-pass forward, first pass: records of every chunk of every head, in parallel.
-template <typename T, int DK, int NWV>
+template <typename T, int DK, bool G2>
 static hipError_t launch_prep_t(const ChunkArgs& a, char* ws, int cpw) {
-  using K = Cfg<T, DK, NWV>;
-  auto kern = chunk_fwd_kernel<T, DK, NWV, true>;
+  using K = Cfg<T, DK, 64>;
+  auto kern = chunk_fwd_kernel<T, DK, 64, true, G2>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, K::LDS);
@@ -1051,14 +1079,19 @@ static hipError_t launch_prep_t(const ChunkArgs& a, char* ws, int cpw) {
   const int nseg = (nchunks + cpw - 1) / cpw;
   if ((long)BH * nseg == 0) return hipSuccess;
   hipLaunchKernelGGL(kern, dim3(BH * nseg), dim3(K::NT), K::LDS, (hipStream_t)a.stream, a.q, a.k, a.v, a.alpha,
-                     a.beta, a.s0, a.o, a.sT, (float*)nullptr, a.T, a.H, a.dv, BH, ws, cpw);
+                     a.beta, a.s0, a.o, a.sT, (float*)nullptr, a.T, a.H, a.dv, BH, ws, cpw, a.erase);
   return hipGetLastError();
 }
 
+template <bool G2>
+static hipError_t launch_prep_g(const ChunkArgs& a, void* ws, int cpw) {
+  if (!a.bf16) return a.dk == 64 ? launch_prep_t<float, 64, G2>(a, (char*)ws, cpw) : hipErrorInvalidValue;
+  return a.dk == 64 ? launch_prep_t<bf16_t, 64, G2>(a, (char*)ws, cpw)
+                    : launch_prep_t<bf16_t, 128, G2>(a, (char*)ws, cpw);
+}
+
 hipError_t launch_prep(const ChunkArgs& a, void* ws, int cpw) {
-  if (!a.bf16) return a.dk == 64 ? launch_prep_t<float, 64, 64>(a, (char*)ws, cpw) : hipErrorInvalidValue;
-  return a.dk == 64 ? launch_prep_t<bf16_t, 64, 64>(a, (char*)ws, cpw)
-                    : launch_prep_t<bf16_t, 128, 64>(a, (char*)ws, cpw);
+  return a.erase ? launch_prep_g<true>(a, ws, cpw) : launch_prep_g<false>(a, ws, cpw);
 }
 
 size_t record_bytes(bool bf16, int dk) {

@@ -18,14 +18,18 @@
 
 namespace kda {
 
-template <typename T, int DK, int DV>
+// G2: Gated DeltaNet-2 step -- the read goes through the erase gate, u = S'^T (b o k),
+// the write through the write gate, delta = w o v - u (no beta).
+template <typename T, int DK, int DV, bool G2>
 __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ q,
                                                      const void* __restrict__ k,
                                                      const void* __restrict__ v,
                                                      const void* __restrict__ alpha,
                                                      const void* __restrict__ beta,
                                                      float* __restrict__ state,
-                                                     void* __restrict__ o) {
+                                                     void* __restrict__ o,
+                                                     const void* __restrict__ erase,
+                                                     const void* __restrict__ write) {
   constexpr int NT = 256;
   constexpr int TPR = DV / 4;      // threads covering one state row (4 columns each)
   constexpr int RG = NT / TPR;     // row groups
@@ -33,6 +37,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ q,
   static_assert(RPT * RG == DK && TPR * 4 == DV, "tile split");
 
   __shared__ float s_q[DK], s_k[DK], s_a[DK], s_v[DV];
+  __shared__ float s_e[G2 ? DK : 1];  // read-side key b o k (G2)
   __shared__ float s_red[4][2][DV];
   __shared__ float s_qk;
 
@@ -60,10 +65,14 @@ __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ q,
     s_q[tid] = qq;
     s_k[tid] = kk;
     s_a[tid] = Elem<T>::load(alpha, bh * DK + tid);
+    if constexpr (G2) s_e[tid] = Elem<T>::load(erase, bh * DK + tid) * kk;
     qk_part = qq * kk;
   }
-  if (tid < DV) s_v[tid] = Elem<T>::load(v, bh * DV + tid);
-  const float bt = Elem<T>::load(beta, bh);
+  // the write value: v (KDA, beta applied below) or w o v (G2)
+  if (tid < DV)
+    s_v[tid] = G2 ? Elem<T>::load(write, bh * DV + tid) * Elem<T>::load(v, bh * DV + tid)
+                  : Elem<T>::load(v, bh * DV + tid);
+  const float bt = G2 ? 1.f : Elem<T>::load(beta, bh);
   // q . k: one product per thread (zero beyond DK), reduced per wave, then across waves
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) qk_part += __shfl_xor(qk_part, off);
@@ -75,7 +84,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ q,
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int r = rg + RG * i;
-    const float a = s_a[r], kk = s_k[r], qq = s_q[r];
+    const float a = s_a[r], kk = G2 ? s_e[r] : s_k[r], qq = s_q[r];
     s[i].x *= a; s[i].y *= a; s[i].z *= a; s[i].w *= a;
     u[0] += kk * s[i].x; u[1] += kk * s[i].y; u[2] += kk * s[i].z; u[3] += kk * s[i].w;
     p[0] += qq * s[i].x; p[1] += qq * s[i].y; p[2] += qq * s[i].z; p[3] += qq * s[i].w;
@@ -120,24 +129,25 @@ __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ q,
   }
 }
 
-template <typename T, int DK, int DV>
+template <typename T, int DK, int DV, bool G2>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
-  hipLaunchKernelGGL((decode_kernel<T, DK, DV>), dim3(a.BH), dim3(256), 0, (hipStream_t)a.stream,
-                     a.q, a.k, a.v, a.alpha, a.beta, a.state, a.o);
+  hipLaunchKernelGGL((decode_kernel<T, DK, DV, G2>), dim3(a.BH), dim3(256), 0, (hipStream_t)a.stream,
+                     a.q, a.k, a.v, a.alpha, a.beta, a.state, a.o, a.erase, a.write);
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool G2>
 static hipError_t launch_decode_d(const DecodeArgs& a) {
-  if (a.dk == 64 && a.dv == 64) return launch_decode_t<T, 64, 64>(a);
-  if (a.dk == 64 && a.dv == 128) return launch_decode_t<T, 64, 128>(a);
-  if (a.dk == 128 && a.dv == 64) return launch_decode_t<T, 128, 64>(a);
-  return launch_decode_t<T, 128, 128>(a);
+  if (a.dk == 64 && a.dv == 64) return launch_decode_t<T, 64, 64, G2>(a);
+  if (a.dk == 64 && a.dv == 128) return launch_decode_t<T, 64, 128, G2>(a);
+  if (a.dk == 128 && a.dv == 64) return launch_decode_t<T, 128, 64, G2>(a);
+  return launch_decode_t<T, 128, 128, G2>(a);
 }
 
 hipError_t launch_decode(const DecodeArgs& a) {
   if (a.BH == 0) return hipSuccess;
-  return a.bf16 ? launch_decode_d<bf16_t>(a) : launch_decode_d<float>(a);
+  if (a.erase) return a.bf16 ? launch_decode_d<bf16_t, true>(a) : launch_decode_d<float, true>(a);
+  return a.bf16 ? launch_decode_d<bf16_t, false>(a) : launch_decode_d<float, false>(a);
 }
 
 }  // namespace kda

@@ -12,6 +12,9 @@ struct DecodeArgs {
   int BH, dk, dv;
   bool bf16;
   void* stream;
+  // Gated DeltaNet-2 gates (both set, beta unused) or both NULL (KDA / CKDA)
+  const void* erase = nullptr;  // [BH, dk]
+  const void* write = nullptr;  // [BH, dv]
 };
 
 struct ChunkArgs {
@@ -24,6 +27,9 @@ struct ChunkArgs {
   bool bf16;
   void* stream;
   int vt_override;  // value-tile width (64 / 128) chosen by the caller; 0 = heuristic
+  // Gated DeltaNet-2 gates (both set, beta unused) or both NULL (KDA / CKDA)
+  const void* erase = nullptr;  // [B, T, H, dk]
+  const void* write = nullptr;  // [B, T, H, dv]
 };
 
 hipError_t launch_decode(const DecodeArgs& a);

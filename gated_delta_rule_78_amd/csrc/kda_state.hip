@@ -62,7 +62,9 @@ __device__ __forceinline__ void full_barrier() {
 // chunk's record and v tile global -> LDS with 16-byte DMA.  A wave stalled issuing
 // DMA cannot issue matrix work, and one wave's DMA issue rate is well below a CU's
 // share of HBM bandwidth, hence several producers beside the compute waves.
-template <typename T, int DK, int VT>
+// G2: Gated DeltaNet-2 -- a write-gate tile (same layout as v) streams beside v and
+// U = M (w o v).
+template <typename T, int DK, int VT, bool G2 = false>
 struct SCfg {
   using RL = RecordLayout<T, DK>;
   static constexpr int ES = Elem<T>::kBytes;
@@ -75,10 +77,11 @@ struct SCfg {
   static constexpr int N_DMA_REC = (RL::IMG + 1023) / 1024;  // wave-wide DMA steps per record
   static constexpr int N_DMA_V = C * UPR / 64;
   static constexpr int V_BYTES = C * RS_V;
+  static constexpr int NTILE = G2 ? 2 : 1;   // v (and write-gate) tiles per buffer
   // two record and v buffers when they fit: the next chunk streams in during this one
-  static constexpr int NBUF = 2 * (RL::IMG + V_BYTES) <= 160 * 1024 ? 2 : 1;
+  static constexpr int NBUF = 2 * (RL::IMG + NTILE * V_BYTES) <= 160 * 1024 ? 2 : 1;
   static_assert(N_DMA_V * 64 == C * UPR, "v tile split");
-  static_assert(NBUF * (RL::IMG + V_BYTES) <= 160 * 1024, "LDS budget");
+  static_assert(NBUF * (RL::IMG + NTILE * V_BYTES) <= 160 * 1024, "LDS budget");
 };
 
 }  // namespace
@@ -97,10 +100,10 @@ __device__ __forceinline__ void fence_sched() {
 //   S <- diag(gamma_last) S + (K o rho)^T Delta
 // With one compute wave per SIMD little else hides LDS latency, so the operand
 // fragments of each group of products are loaded one group ahead (software pipelining).
-template <typename T, int DK, int VT>
-__device__ __forceinline__ void state_chunk(const char* rec, char* vv, f32x4_t (&S)[DK / 16], int wave, int g,
-                                            int n) {
-  using K = SCfg<T, DK, VT>;
+template <typename T, int DK, int VT, bool G2 = false>
+__device__ __forceinline__ void state_chunk(const char* rec, char* vv, const char* wv, f32x4_t (&S)[DK / 16],
+                                            int wave, int g, int n) {
+  using K = SCfg<T, DK, VT, G2>;
   using RL = typename K::RL;
   constexpr int ES = K::ES;
   constexpr int KS = K::KS;
@@ -128,6 +131,18 @@ __device__ __forceinline__ void state_chunk(const char* rec, char* vv, f32x4_t (
   Frag<T> fw[2][KS], fq[2][KS];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) bv[ks].load_col8(vv + (32 * ks + 8 * g) * K::RS_V + (16 * wave + n) * ES, K::RS_V);
+  if constexpr (G2) {  // the write side: z = w o v, rounded once to the operand type
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      Frag<T> bw;
+      bw.load_col8(wv + (32 * ks + 8 * g) * K::RS_V + (16 * wave + n) * ES, K::RS_V);
+      float z[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) z[e] = bv[ks].get(e) * bw.get(e);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bv[ks].set(e, z[e]);
+    }
+  }
 #pragma unroll
   for (int j = 0; j < 6; ++j) {
     const int I = j < 2 ? j : 2 + (j - 2) / 2, ks = j < 2 ? 0 : (j - 2) % 2;
@@ -224,12 +239,13 @@ __device__ __forceinline__ void state_chunk(const char* rec, char* vv, f32x4_t (
     }
 }
 
-template <typename T, int DK, int VT>
+template <typename T, int DK, int VT, bool G2>
 __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const char* __restrict__ ws,
                                                                          const void* __restrict__ gv,
                                                                          const float* s0, void* __restrict__ go,
-                                                                         float* sT, int Tlen, int H, int DV, int BH) {
-  using K = SCfg<T, DK, VT>;
+                                                                         float* sT, int Tlen, int H, int DV, int BH,
+                                                                         const void* __restrict__ gw) {
+  using K = SCfg<T, DK, VT, G2>;
   constexpr int NP = K::NP;
   using RL = typename K::RL;
   constexpr int ES = K::ES;
@@ -241,6 +257,8 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
   __shared__ __align__(16) char v_a[K::V_BYTES];
   __shared__ __align__(16) char rec_b[K::NBUF == 2 ? RL::IMG : 16];
   __shared__ __align__(16) char v_b[K::NBUF == 2 ? K::V_BYTES : 16];
+  __shared__ __align__(16) char w_a[G2 ? K::V_BYTES : 16];  // write-gate tiles (G2)
+  __shared__ __align__(16) char w_b[G2 && K::NBUF == 2 ? K::V_BYTES : 16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -278,7 +296,7 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
 
   // (producer waves) chunk c's record and v tile -> LDS; v rows past the end are clamped
   // to the last row here and zeroed once they have landed
-  auto issue = [&](int c, char* rec_dst, char* v_dst) {
+  auto issue = [&](int c, char* rec_dst, char* v_dst, char* w_dst) {
     const char* rec = rec0 + (size_t)c * RL::BYTES;
     const int t0 = c * C;
 #pragma nounroll
@@ -286,7 +304,9 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
       const int sl = x * 64 + lane;
       const int row = sl / K::UPR, u = sl % K::UPR;
       const size_t gr = ((size_t)b * Tlen + min(t0 + row, Tlen - 1)) * H + h;
-      dma16((const char*)gv + (gr * DV + v0) * ES + (size_t)u * 16, v_dst + x * 1024);
+      const size_t off = (gr * DV + v0) * ES + (size_t)u * 16;
+      dma16((const char*)gv + off, v_dst + x * 1024);
+      if constexpr (G2) dma16((const char*)gw + off, w_dst + x * 1024);
     }
 #pragma nounroll
     for (int x = pw; x < K::N_DMA_REC; x += NP) {
@@ -314,11 +334,11 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
     }
   };
 
-  if (nchunks > 0 && producer) issue(0, rec_a, v_a);
+  if (nchunks > 0 && producer) issue(0, rec_a, v_a, w_a);
   if constexpr (K::NBUF == 2) {
     // chunk c computes from buffers P while the producer streams chunk c + 1 into
     // buffers Q; the outputs of chunk c - 1, staged in Q's v tile, are stored first
-    auto step = [&](int c, const char* recP, char* vP, char* recQ, char* vQ) {
+    auto step = [&](int c, const char* recP, char* vP, const char* wP, char* recQ, char* vQ, char* wQ) {
       full_barrier();  // chunk c landed; chunk c - 1 finished everywhere
       if (c > 0) {
         store_o(c - 1, vQ);
@@ -326,15 +346,15 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
       }
       pad_rows(c, vP);
       if (producer) {
-        if (c + 1 < nchunks) issue(c + 1, recQ, vQ);
+        if (c + 1 < nchunks) issue(c + 1, recQ, vQ, wQ);
       } else {
-        state_chunk<T, DK, VT>(recP, vP, S, wave, g, n);
+        state_chunk<T, DK, VT, G2>(recP, vP, wP, S, wave, g, n);
       }
     };
     for (int chunk = 0; chunk < nchunks; chunk += 2) {
-      step(chunk, rec_a, v_a, rec_b, v_b);
+      step(chunk, rec_a, v_a, w_a, rec_b, v_b, w_b);
       if (chunk + 1 >= nchunks) break;
-      step(chunk + 1, rec_b, v_b, rec_a, v_a);
+      step(chunk + 1, rec_b, v_b, w_b, rec_a, v_a, w_a);
     }
     if (nchunks > 0) {
       lds_barrier();
@@ -344,12 +364,12 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
     for (int chunk = 0; chunk < nchunks; ++chunk) {
       full_barrier();
       pad_rows(chunk, v_a);
-      if (!producer) state_chunk<T, DK, VT>(rec_a, v_a, S, wave, g, n);
+      if (!producer) state_chunk<T, DK, VT, G2>(rec_a, v_a, w_a, S, wave, g, n);
       lds_barrier();
       store_o(chunk, v_a);
       if (chunk + 1 < nchunks) {
         lds_barrier();  // every output read out of v_a before the next chunk lands there
-        if (producer) issue(chunk + 1, rec_a, v_a);
+        if (producer) issue(chunk + 1, rec_a, v_a, w_a);
       }
     }
   }
@@ -363,13 +383,13 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
   }
 }
 
-template <typename T, int DK, int VT>
+template <typename T, int DK, int VT, bool G2>
 static hipError_t launch_state_t(const ChunkArgs& a, const void* ws) {
-  using K = SCfg<T, DK, VT>;
+  using K = SCfg<T, DK, VT, G2>;
   const int BH = a.B * a.H;
-  auto kern = chunk_state_kernel<T, DK, VT>;
+  auto kern = chunk_state_kernel<T, DK, VT, G2>;
   hipLaunchKernelGGL(kern, dim3(BH * (a.dv / VT)), dim3(K::NT), 0, (hipStream_t)a.stream, (const char*)ws, a.v,
-                     a.s0, a.o, a.sT, a.T, a.H, a.dv, BH);
+                     a.s0, a.o, a.sT, a.T, a.H, a.dv, BH, a.write);
   return hipGetLastError();
 }
 
@@ -384,29 +404,41 @@ static int state_vt_override() {
 
 // Value-tile width of the state pass: each workgroup walks the whole chunk chain of one
 // (b, h, tile), so with few (b, h) pairs narrower tiles put more compute units on the
-// chains (every tile reads the whole record; the extra reads hit in L2).
+// chains (every tile reads the whole record; the extra reads hit in L2).  The
+// Gated DeltaNet-2 write-gate tiles need LDS: at d_k = 128 the tiles are at most 32 wide.
 static int pick_state_vt(const ChunkArgs& a) {
+  const int cap = (a.write && a.bf16 && a.dk == 128) ? 32 : 64;
   const int o = state_vt_override();
-  if (o == 16 || o == 32 || o == 64) return o <= a.dv ? o : a.dv;
-  const long bh = (long)a.B * a.H;
-  if (bh * (a.dv / 64) >= 256) return 64;
-  if (bh * (a.dv / 32) >= 256) return 32;
-  return 16;
+  int vt;
+  if (o == 16 || o == 32 || o == 64) {
+    vt = o <= a.dv ? o : a.dv;
+  } else {
+    const long bh = (long)a.B * a.H;
+    vt = bh * (a.dv / 64) >= 256 ? 64 : bh * (a.dv / 32) >= 256 ? 32 : 16;
+  }
+  return vt < cap ? vt : cap;
 }
 
-template <typename T, int DK>
+template <typename T, int DK, bool G2>
 static hipError_t launch_state_vt(const ChunkArgs& a, const void* ws) {
   switch (pick_state_vt(a)) {
-    case 16: return launch_state_t<T, DK, 16>(a, ws);
-    case 32: return launch_state_t<T, DK, 32>(a, ws);
-    default: return launch_state_t<T, DK, 64>(a, ws);
+    case 16: return launch_state_t<T, DK, 16, G2>(a, ws);
+    case 32: return launch_state_t<T, DK, 32, G2>(a, ws);
+    default:
+      if constexpr (G2 && DK == 128 && sizeof(T) == 2) return hipErrorInvalidValue;  // capped at 32 above
+      else return launch_state_t<T, DK, 64, G2>(a, ws);
   }
+}
+
+template <bool G2>
+static hipError_t launch_state_g(const ChunkArgs& a, const void* ws) {
+  if (!a.bf16) return a.dk == 64 && a.dv == 64 ? launch_state_vt<float, 64, G2>(a, ws) : hipErrorInvalidValue;
+  return a.dk == 64 ? launch_state_vt<bf16_t, 64, G2>(a, ws) : launch_state_vt<bf16_t, 128, G2>(a, ws);
 }
 
 hipError_t launch_state(const ChunkArgs& a, const void* ws) {
   if (a.B * a.H == 0) return hipSuccess;
-  if (!a.bf16) return a.dk == 64 && a.dv == 64 ? launch_state_vt<float, 64>(a, ws) : hipErrorInvalidValue;
-  return a.dk == 64 ? launch_state_vt<bf16_t, 64>(a, ws) : launch_state_vt<bf16_t, 128>(a, ws);
+  return a.write ? launch_state_g<true>(a, ws) : launch_state_g<false>(a, ws);
 }
 
 }  // namespace kda

@@ -143,6 +143,28 @@ int kda_chunk_apply_records(const kda_shape* shape, const void* workspace, size_
                             void* stream);
 
 /*
+ * Gated DeltaNet-2 ("Gated DeltaNet-2" summary, section 1): the scalar beta is split
+ * into an erase gate b_t per key channel and a write gate w_t per value channel,
+ *   S_t = (I - k_t (b_t o k_t)^T) Diag(alpha_t) S_{t-1} + k_t (w_t o v_t)^T,
+ *   o_t = S_t^T q_t        (o: elementwise product; b = w = beta gives KDA).
+ * The forward is the two-pass chunk forward of kda_chunk_fwd_ws (same workspace
+ * size, kda_chunk_fwd_workspace_size; a workspace is required), with
+ *   erase_gate : [B, T, H, dk], values in [0, 1] (the range is not checked)
+ *   write_gate : [B, T, H, dv], values in [0, 1]
+ * in the dtype of q and 16-byte aligned; no beta.  Other arguments, layouts, alias
+ * rules and errors as kda_chunk_fwd_ws (the gates are inputs: no output may overlap
+ * them).  The decode step takes erase_gate [B, H, dk] and write_gate [B, H, dv]
+ * (element alignment) in place of beta and is otherwise kda_decode_step.
+ */
+int kda_gdn2_chunk_fwd(const kda_shape* shape, const void* q, const void* k, const void* v,
+                       const void* alpha, const void* erase_gate, const void* write_gate,
+                       const float* initial_state, void* o, float* final_state,
+                       void* workspace, size_t workspace_bytes, void* stream);
+int kda_gdn2_decode_step(const kda_shape* shape, const void* q, const void* k, const void* v,
+                         const void* alpha, const void* erase_gate, const void* write_gate,
+                         float* state, void* o, void* stream);
+
+/*
  * One recurrent decode step for every (b, h), state updated in place:
  *   S <- (I - beta k k^T) Diag(alpha) S + beta k v^T ;  o <- S^T q.
  *   state : [B, H, dk, dv] fp32, read and written in place.

@@ -153,6 +153,35 @@ def test_records_and_apply_argument_errors(L):
     assert app(v=_p(2, off=4)) == ALIGN
 
 
+def test_gdn2_argument_errors(L):
+    shape = kda.Shape(1, 64, 2, 64, 64, 64, 0)
+    need = L.kda_chunk_fwd_workspace_size(ctypes.byref(shape))
+
+    def fwd(q=_p(0), k=_p(1), v=_p(2), a=_p(3), e=_p(4), w=_p(6), o=_p(5), sT=None, ws=_p(9), n=need, sh=shape):
+        return L.kda_gdn2_chunk_fwd(ctypes.byref(sh), q, k, v, a, e, w, None, o, sT, ws, ctypes.c_size_t(n), None)
+
+    assert fwd(e=None) == NULL
+    assert fwd(w=None) == NULL
+    assert fwd(ws=None) == NULL
+    assert fwd(n=need - 1) == WORKSPACE
+    assert fwd(w=_p(6, off=8)) == ALIGN
+    assert fwd(o=_p(4, off=64)) == ALIAS             # output over the erase gate
+    assert fwd(sT=_p(6)) == ALIAS                    # final state over the write gate
+    assert fwd(ws=_p(4)) == ALIAS                    # workspace over the erase gate
+    assert fwd(sh=kda.Shape(1, 64, 2, 96, 64, 64, 0)) == UNSUP
+
+    dshape = kda.Shape(2, 1, 2, 64, 64, 0, 0)
+
+    def dec(e=_p(4), w=_p(6), st=_p(5), o=_p(7)):
+        return L.kda_gdn2_decode_step(ctypes.byref(dshape), _p(0), _p(1), _p(2), _p(3), e, w, st, o, None)
+
+    assert dec(e=None) == NULL
+    assert dec(w=None) == NULL
+    assert dec(st=_p(4)) == ALIAS                    # state over the erase gate
+    assert dec(o=_p(6, off=2)) == ALIAS              # output over the write gate
+    assert dec(w=_p(6, off=1)) == ALIGN
+
+
 def test_decode_argument_errors(L):
     assert L.kda_decode_step(None, *([None] * 8)) == NULL
     assert _decode(L, dtype=3) == DTYPE
