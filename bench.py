@@ -83,8 +83,10 @@ def state_bytes(B, T, H, dk, dv, es=2):
     return B * H * nch * RECORD_PAYLOAD[dk] + B * T * H * es * 2 * dv + 2 * B * H * dk * dv * 4
 
 
-def decode_bytes(B, H, dk, dv, es=2):
-    return 2 * B * H * dk * dv * 4 + B * H * (es * (3 * dk + dv + 1) + es * dv)
+def decode_bytes(B, H, dk, dv, es=2, tokens=1):
+    """Algorithmic bytes of one decode call: the fp32 state read and written once, and
+    per token q, k, alpha, v, beta read and o written."""
+    return 2 * B * H * dk * dv * 4 + tokens * B * H * (es * (3 * dk + dv + 1) + es * dv)
 
 
 def kernel_hash(files):
@@ -226,6 +228,39 @@ def bench_decode(steps_rep, log):
     return w, ms
 
 
+def bench_decode_tokens(ntok, log, reps=3):
+    """The decode workload's 64 tokens as 64 / ntok calls of ntok tokens each (the state
+    read and written once per call)."""
+    import torch
+    import gated_delta_rule_78_amd as kda
+    from gated_delta_rule_78_amd.inputs import make_workload, WORKLOADS, to_torch
+    w = WORKLOADS["ckda_decode_b256"]
+    inp = make_workload("ckda_decode_b256")
+    q, k, v, a, b, s0 = to_torch(inp)
+    # [steps, B, H, .] -> calls of [B, ntok, H, .]
+    calls = []
+    for c in range(w.decode_steps // ntok):
+        sl = slice(c * ntok, (c + 1) * ntok)
+        calls.append(tuple(x[sl].transpose(0, 1).contiguous() for x in (q, k, v, a, b)))
+    S = s0.clone()
+    o = torch.empty((w.B, ntok, w.H, w.dv), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    times = []
+    for rep in range(reps + 1):
+        S.copy_(s0)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for cq, ck, cv, ca, cb in calls:
+            kda.decode_tokens(cq, ck, cv, ca, cb, S, out=o)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if rep > 0:
+            times.append(e0.elapsed_time(e1) / len(calls))
+    return w, float(np.median(times)), ntok
+
+
 def cpu_baseline(inp, budget_s, log):
     """The fp64 oracle on whole sequences of a sample of heads of the prefill
     workload; value scaled to the metric's unit (tokens/s across all H heads)."""
@@ -352,6 +387,13 @@ def main():
                          "tokens_per_s": wd.B / (msd * 1e-3), "frac": gbs / HBM_PEAK_GBS,
                          "bytes_per_step": db, "traffic": stored_traffic("decode")}
         log(f"[bench] decode: {msd * 1e3:.1f} us/step, {gbs:.1f} GB/s")
+        wt, mst, ntk = bench_decode_tokens(4, log)
+        bt_ = decode_bytes(wt.B, wt.H, wt.dk, wt.dv, tokens=ntk)
+        out["decode_tokens"] = {"workload": "ckda_decode_b256", "tokens_per_call": ntk, "ms_per_call": mst,
+                                "us_per_token": mst * 1e3 / ntk, "tokens_per_s": wt.B * ntk / (mst * 1e-3),
+                                "value": bt_ / (mst * 1e-3) / 1e9, "unit": "GB/s",
+                                "frac": bt_ / (mst * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        log(f"[bench] decode, {ntk} tokens per call: {mst * 1e3:.1f} us/call ({mst * 1e3 / ntk:.1f} us/token)")
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, log)
     print(json.dumps(out), flush=True)

@@ -15,7 +15,7 @@ import ctypes
 import os
 
 __all__ = ["chunk_fwd", "chunk_records", "chunk_apply_records", "chunk_fwd_debug", "decode_step",
-           "gdn2_chunk_fwd", "gdn2_decode_step",
+           "gdn2_chunk_fwd", "gdn2_decode_step", "decode_tokens", "gdn2_decode_tokens",
            "workspace_size", "pick_path", "lib", "version", "status_string",
            "LIB_PATH", "KdaError", "Shape", "BF16", "F32"]
 
@@ -64,6 +64,10 @@ def lib() -> ctypes.CDLL:
         L.kda_gdn2_chunk_fwd.restype = ctypes.c_int
         L.kda_gdn2_decode_step.argtypes = [SP, P, P, P, P, P, P, P, P, P]
         L.kda_gdn2_decode_step.restype = ctypes.c_int
+        L.kda_decode_tokens.argtypes = [SP, P, P, P, P, P, P, P, P]
+        L.kda_decode_tokens.restype = ctypes.c_int
+        L.kda_gdn2_decode_tokens.argtypes = [SP, P, P, P, P, P, P, P, P, P]
+        L.kda_gdn2_decode_tokens.restype = ctypes.c_int
         L.kda_status_string.argtypes = [ctypes.c_int]
         L.kda_status_string.restype = ctypes.c_char_p
         L.kda_version.argtypes = []
@@ -334,3 +338,43 @@ def gdn2_decode_step(q, k, v, alpha, erase, write, state, out=None):
     if rc != 0:
         raise KdaError(rc, "kda_gdn2_decode_step")
     return out
+
+
+def decode_tokens(q, k, v, alpha, beta, state, out=None, erase=None, write=None):
+    """Several tokens per (b, h) with the state read and written once: q, k, alpha
+    [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H] (or, for Gated DeltaNet-2, beta=None with
+    erase [B,T,H,dk] and write [B,T,H,dv]); state fp32 [B,H,dk,dv] in place.
+    Returns o [B,T,H,dv]."""
+    torch = _torch()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    code = _dtype_code(q)
+    g2 = erase is not None or write is not None
+    if k.shape != q.shape or alpha.shape != q.shape or v.shape != (B, T, H, dv):
+        raise ValueError("shapes: q, k, alpha [B,T,H,dk]; v [B,T,H,dv]")
+    if g2 and (erase is None or write is None or erase.shape != q.shape or write.shape != v.shape):
+        raise ValueError("Gated DeltaNet-2: erase [B,T,H,dk] and write [B,T,H,dv]")
+    if not g2 and (beta is None or beta.shape != (B, T, H)):
+        raise ValueError("beta [B,T,H]")
+    if state.dtype != torch.float32 or state.shape != (B, H, dk, dv):
+        raise ValueError("state must be float32 [B,H,dk,dv]")
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    _check((q, k, v, alpha, beta, erase, write, state, out),
+           ("q", "k", "v", "alpha", "beta", "erase", "write", "state", "out"), dev)
+    shape = Shape(B, T, H, dk, dv, 0, code)
+    if g2:
+        rc = lib().kda_gdn2_decode_tokens(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase),
+                                          _ptr(write), _ptr(state), _ptr(out), _stream(dev))
+    else:
+        rc = lib().kda_decode_tokens(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                     _ptr(state), _ptr(out), _stream(dev))
+    if rc != 0:
+        raise KdaError(rc, "kda_decode_tokens")
+    return out
+
+
+def gdn2_decode_tokens(q, k, v, alpha, erase, write, state, out=None):
+    """Gated DeltaNet-2 form of decode_tokens."""
+    return decode_tokens(q, k, v, alpha, None, state, out=out, erase=erase, write=write)

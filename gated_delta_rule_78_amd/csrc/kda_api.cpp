@@ -238,35 +238,42 @@ int kda_gdn2_chunk_fwd(const kda_shape* shape, const void* q, const void* k, con
   return rc ? rc : run_apply(*shape, p, stream);
 }
 
+// ntok < 0: the single decode step (shape->T ignored); else ntok = shape->T tokens per (b, h)
 static int decode_impl(const kda_shape* shape, const void* q, const void* k, const void* v, const void* alpha,
                        const void* beta, const void* erase, const void* write, float* state, void* o,
-                       void* stream) {
+                       void* stream, bool multi) {
   int es = 0;
   int rc = check_shape(shape, true, &es);
   if (rc) return rc;
   const kda_shape& s = *shape;
-  const int64_t rows = (int64_t)s.B * s.H;
-  if (rows > 0x7FFFFFFF) return KDA_ERR_SHAPE;
+  if (multi && s.T < 0) return KDA_ERR_SHAPE;
+  const int ntok = multi ? s.T : 1;
+  const int64_t rows = (int64_t)s.B * s.H;             // states
+  const int64_t trows = rows * ntok;                    // token rows of the inputs and o
+  if (rows > 0x7FFFFFFF || trows > (int64_t(1) << 40) / 256) return KDA_ERR_SHAPE;
   const bool g2 = erase || write;
-  if (rows > 0 && (!q || !k || !v || !alpha || !o || !state || (g2 ? (!erase || !write) : !beta)))
+  if (trows > 0 && (!q || !k || !v || !alpha || !o || !state || (g2 ? (!erase || !write) : !beta)))
     return KDA_ERR_NULL;
   // the state moves in 16-byte vectors; the per-token vectors are read per element
   if (state && misaligned(state)) return KDA_ERR_ALIGN;
   const void* ptrs[] = {q, k, v, alpha, beta, o, erase, write};
   for (const void* p : ptrs)
     if (p && misaligned(p, es)) return KDA_ERR_ALIGN;
-  const Range in[] = {range_of(q, rows * s.dk * es),     range_of(k, rows * s.dk * es),
-                      range_of(v, rows * s.dv * es),     range_of(alpha, rows * s.dk * es),
-                      range_of(beta, beta ? rows * es : 0), range_of(erase, erase ? rows * s.dk * es : 0),
-                      range_of(write, write ? rows * s.dv * es : 0)};
-  const Range ro = range_of(o, rows * s.dv * es);
+  const Range in[] = {range_of(q, trows * s.dk * es),     range_of(k, trows * s.dk * es),
+                      range_of(v, trows * s.dv * es),     range_of(alpha, trows * s.dk * es),
+                      range_of(beta, beta ? trows * es : 0), range_of(erase, erase ? trows * s.dk * es : 0),
+                      range_of(write, write ? trows * s.dv * es : 0)};
+  const Range ro = range_of(o, trows * s.dv * es);
   const Range rs = range_of(state, rows * s.dk * s.dv * 4);
   for (const Range& r : in)
     if (overlap(ro, r) || overlap(rs, r)) return KDA_ERR_ALIAS;
   if (overlap(ro, rs)) return KDA_ERR_ALIAS;
+  if (ntok == 0) return KDA_OK;
   kda::DecodeArgs a{q, k, v, alpha, beta, state, o, (int)rows, s.dk, s.dv, s.dtype == KDA_BF16, stream};
   a.erase = erase;
   a.write = write;
+  a.ntok = ntok;
+  a.H = s.H;
   return kda::launch_decode(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -278,12 +285,28 @@ int kda_gdn2_decode_step(const kda_shape* shape, const void* q, const void* k, c
     if (rc) return rc;
     if ((int64_t)shape->B * shape->H > 0) return KDA_ERR_NULL;
   }
-  return decode_impl(shape, q, k, v, alpha, nullptr, erase_gate, write_gate, state, o, stream);
+  return decode_impl(shape, q, k, v, alpha, nullptr, erase_gate, write_gate, state, o, stream, false);
 }
 
 int kda_decode_step(const kda_shape* shape, const void* q, const void* k, const void* v,
                     const void* alpha, const void* beta, float* state, void* o, void* stream) {
-  return decode_impl(shape, q, k, v, alpha, beta, nullptr, nullptr, state, o, stream);
+  return decode_impl(shape, q, k, v, alpha, beta, nullptr, nullptr, state, o, stream, false);
+}
+
+int kda_decode_tokens(const kda_shape* shape, const void* q, const void* k, const void* v, const void* alpha,
+                      const void* beta, float* state, void* o, void* stream) {
+  return decode_impl(shape, q, k, v, alpha, beta, nullptr, nullptr, state, o, stream, true);
+}
+
+int kda_gdn2_decode_tokens(const kda_shape* shape, const void* q, const void* k, const void* v, const void* alpha,
+                           const void* erase_gate, const void* write_gate, float* state, void* o, void* stream) {
+  if (!erase_gate || !write_gate) {
+    int es = 0;
+    int rc = check_shape(shape, true, &es);
+    if (rc) return rc;
+    if ((int64_t)shape->B * shape->H > 0) return KDA_ERR_NULL;
+  }
+  return decode_impl(shape, q, k, v, alpha, nullptr, erase_gate, write_gate, state, o, stream, true);
 }
 
 }  // extern "C"

@@ -8,11 +8,12 @@
 // summary, practical implications: O(1) inference memory).
 //
 // Bandwidth bound: every step streams the fp32 d_k x d_v state from HBM once
-// and back once.  One workgroup of 256 threads owns one (b, h) tile; a thread
-// keeps DK / (256 * 4 / DV) rows x 4 columns of the tile in registers (one
+// and back once.  One workgroup of 512 threads owns one (b, h) tile; a thread
+// keeps DK / (512 * 4 / DV) rows x 4 columns of the tile in registers (one
 // 16-byte load and one 16-byte store per row), so the tile is read and written
-// exactly once.  The two column reductions over d_k (u and p) go through lane
-// shuffles inside a wave and a small LDS exchange across the four waves.
+// exactly once (few registers per thread: many waves in flight per CU).  The two
+// column reductions over d_k (u and p) go through lane shuffles inside a wave
+// and a small LDS exchange across the eight waves.
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -21,7 +22,7 @@ namespace kda {
 // G2: Gated DeltaNet-2 step -- the read goes through the erase gate, u = S'^T (b o k),
 // the write through the write gate, delta = w o v - u (no beta).
 template <typename T, int DK, int DV, bool G2>
-__global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ q,
+__global__ __launch_bounds__(512) void decode_kernel(const void* __restrict__ q,
                                                      const void* __restrict__ k,
                                                      const void* __restrict__ v,
                                                      const void* __restrict__ alpha,
@@ -29,8 +30,9 @@ __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ q,
                                                      float* __restrict__ state,
                                                      void* __restrict__ o,
                                                      const void* __restrict__ erase,
-                                                     const void* __restrict__ write) {
-  constexpr int NT = 256;
+                                                     const void* __restrict__ write, int ntok, int H) {
+  constexpr int NT = 512;
+  constexpr int NWV = NT / 64;
   constexpr int TPR = DV / 4;      // threads covering one state row (4 columns each)
   constexpr int RG = NT / TPR;     // row groups
   constexpr int RPT = DK / RG;     // rows per thread
@@ -38,17 +40,18 @@ __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ q,
 
   __shared__ float s_q[DK], s_k[DK], s_a[DK], s_v[DV];
   __shared__ float s_e[G2 ? DK : 1];  // read-side key b o k (G2)
-  __shared__ float s_red[4][2][DV];
+  __shared__ float s_red[NWV][2][DV];
   __shared__ float s_qk;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const size_t bh = blockIdx.x;
+  const size_t b = bh / H, h = bh % H;
   const int cq = tid % TPR;        // column quad
   const int rg = tid / TPR;        // row group
 
-  // the state streams through once per step: nontemporal loads and stores keep it from
+  // the state streams through once per call: nontemporal loads and stores keep it from
   // displacing cached lines it will not reuse
   f32x4_t* S = reinterpret_cast<f32x4_t*>(state + bh * (size_t)DK * DV);
   float4 s[RPT];
@@ -58,81 +61,100 @@ __global__ __launch_bounds__(256) void decode_kernel(const void* __restrict__ q,
     s[i] = make_float4(t[0], t[1], t[2], t[3]);
   }
 
-  float qk_part = 0.f;
-  if (tid < DK) {
-    const float qq = Elem<T>::load(q, bh * DK + tid);
-    const float kk = Elem<T>::load(k, bh * DK + tid);
-    s_q[tid] = qq;
-    s_k[tid] = kk;
-    s_a[tid] = Elem<T>::load(alpha, bh * DK + tid);
-    if constexpr (G2) s_e[tid] = Elem<T>::load(erase, bh * DK + tid) * kk;
-    qk_part = qq * kk;
-  }
-  // the write value: v (KDA, beta applied below) or w o v (G2)
-  if (tid < DV)
-    s_v[tid] = G2 ? Elem<T>::load(write, bh * DV + tid) * Elem<T>::load(v, bh * DV + tid)
-                  : Elem<T>::load(v, bh * DV + tid);
-  const float bt = G2 ? 1.f : Elem<T>::load(beta, bh);
-  // q . k: one product per thread (zero beyond DK), reduced per wave, then across waves
+  // tokens in order, the state staying in registers ([B, ntok, H, .] inputs and outputs;
+  // ntok = 1 is the single decode step)
+  for (int tk = 0; tk < ntok; ++tk) {
+    const size_t row = (b * ntok + tk) * H + h;
+    if (tk > 0) __syncthreads();  // the previous token's LDS values are consumed
+    float qk_part = 0.f;
+    if (tid < DK) {
+      const float qq = Elem<T>::load(q, row * DK + tid);
+      const float kk = Elem<T>::load(k, row * DK + tid);
+      s_q[tid] = qq;
+      s_k[tid] = kk;
+      s_a[tid] = Elem<T>::load(alpha, row * DK + tid);
+      if constexpr (G2) s_e[tid] = Elem<T>::load(erase, row * DK + tid) * kk;
+      qk_part = qq * kk;
+    }
+    // the write value: v (KDA, beta applied below) or w o v (G2)
+    if (tid < DV)
+      s_v[tid] = G2 ? Elem<T>::load(write, row * DV + tid) * Elem<T>::load(v, row * DV + tid)
+                    : Elem<T>::load(v, row * DV + tid);
+    const float bt = G2 ? 1.f : Elem<T>::load(beta, row);
+    // q . k: one product per thread (zero beyond DK), reduced per wave, then across waves
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) qk_part += __shfl_xor(qk_part, off);
-  if (lane == 0) s_red[wave][0][0] = qk_part;
-  __syncthreads();
-  if (tid == 0) s_qk = s_red[0][0][0] + s_red[1][0][0] + s_red[2][0][0] + s_red[3][0][0];
+    for (int off = 32; off > 0; off >>= 1) qk_part += __shfl_xor(qk_part, off);
+    if (lane == 0) s_red[wave][0][0] = qk_part;
+    __syncthreads();
+    if (tid == 0) {
+      float t = 0.f;
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) t += s_red[w][0][0];
+      s_qk = t;
+    }
 
-  float u[4] = {0.f, 0.f, 0.f, 0.f}, p[4] = {0.f, 0.f, 0.f, 0.f};
+    float u[4] = {0.f, 0.f, 0.f, 0.f}, p[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const int r = rg + RG * i;
-    const float a = s_a[r], kk = G2 ? s_e[r] : s_k[r], qq = s_q[r];
-    s[i].x *= a; s[i].y *= a; s[i].z *= a; s[i].w *= a;
-    u[0] += kk * s[i].x; u[1] += kk * s[i].y; u[2] += kk * s[i].z; u[3] += kk * s[i].w;
-    p[0] += qq * s[i].x; p[1] += qq * s[i].y; p[2] += qq * s[i].z; p[3] += qq * s[i].w;
-  }
-  // reduce the row groups that share a wave
+    for (int i = 0; i < RPT; ++i) {
+      const int r = rg + RG * i;
+      const float a = s_a[r], kk = G2 ? s_e[r] : s_k[r], qq = s_q[r];
+      s[i].x *= a; s[i].y *= a; s[i].z *= a; s[i].w *= a;
+      u[0] += kk * s[i].x; u[1] += kk * s[i].y; u[2] += kk * s[i].z; u[3] += kk * s[i].w;
+      p[0] += qq * s[i].x; p[1] += qq * s[i].y; p[2] += qq * s[i].z; p[3] += qq * s[i].w;
+    }
+    // reduce the row groups that share a wave
 #pragma unroll
-  for (int off = TPR; off < 64; off <<= 1) {
+    for (int off = TPR; off < 64; off <<= 1) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u[j] += __shfl_xor(u[j], off);
+        p[j] += __shfl_xor(p[j], off);
+      }
+    }
+    __syncthreads();  // s_red reuse (q.k partials consumed by thread 0 above)
+    if (lane < TPR) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s_red[wave][0][4 * cq + j] = u[j];
+        s_red[wave][1][4 * cq + j] = p[j];
+      }
+    }
+    __syncthreads();
+    float d[4];
+    const float qk = s_qk;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      u[j] += __shfl_xor(u[j], off);
-      p[j] += __shfl_xor(p[j], off);
-    }
-  }
-  __syncthreads();  // s_red reuse (q.k partials consumed by thread 0 above)
-  if (lane < TPR) {
+      const int c = 4 * cq + j;
+      float uu = 0.f, pp = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      s_red[wave][0][4 * cq + j] = u[j];
-      s_red[wave][1][4 * cq + j] = p[j];
+      for (int w = 0; w < NWV; ++w) {
+        uu += s_red[w][0][c];
+        pp += s_red[w][1][c];
+      }
+      d[j] = bt * (s_v[c] - uu);
+      p[j] = pp;
     }
-  }
-  __syncthreads();
-  float d[4];
-  const float qk = s_qk;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = 4 * cq + j;
-    const float uu = s_red[0][0][c] + s_red[1][0][c] + s_red[2][0][c] + s_red[3][0][c];
-    d[j] = bt * (s_v[c] - uu);
-    p[j] = s_red[0][1][c] + s_red[1][1][c] + s_red[2][1][c] + s_red[3][1][c];
+    for (int i = 0; i < RPT; ++i) {
+      const float kk = s_k[rg + RG * i];
+      s[i].x += kk * d[0]; s[i].y += kk * d[1]; s[i].z += kk * d[2]; s[i].w += kk * d[3];
+    }
+    if (rg == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Elem<T>::store(o, row * DV + 4 * cq + j, p[j] + qk * d[j]);
+    }
   }
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const float kk = s_k[rg + RG * i];
-    s[i].x += kk * d[0]; s[i].y += kk * d[1]; s[i].z += kk * d[2]; s[i].w += kk * d[3];
     const f32x4_t t = {s[i].x, s[i].y, s[i].z, s[i].w};
     __builtin_nontemporal_store(t, &S[(size_t)(rg + RG * i) * TPR + cq]);
-  }
-  if (rg == 0) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) Elem<T>::store(o, bh * DV + 4 * cq + j, p[j] + qk * d[j]);
   }
 }
 
 template <typename T, int DK, int DV, bool G2>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
-  hipLaunchKernelGGL((decode_kernel<T, DK, DV, G2>), dim3(a.BH), dim3(256), 0, (hipStream_t)a.stream,
-                     a.q, a.k, a.v, a.alpha, a.beta, a.state, a.o, a.erase, a.write);
+  hipLaunchKernelGGL((decode_kernel<T, DK, DV, G2>), dim3(a.BH), dim3(512), 0, (hipStream_t)a.stream,
+                     a.q, a.k, a.v, a.alpha, a.beta, a.state, a.o, a.erase, a.write, a.ntok, a.H);
   return hipGetLastError();
 }
 

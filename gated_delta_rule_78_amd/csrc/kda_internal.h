@@ -15,6 +15,9 @@ struct DecodeArgs {
   // Gated DeltaNet-2 gates (both set, beta unused) or both NULL (KDA / CKDA)
   const void* erase = nullptr;  // [BH, dk]
   const void* write = nullptr;  // [BH, dv]
+  // tokens per (b, h) in one call: inputs [B, ntok, H, .]; BH = B * H
+  int ntok = 1;
+  int H = 1;
 };
 
 struct ChunkArgs {

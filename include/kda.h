@@ -175,6 +175,22 @@ int kda_decode_step(const kda_shape* shape, const void* q, const void* k, const 
                     const void* alpha, const void* beta, float* state, void* o,
                     void* stream);
 
+/*
+ * Several tokens per (b, h) in one call (speculative / multi-token decoding): the
+ * recurrence applied to shape->T consecutive tokens with the state read once, kept
+ * on chip and written back once.
+ *   q, k, alpha : [B, T, H, dk]; v : [B, T, H, dv]; beta : [B, T, H] (GDN-2: erase_gate
+ *   [B, T, H, dk], write_gate [B, T, H, dv]); o : [B, T, H, dv], token t's readout after
+ *   token t's update; state : [B, H, dk, dv] fp32, in place.
+ * Same alignment, alias and error rules as kda_decode_step; T == 0 changes nothing.
+ * The result equals T calls of kda_decode_step (up to fp32 summation order).
+ */
+int kda_decode_tokens(const kda_shape* shape, const void* q, const void* k, const void* v,
+                      const void* alpha, const void* beta, float* state, void* o, void* stream);
+int kda_gdn2_decode_tokens(const kda_shape* shape, const void* q, const void* k, const void* v,
+                           const void* alpha, const void* erase_gate, const void* write_gate,
+                           float* state, void* o, void* stream);
+
 /* Human-readable text for a kda_status value (static storage). */
 const char* kda_status_string(int status);
 

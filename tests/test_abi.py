@@ -182,6 +182,29 @@ def test_gdn2_argument_errors(L):
     assert dec(w=_p(6, off=1)) == ALIGN
 
 
+def test_decode_tokens_argument_errors(L):
+    def dec(T=3, ptrs=None, g2=False):
+        shape = kda.Shape(2, T, 2, 64, 64, 0, 0)
+        p = ptrs or [_p(i) for i in range(9)]
+        if g2:
+            return L.kda_gdn2_decode_tokens(ctypes.byref(shape), p[0], p[1], p[2], p[3], p[4], p[6], p[7], p[5], None)
+        return L.kda_decode_tokens(ctypes.byref(shape), p[0], p[1], p[2], p[3], p[4], p[7], p[5], None)
+
+    assert dec(T=-1) == SHAPE
+    p = [_p(i) for i in range(9)]
+    p[4] = None                                    # beta
+    assert dec(ptrs=p) == NULL
+    p = [_p(i) for i in range(9)]
+    p[5] = _p(0, off=2 * 2 * 2 * 64 * 2 - 2)       # o starts inside the last token row of q
+    assert dec(ptrs=p) == ALIAS
+    p = [_p(i) for i in range(9)]
+    p[7] = _p(2, off=64)                           # state inside v
+    assert dec(ptrs=p) == ALIAS
+    p = [_p(i) for i in range(9)]
+    p[6] = None                                    # GDN-2 write gate
+    assert dec(ptrs=p, g2=True) == NULL
+
+
 def test_decode_argument_errors(L):
     assert L.kda_decode_step(None, *([None] * 8)) == NULL
     assert _decode(L, dtype=3) == DTYPE
