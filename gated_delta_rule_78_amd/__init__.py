@@ -15,7 +15,7 @@ import ctypes
 import os
 
 __all__ = ["chunk_fwd", "chunk_records", "chunk_apply_records", "chunk_fwd_debug", "decode_step",
-           "gdn2_chunk_fwd", "gdn2_decode_step", "decode_tokens", "gdn2_decode_tokens",
+           "gdn2_chunk_fwd", "gdn2_decode_step", "decode_tokens", "gdn2_decode_tokens", "chunk_fwd_varlen",
            "workspace_size", "pick_path", "lib", "version", "status_string",
            "LIB_PATH", "KdaError", "Shape", "BF16", "F32"]
 
@@ -64,6 +64,13 @@ def lib() -> ctypes.CDLL:
         L.kda_gdn2_chunk_fwd.restype = ctypes.c_int
         L.kda_gdn2_decode_step.argtypes = [SP, P, P, P, P, P, P, P, P, P]
         L.kda_gdn2_decode_step.restype = ctypes.c_int
+        L.kda_chunk_fwd_varlen_workspace_size.argtypes = [SP, ctypes.c_int]
+        L.kda_chunk_fwd_varlen_workspace_size.restype = ctypes.c_size_t
+        L.kda_chunk_fwd_varlen.argtypes = [SP, P, ctypes.c_int, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.kda_chunk_fwd_varlen.restype = ctypes.c_int
+        L.kda_gdn2_chunk_fwd_varlen.argtypes = [SP, P, ctypes.c_int, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t,
+                                                P]
+        L.kda_gdn2_chunk_fwd_varlen.restype = ctypes.c_int
         L.kda_decode_tokens.argtypes = [SP, P, P, P, P, P, P, P, P]
         L.kda_decode_tokens.restype = ctypes.c_int
         L.kda_gdn2_decode_tokens.argtypes = [SP, P, P, P, P, P, P, P, P, P]
@@ -378,3 +385,49 @@ def decode_tokens(q, k, v, alpha, beta, state, out=None, erase=None, write=None)
 def gdn2_decode_tokens(q, k, v, alpha, erase, write, state, out=None):
     """Gated DeltaNet-2 form of decode_tokens."""
     return decode_tokens(q, k, v, alpha, None, state, out=out, erase=erase, write=write)
+
+
+def chunk_fwd_varlen(q, k, v, alpha, beta, cu_seqlens, initial_state=None, out=None, final_state=None,
+                     want_final=True, workspace=None, erase=None, write=None):
+    """Packed variable-length batch: q, k, alpha [1,T,H,dk]; v [1,T,H,dv]; beta [1,T,H]
+    (or, for Gated DeltaNet-2, beta=None with erase [1,T,H,dk] and write [1,T,H,dv]);
+    cu_seqlens int32 [N+1] on the device; states [N,H,dk,dv] fp32.
+    Returns (o [1,T,H,dv], final_state [N,H,dk,dv] or None)."""
+    torch = _torch()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if B != 1:
+        raise ValueError("a packed batch has B == 1")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+        raise TypeError("cu_seqlens must be a 1-D int32 tensor")
+    N = cu_seqlens.numel() - 1
+    code = _dtype_code(q)
+    g2 = erase is not None or write is not None
+    dev = q.device
+    if out is None:
+        out = torch.empty((1, T, H, dv), dtype=q.dtype, device=dev)
+    if final_state is None and want_final:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    for t, nm in ((initial_state, "initial_state"), (final_state, "final_state")):
+        if t is not None and (t.dtype != torch.float32 or t.shape != (N, H, dk, dv)):
+            raise ValueError(f"{nm} must be float32 [N,H,dk,dv]")
+    shape = Shape(1, T, H, dk, dv, 64, code)
+    need = int(lib().kda_chunk_fwd_varlen_workspace_size(ctypes.byref(shape), N))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check((q, k, v, alpha, beta, erase, write, cu_seqlens, initial_state, out, final_state, workspace),
+           ("q", "k", "v", "alpha", "beta", "erase", "write", "cu_seqlens", "initial_state", "out", "final_state",
+            "workspace"), dev)
+    nbytes = workspace.numel() * workspace.element_size()
+    if g2:
+        rc = lib().kda_gdn2_chunk_fwd_varlen(ctypes.byref(shape), _ptr(cu_seqlens), N, _ptr(q), _ptr(k), _ptr(v),
+                                             _ptr(alpha), _ptr(erase), _ptr(write), _ptr(initial_state), _ptr(out),
+                                             _ptr(final_state), _ptr(workspace), ctypes.c_size_t(nbytes),
+                                             _stream(dev))
+    else:
+        rc = lib().kda_chunk_fwd_varlen(ctypes.byref(shape), _ptr(cu_seqlens), N, _ptr(q), _ptr(k), _ptr(v),
+                                        _ptr(alpha), _ptr(beta), _ptr(initial_state), _ptr(out), _ptr(final_state),
+                                        _ptr(workspace), ctypes.c_size_t(nbytes), _stream(dev))
+    if rc != 0:
+        raise KdaError(rc, "kda_chunk_fwd_varlen")
+    return out, final_state

@@ -82,14 +82,17 @@ struct ChunkPtrs {
 enum : int { kNeedQKAB = 1, kNeedVO = 2, kNeedWS = 4, kNeedG2 = 8 };
 
 // Host-side checks shared by the chunk entry points (nothing touches the device).
-int validate_chunk(const kda_shape* shape, const ChunkPtrs& p, int need) {
+// n_states: state tiles per head (B, or the number of sequences of a varlen batch);
+// ws_need_override: workspace bytes when not the fixed-length record count.
+int validate_chunk(const kda_shape* shape, const ChunkPtrs& p, int need, int64_t n_states = -1,
+                   int64_t ws_need_override = -1) {
   int es = 0;
   int rc = check_shape(shape, false, &es);
   if (rc) return rc;
   const kda_shape& s = *shape;
   if (s.dtype == KDA_F32 && (s.dk != 64 || s.dv != 64)) return KDA_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)s.B * s.T * s.H;
-  const int64_t st_bytes = (int64_t)s.B * s.H * s.dk * s.dv * 4;
+  const int64_t st_bytes = (n_states < 0 ? (int64_t)s.B : n_states) * s.H * s.dk * s.dv * 4;
   const bool g2 = (need & kNeedG2) != 0;
   if (rows > 0) {
     if ((need & kNeedQKAB) && (!p.q || !p.k || !p.alpha || (g2 ? !p.erase : !p.beta))) return KDA_ERR_NULL;
@@ -115,7 +118,7 @@ int validate_chunk(const kda_shape* shape, const ChunkPtrs& p, int need) {
   if (p.s0 != p.sT && overlap(rs, in[5])) return KDA_ERR_ALIAS;  // in place is allowed
   if (overlap(rs, ro)) return KDA_ERR_ALIAS;
   if (need & kNeedWS) {
-    const size_t ws_need = workspace_bytes_for(s);
+    const size_t ws_need = ws_need_override >= 0 ? (size_t)ws_need_override : workspace_bytes_for(s);
     if (ws_need > 0 && !p.ws) return KDA_ERR_NULL;
     if (p.ws_bytes < ws_need) return KDA_ERR_WORKSPACE;
     if (((uintptr_t)p.ws & 255u) != 0) return KDA_ERR_ALIGN;
@@ -150,6 +153,64 @@ int run_records(const kda_shape& s, const ChunkPtrs& p, void* stream) {
 // pass 2: the state walk over the records
 int run_apply(const kda_shape& s, const ChunkPtrs& p, void* stream) {
   return kda::launch_state(chunk_args(s, p, stream), p.ws) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+// Workspace of a packed variable-length batch: records [H][gmax], then the clamped
+// offsets, the chunk table, the first chunk of each sequence and the chunk count.
+struct VarlenLayout {
+  int64_t gmax;
+  size_t off_cs, off_tab, off_base, off_total, bytes;
+};
+
+VarlenLayout varlen_layout(const kda_shape& s, int n_seqs) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  VarlenLayout L;
+  L.gmax = ((int64_t)s.T + 63) / 64 + n_seqs;
+  L.off_cs = up((size_t)s.H * L.gmax * kda::record_bytes(s.dtype == KDA_BF16, s.dk));
+  L.off_tab = up(L.off_cs + (size_t)(n_seqs + 1) * 4);
+  L.off_base = up(L.off_tab + (size_t)L.gmax * 8);
+  L.off_total = up(L.off_base + (size_t)n_seqs * 4);
+  L.bytes = up(L.off_total + 4);
+  return L;
+}
+
+int chunk_varlen_impl(const kda_shape* shape, const int* cu, int n_seqs, ChunkPtrs p, void* stream) {
+  if (!shape) return KDA_ERR_NULL;
+  if (shape->B != 1 || n_seqs < 0 || n_seqs > (1 << 24)) return KDA_ERR_SHAPE;
+  if (!cu) return KDA_ERR_NULL;
+  if (((uintptr_t)cu & 3u) != 0) return KDA_ERR_ALIGN;
+  const VarlenLayout L = varlen_layout(*shape, n_seqs);
+  const bool g2 = p.erase != nullptr || p.write != nullptr;
+  int rc = validate_chunk(shape, p, kNeedQKAB | kNeedVO | kNeedWS | (g2 ? kNeedG2 : 0), n_seqs, (int64_t)L.bytes);
+  if (rc) return rc;
+  const kda_shape& s = *shape;
+  // the offsets are an input: no output (nor the workspace) may overlap them
+  const Range rc_ = range_of(cu, (int64_t)(n_seqs + 1) * 4);
+  const int64_t st_bytes = (int64_t)n_seqs * s.H * s.dk * s.dv * 4;
+  if (overlap(rc_, range_of(p.o, (int64_t)s.T * s.H * s.dv * (s.dtype == KDA_BF16 ? 2 : 4))) ||
+      overlap(rc_, range_of(p.sT, p.sT ? st_bytes : 0)) || overlap(rc_, range_of(p.ws, (int64_t)L.bytes)))
+    return KDA_ERR_ALIAS;
+  if (n_seqs == 0) return KDA_OK;
+  char* ws = (char*)p.ws;
+  kda::ChunkArgs a = chunk_args(s, p, stream);
+  a.cu = (const int*)(ws + L.off_cs);  // the kernels read the clamped offsets
+  a.n_seqs = n_seqs;
+  a.gmax = (int)L.gmax;
+  a.ctab = (const int*)(ws + L.off_tab);
+  a.ctab_base = (const int*)(ws + L.off_base);
+  a.ctab_total = (const int*)(ws + L.off_total);
+  kda::ChunkArgs at = a;
+  at.cu = cu;  // the table kernel reads the caller's offsets
+  if (kda::launch_varlen_table(at, (int*)(ws + L.off_cs), (int*)(ws + L.off_tab), (int*)(ws + L.off_base),
+                               (int*)(ws + L.off_total)) != hipSuccess)
+    return KDA_ERR_HIP;
+  const int64_t total = (int64_t)s.H * L.gmax;
+  int cpw = prep_cpw_override();
+  if (cpw <= 0) cpw = (int)((total + 1535) / 1536);
+  if (cpw < 1) cpw = 1;
+  if (cpw > L.gmax) cpw = (int)L.gmax;
+  if (kda::launch_prep(a, p.ws, cpw) != hipSuccess) return KDA_ERR_HIP;
+  return kda::launch_state(a, p.ws) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 }  // namespace
@@ -199,6 +260,34 @@ int kda_chunk_fwd_ws(const kda_shape* shape, const void* q, const void* k, const
   if (rc) return rc;
   rc = run_records(*shape, p, stream);
   return rc ? rc : run_apply(*shape, p, stream);
+}
+
+size_t kda_chunk_fwd_varlen_workspace_size(const kda_shape* shape, int n_seqs) {
+  int es = 0;
+  if (check_shape(shape, false, &es) != KDA_OK || shape->B != 1 || n_seqs < 0 || n_seqs > (1 << 24)) return 0;
+  if (shape->dtype == KDA_F32 && (shape->dk != 64 || shape->dv != 64)) return 0;
+  return varlen_layout(*shape, n_seqs).bytes;
+}
+
+int kda_chunk_fwd_varlen(const kda_shape* shape, const int* cu_seqlens, int n_seqs, const void* q, const void* k,
+                         const void* v, const void* alpha, const void* beta, const float* initial_state, void* o,
+                         float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+  const ChunkPtrs p{q, k, v, alpha, beta, initial_state, o, final_state, nullptr, workspace, workspace_bytes};
+  return chunk_varlen_impl(shape, cu_seqlens, n_seqs, p, stream);
+}
+
+int kda_gdn2_chunk_fwd_varlen(const kda_shape* shape, const int* cu_seqlens, int n_seqs, const void* q,
+                              const void* k, const void* v, const void* alpha, const void* erase_gate,
+                              const void* write_gate, const float* initial_state, void* o, float* final_state,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  ChunkPtrs p{q, k, v, alpha, nullptr, initial_state, o, final_state, nullptr, workspace, workspace_bytes};
+  p.erase = erase_gate;
+  p.write = write_gate;
+  if (!erase_gate || !write_gate) {
+    if (!shape) return KDA_ERR_NULL;
+    if ((int64_t)shape->T * shape->H > 0) return KDA_ERR_NULL;
+  }
+  return chunk_varlen_impl(shape, cu_seqlens, n_seqs, p, stream);
 }
 
 int kda_chunk_records(const kda_shape* shape, const void* q, const void* k, const void* alpha, const void* beta,

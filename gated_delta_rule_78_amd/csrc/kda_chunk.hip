@@ -207,8 +207,11 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
     const void* __restrict__ gq, const void* __restrict__ gk, const void* __restrict__ gv,
     const void* __restrict__ galpha, const void* __restrict__ gbeta, const float* s0,
     void* __restrict__ go, float* sT, float* __restrict__ dbg, int Tlen, int H, int DV, int BH,
-    char* __restrict__ ws, int cpw, const void* __restrict__ gerase) {
+    char* __restrict__ ws, int cpw, const void* __restrict__ gerase, const int* __restrict__ cu,
+    const int* __restrict__ ctab, const int* __restrict__ ctotal, int gmax) {
   static_assert(PREP || !G2, "the Gated DeltaNet-2 gates run on the two-pass path");
+  // cu != NULL (PREP only): packed variable-length batch; chunk indices are global
+  // (ctab[c] = (sequence, chunk of that sequence)) and records are [H][gmax]
   using K = Cfg<T, DK, VT>;
   using R = Raw<T>;
   constexpr int ES = K::ES;
@@ -230,7 +233,7 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
   const int n = lane & 15;
   // block -> (head, value tile); a head's tiles land on one XCD when the grid allows it
   const int NVT = PREP ? 1 : DV / VT;
-  const int nchunks = (Tlen + C - 1) / C;
+  const int nchunks = cu ? gmax : (Tlen + C - 1) / C;
   int bh, vt, c_begin, c_end;
   {
     const int bid = blockIdx.x;
@@ -239,7 +242,7 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
       bh = bid / nseg;
       vt = 0;
       c_begin = (bid % nseg) * cpw;
-      c_end = min(nchunks, c_begin + cpw);
+      c_end = min(cu ? *ctotal : nchunks, c_begin + cpw);
     } else {
       if (NVT > 1 && (BH & 7) == 0) {
         const int r = bid >> 3;
@@ -253,9 +256,23 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
       c_end = nchunks;
     }
   }
-  const int b = bh / H, h = bh % H;
+  const int b = bh / H, h = bh % H;  // varlen: bh = h (b = 0)
   const int v0 = vt * VT;
   auto row_base = [&](int t) -> size_t { return ((size_t)b * Tlen + t) * H + h; };
+  // where chunk c lies: token rows sbase + t0 .. of a sequence of len rows, record rec
+  struct Geo {
+    size_t sbase;
+    int len, t0;
+    size_t rec;
+  };
+  auto geo = [&](int c) -> Geo {
+    if (cu) {
+      const int sq = ctab[2 * c], lc = ctab[2 * c + 1];
+      return Geo{(size_t)cu[sq], cu[sq + 1] - cu[sq], lc * C, (size_t)h * gmax + c};
+    }
+    return Geo{(size_t)b * Tlen, Tlen, c * C, (size_t)bh * nchunks + c};
+  };
+  auto grow = [&](const Geo& gm, int t) -> size_t { return (gm.sbase + t) * H + h; };
 
   // ---------------- state tiles: rows 16 r + 4 g + e (key channels), column v0 + 16 wave + n
   f32x4_t S[DK / 16];
@@ -278,24 +295,25 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
   const int item_g = K::SPLIT ? tid % K::NITEM : tid;
   const bool item_ok = K::SPLIT ? (tid < 2 * K::NITEM) : (tid < K::NITEM);
   auto issue_qka = [&](int c) {
-    const int t0 = c * C;
+    const Geo gn = geo(c);
+    const int t0 = gn.t0;
 #pragma unroll
     for (int i = 0; i < K::VPT; ++i) {
       const int j = tid + NT * i;
       const int row = j / K::VROW_K, c16 = j % K::VROW_K;
-      const size_t off = row_base(min(t0 + row, Tlen - 1)) * DK * ES + (size_t)c16 * 16;
+      const size_t off = grow(gn, min(t0 + row, gn.len - 1)) * DK * ES + (size_t)c16 * 16;
       pq[i] = *(const uint4*)((const char*)gq + off);
       pk[i] = *(const uint4*)((const char*)gk + off);
       pa[i] = *(const uint4*)((const char*)galpha + off);
     }
     if constexpr (!G2) {
-      const size_t ib = row_base(min(t0 + (tid & (C - 1)), Tlen - 1));
+      const size_t ib = grow(gn, min(t0 + (tid & (C - 1)), gn.len - 1));
       pb = ES == 2 ? (uint32_t)((const uint16_t*)gbeta)[ib] : ((const uint32_t*)gbeta)[ib];
     } else if (item_ok) {
       const int bI = item_g / (DK / 2), cp = item_g % (DK / 2);
 #pragma unroll
       for (int m = 0; m < SUB; ++m)
-        pe[m] = R::ld((const char*)gerase + row_base(min(t0 + SUB * bI + m, Tlen - 1)) * DK * ES + 2 * cp * ES);
+        pe[m] = R::ld((const char*)gerase + grow(gn, min(t0 + SUB * bI + m, gn.len - 1)) * DK * ES + 2 * cp * ES);
     }
   };
   auto issue_v = [&](int c) {
@@ -324,22 +342,23 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
   const int item_off = (SUB * iI) * K::RS_DK + 2 * icp * ES;
 
   for (int chunk = c_begin; chunk < c_end; ++chunk) {
-    const int t0 = chunk * C;
-    const int nv = min(C, Tlen - t0);
+    const Geo gm = geo(chunk);
+    const int t0 = gm.t0;
+    const int nv = min(C, gm.len - t0);
     // ================= phase 0: staged inputs -> LDS (padded rows: q = k = 0, alpha = 1, beta = 0)
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < K::VPT; ++i) {
       const int j = tid + NT * i;
       const int row = j / K::VROW_K, c16 = j % K::VROW_K;
-      const bool ok = t0 + row < Tlen;
+      const bool ok = t0 + row < gm.len;
       const uint32_t one = R::kOneWord;
       const int off = row * K::RS_DK + c16 * 16;
       *(uint4*)(R_IN + 0 * C * K::RS_DK + off) = ok ? pq[i] : make_uint4(0, 0, 0, 0);
       *(uint4*)(R_IN + 1 * C * K::RS_DK + off) = ok ? pk[i] : make_uint4(0, 0, 0, 0);
       *(uint4*)(R_IN + 2 * C * K::RS_DK + off) = ok ? pa[i] : make_uint4(one, one, one, one);
     }
-    if (tid < C) BETA[tid] = (t0 + tid < Tlen) ? (G2 ? 1.f : __uint_as_float(ES == 2 ? pb << 16 : pb)) : 0.f;
+    if (tid < C) BETA[tid] = (t0 + tid < gm.len) ? (G2 ? 1.f : __uint_as_float(ES == 2 ? pb << 16 : pb)) : 0.f;
     if constexpr (G2) {
 #pragma unroll
       for (int m = 0; m < SUB; ++m) er_raw[m] = pe[m];
@@ -939,7 +958,7 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
       // (the LDS tiles are copied whole, padded rows and all: the record is their image)
       using RL = RecordLayout<T, DK>;
       static_assert(RL::RS_DK == K::RS_DK && RL::RS_C == K::RS_C, "record rows match the LDS tiles");
-      char* rec = ws + ((size_t)bh * nchunks + chunk) * RL::BYTES;
+      char* rec = ws + gm.rec * RL::BYTES;
       copy_flat<NT>(rec + RL::WW, WW, RL::QG - RL::WW, tid);
       copy_flat<NT>(rec + RL::QG, R_OP + K::OFF_QG, RL::KRT - RL::QG, tid);
       copy_flat<NT>(rec + RL::KRT, R_OP + K::OFF_KRT, RL::AT - RL::KRT, tid);
@@ -1038,7 +1057,7 @@ static hipError_t launch_chunk_t(const ChunkArgs& a) {
   const int BH = a.B * a.H;
   hipLaunchKernelGGL(kern, dim3(BH * (a.dv / VT)), dim3(K::NT), K::LDS, (hipStream_t)a.stream, a.q, a.k, a.v,
                      a.alpha, a.beta, a.s0, a.o, a.sT, a.dbg, a.T, a.H, a.dv, BH, (char*)nullptr, 0,
-                     (const void*)nullptr);
+                     (const void*)nullptr, (const int*)nullptr, (const int*)nullptr, (const int*)nullptr, 0);
   return hipGetLastError();
 }
 
@@ -1074,12 +1093,14 @@ static hipError_t launch_prep_t(const ChunkArgs& a, char* ws, int cpw) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int BH = a.B * a.H;
-  const int nchunks = (a.T + C - 1) / C;
+  // varlen: workgroups over (head, runs of global chunks); BH = H, b = 0
+  const int BH = a.cu ? a.H : a.B * a.H;
+  const int nchunks = a.cu ? a.gmax : (a.T + C - 1) / C;
   const int nseg = (nchunks + cpw - 1) / cpw;
   if ((long)BH * nseg == 0) return hipSuccess;
   hipLaunchKernelGGL(kern, dim3(BH * nseg), dim3(K::NT), K::LDS, (hipStream_t)a.stream, a.q, a.k, a.v, a.alpha,
-                     a.beta, a.s0, a.o, a.sT, (float*)nullptr, a.T, a.H, a.dv, BH, ws, cpw, a.erase);
+                     a.beta, a.s0, a.o, a.sT, (float*)nullptr, a.T, a.H, a.dv, BH, ws, cpw, a.erase, a.cu, a.ctab,
+                     a.ctab_total, a.gmax);
   return hipGetLastError();
 }
 

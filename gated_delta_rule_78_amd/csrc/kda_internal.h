@@ -33,6 +33,15 @@ struct ChunkArgs {
   // Gated DeltaNet-2 gates (both set, beta unused) or both NULL (KDA / CKDA)
   const void* erase = nullptr;  // [B, T, H, dk]
   const void* write = nullptr;  // [B, T, H, dv]
+  // packed variable-length batch (two-pass path only): B = 1, n_seqs sequences at device
+  // offsets cu[0..n_seqs]; the chunk table (gmax entries (sequence, chunk), the first
+  // global chunk of each sequence, the number of chunks) lives in the workspace
+  const int* cu = nullptr;
+  int n_seqs = 0;
+  int gmax = 0;
+  const int* ctab = nullptr;       // [gmax][2]
+  const int* ctab_base = nullptr;  // [n_seqs]
+  const int* ctab_total = nullptr; // [1]
 };
 
 hipError_t launch_decode(const DecodeArgs& a);
@@ -41,5 +50,7 @@ hipError_t launch_chunk(const ChunkArgs& a);
 hipError_t launch_prep(const ChunkArgs& a, void* ws, int cpw);
 hipError_t launch_state(const ChunkArgs& a, const void* ws);
 size_t record_bytes(bool bf16, int dk);
+// varlen: clamped offsets and the chunk table from a.cu (one workgroup)
+hipError_t launch_varlen_table(const ChunkArgs& a, int* cs, int* ctab, int* cbase, int* ctotal);
 
 }  // namespace kda

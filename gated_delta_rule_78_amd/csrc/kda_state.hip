@@ -244,7 +244,9 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
                                                                          const void* __restrict__ gv,
                                                                          const float* s0, void* __restrict__ go,
                                                                          float* sT, int Tlen, int H, int DV, int BH,
-                                                                         const void* __restrict__ gw) {
+                                                                         const void* __restrict__ gw,
+                                                                         const int* __restrict__ cu,
+                                                                         const int* __restrict__ cbase, int gmax) {
   using K = SCfg<T, DK, VT, G2>;
   constexpr int NP = K::NP;
   using RL = typename K::RL;
@@ -279,10 +281,23 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
       vt = bid % NVT;
     }
   }
+  // the sequence this workgroup walks: batch row b of length Tlen, or (packed varlen
+  // batch, cu != NULL) sequence b = bh / H of length cu[b + 1] - cu[b]
   const int b = bh / H, h = bh % H;
   const int v0 = vt * VT;
-  const int nchunks = (Tlen + C - 1) / C;
-  const char* rec0 = ws + (size_t)bh * nchunks * RL::BYTES;
+  size_t sbase;
+  int slen;
+  const char* rec0;
+  if (cu) {
+    sbase = (size_t)cu[b];
+    slen = cu[b + 1] - cu[b];
+    rec0 = ws + ((size_t)h * gmax + cbase[b]) * RL::BYTES;
+  } else {
+    sbase = (size_t)b * Tlen;
+    slen = Tlen;
+    rec0 = ws + (size_t)bh * ((Tlen + C - 1) / C) * RL::BYTES;
+  }
+  const int nchunks = (slen + C - 1) / C;
 
   f32x4_t S[DK / 16];
 #pragma unroll
@@ -303,7 +318,7 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
     for (int x = pw; x < K::N_DMA_V; x += NP) {
       const int sl = x * 64 + lane;
       const int row = sl / K::UPR, u = sl % K::UPR;
-      const size_t gr = ((size_t)b * Tlen + min(t0 + row, Tlen - 1)) * H + h;
+      const size_t gr = (sbase + min(t0 + row, slen - 1)) * H + h;
       const size_t off = (gr * DV + v0) * ES + (size_t)u * 16;
       dma16((const char*)gv + off, v_dst + x * 1024);
       if constexpr (G2) dma16((const char*)gw + off, w_dst + x * 1024);
@@ -317,17 +332,17 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
   // the staged outputs of chunk c (in the consumed v tile `vv`) -> o
   auto store_o = [&](int c, const char* vv) {
     const int t0 = c * C;
-    const int nv = min(C, Tlen - t0);
+    const int nv = min(C, slen - t0);
     for (int j = tid; j < C * K::UPR; j += NT) {
       const int row = j / K::UPR, u = j % K::UPR;
       if (row < nv)
-        *(uint4*)((char*)go + (((size_t)b * Tlen + t0 + row) * H + h) * DV * ES + (size_t)v0 * ES + (size_t)u * 16) =
+        *(uint4*)((char*)go + ((sbase + t0 + row) * H + h) * DV * ES + (size_t)v0 * ES + (size_t)u * 16) =
             *(const uint4*)(vv + row * K::RS_V + u * 16);
     }
   };
   // v rows past the end of the sequence read as zero
   auto pad_rows = [&](int c, char* vv) {
-    const int nv = Tlen - c * C;
+    const int nv = slen - c * C;
     if (nv < C) {
       for (int j = nv * K::UPR + tid; j < C * K::UPR; j += NT) *(uint4*)(vv + j * 16) = make_uint4(0, 0, 0, 0);
       lds_barrier();
@@ -388,8 +403,10 @@ static hipError_t launch_state_t(const ChunkArgs& a, const void* ws) {
   using K = SCfg<T, DK, VT, G2>;
   const int BH = a.B * a.H;
   auto kern = chunk_state_kernel<T, DK, VT, G2>;
-  hipLaunchKernelGGL(kern, dim3(BH * (a.dv / VT)), dim3(K::NT), 0, (hipStream_t)a.stream, (const char*)ws, a.v,
-                     a.s0, a.o, a.sT, a.T, a.H, a.dv, BH, a.write);
+  // varlen: one chain per (sequence, head): BH = n_seqs * H
+  const int BHc = a.cu ? a.n_seqs * a.H : BH;
+  hipLaunchKernelGGL(kern, dim3(BHc * (a.dv / VT)), dim3(K::NT), 0, (hipStream_t)a.stream, (const char*)ws, a.v,
+                     a.s0, a.o, a.sT, a.T, a.H, a.dv, BHc, a.write, a.cu, a.ctab_base, a.gmax);
   return hipGetLastError();
 }
 
@@ -413,7 +430,7 @@ static int pick_state_vt(const ChunkArgs& a) {
   if (o == 16 || o == 32 || o == 64) {
     vt = o <= a.dv ? o : a.dv;
   } else {
-    const long bh = (long)a.B * a.H;
+    const long bh = (long)(a.cu ? a.n_seqs : a.B) * a.H;
     vt = bh * (a.dv / 64) >= 256 ? 64 : bh * (a.dv / 32) >= 256 ? 32 : 16;
   }
   return vt < cap ? vt : cap;
@@ -437,7 +454,7 @@ static hipError_t launch_state_g(const ChunkArgs& a, const void* ws) {
 }
 
 hipError_t launch_state(const ChunkArgs& a, const void* ws) {
-  if (a.B * a.H == 0) return hipSuccess;
+  if ((a.cu ? a.n_seqs : a.B) * a.H == 0) return hipSuccess;
   return a.write ? launch_state_g<true>(a, ws) : launch_state_g<false>(a, ws);
 }
 

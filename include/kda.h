@@ -143,6 +143,36 @@ int kda_chunk_apply_records(const kda_shape* shape, const void* workspace, size_
                             void* stream);
 
 /*
+ * Packed variable-length batch (two-pass forward): n_seqs sequences lie back to back
+ * along T, sequence i at token rows [cu_seqlens[i], cu_seqlens[i + 1]).  Each sequence
+ * is cut into its own chunks of 64 (no chunk straddles two sequences) and runs the
+ * recurrence from its own start state, exactly as a separate kda_chunk_fwd call would.
+ *   shape->B        : must be 1 (KDA_ERR_SHAPE otherwise); shape->T = total tokens
+ *   cu_seqlens      : DEVICE int32 [n_seqs + 1], 4-byte aligned; offsets are read on
+ *                     the device, clamped to [0, T] and made non-decreasing
+ *                     (cu_seqlens[0] is taken as 0); token rows after the last offset
+ *                     belong to no sequence and are not written in o
+ *   initial_state   : [n_seqs, H, dk, dv] fp32 or NULL (zeros)
+ *   final_state     : [n_seqs, H, dk, dv] fp32 or NULL; may equal initial_state
+ *   workspace       : kda_chunk_fwd_varlen_workspace_size(shape, n_seqs) bytes, 256-byte
+ *                     aligned (records of at most ceil(T/64) + n_seqs chunks per head
+ *                     and the chunk table)
+ * q, k, alpha [1, T, H, dk], v and o [1, T, H, dv], beta [1, T, H]; other rules and
+ * errors as kda_chunk_fwd_ws.  kda_gdn2_chunk_fwd_varlen takes the Gated DeltaNet-2
+ * gates (below) in place of beta.
+ */
+size_t kda_chunk_fwd_varlen_workspace_size(const kda_shape* shape, int n_seqs); /* 0 if invalid */
+int kda_chunk_fwd_varlen(const kda_shape* shape, const int* cu_seqlens, int n_seqs, const void* q,
+                         const void* k, const void* v, const void* alpha, const void* beta,
+                         const float* initial_state, void* o, float* final_state,
+                         void* workspace, size_t workspace_bytes, void* stream);
+int kda_gdn2_chunk_fwd_varlen(const kda_shape* shape, const int* cu_seqlens, int n_seqs,
+                              const void* q, const void* k, const void* v, const void* alpha,
+                              const void* erase_gate, const void* write_gate,
+                              const float* initial_state, void* o, float* final_state,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Gated DeltaNet-2 ("Gated DeltaNet-2" summary, section 1): the scalar beta is split
  * into an erase gate b_t per key channel and a write gate w_t per value channel,
  *   S_t = (I - k_t (b_t o k_t)^T) Diag(alpha_t) S_{t-1} + k_t (w_t o v_t)^T,

@@ -205,6 +205,30 @@ def test_decode_tokens_argument_errors(L):
     assert dec(ptrs=p, g2=True) == NULL
 
 
+def test_varlen_argument_errors(L):
+    shape = kda.Shape(1, 300, 2, 64, 64, 64, 0)
+    need = L.kda_chunk_fwd_varlen_workspace_size(ctypes.byref(shape), 4)
+    # records of at most ceil(300/64) + 4 chunks per head, plus the chunk table
+    one = L.kda_chunk_fwd_workspace_size(ctypes.byref(kda.Shape(1, 64, 1, 64, 64, 64, 0)))
+    assert need >= 2 * (5 + 4) * one
+    assert L.kda_chunk_fwd_varlen_workspace_size(ctypes.byref(kda.Shape(2, 300, 2, 64, 64, 64, 0)), 4) == 0
+    sz = ctypes.c_size_t
+
+    def fwd(sh=shape, cu=_p(8), n=4, ws=_p(9), nb=need, o=_p(5), beta=_p(4)):
+        p = [_p(i) for i in range(6)]
+        return L.kda_chunk_fwd_varlen(ctypes.byref(sh), cu, n, p[0], p[1], p[2], p[3], beta, None, o, None, ws,
+                                      sz(nb), None)
+
+    assert fwd(sh=kda.Shape(2, 300, 2, 64, 64, 64, 0)) == SHAPE
+    assert fwd(n=-1) == SHAPE
+    assert fwd(cu=None) == NULL
+    assert fwd(cu=_p(8, off=2)) == ALIGN
+    assert fwd(nb=need - 1) == WORKSPACE
+    assert fwd(beta=None) == NULL
+    assert fwd(o=_p(8, off=16)) == ALIAS             # output over the offsets
+    assert fwd(ws=_p(8)) == ALIAS                    # workspace over the offsets
+
+
 def test_decode_argument_errors(L):
     assert L.kda_decode_step(None, *([None] * 8)) == NULL
     assert _decode(L, dtype=3) == DTYPE
