@@ -44,28 +44,18 @@
 // layout, and an accumulator pair is directly a matrix-core B fragment (the
 // k-slot order is permuted to match).  q, k, alpha, beta, v of the next chunk
 // are prefetched into registers while the current chunk computes.
+#include <stdlib.h>
+
 #include <type_traits>
 
 #include "kda_common.h"
 #include "kda_internal.h"
 #include "kda_record.h"
+#include "kda_tile.h"
 
 namespace kda {
 
 namespace {
-
-constexpr int C = 64;
-constexpr int SUB = 16;
-constexpr int NB = C / SUB;
-
-// Off-diagonal tile jobs (I, J) and the block-product Pi they need
-// (-1: adjacent, none; 0: g1; 1: g1 g2; 2: g2).
-__constant__ int kOffI[6] = {1, 2, 3, 2, 3, 3};
-__constant__ int kOffJ[6] = {0, 1, 2, 0, 1, 0};
-__constant__ int kOffPi[6] = {-1, -1, -1, 0, 2, 1};
-// Upper 16x16 tiles of A~ that must read as zero.
-__constant__ int kUpI[6] = {0, 0, 0, 1, 1, 2};
-__constant__ int kUpJ[6] = {1, 2, 3, 2, 3, 3};
 
 template <typename T, int DK, int VT>
 struct Cfg {
@@ -124,74 +114,6 @@ struct Cfg {
   static constexpr bool SPLIT = NT >= 2 * NITEM;
   static_assert(NITEM <= NT, "one gate item per thread");
 };
-
-// Two adjacent channels of one row, kept packed until used.
-template <typename T>
-struct Raw;
-template <>
-struct Raw<bf16_t> {
-  typedef uint32_t type;
-  __device__ __forceinline__ static type ld(const char* p) { return *(const uint32_t*)p; }
-  __device__ __forceinline__ static void unpack(type w, float& a, float& b) {
-    a = __uint_as_float(w << 16);
-    b = __uint_as_float(w & 0xFFFF0000u);
-  }
-  __device__ __forceinline__ static void st(char* p, float a, float b) { *(uint32_t*)p = pack_bf16x2(a, b); }
-  static constexpr uint32_t kOneWord = 0x3F803F80u;  // two bf16 ones
-};
-template <>
-struct Raw<float> {
-  typedef float2 type;
-  __device__ __forceinline__ static type ld(const char* p) { return *(const float2*)p; }
-  __device__ __forceinline__ static void unpack(type w, float& a, float& b) {
-    a = w.x;
-    b = w.y;
-  }
-  __device__ __forceinline__ static void st(char* p, float a, float b) { *(float2*)p = make_float2(a, b); }
-  static constexpr uint32_t kOneWord = 0x3F800000u;
-};
-
-__device__ __forceinline__ void st_elem(char* p, float x, int es) {
-  if (es == 2)
-    *(uint16_t*)p = f32_to_bf16(x);
-  else
-    *(float*)p = x;
-}
-
-// eight consecutive elements of one row (16-byte aligned for bf16, 32-byte for fp32)
-template <typename T>
-__device__ __forceinline__ void st_row8(char* p, const float (&v)[8]);
-template <>
-__device__ __forceinline__ void st_row8<bf16_t>(char* p, const float (&v)[8]) {
-  *(uint4*)p = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                          pack_bf16x2(v[6], v[7]));
-}
-template <>
-__device__ __forceinline__ void st_row8<float>(char* p, const float (&v)[8]) {
-  ((float4*)p)[0] = make_float4(v[0], v[1], v[2], v[3]);
-  ((float4*)p)[1] = make_float4(v[4], v[5], v[6], v[7]);
-}
-
-// `bytes` (a multiple of 16) from LDS to global memory, 16 bytes per thread and step
-template <int NT>
-__device__ __forceinline__ void copy_flat(char* dst, const char* src, int bytes, int tid) {
-  for (int j = tid; j < bytes / 16; j += NT) *(uint4*)(dst + j * 16) = *(const uint4*)(src + j * 16);
-}
-
-// value of `x` held by lane `src` (0..15) of this lane's 16-lane DPP row
-template <int src>
-__device__ __forceinline__ float row_bcast(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + src, 0xF,
-                                                               0xF, true));
-}
-
-// 16x16 fp32 product step: acc += A B with A[row n][k-slot 4 g + s], B[k-slot 4 g + s][col n]
-__device__ __forceinline__ void mm4(f32x4_t& acc, const float (&a)[4], const float (&b)[4]) {
-#ifndef KDA_HOST_PASS
-#pragma unroll
-  for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
-#endif
-}
 
 }  // namespace
 
@@ -1111,7 +1033,13 @@ static hipError_t launch_prep_g(const ChunkArgs& a, void* ws, int cpw) {
                     : launch_prep_t<bf16_t, 128, G2>(a, (char*)ws, cpw);
 }
 
+// bf16 records come from the kernel sized for two workgroups per compute unit; the
+// first half of the fused kernel writes the fp32 ones (and the bf16 ones when
+// KDA_RECORDS_FUSED is set in the environment, for comparison)
 hipError_t launch_prep(const ChunkArgs& a, void* ws, int cpw) {
+  if (a.bf16 && (a.dk == 64 || a.dk == 128) && (long)C * a.H * a.dk * 2 < (1L << 32) &&
+      !getenv("KDA_RECORDS_FUSED"))
+    return launch_records(a, ws, cpw);
   return a.erase ? launch_prep_g<true>(a, ws, cpw) : launch_prep_g<false>(a, ws, cpw);
 }
 

@@ -48,6 +48,8 @@ hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_chunk(const ChunkArgs& a);
 // two-pass forward: per-chunk records into ws (cpw chunks per workgroup), then the state pass
 hipError_t launch_prep(const ChunkArgs& a, void* ws, int cpw);
+// the same records from the bf16 kernel sized for two workgroups per compute unit
+hipError_t launch_records(const ChunkArgs& a, void* ws, int cpw);
 hipError_t launch_state(const ChunkArgs& a, const void* ws);
 size_t record_bytes(bool bf16, int dk);
 // varlen: clamped offsets and the chunk table from a.cu (one workgroup)

@@ -1,0 +1,770 @@
+// kda_records.hip -- first pass of the two-pass chunk forward (bf16): the record of every
+// chunk (-W, Q o gamma, (K o rho)^T, A~, M~, gamma_last), sized so that two workgroups
+// share a compute unit (<= 80 KiB of LDS, <= 256 registers per lane): while one
+// workgroup waits on a dependent LDS read or a barrier, the other issues.
+//
+// The math is that of the chunk-WY product form on the SFDA page ("El Teorema de
+// Chunk-WY Constructivo"; "Principales Contribuciones" item 3) and the decay-absorbed WY
+// construction on the Gated DeltaNet-2 page (section 3, efficient chunkwise parallel
+// training), computed exactly as the fused chunk kernel does:
+//   r_ij = prod_{m=j+1..i} alpha_m, T_ij = beta_i sum_c k_ic k_jc r_ijc (j < i),
+//   A_ij = sum_c q_ic k_jc r_ijc (j <= i), M = (I + T)^-1, W = M diag(beta) (K o gamma),
+// with the gate products local to 16-row sub-blocks (off-diagonal tiles anchored at
+// the block edges, diagonal tiles split into the levels 8, 4, 2, 1 of the highest bit
+// where the two local indices differ).
+//
+// What differs from the fused kernel's first half, to fit the smaller LDS:
+//   * q, k, alpha are not staged in LDS: a gate item (16 rows x 2 channels of one
+//     sub-block) reads them from global memory into registers, one chunk ahead;
+//   * the diagonal of A (r_ii = 1) is the items' two-channel dot products summed
+//     across the block's lanes, not a matrix-core pass over the raw q, k tiles;
+//   * the four levels run as three passes through two level buffers, their results
+//     stay in registers until every product is done;
+//   * Q o gamma and (K o rho)^T go from the items' registers straight to the record;
+//     only -W, A~, M~ and gamma_last are assembled in LDS and copied out.
+#include "kda_common.h"
+#include "kda_internal.h"
+#include "kda_record.h"
+#include "kda_tile.h"
+
+namespace kda {
+
+namespace {
+
+template <int DK>
+struct RCfg {
+  using T = bf16_t;
+  static constexpr int ES = 2;
+  static constexpr int NT = 256;
+  static constexpr int KS = DK / 32;
+  static constexpr int RS_DK = DK * ES + 16;  // [pos][channel] rows (padded)
+  static constexpr int RS_C = C * ES + 16;    // [channel][pos] and [pos][pos] rows
+  static constexpr int RS_F = C * 4 + 16;     // fp32 [pos][pos]
+  static constexpr int RS_MB = SUB * 4 + 16;  // fp32 transposed 16x16 blocks
+  static constexpr int LVL_ROWS = 24;         // per block: 8 q rows, 8 key rows (upper ranks), 8 k rows
+  static constexpr int SZ_LV = NB * LVL_ROWS * RS_DK;
+  static constexpr int mx(int a, int b) { return a > b ? a : b; }
+  // region X: Xq, Xk of blocks 1..3 and Y of blocks 0..2 -> level buffer 1 -> (K o gamma)^T, M (fp32)
+  static constexpr int OFF_XQ = 0;
+  static constexpr int OFF_XK = OFF_XQ + 3 * SUB * RS_DK;
+  static constexpr int OFF_Y = OFF_XK + 3 * SUB * RS_DK;
+  static constexpr int SZ_X_A = OFF_Y + 3 * SUB * RS_DK;
+  static constexpr int OFF_KGT = 0;
+  static constexpr int OFF_MM = OFF_KGT + DK * RS_C;
+  static constexpr int SZ_X_B = OFF_MM + C * RS_F;
+  static constexpr int SZ_X = mx(mx(SZ_X_A, SZ_LV), SZ_X_B);
+  // region L: level buffer 0 -> D (fp32: T before its beta row scale), the transposed
+  // inverse blocks (MB), later M~ over MB; -W over D once the inverse is done.  A~ lies
+  // past the level buffer, so its zero entries (upper tiles, upper triangles of the
+  // diagonal tiles) are written once and never overwritten.
+  static constexpr int NMB = 5;
+  static constexpr int OFF_TT = 0;
+  static constexpr int OFF_MB = OFF_TT + C * RS_F;
+  static constexpr int OFF_AT = OFF_MB + mx(NMB * SUB * RS_MB, C * RS_C);
+  static constexpr int SZ_L = OFF_AT + C * RS_C;
+  static_assert(SZ_LV <= OFF_AT, "level buffer 0 stays clear of A~");
+  static constexpr int BASE_X = 0;
+  static constexpr int BASE_L = BASE_X + SZ_X;
+  static constexpr int BASE_GT = BASE_L + SZ_L;         // block totals g[4][DK]
+  static constexpr int BASE_GC = BASE_GT + NB * DK * 4;  // gamma of the last row [DK]
+  static constexpr int BASE_BETA = BASE_GC + DK * 4;     // beta [C]
+  static constexpr int LDS = BASE_BETA + C * 4;
+  static_assert(LDS <= 80 * 1024, "two workgroups per compute unit");
+  static_assert(C * RS_DK <= C * RS_F, "-W fits over D");
+  // gate items: (block, channel pair); GRP items (lanes) per block
+  static constexpr int GRP = DK / 2;
+  static constexpr int NITEM = NB * GRP;
+  static_assert(NITEM <= NT && GRP % 16 == 0, "item layout");
+};
+
+// Sum of d[m] over the GRP lanes of this lane's group, for 16 values at once: four
+// exchange steps each halve the values a lane keeps, then plain butterfly adds.  The
+// lane ends with the sum of value m = (lane % GRP) / (GRP / 16).
+template <int GRP>
+__device__ __forceinline__ float reduce16(const float (&d)[16], int lane) {
+  float v8[8], v4[4], v2[2];
+  {
+    const bool up = lane & (GRP / 2);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float send = up ? d[j] : d[j + 8];
+      v8[j] = (up ? d[j + 8] : d[j]) + __shfl_xor(send, GRP / 2);
+    }
+  }
+  {
+    const bool up = lane & (GRP / 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float send = up ? v8[j] : v8[j + 4];
+      v4[j] = (up ? v8[j + 4] : v8[j]) + __shfl_xor(send, GRP / 4);
+    }
+  }
+  {
+    const bool up = lane & (GRP / 8);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float send = up ? v4[j] : v4[j + 2];
+      v2[j] = (up ? v4[j + 2] : v4[j]) + __shfl_xor(send, GRP / 8);
+    }
+  }
+  const bool up = lane & (GRP / 16);
+  float v = (up ? v2[1] : v2[0]) + __shfl_xor(up ? v2[0] : v2[1], GRP / 16);
+#pragma unroll
+  for (int mask = GRP / 32; mask >= 1; mask >>= 1) v += __shfl_xor(v, mask);
+  return v;
+}
+
+// Level-lam result tile of diagonal block I into A~ (bf16) and D (fp32): entry (row, n)
+// holds the A value (row < 8) or D value (row >= 8) of upper-half rank u = row & 7 and
+// lower-half rank n (n < 8).  It is a pair of the block when both ranks lie in segment
+// s = n / lam; the pair's positions are then 16 I + u + lam (s + 1) and 16 I + n + lam s.
+template <int lam, int RS_C, int LDF>
+__device__ __forceinline__ void put_level(const f32x4_t& acc, int I, int g, int n, char* AT, float* TT) {
+  if (n < 8) {
+    const int s = n / lam;
+    const int u0 = 4 * (g & 1);
+    const int pi = 16 * I + lam * (s + 1) + u0;  // position of rank u0
+    const int pj = 16 * I + n + lam * s;
+    if (g < 2) {
+      char* base = AT + pi * RS_C + pj * 2;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((u0 + e) / lam == s) *(uint16_t*)(base + e * RS_C) = f32_to_bf16(acc[e]);
+    } else {
+      float* base = TT + pi * LDF + pj;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((u0 + e) / lam == s) base[e * LDF] = acc[e];
+    }
+  }
+}
+
+}  // namespace
+
+template <int DK, bool G2>
+__global__ __launch_bounds__(256, 2) void chunk_records_kernel(
+    const void* __restrict__ gq, const void* __restrict__ gk, const void* __restrict__ galpha,
+    const void* __restrict__ gbeta, const void* __restrict__ gerase, int Tlen, int H, char* __restrict__ ws,
+    int cpw, const int* __restrict__ cu, const int* __restrict__ ctab, const int* __restrict__ ctotal, int gmax) {
+  // cu != NULL: packed variable-length batch; chunk indices are global (ctab[c] =
+  // (sequence, chunk of that sequence)) and records are [H][gmax]
+  using K = RCfg<DK>;
+  using RL = RecordLayout<bf16_t, DK>;
+  using R = Raw<bf16_t>;
+  static_assert(RL::RS_DK == K::RS_DK && RL::RS_C == K::RS_C, "record rows match the LDS tiles");
+  constexpr int NT = K::NT;
+  constexpr int LDF = K::RS_F / 4;
+  constexpr int GRP = K::GRP;
+  extern __shared__ __align__(16) char smem[];
+  char* const R_X = smem + K::BASE_X;
+  char* const R_L = smem + K::BASE_L;
+  float* const GT = (float*)(smem + K::BASE_GT);
+  float* const GC = (float*)(smem + K::BASE_GC);
+  float* const BETA = (float*)(smem + K::BASE_BETA);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  const int nchunks = cu ? gmax : (Tlen + C - 1) / C;
+  const int nseg = (nchunks + cpw - 1) / cpw;
+  const int bh = blockIdx.x / nseg;
+  const int c_begin = (blockIdx.x % nseg) * cpw;
+  const int c_end = min(cu ? *ctotal : nchunks, c_begin + cpw);
+  const int b = bh / H, h = bh % H;  // varlen: bh = h (b = 0)
+  struct Geo {
+    size_t sbase;
+    int len, t0;
+    size_t rec;
+  };
+  auto geo = [&](int c) -> Geo {
+    if (cu) {
+      const int sq = ctab[2 * c], lc = ctab[2 * c + 1];
+      return Geo{(size_t)cu[sq], cu[sq + 1] - cu[sq], lc * C, (size_t)h * gmax + c};
+    }
+    return Geo{(size_t)b * Tlen, Tlen, c * C, (size_t)bh * nchunks + c};
+  };
+  auto grow = [&](const Geo& gm, int t) -> size_t { return (gm.sbase + t) * H + h; };
+
+  // gate item of this thread: block iI, channels 2 icp, 2 icp + 1 (wave-uniform presence)
+  const bool has_item = tid < K::NITEM;
+  const int iI = tid / GRP;
+  const int icp = tid % GRP;
+
+  // one chunk ahead: the item's 16 rows of q, k, alpha (and erase gate), raw; beta of row tid & 63.
+  // Loads are unconditional (rows past the end are clamped to the last row and replaced
+  // when used) so that no wait is forced at issue time.
+  uint32_t pq[SUB], pk[SUB], pa[SUB], pe[G2 ? SUB : 1];
+  uint32_t pb = 0u;
+  auto issue = [&](int c) {
+    const Geo gn = geo(c);
+    // chunk base (wave-uniform, 64-bit) + 32-bit row offsets: token rows are H * DK * 2
+    // bytes apart and a chunk spans fewer than 2^32 bytes (checked at launch)
+    const size_t base = grow(gn, gn.t0) * DK * 2;
+    const uint32_t rs = (uint32_t)H * DK * 2;
+    const int last = gn.len - 1 - gn.t0;
+    if (has_item) {
+#pragma unroll
+      for (int m = 0; m < SUB; ++m) {
+        const uint32_t off = (uint32_t)min(SUB * iI + m, last) * rs + 4 * icp;
+        pq[m] = *(const uint32_t*)((const char*)gq + base + off);
+        pk[m] = *(const uint32_t*)((const char*)gk + base + off);
+        pa[m] = *(const uint32_t*)((const char*)galpha + base + off);
+        if constexpr (G2) pe[m] = *(const uint32_t*)((const char*)gerase + base + off);
+      }
+    }
+    if constexpr (!G2) pb = ((const uint16_t*)gbeta)[grow(gn, min(gn.t0 + (tid & (C - 1)), gn.len - 1))];
+  };
+  if (c_begin < c_end) issue(c_begin);
+  {
+    // the entries of A~ that stay zero: six upper tiles (16 rows x 2 segments of 8 each)
+    // and the strict upper triangles of the four diagonal tiles
+    char* const AT = R_L + K::OFF_AT;
+    for (int x = tid; x < 6 * 16 * 2; x += NT) {
+      const int t = x >> 5, i = (x >> 1) & 15, j0 = 8 * (x & 1);
+      const float z8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      st_row8<bf16_t>(AT + (16 * kUpI[t] + i) * K::RS_C + (16 * kUpJ[t] + j0) * 2, z8);
+    }
+    for (int x = tid; x < NB * SUB * SUB; x += NT) {
+      const int I = x >> 8, i = (x >> 4) & 15, j = x & 15;
+      if (j > i) *(uint16_t*)(AT + (16 * I + i) * K::RS_C + (16 * I + j) * 2) = 0;
+    }
+  }
+
+  for (int chunk = c_begin; chunk < c_end; ++chunk) {
+    const Geo gm = geo(chunk);
+    const int t0 = gm.t0;
+    char* const rec = ws + gm.rec * RL::BYTES;
+    lds_barrier();  // the previous chunk's record is out of LDS
+    // lane-dependent indices, recomputed per chunk from an opaque copy of the thread
+    // index: otherwise every LDS address derived from them is hoisted out of the loop
+    // and held (spilled) across it
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int g = lane >> 4;
+    const int n = lane & 15;
+    const int iI = tid / GRP;
+    const int icp = tid % GRP;
+
+    // ---------------- item registers, fp32 (rows past the end: q = k = 0, alpha = 1)
+    float qf[SUB][2], kf[SUB][2], al[SUB][2];
+    if (t0 + C <= gm.len) {  // a whole chunk (wave-uniform): no row is masked
+#pragma unroll
+      for (int m = 0; m < SUB; ++m) {
+        R::unpack(pq[m], qf[m][0], qf[m][1]);
+        R::unpack(pk[m], kf[m][0], kf[m][1]);
+        R::unpack(pa[m], al[m][0], al[m][1]);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < SUB; ++m) {
+        const bool ok = t0 + SUB * iI + m < gm.len;
+        R::unpack(ok ? pq[m] : 0u, qf[m][0], qf[m][1]);
+        R::unpack(ok ? pk[m] : 0u, kf[m][0], kf[m][1]);
+        R::unpack(ok ? pa[m] : R::kOneWord, al[m][0], al[m][1]);
+      }
+    }
+    // the key as the erase side reads it: k (KDA), b o k (Gated DeltaNet-2; the erase gate
+    // stays packed, the product is formed at each use)
+    uint32_t er[G2 ? SUB : 1];
+    if constexpr (G2) {
+#pragma unroll
+      for (int m = 0; m < SUB; ++m) er[m] = pe[m];
+    }
+    auto read_key = [&](int m, float& e0, float& e1) {
+      e0 = kf[m][0];
+      e1 = kf[m][1];
+      if constexpr (G2) {
+        float b0, b1;
+        R::unpack(er[m], b0, b1);
+        e0 *= b0;
+        e1 *= b1;
+      }
+    };
+    if (tid < C) BETA[tid] = (t0 + tid < gm.len) ? (G2 ? 1.f : __uint_as_float(pb << 16)) : 0.f;
+    // level-lam operands of the item's block into level buffer `buf`: rows u (q) and
+    // 8 + u (erase-side key) of the upper-half ranks, prefix products from the upper
+    // half's start; rows 16 + v (k) of the lower-half ranks, suffix products to its end
+    auto write_level = [&](char* buf, int lam) {
+      char* LA = buf + iI * K::LVL_ROWS * K::RS_DK + 4 * icp;
+      char* LB = LA + 16 * K::RS_DK;
+      float f0 = 1.f, f1 = 1.f;
+#pragma unroll
+      for (int m = 0; m < SUB; ++m) {
+        if (m & lam) {
+          if ((m & (lam - 1)) == 0) {
+            f0 = al[m][0];
+            f1 = al[m][1];
+          } else {
+            f0 *= al[m][0];
+            f1 *= al[m][1];
+          }
+          const int u = (m / (2 * lam)) * lam + (m & (lam - 1));
+          const float q0 = qf[m][0], q1 = qf[m][1];
+          float k0, k1;
+          read_key(m, k0, k1);
+          R::st(LA + u * K::RS_DK, q0 * f0, q1 * f1);
+          R::st(LA + (8 + u) * K::RS_DK, k0 * f0, k1 * f1);
+        }
+      }
+      float b0 = 1.f, b1 = 1.f;
+#pragma unroll
+      for (int m = SUB - 1; m >= 0; --m) {
+        if (!(m & lam)) {
+          if ((m & (lam - 1)) == lam - 1) {
+            b0 = 1.f;
+            b1 = 1.f;
+          } else {
+            b0 *= al[m + 1][0];
+            b1 *= al[m + 1][1];
+          }
+          const int v = (m / (2 * lam)) * lam + (m & (lam - 1));
+          const float k0 = kf[m][0], k1 = kf[m][1];
+          R::st(LB + v * K::RS_DK, k0 * b0, k1 * b1);
+        }
+      }
+    };
+
+    // ================= phase B: block-anchored operands, block totals, diagonal of A, level 8
+    float adiag = 0.f;
+    if (has_item) {
+      {
+        char* xq = R_X + K::OFF_XQ + (SUB * (iI - 1)) * K::RS_DK + 4 * icp;
+        char* xk = R_X + K::OFF_XK + (SUB * (iI - 1)) * K::RS_DK + 4 * icp;
+        float f0 = 1.f, f1 = 1.f;
+#pragma unroll
+        for (int m = 0; m < SUB; ++m) {
+          f0 *= al[m][0];
+          f1 *= al[m][1];
+          if (iI >= 1) {
+            const float q0 = qf[m][0], q1 = qf[m][1];
+            float k0, k1;
+            read_key(m, k0, k1);
+            R::st(xq + m * K::RS_DK, q0 * f0, q1 * f1);
+            R::st(xk + m * K::RS_DK, k0 * f0, k1 * f1);
+          }
+        }
+        *(float2*)(GT + iI * DK + 2 * icp) = make_float2(f0, f1);
+      }
+      if (iI <= 2) {
+        char* y = R_X + K::OFF_Y + (SUB * iI) * K::RS_DK + 4 * icp;
+        float b0 = 1.f, b1 = 1.f;
+#pragma unroll
+        for (int m = SUB - 1; m >= 0; --m) {
+          const float k0 = kf[m][0], k1 = kf[m][1];
+          R::st(y + m * K::RS_DK, k0 * b0, k1 * b1);
+          b0 *= al[m][0];
+          b1 *= al[m][1];
+        }
+      }
+      float d[SUB];
+#pragma unroll
+      for (int m = 0; m < SUB; ++m) {
+        const float q0 = qf[m][0], q1 = qf[m][1];
+        const float k0 = kf[m][0], k1 = kf[m][1];
+        d[m] = fmaf(q1, k1, q0 * k0);
+      }
+      adiag = reduce16<GRP>(d, lane);
+      write_level(R_L, 8);
+    }
+    lds_barrier();
+
+    // ================= phase M1: the six off-diagonal tiles of A and T, level 8 tiles.
+    // Waves 0, 1: two off-diagonal jobs; waves 2, 3: one off-diagonal job and two
+    // level-8 blocks.  Job j: (I, J) = (1,0) (2,1) (3,2) (2,0) (3,1) (3,0).
+    auto lvl_job = [&](const char* buf, int I, f32x4_t& acc) {
+      const char* LA = buf + I * K::LVL_ROWS * K::RS_DK;
+      const char* LB = LA + 16 * K::RS_DK;
+      Frag<bf16_t> fa[K::KS], fb[K::KS];
+#pragma unroll
+      for (int ks = 0; ks < K::KS; ++ks) {
+        const int c0 = 32 * ks + 8 * g;
+        fa[ks].load8(LA + n * K::RS_DK + c0 * 2);
+        if (n < 8)
+          fb[ks].load8(LB + n * K::RS_DK + c0 * 2);
+        else
+          fb[ks].zero();
+      }
+      acc = zero4();
+#pragma unroll
+      for (int ks = 0; ks < K::KS; ++ks) mma(acc, fa[ks], fb[ks]);
+    };
+    auto off_job = [&](int j, f32x4_t& ra, f32x4_t& rt) {
+      const int I = kOffI[j], J = kOffJ[j], pi = kOffPi[j];
+      const char* xq = R_X + K::OFF_XQ + (SUB * (I - 1) + n) * K::RS_DK;
+      const char* xk = R_X + K::OFF_XK + (SUB * (I - 1) + n) * K::RS_DK;
+      const char* y = R_X + K::OFF_Y + (SUB * J + n) * K::RS_DK;
+      Frag<bf16_t> fa[K::KS], fk[K::KS], fb[K::KS];
+#pragma unroll
+      for (int ks = 0; ks < K::KS; ++ks) {
+        const int c0 = 32 * ks + 8 * g;
+        fb[ks].load8(y + c0 * 2);
+        fa[ks].load8(xq + c0 * 2);
+        fk[ks].load8(xk + c0 * 2);
+      }
+      ra = zero4();
+      rt = zero4();
+#pragma unroll
+      for (int ks = 0; ks < K::KS; ++ks) {
+        if (pi >= 0) {
+          // whole blocks between J and I: g1 (pi 0), g1 g2 (pi 1), g2 (pi 2)
+          const int c0 = 32 * ks + 8 * g;
+          const float* G1 = GT + (pi == 2 ? 2 : 1) * DK + c0;
+          float4 p0 = *(const float4*)G1, p1 = *(const float4*)(G1 + 4);
+          if (pi == 1) {
+            const float4 e0 = *(const float4*)(GT + 2 * DK + c0), e1 = *(const float4*)(GT + 2 * DK + c0 + 4);
+            p0 = make_float4(p0.x * e0.x, p0.y * e0.y, p0.z * e0.z, p0.w * e0.w);
+            p1 = make_float4(p1.x * e1.x, p1.y * e1.y, p1.z * e1.z, p1.w * e1.w);
+          }
+          const float pv8[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+          fb[ks].scale(pv8);
+        }
+        mma(ra, fa[ks], fb[ks]);
+        mma(rt, fk[ks], fb[ks]);
+      }
+    };
+    f32x4_t acc1[4];
+    off_job(wave, acc1[0], acc1[1]);
+    if (wave < 2) {
+      off_job(wave + 4, acc1[2], acc1[3]);
+    } else {
+      lvl_job(R_L, 2 * (wave - 2), acc1[2]);
+      lvl_job(R_L, 2 * (wave - 2) + 1, acc1[3]);
+    }
+    lds_barrier();
+
+    // ================= phase C: Q o gamma and (K o rho)^T into the record, gamma_last,
+    // level 4 (buffer 1) and level 2 (buffer 0) operands
+    float Gp[2] = {1.f, 1.f};  // gate product of the blocks before the item's block
+    if (has_item) {
+      const float2 t0v = *(const float2*)(GT + 2 * icp), t1v = *(const float2*)(GT + DK + 2 * icp);
+      const float2 t2v = *(const float2*)(GT + 2 * DK + 2 * icp), t3v = *(const float2*)(GT + 3 * DK + 2 * icp);
+      float Rp[2];
+      Gp[0] = iI == 0 ? 1.f : iI == 1 ? t0v.x : iI == 2 ? t0v.x * t1v.x : t0v.x * t1v.x * t2v.x;
+      Gp[1] = iI == 0 ? 1.f : iI == 1 ? t0v.y : iI == 2 ? t0v.y * t1v.y : t0v.y * t1v.y * t2v.y;
+      Rp[0] = iI == 3 ? 1.f : iI == 2 ? t3v.x : iI == 1 ? t2v.x * t3v.x : t1v.x * t2v.x * t3v.x;
+      Rp[1] = iI == 3 ? 1.f : iI == 2 ? t3v.y : iI == 1 ? t2v.y * t3v.y : t1v.y * t2v.y * t3v.y;
+      if (iI == 3) *(float2*)(GC + 2 * icp) = make_float2(Gp[0] * t3v.x, Gp[1] * t3v.y);  // gamma_last
+      {
+        char* qg = rec + RL::QG + (SUB * iI) * K::RS_DK + 4 * icp;
+        float f0 = Gp[0], f1 = Gp[1];
+#pragma unroll
+        for (int m = 0; m < SUB; ++m) {
+          f0 *= al[m][0];
+          f1 *= al[m][1];
+          const float q0 = qf[m][0], q1 = qf[m][1];
+          R::st(qg + m * K::RS_DK, q0 * f0, q1 * f1);
+        }
+      }
+      {
+        char* pr0 = rec + RL::KRT + (2 * icp) * K::RS_C + (SUB * iI) * 2;
+        float b0 = Rp[0], b1 = Rp[1];
+#pragma unroll
+        for (int h8 = SUB - 8; h8 >= 0; h8 -= 8) {
+          float r8a[8], r8b[8];
+#pragma unroll
+          for (int mm = 7; mm >= 0; --mm) {
+            const int m = h8 + mm;
+            const float k0 = kf[m][0], k1 = kf[m][1];
+            r8a[mm] = k0 * b0;
+            r8b[mm] = k1 * b1;
+            b0 *= al[m][0];
+            b1 *= al[m][1];
+          }
+          st_row8<bf16_t>(pr0 + h8 * 2, r8a);
+          st_row8<bf16_t>(pr0 + K::RS_C + h8 * 2, r8b);
+        }
+      }
+      write_level(R_X, 4);
+      write_level(R_L, 2);
+    }
+    // the record's pad bytes of Q o gamma and (K o rho)^T rows (whole lines reach memory)
+    if (tid < C) *(uint4*)(rec + RL::QG + tid * K::RS_DK + DK * 2) = make_uint4(0, 0, 0, 0);
+    if (tid < DK) *(uint4*)(rec + RL::KRT + tid * K::RS_C + C * 2) = make_uint4(0, 0, 0, 0);
+    lds_barrier();
+
+    // ================= phase M2: level 4 and level 2 tiles of block `wave`
+    f32x4_t acc2[2];
+    lvl_job(R_X, wave, acc2[0]);
+    lvl_job(R_L, wave, acc2[1]);
+    lds_barrier();
+
+    // ================= phase C2: level 1 operands (buffer 0), (K o gamma)^T with the
+    // erase-side key, then the next chunk's inputs
+    if (has_item) {
+      write_level(R_L, 1);
+      char* pg0 = R_X + K::OFF_KGT + (2 * icp) * K::RS_C + (SUB * iI) * 2;
+      float f0 = Gp[0], f1 = Gp[1];
+#pragma unroll
+      for (int h8 = 0; h8 < SUB; h8 += 8) {
+        float g8a[8], g8b[8];
+#pragma unroll
+        for (int mm = 0; mm < 8; ++mm) {
+          const int m = h8 + mm;
+          f0 *= al[m][0];
+          f1 *= al[m][1];
+          float k0, k1;
+          read_key(m, k0, k1);
+          g8a[mm] = k0 * f0;
+          g8b[mm] = k1 * f1;
+        }
+        st_row8<bf16_t>(pg0 + h8 * 2, g8a);
+        st_row8<bf16_t>(pg0 + K::RS_C + h8 * 2, g8b);
+      }
+    }
+    if (chunk + 1 < c_end) issue(chunk + 1);
+    lds_barrier();
+
+    // ================= phase M3: level 1 tile of block `wave`
+    f32x4_t acc3;
+    lvl_job(R_L, wave, acc3);
+    lds_barrier();
+
+    // ================= phase D: every product into D (fp32) and A~ (bf16)
+    float* const TT = (float*)(R_L + K::OFF_TT);
+    char* const AT = R_L + K::OFF_AT;
+    auto put_off = [&](int j, const f32x4_t& ra, const f32x4_t& rt) {
+      const int I = kOffI[j], J = kOffJ[j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int gi = 16 * I + 4 * g + e, gj = 16 * J + n;
+        *(uint16_t*)(AT + gi * K::RS_C + gj * 2) = f32_to_bf16(ra[e]);
+        TT[gi * LDF + gj] = rt[e];
+      }
+    };
+    put_off(wave, acc1[0], acc1[1]);
+    if (wave < 2) {
+      put_off(wave + 4, acc1[2], acc1[3]);
+    } else {
+      put_level<8, K::RS_C, LDF>(acc1[2], 2 * (wave - 2), g, n, AT, TT);
+      put_level<8, K::RS_C, LDF>(acc1[3], 2 * (wave - 2) + 1, g, n, AT, TT);
+    }
+    put_level<4, K::RS_C, LDF>(acc2[0], wave, g, n, AT, TT);
+    put_level<2, K::RS_C, LDF>(acc2[1], wave, g, n, AT, TT);
+    put_level<1, K::RS_C, LDF>(acc3, wave, g, n, AT, TT);
+    if (has_item && (tid % (GRP / 16)) == 0) {
+      const int i = SUB * iI + (tid % GRP) / (GRP / 16);
+      *(uint16_t*)(AT + i * K::RS_C + i * 2) = f32_to_bf16(adiag);
+    }
+    lds_barrier();
+
+    // ================= phase I: M = (I + T)^-1 with T = diag(beta) D
+    float* const MM = (float*)(R_X + K::OFF_MM);
+    char* const MB = R_L + K::OFF_MB;  // transposed 16x16 blocks: 0 N00, 1 N11, 2 N22, 3 M10, 4 M20
+    auto mb_row = [&](int blk, int r) -> float* { return (float*)(MB + (blk * SUB + r) * K::RS_MB); };
+    if (wave == 0) {
+      // diagonal blocks by forward substitution: lane = (block I, column col); the lane
+      // also holds row `col` of T_II, broadcast across the 16-lane row
+      const int I = lane >> 4, col = lane & 15;
+      const float* drow = TT + (16 * I + col) * LDF + 16 * I;
+      const float bcol = BETA[16 * I + col];
+      float tr[SUB];
+#pragma unroll
+      for (int p4 = 0; p4 < SUB; p4 += 4) {
+        const float4 w4 = *(const float4*)(drow + p4);
+        tr[p4] = w4.x;
+        tr[p4 + 1] = w4.y;
+        tr[p4 + 2] = w4.z;
+        tr[p4 + 3] = w4.w;
+      }
+#pragma unroll
+      for (int p = 0; p < SUB; ++p) tr[p] = p < col ? bcol * tr[p] : 0.f;
+      float x[SUB], nx[SUB];  // column of N_II and its negation
+#define KDA_FS_ROW(i)                                                                        \
+  {                                                                                          \
+    float acc = (col == i) ? 1.f : 0.f;                                                      \
+    _Pragma("unroll") for (int p = 0; p < i; ++p) acc = fmaf(row_bcast<i>(tr[p]), nx[p], acc); \
+    x[i] = acc;                                                                              \
+    nx[i] = -acc;                                                                            \
+  }
+      KDA_FS_ROW(0) KDA_FS_ROW(1) KDA_FS_ROW(2) KDA_FS_ROW(3) KDA_FS_ROW(4) KDA_FS_ROW(5) KDA_FS_ROW(6)
+      KDA_FS_ROW(7) KDA_FS_ROW(8) KDA_FS_ROW(9) KDA_FS_ROW(10) KDA_FS_ROW(11) KDA_FS_ROW(12) KDA_FS_ROW(13)
+      KDA_FS_ROW(14) KDA_FS_ROW(15)
+#undef KDA_FS_ROW
+#pragma unroll
+      for (int i = 0; i < SUB; ++i) MM[(16 * I + i) * LDF + 16 * I + col] = x[i];
+      if (I < 3) {
+        float* dst = mb_row(I, col);
+#pragma unroll
+        for (int p4 = 0; p4 < SUB; p4 += 4) *(float4*)(dst + p4) = make_float4(x[p4], x[p4 + 1], x[p4 + 2], x[p4 + 3]);
+      }
+    }
+    lds_barrier();
+    // off-diagonal blocks, M_IJ = -N_II sum_{K=J}^{I-1} T_IK M_KJ, in three dependency
+    // stages.  In product instruction s the k-slot is 4 g + s, so an accumulator tile
+    // is directly the B operand of the next product.
+    auto a_T = [&](int I, int Kb, float (&a)[4]) {  // row n of T_IK = beta_i D_IK
+      const float4 w4 = *(const float4*)(TT + (16 * I + n) * LDF + 16 * Kb + 4 * g);
+      const float bi = BETA[16 * I + n];
+      a[0] = bi * w4.x;
+      a[1] = bi * w4.y;
+      a[2] = bi * w4.z;
+      a[3] = bi * w4.w;
+    };
+    auto b_MB = [&](int blk, float (&bb)[4]) {  // B = a block whose transpose is stored in MB
+      const float4 w4 = *(const float4*)(mb_row(blk, n) + 4 * g);
+      bb[0] = w4.x;
+      bb[1] = w4.y;
+      bb[2] = w4.z;
+      bb[3] = w4.w;
+    };
+    auto mm4_acc = [&](f32x4_t& acc, const float (&a)[4], const f32x4_t& bacc) {
+      const float bb[4] = {bacc[0], bacc[1], bacc[2], bacc[3]};
+      mm4(acc, a, bb);
+    };
+    auto neg_N_times = [&](int I, const f32x4_t& z) -> f32x4_t {  // -N_II z
+      const float4 w4 = *(const float4*)(MM + (16 * I + n) * LDF + 16 * I + 4 * g);
+      const float a[4] = {w4.x, w4.y, w4.z, w4.w};
+      f32x4_t r = zero4();
+      mm4_acc(r, a, z);
+      return -r;
+    };
+    auto put_M = [&](int I, int J, const f32x4_t& m, int blk) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) MM[(16 * I + 4 * g + e) * LDF + 16 * J + n] = m[e];
+      if (blk >= 0) *(float4*)(mb_row(blk, n) + 4 * g) = make_float4(m[0], m[1], m[2], m[3]);
+    };
+    f32x4_t keep = zero4();  // partial sum carried across the stages (waves 0 and 3)
+    {
+      float a[4], bb[4];
+      if (wave == 0) {  // M10, then P30 = T30 N00 + T31 M10
+        f32x4_t z = zero4();
+        a_T(1, 0, a);
+        b_MB(0, bb);
+        mm4(z, a, bb);
+        const f32x4_t m10 = neg_N_times(1, z);
+        put_M(1, 0, m10, 3);
+        a_T(3, 0, a);
+        b_MB(0, bb);
+        mm4(keep, a, bb);
+        a_T(3, 1, a);
+        mm4_acc(keep, a, m10);
+      } else if (wave == 1) {  // M21, then M31 = -N33 (T31 N11 + T32 M21)
+        f32x4_t z = zero4();
+        a_T(2, 1, a);
+        b_MB(1, bb);
+        mm4(z, a, bb);
+        const f32x4_t m21 = neg_N_times(2, z);
+        put_M(2, 1, m21, -1);
+        f32x4_t p = zero4();
+        a_T(3, 1, a);
+        b_MB(1, bb);
+        mm4(p, a, bb);
+        a_T(3, 2, a);
+        mm4_acc(p, a, m21);
+        put_M(3, 1, neg_N_times(3, p), -1);
+      } else if (wave == 2) {  // M32
+        f32x4_t z = zero4();
+        a_T(3, 2, a);
+        b_MB(2, bb);
+        mm4(z, a, bb);
+        put_M(3, 2, neg_N_times(3, z), -1);
+      } else {  // P20 = T20 N00
+        a_T(2, 0, a);
+        b_MB(0, bb);
+        mm4(keep, a, bb);
+      }
+    }
+    lds_barrier();
+    if (wave == 3) {  // M20 = -N22 (P20 + T21 M10)
+      float a[4], bb[4];
+      a_T(2, 1, a);
+      b_MB(3, bb);
+      mm4(keep, a, bb);
+      put_M(2, 0, neg_N_times(2, keep), 4);
+    }
+    lds_barrier();
+    if (wave == 0) {  // M30 = -N33 (P30 + T32 M20)
+      float a[4], bb[4];
+      a_T(3, 2, a);
+      b_MB(4, bb);
+      mm4(keep, a, bb);
+      put_M(3, 0, neg_N_times(3, keep), -1);
+    }
+    lds_barrier();
+    // M~ = M diag(beta), lower incl. diagonal, as matrix-core operand (over MB)
+    char* const MT = R_L + K::OFF_MB;
+    for (int x = tid; x < C * C / 8; x += NT) {
+      const int i = x / (C / 8), j0 = 8 * (x % (C / 8));
+      const float4 m0 = *(const float4*)(MM + i * LDF + j0), m1 = *(const float4*)(MM + i * LDF + j0 + 4);
+      const float4 b0 = *(const float4*)(BETA + j0), b1 = *(const float4*)(BETA + j0 + 4);
+      float v8[8] = {m0.x * b0.x, m0.y * b0.y, m0.z * b0.z, m0.w * b0.w,
+                     m1.x * b1.x, m1.y * b1.y, m1.z * b1.z, m1.w * b1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (j0 + e > i) v8[e] = 0.f;
+      st_row8<bf16_t>(MT + i * K::RS_C + j0 * 2, v8);
+    }
+    lds_barrier();
+
+    // ================= phase W: -W = -M~ (K o gamma) over D
+    char* const WW = R_L + K::OFF_TT;
+    {
+      Frag<bf16_t> am[NB][2];
+#pragma unroll
+      for (int I = 0; I < NB; ++I)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          if (ks == 0 || I >= 2)
+            am[I][ks].load8(MT + (16 * I + n) * K::RS_C + (32 * ks + 8 * g) * 2);
+          else
+            am[I][ks].zero();
+        }
+      constexpr int NCT = DK / 16;
+      for (int cn = wave; cn < NCT; cn += 4) {
+        Frag<bf16_t> bk[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          bk[ks].load8(R_X + K::OFF_KGT + (16 * cn + n) * K::RS_C + (32 * ks + 8 * g) * 2);
+#pragma unroll
+        for (int I = 0; I < NB; ++I) {
+          f32x4_t acc = zero4();
+          mma(acc, am[I][0], bk[0]);
+          if (I >= 2) mma(acc, am[I][1], bk[1]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            *(uint16_t*)(WW + (16 * I + 4 * g + e) * K::RS_DK + (16 * cn + n) * 2) = f32_to_bf16(-acc[e]);
+        }
+      }
+    }
+    lds_barrier();
+    // ================= the LDS part of the record: -W, A~, M~, gamma_last
+    copy_flat<NT>(rec + RL::WW, WW, RL::QG - RL::WW, tid);
+    copy_flat<NT>(rec + RL::AT, AT, RL::MT - RL::AT, tid);
+    copy_flat<NT>(rec + RL::MT, MT, RL::GC - RL::MT, tid);
+    copy_flat<NT>(rec + RL::GC, (const char*)GC, RL::IMG - RL::GC, tid);
+  }
+}
+
+template <int DK, bool G2>
+static hipError_t launch_records_t(const ChunkArgs& a, char* ws, int cpw) {
+  using K = RCfg<DK>;
+  auto kern = chunk_records_kernel<DK, G2>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, K::LDS);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  // varlen: workgroups over (head, runs of global chunks); b = 0
+  const int BH = a.cu ? a.H : a.B * a.H;
+  const int nchunks = a.cu ? a.gmax : (a.T + C - 1) / C;
+  const int nseg = (nchunks + cpw - 1) / cpw;
+  if ((long)BH * nseg == 0) return hipSuccess;
+  if ((long)C * a.H * DK * 2 >= (1L << 32)) return hipErrorInvalidValue;  // 32-bit row offsets
+  hipLaunchKernelGGL(kern, dim3(BH * nseg), dim3(K::NT), K::LDS, (hipStream_t)a.stream, a.q, a.k, a.alpha, a.beta,
+                     a.erase, a.T, a.H, ws, cpw, a.cu, a.ctab, a.ctab_total, a.gmax);
+  return hipGetLastError();
+}
+
+// bf16 records with the two-workgroups-per-CU kernel (d_k = 64 or 128)
+hipError_t launch_records(const ChunkArgs& a, void* ws, int cpw) {
+  if (!a.bf16 || (a.dk != 64 && a.dk != 128)) return hipErrorInvalidValue;
+  if (a.erase)
+    return a.dk == 64 ? launch_records_t<64, true>(a, (char*)ws, cpw) : launch_records_t<128, true>(a, (char*)ws, cpw);
+  return a.dk == 64 ? launch_records_t<64, false>(a, (char*)ws, cpw) : launch_records_t<128, false>(a, (char*)ws, cpw);
+}
+
+}  // namespace kda

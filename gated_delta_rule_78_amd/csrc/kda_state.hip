@@ -15,13 +15,11 @@
 #include "kda_common.h"
 #include "kda_internal.h"
 #include "kda_record.h"
+#include "kda_tile.h"
 
 namespace kda {
 
 namespace {
-
-constexpr int C = 64;
-constexpr int NB = 4;
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void global_void;
@@ -33,28 +31,6 @@ typedef __attribute__((address_space(1))) void global_void;
 __device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
 #ifndef KDA_HOST_PASS
   __builtin_amdgcn_global_load_lds((global_void*)g, (lds_void*)lds_wave_base, 16, 0, 0);
-#endif
-}
-
-// Workgroup barriers without a memory fence (a fence would also wait for the DMA still
-// streaming the next chunk).  The empty asm statements keep the compiler from moving
-// memory accesses across them; the explicit waits make this wave's LDS writes (and, for
-// full_barrier, its DMA and global accesses) complete before the barrier.
-__device__ __forceinline__ void lds_barrier() {
-#ifndef KDA_HOST_PASS
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-#endif
-}
-
-__device__ __forceinline__ void full_barrier() {
-#ifndef KDA_HOST_PASS
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 #endif
 }
 

@@ -14,20 +14,31 @@ from kda_testutil import TOL, heads_of, inputs_to_dev, rel_err_slices, state_to_
 pytestmark = pytest.mark.gpu
 
 
-PATHS = ["fused", "twopass"]
+# "twopass_fusedrec": the two-pass path with its bf16 records written by the first half of
+# the fused kernel (KDA_RECORDS_FUSED) instead of the two-workgroups-per-CU record kernel
+PATHS = ["fused", "twopass", "twopass_fusedrec"]
 
 
 def _gpu(inp, S0=None, in_place=False, path="fused"):
+    import os
     import gated_delta_rule_78_amd as kda
     import torch
     q, k, v, a, b = inputs_to_dev(inp)
     s0 = None if S0 is None else state_to_dev(S0)
-    if in_place:
-        o, sT = kda.chunk_fwd(q, k, v, a, b, initial_state=s0, final_state=s0, path=path)
-        assert sT.data_ptr() == s0.data_ptr()
-    else:
-        o, sT = kda.chunk_fwd(q, k, v, a, b, initial_state=s0, path=path)
-    torch.cuda.synchronize()
+    env = path == "twopass_fusedrec"
+    if env:
+        os.environ["KDA_RECORDS_FUSED"] = "1"
+        path = "twopass"
+    try:
+        if in_place:
+            o, sT = kda.chunk_fwd(q, k, v, a, b, initial_state=s0, final_state=s0, path=path)
+            assert sT.data_ptr() == s0.data_ptr()
+        else:
+            o, sT = kda.chunk_fwd(q, k, v, a, b, initial_state=s0, path=path)
+        torch.cuda.synchronize()
+    finally:
+        if env:
+            del os.environ["KDA_RECORDS_FUSED"]
     return o.float().cpu().numpy(), sT.cpu().numpy()
 
 
@@ -146,8 +157,8 @@ def test_records_applied_to_two_value_sets():
     ws = kda.chunk_records(q, k, a, b)
     o1, f1 = kda.chunk_apply_records(ws, v, s0)
     o2, f2 = kda.chunk_apply_records(ws, v2, s02)
-    r1 = kda.chunk_fwd(q, k, v, a, b, initial_state=s0, path="fused")
-    r2 = kda.chunk_fwd(q, k, v2, a, b, initial_state=s02, path="fused")
+    r1 = kda.chunk_fwd(q, k, v, a, b, initial_state=s0, path="twopass")
+    r2 = kda.chunk_fwd(q, k, v2, a, b, initial_state=s02, path="twopass")
     torch.cuda.synchronize()
     for got, want in ((o1, r1[0]), (f1, r1[1]), (o2, r2[0]), (f2, r2[1])):
         assert torch.equal(got, want)
