@@ -19,6 +19,13 @@ patterns, which both sides widen exactly):
   write gate w = sigmoid(x) per value channel, x ~ N(0, 1) (two more streams,
   children 7 and 8 of the same SeedSequence, so the other tensors do not change);
   beta is drawn as for KDA and unused by GDN-2.
+* SFDA gates : complex gates lambda = a e^{i theta} per key-channel pair p, stored
+  as (Re, Im) in channels (2p, 2p+1) of the alpha tensor; magnitude
+  a = exp(-0.1 * softplus(x)) from the even channels of the alpha stream, phase
+  theta ~ U(-pi, pi) from a tenth stream (child 9); a Bernoulli(0.05) mask per pair
+  sets lambda to one of {0, 1, -1, i, -i} (exact zeros and quarter turns); bf16
+  gates whose rounded magnitude exceeds 1 are shrunk by 2^-8 and rounded again;
+  beta = 2 * sigmoid(2x) in [0, 2] as for CKDA.
 * S0     ~ N(0, std 0.02) in fp32, or zeros.
 
 The five named workloads mirror the shapes the method is evaluated on: a tiny
@@ -59,6 +66,7 @@ WORKLOADS = {
     "ckda_decode_b256": Workload("ckda_decode_b256", 256, 1, 32, 128, 128, "bf16", "ckda", False,
                                  decode_steps=64, index=4),
     "gdn2_prefill_8k": Workload("gdn2_prefill_8k", 4, 8192, 32, 128, 128, "bf16", "gdn2", False, index=5),
+    "sfda_prefill_8k": Workload("sfda_prefill_8k", 4, 8192, 32, 128, 128, "bf16", "sfda", False, index=6),
 }
 
 
@@ -109,8 +117,8 @@ def make(B, T, H, dk, dv, dtype="bf16", gates="kda", zero_s0=False, seed=BASE_SE
     ``lead`` (optional) is an extra leading dimension (decode steps): tensors are
     then [lead, B, H, d] and beta [lead, B, H]; otherwise [B, T, H, d], [B, T, H].
     """
-    ss = np.random.SeedSequence(seed).spawn(9)
-    rq, rk, rv, ra, rb, rs, rm, re, rw = [np.random.default_rng(s) for s in ss]
+    ss = np.random.SeedSequence(seed).spawn(10)
+    rq, rk, rv, ra, rb, rs, rm, re, rw, rt = [np.random.default_rng(s) for s in ss]
     shp = (lead, B, H) if lead else (B, T, H)
     f32 = np.float32
     q = _l2n(rq.standard_normal(shp + (dk,), dtype=f32))
@@ -132,6 +140,28 @@ def make(B, T, H, dk, dv, dtype="bf16", gates="kda", zero_s0=False, seed=BASE_SE
             m = rm.random(alpha.shape) < force_mask_p
             vals = np.array([-1.0, 0.0, 1.0], f32)[rm.integers(0, 3, size=int(m.sum()))]
             alpha[m] = vals
+    elif gates == "sfda":
+        if dk % 2:
+            raise ValueError("SFDA gates pair the key channels: dk must be even")
+        mag = np.exp(-0.1 * _softplus(xa[..., 0::2])).astype(np.float64)
+        theta = rt.uniform(-np.pi, np.pi, size=mag.shape)
+        re_, im_ = mag * np.cos(theta), mag * np.sin(theta)
+        if force_mask_p > 0:
+            m = rm.random(mag.shape) < force_mask_p
+            pick = rm.integers(0, 5, size=int(m.sum()))
+            re_[m] = np.array([0.0, 1.0, -1.0, 0.0, 0.0])[pick]
+            im_[m] = np.array([0.0, 0.0, 0.0, 1.0, -1.0])[pick]
+        alpha = np.empty(shp + (dk,), f32)
+        alpha[..., 0::2], alpha[..., 1::2] = re_, im_
+        if dtype == "bf16":
+            for _ in range(4):  # keep |lambda| <= 1 after rounding to bf16
+                r = bf16_to_f32(bf16_bits(alpha)).astype(np.float64)
+                big = r[..., 0::2] ** 2 + r[..., 1::2] ** 2 > 1.0
+                if not big.any():
+                    break
+                big2 = np.repeat(big, 2, axis=-1)
+                alpha[big2] = (alpha[big2] * (1.0 - 2.0 ** -8)).astype(f32)
+        beta = (2.0 * _sigmoid(2.0 * xb)).astype(f32)
     else:
         raise ValueError(gates)
     S0 = None if zero_s0 else (0.02 * rs.standard_normal((B, H, dk, dv), dtype=f32)).astype(f32)

@@ -21,7 +21,9 @@ DeltaNet), beta = 0 (pure decay), spectral norm <= 1, Frobenius-norm
 preservation for alpha in {-1, 1} and beta in {0, 2} with zero writes, the d=2
 reflection-pair rotation and its mod-5 counter, the affine block transfer and
 split invariance, and a mutation test that plants mistakes in copies of the C
-source and checks that the pins catch each one.
+source and checks that the pins catch each one.  The SFDA recurrence (complex
+rotation-decay gates on channel pairs; same page, section "Arquitectura Central")
+has its own pins in ``tests/test_oracle_sfda.py``.
 """
 from __future__ import annotations
 
@@ -64,6 +66,10 @@ def load(path: str = _LIB_PATH):
     lib.kda_oracle_fwd_gdn2.restype = I
     lib.kda_oracle_decode_gdn2.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P, I, I]
     lib.kda_oracle_decode_gdn2.restype = I
+    lib.kda_oracle_fwd_sfda.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, I, I, I]
+    lib.kda_oracle_fwd_sfda.restype = I
+    lib.kda_oracle_decode_sfda.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, I, I]
+    lib.kda_oracle_decode_sfda.restype = I
     if path == _LIB_PATH:
         _lib = lib
     return lib
@@ -93,6 +99,10 @@ def fwd(q, k, v, alpha, beta, S0=None, heads=None, col_block=0, nthreads=0, lib=
     heads: None (all B*H pairs, in b*H + h order) or a list of flat indices.
     Returns (o [n_sel, T, dv] fp64 or None, S_T [n_sel, dk, dv] fp64).
     """
+    return _fwd_impl("kda_oracle_fwd", q, k, v, alpha, beta, S0, heads, col_block, nthreads, lib, want_o)
+
+
+def _fwd_impl(_entry, q, k, v, alpha, beta, S0, heads, col_block, nthreads, lib, want_o):
     lib = lib or load()
     arrs = [np.ascontiguousarray(x) for x in (q, k, v, alpha, beta)]
     code = _dtype_code(arrs[0])
@@ -106,10 +116,10 @@ def fwd(q, k, v, alpha, beta, S0=None, heads=None, col_block=0, nthreads=0, lib=
     S0d = None if S0 is None else np.ascontiguousarray(np.asarray(S0, dtype=np.float64)).reshape(n_sel, dk, dv)
     o = np.empty((n_sel, T, dv), np.float64) if want_o else None
     S = np.empty((n_sel, dk, dv), np.float64)
-    rc = lib.kda_oracle_fwd(B, T, H, dk, dv, code, *[_ptr(a) for a in arrs], _ptr(S0d),
-                            _ptr(o), _ptr(S), _ptr(sel), n_sel, int(col_block), int(nthreads))
+    rc = getattr(lib, _entry)(B, T, H, dk, dv, code, *[_ptr(a) for a in arrs], _ptr(S0d),
+                              _ptr(o), _ptr(S), _ptr(sel), n_sel, int(col_block), int(nthreads))
     if rc != 0:
-        raise RuntimeError("kda_oracle_fwd failed")
+        raise RuntimeError(f"{_entry} failed")
     return o, S
 
 
@@ -118,6 +128,10 @@ def decode(q, k, v, alpha, beta, state, heads=None, nthreads=0, lib=None):
 
     q, k, alpha: [B, H, dk]; v: [B, H, dv]; beta: [B, H].  Returns o [n_sel, dv].
     """
+    return _decode_impl("kda_oracle_decode", q, k, v, alpha, beta, state, heads, nthreads, lib)
+
+
+def _decode_impl(_entry, q, k, v, alpha, beta, state, heads, nthreads, lib):
     lib = lib or load()
     arrs = [np.ascontiguousarray(x) for x in (q, k, v, alpha, beta)]
     code = _dtype_code(arrs[0])
@@ -128,10 +142,10 @@ def decode(q, k, v, alpha, beta, state, heads=None, nthreads=0, lib=None):
     if state.dtype != np.float64 or not state.flags.c_contiguous or state.shape != (n_sel, dk, dv):
         raise TypeError("state must be a C-contiguous float64 array of shape [n_sel, dk, dv]")
     o = np.empty((n_sel, dv), np.float64)
-    rc = lib.kda_oracle_decode(B, H, dk, dv, code, *[_ptr(a) for a in arrs], _ptr(state), _ptr(o),
-                               _ptr(sel), n_sel, int(nthreads))
+    rc = getattr(lib, _entry)(B, H, dk, dv, code, *[_ptr(a) for a in arrs], _ptr(state), _ptr(o),
+                              _ptr(sel), n_sel, int(nthreads))
     if rc != 0:
-        raise RuntimeError("kda_oracle_decode failed")
+        raise RuntimeError(f"{_entry} failed")
     return o
 
 
@@ -179,3 +193,15 @@ def decode_gdn2(q, k, v, alpha, erase, write, state, heads=None, nthreads=0, lib
     if rc != 0:
         raise RuntimeError("kda_oracle_decode_gdn2 failed")
     return o
+
+
+def fwd_sfda(q, k, v, lam, beta, S0=None, heads=None, col_block=0, nthreads=0, lib=None, want_o=True):
+    """SFDA recurrence (phase control) over whole sequences: as fwd, with the decay
+    replaced by complex gates ``lam`` [B, T, H, dk] (channel 2p = Re, 2p+1 = Im of the
+    gate of coordinate p, acting on rows 2p, 2p+1 of the state)."""
+    return _fwd_impl("kda_oracle_fwd_sfda", q, k, v, lam, beta, S0, heads, col_block, nthreads, lib, want_o)
+
+
+def decode_sfda(q, k, v, lam, beta, state, heads=None, nthreads=0, lib=None):
+    """One SFDA decode step; lam [B, H, dk] complex gates as in fwd_sfda."""
+    return _decode_impl("kda_oracle_decode_sfda", q, k, v, lam, beta, state, heads, nthreads, lib)

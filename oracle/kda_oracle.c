@@ -58,6 +58,30 @@
  * functions when b = w = beta (the reduction the page states), against the
  * no-erase case (b = 0: a decayed sum of writes) and against a hand-worked
  * two-token case.
+ *
+ * SFDA with phase control ("Resumen Tecnico: Atencion Delta de Fourier
+ * Semidirecta (SFDA)", section "Arquitectura Central"): the real decay
+ * Diag(alpha_t) becomes Lambda_t = diag(alpha_t o e^{i theta_t}) in complex
+ * coordinates, which the same section says is built in real coordinates as a
+ * direct sum of 2 x 2 rotation-decay blocks.  Reading taken here: key channels
+ * 2p and 2p+1 form complex coordinate p; the gate of coordinate p is the
+ * complex number lambda_p = alpha_p e^{i theta_p}, handed over as its real and
+ * imaginary parts in channels 2p and 2p+1 of the gate tensor; k, q, v, beta and
+ * the state stay real (the kernel-compatible real family Lambda_t - u_t r_t^*
+ * of the same page, section "Expresividad de Estado Finito"), so
+ *
+ *   S_t = (I - beta_t k_t k_t^T) Lambda_t S_{t-1} + beta_t k_t v_t^T,
+ *   (Lambda S)[2p]   = Re(lambda_p) S[2p] - Im(lambda_p) S[2p+1]
+ *   (Lambda S)[2p+1] = Im(lambda_p) S[2p] + Re(lambda_p) S[2p+1]
+ *
+ * (rows 2p, 2p+1 of every column, read as z = S[2p] + i S[2p+1], become
+ * lambda_p z).  kda_oracle_fwd_sfda and kda_oracle_decode_sfda run that update;
+ * the CPU tests pin them against the KDA functions when every phase is zero
+ * (Im lambda = 0, both channels of a pair decayed by Re lambda; the page's
+ * "Principales Contribuciones" item 1), against the closed form of pure
+ * rotation-decay (beta = 0: z_t = (prod lambda) z_0, with numpy's complex
+ * products), against an exact phase-only cyclic counter, against dense real
+ * transition matrices and against a hand-worked two-token case.
  */
 #include <stdint.h>
 #include <stdlib.h>
@@ -79,13 +103,26 @@ static double load_elem(const void* base, int dtype, size_t idx) {
     return ((const double*)base)[idx];
 }
 
-/* One token of the recurrence on columns [j0, j1) of a d_k x d_v state. */
+/* One token of the recurrence on columns [j0, j1) of a d_k x d_v state.
+ * cpx = 0: Diag(alpha) decay (KDA / CKDA); cpx = 1: SFDA rotation-decay, a[2p] and
+ * a[2p+1] being the real and imaginary parts of the gate of coordinate p. */
 static void kda_token(double* S, int dk, int dv, int j0, int j1,
                       const double* q, const double* k, const double* v,
-                      const double* a, double beta, double* u, double* o) {
-    /* 1. decay: S <- Diag(alpha) S */
-    for (int i = 0; i < dk; ++i)
-        for (int j = j0; j < j1; ++j) S[(size_t)i * dv + j] *= a[i];
+                      const double* a, double beta, double* u, double* o, int cpx) {
+    /* 1. decay: S <- Diag(alpha) S, or S <- Lambda S (row pairs times lambda_p) */
+    if (!cpx) {
+        for (int i = 0; i < dk; ++i)
+            for (int j = j0; j < j1; ++j) S[(size_t)i * dv + j] *= a[i];
+    } else {
+        for (int p = 0; p < dk / 2; ++p) {
+            const double lr = a[2 * p], li = a[2 * p + 1];
+            for (int j = j0; j < j1; ++j) {
+                const double x = S[(size_t)(2 * p) * dv + j], y = S[(size_t)(2 * p + 1) * dv + j];
+                S[(size_t)(2 * p) * dv + j] = lr * x - li * y;
+                S[(size_t)(2 * p + 1) * dv + j] = li * x + lr * y;
+            }
+        }
+    }
     /* 2. read: u = S^T k */
     for (int j = j0; j < j1; ++j) u[j] = 0.0;
     for (int i = 0; i < dk; ++i)
@@ -123,12 +160,13 @@ static int pick_threads(int nthreads) {
  *   col_block   : width of the column blocks handed to threads (<= 0: dv)
  * Returns 0, or -1 on bad arguments / allocation failure.
  */
-int kda_oracle_fwd(int B, int T, int H, int dk, int dv, int dtype,
-                   const void* q, const void* k, const void* v,
-                   const void* alpha, const void* beta, const double* S0,
-                   double* o_out, double* S_out, const int* sel, int n_sel,
-                   int col_block, int nthreads) {
+static int fwd_common(int B, int T, int H, int dk, int dv, int dtype,
+                      const void* q, const void* k, const void* v,
+                      const void* alpha, const void* beta, const double* S0,
+                      double* o_out, double* S_out, const int* sel, int n_sel,
+                      int col_block, int nthreads, int cpx) {
     if (B < 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+    if (cpx && dk % 2) return -1;
     if (dtype < ORC_BF16 || dtype > ORC_F64) return -1;
     if (!sel) n_sel = B * H;
     if (n_sel < 0) return -1;
@@ -167,7 +205,7 @@ int kda_oracle_fwd(int B, int T, int H, int dk, int dv, int dtype,
                 }
                 for (int j = j0; j < j1; ++j) vv[j] = load_elem(v, dtype, row * dv + j);
                 const double bt = load_elem(beta, dtype, row);
-                kda_token(S, dk, dv, j0, j1, qq, kk, vv, aa, bt, u, o_out ? oo : NULL);
+                kda_token(S, dk, dv, j0, j1, qq, kk, vv, aa, bt, u, o_out ? oo : NULL, cpx);
                 if (o_out)
                     for (int j = j0; j < j1; ++j)
                         o_out[((size_t)s * T + t) * dv + j] = oo[j];
@@ -183,17 +221,38 @@ int kda_oracle_fwd(int B, int T, int H, int dk, int dv, int dtype,
     return err ? -1 : 0;
 }
 
+int kda_oracle_fwd(int B, int T, int H, int dk, int dv, int dtype,
+                   const void* q, const void* k, const void* v,
+                   const void* alpha, const void* beta, const double* S0,
+                   double* o_out, double* S_out, const int* sel, int n_sel,
+                   int col_block, int nthreads) {
+    return fwd_common(B, T, H, dk, dv, dtype, q, k, v, alpha, beta, S0, o_out, S_out, sel, n_sel,
+                      col_block, nthreads, 0);
+}
+
+/* SFDA forward: as kda_oracle_fwd with alpha [B, T, H, dk] holding the complex gates
+ * (real part in channel 2p, imaginary part in channel 2p+1); dk must be even. */
+int kda_oracle_fwd_sfda(int B, int T, int H, int dk, int dv, int dtype,
+                        const void* q, const void* k, const void* v,
+                        const void* lambda, const void* beta, const double* S0,
+                        double* o_out, double* S_out, const int* sel, int n_sel,
+                        int col_block, int nthreads) {
+    return fwd_common(B, T, H, dk, dv, dtype, q, k, v, lambda, beta, S0, o_out, S_out, sel, n_sel,
+                      col_block, nthreads, 1);
+}
+
 /*
  * One recurrent decode step (the same token body), state carried by caller.
  *   q, k, alpha : [B, H, dk]; v : [B, H, dv]; beta : [B, H]   (dtype)
  *   state       : [n_sel, dk, dv] fp64, updated in place
  *   o_out       : [n_sel, dv] fp64, or NULL
  */
-int kda_oracle_decode(int B, int H, int dk, int dv, int dtype,
-                      const void* q, const void* k, const void* v,
-                      const void* alpha, const void* beta, double* state,
-                      double* o_out, const int* sel, int n_sel, int nthreads) {
+static int decode_common(int B, int H, int dk, int dv, int dtype,
+                         const void* q, const void* k, const void* v,
+                         const void* alpha, const void* beta, double* state,
+                         double* o_out, const int* sel, int n_sel, int nthreads, int cpx) {
     if (B < 0 || H <= 0 || dk <= 0 || dv <= 0 || !state) return -1;
+    if (cpx && dk % 2) return -1;
     if (dtype < ORC_BF16 || dtype > ORC_F64) return -1;
     if (!sel) n_sel = B * H;
     if (n_sel < 0) return -1;
@@ -219,13 +278,30 @@ int kda_oracle_decode(int B, int H, int dk, int dv, int dtype,
             for (int j = 0; j < dv; ++j) vv[j] = load_elem(v, dtype, (size_t)bh * dv + j);
             const double bt = load_elem(beta, dtype, (size_t)bh);
             kda_token(state + (size_t)s * dk * dv, dk, dv, 0, dv, qq, kk, vv, aa, bt, u,
-                      o_out ? oo : NULL);
+                      o_out ? oo : NULL, cpx);
             if (o_out)
                 for (int j = 0; j < dv; ++j) o_out[(size_t)s * dv + j] = oo[j];
         }
         free(buf);
     }
     return err ? -1 : 0;
+}
+
+int kda_oracle_decode(int B, int H, int dk, int dv, int dtype,
+                      const void* q, const void* k, const void* v,
+                      const void* alpha, const void* beta, double* state,
+                      double* o_out, const int* sel, int n_sel, int nthreads) {
+    return decode_common(B, H, dk, dv, dtype, q, k, v, alpha, beta, state, o_out, sel, n_sel,
+                         nthreads, 0);
+}
+
+/* One SFDA decode step: lambda [B, H, dk] holds the complex gates as in kda_oracle_fwd_sfda. */
+int kda_oracle_decode_sfda(int B, int H, int dk, int dv, int dtype,
+                           const void* q, const void* k, const void* v,
+                           const void* lambda, const void* beta, double* state,
+                           double* o_out, const int* sel, int n_sel, int nthreads) {
+    return decode_common(B, H, dk, dv, dtype, q, k, v, lambda, beta, state, o_out, sel, n_sel,
+                         nthreads, 1);
 }
 
 /* One Gated DeltaNet-2 token on columns [j0, j1): the read goes through the erase

@@ -41,10 +41,11 @@ MUTANTS = {
         "o[j] += q[i] * S[(size_t)i * dv + j]; } o = NULL; }\n"
         "    /* 3. erase + write: S <- S + beta k (v - u)^T */"),
     "decay_after_write": (
-        "    /* 1. decay: S <- Diag(alpha) S */\n"
-        "    for (int i = 0; i < dk; ++i)\n"
-        "        for (int j = j0; j < j1; ++j) S[(size_t)i * dv + j] *= a[i];\n",
-        ""),
+        "    if (!cpx) {\n"
+        "        for (int i = 0; i < dk; ++i)\n"
+        "            for (int j = j0; j < j1; ++j) S[(size_t)i * dv + j] *= a[i];\n"
+        "    } else {",
+        "    if (!cpx) {\n    } else {"),
 }
 # decay_after_write removes the first decay and re-inserts it after the write:
 _DECAY_AFTER_WRITE_TAIL = (
@@ -166,3 +167,61 @@ def test_gdn2_mutant_is_caught(name, src_text, monkeypatch, tmp_path):
     assert src_text.count(old) == 1, f"mutation anchor for {name} not unique"
     lib = _build_variant(src_text.replace(old, new), str(tmp_path), name)
     assert _caught_gdn2(lib, monkeypatch), f"mutant {name} passed every GDN-2 pin"
+
+
+# ---- the SFDA rotation-decay code: plausible mistakes, each must fail an SFDA pin
+import test_oracle_sfda as spins  # noqa: E402
+
+_ROT = ("                S[(size_t)(2 * p) * dv + j] = lr * x - li * y;\n"
+        "                S[(size_t)(2 * p + 1) * dv + j] = li * x + lr * y;")
+MUTANTS_SFDA = {
+    "sfda_conjugate_rotation": (_ROT, _ROT.replace("lr * x - li * y", "lr * x + li * y")
+                                .replace("li * x + lr * y", "-li * x + lr * y")),
+    "sfda_real_part_only": (_ROT, _ROT.replace("lr * x - li * y", "lr * x").replace("li * x + lr * y", "lr * y")),
+    "sfda_re_im_swapped": ("const double lr = a[2 * p], li = a[2 * p + 1];",
+                           "const double lr = a[2 * p + 1], li = a[2 * p];"),
+    "sfda_rows_mixed_wrong_way": (_ROT, _ROT.replace("lr * x - li * y", "lr * x - li * x")
+                                  .replace("li * x + lr * y", "li * y + lr * y")),
+    "sfda_pairs_are_halves": (
+        "const double x = S[(size_t)(2 * p) * dv + j], y = S[(size_t)(2 * p + 1) * dv + j];\n" + _ROT,
+        "const double x = S[(size_t)(p) * dv + j], y = S[(size_t)(p + dk / 2) * dv + j];\n"
+        + _ROT.replace("(2 * p) * dv", "(p) * dv").replace("(2 * p + 1) * dv", "(p + dk / 2) * dv")),
+    "sfda_gate_from_next_pair": ("const double lr = a[2 * p], li = a[2 * p + 1];",
+                                 "const double lr = a[(2 * p + 2) % dk], li = a[(2 * p + 3) % dk];"),
+}
+
+PIN_TESTS_SFDA = [
+    ("hand", lambda: spins.test_sfda_hand_derived_two_tokens()),
+    ("explicit", lambda: spins.test_sfda_explicit_transition_products(4, 2, 32)),
+    ("zero_phase_kda", lambda: spins.test_sfda_with_zero_phases_is_kda_with_paired_decay()),
+    ("closed_form", lambda: spins.test_sfda_pure_rotation_decay_closed_form()),
+    ("counter", lambda: spins.test_sfda_phase_only_cyclic_counter(5)),
+]
+
+
+def _caught_sfda(lib, monkeypatch):
+    failed = []
+    with monkeypatch.context() as m:
+        real = {n: getattr(oracle, n) for n in ("fwd", "decode", "fwd_sfda", "decode_sfda")}
+        for n, f in real.items():
+            m.setattr(oracle, n, (lambda f: lambda *a, **kw: f(*a, lib=lib, **kw))(f))
+        for name, fn in PIN_TESTS_SFDA:
+            try:
+                with np.errstate(all="ignore"):
+                    fn()
+            except AssertionError:
+                failed.append(name)
+    return failed
+
+
+def test_unmodified_source_passes_sfda_pins(src_text, monkeypatch, tmp_path):
+    lib = _build_variant(src_text, str(tmp_path), "clean_sfda")
+    assert _caught_sfda(lib, monkeypatch) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS_SFDA))
+def test_sfda_mutant_is_caught(name, src_text, monkeypatch, tmp_path):
+    old, new = MUTANTS_SFDA[name]
+    assert src_text.count(old) == 1, f"mutation anchor for {name} not unique"
+    lib = _build_variant(src_text.replace(old, new), str(tmp_path), name)
+    assert _caught_sfda(lib, monkeypatch), f"mutant {name} passed every SFDA pin"
