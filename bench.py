@@ -42,11 +42,11 @@ CSRC = os.path.join(ROOT, "gated_delta_rule_78_amd", "csrc")
 # the rocprofv3 counter summary of each kernel, and the sources that kernel is built from
 PMC_FILES = {
     "chunk_records": (os.path.join(ROOT, "profiles", "chunk_records_kda_prefill_8k_counters.md"),
-                      ["kda_chunk.hip", "kda_record.h", "kda_common.h"]),
+                      ["kda_records.hip", "kda_tile.h", "kda_record.h", "kda_common.h"]),
     "chunk_state": (os.path.join(ROOT, "profiles", "chunk_state_kda_prefill_8k_counters.md"),
-                    ["kda_state.hip", "kda_record.h", "kda_common.h"]),
+                    ["kda_state.hip", "kda_tile.h", "kda_record.h", "kda_common.h"]),
     "chunk_fused": (os.path.join(ROOT, "profiles", "chunk_fused_kda_prefill_8k_counters.md"),
-                    ["kda_chunk.hip", "kda_common.h"]),
+                    ["kda_chunk.hip", "kda_tile.h", "kda_common.h"]),
     "decode": (os.path.join(ROOT, "profiles", "decode_ckda_decode_b256_counters.md"),
                ["kda_decode.hip", "kda_common.h"]),
 }
@@ -173,6 +173,13 @@ def bench_prefill(name, steps, warmup, log):
                                               workspace=ws), steps, warmup, stream)
         res.update(path="gdn2-twopass", ms=ms, kernels={"gdn2_chunk_fwd": ms})
         del ws, e, wg
+    elif w.gates == "sfda":
+        # SFDA: complex rotation-decay gates in alpha's place, two-pass path
+        ws = torch.empty(kda.workspace_size(w.B, w.T, w.H, w.dk, w.dv), dtype=torch.uint8, device="cuda")
+        ms = timed(lambda: kda.sfda_chunk_fwd(q, k, v, a, b, initial_state=s0, out=o, final_state=sT,
+                                              workspace=ws), steps, warmup, stream)
+        res.update(path="sfda-twopass", ms=ms, kernels={"sfda_chunk_fwd": ms})
+        del ws
     elif path == "twopass":
         ws = torch.empty(kda.workspace_size(w.B, w.T, w.H, w.dk, w.dv), dtype=torch.uint8, device="cuda")
         ms, t1, t2 = timed_split(lambda: kda.chunk_records(q, k, a, b, workspace=ws, dv=w.dv),
@@ -198,13 +205,14 @@ def kernel_bytes(kernel, w):
     return chunk_bytes(w.B, w.T, w.H, w.dk, w.dv)
 
 
-def bench_decode(steps_rep, log):
+def bench_decode(steps_rep, log, name="ckda_decode_b256"):
     import torch
     import gated_delta_rule_78_amd as kda
     from gated_delta_rule_78_amd.inputs import make_workload, WORKLOADS, to_torch
-    w = WORKLOADS["ckda_decode_b256"]
+    w = WORKLOADS[name]
+    step = kda.sfda_decode_step if w.gates == "sfda" else kda.decode_step
     t0 = time.time()
-    inp = make_workload("ckda_decode_b256")
+    inp = make_workload(name)
     q, k, v, a, b, s0 = to_torch(inp)
     log(f"[bench] decode: inputs ready in {time.time() - t0:.1f}s")
     S = s0.clone()
@@ -219,7 +227,7 @@ def bench_decode(steps_rep, log):
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for t in range(n):
-            kda.decode_step(q[t], k[t], v[t], a[t], b[t], S, out=o)
+            step(q[t], k[t], v[t], a[t], b[t], S, out=o)
         e1.record(stream)
         torch.cuda.synchronize()
         if rep > 0:                      # first repetition is the warm-up
@@ -371,7 +379,7 @@ def main():
         + ", ".join(f"{k2} {v2:.3f} ms" for k2, v2 in res["kernels"].items()))
     if not args.no_extras:
         for name, steps in (("ckda_prefill_8k", args.steps), ("ckda_prefill_128k", max(2, args.steps // 4)),
-                            ("gdn2_prefill_8k", args.steps)):
+                            ("gdn2_prefill_8k", args.steps), ("sfda_prefill_8k", args.steps)):
             w3, r3, _ = bench_prefill(name, steps, min(args.warmup, 2), log)
             ms3 = r3["ms"]
             out[name] = {"value": w3.B * w3.T / (ms3 * 1e-3), "unit": "tokens/s", "ms_per_step": ms3,
@@ -387,6 +395,11 @@ def main():
                          "tokens_per_s": wd.B / (msd * 1e-3), "frac": gbs / HBM_PEAK_GBS,
                          "bytes_per_step": db, "traffic": stored_traffic("decode")}
         log(f"[bench] decode: {msd * 1e3:.1f} us/step, {gbs:.1f} GB/s")
+        ws_, mss = bench_decode(3, log, name="sfda_decode_b256")
+        gbs_s = db / (mss * 1e-3) / 1e9
+        out["sfda_decode"] = {"workload": "sfda_decode_b256", "ms_per_step": mss, "value": gbs_s, "unit": "GB/s",
+                              "tokens_per_s": ws_.B / (mss * 1e-3), "frac": gbs_s / HBM_PEAK_GBS}
+        log(f"[bench] sfda decode: {mss * 1e3:.1f} us/step, {gbs_s:.1f} GB/s")
         wt, mst, ntk = bench_decode_tokens(4, log)
         bt_ = decode_bytes(wt.B, wt.H, wt.dk, wt.dv, tokens=ntk)
         out["decode_tokens"] = {"workload": "ckda_decode_b256", "tokens_per_call": ntk, "ms_per_call": mst,

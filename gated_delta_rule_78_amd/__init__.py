@@ -75,6 +75,14 @@ def lib() -> ctypes.CDLL:
         L.kda_decode_tokens.restype = ctypes.c_int
         L.kda_gdn2_decode_tokens.argtypes = [SP, P, P, P, P, P, P, P, P, P]
         L.kda_gdn2_decode_tokens.restype = ctypes.c_int
+        L.kda_sfda_chunk_fwd.argtypes = [SP, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.kda_sfda_chunk_fwd.restype = ctypes.c_int
+        L.kda_sfda_chunk_fwd_varlen.argtypes = [SP, P, ctypes.c_int, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.kda_sfda_chunk_fwd_varlen.restype = ctypes.c_int
+        L.kda_sfda_decode_step.argtypes = [SP, P, P, P, P, P, P, P, P]
+        L.kda_sfda_decode_step.restype = ctypes.c_int
+        L.kda_sfda_decode_tokens.argtypes = [SP, P, P, P, P, P, P, P, P]
+        L.kda_sfda_decode_tokens.restype = ctypes.c_int
         L.kda_status_string.argtypes = [ctypes.c_int]
         L.kda_status_string.restype = ctypes.c_char_p
         L.kda_version.argtypes = []
@@ -261,7 +269,7 @@ def chunk_fwd_debug(q, k, v, alpha, beta, initial_state=None):
     return _chunk_call(True, q, k, v, alpha, beta, initial_state, None, None, True)
 
 
-def decode_step(q, k, v, alpha, beta, state, out=None):
+def decode_step(q, k, v, alpha, beta, state, out=None, _entry="kda_decode_step"):
     """One recurrent token for every (b, h).  q, k, alpha [B,H,dk]; v [B,H,dv];
     beta [B,H]; state fp32 [B,H,dk,dv] updated in place.  Returns o [B,H,dv]."""
     torch = _torch()
@@ -277,10 +285,10 @@ def decode_step(q, k, v, alpha, beta, state, out=None):
         out = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
     _check((q, k, v, alpha, beta, state, out), ("q", "k", "v", "alpha", "beta", "state", "out"), dev)
     shape = Shape(B, 1, H, dk, dv, 0, code)
-    rc = lib().kda_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
-                               _ptr(state), _ptr(out), _stream(dev))
+    rc = getattr(lib(), _entry)(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                _ptr(state), _ptr(out), _stream(dev))
     if rc != 0:
-        raise KdaError(rc, "kda_decode_step")
+        raise KdaError(rc, _entry)
     return out
 
 
@@ -347,7 +355,7 @@ def gdn2_decode_step(q, k, v, alpha, erase, write, state, out=None):
     return out
 
 
-def decode_tokens(q, k, v, alpha, beta, state, out=None, erase=None, write=None):
+def decode_tokens(q, k, v, alpha, beta, state, out=None, erase=None, write=None, _entry="kda_decode_tokens"):
     """Several tokens per (b, h) with the state read and written once: q, k, alpha
     [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H] (or, for Gated DeltaNet-2, beta=None with
     erase [B,T,H,dk] and write [B,T,H,dv]); state fp32 [B,H,dk,dv] in place.
@@ -375,10 +383,10 @@ def decode_tokens(q, k, v, alpha, beta, state, out=None, erase=None, write=None)
         rc = lib().kda_gdn2_decode_tokens(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase),
                                           _ptr(write), _ptr(state), _ptr(out), _stream(dev))
     else:
-        rc = lib().kda_decode_tokens(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
-                                     _ptr(state), _ptr(out), _stream(dev))
+        rc = getattr(lib(), _entry)(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                    _ptr(state), _ptr(out), _stream(dev))
     if rc != 0:
-        raise KdaError(rc, "kda_decode_tokens")
+        raise KdaError(rc, _entry)
     return out
 
 
@@ -388,10 +396,11 @@ def gdn2_decode_tokens(q, k, v, alpha, erase, write, state, out=None):
 
 
 def chunk_fwd_varlen(q, k, v, alpha, beta, cu_seqlens, initial_state=None, out=None, final_state=None,
-                     want_final=True, workspace=None, erase=None, write=None):
+                     want_final=True, workspace=None, erase=None, write=None, sfda=False):
     """Packed variable-length batch: q, k, alpha [1,T,H,dk]; v [1,T,H,dv]; beta [1,T,H]
-    (or, for Gated DeltaNet-2, beta=None with erase [1,T,H,dk] and write [1,T,H,dv]);
-    cu_seqlens int32 [N+1] on the device; states [N,H,dk,dv] fp32.
+    (or, for Gated DeltaNet-2, beta=None with erase [1,T,H,dk] and write [1,T,H,dv];
+    sfda=True: alpha holds the SFDA complex gates); cu_seqlens int32 [N+1] on the
+    device; states [N,H,dk,dv] fp32.
     Returns (o [1,T,H,dv], final_state [N,H,dk,dv] or None)."""
     torch = _torch()
     B, T, H, dk = q.shape
@@ -419,7 +428,12 @@ def chunk_fwd_varlen(q, k, v, alpha, beta, cu_seqlens, initial_state=None, out=N
            ("q", "k", "v", "alpha", "beta", "erase", "write", "cu_seqlens", "initial_state", "out", "final_state",
             "workspace"), dev)
     nbytes = workspace.numel() * workspace.element_size()
-    if g2:
+    if sfda:
+        rc = lib().kda_sfda_chunk_fwd_varlen(ctypes.byref(shape), _ptr(cu_seqlens), N, _ptr(q), _ptr(k), _ptr(v),
+                                             _ptr(alpha), _ptr(beta), _ptr(initial_state), _ptr(out),
+                                             _ptr(final_state), _ptr(workspace), ctypes.c_size_t(nbytes),
+                                             _stream(dev))
+    elif g2:
         rc = lib().kda_gdn2_chunk_fwd_varlen(ctypes.byref(shape), _ptr(cu_seqlens), N, _ptr(q), _ptr(k), _ptr(v),
                                              _ptr(alpha), _ptr(erase), _ptr(write), _ptr(initial_state), _ptr(out),
                                              _ptr(final_state), _ptr(workspace), ctypes.c_size_t(nbytes),
@@ -431,3 +445,52 @@ def chunk_fwd_varlen(q, k, v, alpha, beta, cu_seqlens, initial_state=None, out=N
     if rc != 0:
         raise KdaError(rc, "kda_chunk_fwd_varlen")
     return out, final_state
+
+
+def sfda_chunk_fwd(q, k, v, lam, beta, initial_state=None, out=None, final_state=None, want_final=True,
+                   workspace=None):
+    """SFDA chunk forward with phase control: as chunk_fwd with the decay alpha replaced by
+    the complex gates ``lam`` [B,T,H,dk] (channel 2p = Re, 2p+1 = Im of the gate of key
+    pair p); two-pass path, bf16; the workspace is allocated here when omitted.
+    Returns (o, final_state or None)."""
+    torch = _torch()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    code = _dtype_code(q)
+    for t, nm in ((k, "k"), (lam, "lam"), (v, "v"), (beta, "beta")):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{nm} must have the dtype of q")
+    if k.shape != q.shape or lam.shape != q.shape or v.shape != (B, T, H, dv) or beta.shape != (B, T, H):
+        raise ValueError("shapes: q, k, lam [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H]")
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    if final_state is None and want_final:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    for t, nm in ((initial_state, "initial_state"), (final_state, "final_state")):
+        if t is not None and (t.dtype != torch.float32 or t.shape != (B, H, dk, dv)):
+            raise ValueError(f"{nm} must be float32 [B,H,dk,dv]")
+    shape = Shape(B, T, H, dk, dv, 64, code)
+    need = int(lib().kda_chunk_fwd_workspace_size(ctypes.byref(shape)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check((q, k, v, lam, beta, initial_state, out, final_state, workspace),
+           ("q", "k", "v", "lam", "beta", "initial_state", "out", "final_state", "workspace"), dev)
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = lib().kda_sfda_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(lam), _ptr(beta),
+                                  _ptr(initial_state), _ptr(out), _ptr(final_state), _ptr(workspace),
+                                  ctypes.c_size_t(nbytes), _stream(dev))
+    if rc != 0:
+        raise KdaError(rc, "kda_sfda_chunk_fwd")
+    return out, final_state
+
+
+def sfda_decode_step(q, k, v, lam, beta, state, out=None):
+    """One SFDA token for every (b, h): lam [B,H,dk] complex gates in place of alpha;
+    otherwise decode_step."""
+    return decode_step(q, k, v, lam, beta, state, out=out, _entry="kda_sfda_decode_step")
+
+
+def sfda_decode_tokens(q, k, v, lam, beta, state, out=None):
+    """SFDA form of decode_tokens (lam [B,T,H,dk] complex gates in place of alpha)."""
+    return decode_tokens(q, k, v, lam, beta, state, out=out, _entry="kda_sfda_decode_tokens")

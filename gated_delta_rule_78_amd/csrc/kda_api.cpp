@@ -76,6 +76,7 @@ struct ChunkPtrs {
   size_t ws_bytes;
   const void* erase = nullptr;  // Gated DeltaNet-2 gates
   const void* write = nullptr;
+  bool cpx = false;             // SFDA complex gates in alpha (two-pass, bf16 only)
 };
 
 // kNeedQKAB: q, k, alpha and beta (or, with kNeedG2, the erase gate in beta's place)
@@ -91,6 +92,7 @@ int validate_chunk(const kda_shape* shape, const ChunkPtrs& p, int need, int64_t
   if (rc) return rc;
   const kda_shape& s = *shape;
   if (s.dtype == KDA_F32 && (s.dk != 64 || s.dv != 64)) return KDA_ERR_UNSUPPORTED;
+  if (p.cpx && (s.dtype != KDA_BF16 || p.erase || p.write)) return KDA_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)s.B * s.T * s.H;
   const int64_t st_bytes = (n_states < 0 ? (int64_t)s.B : n_states) * s.H * s.dk * s.dv * 4;
   const bool g2 = (need & kNeedG2) != 0;
@@ -135,6 +137,7 @@ kda::ChunkArgs chunk_args(const kda_shape& s, const ChunkPtrs& p, void* stream) 
                    s.dtype == KDA_BF16, stream, value_tile_override()};
   a.erase = p.erase;
   a.write = p.write;
+  a.cpx = p.cpx;
   return a;
 }
 
@@ -330,7 +333,7 @@ int kda_gdn2_chunk_fwd(const kda_shape* shape, const void* q, const void* k, con
 // ntok < 0: the single decode step (shape->T ignored); else ntok = shape->T tokens per (b, h)
 static int decode_impl(const kda_shape* shape, const void* q, const void* k, const void* v, const void* alpha,
                        const void* beta, const void* erase, const void* write, float* state, void* o,
-                       void* stream, bool multi) {
+                       void* stream, bool multi, bool cpx = false) {
   int es = 0;
   int rc = check_shape(shape, true, &es);
   if (rc) return rc;
@@ -363,6 +366,7 @@ static int decode_impl(const kda_shape* shape, const void* q, const void* k, con
   a.write = write;
   a.ntok = ntok;
   a.H = s.H;
+  a.cpx = cpx;
   return kda::launch_decode(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -396,6 +400,36 @@ int kda_gdn2_decode_tokens(const kda_shape* shape, const void* q, const void* k,
     if ((int64_t)shape->B * shape->H > 0) return KDA_ERR_NULL;
   }
   return decode_impl(shape, q, k, v, alpha, nullptr, erase_gate, write_gate, state, o, stream, true);
+}
+
+int kda_sfda_chunk_fwd(const kda_shape* shape, const void* q, const void* k, const void* v, const void* lambda,
+                       const void* beta, const float* initial_state, void* o, float* final_state, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  ChunkPtrs p{q, k, v, lambda, beta, initial_state, o, final_state, nullptr, workspace, workspace_bytes};
+  p.cpx = true;
+  int rc = validate_chunk(shape, p, kNeedQKAB | kNeedVO | kNeedWS);
+  if (rc) return rc;
+  rc = run_records(*shape, p, stream);
+  return rc ? rc : run_apply(*shape, p, stream);
+}
+
+int kda_sfda_chunk_fwd_varlen(const kda_shape* shape, const int* cu_seqlens, int n_seqs, const void* q,
+                              const void* k, const void* v, const void* lambda, const void* beta,
+                              const float* initial_state, void* o, float* final_state, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  ChunkPtrs p{q, k, v, lambda, beta, initial_state, o, final_state, nullptr, workspace, workspace_bytes};
+  p.cpx = true;
+  return chunk_varlen_impl(shape, cu_seqlens, n_seqs, p, stream);
+}
+
+int kda_sfda_decode_step(const kda_shape* shape, const void* q, const void* k, const void* v, const void* lambda,
+                         const void* beta, float* state, void* o, void* stream) {
+  return decode_impl(shape, q, k, v, lambda, beta, nullptr, nullptr, state, o, stream, false, true);
+}
+
+int kda_sfda_decode_tokens(const kda_shape* shape, const void* q, const void* k, const void* v, const void* lambda,
+                           const void* beta, float* state, void* o, void* stream) {
+  return decode_impl(shape, q, k, v, lambda, beta, nullptr, nullptr, state, o, stream, true, true);
 }
 
 }  // extern "C"

@@ -1037,6 +1037,7 @@ static hipError_t launch_prep_g(const ChunkArgs& a, void* ws, int cpw) {
 // first half of the fused kernel writes the fp32 ones (and the bf16 ones when
 // KDA_RECORDS_FUSED is set in the environment, for comparison)
 hipError_t launch_prep(const ChunkArgs& a, void* ws, int cpw) {
+  if (a.cpx) return launch_records(a, ws, cpw);  // complex gates: that kernel only
   if (a.bf16 && (a.dk == 64 || a.dk == 128) && (long)C * a.H * a.dk * 2 < (1L << 32) &&
       !getenv("KDA_RECORDS_FUSED"))
     return launch_records(a, ws, cpw);

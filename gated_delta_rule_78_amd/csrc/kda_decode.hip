@@ -21,7 +21,10 @@ namespace kda {
 
 // G2: Gated DeltaNet-2 step -- the read goes through the erase gate, u = S'^T (b o k),
 // the write through the write gate, delta = w o v - u (no beta).
-template <typename T, int DK, int DV, bool G2>
+// CPX: SFDA step -- S' = Lambda S with complex gates (SFDA page, "Arquitectura
+// Central"): alpha holds (Re, Im) of the gate of each key-channel pair, and rows 2p, 2p+1
+// of every state column (one complex coordinate) are multiplied by that gate.
+template <typename T, int DK, int DV, bool G2, bool CPX = false>
 __global__ __launch_bounds__(512) void decode_kernel(const void* __restrict__ q,
                                                      const void* __restrict__ k,
                                                      const void* __restrict__ v,
@@ -37,6 +40,7 @@ __global__ __launch_bounds__(512) void decode_kernel(const void* __restrict__ q,
   constexpr int RG = NT / TPR;     // row groups
   constexpr int RPT = DK / RG;     // rows per thread
   static_assert(RPT * RG == DK && TPR * 4 == DV, "tile split");
+  static_assert(!CPX || (TPR < 64 && RG % 2 == 0), "row pairs sit TPR lanes apart in one wave");
 
   __shared__ float s_q[DK], s_k[DK], s_a[DK], s_v[DV];
   __shared__ float s_e[G2 ? DK : 1];  // read-side key b o k (G2)
@@ -97,8 +101,19 @@ __global__ __launch_bounds__(512) void decode_kernel(const void* __restrict__ q,
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int r = rg + RG * i;
-      const float a = s_a[r], kk = G2 ? s_e[r] : s_k[r], qq = s_q[r];
-      s[i].x *= a; s[i].y *= a; s[i].z *= a; s[i].w *= a;
+      const float kk = G2 ? s_e[r] : s_k[r], qq = s_q[r];
+      if constexpr (CPX) {
+        // the pair row r ^ 1 is held by lane ^ TPR (row group rg ^ 1, same columns):
+        // row 2p <- Re s_2p - Im s_2p+1, row 2p+1 <- Im s_2p + Re s_2p+1
+        const float lr = s_a[r & ~1], li = (r & 1) ? s_a[r] : -s_a[r | 1];
+        const float px = __shfl_xor(s[i].x, TPR), py = __shfl_xor(s[i].y, TPR);
+        const float pz = __shfl_xor(s[i].z, TPR), pw = __shfl_xor(s[i].w, TPR);
+        s[i].x = lr * s[i].x + li * px; s[i].y = lr * s[i].y + li * py;
+        s[i].z = lr * s[i].z + li * pz; s[i].w = lr * s[i].w + li * pw;
+      } else {
+        const float a = s_a[r];
+        s[i].x *= a; s[i].y *= a; s[i].z *= a; s[i].w *= a;
+      }
       u[0] += kk * s[i].x; u[1] += kk * s[i].y; u[2] += kk * s[i].z; u[3] += kk * s[i].w;
       p[0] += qq * s[i].x; p[1] += qq * s[i].y; p[2] += qq * s[i].z; p[3] += qq * s[i].w;
     }
@@ -151,23 +166,27 @@ __global__ __launch_bounds__(512) void decode_kernel(const void* __restrict__ q,
   }
 }
 
-template <typename T, int DK, int DV, bool G2>
+template <typename T, int DK, int DV, bool G2, bool CPX>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
-  hipLaunchKernelGGL((decode_kernel<T, DK, DV, G2>), dim3(a.BH), dim3(512), 0, (hipStream_t)a.stream,
+  hipLaunchKernelGGL((decode_kernel<T, DK, DV, G2, CPX>), dim3(a.BH), dim3(512), 0, (hipStream_t)a.stream,
                      a.q, a.k, a.v, a.alpha, a.beta, a.state, a.o, a.erase, a.write, a.ntok, a.H);
   return hipGetLastError();
 }
 
-template <typename T, bool G2>
+template <typename T, bool G2, bool CPX = false>
 static hipError_t launch_decode_d(const DecodeArgs& a) {
-  if (a.dk == 64 && a.dv == 64) return launch_decode_t<T, 64, 64, G2>(a);
-  if (a.dk == 64 && a.dv == 128) return launch_decode_t<T, 64, 128, G2>(a);
-  if (a.dk == 128 && a.dv == 64) return launch_decode_t<T, 128, 64, G2>(a);
-  return launch_decode_t<T, 128, 128, G2>(a);
+  if (a.dk == 64 && a.dv == 64) return launch_decode_t<T, 64, 64, G2, CPX>(a);
+  if (a.dk == 64 && a.dv == 128) return launch_decode_t<T, 64, 128, G2, CPX>(a);
+  if (a.dk == 128 && a.dv == 64) return launch_decode_t<T, 128, 64, G2, CPX>(a);
+  return launch_decode_t<T, 128, 128, G2, CPX>(a);
 }
 
 hipError_t launch_decode(const DecodeArgs& a) {
   if (a.BH == 0) return hipSuccess;
+  if (a.cpx) {
+    if (a.erase) return hipErrorInvalidValue;
+    return a.bf16 ? launch_decode_d<bf16_t, false, true>(a) : launch_decode_d<float, false, true>(a);
+  }
   if (a.erase) return a.bf16 ? launch_decode_d<bf16_t, true>(a) : launch_decode_d<float, true>(a);
   return a.bf16 ? launch_decode_d<bf16_t, false>(a) : launch_decode_d<float, false>(a);
 }

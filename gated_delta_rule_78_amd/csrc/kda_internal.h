@@ -15,6 +15,8 @@ struct DecodeArgs {
   // Gated DeltaNet-2 gates (both set, beta unused) or both NULL (KDA / CKDA)
   const void* erase = nullptr;  // [BH, dk]
   const void* write = nullptr;  // [BH, dv]
+  // SFDA complex gates: alpha holds (Re, Im) of the gate of each key-channel pair
+  bool cpx = false;
   // tokens per (b, h) in one call: inputs [B, ntok, H, .]; BH = B * H
   int ntok = 1;
   int H = 1;
@@ -33,6 +35,8 @@ struct ChunkArgs {
   // Gated DeltaNet-2 gates (both set, beta unused) or both NULL (KDA / CKDA)
   const void* erase = nullptr;  // [B, T, H, dk]
   const void* write = nullptr;  // [B, T, H, dv]
+  // SFDA complex gates: alpha holds (Re, Im) of the gate of each key-channel pair
+  bool cpx = false;
   // packed variable-length batch (two-pass path only): B = 1, n_seqs sequences at device
   // offsets cu[0..n_seqs]; the chunk table (gmax entries (sequence, chunk), the first
   // global chunk of each sequence, the number of chunks) lives in the workspace

@@ -139,9 +139,66 @@ __device__ __forceinline__ void put_level(const f32x4_t& acc, int I, int g, int 
   }
 }
 
+// Running gate products on an item's channel pair (2c, 2c+1).  Real gates (KDA / CKDA /
+// Gated DeltaNet-2): two independent channels, (x, y) their products.  Complex gates
+// (SFDA page, "Arquitectura Central": the pair is one complex coordinate and its gate the
+// complex number lambda = (Re, Im) in channels (2c, 2c+1)): (x, y) = (Re, Im) of the
+// product.  The row side of a decayed product takes the conjugate (the transpose of a
+// rotation-decay block), the column side the product itself:
+//   r_ij = F_i B_j,  x_i^T R_ij y_j = (conj(F_i) x_i) . (B_j y_j)  over real channel pairs.
+template <bool CPX>
+struct Gp2 {
+  float x, y;
+  __device__ __forceinline__ static Gp2 one() { return Gp2{1.f, CPX ? 0.f : 1.f}; }
+  __device__ __forceinline__ Gp2 operator*(const Gp2& o) const {
+    if constexpr (CPX) return Gp2{x * o.x - y * o.y, x * o.y + y * o.x};
+    else return Gp2{x * o.x, y * o.y};
+  }
+  __device__ __forceinline__ void operator*=(const Gp2& o) { *this = *this * o; }
+  // row-side operand of the pair (v0, v1): conj(F) v (complex) or (F0 v0, F1 v1)
+  __device__ __forceinline__ void row(float v0, float v1, float& r0, float& r1) const {
+    if constexpr (CPX) {
+      r0 = x * v0 + y * v1;
+      r1 = x * v1 - y * v0;
+    } else {
+      r0 = v0 * x;
+      r1 = v1 * y;
+    }
+  }
+  // column-side operand: B v (complex) or (B0 v0, B1 v1)
+  __device__ __forceinline__ void col(float v0, float v1, float& r0, float& r1) const {
+    if constexpr (CPX) {
+      r0 = x * v0 - y * v1;
+      r1 = x * v1 + y * v0;
+    } else {
+      r0 = v0 * x;
+      r1 = v1 * y;
+    }
+  }
+};
+
+// Column-side scale of eight consecutive channels of a bf16 fragment by the gate products p
+// (channel pairs (2i, 2i+1) of p: complex numbers when CPX)
+template <bool CPX>
+__device__ __forceinline__ void scale_col(Frag<bf16_t>& f, const float (&p)[8]) {
+  if constexpr (!CPX) {
+    f.scale(p);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float v0 = __uint_as_float(f.w[i] << 16), v1 = __uint_as_float(f.w[i] & 0xFFFF0000u);
+      const Gp2<true> g{p[2 * i], p[2 * i + 1]};
+      float r0, r1;
+      g.col(v0, v1, r0, r1);
+      f.w[i] = pack_bf16x2(r0, r1);
+    }
+  }
+}
+
 }  // namespace
 
-template <int DK, bool G2>
+// CPX: SFDA complex gates (the alpha tensor holds (Re, Im) of each channel pair's gate).
+template <int DK, bool G2, bool CPX>
 __global__ __launch_bounds__(256, 2) void chunk_records_kernel(
     const void* __restrict__ gq, const void* __restrict__ gk, const void* __restrict__ galpha,
     const void* __restrict__ gbeta, const void* __restrict__ gerase, int Tlen, int H, char* __restrict__ ws,
@@ -151,6 +208,8 @@ __global__ __launch_bounds__(256, 2) void chunk_records_kernel(
   using K = RCfg<DK>;
   using RL = RecordLayout<bf16_t, DK>;
   using R = Raw<bf16_t>;
+  using G = Gp2<CPX>;
+  static_assert(!(G2 && CPX), "complex gates take the KDA erase/write form");
   static_assert(RL::RS_DK == K::RS_DK && RL::RS_C == K::RS_C, "record rows match the LDS tiles");
   constexpr int NT = K::NT;
   constexpr int LDF = K::RS_F / 4;
@@ -249,13 +308,16 @@ __global__ __launch_bounds__(256, 2) void chunk_records_kernel(
     const int icp = tid % GRP;
 
     // ---------------- item registers, fp32 (rows past the end: q = k = 0, alpha = 1)
-    float qf[SUB][2], kf[SUB][2], al[SUB][2];
+    // (rows past the end: gate 1, i.e. (1, 1) for real gates, 1 + 0i for complex ones)
+    float qf[SUB][2], kf[SUB][2];
+    G al[SUB];
+    constexpr uint32_t kOne = CPX ? 0x00003F80u : R::kOneWord;
     if (t0 + C <= gm.len) {  // a whole chunk (wave-uniform): no row is masked
 #pragma unroll
       for (int m = 0; m < SUB; ++m) {
         R::unpack(pq[m], qf[m][0], qf[m][1]);
         R::unpack(pk[m], kf[m][0], kf[m][1]);
-        R::unpack(pa[m], al[m][0], al[m][1]);
+        R::unpack(pa[m], al[m].x, al[m].y);
       }
     } else {
 #pragma unroll
@@ -263,7 +325,7 @@ __global__ __launch_bounds__(256, 2) void chunk_records_kernel(
         const bool ok = t0 + SUB * iI + m < gm.len;
         R::unpack(ok ? pq[m] : 0u, qf[m][0], qf[m][1]);
         R::unpack(ok ? pk[m] : 0u, kf[m][0], kf[m][1]);
-        R::unpack(ok ? pa[m] : R::kOneWord, al[m][0], al[m][1]);
+        R::unpack(ok ? pa[m] : kOne, al[m].x, al[m].y);
       }
     }
     // the key as the erase side reads it: k (KDA), b o k (Gated DeltaNet-2; the erase gate
@@ -290,39 +352,35 @@ __global__ __launch_bounds__(256, 2) void chunk_records_kernel(
     auto write_level = [&](char* buf, int lam) {
       char* LA = buf + iI * K::LVL_ROWS * K::RS_DK + 4 * icp;
       char* LB = LA + 16 * K::RS_DK;
-      float f0 = 1.f, f1 = 1.f;
+      G f = G::one();
 #pragma unroll
       for (int m = 0; m < SUB; ++m) {
         if (m & lam) {
-          if ((m & (lam - 1)) == 0) {
-            f0 = al[m][0];
-            f1 = al[m][1];
-          } else {
-            f0 *= al[m][0];
-            f1 *= al[m][1];
-          }
+          if ((m & (lam - 1)) == 0)
+            f = al[m];
+          else
+            f *= al[m];
           const int u = (m / (2 * lam)) * lam + (m & (lam - 1));
-          const float q0 = qf[m][0], q1 = qf[m][1];
-          float k0, k1;
+          float k0, k1, r0, r1;
           read_key(m, k0, k1);
-          R::st(LA + u * K::RS_DK, q0 * f0, q1 * f1);
-          R::st(LA + (8 + u) * K::RS_DK, k0 * f0, k1 * f1);
+          f.row(qf[m][0], qf[m][1], r0, r1);
+          R::st(LA + u * K::RS_DK, r0, r1);
+          f.row(k0, k1, r0, r1);
+          R::st(LA + (8 + u) * K::RS_DK, r0, r1);
         }
       }
-      float b0 = 1.f, b1 = 1.f;
+      G bb = G::one();
 #pragma unroll
       for (int m = SUB - 1; m >= 0; --m) {
         if (!(m & lam)) {
-          if ((m & (lam - 1)) == lam - 1) {
-            b0 = 1.f;
-            b1 = 1.f;
-          } else {
-            b0 *= al[m + 1][0];
-            b1 *= al[m + 1][1];
-          }
+          if ((m & (lam - 1)) == lam - 1)
+            bb = G::one();
+          else
+            bb *= al[m + 1];
           const int v = (m / (2 * lam)) * lam + (m & (lam - 1));
-          const float k0 = kf[m][0], k1 = kf[m][1];
-          R::st(LB + v * K::RS_DK, k0 * b0, k1 * b1);
+          float r0, r1;
+          bb.col(kf[m][0], kf[m][1], r0, r1);
+          R::st(LB + v * K::RS_DK, r0, r1);
         }
       }
     };
@@ -333,30 +391,30 @@ __global__ __launch_bounds__(256, 2) void chunk_records_kernel(
       {
         char* xq = R_X + K::OFF_XQ + (SUB * (iI - 1)) * K::RS_DK + 4 * icp;
         char* xk = R_X + K::OFF_XK + (SUB * (iI - 1)) * K::RS_DK + 4 * icp;
-        float f0 = 1.f, f1 = 1.f;
+        G f = G::one();
 #pragma unroll
         for (int m = 0; m < SUB; ++m) {
-          f0 *= al[m][0];
-          f1 *= al[m][1];
+          f *= al[m];
           if (iI >= 1) {
-            const float q0 = qf[m][0], q1 = qf[m][1];
-            float k0, k1;
+            float k0, k1, r0, r1;
             read_key(m, k0, k1);
-            R::st(xq + m * K::RS_DK, q0 * f0, q1 * f1);
-            R::st(xk + m * K::RS_DK, k0 * f0, k1 * f1);
+            f.row(qf[m][0], qf[m][1], r0, r1);
+            R::st(xq + m * K::RS_DK, r0, r1);
+            f.row(k0, k1, r0, r1);
+            R::st(xk + m * K::RS_DK, r0, r1);
           }
         }
-        *(float2*)(GT + iI * DK + 2 * icp) = make_float2(f0, f1);
+        *(float2*)(GT + iI * DK + 2 * icp) = make_float2(f.x, f.y);
       }
       if (iI <= 2) {
         char* y = R_X + K::OFF_Y + (SUB * iI) * K::RS_DK + 4 * icp;
-        float b0 = 1.f, b1 = 1.f;
+        G bb = G::one();
 #pragma unroll
         for (int m = SUB - 1; m >= 0; --m) {
-          const float k0 = kf[m][0], k1 = kf[m][1];
-          R::st(y + m * K::RS_DK, k0 * b0, k1 * b1);
-          b0 *= al[m][0];
-          b1 *= al[m][1];
+          float r0, r1;
+          bb.col(kf[m][0], kf[m][1], r0, r1);
+          R::st(y + m * K::RS_DK, r0, r1);
+          bb *= al[m];
         }
       }
       float d[SUB];
@@ -415,11 +473,13 @@ __global__ __launch_bounds__(256, 2) void chunk_records_kernel(
           float4 p0 = *(const float4*)G1, p1 = *(const float4*)(G1 + 4);
           if (pi == 1) {
             const float4 e0 = *(const float4*)(GT + 2 * DK + c0), e1 = *(const float4*)(GT + 2 * DK + c0 + 4);
-            p0 = make_float4(p0.x * e0.x, p0.y * e0.y, p0.z * e0.z, p0.w * e0.w);
-            p1 = make_float4(p1.x * e1.x, p1.y * e1.y, p1.z * e1.z, p1.w * e1.w);
+            const G a0 = G{p0.x, p0.y} * G{e0.x, e0.y}, a1 = G{p0.z, p0.w} * G{e0.z, e0.w};
+            const G a2 = G{p1.x, p1.y} * G{e1.x, e1.y}, a3 = G{p1.z, p1.w} * G{e1.z, e1.w};
+            p0 = make_float4(a0.x, a0.y, a1.x, a1.y);
+            p1 = make_float4(a2.x, a2.y, a3.x, a3.y);
           }
           const float pv8[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-          fb[ks].scale(pv8);
+          scale_col<CPX>(fb[ks], pv8);
         }
         mma(ra, fa[ks], fb[ks]);
         mma(rt, fk[ks], fb[ks]);
@@ -437,41 +497,39 @@ __global__ __launch_bounds__(256, 2) void chunk_records_kernel(
 
     // ================= phase C: Q o gamma and (K o rho)^T into the record, gamma_last,
     // level 4 (buffer 1) and level 2 (buffer 0) operands
-    float Gp[2] = {1.f, 1.f};  // gate product of the blocks before the item's block
+    G Gp = G::one();  // gate product of the blocks before the item's block
     if (has_item) {
-      const float2 t0v = *(const float2*)(GT + 2 * icp), t1v = *(const float2*)(GT + DK + 2 * icp);
-      const float2 t2v = *(const float2*)(GT + 2 * DK + 2 * icp), t3v = *(const float2*)(GT + 3 * DK + 2 * icp);
-      float Rp[2];
-      Gp[0] = iI == 0 ? 1.f : iI == 1 ? t0v.x : iI == 2 ? t0v.x * t1v.x : t0v.x * t1v.x * t2v.x;
-      Gp[1] = iI == 0 ? 1.f : iI == 1 ? t0v.y : iI == 2 ? t0v.y * t1v.y : t0v.y * t1v.y * t2v.y;
-      Rp[0] = iI == 3 ? 1.f : iI == 2 ? t3v.x : iI == 1 ? t2v.x * t3v.x : t1v.x * t2v.x * t3v.x;
-      Rp[1] = iI == 3 ? 1.f : iI == 2 ? t3v.y : iI == 1 ? t2v.y * t3v.y : t1v.y * t2v.y * t3v.y;
-      if (iI == 3) *(float2*)(GC + 2 * icp) = make_float2(Gp[0] * t3v.x, Gp[1] * t3v.y);  // gamma_last
+      const float2 t0f = *(const float2*)(GT + 2 * icp), t1f = *(const float2*)(GT + DK + 2 * icp);
+      const float2 t2f = *(const float2*)(GT + 2 * DK + 2 * icp), t3f = *(const float2*)(GT + 3 * DK + 2 * icp);
+      const G t0v{t0f.x, t0f.y}, t1v{t1f.x, t1f.y}, t2v{t2f.x, t2f.y}, t3v{t3f.x, t3f.y};
+      Gp = iI == 0 ? G::one() : iI == 1 ? t0v : iI == 2 ? t0v * t1v : t0v * t1v * t2v;
+      const G Rp = iI == 3 ? G::one() : iI == 2 ? t3v : iI == 1 ? t2v * t3v : t1v * t2v * t3v;
+      if (iI == 3) {  // gamma_last
+        const G gl = Gp * t3v;
+        *(float2*)(GC + 2 * icp) = make_float2(gl.x, gl.y);
+      }
       {
         char* qg = rec + RL::QG + (SUB * iI) * K::RS_DK + 4 * icp;
-        float f0 = Gp[0], f1 = Gp[1];
+        G f = Gp;
 #pragma unroll
         for (int m = 0; m < SUB; ++m) {
-          f0 *= al[m][0];
-          f1 *= al[m][1];
-          const float q0 = qf[m][0], q1 = qf[m][1];
-          R::st(qg + m * K::RS_DK, q0 * f0, q1 * f1);
+          f *= al[m];
+          float r0, r1;
+          f.row(qf[m][0], qf[m][1], r0, r1);
+          R::st(qg + m * K::RS_DK, r0, r1);
         }
       }
       {
         char* pr0 = rec + RL::KRT + (2 * icp) * K::RS_C + (SUB * iI) * 2;
-        float b0 = Rp[0], b1 = Rp[1];
+        G bb = Rp;
 #pragma unroll
         for (int h8 = SUB - 8; h8 >= 0; h8 -= 8) {
           float r8a[8], r8b[8];
 #pragma unroll
           for (int mm = 7; mm >= 0; --mm) {
             const int m = h8 + mm;
-            const float k0 = kf[m][0], k1 = kf[m][1];
-            r8a[mm] = k0 * b0;
-            r8b[mm] = k1 * b1;
-            b0 *= al[m][0];
-            b1 *= al[m][1];
+            bb.col(kf[m][0], kf[m][1], r8a[mm], r8b[mm]);
+            bb *= al[m];
           }
           st_row8<bf16_t>(pr0 + h8 * 2, r8a);
           st_row8<bf16_t>(pr0 + K::RS_C + h8 * 2, r8b);
@@ -496,19 +554,17 @@ __global__ __launch_bounds__(256, 2) void chunk_records_kernel(
     if (has_item) {
       write_level(R_L, 1);
       char* pg0 = R_X + K::OFF_KGT + (2 * icp) * K::RS_C + (SUB * iI) * 2;
-      float f0 = Gp[0], f1 = Gp[1];
+      G f = Gp;
 #pragma unroll
       for (int h8 = 0; h8 < SUB; h8 += 8) {
         float g8a[8], g8b[8];
 #pragma unroll
         for (int mm = 0; mm < 8; ++mm) {
           const int m = h8 + mm;
-          f0 *= al[m][0];
-          f1 *= al[m][1];
+          f *= al[m];
           float k0, k1;
           read_key(m, k0, k1);
-          g8a[mm] = k0 * f0;
-          g8b[mm] = k1 * f1;
+          f.row(k0, k1, g8a[mm], g8b[mm]);
         }
         st_row8<bf16_t>(pg0 + h8 * 2, g8a);
         st_row8<bf16_t>(pg0 + K::RS_C + h8 * 2, g8b);
@@ -738,10 +794,10 @@ __global__ __launch_bounds__(256, 2) void chunk_records_kernel(
   }
 }
 
-template <int DK, bool G2>
+template <int DK, bool G2, bool CPX>
 static hipError_t launch_records_t(const ChunkArgs& a, char* ws, int cpw) {
   using K = RCfg<DK>;
-  auto kern = chunk_records_kernel<DK, G2>;
+  auto kern = chunk_records_kernel<DK, G2, CPX>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, K::LDS);
@@ -761,10 +817,11 @@ static hipError_t launch_records_t(const ChunkArgs& a, char* ws, int cpw) {
 
 // bf16 records with the two-workgroups-per-CU kernel (d_k = 64 or 128)
 hipError_t launch_records(const ChunkArgs& a, void* ws, int cpw) {
-  if (!a.bf16 || (a.dk != 64 && a.dk != 128)) return hipErrorInvalidValue;
-  if (a.erase)
-    return a.dk == 64 ? launch_records_t<64, true>(a, (char*)ws, cpw) : launch_records_t<128, true>(a, (char*)ws, cpw);
-  return a.dk == 64 ? launch_records_t<64, false>(a, (char*)ws, cpw) : launch_records_t<128, false>(a, (char*)ws, cpw);
+  if (!a.bf16 || (a.dk != 64 && a.dk != 128) || (a.cpx && a.erase)) return hipErrorInvalidValue;
+  char* w = (char*)ws;
+  if (a.cpx) return a.dk == 64 ? launch_records_t<64, false, true>(a, w, cpw) : launch_records_t<128, false, true>(a, w, cpw);
+  if (a.erase) return a.dk == 64 ? launch_records_t<64, true, false>(a, w, cpw) : launch_records_t<128, true, false>(a, w, cpw);
+  return a.dk == 64 ? launch_records_t<64, false, false>(a, w, cpw) : launch_records_t<128, false, false>(a, w, cpw);
 }
 
 }  // namespace kda

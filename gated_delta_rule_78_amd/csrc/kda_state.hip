@@ -76,7 +76,9 @@ __device__ __forceinline__ void fence_sched() {
 //   S <- diag(gamma_last) S + (K o rho)^T Delta
 // With one compute wave per SIMD little else hides LDS latency, so the operand
 // fragments of each group of products are loaded one group ahead (software pipelining).
-template <typename T, int DK, int VT, bool G2 = false>
+// CPX: SFDA complex gates -- gamma_last holds (Re, Im) per key-channel pair and turns the
+// state's row pairs (rows 2p, 2p+1 = one complex coordinate, same lane) by that product.
+template <typename T, int DK, int VT, bool G2 = false, bool CPX = false>
 __device__ __forceinline__ void state_chunk(const char* rec, char* vv, const char* wv, f32x4_t (&S)[DK / 16],
                                             int wave, int g, int n) {
   using K = SCfg<T, DK, VT, G2>;
@@ -195,10 +197,19 @@ __device__ __forceinline__ void state_chunk(const char* rec, char* vv, const cha
 #pragma unroll
     for (int rr = 0; rr < RH; ++rr) {
       const int r = half * RH + rr;
-      S[r][0] *= gc[half][rr].x;
-      S[r][1] *= gc[half][rr].y;
-      S[r][2] *= gc[half][rr].z;
-      S[r][3] *= gc[half][rr].w;
+      if constexpr (CPX) {
+        const float4 c = gc[half][rr];
+        const float s0 = S[r][0], s1 = S[r][1], s2 = S[r][2], s3 = S[r][3];
+        S[r][0] = c.x * s0 - c.y * s1;
+        S[r][1] = c.y * s0 + c.x * s1;
+        S[r][2] = c.z * s2 - c.w * s3;
+        S[r][3] = c.w * s2 + c.z * s3;
+      } else {
+        S[r][0] *= gc[half][rr].x;
+        S[r][1] *= gc[half][rr].y;
+        S[r][2] *= gc[half][rr].z;
+        S[r][3] *= gc[half][rr].w;
+      }
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) mma(S[r], fk[half][rr][s2], bd[s2]);
     }
@@ -215,7 +226,7 @@ __device__ __forceinline__ void state_chunk(const char* rec, char* vv, const cha
     }
 }
 
-template <typename T, int DK, int VT, bool G2>
+template <typename T, int DK, int VT, bool G2, bool CPX = false>
 __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const char* __restrict__ ws,
                                                                          const void* __restrict__ gv,
                                                                          const float* s0, void* __restrict__ go,
@@ -339,7 +350,7 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
       if (producer) {
         if (c + 1 < nchunks) issue(c + 1, recQ, vQ, wQ);
       } else {
-        state_chunk<T, DK, VT, G2>(recP, vP, wP, S, wave, g, n);
+        state_chunk<T, DK, VT, G2, CPX>(recP, vP, wP, S, wave, g, n);
       }
     };
     for (int chunk = 0; chunk < nchunks; chunk += 2) {
@@ -355,7 +366,7 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
     for (int chunk = 0; chunk < nchunks; ++chunk) {
       full_barrier();
       pad_rows(chunk, v_a);
-      if (!producer) state_chunk<T, DK, VT, G2>(rec_a, v_a, w_a, S, wave, g, n);
+      if (!producer) state_chunk<T, DK, VT, G2, CPX>(rec_a, v_a, w_a, S, wave, g, n);
       lds_barrier();
       store_o(chunk, v_a);
       if (chunk + 1 < nchunks) {
@@ -374,11 +385,11 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
   }
 }
 
-template <typename T, int DK, int VT, bool G2>
+template <typename T, int DK, int VT, bool G2, bool CPX>
 static hipError_t launch_state_t(const ChunkArgs& a, const void* ws) {
   using K = SCfg<T, DK, VT, G2>;
   const int BH = a.B * a.H;
-  auto kern = chunk_state_kernel<T, DK, VT, G2>;
+  auto kern = chunk_state_kernel<T, DK, VT, G2, CPX>;
   // varlen: one chain per (sequence, head): BH = n_seqs * H
   const int BHc = a.cu ? a.n_seqs * a.H : BH;
   hipLaunchKernelGGL(kern, dim3(BHc * (a.dv / VT)), dim3(K::NT), 0, (hipStream_t)a.stream, (const char*)ws, a.v,
@@ -412,25 +423,26 @@ static int pick_state_vt(const ChunkArgs& a) {
   return vt < cap ? vt : cap;
 }
 
-template <typename T, int DK, bool G2>
+template <typename T, int DK, bool G2, bool CPX>
 static hipError_t launch_state_vt(const ChunkArgs& a, const void* ws) {
   switch (pick_state_vt(a)) {
-    case 16: return launch_state_t<T, DK, 16, G2>(a, ws);
-    case 32: return launch_state_t<T, DK, 32, G2>(a, ws);
+    case 16: return launch_state_t<T, DK, 16, G2, CPX>(a, ws);
+    case 32: return launch_state_t<T, DK, 32, G2, CPX>(a, ws);
     default:
       if constexpr (G2 && DK == 128 && sizeof(T) == 2) return hipErrorInvalidValue;  // capped at 32 above
-      else return launch_state_t<T, DK, 64, G2>(a, ws);
+      else return launch_state_t<T, DK, 64, G2, CPX>(a, ws);
   }
 }
 
-template <bool G2>
+template <bool G2, bool CPX = false>
 static hipError_t launch_state_g(const ChunkArgs& a, const void* ws) {
-  if (!a.bf16) return a.dk == 64 && a.dv == 64 ? launch_state_vt<float, 64, G2>(a, ws) : hipErrorInvalidValue;
-  return a.dk == 64 ? launch_state_vt<bf16_t, 64, G2>(a, ws) : launch_state_vt<bf16_t, 128, G2>(a, ws);
+  if (!a.bf16) return a.dk == 64 && a.dv == 64 ? launch_state_vt<float, 64, G2, CPX>(a, ws) : hipErrorInvalidValue;
+  return a.dk == 64 ? launch_state_vt<bf16_t, 64, G2, CPX>(a, ws) : launch_state_vt<bf16_t, 128, G2, CPX>(a, ws);
 }
 
 hipError_t launch_state(const ChunkArgs& a, const void* ws) {
   if ((a.cu ? a.n_seqs : a.B) * a.H == 0) return hipSuccess;
+  if (a.cpx) return a.write ? hipErrorInvalidValue : launch_state_g<false, true>(a, ws);
   return a.write ? launch_state_g<true>(a, ws) : launch_state_g<false>(a, ws);
 }
 

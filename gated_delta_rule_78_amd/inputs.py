@@ -67,6 +67,8 @@ WORKLOADS = {
                                  decode_steps=64, index=4),
     "gdn2_prefill_8k": Workload("gdn2_prefill_8k", 4, 8192, 32, 128, 128, "bf16", "gdn2", False, index=5),
     "sfda_prefill_8k": Workload("sfda_prefill_8k", 4, 8192, 32, 128, 128, "bf16", "sfda", False, index=6),
+    "sfda_decode_b256": Workload("sfda_decode_b256", 256, 1, 32, 128, 128, "bf16", "sfda", False,
+                                 decode_steps=64, index=7),
 }
 
 

@@ -195,6 +195,41 @@ int kda_gdn2_decode_step(const kda_shape* shape, const void* q, const void* k, c
                          float* state, void* o, void* stream);
 
 /*
+ * SFDA with phase control ("Resumen Tecnico: Atencion Delta de Fourier Semidirecta
+ * (SFDA)", section "Arquitectura Central"): the real decay becomes the complex diagonal
+ * Lambda_t = diag(alpha_t o e^{i theta_t}), applied in real coordinates as 2 x 2
+ * rotation-decay blocks on key-channel pairs:
+ *   S_t = (I - beta_t k_t k_t^T) Lambda_t S_{t-1} + beta_t k_t v_t^T,   o_t = S_t^T q_t,
+ *   (Lambda S)[2p]   = Re(l_p) S[2p] - Im(l_p) S[2p+1],
+ *   (Lambda S)[2p+1] = Im(l_p) S[2p] + Re(l_p) S[2p+1]      (every state column),
+ * where l_p = alpha_p e^{i theta_p} is the gate of coordinate p.  The chunk forward is
+ * the exact chunk-WY product form of the same page ("El Teorema de Chunk-WY
+ * Constructivo"), run as the two-pass forward of kda_chunk_fwd_ws.
+ *   lambda : [B, T, H, dk] in the dtype of q, 16-byte aligned: channel 2p holds Re(l_p),
+ *            channel 2p+1 holds Im(l_p) (|l_p| <= 1 is the intended range; not checked).
+ *            Zero phases (Im = 0) give KDA with the two channels of a pair sharing a decay.
+ * Other arguments, layouts, alias rules and errors as kda_chunk_fwd_ws (a workspace of
+ * kda_chunk_fwd_workspace_size bytes is required); bf16 only (KDA_ERR_UNSUPPORTED for
+ * fp32).  The varlen form takes the arguments of kda_chunk_fwd_varlen (its workspace
+ * size).  The decode step and the multi-token decode take lambda [B, H, dk] (resp.
+ * [B, T, H, dk]) in place of alpha, bf16 or fp32, otherwise as kda_decode_step and
+ * kda_decode_tokens.
+ */
+int kda_sfda_chunk_fwd(const kda_shape* shape, const void* q, const void* k, const void* v,
+                       const void* lambda, const void* beta, const float* initial_state, void* o,
+                       float* final_state, void* workspace, size_t workspace_bytes, void* stream);
+int kda_sfda_chunk_fwd_varlen(const kda_shape* shape, const int* cu_seqlens, int n_seqs,
+                              const void* q, const void* k, const void* v, const void* lambda,
+                              const void* beta, const float* initial_state, void* o,
+                              float* final_state, void* workspace, size_t workspace_bytes,
+                              void* stream);
+int kda_sfda_decode_step(const kda_shape* shape, const void* q, const void* k, const void* v,
+                         const void* lambda, const void* beta, float* state, void* o, void* stream);
+int kda_sfda_decode_tokens(const kda_shape* shape, const void* q, const void* k, const void* v,
+                           const void* lambda, const void* beta, float* state, void* o,
+                           void* stream);
+
+/*
  * One recurrent decode step for every (b, h), state updated in place:
  *   S <- (I - beta k k^T) Diag(alpha) S + beta k v^T ;  o <- S^T q.
  *   state : [B, H, dk, dv] fp32, read and written in place.

@@ -229,6 +229,48 @@ def test_varlen_argument_errors(L):
     assert fwd(ws=_p(8)) == ALIAS                    # workspace over the offsets
 
 
+def test_sfda_argument_errors(L):
+    shape = kda.Shape(1, 64, 2, 64, 64, 64, 0)
+    need = L.kda_chunk_fwd_workspace_size(ctypes.byref(shape))
+    sz = ctypes.c_size_t
+
+    def fwd(q=_p(0), lam=_p(3), beta=_p(4), o=_p(5), sT=None, ws=_p(9), n=need, sh=shape):
+        return L.kda_sfda_chunk_fwd(ctypes.byref(sh), q, _p(1), _p(2), lam, beta, None, o, sT, ws, sz(n), None)
+
+    assert L.kda_sfda_chunk_fwd(None, *([None] * 9), sz(0), None) == NULL
+    assert fwd(lam=None) == NULL
+    assert fwd(beta=None) == NULL
+    assert fwd(ws=None) == NULL
+    assert fwd(n=need - 1) == WORKSPACE
+    assert fwd(lam=_p(3, off=8)) == ALIGN
+    assert fwd(o=_p(3, off=64)) == ALIAS             # output over the complex gates
+    assert fwd(ws=_p(3)) == ALIAS                    # workspace over the gates
+    assert fwd(sh=kda.Shape(1, 64, 2, 64, 64, 64, 1)) == UNSUP   # the SFDA chunk forward is bf16
+    assert fwd(sh=kda.Shape(1, 64, 2, 96, 64, 64, 0)) == UNSUP
+
+    vshape = kda.Shape(1, 300, 2, 64, 64, 64, 0)
+    vneed = L.kda_chunk_fwd_varlen_workspace_size(ctypes.byref(vshape), 4)
+
+    def vfwd(cu=_p(8), nb=vneed, lam=_p(3)):
+        return L.kda_sfda_chunk_fwd_varlen(ctypes.byref(vshape), cu, 4, _p(0), _p(1), _p(2), lam, _p(4), None,
+                                           _p(5), None, _p(9), sz(nb), None)
+
+    assert vfwd(cu=None) == NULL
+    assert vfwd(nb=vneed - 1) == WORKSPACE
+    assert vfwd(lam=None) == NULL
+
+    dshape = kda.Shape(2, 1, 2, 64, 64, 0, 0)
+
+    def dec(lam=_p(3), st=_p(6), o=_p(7), fn=L.kda_sfda_decode_step, sh=dshape):
+        return fn(ctypes.byref(sh), _p(0), _p(1), _p(2), lam, _p(4), st, o, None)
+
+    assert dec(lam=None) == NULL
+    assert dec(st=_p(3)) == ALIAS                    # state over the gates
+    assert dec(lam=_p(3, off=1)) == ALIGN
+    assert dec(fn=L.kda_sfda_decode_tokens, sh=kda.Shape(2, -1, 2, 64, 64, 0, 0)) == SHAPE
+    assert dec(fn=L.kda_sfda_decode_tokens, lam=None, sh=kda.Shape(2, 3, 2, 64, 64, 0, 0)) == NULL
+
+
 def test_decode_argument_errors(L):
     assert L.kda_decode_step(None, *([None] * 8)) == NULL
     assert _decode(L, dtype=3) == DTYPE

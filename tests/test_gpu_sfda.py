@@ -1,0 +1,173 @@
+"""SFDA (phase control) on the GPU against the fp64 oracle (gpu).
+
+The complex gates lambda = alpha e^{i theta} of each key-channel pair ride in the alpha
+tensor as (Re, Im); the chunk forward runs the two-pass path (bf16), the decode step and
+the multi-token decode run bf16 and fp32.  Small cases are compared on every (b, h); the
+full 8K-token workload is compared on sampled heads.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gated_delta_rule_78_amd.inputs import bf16_bits, make, make_workload, as_float
+from kda_testutil import TOL, heads_of, inputs_to_dev, rel_err_slices, state_to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu(inp, S0):
+    import gated_delta_rule_78_amd as kda
+    import torch
+    q, k, v, lam, b = inputs_to_dev(inp)
+    s0 = None if S0 is None else state_to_dev(S0)
+    o, sT = kda.sfda_chunk_fwd(q, k, v, lam, b, initial_state=s0)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), sT.cpu().numpy()
+
+
+def _check(inp, S0, heads=None, label=""):
+    m = inp.meta
+    B, T, H, dk, dv = m["B"], m["T"], m["H"], m["dk"], m["dv"]
+    print(f"sfda {label} B={B} T={T} H={H} dk={dk} dv={dv} {inp.dtype}", flush=True)
+    o_gpu, s_gpu = _gpu(inp, S0)
+    sel = list(range(B * H)) if heads is None else list(heads)
+    s0_ref = None if S0 is None else S0.reshape(B * H, dk, dv)[sel]
+    o_ref, s_ref = oracle.fwd_sfda(inp.q, inp.k, inp.v, inp.alpha, inp.beta, S0=s0_ref, heads=sel, col_block=16)
+    eo = rel_err_slices(heads_of(o_gpu, sel, H), o_ref, len(sel))
+    es = rel_err_slices(s_gpu.reshape(B * H, dk, dv)[sel], s_ref, len(sel))
+    print(f"   err o {eo:.3e}  state {es:.3e}", flush=True)
+    assert eo <= TOL[inp.dtype], (label, eo)
+    assert es <= TOL[inp.dtype], (label, es)
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 200])
+def test_sfda_lengths(T):
+    inp = make(1, T, 2, 128, 128, "bf16", "sfda", False, seed=600 + T)
+    _check(inp, inp.S0, label=f"T{T}")
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64)])
+def test_sfda_head_widths(dk, dv):
+    inp = make(2, 150, 3, dk, dv, "bf16", "sfda", False, seed=61 + dk + dv)
+    _check(inp, inp.S0, label=f"d{dk}x{dv}")
+
+
+def test_sfda_zero_start_and_wide_batch():
+    """B*H = 100: the state pass runs 32-column tiles; zero start state."""
+    inp = make(4, 130, 25, 128, 128, "bf16", "sfda", False, seed=63)
+    _check(inp, None, label="B4H25")
+
+
+def test_sfda_quarter_turns_zeros_and_unit_gates():
+    """Gates drawn from {0, 1, -1, i, -i} on a third of the pairs: exact zeros, pure
+    quarter and half turns of the state mixed with ordinary decay."""
+    inp = make(1, 256, 2, 128, 128, "bf16", "sfda", False, seed=65)
+    rng = np.random.default_rng(65)
+    g = as_float(inp.alpha, "bf16").copy()
+    m = rng.random(g.shape[:-1] + (g.shape[-1] // 2,)) < 0.33
+    pick = rng.integers(0, 5, size=int(m.sum()))
+    re_ = np.array([0.0, 1.0, -1.0, 0.0, 0.0], np.float32)[pick]
+    im_ = np.array([0.0, 0.0, 0.0, 1.0, -1.0], np.float32)[pick]
+    gr, gi = g[..., 0::2], g[..., 1::2]
+    gr[m], gi[m] = re_, im_
+    g[..., 0::2], g[..., 1::2] = gr, gi
+    inp.alpha = bf16_bits(g)
+    _check(inp, inp.S0, label="special gates")
+
+
+def test_sfda_zero_phases_match_kda_path():
+    """Im lambda = 0 with both channels of a pair decayed by Re lambda is KDA: the SFDA
+    path and the KDA two-pass path agree to rounding."""
+    import gated_delta_rule_78_amd as kda
+    import torch
+    inp = make(2, 200, 3, 128, 128, "bf16", "kda", False, seed=67)
+    a = as_float(inp.alpha, "bf16")
+    tied = np.repeat(a[..., 0::2], 2, axis=-1)
+    lam = tied.copy()
+    lam[..., 1::2] = 0.0
+    inp.alpha = bf16_bits(tied)
+    q, k, v, at, b = inputs_to_dev(inp)
+    inp.alpha = bf16_bits(lam)
+    lam_d = inputs_to_dev(inp)[3]
+    s0 = state_to_dev(inp.S0)
+    o1, s1 = kda.sfda_chunk_fwd(q, k, v, lam_d, b, initial_state=s0)
+    o2, s2 = kda.chunk_fwd(q, k, v, at, b, initial_state=s0, path="twopass")
+    torch.cuda.synchronize()
+    f = lambda x: x.float().cpu().numpy().transpose(0, 2, 1, 3).reshape(6, -1)
+    assert rel_err_slices(f(o1), f(o2), 6) < 1e-3
+    assert rel_err_slices(s1.cpu().numpy().reshape(6, -1), s2.cpu().numpy().reshape(6, -1), 6) < 1e-3
+
+
+def test_sfda_full_prefill_8k_sampled():
+    w = make_workload("sfda_prefill_8k")
+    rng = np.random.default_rng(6)
+    BH = w.meta["B"] * w.meta["H"]
+    heads = sorted(set(rng.choice(BH, size=5, replace=False).tolist()) | {0, BH - 1})
+    _check(w, w.S0, heads=heads, label="8k")
+
+
+def test_sfda_varlen_packed_batch():
+    """Sequences of 1, 64, 70, 0 and 200 tokens packed in one call: each matches the
+    oracle run from its own start state."""
+    import gated_delta_rule_78_amd as kda
+    import torch
+    lens = [1, 64, 70, 0, 200]
+    T = sum(lens)
+    inp = make(1, T, 2, 128, 128, "bf16", "sfda", False, seed=69)
+    N = len(lens)
+    rng = np.random.default_rng(69)
+    S0 = (0.02 * rng.standard_normal((N, 2, 128, 128))).astype(np.float32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    q, k, v, lam, b = inputs_to_dev(inp)
+    o, sT = kda.chunk_fwd_varlen(q, k, v, lam, b, torch.from_numpy(cu).cuda(),
+                                 initial_state=torch.from_numpy(S0).cuda(), sfda=True)
+    torch.cuda.synchronize()
+    o, sT = o.float().cpu().numpy(), sT.cpu().numpy()
+    for n in range(N):
+        a0, a1 = cu[n], cu[n + 1]
+        sl = lambda x: x[:, a0:a1]
+        print(f"sfda varlen seq {n} len {a1 - a0}", flush=True)
+        o_ref, s_ref = oracle.fwd_sfda(sl(inp.q), sl(inp.k), sl(inp.v), sl(inp.alpha), sl(inp.beta),
+                                       S0=S0[n], col_block=16)
+        if a1 > a0:
+            assert rel_err_slices(heads_of(o[:, a0:a1], [0, 1], 2), o_ref, 2) <= TOL["bf16"]
+        assert rel_err_slices(sT[n], s_ref, 2) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dk,dv,dtype", [(128, 128, "bf16"), (64, 128, "bf16"), (128, 64, "f32"), (64, 64, "f32")])
+def test_sfda_decode_steps(dk, dv, dtype):
+    import gated_delta_rule_78_amd as kda
+    import torch
+    B, H, steps = 3, 2, 6
+    inp = make(B, 1, H, dk, dv, dtype, "sfda", False, seed=71 + dk + dv, lead=steps)
+    q, k, v, lam, b = inputs_to_dev(inp)
+    S = state_to_dev(inp.S0)
+    ref = inp.S0.reshape(B * H, dk, dv).astype(np.float64).copy()
+    for t in range(steps):
+        print(f"sfda decode dk={dk} dv={dv} {dtype} step {t}", flush=True)
+        o = kda.sfda_decode_step(q[t], k[t], v[t], lam[t], b[t], S)
+        o_ref = oracle.decode_sfda(inp.q[t], inp.k[t], inp.v[t], inp.alpha[t], inp.beta[t], ref)
+        assert rel_err_slices(o.float().cpu().numpy().reshape(B * H, dv), o_ref, B * H) <= TOL[dtype]
+    torch.cuda.synchronize()
+    assert rel_err_slices(S.cpu().numpy().reshape(B * H, dk, dv), ref, B * H) <= 1e-5
+
+
+def test_sfda_decode_matches_chunk_forward_and_multi_token():
+    """40 single decode steps, one 40-token decode call and the chunk forward agree."""
+    import gated_delta_rule_78_amd as kda
+    import torch
+    inp = make(2, 40, 3, 128, 128, "bf16", "sfda", False, seed=73)
+    q, k, v, lam, b = inputs_to_dev(inp)
+    s0 = state_to_dev(inp.S0)
+    o, sT = kda.sfda_chunk_fwd(q, k, v, lam, b, initial_state=s0)
+    S = s0.clone()
+    outs = [kda.sfda_decode_step(*(x[:, t].contiguous() for x in (q, k, v, lam, b)), S) for t in range(40)]
+    od = torch.stack(outs, dim=1)
+    S2 = s0.clone()
+    om = kda.sfda_decode_tokens(q, k, v, lam, b, S2)
+    torch.cuda.synchronize()
+    f = lambda x: x.float().cpu().numpy().transpose(0, 2, 1, 3).reshape(6, -1)
+    assert rel_err_slices(f(od), f(o), 6) <= TOL["bf16"]
+    assert rel_err_slices(S.cpu().numpy().reshape(6, -1), sT.cpu().numpy().reshape(6, -1), 6) <= TOL["bf16"]
+    assert rel_err_slices(f(om), f(od), 6) <= 1e-5
+    assert rel_err_slices(S2.cpu().numpy().reshape(6, -1), S.cpu().numpy().reshape(6, -1), 6) <= 1e-5
