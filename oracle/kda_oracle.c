@@ -444,3 +444,169 @@ int kda_oracle_decode_gdn2(int B, int H, int dk, int dv, int dtype,
     }
     return err ? -1 : 0;
 }
+
+/*
+ * Backward of the KDA / CKDA forward: the gradients of
+ *   L = sum_t <dO_t, o_t> + <dS_T, S_T>
+ * with respect to q, k, v, alpha, beta and S_0, by reverse-mode differentiation of the
+ * token recurrence above (the training use of the chunked forward on the GDN-2 page,
+ * section 3; the pages print no backward formulas, so this is the plain adjoint of the
+ * literal step order).  Per token, with S_prev = S_{t-1} and G the gradient with respect
+ * to S_t:
+ *   forward   S' = Diag(alpha) S_prev;  u = S'^T k;  delta = v - u;  S_t = S' + beta k delta^T
+ *   G        += q dO_t^T                      (o_t = S_t^T q)
+ *   dq_t      = S_t dO_t
+ *   ddelta    = beta G^T k;   dv_t = ddelta;   dbeta_t = k^T G delta
+ *   dk_t      = beta G delta - S' ddelta
+ *   dS'       = G - k ddelta^T
+ *   dalpha_t  = rowsum(dS' o S_prev)
+ *   G         = Diag(alpha) dS'               (now the gradient with respect to S_{t-1})
+ * and dS_0 = G after the first token.  The states S_{t-1} are recomputed one 64-token
+ * block at a time from checkpoints taken every 64 tokens of a forward sweep.
+ *
+ *   dO    : [n_sel, T, dv] fp64;  dST : [n_sel, dk, dv] fp64 or NULL (zero)
+ *   dq, dk_out, dalpha : [n_sel, T, dk] fp64;  dv_out : [n_sel, T, dv];  dbeta : [n_sel, T]
+ *   dS0   : [n_sel, dk, dv] fp64 or NULL
+ * Other arguments as kda_oracle_fwd.  Parallel over heads.
+ */
+int kda_oracle_bwd(int B, int T, int H, int dk, int dv, int dtype,
+                   const void* q, const void* k, const void* v,
+                   const void* alpha, const void* beta, const double* S0,
+                   const double* dO, const double* dST,
+                   double* dq, double* dk_out, double* dv_out, double* dalpha, double* dbeta,
+                   double* dS0, const int* sel, int n_sel, int nthreads) {
+    if (B < 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0 || !dO) return -1;
+    if (!dq || !dk_out || !dv_out || !dalpha || !dbeta) return -1;
+    if (dtype < ORC_BF16 || dtype > ORC_F64) return -1;
+    if (!sel) n_sel = B * H;
+    if (n_sel < 0) return -1;
+    const int BLK = 64;
+    const int nblk = (T + BLK - 1) / BLK;
+    const size_t SS = (size_t)dk * dv;
+    int err = 0;
+
+#pragma omp parallel num_threads(pick_threads(nthreads))
+    {
+        double* ck = (double*)malloc(sizeof(double) * SS * (size_t)(nblk > 0 ? nblk : 1));
+        double* hist = (double*)malloc(sizeof(double) * SS * (size_t)(BLK + 1));
+        double* G = (double*)malloc(sizeof(double) * SS);
+        double* Sp = (double*)malloc(sizeof(double) * SS);   /* S' of the current token */
+        double* buf = (double*)malloc(sizeof(double) * (size_t)(3 * dk + 5 * dv));
+        if (!ck || !hist || !G || !Sp || !buf) {
+#pragma omp atomic write
+            err = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int s = 0; s < n_sel; ++s) {
+            if (!ck || !hist || !G || !Sp || !buf) continue;
+            const int bh = sel ? sel[s] : s;
+            const int b = bh / H, h = bh % H;
+            double *qq = buf, *kk = buf + dk, *aa = buf + 2 * dk;
+            double *vv = buf + 3 * dk, *u = vv + dv, *del = u + dv, *dd = del + dv, *tmp = dd + dv;
+            /* forward sweep: checkpoint S at the start of every 64-token block */
+            double* S = hist;  /* scratch for the sweep */
+            for (size_t x = 0; x < SS; ++x) S[x] = S0 ? S0[(size_t)s * SS + x] : 0.0;
+            for (int t = 0; t < T; ++t) {
+                if (t % BLK == 0) memcpy(ck + (size_t)(t / BLK) * SS, S, sizeof(double) * SS);
+                const size_t row = ((size_t)b * T + t) * H + h;
+                for (int i = 0; i < dk; ++i) {
+                    qq[i] = load_elem(q, dtype, row * dk + i);
+                    kk[i] = load_elem(k, dtype, row * dk + i);
+                    aa[i] = load_elem(alpha, dtype, row * dk + i);
+                }
+                for (int j = 0; j < dv; ++j) vv[j] = load_elem(v, dtype, row * dv + j);
+                kda_token(S, dk, dv, 0, dv, qq, kk, vv, aa, load_elem(beta, dtype, row), u, NULL, 0);
+            }
+            /* backward sweep */
+            for (size_t x = 0; x < SS; ++x) G[x] = dST ? dST[(size_t)s * SS + x] : 0.0;
+            for (int bk = nblk - 1; bk >= 0; --bk) {
+                const int t0 = bk * BLK, t1 = t0 + BLK < T ? t0 + BLK : T;
+                /* hist[x] = S_{t0 + x - 1}: the states before each token of the block */
+                memcpy(hist, ck + (size_t)bk * SS, sizeof(double) * SS);
+                for (int t = t0; t < t1 - 1; ++t) {
+                    const size_t row = ((size_t)b * T + t) * H + h;
+                    for (int i = 0; i < dk; ++i) {
+                        qq[i] = load_elem(q, dtype, row * dk + i);
+                        kk[i] = load_elem(k, dtype, row * dk + i);
+                        aa[i] = load_elem(alpha, dtype, row * dk + i);
+                    }
+                    for (int j = 0; j < dv; ++j) vv[j] = load_elem(v, dtype, row * dv + j);
+                    double* nx = hist + (size_t)(t - t0 + 1) * SS;
+                    memcpy(nx, hist + (size_t)(t - t0) * SS, sizeof(double) * SS);
+                    kda_token(nx, dk, dv, 0, dv, qq, kk, vv, aa, load_elem(beta, dtype, row), u, NULL, 0);
+                }
+                for (int t = t1 - 1; t >= t0; --t) {
+                    const size_t row = ((size_t)b * T + t) * H + h;
+                    const double* Sprev = hist + (size_t)(t - t0) * SS;
+                    for (int i = 0; i < dk; ++i) {
+                        qq[i] = load_elem(q, dtype, row * dk + i);
+                        kk[i] = load_elem(k, dtype, row * dk + i);
+                        aa[i] = load_elem(alpha, dtype, row * dk + i);
+                    }
+                    for (int j = 0; j < dv; ++j) vv[j] = load_elem(v, dtype, row * dv + j);
+                    const double bt = load_elem(beta, dtype, row);
+                    const double* dOt = dO + ((size_t)s * T + t) * dv;
+                    /* recompute S' = Diag(alpha) S_prev, u = S'^T k, delta = v - u */
+                    for (int i = 0; i < dk; ++i)
+                        for (int j = 0; j < dv; ++j) Sp[(size_t)i * dv + j] = aa[i] * Sprev[(size_t)i * dv + j];
+                    for (int j = 0; j < dv; ++j) u[j] = 0.0;
+                    for (int i = 0; i < dk; ++i)
+                        for (int j = 0; j < dv; ++j) u[j] += kk[i] * Sp[(size_t)i * dv + j];
+                    for (int j = 0; j < dv; ++j) del[j] = vv[j] - u[j];
+                    /* readout: G += q dO^T ; dq = S_t dO with S_t = S' + beta k delta^T */
+                    for (int i = 0; i < dk; ++i)
+                        for (int j = 0; j < dv; ++j) G[(size_t)i * dv + j] += qq[i] * dOt[j];
+                    double* dqt = dq + ((size_t)s * T + t) * dk;
+                    for (int i = 0; i < dk; ++i) {
+                        double a = 0.0;
+                        for (int j = 0; j < dv; ++j)
+                            a += (Sp[(size_t)i * dv + j] + bt * kk[i] * del[j]) * dOt[j];
+                        dqt[i] = a;
+                    }
+                    /* ddelta = beta G^T k ; dv = ddelta ; dbeta = k^T G delta */
+                    for (int j = 0; j < dv; ++j) dd[j] = 0.0;
+                    for (int i = 0; i < dk; ++i)
+                        for (int j = 0; j < dv; ++j) dd[j] += kk[i] * G[(size_t)i * dv + j];
+                    double db = 0.0;
+                    for (int j = 0; j < dv; ++j) {
+                        db += dd[j] * del[j];   /* (G^T k) . delta = k^T G delta */
+                        dd[j] *= bt;
+                    }
+                    dbeta[(size_t)s * T + t] = db;
+                    double* dvt = dv_out + ((size_t)s * T + t) * dv;
+                    for (int j = 0; j < dv; ++j) dvt[j] = dd[j];
+                    /* dk = beta G delta - S' ddelta */
+                    double* dkt = dk_out + ((size_t)s * T + t) * dk;
+                    for (int i = 0; i < dk; ++i) {
+                        double a = 0.0, c = 0.0;
+                        for (int j = 0; j < dv; ++j) {
+                            a += G[(size_t)i * dv + j] * del[j];
+                            c += Sp[(size_t)i * dv + j] * dd[j];
+                        }
+                        dkt[i] = bt * a - c;
+                    }
+                    /* dS' = G - k ddelta^T ; dalpha = rowsum(dS' o S_prev) ; G <- Diag(alpha) dS' */
+                    double* dat = dalpha + ((size_t)s * T + t) * dk;
+                    for (int i = 0; i < dk; ++i) {
+                        double a = 0.0;
+                        for (int j = 0; j < dv; ++j) {
+                            const double g = G[(size_t)i * dv + j] - kk[i] * dd[j];
+                            a += g * Sprev[(size_t)i * dv + j];
+                            G[(size_t)i * dv + j] = aa[i] * g;
+                        }
+                        dat[i] = a;
+                    }
+                    (void)tmp;
+                }
+            }
+            if (dS0)
+                for (size_t x = 0; x < SS; ++x) dS0[(size_t)s * SS + x] = G[x];
+        }
+        free(ck);
+        free(hist);
+        free(G);
+        free(Sp);
+        free(buf);
+    }
+    return err ? -1 : 0;
+}

@@ -1,0 +1,124 @@
+"""Pins of the oracle's backward (CPU).
+
+The gradients are those of L = sum_t <dO_t, o_t> + <dS_T, S_T> through the forward
+recurrence.  The pins use the forward oracle (itself pinned in test_oracle.py), never the
+backward's own code:
+
+* L is affine in each single entry of q, v, alpha, beta and S0 (each enters every
+  state and output at most linearly), so the secant L(x + s e) - L(x) equals s times
+  the gradient exactly, for any step s -- including at an exact zero gate, where a
+  division-based log-derivative would be undefined;
+* k enters quadratically, so its gradient is pinned by central finite differences;
+* a one-token scalar case is checked against derivatives worked by hand.
+"""
+import numpy as np
+import pytest
+
+import oracle
+
+
+def _inputs(rng, B, T, H, dk, dv, zeros=0.1):
+    q = rng.standard_normal((B, T, H, dk))
+    k = rng.standard_normal((B, T, H, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, T, H, dv))
+    a = np.tanh(2 * rng.standard_normal((B, T, H, dk)))
+    m = rng.random(a.shape) < zeros
+    a[m] = rng.choice([-1.0, 0.0, 1.0], size=int(m.sum()))
+    b = rng.uniform(0.0, 2.0, (B, T, H))
+    S0 = rng.standard_normal((B * H, dk, dv))
+    dO = rng.standard_normal((B * H, T, dv))
+    dST = rng.standard_normal((B * H, dk, dv))
+    return dict(q=q, k=k, v=v, alpha=a, beta=b, S0=S0), dO, dST
+
+
+def _loss(x, dO, dST):
+    o, S = oracle.fwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"], S0=x["S0"])
+    return float((o * dO).sum() + (S * dST).sum())
+
+
+def _grads(x, dO, dST):
+    return oracle.bwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"], dO, S0=x["S0"], dST=dST)
+
+
+def _entry_grad(g, name, idx, H):
+    """Gradient entry for input `name` at input index idx (inputs are [B, T, H, d])."""
+    if name == "S0":
+        return g["dS0"][idx]
+    key = {"q": "dq", "k": "dk", "v": "dv", "alpha": "dalpha", "beta": "dbeta"}[name]
+    b, t, h = idx[:3]
+    return g[key][(b * H + h, t) + tuple(idx[3:])]
+
+
+@pytest.mark.parametrize("T", [5, 150])
+def test_bwd_exact_secants(T):
+    """Affine inputs: a secant of any step equals the gradient (zero gates included)."""
+    rng = np.random.default_rng(100 + T)
+    B, H, dk, dv = 2, 2, 4, 3
+    x, dO, dST = _inputs(rng, B, T, H, dk, dv)
+    x["alpha"][0, 1, 0, 2] = 0.0   # exact zero gates, two in one channel
+    x["alpha"][0, 3, 0, 2] = 0.0
+    g = _grads(x, dO, dST)
+    L0 = _loss(x, dO, dST)
+    checked_zero = 0
+    for name in ("q", "v", "alpha", "beta", "S0"):
+        for _ in range(6):
+            idx = tuple(int(rng.integers(0, n)) for n in x[name].shape)
+            if name == "alpha" and checked_zero < 2:  # make sure exact zero gates are covered
+                z = np.argwhere(x["alpha"] == 0.0)
+                if len(z):
+                    idx = tuple(int(c) for c in z[int(rng.integers(0, len(z)))])
+                    checked_zero += 1
+            step = 0.75
+            y = {kk: vv.copy() for kk, vv in x.items()}
+            y[name][idx] += step
+            sec = (_loss(y, dO, dST) - L0) / step
+            ref = _entry_grad(g, name, idx, H)
+            assert abs(sec - ref) <= 1e-9 * max(1.0, abs(ref)), (name, idx, sec, ref)
+    assert checked_zero > 0
+
+
+def test_bwd_key_central_differences():
+    rng = np.random.default_rng(7)
+    B, T, H, dk, dv = 1, 70, 2, 4, 3
+    x, dO, dST = _inputs(rng, B, T, H, dk, dv)
+    g = _grads(x, dO, dST)
+    h = 1e-5
+    for _ in range(12):
+        idx = tuple(int(rng.integers(0, n)) for n in x["k"].shape)
+        yp = {kk: vv.copy() for kk, vv in x.items()}
+        ym = {kk: vv.copy() for kk, vv in x.items()}
+        yp["k"][idx] += h
+        ym["k"][idx] -= h
+        fd = (_loss(yp, dO, dST) - _loss(ym, dO, dST)) / (2 * h)
+        ref = _entry_grad(g, "k", idx, H)
+        assert abs(fd - ref) <= 1e-6 * max(1.0, abs(ref)), (idx, fd, ref)
+
+
+def test_bwd_scalar_token_by_hand():
+    """d_k = d_v = 1, one token, L = o = q ((1 - beta k^2) alpha S0 + beta k v):
+       dq = S1, dv = q beta k, dbeta = q (k v - k^2 alpha S0), dk = q beta (v - 2 k alpha S0),
+       dalpha = q (1 - beta k^2) S0, dS0 = q (1 - beta k^2) alpha."""
+    q, k, v, a, b, s0 = 1.5, 0.5, 2.0, 0.8, 1.2, -0.4
+    f = lambda z: np.array(z, dtype=np.float64).reshape(1, 1, 1, 1)
+    g = oracle.bwd(f(q), f(k), f(v), f(a), np.array([[[b]]]), np.ones((1, 1, 1)), S0=np.array([[[s0]]]))
+    S1 = (1 - b * k * k) * a * s0 + b * k * v
+    want = {"dq": S1, "dv": q * b * k, "dbeta": q * (k * v - k * k * a * s0), "dk": q * b * (v - 2 * k * a * s0),
+            "dalpha": q * (1 - b * k * k) * s0, "dS0": q * (1 - b * k * k) * a}
+    for key, val in want.items():
+        np.testing.assert_allclose(g[key].ravel()[0], val, rtol=0, atol=1e-15)
+
+
+def test_bwd_head_selection_and_no_final_gradient():
+    rng = np.random.default_rng(9)
+    B, T, H, dk, dv = 2, 20, 3, 3, 2
+    x, dO, _ = _inputs(rng, B, T, H, dk, dv)
+    g = oracle.bwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"], dO, S0=x["S0"])
+    sel = [5, 0, 3]
+    gs = oracle.bwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"], dO[sel], S0=x["S0"][sel], heads=sel)
+    for key in g:
+        np.testing.assert_array_equal(gs[key], g[key][sel])
+    # dST = None is the zero upstream gradient
+    g0 = oracle.bwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"], dO, S0=x["S0"], dST=np.zeros((B * H, dk, dv)))
+    for key in g:
+        np.testing.assert_array_equal(g0[key], g[key])

@@ -225,3 +225,56 @@ def test_sfda_mutant_is_caught(name, src_text, monkeypatch, tmp_path):
     assert src_text.count(old) == 1, f"mutation anchor for {name} not unique"
     lib = _build_variant(src_text.replace(old, new), str(tmp_path), name)
     assert _caught_sfda(lib, monkeypatch), f"mutant {name} passed every SFDA pin"
+
+
+# ---- the backward (reverse-mode) code: plausible mistakes, each must fail a backward pin
+import test_oracle_bwd as bpins  # noqa: E402
+
+MUTANTS_BWD = {
+    "bwd_dk_sign_of_read_term": ("dkt[i] = bt * a - c;", "dkt[i] = bt * a + c;"),
+    "bwd_dk_read_term_dropped": ("dkt[i] = bt * a - c;", "dkt[i] = bt * a;"),
+    "bwd_erase_adjoint_dropped": ("const double g = G[(size_t)i * dv + j] - kk[i] * dd[j];",
+                                  "const double g = G[(size_t)i * dv + j];"),
+    "bwd_decay_adjoint_dropped": ("G[(size_t)i * dv + j] = aa[i] * g;", "G[(size_t)i * dv + j] = g;"),
+    "bwd_dalpha_from_decayed_state": ("a += g * Sprev[(size_t)i * dv + j];", "a += g * Sp[(size_t)i * dv + j];"),
+    "bwd_dq_before_update": ("a += (Sp[(size_t)i * dv + j] + bt * kk[i] * del[j]) * dOt[j];",
+                             "a += Sp[(size_t)i * dv + j] * dOt[j];"),
+    "bwd_dbeta_with_v": ("db += dd[j] * del[j];", "db += dd[j] * vv[j];"),
+    "bwd_dv_without_beta": ("        dd[j] *= bt;\n", ""),
+    "bwd_stale_block_history": ("for (int t = t0; t < t1 - 1; ++t) {", "for (int t = t0; t < t1 - 2; ++t) {"),
+}
+
+PIN_TESTS_BWD = [
+    ("secants_short", lambda: bpins.test_bwd_exact_secants(5)),
+    ("secants_blocks", lambda: bpins.test_bwd_exact_secants(150)),
+    ("key_fd", lambda: bpins.test_bwd_key_central_differences()),
+    ("scalar_hand", lambda: bpins.test_bwd_scalar_token_by_hand()),
+]
+
+
+def _caught_bwd(lib, monkeypatch):
+    """The forward stays the clean library (the pins measure the backward against it)."""
+    failed = []
+    with monkeypatch.context() as m:
+        real = oracle.bwd
+        m.setattr(oracle, "bwd", lambda *a, **kw: real(*a, lib=lib, **kw))
+        for name, fn in PIN_TESTS_BWD:
+            try:
+                with np.errstate(all="ignore"):
+                    fn()
+            except AssertionError:
+                failed.append(name)
+    return failed
+
+
+def test_unmodified_source_passes_bwd_pins(src_text, monkeypatch, tmp_path):
+    lib = _build_variant(src_text, str(tmp_path), "clean_bwd")
+    assert _caught_bwd(lib, monkeypatch) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS_BWD))
+def test_bwd_mutant_is_caught(name, src_text, monkeypatch, tmp_path):
+    old, new = MUTANTS_BWD[name]
+    assert src_text.count(old) == 1, f"mutation anchor for {name} not unique"
+    lib = _build_variant(src_text.replace(old, new), str(tmp_path), name)
+    assert _caught_bwd(lib, monkeypatch), f"mutant {name} passed every backward pin"
