@@ -210,3 +210,143 @@ def chunk_forward(q, k, v, a, beta, S0=None, C=64, emulate=None, debug=None):
     if emulate == "bf16":
         o = _bf16(o)
     return o, S
+
+
+# ---------------------------------------------------------------------------
+# Backward of the chunk algebra (fp64 specification, test infrastructure).
+#
+# Gradients of L = sum <dO, O> + <dS_T, S_T>.  Per chunk, in reverse order, with the
+# chunk's start state S and the gradient dS' of its end state:
+#   dDelta = K^ dS' + A^T dO                 (K^ = K o rho, A lower incl. diagonal)
+#   dS     = diag(gamma_L) dS' + Q~^T dO - W^T dDelta        (carried to the previous chunk)
+#   dQ~ = dO S^T,  dA = (dO Delta^T) o lower,  dK^ = Delta dS'^T,  dgamma_L = rowsum(dS' o S)
+#   dW = -dDelta S^T,  dV = M~^T dDelta,  dM~ = (dDelta V^T + dW K~^T) o lower,  dK~ = M~^T dW
+#   dbeta_j = sum_i dM~_ij M_ij,  dM = dM~ diag(beta),  dT = -(M^T dM M^T) o strict lower
+#   dbeta_i += sum_j dT_ij D_ij,  dD = diag(beta) dT          (T = diag(beta) D)
+# and through the decayed products A_ij = sum_c q_ic k_jc r_ijc, D_ij = sum_c k_ic k_jc r_ijc:
+#   Zq_i = sum_{j<=i} dA_ij k_j o r_ij,   Zr_i = sum_{j<i} dD_ij k_j o r_ij,
+#   Zc_j = sum_{i>=j} dA_ij q_i o r_ij + sum_{i>j} dD_ij k_i o r_ij,
+#   dq = dQ~ o gamma + Zq,   dk = dK~ o gamma + dK^ o rho + Zr + Zc.
+# Gate gradient, per channel: with
+#   dG_i = dQ~_i Q~_i + dK~_i K~_i + q_i Zq_i + k_i Zr_i - k_i Zc_i - dK^_i K^_i
+#          (+ sum_j dK^_j K^_j + dgamma_L gamma_L at i = C-1),
+# the reverse sum P_m = sum_{i>=m} dG_i equals alpha_m dalpha_m (the terms with both ends
+# at or after m cancel), so dalpha_m = P_m / alpha_m for a nonzero gate.  For a zero gate
+# P_m = 0 and the derivative is the product with alpha_m left out:
+#   dalpha_m = sum_{i>=m} r_(i,m) [sum_{j<m} w_ij r_(m-1,j) + a_i gamma_(m-1)]
+#              + r_(L,m) [sum_{j<m} b_j r_(m-1,j) + dgamma_L gamma_(m-1)]
+# with w_ij = dA_ij q_i k_j + dD_ij k_i k_j, a_i = dQ~_i q_i + dK~_i k_i, b_j = dK^_j k_j and
+# r_(x,y) = prod_{y<l<=x} alpha_l (the products exclusive of m on both sides).
+# ---------------------------------------------------------------------------
+
+def _ranges(a):
+    """r[i, j] = prod_{j<l<=i} a_l for i >= j (1 on the diagonal, 0 above), [C, C, dk]."""
+    C, dk = a.shape
+    r = np.zeros((C, C, dk))
+    for j in range(C):
+        run = np.ones(dk)
+        r[j, j] = 1.0
+        for i in range(j + 1, C):
+            run = run * a[i]
+            r[i, j] = run
+    return r
+
+
+def _chunk_fwd_parts(q, k, v, a, beta, S):
+    C = q.shape[0]
+    r = _ranges(a)
+    gam = np.cumprod(a, axis=0)                       # gamma_i = prod_{l<=i}
+    rho = r[C - 1]                                     # rho_j = prod_{j<l<=C-1}
+    gL = gam[C - 1]
+    A = np.einsum("ic,jc,ijc->ij", q, k, r) * np.tril(np.ones((C, C)))
+    D = np.einsum("ic,jc,ijc->ij", k, k, r) * np.tril(np.ones((C, C)), -1)
+    M = np.linalg.inv(np.eye(C) + beta[:, None] * D)
+    Mt = M * beta[None, :]
+    Kg, Qg, Kr = k * gam, q * gam, k * rho
+    U, W = Mt @ v, Mt @ Kg
+    Dl = U - W @ S
+    O = Qg @ S + A @ Dl
+    Sn = gL[:, None] * S + Kr.T @ Dl
+    return dict(r=r, gam=gam, rho=rho, gL=gL, A=A, D=D, M=M, Mt=Mt, Kg=Kg, Qg=Qg, Kr=Kr, W=W, Dl=Dl,
+                O=O, S=S, Sn=Sn)
+
+
+def chunk_backward(q, k, v, a, beta, dO, S0=None, dST=None, C=64, check_zero_formula=False):
+    """Gradients for one head through the chunk algebra (fp64).  q, k, a [T, dk]; v, dO
+    [T, dv]; beta [T]; S0, dST [dk, dv] or None.  Returns dict dq, dk, dv, dalpha, dbeta,
+    dS0.  check_zero_formula: also evaluate the exclusive-product formula for every gate
+    (zero or not) and assert it equals P_m / alpha_m where alpha_m != 0."""
+    T, dk = q.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if S0 is None else np.asarray(S0, np.float64).copy()
+    parts = []
+    for c0 in range(0, T, C):
+        n = min(C, T - c0)
+        pad = lambda x, fill, w: np.concatenate([x[c0:c0 + n], np.full((C - n,) + x.shape[1:], fill)])[:C]
+        qc, kc, vc = pad(q, 0.0, dk), pad(k, 0.0, dk), pad(v, 0.0, dv)
+        ac, bc, dOc = pad(a, 1.0, dk), pad(beta, 0.0, 1), pad(dO, 0.0, dv)
+        p = _chunk_fwd_parts(qc, kc, vc, ac, bc, S)
+        p.update(q=qc, k=kc, v=vc, a=ac, beta=bc, dO=dOc, c0=c0, n=n)
+        parts.append(p)
+        S = p["Sn"]
+    out = {x: np.zeros((T, dk)) for x in ("dq", "dk", "dalpha")}
+    out["dv"] = np.zeros((T, dv))
+    out["dbeta"] = np.zeros(T)
+    dSn = np.zeros((dk, dv)) if dST is None else np.asarray(dST, np.float64).copy()
+    low, slow = np.tril(np.ones((C, C))), np.tril(np.ones((C, C)), -1)
+    for p in reversed(parts):
+        S, dO_, qc, kc, vc, ac, bc = p["S"], p["dO"], p["q"], p["k"], p["v"], p["a"], p["beta"]
+        r, gam, rho, gL = p["r"], p["gam"], p["rho"], p["gL"]
+        dDl = p["Kr"] @ dSn + p["A"].T @ dO_
+        dS = gL[:, None] * dSn + p["Qg"].T @ dO_ - p["W"].T @ dDl
+        dQg = dO_ @ S.T
+        dA = (dO_ @ p["Dl"].T) * low
+        dKr = p["Dl"] @ dSn.T
+        dgL = (dSn * S).sum(axis=1)
+        dW = -dDl @ S.T
+        dV = p["Mt"].T @ dDl
+        dMt = (dDl @ vc.T + dW @ p["Kg"].T) * low
+        dKg = p["Mt"].T @ dW
+        dbeta = (dMt * p["M"]).sum(axis=0)
+        dM = dMt * bc[None, :]
+        dT = -(p["M"].T @ dM @ p["M"].T) * slow
+        dbeta = dbeta + (dT * p["D"]).sum(axis=1)
+        dD = bc[:, None] * dT
+        Zq = np.einsum("ij,jc,ijc->ic", dA, kc, r)
+        Zr = np.einsum("ij,jc,ijc->ic", dD, kc, r)
+        Zc = np.einsum("ij,ic,ijc->jc", dA, qc, r) + np.einsum("ij,ic,ijc->jc", dD, kc, r)
+        dq = dQg * gam + Zq
+        dk_ = dKg * gam + dKr * rho + Zr + Zc
+        dG = dQg * p["Qg"] + dKg * p["Kg"] + qc * Zq + kc * Zr - kc * Zc - dKr * p["Kr"]
+        dG[C - 1] += (dKr * p["Kr"]).sum(axis=0) + dgL * gL
+        P = np.cumsum(dG[::-1], axis=0)[::-1]            # P_m = sum_{i >= m} dG_i
+        nz = ac != 0.0
+        dal = np.where(nz, P / np.where(nz, ac, 1.0), 0.0)
+        if check_zero_formula or (~nz).any():
+            w = np.einsum("ij,ic,jc->ijc", dA, qc, kc) + np.einsum("ij,ic,jc->ijc", dD, kc, kc)
+            av = dQg * qc + dKg * kc
+            bv = dKr * kc
+            for m in range(C):
+                for c in range(dk):
+                    if nz[m, c] and not check_zero_formula:
+                        continue
+                    gm1 = np.prod(ac[:m, c])                      # gamma_(m-1)
+                    left = np.array([np.prod(ac[j + 1:m, c]) for j in range(m)])   # r_(m-1, j)
+                    tot = 0.0
+                    for i in range(m, C):
+                        right = np.prod(ac[m + 1:i + 1, c])                      # r_(i, m)
+                        tot += right * ((w[i, :m, c] * left).sum() + av[i, c] * gm1)
+                    tot += np.prod(ac[m + 1:, c]) * ((bv[:m, c] * left).sum() + dgL[c] * gm1)
+                    if nz[m, c]:
+                        assert abs(tot - dal[m, c]) <= 1e-9 * max(1.0, abs(tot)), (m, c, tot, dal[m, c])
+                    else:
+                        dal[m, c] = tot
+        n, c0 = p["n"], p["c0"]
+        out["dq"][c0:c0 + n] = dq[:n]
+        out["dk"][c0:c0 + n] = dk_[:n]
+        out["dv"][c0:c0 + n] = dV[:n]
+        out["dalpha"][c0:c0 + n] = dal[:n]
+        out["dbeta"][c0:c0 + n] = dbeta[:n]
+        dSn = dS
+    out["dS0"] = dSn
+    return out

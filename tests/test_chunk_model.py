@@ -71,3 +71,30 @@ def test_bf16_emulation_within_tolerance():
                               inp.S0[0, 0], emulate="bf16")
     assert np.abs(om - o[0]).max() / np.abs(o[0]).max() < 1e-2
     assert np.abs(Sm - S[0]).max() / np.abs(S[0]).max() < 1e-2
+
+
+@pytest.mark.parametrize("T,dk,dv,zero_frac,check", [(150, 6, 5, 0.1, True), (64, 4, 3, 0.3, True),
+                                                     (200, 8, 4, 0.0, False)])
+def test_chunk_backward_matches_oracle(T, dk, dv, zero_frac, check):
+    """The chunkwise backward (adjoint state pass, dv contractions, WY and inverse
+    adjoints, decayed-product gradients, reverse-summed gate gradient with the
+    exclusive-product form at zero gates) equals the oracle's reverse-mode gradients."""
+    import oracle
+    rng = np.random.default_rng(T + dk)
+    q = rng.standard_normal((T, dk))
+    k = rng.standard_normal((T, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    v = rng.standard_normal((T, dv))
+    a = np.tanh(2 * rng.standard_normal((T, dk)))
+    m = rng.random(a.shape) < zero_frac
+    a[m] = rng.choice([-1.0, 0.0, 1.0], size=int(m.sum()))
+    b = rng.uniform(0.0, 2.0, T)
+    S0 = rng.standard_normal((dk, dv))
+    dO = rng.standard_normal((T, dv))
+    dST = rng.standard_normal((dk, dv))
+    g = cm.chunk_backward(q, k, v, a, b, dO, S0, dST, C=64, check_zero_formula=check)
+    r = oracle.bwd(q[None, :, None], k[None, :, None], v[None, :, None], a[None, :, None], b[None, :, None],
+                   dO[None], S0=S0[None], dST=dST[None])
+    for key in ("dq", "dk", "dv", "dalpha", "dbeta", "dS0"):
+        y = r[key][0]
+        assert np.abs(g[key] - y).max() <= 1e-10 * max(1.0, np.abs(y).max()), key
