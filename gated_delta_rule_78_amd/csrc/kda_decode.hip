@@ -40,7 +40,7 @@ __global__ __launch_bounds__(512) void decode_kernel(const void* __restrict__ q,
   constexpr int RG = NT / TPR;     // row groups
   constexpr int RPT = DK / RG;     // rows per thread
   static_assert(RPT * RG == DK && TPR * 4 == DV, "tile split");
-  static_assert(!CPX || (TPR < 64 && RG % 2 == 0), "row pairs sit TPR lanes apart in one wave");
+  static_assert(!CPX || RPT % 2 == 0, "complex gates: a thread holds whole row pairs");
 
   __shared__ float s_q[DK], s_k[DK], s_a[DK], s_v[DV];
   __shared__ float s_e[G2 ? DK : 1];  // read-side key b o k (G2)
@@ -54,6 +54,9 @@ __global__ __launch_bounds__(512) void decode_kernel(const void* __restrict__ q,
   const size_t b = bh / H, h = bh % H;
   const int cq = tid % TPR;        // column quad
   const int rg = tid / TPR;        // row group
+  // the thread's i-th state row: rows rg + RG i; with complex gates, the row pairs
+  // (2p, 2p+1) for p = rg + RG (i / 2), so that both rows of a coordinate sit in one thread
+  auto row_of = [&](int i) { return CPX ? 2 * (rg + RG * (i >> 1)) + (i & 1) : rg + RG * i; };
 
   // the state streams through once per call: nontemporal loads and stores keep it from
   // displacing cached lines it will not reuse
@@ -61,7 +64,7 @@ __global__ __launch_bounds__(512) void decode_kernel(const void* __restrict__ q,
   float4 s[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const f32x4_t t = __builtin_nontemporal_load(&S[(size_t)(rg + RG * i) * TPR + cq]);
+    const f32x4_t t = __builtin_nontemporal_load(&S[(size_t)row_of(i) * TPR + cq]);
     s[i] = make_float4(t[0], t[1], t[2], t[3]);
   }
 
@@ -100,16 +103,17 @@ __global__ __launch_bounds__(512) void decode_kernel(const void* __restrict__ q,
     float u[4] = {0.f, 0.f, 0.f, 0.f}, p[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int r = rg + RG * i;
+      const int r = row_of(i);
       const float kk = G2 ? s_e[r] : s_k[r], qq = s_q[r];
       if constexpr (CPX) {
-        // the pair row r ^ 1 is held by lane ^ TPR (row group rg ^ 1, same columns):
+        // rows 2p (i even) and 2p+1 (i odd) of this thread: z <- lambda z with
         // row 2p <- Re s_2p - Im s_2p+1, row 2p+1 <- Im s_2p + Re s_2p+1
-        const float lr = s_a[r & ~1], li = (r & 1) ? s_a[r] : -s_a[r | 1];
-        const float px = __shfl_xor(s[i].x, TPR), py = __shfl_xor(s[i].y, TPR);
-        const float pz = __shfl_xor(s[i].z, TPR), pw = __shfl_xor(s[i].w, TPR);
-        s[i].x = lr * s[i].x + li * px; s[i].y = lr * s[i].y + li * py;
-        s[i].z = lr * s[i].z + li * pz; s[i].w = lr * s[i].w + li * pw;
+        if ((i & 1) == 0) {
+          const float lr = s_a[r], li = s_a[r + 1];
+          const float4 x = s[i], y = s[i + 1];
+          s[i] = make_float4(lr * x.x - li * y.x, lr * x.y - li * y.y, lr * x.z - li * y.z, lr * x.w - li * y.w);
+          s[i + 1] = make_float4(li * x.x + lr * y.x, li * x.y + lr * y.y, li * x.z + lr * y.z, li * x.w + lr * y.w);
+        }
       } else {
         const float a = s_a[r];
         s[i].x *= a; s[i].y *= a; s[i].z *= a; s[i].w *= a;
@@ -151,7 +155,7 @@ __global__ __launch_bounds__(512) void decode_kernel(const void* __restrict__ q,
     }
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const float kk = s_k[rg + RG * i];
+      const float kk = s_k[row_of(i)];
       s[i].x += kk * d[0]; s[i].y += kk * d[1]; s[i].z += kk * d[2]; s[i].w += kk * d[3];
     }
     if (rg == 0) {
@@ -162,7 +166,7 @@ __global__ __launch_bounds__(512) void decode_kernel(const void* __restrict__ q,
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const f32x4_t t = {s[i].x, s[i].y, s[i].z, s[i].w};
-    __builtin_nontemporal_store(t, &S[(size_t)(rg + RG * i) * TPR + cq]);
+    __builtin_nontemporal_store(t, &S[(size_t)row_of(i) * TPR + cq]);
   }
 }
 

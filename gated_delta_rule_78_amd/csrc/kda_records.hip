@@ -308,25 +308,19 @@ __global__ __launch_bounds__(256, 2) void chunk_records_kernel(
     const int icp = tid % GRP;
 
     // ---------------- item registers, fp32 (rows past the end: q = k = 0, alpha = 1)
-    // (rows past the end: gate 1, i.e. (1, 1) for real gates, 1 + 0i for complex ones)
+    // Rows past the end keep the clamped copies of the last row's q and k: their beta is 0,
+    // so their rows of T and of M~ are zero, they add nothing to any state, and their
+    // outputs are never stored.  Only their gate must be the identity (it enters gamma_last
+    // and rho): (1, 1) for real gates, 1 + 0i for complex ones.
     float qf[SUB][2], kf[SUB][2];
     G al[SUB];
     constexpr uint32_t kOne = CPX ? 0x00003F80u : R::kOneWord;
-    if (t0 + C <= gm.len) {  // a whole chunk (wave-uniform): no row is masked
+    const int lim = gm.len - t0 - SUB * iI;  // rows of this item that exist
 #pragma unroll
-      for (int m = 0; m < SUB; ++m) {
-        R::unpack(pq[m], qf[m][0], qf[m][1]);
-        R::unpack(pk[m], kf[m][0], kf[m][1]);
-        R::unpack(pa[m], al[m].x, al[m].y);
-      }
-    } else {
-#pragma unroll
-      for (int m = 0; m < SUB; ++m) {
-        const bool ok = t0 + SUB * iI + m < gm.len;
-        R::unpack(ok ? pq[m] : 0u, qf[m][0], qf[m][1]);
-        R::unpack(ok ? pk[m] : 0u, kf[m][0], kf[m][1]);
-        R::unpack(ok ? pa[m] : kOne, al[m].x, al[m].y);
-      }
+    for (int m = 0; m < SUB; ++m) {
+      R::unpack(pq[m], qf[m][0], qf[m][1]);
+      R::unpack(pk[m], kf[m][0], kf[m][1]);
+      R::unpack(m < lim ? pa[m] : kOne, al[m].x, al[m].y);
     }
     // the key as the erase side reads it: k (KDA), b o k (Gated DeltaNet-2; the erase gate
     // stays packed, the product is formed at each use)
