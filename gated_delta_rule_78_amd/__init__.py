@@ -16,6 +16,7 @@ import os
 
 __all__ = ["chunk_fwd", "chunk_records", "chunk_apply_records", "chunk_fwd_debug", "decode_step",
            "gdn2_chunk_fwd", "gdn2_decode_step", "decode_tokens", "gdn2_decode_tokens", "chunk_fwd_varlen",
+           "sfda_chunk_fwd", "sfda_decode_step", "sfda_decode_tokens", "chunk_bwd", "bwd_workspace_size",
            "workspace_size", "pick_path", "lib", "version", "status_string",
            "LIB_PATH", "KdaError", "Shape", "BF16", "F32"]
 
@@ -83,6 +84,10 @@ def lib() -> ctypes.CDLL:
         L.kda_sfda_decode_step.restype = ctypes.c_int
         L.kda_sfda_decode_tokens.argtypes = [SP, P, P, P, P, P, P, P, P]
         L.kda_sfda_decode_tokens.restype = ctypes.c_int
+        L.kda_chunk_bwd_workspace_size.argtypes = [SP]
+        L.kda_chunk_bwd_workspace_size.restype = ctypes.c_size_t
+        L.kda_chunk_bwd.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.kda_chunk_bwd.restype = ctypes.c_int
         L.kda_status_string.argtypes = [ctypes.c_int]
         L.kda_status_string.restype = ctypes.c_char_p
         L.kda_version.argtypes = []
@@ -495,3 +500,51 @@ def sfda_decode_step(q, k, v, lam, beta, state, out=None):
 def sfda_decode_tokens(q, k, v, lam, beta, state, out=None):
     """SFDA form of decode_tokens (lam [B,T,H,dk] complex gates in place of alpha)."""
     return decode_tokens(q, k, v, lam, beta, state, out=out, _entry="kda_sfda_decode_tokens")
+
+
+def bwd_workspace_size(B, T, H, dk, dv, dtype="bf16") -> int:
+    """Bytes of device workspace chunk_bwd needs for this shape (0 if invalid)."""
+    shape = Shape(B, T, H, dk, dv, 64, BF16 if dtype == "bf16" else F32)
+    return int(lib().kda_chunk_bwd_workspace_size(ctypes.byref(shape)))
+
+
+def chunk_bwd(q, k, v, alpha, beta, d_o, initial_state=None, d_final_state=None, want_d_initial=True,
+              workspace=None):
+    """Gradients of L = sum <d_o, o> + <d_final_state, S_T> through chunk_fwd (KDA / CKDA),
+    the forward recomputed inside.  Inputs as chunk_fwd; d_o [B,T,H,dv] in the dtype of q;
+    d_final_state fp32 [B,H,dk,dv] or None (zero).  workspace: optional uint8 device
+    tensor of at least bwd_workspace_size(...) bytes (allocated here when omitted).
+    Returns (dq, dk, dv, dalpha, dbeta, d_initial_state or None), all fp32."""
+    torch = _torch()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    code = _dtype_code(q)
+    for t, nm in ((k, "k"), (alpha, "alpha"), (v, "v"), (beta, "beta"), (d_o, "d_o")):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{nm} must have the dtype of q")
+    if (k.shape != q.shape or alpha.shape != q.shape or v.shape != (B, T, H, dv) or beta.shape != (B, T, H)
+            or d_o.shape != (B, T, H, dv)):
+        raise ValueError("shapes: q, k, alpha [B,T,H,dk]; v, d_o [B,T,H,dv]; beta [B,T,H]")
+    for t, nm in ((initial_state, "initial_state"), (d_final_state, "d_final_state")):
+        if t is not None and (t.dtype != torch.float32 or t.shape != (B, H, dk, dv)):
+            raise ValueError(f"{nm} must be float32 [B,H,dk,dv]")
+    dev = q.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq, dkk, dal = (torch.empty((B, T, H, dk), **f32) for _ in range(3))
+    dvv = torch.empty((B, T, H, dv), **f32)
+    dbeta = torch.empty((B, T, H), **f32)
+    ds0 = torch.empty((B, H, dk, dv), **f32) if want_d_initial else None
+    shape = Shape(B, T, H, dk, dv, 64, code)
+    need = int(lib().kda_chunk_bwd_workspace_size(ctypes.byref(shape)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check((q, k, v, alpha, beta, d_o, initial_state, d_final_state, workspace),
+           ("q", "k", "v", "alpha", "beta", "d_o", "initial_state", "d_final_state", "workspace"), dev)
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = lib().kda_chunk_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                             _ptr(initial_state), _ptr(d_o), _ptr(d_final_state), _ptr(dq), _ptr(dkk), _ptr(dvv),
+                             _ptr(dal), _ptr(dbeta), _ptr(ds0), _ptr(workspace), ctypes.c_size_t(nbytes),
+                             _stream(dev))
+    if rc != 0:
+        raise KdaError(rc, "kda_chunk_bwd")
+    return dq, dkk, dvv, dal, dbeta, ds0

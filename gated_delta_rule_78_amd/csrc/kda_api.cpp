@@ -432,4 +432,54 @@ int kda_sfda_decode_tokens(const kda_shape* shape, const void* q, const void* k,
   return decode_impl(shape, q, k, v, lambda, beta, nullptr, nullptr, state, o, stream, true, true);
 }
 
+size_t kda_chunk_bwd_workspace_size(const kda_shape* shape) {
+  int es = 0;
+  if (check_shape(shape, false, &es) != KDA_OK) return 0;
+  return kda::bwd_workspace_bytes(shape->B, shape->T, shape->H, shape->dk, shape->dv);
+}
+
+int kda_chunk_bwd(const kda_shape* shape, const void* q, const void* k, const void* v, const void* alpha,
+                  const void* beta, const float* initial_state, const void* d_o, const float* d_final_state,
+                  float* dq, float* dk, float* dv, float* dalpha, float* dbeta, float* d_initial_state,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  int es = 0;
+  int rc = check_shape(shape, false, &es);
+  if (rc) return rc;
+  const kda_shape& s = *shape;
+  const int64_t rows = (int64_t)s.B * s.T * s.H;
+  const int64_t st_bytes = (int64_t)s.B * s.H * s.dk * s.dv * 4;
+  if (rows > 0 && (!q || !k || !v || !alpha || !beta || !d_o || !dq || !dk || !dv || !dalpha || !dbeta))
+    return KDA_ERR_NULL;
+  const size_t ws_need = kda::bwd_workspace_bytes(s.B, s.T, s.H, s.dk, s.dv);
+  if (ws_need > 0 && !workspace) return KDA_ERR_NULL;
+  if (workspace_bytes < ws_need) return KDA_ERR_WORKSPACE;
+  const void* in_ptrs[] = {q, k, v, alpha, beta, d_o};
+  for (const void* x : in_ptrs)
+    if (x && misaligned(x, es)) return KDA_ERR_ALIGN;
+  const void* out_ptrs[] = {dq, dk, dv, dalpha, d_initial_state, initial_state, d_final_state};
+  for (const void* x : out_ptrs)
+    if (x && misaligned(x)) return KDA_ERR_ALIGN;
+  if (dbeta && misaligned(dbeta, 4)) return KDA_ERR_ALIGN;
+  if (workspace && ((uintptr_t)workspace & 255u) != 0) return KDA_ERR_ALIGN;
+  const Range in[] = {range_of(q, rows * s.dk * es),       range_of(k, rows * s.dk * es),
+                      range_of(v, rows * s.dv * es),       range_of(alpha, rows * s.dk * es),
+                      range_of(beta, rows * es),           range_of(d_o, rows * s.dv * es),
+                      range_of(initial_state, initial_state ? st_bytes : 0),
+                      range_of(d_final_state, d_final_state ? st_bytes : 0)};
+  const Range out[] = {range_of(dq, rows * s.dk * 4),      range_of(dk, rows * s.dk * 4),
+                       range_of(dv, rows * s.dv * 4),      range_of(dalpha, rows * s.dk * 4),
+                       range_of(dbeta, rows * 4),          range_of(d_initial_state, d_initial_state ? st_bytes : 0),
+                       range_of(workspace, (int64_t)ws_need)};
+  constexpr int nout = sizeof(out) / sizeof(out[0]);
+  for (int i = 0; i < nout; ++i) {
+    for (const Range& r : in)
+      if (overlap(out[i], r)) return KDA_ERR_ALIAS;
+    for (int j = i + 1; j < nout; ++j)
+      if (overlap(out[i], out[j])) return KDA_ERR_ALIAS;
+  }
+  kda::BwdArgs a{q,  k,  v,      alpha, beta,           d_o, initial_state, d_final_state, dq, dk, dv, dalpha,
+                 dbeta, d_initial_state, (float*)workspace, s.B, s.T, s.H, s.dk, s.dv, s.dtype == KDA_BF16, stream};
+  return kda::launch_bwd(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 }  // extern "C"

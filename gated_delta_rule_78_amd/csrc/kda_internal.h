@@ -59,4 +59,54 @@ size_t record_bytes(bool bf16, int dk);
 // varlen: clamped offsets and the chunk table from a.cu (one workgroup)
 hipError_t launch_varlen_table(const ChunkArgs& a, int* cs, int* ctab, int* cbase, int* ctotal);
 
+// Backward of the chunk forward (fixed-length batches).  Gradients are fp32 in the
+// layouts of their inputs; ds0 may be NULL.  ws: bwd_workspace_bytes() of scratch.
+struct BwdArgs {
+  const void *q, *k, *v, *alpha, *beta, *dO;
+  const float* s0;   // may be NULL (zero start state)
+  const float* dsT;  // may be NULL (zero final-state gradient)
+  float *dq, *dk, *dv, *dalpha, *dbeta, *ds0;
+  float* ws;
+  int B, T, H, Dk, Dv;
+  bool bf16;
+  void* stream;
+};
+
+// fp32 offsets inside one chunk's workspace block of the backward (C = 64 rows, NB = 4
+// blocks of 16): gate products, A, D, M, W (records); S_n, Delta_n (forward walk);
+// dS'_n, dDelta_n (adjoint walk); scratch of the gradient kernel.
+struct BwdLayout {
+  int gam, rho, pin, sig, pib, A, D, M, W, S, DL, DS, DDL, AV, BV, DW, F, PA, PD, total;
+  __host__ __device__ BwdLayout(int dk, int dv) {
+    const int C = 64, CK = C * dk;
+    gam = 0;
+    rho = gam + CK;
+    pin = rho + CK;
+    sig = pin + CK;
+    pib = sig + CK;
+    A = pib + 4 * dk;
+    D = A + C * C;
+    M = D + C * C;
+    W = M + C * C;
+    S = W + CK;
+    DL = S + dk * dv;
+    DS = DL + C * dv;
+    DDL = DS + dk * dv;
+    AV = DDL + C * dv;
+    BV = AV + CK;
+    DW = BV + CK;
+    F = DW + CK;
+    PA = F + CK;
+    PD = PA + 3 * CK;
+    total = (PD + 3 * CK + 63) / 64 * 64;
+  }
+};
+
+inline size_t bwd_workspace_bytes(int B, int T, int H, int dk, int dv) {
+  const size_t nchunks = ((size_t)T + 63) / 64;
+  return (size_t)B * H * nchunks * BwdLayout(dk, dv).total * sizeof(float);
+}
+
+hipError_t launch_bwd(const BwdArgs& a);
+
 }  // namespace kda

@@ -177,6 +177,16 @@ def make(B, T, H, dk, dv, dtype="bf16", gates="kda", zero_s0=False, seed=BASE_SE
                   dict(B=B, T=T, H=H, dk=dk, dv=dv, gates=gates, seed=seed, lead=lead), erase, write)
 
 
+def make_upstream(B: int, T: int, H: int, dk: int, dv: int, dtype: str = "bf16", seed: int = BASE_SEED):
+    """Upstream gradients for the backward: dO [B, T, H, dv] N(0, 1) in the input dtype
+    (bf16 bits or fp32) and dS_T [B, H, dk, dv] fp32 N(0, 0.02), from their own seeded
+    streams."""
+    rd, rs = [np.random.default_rng(s) for s in np.random.SeedSequence([seed, 7]).spawn(2)]
+    dO = rd.standard_normal((B, T, H, dv), dtype=np.float32)
+    dST = (0.02 * rs.standard_normal((B, H, dk, dv), dtype=np.float32)).astype(np.float32)
+    return (bf16_bits(dO) if dtype == "bf16" else dO), dST
+
+
 def make_workload(name: str, T: int | None = None, B: int | None = None, H: int | None = None,
                   seed: int | None = None) -> Inputs:
     """Draw a named workload, optionally overriding B / T / H (tests use small T)."""

@@ -232,6 +232,40 @@ int kda_sfda_decode_tokens(const kda_shape* shape, const void* q, const void* k,
                            void* stream);
 
 /*
+ * Backward of the chunk forward (training): the gradients of
+ *   L = sum_t <dO_t, o_t> + <dS_T, S_T>
+ * through the KDA / CKDA forward of kda_chunk_fwd, with respect to q, k, v, alpha, beta
+ * and the start state, taken through the same chunk-WY form (SFDA page, "El Teorema de
+ * Chunk-WY Constructivo"; Gated DeltaNet-2 page, section 3, whose gate-aware backward
+ * item keeps the per-channel gates inside the gradients of the intra-chunk matrices).
+ * The forward is recomputed inside (the call takes the forward's inputs, not its
+ * outputs).  Arithmetic is fp32 throughout (inputs widened from their dtype); the gate
+ * gradient is formed without dividing by a gate, so exact zero gates get their exact
+ * gradient.
+ *   q, k, alpha, v, beta, initial_state : as kda_chunk_fwd (initial_state NULL = zeros)
+ *   d_o             : [B, T, H, dv], dtype of q: the gradient of L with respect to o
+ *   d_final_state   : [B, H, dk, dv] fp32, or NULL for a zero gradient of S_T
+ *   dq, dk, dalpha  : [B, T, H, dk] fp32 outputs
+ *   dv              : [B, T, H, dv] fp32 output
+ *   dbeta           : [B, T, H] fp32 output
+ *   d_initial_state : [B, H, dk, dv] fp32 output, or NULL when not wanted
+ *   workspace       : kda_chunk_bwd_workspace_size(shape) bytes of device memory,
+ *                     256-byte aligned (about 740 KB per chunk of 64 tokens and head at
+ *                     dk = dv = 128); its contents on entry do not matter.
+ * Supported: dk, dv in {64, 128}, bf16 or fp32 inputs, chunk 0 or 64.  Inputs need the
+ * alignment of their element type; outputs and the states 16 bytes.  No output may
+ * overlap an input, another output or the workspace (KDA_ERR_ALIAS); a NULL required
+ * pointer is KDA_ERR_NULL (unless B*T*H == 0), a short workspace KDA_ERR_WORKSPACE.
+ * T == 0 writes d_initial_state = d_final_state (or zeros).
+ */
+size_t kda_chunk_bwd_workspace_size(const kda_shape* shape);  /* 0 if the shape is invalid */
+int kda_chunk_bwd(const kda_shape* shape, const void* q, const void* k, const void* v,
+                  const void* alpha, const void* beta, const float* initial_state,
+                  const void* d_o, const float* d_final_state, float* dq, float* dk,
+                  float* dv, float* dalpha, float* dbeta, float* d_initial_state,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * One recurrent decode step for every (b, h), state updated in place:
  *   S <- (I - beta k k^T) Diag(alpha) S + beta k v^T ;  o <- S^T q.
  *   state : [B, H, dk, dv] fp32, read and written in place.

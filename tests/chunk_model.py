@@ -271,11 +271,13 @@ def _chunk_fwd_parts(q, k, v, a, beta, S):
                 O=O, S=S, Sn=Sn)
 
 
-def chunk_backward(q, k, v, a, beta, dO, S0=None, dST=None, C=64, check_zero_formula=False):
+def chunk_backward(q, k, v, a, beta, dO, S0=None, dST=None, C=64, check_zero_formula=False, blocked=False):
     """Gradients for one head through the chunk algebra (fp64).  q, k, a [T, dk]; v, dO
     [T, dv]; beta [T]; S0, dST [dk, dv] or None.  Returns dict dq, dk, dv, dalpha, dbeta,
     dS0.  check_zero_formula: also evaluate the exclusive-product formula for every gate
-    (zero or not) and assert it equals P_m / alpha_m where alpha_m != 0."""
+    (zero or not) and assert it equals P_m / alpha_m where alpha_m != 0.  blocked: take the
+    decayed sums and the gate gradient from blocked_decay_grads (the GPU kernel's
+    decomposition) instead."""
     T, dk = q.shape
     dv = v.shape[1]
     S = np.zeros((dk, dv)) if S0 is None else np.asarray(S0, np.float64).copy()
@@ -315,6 +317,8 @@ def chunk_backward(q, k, v, a, beta, dO, S0=None, dST=None, C=64, check_zero_for
         Zq = np.einsum("ij,jc,ijc->ic", dA, kc, r)
         Zr = np.einsum("ij,jc,ijc->ic", dD, kc, r)
         Zc = np.einsum("ij,ic,ijc->jc", dA, qc, r) + np.einsum("ij,ic,ijc->jc", dD, kc, r)
+        if blocked:
+            Zq, Zr, Zc, dal_b = blocked_decay_grads(dA, dD, qc, kc, ac, dQg * qc + dKg * kc, dKr * kc, dgL)
         dq = dQg * gam + Zq
         dk_ = dKg * gam + dKr * rho + Zr + Zc
         dG = dQg * p["Qg"] + dKg * p["Kg"] + qc * Zq + kc * Zr - kc * Zc - dKr * p["Kr"]
@@ -341,6 +345,8 @@ def chunk_backward(q, k, v, a, beta, dO, S0=None, dST=None, C=64, check_zero_for
                         assert abs(tot - dal[m, c]) <= 1e-9 * max(1.0, abs(tot)), (m, c, tot, dal[m, c])
                     else:
                         dal[m, c] = tot
+        if blocked:
+            dal = dal_b
         n, c0 = p["n"], p["c0"]
         out["dq"][c0:c0 + n] = dq[:n]
         out["dk"][c0:c0 + n] = dk_[:n]
@@ -350,3 +356,106 @@ def chunk_backward(q, k, v, a, beta, dO, S0=None, dST=None, C=64, check_zero_for
         dSn = dS
     out["dS0"] = dSn
     return out
+
+
+def blocked_decay_grads(dA, dD, q, k, a, av, bv, dgl):
+    """The decayed sums and the gate gradient of one chunk as the GPU gradient kernel forms
+    them (fp64), from dA (lower, diagonal included), dD (strictly lower), the per-row
+    start-state weights av = d(Q o gamma) o q + d(K o gamma) o k, the final-state weights
+    bv = d(K o rho) o k and dgl = d gamma_last.  Returns Zq, Zr, Zc (the sums
+    sum_j dA_ij k_j r_ij, sum_j dD_ij k_j r_ij, sum_i (dA_ij q_i + dD_ij k_i) r_ij) and
+    dalpha, with no division by a gate:
+
+    * block products anchored at the 16-row block edges: PA^M = dA[>= s, < s] Khat^M,
+      PD^M likewise (Khat^M_j = k_j r(s-1, j)), F^M_j = sum_{i > e} (dA_ij q_i + dD_ij k_i)
+      r(i, e), with every r a product of in-block prefix / suffix products and whole
+      block totals;
+    * per (channel, block): the in-block parts of the sums, and for the gate gradient
+      the recursion u_i <- alpha_m u_i + E_im over m, started from the weights of the
+      pairs that reach left of the block (g_i), the rows below the block folded into
+      its last row (X, f).
+    """
+    C, dk = q.shape
+    NB = C // SUB
+    pin, sig, pib = np.zeros((C, dk)), np.zeros((C, dk)), np.zeros((NB, dk))
+    for I in range(NB):
+        p = np.ones(dk)
+        for r in range(SUB):
+            p = p * a[I * SUB + r]
+            pin[I * SUB + r] = p
+        pib[I] = p
+        sf = np.ones(dk)
+        for r in range(SUB - 1, -1, -1):
+            sig[I * SUB + r] = sf
+            sf = sf * a[I * SUB + r]
+
+    def between(J, I):
+        p = np.ones(dk)
+        for x in range(J + 1, I):
+            p = p * pib[x]
+        return p
+
+    PA, PD, F = np.zeros((NB, C, dk)), np.zeros((NB, C, dk)), np.zeros((C, dk))
+    for M in range(1, NB):
+        s = M * SUB
+        khat = np.stack([k[j] * sig[j] * between(j // SUB, M) for j in range(s)])
+        PA[M, s:] = dA[s:, :s] @ khat
+        PD[M, s:] = dD[s:, :s] @ khat
+    for M in range(NB - 1):
+        s, e1 = M * SUB, M * SUB + SUB
+        rie = np.stack([pin[i] * between(M, i // SUB) for i in range(e1, C)])
+        F[s:e1] = dA[e1:, s:e1].T @ (q[e1:] * rie) + dD[e1:, s:e1].T @ (k[e1:] * rie)
+
+    Zq, Zr, Zc, dal = np.zeros((C, dk)), np.zeros((C, dk)), np.zeros((C, dk)), np.zeros((C, dk))
+    for M in range(NB):
+        s = M * SUB
+        al, qv, kv = a[s:s + SUB], q[s:s + SUB], k[s:s + SUB]
+        gs = np.prod(pib[:M], axis=0) if M > 0 else np.ones(dk)
+        rend = np.prod(pib[M + 1:], axis=0) if M < NB - 1 else np.ones(dk)
+        for r in range(SUB):
+            i = s + r
+            zq, zr, P = dA[i, i] * kv[r], np.zeros(dk), np.ones(dk)
+            for rj in range(r - 1, -1, -1):
+                P = P * al[rj + 1]
+                zq = zq + dA[i, s + rj] * kv[rj] * P
+                zr = zr + dD[i, s + rj] * kv[rj] * P
+            if M > 0:
+                zq = zq + pin[i] * PA[M, i]
+                zr = zr + pin[i] * PD[M, i]
+            zc, P = dA[i, i] * qv[r], np.ones(dk)
+            for ri in range(r + 1, SUB):
+                P = P * al[ri]
+                zc = zc + (dA[s + ri, i] * qv[ri] + dD[s + ri, i] * kv[ri]) * P
+            if M < NB - 1:
+                zc = zc + sig[i] * F[i]
+            Zq[i], Zr[i], Zc[i] = zq, zr, zc
+        bvs = sum((bv[j] * sig[j] * between(j // SUB, M) for j in range(s)), np.zeros(dk))
+
+        def g_at(i):
+            g = av[i] * gs
+            if M > 0:
+                g = g + q[i] * PA[M, i] + k[i] * PD[M, i]
+            if i == C - 1:
+                g = g + bvs + dgl * gs
+            return g
+
+        u = [g_at(s + r) for r in range(SUB)]
+        if M < NB - 1:
+            x = np.zeros(dk)
+            for i in range(C - 1, s + SUB - 1, -1):   # sum_{i > e} r(i, e) g_i
+                x = a[i] * (g_at(i) + x)
+            u[SUB - 1] = u[SUB - 1] + x
+            f = [kv[r] * F[s + r] + bv[s + r] * rend for r in range(SUB)]
+        else:
+            f = [bv[s + r] for r in range(SUB)]
+        for m in range(SUB):
+            acc = u[SUB - 1]
+            for i in range(SUB - 2, m - 1, -1):
+                acc = u[i] + al[i + 1] * acc
+            dal[s + m] = acc
+            for i in range(m + 1, SUB):
+                E = (qv[i] * dA[s + i, s + m] + kv[i] * dD[s + i, s + m]) * kv[m]
+                if i == SUB - 1:
+                    E = E + f[m]
+                u[i] = al[m] * u[i] + E
+    return Zq, Zr, Zc, dal

@@ -298,3 +298,38 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
     with pytest.raises((ValueError, RuntimeError)):
         kda.chunk_fwd(x, x, x, x, torch.zeros(1, 4, 1, dtype=torch.bfloat16))
+
+
+def test_bwd_argument_errors(L):
+    shape = kda.Shape(1, 64, 2, 64, 64, 64, 0)
+    need = L.kda_chunk_bwd_workspace_size(ctypes.byref(shape))
+    assert need > 0
+    assert L.kda_chunk_bwd_workspace_size(None) == 0
+    assert L.kda_chunk_bwd_workspace_size(ctypes.byref(kda.Shape(1, 64, 2, 96, 64, 64, 0))) == 0
+    sz = ctypes.c_size_t
+
+    def bwd(q=_p(0), a=_p(3), dO=_p(5), dq=_p(10), dbeta=_p(14), ds0=_p(15), s0=None, dst=None, ws=_p(16),
+            n=need, sh=shape):
+        return L.kda_chunk_bwd(ctypes.byref(sh), q, _p(1), _p(2), a, _p(4), s0, dO, dst, dq, _p(11), _p(12),
+                               _p(13), dbeta, ds0, ws, sz(n), None)
+
+    assert L.kda_chunk_bwd(None, *([None] * 15), sz(0), None) == NULL
+    assert bwd(q=None) == NULL
+    assert bwd(dO=None) == NULL
+    assert bwd(dq=None) == NULL
+    assert bwd(ws=None) == NULL
+    assert bwd(n=need - 1) == WORKSPACE
+    assert bwd(ws=_p(16, off=16)) == ALIGN         # the workspace wants 256-byte alignment
+    assert bwd(dq=_p(10, off=4)) == ALIGN
+    assert bwd(a=_p(3, off=1)) == ALIGN
+    assert bwd(dq=_p(3)) == ALIAS                  # gradient over an input
+    assert bwd(dbeta=_p(10, off=64)) == ALIAS      # two outputs overlap
+    assert bwd(ws=_p(5)) == ALIAS                  # workspace over d_o
+    assert bwd(ds0=_p(16)) == ALIAS                # d_initial_state inside the workspace
+    assert bwd(sh=kda.Shape(1, 64, 2, 96, 64, 64, 0)) == UNSUP
+    assert bwd(sh=kda.Shape(1, 64, 2, 64, 64, 32, 0)) == UNSUP
+    assert bwd(sh=kda.Shape(1, -1, 2, 64, 64, 64, 0)) == SHAPE
+    assert bwd(sh=kda.Shape(1, 64, 2, 64, 64, 64, 5)) == DTYPE
+    # nothing to do: no pointers needed, d_initial_state still written (on the device)
+    zero = kda.Shape(0, 64, 2, 64, 64, 64, 0)
+    assert L.kda_chunk_bwd(ctypes.byref(zero), *([None] * 14), None, sz(0), None) == 0

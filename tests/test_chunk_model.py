@@ -98,3 +98,30 @@ def test_chunk_backward_matches_oracle(T, dk, dv, zero_frac, check):
     for key in ("dq", "dk", "dv", "dalpha", "dbeta", "dS0"):
         y = r[key][0]
         assert np.abs(g[key] - y).max() <= 1e-10 * max(1.0, np.abs(y).max()), key
+
+
+@pytest.mark.parametrize("T,dk,dv,zero_frac", [(150, 6, 5, 0.1), (64, 4, 3, 0.3), (200, 8, 4, 0.0), (37, 3, 2, 0.5)])
+def test_blocked_gate_gradient_matches_oracle(T, dk, dv, zero_frac):
+    """The GPU gradient kernel's decomposition (block-anchored products, rows below a
+    block folded into its last row, in-block recursion over the gates) gives the
+    oracle's gradients, exact zero gates included."""
+    import oracle
+    rng = np.random.default_rng(3 * T + dk)
+    q = rng.standard_normal((T, dk))
+    k = rng.standard_normal((T, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    v = rng.standard_normal((T, dv))
+    a = np.tanh(2 * rng.standard_normal((T, dk)))
+    m = rng.random(a.shape) < zero_frac
+    a[m] = rng.choice([-1.0, 0.0, 1.0], size=int(m.sum()))
+    a[5, 0] = a[17, 0] = 0.0   # zeros in both of two adjacent blocks of one channel
+    b = rng.uniform(0.0, 2.0, T)
+    S0 = rng.standard_normal((dk, dv))
+    dO = rng.standard_normal((T, dv))
+    dST = rng.standard_normal((dk, dv))
+    g = cm.chunk_backward(q, k, v, a, b, dO, S0, dST, C=64, blocked=True)
+    r = oracle.bwd(q[None, :, None], k[None, :, None], v[None, :, None], a[None, :, None], b[None, :, None],
+                   dO[None], S0=S0[None], dST=dST[None])
+    for key in ("dq", "dk", "dv", "dalpha", "dbeta", "dS0"):
+        y = r[key][0]
+        assert np.abs(g[key] - y).max() <= 1e-10 * max(1.0, np.abs(y).max()), key
