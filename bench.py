@@ -38,6 +38,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix cores
+MFMA_FP32_PEAK_TFLOPS = 157.3   # dense fp32 matrix cores
 CSRC = os.path.join(ROOT, "gated_delta_rule_78_amd", "csrc")
 # the rocprofv3 counter summary of each kernel, and the sources that kernel is built from
 PMC_FILES = {
@@ -197,6 +198,45 @@ def bench_prefill(name, steps, warmup, log):
     return w, res, inp
 
 
+def bwd_flops(B, T, H, dk, dv, C=64):
+    """Dense product flops of the chunk backward per call (forward recomputed inside): per
+    chunk A, D, W (records); Delta, S' (forward walk); dDelta, dS (adjoint walk); dQg, dKr,
+    dW, dA, dV, dMt, dKg, dMt Mt^T, M^T X and the block-anchored products (gradients)."""
+    nch = B * H * ((T + C - 1) // C)
+    mm = lambda m, n, k: 2 * m * n * k
+    anchored = sum(mm(C - s, dk, s) for s in (16, 32, 48))        # PA (or PD) over the three blocks
+    per = (mm(C, C, dk) * 2 + mm(C, dk, C)                           # A, D, W
+           + mm(C, dv, C + dk) + mm(dk, dv, C)                       # Delta, S'
+           + mm(C, dv, dk + C) + mm(dk, dv, 2 * C)                   # dDelta, dS
+           + 3 * mm(C, dk, dv) + mm(C, C, dv) + mm(C, dv, C)         # dQg, dKr, dW, dA, dV
+           + mm(C, C, dv + dk) + mm(C, dk, C) + 2 * mm(C, C, C)      # dMt, dKg, X, dT
+           + 2 * anchored + sum(mm(16, dk, 2 * n) for n in (48, 32, 16)))  # PA, PD, F
+    return nch * per
+
+
+def bench_backward(steps, warmup, log, name="ckda_prefill_8k"):
+    """Times kda_chunk_bwd on workload `name` (start state and a final-state gradient
+    given).  Returns (workload, ms per call)."""
+    import torch
+    import gated_delta_rule_78_amd as kda
+    from gated_delta_rule_78_amd.inputs import make_workload, make_upstream, WORKLOADS, to_torch
+    w = WORKLOADS[name]
+    t0 = time.time()
+    inp = make_workload(name)
+    q, k, v, a, b, s0 = to_torch(inp)
+    dO, dST = make_upstream(w.B, w.T, w.H, w.dk, w.dv, w.dtype, seed=90)
+    d_o = torch.from_numpy(np.ascontiguousarray(dO).view(np.int16)).to("cuda").view(torch.bfloat16)
+    dst = torch.from_numpy(dST).to("cuda")
+    ws = torch.empty(kda.bwd_workspace_size(w.B, w.T, w.H, w.dk, w.dv), dtype=torch.uint8, device="cuda")
+    log(f"[bench] {name} backward: inputs ready in {time.time() - t0:.1f}s, workspace {ws.numel() / 1e9:.2f} GB")
+    stream = torch.cuda.current_stream()
+    ms = timed(lambda: kda.chunk_bwd(q, k, v, a, b, d_o, initial_state=s0, d_final_state=dst, workspace=ws),
+               steps, warmup, stream)
+    del q, k, v, a, b, s0, d_o, dst, ws
+    torch.cuda.empty_cache()
+    return w, ms
+
+
 def kernel_bytes(kernel, w):
     if kernel == "chunk_records":
         return records_bytes(w.B, w.T, w.H, w.dk)
@@ -308,6 +348,8 @@ def main():
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode measurement (for profiling the decode kernel)")
+    ap.add_argument("--bwd-only", action="store_true",
+                    help="only the backward measurement (for profiling the backward kernels)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -337,6 +379,13 @@ def main():
         gbs = db / (msd * 1e-3) / 1e9
         print(json.dumps({"workload": "ckda_decode_b256", "ms_per_step": msd, "value": gbs, "unit": "GB/s",
                           "frac": gbs / HBM_PEAK_GBS, "bytes_per_step": db}), flush=True)
+        return
+    if args.bwd_only:
+        wb, msb = bench_backward(max(1, args.steps // 4), 1, log)
+        fl = bwd_flops(wb.B, wb.T, wb.H, wb.dk, wb.dv)
+        print(json.dumps({"workload": "ckda_prefill_8k backward", "ms_per_call": msb,
+                          "tokens_per_s": wb.B * wb.T / (msb * 1e-3),
+                          "tflops_fp32": fl / (msb * 1e-3) / 1e12}), flush=True)
         return
     w, res, inp = bench_prefill("kda_prefill_8k", args.steps, args.warmup, log)
     ms = res["ms"]
@@ -400,6 +449,13 @@ def main():
         out["sfda_decode"] = {"workload": "sfda_decode_b256", "ms_per_step": mss, "value": gbs_s, "unit": "GB/s",
                               "tokens_per_s": ws_.B / (mss * 1e-3), "frac": gbs_s / HBM_PEAK_GBS}
         log(f"[bench] sfda decode: {mss * 1e3:.1f} us/step, {gbs_s:.1f} GB/s")
+        wb, msb = bench_backward(max(2, args.steps // 4), 1, log)
+        flb = bwd_flops(wb.B, wb.T, wb.H, wb.dk, wb.dv)
+        out["ckda_backward_8k"] = {"workload": "ckda_prefill_8k", "ms_per_call": msb,
+                                   "tokens_per_s": wb.B * wb.T / (msb * 1e-3), "dtype": "f32",
+                                   "dense_flops_per_call": flb, "tflops_fp32": flb / (msb * 1e-3) / 1e12,
+                                   "frac_fp32_mfma": flb / (msb * 1e-3) / 1e12 / MFMA_FP32_PEAK_TFLOPS}
+        log(f"[bench] ckda backward 8k: {msb:.3f} ms/call, {flb / (msb * 1e-3) / 1e12:.1f} dense fp32 TFLOP/s")
         wt, mst, ntk = bench_decode_tokens(4, log)
         bt_ = decode_bytes(wt.B, wt.H, wt.dk, wt.dv, tokens=ntk)
         out["decode_tokens"] = {"workload": "ckda_decode_b256", "tokens_per_call": ntk, "ms_per_call": mst,

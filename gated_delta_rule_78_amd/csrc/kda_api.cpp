@@ -453,9 +453,11 @@ int kda_chunk_bwd(const kda_shape* shape, const void* q, const void* k, const vo
   const size_t ws_need = kda::bwd_workspace_bytes(s.B, s.T, s.H, s.dk, s.dv);
   if (ws_need > 0 && !workspace) return KDA_ERR_NULL;
   if (workspace_bytes < ws_need) return KDA_ERR_WORKSPACE;
-  const void* in_ptrs[] = {q, k, v, alpha, beta, d_o};
+  // q, k, v, alpha and d_o move in vectors; beta is read per element
+  const void* in_ptrs[] = {q, k, v, alpha, d_o};
   for (const void* x : in_ptrs)
-    if (x && misaligned(x, es)) return KDA_ERR_ALIGN;
+    if (x && misaligned(x)) return KDA_ERR_ALIGN;
+  if (beta && misaligned(beta, es)) return KDA_ERR_ALIGN;
   const void* out_ptrs[] = {dq, dk, dv, dalpha, d_initial_state, initial_state, d_final_state};
   for (const void* x : out_ptrs)
     if (x && misaligned(x)) return KDA_ERR_ALIGN;

@@ -45,15 +45,36 @@ constexpr int NT = 256;  // threads per workgroup of every kernel here
 // One 16x16 fp32 tile: acc[i][j] = sum_k fa(i, k) fb(k, j), K a multiple of 4.  Lane
 // (n = lane & 15, g = lane >> 4) feeds A[n][k0 + g] and B[k0 + g][n]; the result holds
 // element (4 g + r, n) in acc[r].
+// K a multiple of 16: the operands of the next 16 k are loaded while the current four
+// steps run.
 template <class FA, class FB>
 __device__ __forceinline__ f32x4_t tile_mm(int K, FA fa, FB fb) {
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int k0 = 0; k0 < K; k0 += 4) {
+  float a0[4], b0[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    a0[t] = fa(n, 4 * t + g);
+    b0[t] = fb(4 * t + g, n);
+  }
+#pragma unroll 1
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    float a1[4], b1[4];
+    if (k0 + 16 < K) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        a1[t] = fa(n, k0 + 16 + 4 * t + g);
+        b1[t] = fb(k0 + 16 + 4 * t + g, n);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
 #ifndef KDA_HOST_PASS
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa(n, k0 + g), fb(k0 + g, n), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[t], b0[t], acc, 0, 0, 0);
 #endif
+      a0[t] = a1[t];
+      b0[t] = b1[t];
+    }
   }
   return acc;
 }
@@ -136,29 +157,39 @@ __global__ __launch_bounds__(NT) void bwd_records_kernel(BwdArgs a, int NC) {
   // end, exclusive), pi (from the block start, inclusive), sigma (to the block end,
   // exclusive) and the block totals.
   for (int c = tid; c < dk; c += NT) {
-    float gm = 1.f;
+    float gm = 1.f, pib[NB];
     for (int I = 0; I < NB; ++I) {
+      float al[SUB];
+#pragma unroll
+      for (int r = 0; r < SUB; ++r) al[r] = AL.at(I * SUB + r, c, 1.f);
       float p = 1.f;
+#pragma unroll
       for (int r = 0; r < SUB; ++r) {
         const int i = I * SUB + r;
-        const float al = AL.at(i, c, 1.f);
-        p *= al;
-        gm *= al;
+        p *= al[r];
+        gm *= al[r];
         PIN[i * dk + c] = p;
         GAM[i * dk + c] = gm;
       }
-      PIB[I * dk + c] = p;
+      PIB[I * dk + c] = pib[I] = p;
       float sf = 1.f;
+#pragma unroll
       for (int r = SUB - 1; r >= 0; --r) {
-        const int i = I * SUB + r;
-        SIG[i * dk + c] = sf;
-        sf *= AL.at(i, c, 1.f);
+        SIG[(I * SUB + r) * dk + c] = sf;
+        sf *= al[r];
       }
     }
-    float sf = 1.f;
-    for (int i = C - 1; i >= 0; --i) {
-      RHO[i * dk + c] = sf;
-      sf *= AL.at(i, c, 1.f);
+    // rho_i = sigma_i * the whole blocks after i's block
+    float tail = 1.f;
+    for (int I = NB - 1; I >= 0; --I) {
+      float sf = tail;
+#pragma unroll
+      for (int r = SUB - 1; r >= 0; --r) {
+        const int i = I * SUB + r;
+        RHO[i * dk + c] = sf;
+        sf *= AL.at(i, c, 1.f);
+      }
+      tail *= pib[I];
     }
   }
   for (int i = tid; i < C; i += NT) sB[i] = BE.at(i, 0);
@@ -196,13 +227,20 @@ __global__ __launch_bounds__(NT) void bwd_records_kernel(BwdArgs a, int NC) {
     const int s = I * SUB;
     for (int mat = 0; mat < 2; ++mat) {
       for (int c = tid; c < dk; c += NT) {
+        float kv[SUB], xv[SUB], av[SUB];
+#pragma unroll
+        for (int r = 0; r < SUB; ++r) {
+          kv[r] = K.at(s + r, c);
+          xv[r] = mat ? kv[r] : Q.at(s + r, c);
+          av[r] = AL.at(s + r, c, 1.f);
+        }
+#pragma unroll
         for (int rj = 0; rj < SUB; ++rj) {
-          const float kj = K.at(s + rj, c);
           float P = 1.f;
+#pragma unroll
           for (int ri = rj; ri < SUB; ++ri) {
-            if (ri > rj) P *= AL.at(s + ri, c, 1.f);
-            const float xi = mat ? K.at(s + ri, c) : Q.at(s + ri, c);
-            sRed[(ri * (ri + 1) / 2 + rj) * (dk + 1) + c] = (mat && ri == rj) ? 0.f : xi * kj * P;
+            if (ri > rj) P *= av[ri];
+            sRed[(ri * (ri + 1) / 2 + rj) * (dk + 1) + c] = (mat && ri == rj) ? 0.f : xv[ri] * kv[rj] * P;
           }
         }
       }
@@ -211,8 +249,13 @@ __global__ __launch_bounds__(NT) void bwd_records_kernel(BwdArgs a, int NC) {
         int ri = 0;
         while ((ri + 1) * (ri + 2) / 2 <= p) ++ri;
         const int rj = p - ri * (ri + 1) / 2;
-        float sum = 0.f;
-        for (int c = 0; c < dk; ++c) sum += sRed[p * (dk + 1) + c];
+        float sum = 0.f, sum2 = 0.f;
+#pragma unroll 8
+        for (int c = 0; c < dk; c += 2) {
+          sum += sRed[p * (dk + 1) + c];
+          sum2 += sRed[p * (dk + 1) + c + 1];
+        }
+        sum += sum2;
         (mat ? sD : sA)[s + ri][s + rj] = sum;
       }
       __syncthreads();
@@ -269,100 +312,241 @@ __global__ __launch_bounds__(NT) void bwd_records_kernel(BwdArgs a, int NC) {
 }
 
 // ---------------------------------------------------------------------------------------
-// bwd_state_kernel: one workgroup per (b, h, value tile of VT columns), chunks in order.
-// Writes the chunk-start state S_n and Delta_n of every chunk.
-template <typename T, int VT>
-__global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC) {
-  const int tid = threadIdx.x, dk = a.Dk, dv = a.Dv, ntile = dv / VT;
-  const BwdLayout L(dk, dv);
-  const int bh = blockIdx.x / ntile, v0 = (blockIdx.x % ntile) * VT;
-  __shared__ float sS[2][128 * VT];
-  __shared__ float sDl[C * VT];
-  for (int x = tid; x < dk * VT; x += NT) {
-    const int c = x / VT, j = x % VT;
-    sS[0][x] = a.s0 ? a.s0[((size_t)bh * dk + c) * dv + v0 + j] : 0.f;
+// The two walks.  One workgroup per (b, h, 64 value columns); wave w owns the 16 columns
+// v0 + 16 w .. v0 + 16 w + 15 (the value columns of the state evolve independently) and
+// keeps them in matrix-core accumulators for the whole walk: DK / 16 tiles, element
+// (16 I + 4 g + r, n) in register r of tile I.  The four steps of each 16-wide slice of a
+// product take k-slot k0 + 4 g + t at step t, so an accumulator tile is itself the B
+// operand of a product over its rows: neither the state nor Delta leaves the registers.
+// Only the chunk's shared operands are staged in LDS (row strides padded by four floats),
+// with vector loads issued together.
+namespace {
+
+constexpr int VTW = 64;  // value columns per walk workgroup, 16 per wave
+
+// four consecutive elements (i % 4 == 0) of an input tensor, widened
+template <typename T>
+__device__ __forceinline__ float4 ld4(const void* p, size_t i);
+template <>
+__device__ __forceinline__ float4 ld4<bf16_t>(const void* p, size_t i) {
+  const uint2 w = *(const uint2*)((const uint16_t*)p + i);
+  return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u), __uint_as_float(w.y << 16),
+                     __uint_as_float(w.y & 0xFFFF0000u));
+}
+template <>
+__device__ __forceinline__ float4 ld4<float>(const void* p, size_t i) {
+  return *(const float4*)((const float*)p + i);
+}
+
+__device__ __forceinline__ f32x4_t zero4f() {
+  f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+  return z;
+}
+
+// acc += sgn * A[row][k0 .. k0 + 15] B[k0 .. k0 + 15][n], this lane's A row in LDS at `arow`,
+// fb(t) = B[k0 + 4 g + t][n]
+template <class FB>
+__device__ __forceinline__ void mm16(f32x4_t& acc, const float* arow, int k0, FB fb, float sgn = 1.f) {
+  const int g = (threadIdx.x & 63) >> 4;
+  const float4 a4 = *(const float4*)(arow + k0 + 4 * g);
+  const float av[4] = {sgn * a4.x, sgn * a4.y, sgn * a4.z, sgn * a4.w};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#ifndef KDA_HOST_PASS
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[t], fb(t), acc, 0, 0, 0);
+#endif
   }
-  __syncthreads();
-  int cur = 0;
-  for (int n = 0; n < NC; ++n) {
-    const ChunkGeom cg = chunk_geom(bh * NC + n, NC, a.H, a.T);
-    float* ch = a.ws + (size_t)(bh * NC + n) * L.total;
-    const Rows<T> V{a.v, row0(cg, a.T, a.H, dv), (size_t)a.H * dv, cg.len};
-    const Rows<T> K{a.k, row0(cg, a.T, a.H, dk), (size_t)a.H * dk, cg.len};
-    const Rows<T> BE{a.beta, ((size_t)cg.b * a.T + cg.t0) * a.H + cg.h, (size_t)a.H, cg.len};
-    const float* S = sS[cur];
-    for (int x = tid; x < dk * VT; x += NT) ch[L.S + (x / VT) * dv + v0 + x % VT] = S[x];
-    // Delta = Mt V - W S   (K = C + dk: [Mt | -W] [V ; S])
-    wg_mm(
-        C / 16, VT / 16, C + dk,
-        [&](int i, int kk) { return kk < C ? ch[L.M + i * C + kk] * BE.at(kk, 0) : -ch[L.W + i * dk + kk - C]; },
-        [&](int kk, int j) { return kk < C ? V.at(kk, v0 + j) : S[(kk - C) * VT + j]; },
-        [&](int i, int j, float x) {
-          sDl[i * VT + j] = x;
-          ch[L.DL + i * dv + v0 + j] = x;
-        });
+}
+
+}  // namespace
+
+// bwd_state_kernel: chunks in order; writes the chunk-start state S_n and Delta_n.
+template <typename T, int DK>
+__global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC) {
+  constexpr int LM = C + 4, LW = DK + 4, LV = VTW + 4;
+  __shared__ float sM[C * LM], sW[C * LW], sKrT[DK * LM], sV[C * LV], sGl[DK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, g = lane >> 4;
+  const int dv = a.Dv, ntile = dv / VTW, bh = blockIdx.x / ntile, v0 = (blockIdx.x % ntile) * VTW;
+  const int col = v0 + 16 * wave + n;  // this lane's state column
+  const BwdLayout L(DK, dv);
+  f32x4_t S[DK / 16];
+#pragma unroll
+  for (int I = 0; I < DK / 16; ++I)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) S[I][r] = a.s0 ? a.s0[((size_t)bh * DK + 16 * I + 4 * g + r) * dv + col] : 0.f;
+  for (int nc = 0; nc < NC; ++nc) {
+    const ChunkGeom cg = chunk_geom(bh * NC + nc, NC, a.H, a.T);
+    float* ch = a.ws + (size_t)(bh * NC + nc) * L.total;
+    const size_t kb = row0(cg, a.T, a.H, DK), ks = (size_t)a.H * DK;
+    const size_t vb = row0(cg, a.T, a.H, dv), vs = (size_t)a.H * dv;
+    const size_t bb = ((size_t)cg.b * a.T + cg.t0) * a.H + cg.h;
+    __syncthreads();  // the previous chunk's LDS reads are done
+    // M; W; (K o rho)^T; diag(beta) V (so that M (beta o V) = Mt V); gamma_last
+#pragma unroll
+    for (int it = 0; it < C * C / 4 / NT; ++it) {
+      const int x = tid + it * NT, i = x / (C / 4), j = 4 * (x % (C / 4));
+      *(float4*)(sM + i * LM + j) = *(const float4*)(ch + L.M + i * C + j);
+    }
+#pragma unroll
+    for (int it = 0; it < C * DK / 4 / NT; ++it) {
+      const int x = tid + it * NT, i = x / (DK / 4), c = 4 * (x % (DK / 4));
+      *(float4*)(sW + i * LW + c) = *(const float4*)(ch + L.W + i * DK + c);
+      const float4 kv = i < cg.len ? ld4<T>(a.k, kb + i * ks + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 rv = *(const float4*)(ch + L.rho + i * DK + c);
+      sKrT[(c + 0) * LM + i] = kv.x * rv.x;
+      sKrT[(c + 1) * LM + i] = kv.y * rv.y;
+      sKrT[(c + 2) * LM + i] = kv.z * rv.z;
+      sKrT[(c + 3) * LM + i] = kv.w * rv.w;
+    }
+#pragma unroll
+    for (int it = 0; it < C * VTW / 4 / NT; ++it) {
+      const int x = tid + it * NT, j = x / (VTW / 4), c = 4 * (x % (VTW / 4));
+      float4 vv = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j < cg.len) {
+        vv = ld4<T>(a.v, vb + j * vs + v0 + c);
+        const float bt = Elem<T>::load(a.beta, bb + (size_t)j * a.H);
+        vv.x *= bt;
+        vv.y *= bt;
+        vv.z *= bt;
+        vv.w *= bt;
+      }
+      *(float4*)(sV + j * LV + c) = vv;
+    }
+    for (int c = tid; c < DK; c += NT) sGl[c] = ch[L.gam + (C - 1) * DK + c];
     __syncthreads();
-    if (n + 1 < NC) {
+#pragma unroll
+    for (int I = 0; I < DK / 16; ++I)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ch[L.S + (16 * I + 4 * g + r) * dv + col] = S[I][r];
+    // Delta = M (beta o V) - W S
+    f32x4_t Dl[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      f32x4_t acc = zero4f();
+      const float* mrow = sM + (16 * I + n) * LM;
+#pragma unroll
+      for (int k0 = 0; k0 < C; k0 += 16)
+        mm16(acc, mrow, k0, [&](int t) { return sV[(k0 + 4 * g + t) * LV + 16 * wave + n]; });
+      const float* wrow = sW + (16 * I + n) * LW;
+#pragma unroll
+      for (int kt = 0; kt < DK / 16; ++kt) mm16(acc, wrow, 16 * kt, [&](int t) { return S[kt][t]; }, -1.f);
+      Dl[I] = acc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ch[L.DL + (16 * I + 4 * g + r) * dv + col] = acc[r];
+    }
+    if (nc + 1 < NC) {
       // S' = gamma_L o S + (K o rho)^T Delta
-      float* Sn = sS[cur ^ 1];
-      wg_mm(
-          dk / 16, VT / 16, C, [&](int c, int j) { return K.at(j, c) * ch[L.rho + j * dk + c]; },
-          [&](int j, int col) { return sDl[j * VT + col]; },
-          [&](int c, int col, float x) { Sn[c * VT + col] = ch[L.gam + (C - 1) * dk + c] * S[c * VT + col] + x; });
-      __syncthreads();
-      cur ^= 1;
+#pragma unroll
+      for (int I = 0; I < DK / 16; ++I) {
+        f32x4_t acc = zero4f();
+        const float* krow = sKrT + (16 * I + n) * LM;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) mm16(acc, krow, 16 * kt, [&](int t) { return Dl[kt][t]; });
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[I][r] = sGl[16 * I + 4 * g + r] * S[I][r] + acc[r];
+      }
     }
   }
 }
 
-// ---------------------------------------------------------------------------------------
-// bwd_adjoint_kernel: one workgroup per (b, h, value tile), chunks in reverse.  Writes the
-// end-state adjoint dS'_n and dDelta_n of every chunk, and dS_0.
-template <typename T, int VT>
+// bwd_adjoint_kernel: chunks in reverse; writes the end-state adjoint dS'_n and dDelta_n
+// of every chunk, and dS_0.
+template <typename T, int DK>
 __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC) {
-  const int tid = threadIdx.x, dk = a.Dk, dv = a.Dv, ntile = dv / VT;
-  const BwdLayout L(dk, dv);
-  const int bh = blockIdx.x / ntile, v0 = (blockIdx.x % ntile) * VT;
-  __shared__ float sS[2][128 * VT];
-  __shared__ float sDd[C * VT];
-  for (int x = tid; x < dk * VT; x += NT) {
-    const int c = x / VT, j = x % VT;
-    sS[0][x] = a.dsT ? a.dsT[((size_t)bh * dk + c) * dv + v0 + j] : 0.f;
-  }
-  __syncthreads();
-  int cur = 0;
-  for (int n = NC - 1; n >= 0; --n) {
-    const ChunkGeom cg = chunk_geom(bh * NC + n, NC, a.H, a.T);
-    float* ch = a.ws + (size_t)(bh * NC + n) * L.total;
-    const Rows<T> DO{a.dO, row0(cg, a.T, a.H, dv), (size_t)a.H * dv, cg.len};
-    const Rows<T> Q{a.q, row0(cg, a.T, a.H, dk), (size_t)a.H * dk, cg.len};
-    const Rows<T> K{a.k, Q.base, Q.stride, cg.len};
-    const float* dS = sS[cur];
-    for (int x = tid; x < dk * VT; x += NT) ch[L.DS + (x / VT) * dv + v0 + x % VT] = dS[x];
-    // dDelta = (K o rho) dS' + A^T dO   (K = dk + C)
-    wg_mm(
-        C / 16, VT / 16, dk + C,
-        [&](int i, int kk) { return kk < dk ? K.at(i, kk) * ch[L.rho + i * dk + kk] : ch[L.A + (kk - dk) * C + i]; },
-        [&](int kk, int j) { return kk < dk ? dS[kk * VT + j] : DO.at(kk - dk, v0 + j); },
-        [&](int i, int j, float x) {
-          sDd[i * VT + j] = x;
-          ch[L.DDL + i * dv + v0 + j] = x;
-        });
+  constexpr int LK = DK + 4, LM = C + 4, LV = VTW + 4;
+  __shared__ float sKr[C * LK], sAT[C * LM], sQgT[DK * LM], sWT[DK * LM], sO[C * LV], sGl[DK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, g = lane >> 4;
+  const int dv = a.Dv, ntile = dv / VTW, bh = blockIdx.x / ntile, v0 = (blockIdx.x % ntile) * VTW;
+  const int col = v0 + 16 * wave + n;
+  const BwdLayout L(DK, dv);
+  f32x4_t dS[DK / 16];
+#pragma unroll
+  for (int I = 0; I < DK / 16; ++I)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dS[I][r] = a.dsT ? a.dsT[((size_t)bh * DK + 16 * I + 4 * g + r) * dv + col] : 0.f;
+  for (int nc = NC - 1; nc >= 0; --nc) {
+    const ChunkGeom cg = chunk_geom(bh * NC + nc, NC, a.H, a.T);
+    float* ch = a.ws + (size_t)(bh * NC + nc) * L.total;
+    const size_t kb = row0(cg, a.T, a.H, DK), ks = (size_t)a.H * DK;
+    const size_t vb = row0(cg, a.T, a.H, dv), vs = (size_t)a.H * dv;
     __syncthreads();
-    // dS = gamma_L o dS' + (Q o gamma)^T dO - W^T dDelta   (K = 2 C)
-    float* dSn = sS[cur ^ 1];
-    wg_mm(
-        dk / 16, VT / 16, 2 * C,
-        [&](int c, int kk) {
-          return kk < C ? Q.at(kk, c) * ch[L.gam + kk * dk + c] : -ch[L.W + (kk - C) * dk + c];
-        },
-        [&](int kk, int j) { return kk < C ? DO.at(kk, v0 + j) : sDd[(kk - C) * VT + j]; },
-        [&](int c, int j, float x) { dSn[c * VT + j] = ch[L.gam + (C - 1) * dk + c] * dS[c * VT + j] + x; });
+    // K o rho; A^T; (Q o gamma)^T; W^T; dO; gamma_last
+#pragma unroll
+    for (int it = 0; it < C * DK / 4 / NT; ++it) {
+      const int x = tid + it * NT, i = x / (DK / 4), c = 4 * (x % (DK / 4));
+      const bool in = i < cg.len;
+      const float4 kv = in ? ld4<T>(a.k, kb + i * ks + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 qv = in ? ld4<T>(a.q, kb + i * ks + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 rv = *(const float4*)(ch + L.rho + i * DK + c);
+      const float4 gv = *(const float4*)(ch + L.gam + i * DK + c);
+      const float4 wv = *(const float4*)(ch + L.W + i * DK + c);
+      *(float4*)(sKr + i * LK + c) = make_float4(kv.x * rv.x, kv.y * rv.y, kv.z * rv.z, kv.w * rv.w);
+      sQgT[(c + 0) * LM + i] = qv.x * gv.x;
+      sQgT[(c + 1) * LM + i] = qv.y * gv.y;
+      sQgT[(c + 2) * LM + i] = qv.z * gv.z;
+      sQgT[(c + 3) * LM + i] = qv.w * gv.w;
+      sWT[(c + 0) * LM + i] = wv.x;
+      sWT[(c + 1) * LM + i] = wv.y;
+      sWT[(c + 2) * LM + i] = wv.z;
+      sWT[(c + 3) * LM + i] = wv.w;
+    }
+#pragma unroll
+    for (int it = 0; it < C * C / 4 / NT; ++it) {
+      const int x = tid + it * NT, j = x / (C / 4), i = 4 * (x % (C / 4));
+      const float4 av = *(const float4*)(ch + L.A + j * C + i);
+      sAT[(i + 0) * LM + j] = av.x;
+      sAT[(i + 1) * LM + j] = av.y;
+      sAT[(i + 2) * LM + j] = av.z;
+      sAT[(i + 3) * LM + j] = av.w;
+    }
+#pragma unroll
+    for (int it = 0; it < C * VTW / 4 / NT; ++it) {
+      const int x = tid + it * NT, i = x / (VTW / 4), c = 4 * (x % (VTW / 4));
+      *(float4*)(sO + i * LV + c) = i < cg.len ? ld4<T>(a.dO, vb + i * vs + v0 + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    for (int c = tid; c < DK; c += NT) sGl[c] = ch[L.gam + (C - 1) * DK + c];
     __syncthreads();
-    cur ^= 1;
+#pragma unroll
+    for (int I = 0; I < DK / 16; ++I)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ch[L.DS + (16 * I + 4 * g + r) * dv + col] = dS[I][r];
+    // dDelta = (K o rho) dS' + A^T dO
+    f32x4_t dD[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      f32x4_t acc = zero4f();
+      const float* krow = sKr + (16 * I + n) * LK;
+#pragma unroll
+      for (int kt = 0; kt < DK / 16; ++kt) mm16(acc, krow, 16 * kt, [&](int t) { return dS[kt][t]; });
+      const float* arow = sAT + (16 * I + n) * LM;
+#pragma unroll
+      for (int k0 = 0; k0 < C; k0 += 16)
+        mm16(acc, arow, k0, [&](int t) { return sO[(k0 + 4 * g + t) * LV + 16 * wave + n]; });
+      dD[I] = acc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ch[L.DDL + (16 * I + 4 * g + r) * dv + col] = acc[r];
+    }
+    // dS = gamma_L o dS' + (Q o gamma)^T dO - W^T dDelta
+#pragma unroll
+    for (int I = 0; I < DK / 16; ++I) {
+      f32x4_t acc = zero4f();
+      const float* qrow = sQgT + (16 * I + n) * LM;
+#pragma unroll
+      for (int k0 = 0; k0 < C; k0 += 16)
+        mm16(acc, qrow, k0, [&](int t) { return sO[(k0 + 4 * g + t) * LV + 16 * wave + n]; });
+      const float* wrow = sWT + (16 * I + n) * LM;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) mm16(acc, wrow, 16 * kt, [&](int t) { return dD[kt][t]; }, -1.f);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dS[I][r] = sGl[16 * I + 4 * g + r] * dS[I][r] + acc[r];
+    }
   }
-  if (a.ds0)
-    for (int x = tid; x < dk * VT; x += NT) a.ds0[((size_t)bh * dk + x / VT) * dv + v0 + x % VT] = sS[cur][x];
+  if (a.ds0) {
+#pragma unroll
+    for (int I = 0; I < DK / 16; ++I)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a.ds0[((size_t)bh * DK + 16 * I + 4 * g + r) * dv + col] = dS[I][r];
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -424,7 +608,11 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a, int NC) {
   // dgamma_L = rowsum(dS' o S)
   for (int c = tid; c < dk; c += NT) {
     float s = 0.f;
-    for (int v = 0; v < dv; ++v) s += DS[c * dv + v] * S[c * dv + v];
+#pragma unroll 16
+    for (int v = 0; v < dv; v += 4) {
+      const float4 x = *(const float4*)(DS + c * dv + v), y = *(const float4*)(S + c * dv + v);
+      s += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+    }
     sGl[c] = s;
   }
   __syncthreads();
@@ -460,6 +648,7 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a, int NC) {
   // dbeta += rowsum(dT o D); dD = diag(beta) dT (in place)
   for (int i = tid; i < C; i += NT) {
     float s = 0.f;
+#pragma unroll 16
     for (int j = 0; j < i; ++j) s += sdT[i][j] * ch[L.D + i * C + j];
     if (i < cg.len) a.dbeta[ob + (size_t)i * a.H] = sdB[i] + s;
     for (int j = 0; j < i; ++j) sdT[i][j] *= sB[i];
@@ -552,7 +741,14 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a, int NC) {
     // gate gradient.  g_i = sum over j < s (and the start-state column j = -1) of the
     // pair weights times r(s-1, j), for rows i >= s.
     float bvs = 0.f;  // sum_{j < s} bv_j r(s-1, j)
-    for (int j = 0; j < s; ++j) bvs += BV[j * dk + c] * SIG[j * dk + c] * between(PIB, dk, j / SUB, Mb, c);
+    for (int J = 0; J < Mb; ++J) {
+      float part = 0.f;
+#pragma unroll
+      for (int r = 0; r < SUB; ++r) part += BV[(J * SUB + r) * dk + c] * SIG[(J * SUB + r) * dk + c];
+      float w = 1.f;
+      for (int x = J + 1; x < Mb; ++x) w *= pib[x];
+      bvs += part * w;
+    }
     const float dgl = sGl[c];
     auto g_at = [&](int i) {
       float g = AV[i * dk + c] * gs;
@@ -567,7 +763,16 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a, int NC) {
     if (Mb < NB - 1) {
       // rows below the block fold into its last row: X = sum_{i > e} r(i, e) g_i
       float x = 0.f;
-      for (int i = C - 1; i >= s + SUB; --i) x = AL.at(i, c, 1.f) * (g_at(i) + x);
+      for (int I = NB - 1; I > Mb; --I) {
+        float gv[SUB], av[SUB];
+#pragma unroll
+        for (int r = 0; r < SUB; ++r) {
+          gv[r] = g_at(I * SUB + r);
+          av[r] = AL.at(I * SUB + r, c, 1.f);
+        }
+#pragma unroll
+        for (int r = SUB - 1; r >= 0; --r) x = av[r] * (gv[r] + x);
+      }
       u[SUB - 1] += x;
 #pragma unroll
       for (int r = 0; r < SUB; ++r) f[r] = kv[r] * F[(s + r) * dk + c] + BV[(s + r) * dk + c] * rend;
@@ -592,25 +797,22 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a, int NC) {
 }
 
 // ---------------------------------------------------------------------------------------
-template <typename T, int VT>
-static hipError_t launch_bwd_vt(const BwdArgs& a, int NC) {
-  const int BH = a.B * a.H;
+template <typename T, int DK>
+static hipError_t launch_bwd_dk(const BwdArgs& a, int NC) {
+  const int BH = a.B * a.H, walks = BH * (a.Dv / VTW);
   hipStream_t st = (hipStream_t)a.stream;
   if (NC > 0) {
     hipLaunchKernelGGL((bwd_records_kernel<T>), dim3(BH * NC), dim3(NT), 0, st, a, NC);
-    hipLaunchKernelGGL((bwd_state_kernel<T, VT>), dim3(BH * (a.Dv / VT)), dim3(NT), 0, st, a, NC);
+    hipLaunchKernelGGL((bwd_state_kernel<T, DK>), dim3(walks), dim3(NT), 0, st, a, NC);
   }
-  hipLaunchKernelGGL((bwd_adjoint_kernel<T, VT>), dim3(BH * (a.Dv / VT)), dim3(NT), 0, st, a, NC);
+  hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK>), dim3(walks), dim3(NT), 0, st, a, NC);
   if (NC > 0) hipLaunchKernelGGL((bwd_grads_kernel<T>), dim3(BH * NC), dim3(NT), 0, st, a, NC);
   return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t launch_bwd_t(const BwdArgs& a, int NC) {
-  const long wgs = (long)a.B * a.H * a.Dv;
-  if (wgs / 64 >= 1024) return launch_bwd_vt<T, 64>(a, NC);
-  if (wgs / 32 >= 1024) return launch_bwd_vt<T, 32>(a, NC);
-  return launch_bwd_vt<T, 16>(a, NC);
+  return a.Dk == 64 ? launch_bwd_dk<T, 64>(a, NC) : launch_bwd_dk<T, 128>(a, NC);
 }
 
 hipError_t launch_bwd(const BwdArgs& a) {

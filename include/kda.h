@@ -252,8 +252,9 @@ int kda_sfda_decode_tokens(const kda_shape* shape, const void* q, const void* k,
  *   workspace       : kda_chunk_bwd_workspace_size(shape) bytes of device memory,
  *                     256-byte aligned (about 740 KB per chunk of 64 tokens and head at
  *                     dk = dv = 128); its contents on entry do not matter.
- * Supported: dk, dv in {64, 128}, bf16 or fp32 inputs, chunk 0 or 64.  Inputs need the
- * alignment of their element type; outputs and the states 16 bytes.  No output may
+ * Supported: dk, dv in {64, 128}, bf16 or fp32 inputs, chunk 0 or 64.  q, k, v, alpha,
+ * d_o, the outputs and the states need 16-byte alignment, beta that of its element type
+ * (KDA_ERR_ALIGN otherwise).  No output may
  * overlap an input, another output or the workspace (KDA_ERR_ALIAS); a NULL required
  * pointer is KDA_ERR_NULL (unless B*T*H == 0), a short workspace KDA_ERR_WORKSPACE.
  * T == 0 writes d_initial_state = d_final_state (or zeros).

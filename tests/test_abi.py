@@ -322,6 +322,7 @@ def test_bwd_argument_errors(L):
     assert bwd(ws=_p(16, off=16)) == ALIGN         # the workspace wants 256-byte alignment
     assert bwd(dq=_p(10, off=4)) == ALIGN
     assert bwd(a=_p(3, off=1)) == ALIGN
+    assert bwd(q=_p(0, off=8)) == ALIGN            # q moves in 16-byte vectors
     assert bwd(dq=_p(3)) == ALIAS                  # gradient over an input
     assert bwd(dbeta=_p(10, off=64)) == ALIAS      # two outputs overlap
     assert bwd(ws=_p(5)) == ALIAS                  # workspace over d_o
