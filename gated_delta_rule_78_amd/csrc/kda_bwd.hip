@@ -550,191 +550,407 @@ __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC) {
 }
 
 // ---------------------------------------------------------------------------------------
-// bwd_grads_kernel: one workgroup per (b, h, chunk).
-template <typename T>
+// bwd_grads_kernel: one workgroup per (b, h, chunk), in five phases:
+//   A  products over the value dimension, by key-channel tile: a wave holds its 16
+//      channels' rows of S and dS' as B fragments in registers and runs d(Q o gamma),
+//      dW and d(K o rho) against dO, dDelta and Delta staged in LDS; dgamma_L comes from
+//      the same registers;
+//   B  dA, dV, dMt, d(K o gamma) from LDS (dW staged where dO and Delta were);
+//   C  dbeta, X = dMt Mt^T, dT and dD in LDS;
+//   D  the block-anchored products PA, PD, F with their B operands staged in LDS;
+//   E  per (channel, block): the in-block decayed sums, dq and dk, the gate gradient.
+namespace {
+__device__ __forceinline__ float f4c(const float4& v, int t) {
+  return t == 0 ? v.x : (t == 1 ? v.y : (t == 2 ? v.z : v.w));
+}
+__device__ __forceinline__ float4 mul4(const float4& a, const float4& b) {
+  return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w);
+}
+__device__ __forceinline__ void mfma4(f32x4_t& acc, const float (&av)[4], const float (&bv)[4]) {
+#ifndef KDA_HOST_PASS
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[t], bv[t], acc, 0, 0, 0);
+#endif
+}
+}  // namespace
+
+template <typename T, int DK, int DV>
 __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a, int NC) {
-  const int tid = threadIdx.x, dk = a.Dk, dv = a.Dv;
-  const BwdLayout L(dk, dv);
+  constexpr int LV = DV + 4, LK = DK + 4, LC = C + 1;
+  constexpr int RSZ = (3 * C * LV > 3 * C * LK) ? 3 * C * LV : 3 * C * LK;
+  static_assert(LK <= 2 * LV, "dW must fit where dO and Delta were");
+  __shared__ float sR[RSZ];  // staging region, reused by every phase
+  __shared__ float sM[C * LC], sdA[C * LC], sdT[C * LC];  // sdT: dMt, then dT, then dD
+  __shared__ float sB[C], sdB[C], sGl[DK], sPib[NB * DK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, g = lane >> 4;
+  const BwdLayout L(DK, DV);
   const ChunkGeom cg = chunk_geom(blockIdx.x, NC, a.H, a.T);
+  const int len = cg.len;
   float* ch = a.ws + (size_t)blockIdx.x * L.total;
-  const Rows<T> Q{a.q, row0(cg, a.T, a.H, dk), (size_t)a.H * dk, cg.len};
-  const Rows<T> K{a.k, Q.base, Q.stride, cg.len};
-  const Rows<T> AL{a.alpha, Q.base, Q.stride, cg.len};
-  const Rows<T> V{a.v, row0(cg, a.T, a.H, dv), (size_t)a.H * dv, cg.len};
-  const Rows<T> DO{a.dO, V.base, V.stride, cg.len};
-  const size_t ob = ((size_t)cg.b * a.T + cg.t0) * a.H + cg.h;  // beta / dbeta row 0
-  const Rows<T> BE{a.beta, ob, (size_t)a.H, cg.len};
-  const size_t okb = Q.base, ovb = V.base;                      // dq / dk / dalpha and dv row 0
-  const float *GAM = ch + L.gam, *RHO = ch + L.rho, *PIN = ch + L.pin, *SIG = ch + L.sig, *PIB = ch + L.pib;
-  const float *S = ch + L.S, *DL = ch + L.DL, *DS = ch + L.DS, *DD = ch + L.DDL;
-  float *AV = ch + L.AV, *BV = ch + L.BV, *DW = ch + L.DW, *F = ch + L.F, *PA = ch + L.PA, *PD = ch + L.PD;
+  const size_t kb = row0(cg, a.T, a.H, DK), ks = (size_t)a.H * DK;
+  const size_t vb = row0(cg, a.T, a.H, DV), vs = (size_t)a.H * DV;
+  const size_t bb = ((size_t)cg.b * a.T + cg.t0) * a.H + cg.h;
+  const float *GAM = ch + L.gam, *RHO = ch + L.rho, *PIN = ch + L.pin, *SIG = ch + L.sig;
+  const float *S = ch + L.S, *DS = ch + L.DS;
+  float *AV = ch + L.AV, *BV = ch + L.BV, *DWg = ch + L.DW, *F = ch + L.F, *PA = ch + L.PA, *PD = ch + L.PD;
+  const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto in4 = [&](const void* p, int i, int c) { return i < len ? ld4<T>(p, kb + i * ks + c) : z4; };
+  auto in1 = [&](const void* p, int i, int c) { return i < len ? Elem<T>::load(p, kb + i * ks + c) : 0.f; };
+  auto between = [&](int J, int I, int c) {
+    float w = 1.f;
+    for (int x = J + 1; x < I; ++x) w *= sPib[x * DK + c];
+    return w;
+  };
 
-  __shared__ float sdA[C][C + 1], sdT[C][C + 1], sdM[C][C + 1], sX[C][C + 1], sM[C][C + 1];
-  __shared__ float sB[C], sdB[C], sGl[128];
-
-  for (int x = tid; x < C * C; x += NT) sM[x / C][x % C] = ch[L.M + x];
-  for (int i = tid; i < C; i += NT) sB[i] = BE.at(i, 0);
+  // ---- stage dO, Delta, dDelta; M, beta, the block totals
+  float *RO = sR, *RL = sR + C * LV, *RD = sR + 2 * C * LV;
+#pragma unroll
+  for (int it = 0; it < C * DV / 4 / NT; ++it) {
+    const int x = tid + it * NT, i = x / (DV / 4), v = 4 * (x % (DV / 4));
+    *(float4*)(RO + i * LV + v) = i < len ? ld4<T>(a.dO, vb + i * vs + v) : z4;
+    *(float4*)(RL + i * LV + v) = *(const float4*)(ch + L.DL + i * DV + v);
+    *(float4*)(RD + i * LV + v) = *(const float4*)(ch + L.DDL + i * DV + v);
+  }
+  for (int x = tid; x < C * C; x += NT) sM[(x / C) * LC + x % C] = ch[L.M + x];
+  for (int i = tid; i < C; i += NT) sB[i] = i < len ? Elem<T>::load(a.beta, bb + (size_t)i * a.H) : 0.f;
+  for (int x = tid; x < NB * DK; x += NT) sPib[x] = ch[L.pib + x];
   __syncthreads();
 
-  // ---- products over the value dimension
-  // d(Q o gamma) = dO S^T: dq = . o gamma, av = . o q
-  wg_mm(
-      C / 16, dk / 16, dv, [&](int i, int v) { return DO.at(i, v); }, [&](int v, int c) { return S[c * dv + v]; },
-      [&](int i, int c, float x) {
-        if (i < cg.len) a.dq[okb + (size_t)i * Q.stride + c] = x * GAM[i * dk + c];
-        AV[i * dk + c] = x * Q.at(i, c);
-      });
-  // d(K o rho) = Delta dS'^T: dk = . o rho, bv = . o k
-  wg_mm(
-      C / 16, dk / 16, dv, [&](int i, int v) { return DL[i * dv + v]; }, [&](int v, int c) { return DS[c * dv + v]; },
-      [&](int i, int c, float x) {
-        if (i < cg.len) a.dk[okb + (size_t)i * Q.stride + c] = x * RHO[i * dk + c];
-        BV[i * dk + c] = x * K.at(i, c);
-      });
-  // dW = -dDelta S^T
-  wg_mm(
-      C / 16, dk / 16, dv, [&](int i, int v) { return DD[i * dv + v]; }, [&](int v, int c) { return S[c * dv + v]; },
-      [&](int i, int c, float x) { DW[i * dk + c] = -x; });
-  // dA = (dO Delta^T) o low
-  wg_mm(
-      C / 16, C / 16, dv, [&](int i, int v) { return DO.at(i, v); }, [&](int v, int j) { return DL[j * dv + v]; },
-      [&](int i, int j, float x) { sdA[i][j] = j <= i ? x : 0.f; });
-  // dV = Mt^T dDelta
-  wg_mm(
-      C / 16, dv / 16, C, [&](int j, int i) { return sM[i][j] * sB[j]; }, [&](int i, int v) { return DD[i * dv + v]; },
-      [&](int j, int v, float x) {
-        if (j < cg.len) a.dv[ovb + (size_t)j * V.stride + v] = x;
-      });
-  // dgamma_L = rowsum(dS' o S)
-  for (int c = tid; c < dk; c += NT) {
-    float s = 0.f;
-#pragma unroll 16
-    for (int v = 0; v < dv; v += 4) {
-      const float4 x = *(const float4*)(DS + c * dv + v), y = *(const float4*)(S + c * dv + v);
-      s += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+  // ---- A: d(Q o gamma) = dO S^T, dW = -dDelta S^T, d(K o rho) = Delta dS'^T, dgamma_L
+  for (int ct = wave; ct < DK / 16; ct += NT / 64) {
+    const int c = 16 * ct + n;
+    float4 sf[DV / 16], df[DV / 16];
+#pragma unroll
+    for (int u = 0; u < DV / 16; ++u) {
+      sf[u] = *(const float4*)(S + c * DV + 16 * u + 4 * g);
+      df[u] = *(const float4*)(DS + c * DV + 16 * u + 4 * g);
     }
-    sGl[c] = s;
+    float gm[4][4], rh[4][4], qq[4][4], kk[4][4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * I + 4 * g + r;
+        gm[I][r] = GAM[i * DK + c];
+        rh[I][r] = RHO[i * DK + c];
+        qq[I][r] = in1(a.q, i, c);
+        kk[I][r] = in1(a.k, i, c);
+      }
+    float part = 0.f;
+#pragma unroll
+    for (int u = 0; u < DV / 16; ++u)
+      part += sf[u].x * df[u].x + sf[u].y * df[u].y + sf[u].z * df[u].z + sf[u].w * df[u].w;
+    part += __shfl_xor(part, 16);
+    part += __shfl_xor(part, 32);
+    if (g == 0) sGl[c] = part;
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      f32x4_t aq = zero4f(), aw = zero4f(), ar = zero4f();
+      const float *ro = RO + (16 * I + n) * LV, *rd = RD + (16 * I + n) * LV, *rl = RL + (16 * I + n) * LV;
+#pragma unroll
+      for (int u = 0; u < DV / 16; ++u) {
+        mm16(aq, ro, 16 * u, [&](int t) { return f4c(sf[u], t); });
+        mm16(aw, rd, 16 * u, [&](int t) { return f4c(sf[u], t); });
+        mm16(ar, rl, 16 * u, [&](int t) { return f4c(df[u], t); });
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * I + 4 * g + r;
+        AV[i * DK + c] = aq[r] * qq[I][r];
+        BV[i * DK + c] = ar[r] * kk[I][r];
+        DWg[i * DK + c] = -aw[r];
+        if (i < len) {
+          a.dq[kb + i * ks + c] = aq[r] * gm[I][r];
+          a.dk[kb + i * ks + c] = ar[r] * rh[I][r];
+        }
+      }
+    }
+  }
+
+  // ---- B: dA = (dO Delta^T) o low;  dV = Mt^T dDelta
+  for (int job = wave; job < 16 + 4 * (DV / 16); job += NT / 64) {
+    if (job < 16) {
+      const int I = job / 4, J = job % 4;
+      f32x4_t acc = zero4f();
+      if (J <= I) {
+        const float *ro = RO + (16 * I + n) * LV, *rl = RL + (16 * J + n) * LV;
+#pragma unroll
+        for (int u = 0; u < DV / 16; ++u) mm16(acc, ro, 16 * u, [&](int t) { return rl[16 * u + 4 * g + t]; });
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * I + 4 * g + r, j = 16 * J + n;
+        sdA[i * LC + j] = j <= i ? acc[r] : 0.f;
+      }
+    } else {
+      const int jj = job - 16, J = jj / (DV / 16), vt = jj % (DV / 16);
+      f32x4_t acc = zero4f();
+#pragma unroll
+      for (int k0 = 0; k0 < C; k0 += 16) {
+        float av[4], bv[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int i = k0 + 4 * g + t;
+          av[t] = sM[i * LC + 16 * J + n] * sB[16 * J + n];
+          bv[t] = RD[i * LV + 16 * vt + n];
+        }
+        mfma4(acc, av, bv);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * J + 4 * g + r;
+        if (j < len) a.dv[vb + j * vs + 16 * vt + n] = acc[r];
+      }
+    }
+  }
+  __syncthreads();
+  float* RW = sR;  // dW [C][LK], where dO and Delta were
+#pragma unroll
+  for (int it = 0; it < C * DK / 4 / NT; ++it) {
+    const int x = tid + it * NT, i = x / (DK / 4), c = 4 * (x % (DK / 4));
+    *(float4*)(RW + i * LK + c) = *(const float4*)(DWg + i * DK + c);
+  }
+  __syncthreads();
+  // dMt = (dDelta V^T + dW (K o gamma)^T) o low;  d(K o gamma) = Mt^T dW
+  for (int job = wave; job < 16 + 4 * (DK / 16); job += NT / 64) {
+    if (job < 16) {
+      const int I = job / 4, J = job % 4, j = 16 * J + n;
+      f32x4_t acc = zero4f();
+      if (J <= I) {
+        float4 vv[DV / 16], kg[DK / 16];
+#pragma unroll
+        for (int u = 0; u < DV / 16; ++u) vv[u] = j < len ? ld4<T>(a.v, vb + j * vs + 16 * u + 4 * g) : z4;
+#pragma unroll
+        for (int u = 0; u < DK / 16; ++u)
+          kg[u] = mul4(in4(a.k, j, 16 * u + 4 * g), *(const float4*)(GAM + j * DK + 16 * u + 4 * g));
+        const float *rd = RD + (16 * I + n) * LV, *rw = RW + (16 * I + n) * LK;
+#pragma unroll
+        for (int u = 0; u < DV / 16; ++u) mm16(acc, rd, 16 * u, [&](int t) { return f4c(vv[u], t); });
+#pragma unroll
+        for (int u = 0; u < DK / 16; ++u) mm16(acc, rw, 16 * u, [&](int t) { return f4c(kg[u], t); });
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * I + 4 * g + r;
+        sdT[i * LC + j] = j <= i ? acc[r] : 0.f;
+      }
+    } else {
+      const int jj = job - 16, J = jj / (DK / 16), ct = jj % (DK / 16), c = 16 * ct + n;
+      f32x4_t acc = zero4f();
+#pragma unroll
+      for (int k0 = 0; k0 < C; k0 += 16) {
+        float av[4], bv[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int i = k0 + 4 * g + t;
+          av[t] = sM[i * LC + 16 * J + n] * sB[16 * J + n];
+          bv[t] = RW[i * LK + c];
+        }
+        mfma4(acc, av, bv);
+      }
+      float kv[4], gv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * J + 4 * g + r;
+        kv[r] = in1(a.k, j, c);
+        gv[r] = GAM[j * DK + c];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * J + 4 * g + r;
+        AV[j * DK + c] += acc[r] * kv[r];
+        if (j < len) a.dk[kb + j * ks + c] += acc[r] * gv[r];
+      }
+    }
   }
   __syncthreads();
 
-  // ---- dMt = (dDelta V^T + dW (K o gamma)^T) o low;  d(K o gamma) = Mt^T dW
-  wg_mm(
-      C / 16, C / 16, dv + dk, [&](int i, int kk) { return kk < dv ? DD[i * dv + kk] : DW[i * dk + kk - dv]; },
-      [&](int kk, int j) { return kk < dv ? V.at(j, kk) : K.at(j, kk - dv) * GAM[j * dk + kk - dv]; },
-      [&](int i, int j, float x) { sdM[i][j] = j <= i ? x : 0.f; });
-  wg_mm(
-      C / 16, dk / 16, C, [&](int j, int i) { return sM[i][j] * sB[j]; }, [&](int i, int c) { return DW[i * dk + c]; },
-      [&](int j, int c, float x) {
-        if (j < cg.len) a.dk[okb + (size_t)j * Q.stride + c] += x * GAM[j * dk + c];
-        AV[j * dk + c] += x * K.at(j, c);
-      });
-  __syncthreads();
-
-  // ---- dbeta (first part) = colsum(dMt o M);  X = dMt Mt^T
+  // ---- C: dbeta = colsum(dMt o M) + rowsum(dT o D);  X = dMt Mt^T;  dT = -(M^T X) o strict-low
   for (int j = tid; j < C; j += NT) {
     float s = 0.f;
-    for (int i = j; i < C; ++i) s += sdM[i][j] * sM[i][j];
+    for (int i = j; i < C; ++i) s += sdT[i * LC + j] * sM[i * LC + j];
     sdB[j] = s;
   }
-  wg_mm(
-      C / 16, C / 16, C, [&](int i, int kk) { return sdM[i][kk]; }, [&](int kk, int j) { return sM[j][kk] * sB[kk]; },
-      [&](int i, int j, float x) { sX[i][j] = x; });
+  float* RX = sR;  // X [C][LC]
+  for (int job = wave; job < 16; job += NT / 64) {
+    const int I = job / 4, J = job % 4;
+    f32x4_t acc = zero4f();
+#pragma unroll
+    for (int k0 = 0; k0 < C; k0 += 16) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int kx = k0 + 4 * g + t;
+        av[t] = sdT[(16 * I + n) * LC + kx];
+        bv[t] = sM[(16 * J + n) * LC + kx] * sB[kx];
+      }
+      mfma4(acc, av, bv);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) RX[(16 * I + 4 * g + r) * LC + 16 * J + n] = acc[r];
+  }
   __syncthreads();
-  // dT = -(M^T X) o strict-low
-  wg_mm(
-      C / 16, C / 16, C, [&](int i, int kk) { return sM[kk][i]; }, [&](int kk, int j) { return sX[kk][j]; },
-      [&](int i, int j, float x) { sdT[i][j] = j < i ? -x : 0.f; });
+  for (int job = wave; job < 16; job += NT / 64) {
+    const int I = job / 4, J = job % 4;
+    f32x4_t acc = zero4f();
+    if (J <= I) {
+#pragma unroll
+      for (int k0 = 0; k0 < C; k0 += 16) {
+        float av[4], bv[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int kx = k0 + 4 * g + t;
+          av[t] = sM[kx * LC + 16 * I + n];
+          bv[t] = RX[kx * LC + 16 * J + n];
+        }
+        mfma4(acc, av, bv);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * I + 4 * g + r, j = 16 * J + n;
+      sdT[i * LC + j] = j < i ? -acc[r] : 0.f;
+    }
+  }
   __syncthreads();
-  // dbeta += rowsum(dT o D); dD = diag(beta) dT (in place)
   for (int i = tid; i < C; i += NT) {
     float s = 0.f;
-#pragma unroll 16
-    for (int j = 0; j < i; ++j) s += sdT[i][j] * ch[L.D + i * C + j];
-    if (i < cg.len) a.dbeta[ob + (size_t)i * a.H] = sdB[i] + s;
-    for (int j = 0; j < i; ++j) sdT[i][j] *= sB[i];
+#pragma unroll 8
+    for (int j = 0; j < i; ++j) s += sdT[i * LC + j] * ch[L.D + i * C + j];
+    if (i < len) a.dbeta[bb + (size_t)i * a.H] = sdB[i] + s;
+    for (int j = 0; j < i; ++j) sdT[i * LC + j] *= sB[i];
   }
   __syncthreads();
-  float(*sdD)[C + 1] = sdT;
+  const float* sdD = sdT;
 
-  // ---- block-anchored products for the decayed sums
-  // PA^M = dA[>= s_M, < s_M] Khat^M, PD^M likewise with dD (M = 1..3), where
-  // Khat^M_j = k_j r(s_M - 1, j) = k_j sigma_j (blocks between)
-  for (int Mb = 1; Mb < NB; ++Mb) {
-    const int s = Mb * SUB;
-    for (int mat = 0; mat < 2; ++mat) {
-      float* out = (mat ? PD : PA) + (size_t)(Mb - 1) * C * dk;
-      wg_mm(
-          NB - Mb, dk / 16, s, [&](int i, int j) { return mat ? sdD[s + i][j] : sdA[s + i][j]; },
-          [&](int j, int c) { return K.at(j, c) * SIG[j * dk + c] * between(PIB, dk, j / SUB, Mb, c); },
-          [&](int i, int c, float x) { out[(s + i) * dk + c] = x; });
-    }
+  // ---- D: PA^M = dA[>= s_M, < s_M] Khat^M, PD^M likewise with dD (M = 1..3), with
+  // Khat^M_j = k_j sigma_j (blocks between); F^M_j = sum_{i > e_M} (dA_ij q_i + dD_ij k_i)
+  // r(i, e_M), r(i, e_M) = pi_i (blocks between) (M = 0..2)
+  float *RKS = sR, *RQP = sR + C * LK, *RKP = sR + 2 * C * LK;
+#pragma unroll
+  for (int it = 0; it < C * DK / 4 / NT; ++it) {
+    const int x = tid + it * NT, i = x / (DK / 4), c = 4 * (x % (DK / 4));
+    const float4 kv = in4(a.k, i, c), qv = in4(a.q, i, c);
+    const float4 sg = *(const float4*)(SIG + i * DK + c), pn = *(const float4*)(PIN + i * DK + c);
+    *(float4*)(RKS + i * LK + c) = mul4(kv, sg);
+    *(float4*)(RQP + i * LK + c) = mul4(qv, pn);
+    *(float4*)(RKP + i * LK + c) = mul4(kv, pn);
   }
-  // F^M_j = sum_{i > e_M} (dA_ij q_i + dD_ij k_i) r(i, e_M) for j in block M (M = 0..2),
-  // r(i, e_M) = pi_i (blocks between)
-  for (int Mb = 0; Mb < NB - 1; ++Mb) {
-    const int s = Mb * SUB, e1 = s + SUB, nM = C - e1;
-    wg_mm(
-        1, dk / 16, 2 * nM,
-        [&](int j, int kk) { return kk < nM ? sdA[e1 + kk][s + j] : sdD[e1 + kk - nM][s + j]; },
-        [&](int kk, int c) {
-          const int i = e1 + (kk < nM ? kk : kk - nM);
-          const float x = kk < nM ? Q.at(i, c) : K.at(i, c);
-          return x * PIN[i * dk + c] * between(PIB, dk, Mb, i / SUB, c);
-        },
-        [&](int j, int c, float x) { F[(s + j) * dk + c] = x; });
+  __syncthreads();
+  for (int job = wave; job < 12 * (DK / 16); job += NT / 64) {
+    const int ct = job % (DK / 16), p6 = (job / (DK / 16)) % 6, mat = job / (DK / 16) / 6;
+    // (M, I): (1,1) (1,2) (1,3) (2,2) (2,3) (3,3)
+    const int Mb = p6 < 3 ? 1 : (p6 < 5 ? 2 : 3), I = Mb + (p6 < 3 ? p6 : (p6 < 5 ? p6 - 3 : 0));
+    const int c = 16 * ct + n;
+    const float* src = mat ? sdD : sdA;
+    f32x4_t acc = zero4f();
+    for (int J = 0; J < Mb; ++J) {
+      const float w = between(J, Mb, c);
+      float av[4], bv[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int jx = 16 * J + 4 * g + t;
+        av[t] = src[(16 * I + n) * LC + jx];
+        bv[t] = RKS[jx * LK + c] * w;
+      }
+      mfma4(acc, av, bv);
+    }
+    float* out = (mat ? PD : PA) + (size_t)(Mb - 1) * C * DK;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) out[(16 * I + 4 * g + r) * DK + c] = acc[r];
+  }
+  for (int job = wave; job < 3 * (DK / 16); job += NT / 64) {
+    const int Mb = job / (DK / 16), ct = job % (DK / 16), s = 16 * Mb, c = 16 * ct + n;
+    f32x4_t acc = zero4f();
+    for (int I = Mb + 1; I < NB; ++I) {
+      const float w = between(Mb, I, c);
+      float av[4], bv[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int ix = 16 * I + 4 * g + t;
+        av[t] = sdA[ix * LC + s + n];
+        bv[t] = RQP[ix * LK + c] * w;
+      }
+      mfma4(acc, av, bv);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int ix = 16 * I + 4 * g + t;
+        av[t] = sdD[ix * LC + s + n];
+        bv[t] = RKP[ix * LK + c] * w;
+      }
+      mfma4(acc, av, bv);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) F[(s + 4 * g + r) * DK + c] = acc[r];
   }
   __syncthreads();
 
-  // ---- per (channel, block): the decayed sums' in-block parts, dq / dk, the gate gradient
-  for (int item = tid; item < dk * NB; item += NT) {
-    const int c = item % dk, Mb = item / dk, s = Mb * SUB;
-    float al[SUB], qv[SUB], kv[SUB];
+  // ---- E: stage q, k, alpha; per (channel, block) items
+  float *RQ = sR, *RK = sR + C * LK, *RA = sR + 2 * C * LK;
 #pragma unroll
-    for (int r = 0; r < SUB; ++r) {
-      al[r] = AL.at(s + r, c, 1.f);
-      qv[r] = Q.at(s + r, c);
-      kv[r] = K.at(s + r, c);
-    }
-    float pib[NB];
-#pragma unroll
-    for (int J = 0; J < NB; ++J) pib[J] = PIB[J * dk + c];
-    float gs = 1.f, rend = 1.f;  // gamma_(s-1); r(C-1, e)
-#pragma unroll
-    for (int J = 0; J < NB; ++J) {
-      if (J < Mb) gs *= pib[J];
-      if (J > Mb) rend *= pib[J];
-    }
-    const float* PAm = PA + (size_t)(Mb > 0 ? Mb - 1 : 0) * C * dk;
-    const float* PDm = PD + (size_t)(Mb > 0 ? Mb - 1 : 0) * C * dk;
-
-    // Zq_i = sum_{j <= i} dA_ij k_j r_ij, Zr_i = sum_{j < i} dD_ij k_j r_ij,
-    // Zc_j = sum_{i >= j} (dA_ij q_i + dD_ij k_i) r_ij
+  for (int it = 0; it < C * DK / 4 / NT; ++it) {
+    const int x = tid + it * NT, i = x / (DK / 4), c = 4 * (x % (DK / 4));
+    *(float4*)(RQ + i * LK + c) = in4(a.q, i, c);
+    *(float4*)(RK + i * LK + c) = in4(a.k, i, c);
+    *(float4*)(RA + i * LK + c) = i < len ? ld4<T>(a.alpha, kb + i * ks + c) : make_float4(1.f, 1.f, 1.f, 1.f);
+  }
+  __syncthreads();
+  for (int item = tid; item < DK * NB; item += NT) {
+    const int c = item % DK, Mb = item / DK, s = Mb * SUB;
+    float al[SUB], qv[SUB], kv[SUB], pin[SUB], pa[SUB], pd[SUB];
 #pragma unroll
     for (int r = 0; r < SUB; ++r) {
       const int i = s + r;
-      float zq = sdA[i][i] * kv[r], zr = 0.f, P = 1.f;
+      al[r] = RA[i * LK + c];
+      qv[r] = RQ[i * LK + c];
+      kv[r] = RK[i * LK + c];
+      pin[r] = PIN[i * DK + c];
+    }
+    const float* PAm = PA + (size_t)(Mb > 0 ? Mb - 1 : 0) * C * DK;
+    const float* PDm = PD + (size_t)(Mb > 0 ? Mb - 1 : 0) * C * DK;
+#pragma unroll
+    for (int r = 0; r < SUB; ++r) {
+      pa[r] = Mb > 0 ? PAm[(s + r) * DK + c] : 0.f;
+      pd[r] = Mb > 0 ? PDm[(s + r) * DK + c] : 0.f;
+    }
+    float gs = 1.f, rend = 1.f;  // gamma_(s-1); r(C-1, e)
+#pragma unroll
+    for (int J = 0; J < NB; ++J) {
+      if (J < Mb) gs *= sPib[J * DK + c];
+      if (J > Mb) rend *= sPib[J * DK + c];
+    }
+
+    // Zq_i = sum_{j <= i} dA_ij k_j r_ij, Zr_i = sum_{j < i} dD_ij k_j r_ij,
+    // Zc_j = sum_{i >= j} (dA_ij q_i + dD_ij k_i) r_ij
+    float fr[SUB], sg[SUB];
+#pragma unroll
+    for (int r = 0; r < SUB; ++r) {
+      fr[r] = Mb < NB - 1 ? F[(s + r) * DK + c] : 0.f;
+      sg[r] = SIG[(s + r) * DK + c];
+    }
+#pragma unroll
+    for (int r = 0; r < SUB; ++r) {
+      const int i = s + r;
+      float zq = sdA[i * LC + i] * kv[r], zr = 0.f, P = 1.f;
 #pragma unroll
       for (int rj = r - 1; rj >= 0; --rj) {
         P *= al[rj + 1];
-        zq += sdA[i][s + rj] * kv[rj] * P;
-        zr += sdD[i][s + rj] * kv[rj] * P;
+        zq += sdA[i * LC + s + rj] * kv[rj] * P;
+        zr += sdD[i * LC + s + rj] * kv[rj] * P;
       }
-      if (Mb > 0) {
-        const float pin = PIN[i * dk + c];
-        zq += pin * PAm[i * dk + c];
-        zr += pin * PDm[i * dk + c];
-      }
-      float zc = sdA[i][i] * qv[r];
+      zq += pin[r] * pa[r];
+      zr += pin[r] * pd[r];
+      float zc = sdA[i * LC + i] * qv[r];
       P = 1.f;
 #pragma unroll
       for (int ri = r + 1; ri < SUB; ++ri) {
         P *= al[ri];
-        zc += (sdA[s + ri][i] * qv[ri] + sdD[s + ri][i] * kv[ri]) * P;
+        zc += (sdA[(s + ri) * LC + i] * qv[ri] + sdD[(s + ri) * LC + i] * kv[ri]) * P;
       }
-      if (Mb < NB - 1) zc += SIG[i * dk + c] * F[i * dk + c];
-      if (i < cg.len) {
-        a.dq[okb + (size_t)i * Q.stride + c] += zq;
-        a.dk[okb + (size_t)i * Q.stride + c] += zr + zc;
+      zc += sg[r] * fr[r];
+      if (i < len) {
+        a.dq[kb + i * ks + c] += zq;
+        a.dk[kb + i * ks + c] += zr + zc;
       }
     }
 
@@ -744,51 +960,49 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a, int NC) {
     for (int J = 0; J < Mb; ++J) {
       float part = 0.f;
 #pragma unroll
-      for (int r = 0; r < SUB; ++r) part += BV[(J * SUB + r) * dk + c] * SIG[(J * SUB + r) * dk + c];
-      float w = 1.f;
-      for (int x = J + 1; x < Mb; ++x) w *= pib[x];
-      bvs += part * w;
+      for (int r = 0; r < SUB; ++r) part += BV[(J * SUB + r) * DK + c] * SIG[(J * SUB + r) * DK + c];
+      bvs += part * between(J, Mb, c);
     }
     const float dgl = sGl[c];
-    auto g_at = [&](int i) {
-      float g = AV[i * dk + c] * gs;
-      if (Mb > 0) g += Q.at(i, c) * PAm[i * dk + c] + K.at(i, c) * PDm[i * dk + c];
-      if (i == C - 1) g += bvs + dgl * gs;
-      return g;
-    };
     float u[SUB];
 #pragma unroll
-    for (int r = 0; r < SUB; ++r) u[r] = g_at(s + r);
+    for (int r = 0; r < SUB; ++r) {
+      const int i = s + r;
+      u[r] = AV[i * DK + c] * gs + qv[r] * pa[r] + kv[r] * pd[r];
+      if (i == C - 1) u[r] += bvs + dgl * gs;
+    }
     float f[SUB];
     if (Mb < NB - 1) {
       // rows below the block fold into its last row: X = sum_{i > e} r(i, e) g_i
       float x = 0.f;
       for (int I = NB - 1; I > Mb; --I) {
-        float gv[SUB], av[SUB];
+        float gv[SUB];
 #pragma unroll
         for (int r = 0; r < SUB; ++r) {
-          gv[r] = g_at(I * SUB + r);
-          av[r] = AL.at(I * SUB + r, c, 1.f);
+          const int i = I * SUB + r;
+          gv[r] = AV[i * DK + c] * gs;
+          if (Mb > 0) gv[r] += RQ[i * LK + c] * PAm[i * DK + c] + RK[i * LK + c] * PDm[i * DK + c];
+          if (i == C - 1) gv[r] += bvs + dgl * gs;
         }
 #pragma unroll
-        for (int r = SUB - 1; r >= 0; --r) x = av[r] * (gv[r] + x);
+        for (int r = SUB - 1; r >= 0; --r) x = RA[(I * SUB + r) * LK + c] * (gv[r] + x);
       }
       u[SUB - 1] += x;
 #pragma unroll
-      for (int r = 0; r < SUB; ++r) f[r] = kv[r] * F[(s + r) * dk + c] + BV[(s + r) * dk + c] * rend;
+      for (int r = 0; r < SUB; ++r) f[r] = kv[r] * fr[r] + BV[(s + r) * DK + c] * rend;
     } else {
 #pragma unroll
-      for (int r = 0; r < SUB; ++r) f[r] = BV[(s + r) * dk + c];  // the final-state row C - 1
+      for (int r = 0; r < SUB; ++r) f[r] = BV[(s + r) * DK + c];  // the final-state row C - 1
     }
 #pragma unroll
     for (int m = 0; m < SUB; ++m) {
       float acc = u[SUB - 1];
 #pragma unroll
       for (int i = SUB - 2; i >= m; --i) acc = u[i] + al[i + 1] * acc;
-      if (s + m < cg.len) a.dalpha[okb + (size_t)(s + m) * Q.stride + c] = acc;
+      if (s + m < len) a.dalpha[kb + (s + m) * ks + c] = acc;
 #pragma unroll
       for (int i = m + 1; i < SUB; ++i) {
-        float E = (qv[i] * sdA[s + i][s + m] + kv[i] * sdD[s + i][s + m]) * kv[m];
+        float E = (qv[i] * sdA[(s + i) * LC + s + m] + kv[i] * sdD[(s + i) * LC + s + m]) * kv[m];
         if (i == SUB - 1) E += f[m];
         u[i] = al[m] * u[i] + E;
       }
@@ -806,7 +1020,12 @@ static hipError_t launch_bwd_dk(const BwdArgs& a, int NC) {
     hipLaunchKernelGGL((bwd_state_kernel<T, DK>), dim3(walks), dim3(NT), 0, st, a, NC);
   }
   hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK>), dim3(walks), dim3(NT), 0, st, a, NC);
-  if (NC > 0) hipLaunchKernelGGL((bwd_grads_kernel<T>), dim3(BH * NC), dim3(NT), 0, st, a, NC);
+  if (NC > 0) {
+    if (a.Dv == 64)
+      hipLaunchKernelGGL((bwd_grads_kernel<T, DK, 64>), dim3(BH * NC), dim3(NT), 0, st, a, NC);
+    else
+      hipLaunchKernelGGL((bwd_grads_kernel<T, DK, 128>), dim3(BH * NC), dim3(NT), 0, st, a, NC);
+  }
   return hipGetLastError();
 }
 
