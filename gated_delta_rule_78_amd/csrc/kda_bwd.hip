@@ -134,192 +134,6 @@ __device__ __forceinline__ float between(const float* pib, int dk, int J, int I,
 
 }  // namespace
 
-// ---------------------------------------------------------------------------------------
-// bwd_records_kernel: one workgroup per (b, h, chunk).
-template <typename T>
-__global__ __launch_bounds__(NT) void bwd_records_kernel(BwdArgs a, int NC) {
-  const int tid = threadIdx.x, dk = a.Dk;
-  const BwdLayout L(dk, a.Dv);
-  const ChunkGeom cg = chunk_geom(blockIdx.x, NC, a.H, a.T);
-  float* ch = a.ws + (size_t)blockIdx.x * L.total;
-  const Rows<T> Q{a.q, row0(cg, a.T, a.H, dk), (size_t)a.H * dk, cg.len};
-  const Rows<T> K{a.k, Q.base, Q.stride, cg.len};
-  const Rows<T> AL{a.alpha, Q.base, Q.stride, cg.len};
-  const Rows<T> BE{a.beta, ((size_t)cg.b * a.T + cg.t0) * a.H + cg.h, (size_t)a.H, cg.len};
-  float *GAM = ch + L.gam, *RHO = ch + L.rho, *PIN = ch + L.pin, *SIG = ch + L.sig, *PIB = ch + L.pib;
-
-  __shared__ float sA[C][C + 1], sD[C][C + 1], sM[C][C + 1];
-  __shared__ float sRed[136 * 129];  // 136 pairs of a 16-row block x up to 128 channels (+1 pad)
-  __shared__ float sY[3][16][17];
-  __shared__ float sB[C];
-
-  // (a) gate products per key channel: gamma (from the chunk start), rho (to the chunk
-  // end, exclusive), pi (from the block start, inclusive), sigma (to the block end,
-  // exclusive) and the block totals.
-  for (int c = tid; c < dk; c += NT) {
-    float gm = 1.f, pib[NB];
-    for (int I = 0; I < NB; ++I) {
-      float al[SUB];
-#pragma unroll
-      for (int r = 0; r < SUB; ++r) al[r] = AL.at(I * SUB + r, c, 1.f);
-      float p = 1.f;
-#pragma unroll
-      for (int r = 0; r < SUB; ++r) {
-        const int i = I * SUB + r;
-        p *= al[r];
-        gm *= al[r];
-        PIN[i * dk + c] = p;
-        GAM[i * dk + c] = gm;
-      }
-      PIB[I * dk + c] = pib[I] = p;
-      float sf = 1.f;
-#pragma unroll
-      for (int r = SUB - 1; r >= 0; --r) {
-        SIG[(I * SUB + r) * dk + c] = sf;
-        sf *= al[r];
-      }
-    }
-    // rho_i = sigma_i * the whole blocks after i's block
-    float tail = 1.f;
-    for (int I = NB - 1; I >= 0; --I) {
-      float sf = tail;
-#pragma unroll
-      for (int r = SUB - 1; r >= 0; --r) {
-        const int i = I * SUB + r;
-        RHO[i * dk + c] = sf;
-        sf *= AL.at(i, c, 1.f);
-      }
-      tail *= pib[I];
-    }
-  }
-  for (int i = tid; i < C; i += NT) sB[i] = BE.at(i, 0);
-  for (int x = tid; x < C * C; x += NT) {
-    const int i = x / C, j = x % C;
-    if (j > i) sA[i][j] = sD[i][j] = 0.f;
-  }
-  __syncthreads();
-
-  // (b) the six off-diagonal 16x16 tiles (I > J) of A and of D, anchored at row
-  // s_I - 1: r_ij = pi_i * (sigma_j * the whole blocks between J and I).
-  {
-    const int lane = tid & 63, wave = tid >> 6, n = lane & 15, g = lane >> 4;
-    for (int job = wave; job < 12; job += NT / 64) {
-      // tiles (I, J) = (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
-      const int mat = job / 6, p = job % 6, I = p < 1 ? 1 : (p < 3 ? 2 : 3), J = p - I * (I - 1) / 2;
-      const int si = I * SUB, sj = J * SUB;
-      const f32x4_t acc = tile_mm(
-          dk,
-          [&](int r, int c) {
-            const int i = si + r;
-            return (mat ? K.at(i, c) : Q.at(i, c)) * PIN[i * dk + c];
-          },
-          [&](int c, int col) {
-            const int j = sj + col;
-            return K.at(j, c) * SIG[j * dk + c] * between(PIB, dk, J, I, c);
-          });
-#pragma unroll
-      for (int r = 0; r < 4; ++r) (mat ? sD : sA)[si + 4 * g + r][sj + n] = acc[r];
-    }
-  }
-
-  // (c) the diagonal tiles: per channel products, then sums over the channels.
-  for (int I = 0; I < NB; ++I) {
-    const int s = I * SUB;
-    for (int mat = 0; mat < 2; ++mat) {
-      for (int c = tid; c < dk; c += NT) {
-        float kv[SUB], xv[SUB], av[SUB];
-#pragma unroll
-        for (int r = 0; r < SUB; ++r) {
-          kv[r] = K.at(s + r, c);
-          xv[r] = mat ? kv[r] : Q.at(s + r, c);
-          av[r] = AL.at(s + r, c, 1.f);
-        }
-#pragma unroll
-        for (int rj = 0; rj < SUB; ++rj) {
-          float P = 1.f;
-#pragma unroll
-          for (int ri = rj; ri < SUB; ++ri) {
-            if (ri > rj) P *= av[ri];
-            sRed[(ri * (ri + 1) / 2 + rj) * (dk + 1) + c] = (mat && ri == rj) ? 0.f : xv[ri] * kv[rj] * P;
-          }
-        }
-      }
-      __syncthreads();
-      for (int p = tid; p < 136; p += NT) {
-        int ri = 0;
-        while ((ri + 1) * (ri + 2) / 2 <= p) ++ri;
-        const int rj = p - ri * (ri + 1) / 2;
-        float sum = 0.f, sum2 = 0.f;
-#pragma unroll 8
-        for (int c = 0; c < dk; c += 2) {
-          sum += sRed[p * (dk + 1) + c];
-          sum2 += sRed[p * (dk + 1) + c + 1];
-        }
-        sum += sum2;
-        (mat ? sD : sA)[s + ri][s + rj] = sum;
-      }
-      __syncthreads();
-    }
-  }
-
-  // (d) M = (I + diag(beta) D)^-1: the four diagonal 16x16 blocks by substitution, then
-  // block rows I = 1..3: M_IJ = -M_II sum_{J <= K < I} (beta D)_IK M_KJ.
-  if (tid < 4 * SUB) {
-    const int s = (tid / SUB) * SUB, col = tid % SUB;
-    for (int r = 0; r < SUB; ++r) {
-      float acc = 0.f;
-      for (int j = 0; j < r; ++j) acc += sD[s + r][s + j] * sM[s + j][s + col];
-      sM[s + r][s + col] = (r == col ? 1.f : 0.f) - sB[s + r] * acc;
-    }
-  }
-  for (int x = tid; x < C * C; x += NT) {
-    const int i = x / C, j = x % C;
-    if (j / SUB > i / SUB) sM[i][j] = 0.f;
-  }
-  __syncthreads();
-  for (int I = 1; I < NB; ++I) {
-    const int si = I * SUB, lane = tid & 63, wave = tid >> 6, n = lane & 15, g = lane >> 4;
-    for (int J = wave; J < I; J += NT / 64) {
-      const int sj = J * SUB;
-      const f32x4_t y = tile_mm(
-          si - sj, [&](int r, int kk) { return sB[si + r] * sD[si + r][sj + kk]; },
-          [&](int kk, int col) { return sM[sj + kk][sj + col]; });
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sY[J][4 * g + r][n] = y[r];
-    }
-    __syncthreads();
-    for (int J = wave; J < I; J += NT / 64) {
-      const int sj = J * SUB;
-      const f32x4_t m = tile_mm(
-          SUB, [&](int r, int kk) { return sM[si + r][si + kk]; }, [&](int kk, int col) { return sY[J][kk][col]; });
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sM[si + 4 * g + r][sj + n] = -m[r];
-    }
-    __syncthreads();
-  }
-
-  // (e) W = M diag(beta) (K o gamma); A, D, M to the workspace
-  wg_mm(
-      C / 16, dk / 16, C, [&](int i, int j) { return sM[i][j] * sB[j]; },
-      [&](int j, int c) { return K.at(j, c) * GAM[j * dk + c]; },
-      [&](int i, int c, float x) { ch[L.W + i * dk + c] = x; });
-  for (int x = tid; x < C * C; x += NT) {
-    const int i = x / C, j = x % C;
-    ch[L.A + x] = sA[i][j];
-    ch[L.D + x] = sD[i][j];
-    ch[L.M + x] = sM[i][j];
-  }
-}
-
-// ---------------------------------------------------------------------------------------
-// The two walks.  One workgroup per (b, h, 64 value columns); wave w owns the 16 columns
-// v0 + 16 w .. v0 + 16 w + 15 (the value columns of the state evolve independently) and
-// keeps them in matrix-core accumulators for the whole walk: DK / 16 tiles, element
-// (16 I + 4 g + r, n) in register r of tile I.  The four steps of each 16-wide slice of a
-// product take k-slot k0 + 4 g + t at step t, so an accumulator tile is itself the B
-// operand of a product over its rows: neither the state nor Delta leaves the registers.
-// Only the chunk's shared operands are staged in LDS (row strides padded by four floats),
-// with vector loads issued together.
 namespace {
 
 constexpr int VTW = 64;  // value columns per walk workgroup, 16 per wave
@@ -356,9 +170,280 @@ __device__ __forceinline__ void mm16(f32x4_t& acc, const float* arow, int k0, FB
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[t], fb(t), acc, 0, 0, 0);
 #endif
   }
+  (void)av;
 }
 
 }  // namespace
+
+namespace {
+__device__ __forceinline__ float f4c(const float4& v, int t) {
+  return t == 0 ? v.x : (t == 1 ? v.y : (t == 2 ? v.z : v.w));
+}
+__device__ __forceinline__ float4 mul4(const float4& a, const float4& b) {
+  return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w);
+}
+__device__ __forceinline__ void mfma4(f32x4_t& acc, const float (&av)[4], const float (&bv)[4]) {
+#ifndef KDA_HOST_PASS
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[t], bv[t], acc, 0, 0, 0);
+#endif
+}
+}  // namespace
+
+// ---------------------------------------------------------------------------------------
+// bwd_records_kernel: one workgroup per (b, h, chunk).  A (channel, block) item keeps the
+// 16 rows of alpha, q, k of its channel and block in registers throughout.
+//   (a) gate products: pi (from the block start, inclusive), sigma (to the block end,
+//       exclusive), block totals, gamma (from the chunk start), rho (to the chunk end,
+//       exclusive);
+//   (b) the six off-diagonal 16x16 tiles (I > J) of A and D, anchored at row s_I - 1:
+//       r_ij = pi_i * sigma_j * (the whole blocks between J and I);
+//   (c) the diagonal tiles, one matrix-core product per level lam = 8, 4, 2, 1: a pair
+//       (i, j) of one block whose local indices differ first in bit lam has
+//       r_ij = F_i B_j, F the product from the start of i's lam-half through i, B the
+//       product after j through the end of j's lam-half; level 0 gives A's diagonal;
+//   (d) M = (I + diag(beta) D)^-1 by blocks; (e) W = M diag(beta) (K o gamma).
+template <typename T, int DK>
+__global__ __launch_bounds__(NT) void bwd_records_kernel(BwdArgs a, int NC) {
+  constexpr int LK = DK + 4, LC = C + 1, NI = DK * NB / NT;  // items per thread
+  static_assert(NI >= 1 && DK * NB % NT == 0, "items");
+  __shared__ float sR[3 * C * LK];  // operand staging, reused by (b), (c), (e)
+  __shared__ float sA[C * LC], sD[C * LC], sM[C * LC];
+  __shared__ float sPib[NB * DK], sB[C], sY[3][16][17];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, g = lane >> 4;
+  const BwdLayout L(DK, a.Dv);
+  const ChunkGeom cg = chunk_geom(blockIdx.x, NC, a.H, a.T);
+  const int len = cg.len;
+  float* ch = a.ws + (size_t)blockIdx.x * L.total;
+  const size_t kb = row0(cg, a.T, a.H, DK), ks = (size_t)a.H * DK;
+  const size_t bb = ((size_t)cg.b * a.T + cg.t0) * a.H + cg.h;
+  float *R0 = sR, *R1 = sR + C * LK, *R2 = sR + 2 * C * LK;
+
+  // ---- (a) items (c, I): load, block products
+  float al[NI][SUB], qv[NI][SUB], kv[NI][SUB], pi[NI][SUB], sg[NI][SUB];
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    const int item = tid + it * NT, c = item % DK, I = item / DK;
+#pragma unroll
+    for (int r = 0; r < SUB; ++r) {
+      const int i = I * SUB + r;
+      const bool in = i < len;
+      al[it][r] = in ? Elem<T>::load(a.alpha, kb + i * ks + c) : 1.f;
+      qv[it][r] = in ? Elem<T>::load(a.q, kb + i * ks + c) : 0.f;
+      kv[it][r] = in ? Elem<T>::load(a.k, kb + i * ks + c) : 0.f;
+    }
+  }
+  for (int i = tid; i < C; i += NT) sB[i] = i < len ? Elem<T>::load(a.beta, bb + (size_t)i * a.H) : 0.f;
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    const int item = tid + it * NT, c = item % DK, I = item / DK;
+    float p = 1.f;
+#pragma unroll
+    for (int r = 0; r < SUB; ++r) {
+      p *= al[it][r];
+      pi[it][r] = p;
+    }
+    sPib[I * DK + c] = p;
+    ch[L.pib + I * DK + c] = p;
+    float sf = 1.f;
+#pragma unroll
+    for (int r = SUB - 1; r >= 0; --r) {
+      sg[it][r] = sf;
+      sf *= al[it][r];
+    }
+#pragma unroll
+    for (int r = 0; r < SUB; ++r) {
+      ch[L.pin + (I * SUB + r) * DK + c] = pi[it][r];
+      ch[L.sig + (I * SUB + r) * DK + c] = sg[it][r];
+    }
+  }
+  for (int x = tid; x < C * C; x += NT) {
+    const int i = x / C, j = x % C;
+    if (j / SUB > i / SUB) sA[i * LC + j] = sD[i * LC + j] = sM[i * LC + j] = 0.f;
+  }
+  __syncthreads();
+  // gamma, rho; the anchored operands of (b): q o pi, k o pi, k o sigma
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    const int item = tid + it * NT, c = item % DK, I = item / DK;
+    float before = 1.f, after = 1.f;
+#pragma unroll
+    for (int J = 0; J < NB; ++J) {
+      if (J < I) before *= sPib[J * DK + c];
+      if (J > I) after *= sPib[J * DK + c];
+    }
+#pragma unroll
+    for (int r = 0; r < SUB; ++r) {
+      const int i = I * SUB + r;
+      ch[L.gam + i * DK + c] = before * pi[it][r];
+      ch[L.rho + i * DK + c] = after * sg[it][r];
+      R0[i * LK + c] = qv[it][r] * pi[it][r];
+      R1[i * LK + c] = kv[it][r] * pi[it][r];
+      R2[i * LK + c] = kv[it][r] * sg[it][r];
+    }
+  }
+  __syncthreads();
+
+  // ---- (b) off-diagonal tiles: A[I, J] = (q o pi)_I ((k o sigma) btw)_J^T, D likewise
+  for (int job = wave; job < 12; job += NT / 64) {
+    // tiles (I, J) = (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+    const int mat = job / 6, p = job % 6, I = p < 1 ? 1 : (p < 3 ? 2 : 3), J = p - I * (I - 1) / 2;
+    const float* xrow = (mat ? R1 : R0) + (16 * I + n) * LK;
+    const float* yrow = R2 + (16 * J + n) * LK;
+    f32x4_t acc = zero4f();
+#pragma unroll
+    for (int k0 = 0; k0 < DK; k0 += 16) {
+      const float4 y4 = *(const float4*)(yrow + k0 + 4 * g);
+      float w[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        w[t] = 1.f;
+        for (int x = J + 1; x < I; ++x) w[t] *= sPib[x * DK + k0 + 4 * g + t];
+      }
+      mm16(acc, xrow, k0, [&](int t) { return f4c(y4, t) * w[t]; });
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) (mat ? sD : sA)[(16 * I + 4 * g + r) * LC + 16 * J + n] = acc[r];
+  }
+
+  // ---- (c) diagonal tiles by levels lam = 8, 4, 2, 1, then 0 (A's diagonal)
+  for (int lam = 8; lam >= 0; lam = lam > 1 ? lam / 2 : lam - 1) {
+    __syncthreads();  // the previous readers of the staging region are done
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      const int item = tid + it * NT, c = item % DK, I = item / DK;
+      float Fv[SUB], Bv[SUB];
+      if (lam > 0) {
+        float p = 1.f;
+#pragma unroll
+        for (int r = 0; r < SUB; ++r) {
+          if ((r & (lam - 1)) == 0) p = 1.f;
+          p *= al[it][r];
+          Fv[r] = p;
+        }
+        p = 1.f;
+#pragma unroll
+        for (int r = SUB - 1; r >= 0; --r) {
+          if (((r + 1) & (lam - 1)) == 0) p = 1.f;
+          Bv[r] = p;
+          p *= al[it][r];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < SUB; ++r) Fv[r] = Bv[r] = 1.f;
+      }
+#pragma unroll
+      for (int r = 0; r < SUB; ++r) {
+        const int i = I * SUB + r;
+        R0[i * LK + c] = qv[it][r] * Fv[r];
+        R1[i * LK + c] = kv[it][r] * Fv[r];
+        R2[i * LK + c] = kv[it][r] * Bv[r];
+      }
+    }
+    __syncthreads();
+    for (int job = wave; job < 8; job += NT / 64) {  // level 0 also clears D's diagonal and upper part
+      const int I = job % NB, mat = job / NB, si = 16 * I;
+      const float* xrow = (mat ? R1 : R0) + (si + n) * LK;
+      const float* yrow = R2 + (si + n) * LK;
+      f32x4_t acc = zero4f();
+#pragma unroll
+      for (int k0 = 0; k0 < DK; k0 += 16) {
+        const float4 y4 = *(const float4*)(yrow + k0 + 4 * g);
+        mm16(acc, xrow, k0, [&](int t) { return f4c(y4, t); });
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int il = 4 * g + r, jl = n;  // local row, column
+        bool keep;
+        if (lam > 0)
+          keep = (il & lam) && !(jl & lam) && ((il & ~(2 * lam - 1)) == (jl & ~(2 * lam - 1)));
+        else
+          keep = il == jl && !mat;
+        if (keep) (mat ? sD : sA)[(si + il) * LC + si + jl] = acc[r];
+        else if (lam == 0 && jl >= il) (mat ? sD : sA)[(si + il) * LC + si + jl] = 0.f;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- (d) M = (I + diag(beta) D)^-1: diagonal blocks by substitution, then block rows
+  // I = 1..3: M_IJ = -M_II sum_{J <= K < I} (beta D)_IK M_KJ
+  if (tid < 4 * SUB) {
+    const int s = (tid / SUB) * SUB, col = tid % SUB;
+    for (int r = 0; r < SUB; ++r) {
+      float acc = 0.f;
+      for (int j = 0; j < r; ++j) acc += sD[(s + r) * LC + s + j] * sM[(s + j) * LC + s + col];
+      sM[(s + r) * LC + s + col] = (r == col ? 1.f : 0.f) - sB[s + r] * acc;
+    }
+  }
+  __syncthreads();
+  for (int I = 1; I < NB; ++I) {
+    const int si = I * SUB;
+    for (int J = wave; J < I; J += NT / 64) {
+      const int sj = J * SUB;
+      const f32x4_t y = tile_mm(
+          si - sj, [&](int r, int kk) { return sB[si + r] * sD[(si + r) * LC + sj + kk]; },
+          [&](int kk, int col) { return sM[(sj + kk) * LC + sj + col]; });
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sY[J][4 * g + r][n] = y[r];
+    }
+    __syncthreads();
+    for (int J = wave; J < I; J += NT / 64) {
+      const int sj = J * SUB;
+      const f32x4_t m = tile_mm(
+          SUB, [&](int r, int kk) { return sM[(si + r) * LC + si + kk]; }, [&](int kk, int col) { return sY[J][kk][col]; });
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sM[(si + 4 * g + r) * LC + sj + n] = -m[r];
+    }
+    __syncthreads();
+  }
+
+  // ---- (e) K o gamma into the staging region; W = M diag(beta) (K o gamma); A, D, M out
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    const int item = tid + it * NT, c = item % DK, I = item / DK;
+    float before = 1.f;
+#pragma unroll
+    for (int J = 0; J < NB; ++J)
+      if (J < I) before *= sPib[J * DK + c];
+#pragma unroll
+    for (int r = 0; r < SUB; ++r) R0[(I * SUB + r) * LK + c] = kv[it][r] * pi[it][r] * before;
+  }
+  __syncthreads();
+  for (int job = wave; job < 4 * (DK / 16); job += NT / 64) {
+    const int I = job / (DK / 16), ct = job % (DK / 16), c = 16 * ct + n;
+    f32x4_t acc = zero4f();
+#pragma unroll
+    for (int k0 = 0; k0 < C; k0 += 16) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int j = k0 + 4 * g + t;
+        av[t] = sM[(16 * I + n) * LC + j] * sB[j];
+        bv[t] = R0[j * LK + c];
+      }
+      mfma4(acc, av, bv);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ch[L.W + (16 * I + 4 * g + r) * DK + c] = acc[r];
+  }
+  for (int x = tid; x < C * C; x += NT) {
+    const int i = x / C, j = x % C;
+    ch[L.A + x] = sA[i * LC + j];
+    ch[L.D + x] = sD[i * LC + j];
+    ch[L.M + x] = sM[i * LC + j];
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// The two walks.  One workgroup per (b, h, 64 value columns); wave w owns the 16 columns
+// v0 + 16 w .. v0 + 16 w + 15 (the value columns of the state evolve independently) and
+// keeps them in matrix-core accumulators for the whole walk: DK / 16 tiles, element
+// (16 I + 4 g + r, n) in register r of tile I.  The four steps of each 16-wide slice of a
+// product take k-slot k0 + 4 g + t at step t, so an accumulator tile is itself the B
+// operand of a product over its rows: neither the state nor Delta leaves the registers.
+// Only the chunk's shared operands are staged in LDS (row strides padded by four floats),
+// with vector loads issued together.
 
 // bwd_state_kernel: chunks in order; writes the chunk-start state S_n and Delta_n.
 template <typename T, int DK>
@@ -559,20 +644,6 @@ __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC) {
 //   C  dbeta, X = dMt Mt^T, dT and dD in LDS;
 //   D  the block-anchored products PA, PD, F with their B operands staged in LDS;
 //   E  per (channel, block): the in-block decayed sums, dq and dk, the gate gradient.
-namespace {
-__device__ __forceinline__ float f4c(const float4& v, int t) {
-  return t == 0 ? v.x : (t == 1 ? v.y : (t == 2 ? v.z : v.w));
-}
-__device__ __forceinline__ float4 mul4(const float4& a, const float4& b) {
-  return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w);
-}
-__device__ __forceinline__ void mfma4(f32x4_t& acc, const float (&av)[4], const float (&bv)[4]) {
-#ifndef KDA_HOST_PASS
-#pragma unroll
-  for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[t], bv[t], acc, 0, 0, 0);
-#endif
-}
-}  // namespace
 
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a, int NC) {
@@ -1016,7 +1087,7 @@ static hipError_t launch_bwd_dk(const BwdArgs& a, int NC) {
   const int BH = a.B * a.H, walks = BH * (a.Dv / VTW);
   hipStream_t st = (hipStream_t)a.stream;
   if (NC > 0) {
-    hipLaunchKernelGGL((bwd_records_kernel<T>), dim3(BH * NC), dim3(NT), 0, st, a, NC);
+    hipLaunchKernelGGL((bwd_records_kernel<T, DK>), dim3(BH * NC), dim3(NT), 0, st, a, NC);
     hipLaunchKernelGGL((bwd_state_kernel<T, DK>), dim3(walks), dim3(NT), 0, st, a, NC);
   }
   hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK>), dim3(walks), dim3(NT), 0, st, a, NC);
