@@ -39,7 +39,9 @@ namespace kda {
 
 namespace {
 
-constexpr int NT = 256;  // threads per workgroup of every kernel here
+constexpr int NT = 256;   // threads per workgroup of the walks
+constexpr int NTG = 512;  // threads per workgroup of the gradient kernel and, at d_k = 128, of the
+                          // records kernel (two waves per SIMD)
 
 // ---------------------------------------------------------------------------------------
 // One 16x16 fp32 tile: acc[i][j] = sum_k fa(i, k) fb(k, j), K a multiple of 4.  Lane
@@ -204,9 +206,10 @@ __device__ __forceinline__ void mfma4(f32x4_t& acc, const float (&av)[4], const 
 //       product after j through the end of j's lam-half; level 0 gives A's diagonal;
 //   (d) M = (I + diag(beta) D)^-1 by blocks; (e) W = M diag(beta) (K o gamma).
 template <typename T, int DK>
-__global__ __launch_bounds__(NT) void bwd_records_kernel(BwdArgs a, int NC) {
-  constexpr int LK = DK + 4, LC = C + 1, NI = DK * NB / NT;  // items per thread
-  static_assert(NI >= 1 && DK * NB % NT == 0, "items");
+__global__ __launch_bounds__(DK == 128 ? NTG : NT) void bwd_records_kernel(BwdArgs a, int NC) {
+  constexpr int NTR = DK == 128 ? NTG : NT;  // one (channel, block) item per thread
+  constexpr int LK = DK + 4, LC = C + 1, NI = DK * NB / NTR;  // items per thread
+  static_assert(NI >= 1 && DK * NB % NTR == 0, "items");
   __shared__ float sR[3 * C * LK];  // operand staging, reused by (b), (c), (e)
   __shared__ float sA[C * LC], sD[C * LC], sM[C * LC];
   __shared__ float sPib[NB * DK], sB[C], sY[3][16][17];
@@ -223,7 +226,7 @@ __global__ __launch_bounds__(NT) void bwd_records_kernel(BwdArgs a, int NC) {
   float al[NI][SUB], qv[NI][SUB], kv[NI][SUB], pi[NI][SUB], sg[NI][SUB];
 #pragma unroll
   for (int it = 0; it < NI; ++it) {
-    const int item = tid + it * NT, c = item % DK, I = item / DK;
+    const int item = tid + it * NTR, c = item % DK, I = item / DK;
 #pragma unroll
     for (int r = 0; r < SUB; ++r) {
       const int i = I * SUB + r;
@@ -233,10 +236,10 @@ __global__ __launch_bounds__(NT) void bwd_records_kernel(BwdArgs a, int NC) {
       kv[it][r] = in ? Elem<T>::load(a.k, kb + i * ks + c) : 0.f;
     }
   }
-  for (int i = tid; i < C; i += NT) sB[i] = i < len ? Elem<T>::load(a.beta, bb + (size_t)i * a.H) : 0.f;
+  for (int i = tid; i < C; i += NTR) sB[i] = i < len ? Elem<T>::load(a.beta, bb + (size_t)i * a.H) : 0.f;
 #pragma unroll
   for (int it = 0; it < NI; ++it) {
-    const int item = tid + it * NT, c = item % DK, I = item / DK;
+    const int item = tid + it * NTR, c = item % DK, I = item / DK;
     float p = 1.f;
 #pragma unroll
     for (int r = 0; r < SUB; ++r) {
@@ -257,7 +260,7 @@ __global__ __launch_bounds__(NT) void bwd_records_kernel(BwdArgs a, int NC) {
       ch[L.sig + (I * SUB + r) * DK + c] = sg[it][r];
     }
   }
-  for (int x = tid; x < C * C; x += NT) {
+  for (int x = tid; x < C * C; x += NTR) {
     const int i = x / C, j = x % C;
     if (j / SUB > i / SUB) sA[i * LC + j] = sD[i * LC + j] = sM[i * LC + j] = 0.f;
   }
@@ -265,7 +268,7 @@ __global__ __launch_bounds__(NT) void bwd_records_kernel(BwdArgs a, int NC) {
   // gamma, rho; the anchored operands of (b): q o pi, k o pi, k o sigma
 #pragma unroll
   for (int it = 0; it < NI; ++it) {
-    const int item = tid + it * NT, c = item % DK, I = item / DK;
+    const int item = tid + it * NTR, c = item % DK, I = item / DK;
     float before = 1.f, after = 1.f;
 #pragma unroll
     for (int J = 0; J < NB; ++J) {
@@ -285,7 +288,7 @@ __global__ __launch_bounds__(NT) void bwd_records_kernel(BwdArgs a, int NC) {
   __syncthreads();
 
   // ---- (b) off-diagonal tiles: A[I, J] = (q o pi)_I ((k o sigma) btw)_J^T, D likewise
-  for (int job = wave; job < 12; job += NT / 64) {
+  for (int job = wave; job < 12; job += NTR / 64) {
     // tiles (I, J) = (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
     const int mat = job / 6, p = job % 6, I = p < 1 ? 1 : (p < 3 ? 2 : 3), J = p - I * (I - 1) / 2;
     const float* xrow = (mat ? R1 : R0) + (16 * I + n) * LK;
@@ -311,7 +314,7 @@ __global__ __launch_bounds__(NT) void bwd_records_kernel(BwdArgs a, int NC) {
     __syncthreads();  // the previous readers of the staging region are done
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
-      const int item = tid + it * NT, c = item % DK, I = item / DK;
+      const int item = tid + it * NTR, c = item % DK, I = item / DK;
       float Fv[SUB], Bv[SUB];
       if (lam > 0) {
         float p = 1.f;
@@ -341,7 +344,7 @@ __global__ __launch_bounds__(NT) void bwd_records_kernel(BwdArgs a, int NC) {
       }
     }
     __syncthreads();
-    for (int job = wave; job < 8; job += NT / 64) {  // level 0 also clears D's diagonal and upper part
+    for (int job = wave; job < 8; job += NTR / 64) {  // level 0 also clears D's diagonal and upper part
       const int I = job % NB, mat = job / NB, si = 16 * I;
       const float* xrow = (mat ? R1 : R0) + (si + n) * LK;
       const float* yrow = R2 + (si + n) * LK;
@@ -379,7 +382,7 @@ __global__ __launch_bounds__(NT) void bwd_records_kernel(BwdArgs a, int NC) {
   __syncthreads();
   for (int I = 1; I < NB; ++I) {
     const int si = I * SUB;
-    for (int J = wave; J < I; J += NT / 64) {
+    for (int J = wave; J < I; J += NTR / 64) {
       const int sj = J * SUB;
       const f32x4_t y = tile_mm(
           si - sj, [&](int r, int kk) { return sB[si + r] * sD[(si + r) * LC + sj + kk]; },
@@ -388,7 +391,7 @@ __global__ __launch_bounds__(NT) void bwd_records_kernel(BwdArgs a, int NC) {
       for (int r = 0; r < 4; ++r) sY[J][4 * g + r][n] = y[r];
     }
     __syncthreads();
-    for (int J = wave; J < I; J += NT / 64) {
+    for (int J = wave; J < I; J += NTR / 64) {
       const int sj = J * SUB;
       const f32x4_t m = tile_mm(
           SUB, [&](int r, int kk) { return sM[(si + r) * LC + si + kk]; }, [&](int kk, int col) { return sY[J][kk][col]; });
@@ -401,7 +404,7 @@ __global__ __launch_bounds__(NT) void bwd_records_kernel(BwdArgs a, int NC) {
   // ---- (e) K o gamma into the staging region; W = M diag(beta) (K o gamma); A, D, M out
 #pragma unroll
   for (int it = 0; it < NI; ++it) {
-    const int item = tid + it * NT, c = item % DK, I = item / DK;
+    const int item = tid + it * NTR, c = item % DK, I = item / DK;
     float before = 1.f;
 #pragma unroll
     for (int J = 0; J < NB; ++J)
@@ -410,7 +413,7 @@ __global__ __launch_bounds__(NT) void bwd_records_kernel(BwdArgs a, int NC) {
     for (int r = 0; r < SUB; ++r) R0[(I * SUB + r) * LK + c] = kv[it][r] * pi[it][r] * before;
   }
   __syncthreads();
-  for (int job = wave; job < 4 * (DK / 16); job += NT / 64) {
+  for (int job = wave; job < 4 * (DK / 16); job += NTR / 64) {
     const int I = job / (DK / 16), ct = job % (DK / 16), c = 16 * ct + n;
     f32x4_t acc = zero4f();
 #pragma unroll
@@ -427,7 +430,7 @@ __global__ __launch_bounds__(NT) void bwd_records_kernel(BwdArgs a, int NC) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) ch[L.W + (16 * I + 4 * g + r) * DK + c] = acc[r];
   }
-  for (int x = tid; x < C * C; x += NT) {
+  for (int x = tid; x < C * C; x += NTR) {
     const int i = x / C, j = x % C;
     ch[L.A + x] = sA[i * LC + j];
     ch[L.D + x] = sD[i * LC + j];
@@ -638,15 +641,16 @@ __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC) {
 // bwd_grads_kernel: one workgroup per (b, h, chunk), in five phases:
 //   A  products over the value dimension, by key-channel tile: a wave holds its 16
 //      channels' rows of S and dS' as B fragments in registers and runs d(Q o gamma),
-//      dW and d(K o rho) against dO, dDelta and Delta staged in LDS; dgamma_L comes from
-//      the same registers;
-//   B  dA, dV, dMt, d(K o gamma) from LDS (dW staged where dO and Delta were);
+//      dW and d(K o rho) against dO, dDelta and Delta staged in LDS, then
+//      d(K o gamma) = Mt^T dW with its dW tiles as B operands; dgamma_L comes from the
+//      same registers;
+//   B  dA, dV, dMt from LDS (dW staged where dO and Delta were);
 //   C  dbeta, X = dMt Mt^T, dT and dD in LDS;
 //   D  the block-anchored products PA, PD, F with their B operands staged in LDS;
 //   E  per (channel, block): the in-block decayed sums, dq and dk, the gate gradient.
 
 template <typename T, int DK, int DV>
-__global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a, int NC) {
+__global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
   constexpr int LV = DV + 4, LK = DK + 4, LC = C + 1;
   constexpr int RSZ = (3 * C * LV > 3 * C * LK) ? 3 * C * LV : 3 * C * LK;
   static_assert(LK <= 2 * LV, "dW must fit where dO and Delta were");
@@ -676,19 +680,27 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a, int NC) {
   // ---- stage dO, Delta, dDelta; M, beta, the block totals
   float *RO = sR, *RL = sR + C * LV, *RD = sR + 2 * C * LV;
 #pragma unroll
-  for (int it = 0; it < C * DV / 4 / NT; ++it) {
-    const int x = tid + it * NT, i = x / (DV / 4), v = 4 * (x % (DV / 4));
+  for (int it = 0; it < C * DV / 4 / NTG; ++it) {
+    const int x = tid + it * NTG, i = x / (DV / 4), v = 4 * (x % (DV / 4));
     *(float4*)(RO + i * LV + v) = i < len ? ld4<T>(a.dO, vb + i * vs + v) : z4;
     *(float4*)(RL + i * LV + v) = *(const float4*)(ch + L.DL + i * DV + v);
     *(float4*)(RD + i * LV + v) = *(const float4*)(ch + L.DDL + i * DV + v);
   }
-  for (int x = tid; x < C * C; x += NT) sM[(x / C) * LC + x % C] = ch[L.M + x];
-  for (int i = tid; i < C; i += NT) sB[i] = i < len ? Elem<T>::load(a.beta, bb + (size_t)i * a.H) : 0.f;
-  for (int x = tid; x < NB * DK; x += NT) sPib[x] = ch[L.pib + x];
+#pragma unroll
+  for (int it = 0; it < C * C / 4 / NTG; ++it) {
+    const int x = tid + it * NTG, i = x / (C / 4), j = 4 * (x % (C / 4));
+    const float4 m = *(const float4*)(ch + L.M + i * C + j);
+    sM[i * LC + j] = m.x;
+    sM[i * LC + j + 1] = m.y;
+    sM[i * LC + j + 2] = m.z;
+    sM[i * LC + j + 3] = m.w;
+  }
+  for (int i = tid; i < C; i += NTG) sB[i] = i < len ? Elem<T>::load(a.beta, bb + (size_t)i * a.H) : 0.f;
+  for (int x = tid; x < NB * DK; x += NTG) sPib[x] = ch[L.pib + x];
   __syncthreads();
 
   // ---- A: d(Q o gamma) = dO S^T, dW = -dDelta S^T, d(K o rho) = Delta dS'^T, dgamma_L
-  for (int ct = wave; ct < DK / 16; ct += NT / 64) {
+  for (int ct = wave; ct < DK / 16; ct += NTG / 64) {
     const int c = 16 * ct + n;
     float4 sf[DV / 16], df[DV / 16];
 #pragma unroll
@@ -714,32 +726,48 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a, int NC) {
     part += __shfl_xor(part, 16);
     part += __shfl_xor(part, 32);
     if (g == 0) sGl[c] = part;
+    f32x4_t aq[4], aw[4], ar[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-      f32x4_t aq = zero4f(), aw = zero4f(), ar = zero4f();
+      aq[I] = aw[I] = ar[I] = zero4f();
       const float *ro = RO + (16 * I + n) * LV, *rd = RD + (16 * I + n) * LV, *rl = RL + (16 * I + n) * LV;
 #pragma unroll
       for (int u = 0; u < DV / 16; ++u) {
-        mm16(aq, ro, 16 * u, [&](int t) { return f4c(sf[u], t); });
-        mm16(aw, rd, 16 * u, [&](int t) { return f4c(sf[u], t); });
-        mm16(ar, rl, 16 * u, [&](int t) { return f4c(df[u], t); });
+        mm16(aq[I], ro, 16 * u, [&](int t) { return f4c(sf[u], t); });
+        mm16(aw[I], rd, 16 * u, [&](int t) { return f4c(sf[u], t); }, -1.f);
+        mm16(ar[I], rl, 16 * u, [&](int t) { return f4c(df[u], t); });
+      }
+    }
+    // d(K o gamma) = Mt^T dW for this channel tile: the dW tiles are the B operands
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      f32x4_t kg = zero4f();
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        float av[4], bv[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          av[t] = sM[(16 * kt + 4 * g + t) * LC + 16 * J + n] * sB[16 * J + n];
+          bv[t] = aw[kt][t];
+        }
+        mfma4(kg, av, bv);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = 16 * I + 4 * g + r;
-        AV[i * DK + c] = aq[r] * qq[I][r];
-        BV[i * DK + c] = ar[r] * kk[I][r];
-        DWg[i * DK + c] = -aw[r];
+        const int i = 16 * J + 4 * g + r;
+        AV[i * DK + c] = aq[J][r] * qq[J][r] + kg[r] * kk[J][r];
+        BV[i * DK + c] = ar[J][r] * kk[J][r];
+        DWg[i * DK + c] = aw[J][r];
         if (i < len) {
-          a.dq[kb + i * ks + c] = aq[r] * gm[I][r];
-          a.dk[kb + i * ks + c] = ar[r] * rh[I][r];
+          a.dq[kb + i * ks + c] = aq[J][r] * gm[J][r];
+          a.dk[kb + i * ks + c] = ar[J][r] * rh[J][r] + kg[r] * gm[J][r];
         }
       }
     }
   }
 
   // ---- B: dA = (dO Delta^T) o low;  dV = Mt^T dDelta
-  for (int job = wave; job < 16 + 4 * (DV / 16); job += NT / 64) {
+  for (int job = wave; job < 16 + 4 * (DV / 16); job += NTG / 64) {
     if (job < 16) {
       const int I = job / 4, J = job % 4;
       f32x4_t acc = zero4f();
@@ -777,14 +805,14 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a, int NC) {
   __syncthreads();
   float* RW = sR;  // dW [C][LK], where dO and Delta were
 #pragma unroll
-  for (int it = 0; it < C * DK / 4 / NT; ++it) {
-    const int x = tid + it * NT, i = x / (DK / 4), c = 4 * (x % (DK / 4));
+  for (int it = 0; it < C * DK / 4 / NTG; ++it) {
+    const int x = tid + it * NTG, i = x / (DK / 4), c = 4 * (x % (DK / 4));
     *(float4*)(RW + i * LK + c) = *(const float4*)(DWg + i * DK + c);
   }
   __syncthreads();
-  // dMt = (dDelta V^T + dW (K o gamma)^T) o low;  d(K o gamma) = Mt^T dW
-  for (int job = wave; job < 16 + 4 * (DK / 16); job += NT / 64) {
-    if (job < 16) {
+  // dMt = (dDelta V^T + dW (K o gamma)^T) o low
+  for (int job = wave; job < 16; job += NTG / 64) {
+    {
       const int I = job / 4, J = job % 4, j = 16 * J + n;
       f32x4_t acc = zero4f();
       if (J <= I) {
@@ -805,45 +833,18 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a, int NC) {
         const int i = 16 * I + 4 * g + r;
         sdT[i * LC + j] = j <= i ? acc[r] : 0.f;
       }
-    } else {
-      const int jj = job - 16, J = jj / (DK / 16), ct = jj % (DK / 16), c = 16 * ct + n;
-      f32x4_t acc = zero4f();
-#pragma unroll
-      for (int k0 = 0; k0 < C; k0 += 16) {
-        float av[4], bv[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int i = k0 + 4 * g + t;
-          av[t] = sM[i * LC + 16 * J + n] * sB[16 * J + n];
-          bv[t] = RW[i * LK + c];
-        }
-        mfma4(acc, av, bv);
-      }
-      float kv[4], gv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 16 * J + 4 * g + r;
-        kv[r] = in1(a.k, j, c);
-        gv[r] = GAM[j * DK + c];
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 16 * J + 4 * g + r;
-        AV[j * DK + c] += acc[r] * kv[r];
-        if (j < len) a.dk[kb + j * ks + c] += acc[r] * gv[r];
-      }
     }
   }
   __syncthreads();
 
   // ---- C: dbeta = colsum(dMt o M) + rowsum(dT o D);  X = dMt Mt^T;  dT = -(M^T X) o strict-low
-  for (int j = tid; j < C; j += NT) {
+  for (int j = tid; j < C; j += NTG) {
     float s = 0.f;
     for (int i = j; i < C; ++i) s += sdT[i * LC + j] * sM[i * LC + j];
     sdB[j] = s;
   }
   float* RX = sR;  // X [C][LC]
-  for (int job = wave; job < 16; job += NT / 64) {
+  for (int job = wave; job < 16; job += NTG / 64) {
     const int I = job / 4, J = job % 4;
     f32x4_t acc = zero4f();
 #pragma unroll
@@ -861,7 +862,7 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a, int NC) {
     for (int r = 0; r < 4; ++r) RX[(16 * I + 4 * g + r) * LC + 16 * J + n] = acc[r];
   }
   __syncthreads();
-  for (int job = wave; job < 16; job += NT / 64) {
+  for (int job = wave; job < 16; job += NTG / 64) {
     const int I = job / 4, J = job % 4;
     f32x4_t acc = zero4f();
     if (J <= I) {
@@ -884,7 +885,7 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a, int NC) {
     }
   }
   __syncthreads();
-  for (int i = tid; i < C; i += NT) {
+  for (int i = tid; i < C; i += NTG) {
     float s = 0.f;
 #pragma unroll 8
     for (int j = 0; j < i; ++j) s += sdT[i * LC + j] * ch[L.D + i * C + j];
@@ -899,8 +900,8 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a, int NC) {
   // r(i, e_M), r(i, e_M) = pi_i (blocks between) (M = 0..2)
   float *RKS = sR, *RQP = sR + C * LK, *RKP = sR + 2 * C * LK;
 #pragma unroll
-  for (int it = 0; it < C * DK / 4 / NT; ++it) {
-    const int x = tid + it * NT, i = x / (DK / 4), c = 4 * (x % (DK / 4));
+  for (int it = 0; it < C * DK / 4 / NTG; ++it) {
+    const int x = tid + it * NTG, i = x / (DK / 4), c = 4 * (x % (DK / 4));
     const float4 kv = in4(a.k, i, c), qv = in4(a.q, i, c);
     const float4 sg = *(const float4*)(SIG + i * DK + c), pn = *(const float4*)(PIN + i * DK + c);
     *(float4*)(RKS + i * LK + c) = mul4(kv, sg);
@@ -908,7 +909,7 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a, int NC) {
     *(float4*)(RKP + i * LK + c) = mul4(kv, pn);
   }
   __syncthreads();
-  for (int job = wave; job < 12 * (DK / 16); job += NT / 64) {
+  for (int job = wave; job < 12 * (DK / 16); job += NTG / 64) {
     const int ct = job % (DK / 16), p6 = (job / (DK / 16)) % 6, mat = job / (DK / 16) / 6;
     // (M, I): (1,1) (1,2) (1,3) (2,2) (2,3) (3,3)
     const int Mb = p6 < 3 ? 1 : (p6 < 5 ? 2 : 3), I = Mb + (p6 < 3 ? p6 : (p6 < 5 ? p6 - 3 : 0));
@@ -930,7 +931,7 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a, int NC) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) out[(16 * I + 4 * g + r) * DK + c] = acc[r];
   }
-  for (int job = wave; job < 3 * (DK / 16); job += NT / 64) {
+  for (int job = wave; job < 3 * (DK / 16); job += NTG / 64) {
     const int Mb = job / (DK / 16), ct = job % (DK / 16), s = 16 * Mb, c = 16 * ct + n;
     f32x4_t acc = zero4f();
     for (int I = Mb + 1; I < NB; ++I) {
@@ -959,14 +960,14 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a, int NC) {
   // ---- E: stage q, k, alpha; per (channel, block) items
   float *RQ = sR, *RK = sR + C * LK, *RA = sR + 2 * C * LK;
 #pragma unroll
-  for (int it = 0; it < C * DK / 4 / NT; ++it) {
-    const int x = tid + it * NT, i = x / (DK / 4), c = 4 * (x % (DK / 4));
+  for (int it = 0; it < C * DK / 4 / NTG; ++it) {
+    const int x = tid + it * NTG, i = x / (DK / 4), c = 4 * (x % (DK / 4));
     *(float4*)(RQ + i * LK + c) = in4(a.q, i, c);
     *(float4*)(RK + i * LK + c) = in4(a.k, i, c);
     *(float4*)(RA + i * LK + c) = i < len ? ld4<T>(a.alpha, kb + i * ks + c) : make_float4(1.f, 1.f, 1.f, 1.f);
   }
   __syncthreads();
-  for (int item = tid; item < DK * NB; item += NT) {
+  for (int item = tid; item < DK * NB; item += NTG) {
     const int c = item % DK, Mb = item / DK, s = Mb * SUB;
     float al[SUB], qv[SUB], kv[SUB], pin[SUB], pa[SUB], pd[SUB];
 #pragma unroll
@@ -1087,15 +1088,15 @@ static hipError_t launch_bwd_dk(const BwdArgs& a, int NC) {
   const int BH = a.B * a.H, walks = BH * (a.Dv / VTW);
   hipStream_t st = (hipStream_t)a.stream;
   if (NC > 0) {
-    hipLaunchKernelGGL((bwd_records_kernel<T, DK>), dim3(BH * NC), dim3(NT), 0, st, a, NC);
+    hipLaunchKernelGGL((bwd_records_kernel<T, DK>), dim3(BH * NC), dim3(DK == 128 ? NTG : NT), 0, st, a, NC);
     hipLaunchKernelGGL((bwd_state_kernel<T, DK>), dim3(walks), dim3(NT), 0, st, a, NC);
   }
   hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK>), dim3(walks), dim3(NT), 0, st, a, NC);
   if (NC > 0) {
     if (a.Dv == 64)
-      hipLaunchKernelGGL((bwd_grads_kernel<T, DK, 64>), dim3(BH * NC), dim3(NT), 0, st, a, NC);
+      hipLaunchKernelGGL((bwd_grads_kernel<T, DK, 64>), dim3(BH * NC), dim3(NTG), 0, st, a, NC);
     else
-      hipLaunchKernelGGL((bwd_grads_kernel<T, DK, 128>), dim3(BH * NC), dim3(NT), 0, st, a, NC);
+      hipLaunchKernelGGL((bwd_grads_kernel<T, DK, 128>), dim3(BH * NC), dim3(NTG), 0, st, a, NC);
   }
   return hipGetLastError();
 }
