@@ -280,6 +280,8 @@ __global__ __launch_bounds__(DK == 128 ? NTG : NT) void bwd_records_kernel(BwdAr
       const int i = I * SUB + r;
       ch[L.gam + i * DK + c] = before * pi[it][r];
       ch[L.rho + i * DK + c] = after * sg[it][r];
+      ch[L.KR + i * DK + c] = kv[it][r] * (after * sg[it][r]);
+      ch[L.QG + i * DK + c] = qv[it][r] * (before * pi[it][r]);
       R0[i * LK + c] = qv[it][r] * pi[it][r];
       R1[i * LK + c] = kv[it][r] * pi[it][r];
       R2[i * LK + c] = kv[it][r] * sg[it][r];
@@ -448,10 +450,12 @@ __global__ __launch_bounds__(DK == 128 ? NTG : NT) void bwd_records_kernel(BwdAr
 // Only the chunk's shared operands are staged in LDS (row strides padded by four floats),
 // with vector loads issued together.
 
-// bwd_state_kernel: chunks in order; writes the chunk-start state S_n and Delta_n.
+// bwd_state_kernel: chunks in order; writes the chunk-start state S_n and Delta_n.  The
+// next chunk's operands are loaded into registers while the current one computes.
 template <typename T, int DK>
 __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC) {
   constexpr int LM = C + 4, LW = DK + 4, LV = VTW + 4;
+  constexpr int NM = C * C / 4 / NT, NW = C * DK / 4 / NT, NV = C * VTW / 4 / NT;
   __shared__ float sM[C * LM], sW[C * LW], sKrT[DK * LM], sV[C * LV], sGl[DK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, g = lane >> 4;
   const int dv = a.Dv, ntile = dv / VTW, bh = blockIdx.x / ntile, v0 = (blockIdx.x % ntile) * VTW;
@@ -462,46 +466,65 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC) {
   for (int I = 0; I < DK / 16; ++I)
 #pragma unroll
     for (int r = 0; r < 4; ++r) S[I][r] = a.s0 ? a.s0[((size_t)bh * DK + 16 * I + 4 * g + r) * dv + col] : 0.f;
-  for (int nc = 0; nc < NC; ++nc) {
-    const ChunkGeom cg = chunk_geom(bh * NC + nc, NC, a.H, a.T);
-    float* ch = a.ws + (size_t)(bh * NC + nc) * L.total;
-    const size_t kb = row0(cg, a.T, a.H, DK), ks = (size_t)a.H * DK;
-    const size_t vb = row0(cg, a.T, a.H, dv), vs = (size_t)a.H * dv;
-    const size_t bb = ((size_t)cg.b * a.T + cg.t0) * a.H + cg.h;
-    __syncthreads();  // the previous chunk's LDS reads are done
-    // M; W; (K o rho)^T; diag(beta) V (so that M (beta o V) = Mt V); gamma_last
+  // one chunk's operands in registers: M; W; K o rho; V and beta; gamma_last.  Step st
+  // moves chunk st - 1 from registers to LDS, issues the loads of chunk st, then computes
+  // chunk st - 1 while they are in flight.
+  float4 pm[NM], pw[NW], pk[NW], pv[NV];
+  float pb[NV], pg = 0.f;
+  for (int st = 0; st <= NC; ++st) {
+    if (st > 0) {
+      __syncthreads();  // the previous chunk's LDS reads are done
 #pragma unroll
-    for (int it = 0; it < C * C / 4 / NT; ++it) {
-      const int x = tid + it * NT, i = x / (C / 4), j = 4 * (x % (C / 4));
-      *(float4*)(sM + i * LM + j) = *(const float4*)(ch + L.M + i * C + j);
-    }
-#pragma unroll
-    for (int it = 0; it < C * DK / 4 / NT; ++it) {
-      const int x = tid + it * NT, i = x / (DK / 4), c = 4 * (x % (DK / 4));
-      *(float4*)(sW + i * LW + c) = *(const float4*)(ch + L.W + i * DK + c);
-      const float4 kv = i < cg.len ? ld4<T>(a.k, kb + i * ks + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-      const float4 rv = *(const float4*)(ch + L.rho + i * DK + c);
-      sKrT[(c + 0) * LM + i] = kv.x * rv.x;
-      sKrT[(c + 1) * LM + i] = kv.y * rv.y;
-      sKrT[(c + 2) * LM + i] = kv.z * rv.z;
-      sKrT[(c + 3) * LM + i] = kv.w * rv.w;
-    }
-#pragma unroll
-    for (int it = 0; it < C * VTW / 4 / NT; ++it) {
-      const int x = tid + it * NT, j = x / (VTW / 4), c = 4 * (x % (VTW / 4));
-      float4 vv = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (j < cg.len) {
-        vv = ld4<T>(a.v, vb + j * vs + v0 + c);
-        const float bt = Elem<T>::load(a.beta, bb + (size_t)j * a.H);
-        vv.x *= bt;
-        vv.y *= bt;
-        vv.z *= bt;
-        vv.w *= bt;
+      for (int it = 0; it < NM; ++it) {
+        const int x = tid + it * NT, i = x / (C / 4), j = 4 * (x % (C / 4));
+        *(float4*)(sM + i * LM + j) = pm[it];
       }
-      *(float4*)(sV + j * LV + c) = vv;
+#pragma unroll
+      for (int it = 0; it < NW; ++it) {
+        const int x = tid + it * NT, i = x / (DK / 4), c = 4 * (x % (DK / 4));
+        *(float4*)(sW + i * LW + c) = pw[it];
+        sKrT[(c + 0) * LM + i] = pk[it].x;
+        sKrT[(c + 1) * LM + i] = pk[it].y;
+        sKrT[(c + 2) * LM + i] = pk[it].z;
+        sKrT[(c + 3) * LM + i] = pk[it].w;
+      }
+#pragma unroll
+      for (int it = 0; it < NV; ++it) {
+        const int x = tid + it * NT, j = x / (VTW / 4), c = 4 * (x % (VTW / 4));
+        const float b = pb[it];
+        *(float4*)(sV + j * LV + c) = make_float4(pv[it].x * b, pv[it].y * b, pv[it].z * b, pv[it].w * b);
+      }
+      if (tid < DK) sGl[tid] = pg;
+      __syncthreads();
     }
-    for (int c = tid; c < DK; c += NT) sGl[c] = ch[L.gam + (C - 1) * DK + c];
-    __syncthreads();
+    if (st < NC) {
+      const ChunkGeom cg = chunk_geom(bh * NC + st, NC, a.H, a.T);
+      const float* cl = a.ws + (size_t)(bh * NC + st) * L.total;
+      const size_t vb = row0(cg, a.T, a.H, dv), vs = (size_t)a.H * dv;
+      const size_t bb = ((size_t)cg.b * a.T + cg.t0) * a.H + cg.h;
+#pragma unroll
+      for (int it = 0; it < NM; ++it) {
+        const int x = tid + it * NT, i = x / (C / 4), j = 4 * (x % (C / 4));
+        pm[it] = *(const float4*)(cl + L.M + i * C + j);
+      }
+#pragma unroll
+      for (int it = 0; it < NW; ++it) {
+        const int x = tid + it * NT, i = x / (DK / 4), c = 4 * (x % (DK / 4));
+        pw[it] = *(const float4*)(cl + L.W + i * DK + c);
+        pk[it] = *(const float4*)(cl + L.KR + i * DK + c);
+      }
+#pragma unroll
+      for (int it = 0; it < NV; ++it) {
+        const int x = tid + it * NT, j = x / (VTW / 4), c = 4 * (x % (VTW / 4));
+        const bool in = j < cg.len;
+        pv[it] = in ? ld4<T>(a.v, vb + j * vs + v0 + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+        pb[it] = in ? Elem<T>::load(a.beta, bb + (size_t)j * a.H) : 0.f;
+      }
+      if (tid < DK) pg = cl[L.gam + (C - 1) * DK + tid];
+    }
+    if (st == 0) continue;
+    const int nc = st - 1;
+    float* ch = a.ws + (size_t)(bh * NC + nc) * L.total;
 #pragma unroll
     for (int I = 0; I < DK / 16; ++I)
 #pragma unroll
@@ -538,10 +561,12 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC) {
 }
 
 // bwd_adjoint_kernel: chunks in reverse; writes the end-state adjoint dS'_n and dDelta_n
-// of every chunk, and dS_0.
+// of every chunk, and dS_0.  The next chunk's operands are loaded into registers while
+// the current one computes.
 template <typename T, int DK>
 __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC) {
   constexpr int LK = DK + 4, LM = C + 4, LV = VTW + 4;
+  constexpr int NM = C * C / 4 / NT, NW = C * DK / 4 / NT, NV = C * VTW / 4 / NT;
   __shared__ float sKr[C * LK], sAT[C * LM], sQgT[DK * LM], sWT[DK * LM], sO[C * LV], sGl[DK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, g = lane >> 4;
   const int dv = a.Dv, ntile = dv / VTW, bh = blockIdx.x / ntile, v0 = (blockIdx.x % ntile) * VTW;
@@ -552,48 +577,70 @@ __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC) {
   for (int I = 0; I < DK / 16; ++I)
 #pragma unroll
     for (int r = 0; r < 4; ++r) dS[I][r] = a.dsT ? a.dsT[((size_t)bh * DK + 16 * I + 4 * g + r) * dv + col] : 0.f;
-  for (int nc = NC - 1; nc >= 0; --nc) {
-    const ChunkGeom cg = chunk_geom(bh * NC + nc, NC, a.H, a.T);
+  // one chunk's operands in registers: K o rho; Q o gamma; W; A; dO; gamma_last.  Step st
+  // moves chunk NC - st from registers to LDS, issues the loads of chunk NC - 1 - st, then
+  // computes chunk NC - st while they are in flight.
+  float4 pk[NW], pq[NW], pw[NW], pa[NM], po[NV];
+  float pg = 0.f;
+  for (int st = 0; st <= NC; ++st) {
+    if (st > 0) {
+      __syncthreads();
+#pragma unroll
+      for (int it = 0; it < NW; ++it) {
+        const int x = tid + it * NT, i = x / (DK / 4), c = 4 * (x % (DK / 4));
+        *(float4*)(sKr + i * LK + c) = pk[it];
+        sQgT[(c + 0) * LM + i] = pq[it].x;
+        sQgT[(c + 1) * LM + i] = pq[it].y;
+        sQgT[(c + 2) * LM + i] = pq[it].z;
+        sQgT[(c + 3) * LM + i] = pq[it].w;
+        sWT[(c + 0) * LM + i] = pw[it].x;
+        sWT[(c + 1) * LM + i] = pw[it].y;
+        sWT[(c + 2) * LM + i] = pw[it].z;
+        sWT[(c + 3) * LM + i] = pw[it].w;
+      }
+#pragma unroll
+      for (int it = 0; it < NM; ++it) {
+        const int x = tid + it * NT, j = x / (C / 4), i = 4 * (x % (C / 4));
+        sAT[(i + 0) * LM + j] = pa[it].x;
+        sAT[(i + 1) * LM + j] = pa[it].y;
+        sAT[(i + 2) * LM + j] = pa[it].z;
+        sAT[(i + 3) * LM + j] = pa[it].w;
+      }
+#pragma unroll
+      for (int it = 0; it < NV; ++it) {
+        const int x = tid + it * NT, i = x / (VTW / 4), c = 4 * (x % (VTW / 4));
+        *(float4*)(sO + i * LV + c) = po[it];
+      }
+      if (tid < DK) sGl[tid] = pg;
+      __syncthreads();
+    }
+    if (st < NC) {
+      const int ld = NC - 1 - st;
+      const ChunkGeom cg = chunk_geom(bh * NC + ld, NC, a.H, a.T);
+      const float* cl = a.ws + (size_t)(bh * NC + ld) * L.total;
+      const size_t vb = row0(cg, a.T, a.H, dv), vs = (size_t)a.H * dv;
+#pragma unroll
+      for (int it = 0; it < NW; ++it) {
+        const int x = tid + it * NT, i = x / (DK / 4), c = 4 * (x % (DK / 4));
+        pk[it] = *(const float4*)(cl + L.KR + i * DK + c);
+        pq[it] = *(const float4*)(cl + L.QG + i * DK + c);
+        pw[it] = *(const float4*)(cl + L.W + i * DK + c);
+      }
+#pragma unroll
+      for (int it = 0; it < NM; ++it) {
+        const int x = tid + it * NT, j = x / (C / 4), i = 4 * (x % (C / 4));
+        pa[it] = *(const float4*)(cl + L.A + j * C + i);
+      }
+#pragma unroll
+      for (int it = 0; it < NV; ++it) {
+        const int x = tid + it * NT, i = x / (VTW / 4), c = 4 * (x % (VTW / 4));
+        po[it] = i < cg.len ? ld4<T>(a.dO, vb + i * vs + v0 + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      if (tid < DK) pg = cl[L.gam + (C - 1) * DK + tid];
+    }
+    if (st == 0) continue;
+    const int nc = NC - st;
     float* ch = a.ws + (size_t)(bh * NC + nc) * L.total;
-    const size_t kb = row0(cg, a.T, a.H, DK), ks = (size_t)a.H * DK;
-    const size_t vb = row0(cg, a.T, a.H, dv), vs = (size_t)a.H * dv;
-    __syncthreads();
-    // K o rho; A^T; (Q o gamma)^T; W^T; dO; gamma_last
-#pragma unroll
-    for (int it = 0; it < C * DK / 4 / NT; ++it) {
-      const int x = tid + it * NT, i = x / (DK / 4), c = 4 * (x % (DK / 4));
-      const bool in = i < cg.len;
-      const float4 kv = in ? ld4<T>(a.k, kb + i * ks + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-      const float4 qv = in ? ld4<T>(a.q, kb + i * ks + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-      const float4 rv = *(const float4*)(ch + L.rho + i * DK + c);
-      const float4 gv = *(const float4*)(ch + L.gam + i * DK + c);
-      const float4 wv = *(const float4*)(ch + L.W + i * DK + c);
-      *(float4*)(sKr + i * LK + c) = make_float4(kv.x * rv.x, kv.y * rv.y, kv.z * rv.z, kv.w * rv.w);
-      sQgT[(c + 0) * LM + i] = qv.x * gv.x;
-      sQgT[(c + 1) * LM + i] = qv.y * gv.y;
-      sQgT[(c + 2) * LM + i] = qv.z * gv.z;
-      sQgT[(c + 3) * LM + i] = qv.w * gv.w;
-      sWT[(c + 0) * LM + i] = wv.x;
-      sWT[(c + 1) * LM + i] = wv.y;
-      sWT[(c + 2) * LM + i] = wv.z;
-      sWT[(c + 3) * LM + i] = wv.w;
-    }
-#pragma unroll
-    for (int it = 0; it < C * C / 4 / NT; ++it) {
-      const int x = tid + it * NT, j = x / (C / 4), i = 4 * (x % (C / 4));
-      const float4 av = *(const float4*)(ch + L.A + j * C + i);
-      sAT[(i + 0) * LM + j] = av.x;
-      sAT[(i + 1) * LM + j] = av.y;
-      sAT[(i + 2) * LM + j] = av.z;
-      sAT[(i + 3) * LM + j] = av.w;
-    }
-#pragma unroll
-    for (int it = 0; it < C * VTW / 4 / NT; ++it) {
-      const int x = tid + it * NT, i = x / (VTW / 4), c = 4 * (x % (VTW / 4));
-      *(float4*)(sO + i * LV + c) = i < cg.len ? ld4<T>(a.dO, vb + i * vs + v0 + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    for (int c = tid; c < DK; c += NT) sGl[c] = ch[L.gam + (C - 1) * DK + c];
-    __syncthreads();
 #pragma unroll
     for (int I = 0; I < DK / 16; ++I)
 #pragma unroll

@@ -73,10 +73,11 @@ struct BwdArgs {
 };
 
 // fp32 offsets inside one chunk's workspace block of the backward (C = 64 rows, NB = 4
-// blocks of 16): gate products, A, D, M, W (records); S_n, Delta_n (forward walk);
+// blocks of 16): gate products, A, D, M, W, K o rho, Q o gamma (records); S_n, Delta_n
+// (forward walk);
 // dS'_n, dDelta_n (adjoint walk); scratch of the gradient kernel.
 struct BwdLayout {
-  int gam, rho, pin, sig, pib, A, D, M, W, S, DL, DS, DDL, AV, BV, DW, F, PA, PD, total;
+  int gam, rho, pin, sig, pib, A, D, M, W, KR, QG, S, DL, DS, DDL, AV, BV, DW, F, PA, PD, total;
   __host__ __device__ BwdLayout(int dk, int dv) {
     const int C = 64, CK = C * dk;
     gam = 0;
@@ -88,7 +89,9 @@ struct BwdLayout {
     D = A + C * C;
     M = D + C * C;
     W = M + C * C;
-    S = W + CK;
+    KR = W + CK;  // K o rho
+    QG = KR + CK; // Q o gamma
+    S = QG + CK;
     DL = S + dk * dv;
     DS = DL + C * dv;
     DDL = DS + dk * dv;
