@@ -16,7 +16,7 @@
  * negative gates.  The readout after the update is the reading this library
  * implements (the pages print no readout).
  *
- * Two entry points:
+ * Entry points:
  *   kda_chunk_fwd   -- chunkwise-parallel WY forward over whole sequences
  *                      (prefill), the chunk-WY form of the SFDA page ("El
  *                      Teorema de Chunk-WY Constructivo") with the decay-
@@ -24,7 +24,12 @@
  *                      (section 3), chunk C = 64;
  *   kda_decode_step -- one recurrent token with the state updated in place
  *                      (constant-memory inference, "Complex KDA" summary,
- *                      section on practical implications).
+ *                      section on practical implications);
+ *   kda_chunk_bwd   -- the gradients of the chunk forward (training), declared
+ *                      with its workspace query further down.
+ * Variants further down: the two-pass forward with a caller workspace, packed
+ * variable-length batches, multi-token decode, Gated DeltaNet-2 gates and SFDA
+ * complex gates.
  *
  * Conventions shared by all entry points
  *   - Every pointer except `shape` is a DEVICE pointer on the current HIP
