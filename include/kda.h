@@ -255,7 +255,7 @@ int kda_sfda_decode_tokens(const kda_shape* shape, const void* q, const void* k,
  *   dbeta           : [B, T, H] fp32 output
  *   d_initial_state : [B, H, dk, dv] fp32 output, or NULL when not wanted
  *   workspace       : kda_chunk_bwd_workspace_size(shape) bytes of device memory,
- *                     256-byte aligned (about 740 KB per chunk of 64 tokens and head at
+ *                     256-byte aligned (about 805 KB per chunk of 64 tokens and head at
  *                     dk = dv = 128); its contents on entry do not matter.
  * Supported: dk, dv in {64, 128}, bf16 or fp32 inputs, chunk 0 or 64.  q, k, v, alpha,
  * d_o, the outputs and the states need 16-byte alignment, beta that of its element type
