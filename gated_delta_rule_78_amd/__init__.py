@@ -16,7 +16,8 @@ import os
 
 __all__ = ["chunk_fwd", "chunk_records", "chunk_apply_records", "chunk_fwd_debug", "decode_step",
            "gdn2_chunk_fwd", "gdn2_decode_step", "decode_tokens", "gdn2_decode_tokens", "chunk_fwd_varlen",
-           "sfda_chunk_fwd", "sfda_decode_step", "sfda_decode_tokens", "chunk_bwd", "bwd_workspace_size",
+           "sfda_chunk_fwd", "sfda_decode_step", "sfda_decode_tokens", "chunk_bwd", "chunk_bwd_varlen",
+           "bwd_workspace_size",
            "workspace_size", "pick_path", "lib", "version", "status_string",
            "LIB_PATH", "KdaError", "Shape", "BF16", "F32"]
 
@@ -88,6 +89,11 @@ def lib() -> ctypes.CDLL:
         L.kda_chunk_bwd_workspace_size.restype = ctypes.c_size_t
         L.kda_chunk_bwd.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.kda_chunk_bwd.restype = ctypes.c_int
+        L.kda_chunk_bwd_varlen_workspace_size.argtypes = [SP, ctypes.c_int]
+        L.kda_chunk_bwd_varlen_workspace_size.restype = ctypes.c_size_t
+        L.kda_chunk_bwd_varlen.argtypes = [SP, P, ctypes.c_int, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                           ctypes.c_size_t, P]
+        L.kda_chunk_bwd_varlen.restype = ctypes.c_int
         L.kda_status_string.argtypes = [ctypes.c_int]
         L.kda_status_string.restype = ctypes.c_char_p
         L.kda_version.argtypes = []
@@ -547,4 +553,50 @@ def chunk_bwd(q, k, v, alpha, beta, d_o, initial_state=None, d_final_state=None,
                              _stream(dev))
     if rc != 0:
         raise KdaError(rc, "kda_chunk_bwd")
+    return dq, dkk, dvv, dal, dbeta, ds0
+
+
+def chunk_bwd_varlen(q, k, v, alpha, beta, d_o, cu_seqlens, initial_state=None, d_final_state=None,
+                     want_d_initial=True, workspace=None):
+    """Backward of chunk_fwd_varlen: a packed batch (B = 1) of len(cu_seqlens) - 1 sequences
+    at the int32 device offsets cu_seqlens, each differentiated from its own start state.
+    initial_state, d_final_state: fp32 [n_seqs, H, dk, dv] or None.  Returns (dq, dk, dv,
+    dalpha, dbeta, d_initial_state [n_seqs, H, dk, dv] or None), all fp32."""
+    torch = _torch()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if B != 1:
+        raise ValueError("a packed batch has B = 1")
+    code = _dtype_code(q)
+    for t, nm in ((k, "k"), (alpha, "alpha"), (v, "v"), (beta, "beta"), (d_o, "d_o")):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{nm} must have the dtype of q")
+    if (k.shape != q.shape or alpha.shape != q.shape or v.shape != (B, T, H, dv) or beta.shape != (B, T, H)
+            or d_o.shape != (B, T, H, dv)):
+        raise ValueError("shapes: q, k, alpha [1,T,H,dk]; v, d_o [1,T,H,dv]; beta [1,T,H]")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+        raise TypeError("cu_seqlens must be a 1-d int32 tensor")
+    n = cu_seqlens.numel() - 1
+    for t, nm in ((initial_state, "initial_state"), (d_final_state, "d_final_state")):
+        if t is not None and (t.dtype != torch.float32 or t.shape != (n, H, dk, dv)):
+            raise ValueError(f"{nm} must be float32 [n_seqs,H,dk,dv]")
+    dev = q.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq, dkk, dal = (torch.zeros((B, T, H, dk), **f32) for _ in range(3))
+    dvv = torch.zeros((B, T, H, dv), **f32)
+    dbeta = torch.zeros((B, T, H), **f32)
+    ds0 = torch.empty((n, H, dk, dv), **f32) if want_d_initial else None
+    shape = Shape(B, T, H, dk, dv, 64, code)
+    need = int(lib().kda_chunk_bwd_varlen_workspace_size(ctypes.byref(shape), n))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check((q, k, v, alpha, beta, d_o, cu_seqlens, initial_state, d_final_state, workspace),
+           ("q", "k", "v", "alpha", "beta", "d_o", "cu_seqlens", "initial_state", "d_final_state", "workspace"), dev)
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = lib().kda_chunk_bwd_varlen(ctypes.byref(shape), _ptr(cu_seqlens), n, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                    _ptr(beta), _ptr(initial_state), _ptr(d_o), _ptr(d_final_state), _ptr(dq),
+                                    _ptr(dkk), _ptr(dvv), _ptr(dal), _ptr(dbeta), _ptr(ds0), _ptr(workspace),
+                                    ctypes.c_size_t(nbytes), _stream(dev))
+    if rc != 0:
+        raise KdaError(rc, "kda_chunk_bwd_varlen")
     return dq, dkk, dvv, dal, dbeta, ds0

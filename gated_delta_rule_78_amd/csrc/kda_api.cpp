@@ -216,6 +216,108 @@ int chunk_varlen_impl(const kda_shape* shape, const int* cu, int n_seqs, ChunkPt
   return kda::launch_state(a, p.ws) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+
+// ---- backward ---------------------------------------------------------------------
+
+struct BwdPtrs {
+  const void *q, *k, *v, *alpha, *beta;
+  const float* s0;
+  const void* d_o;
+  const float* dsT;
+  float *dq, *dk, *dv, *dalpha, *dbeta, *ds0;
+  void* ws;
+  size_t ws_bytes;
+};
+
+// Workspace of a packed batch's backward: chunk blocks [H][gmax], then the chunk table
+// (clamped offsets, (sequence, chunk) pairs, first chunk of each sequence, chunk count).
+struct BwdVarlenLayout {
+  int64_t gmax;
+  size_t off_cs, off_tab, off_base, off_total, bytes;
+};
+
+BwdVarlenLayout bwd_varlen_layout(const kda_shape& s, int n_seqs) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  BwdVarlenLayout L;
+  L.gmax = ((int64_t)s.T + 63) / 64 + n_seqs;
+  L.off_cs = up((size_t)s.H * L.gmax * kda::BwdLayout(s.dk, s.dv).total * sizeof(float));
+  L.off_tab = up(L.off_cs + (size_t)(n_seqs + 1) * 4);
+  L.off_base = up(L.off_tab + (size_t)L.gmax * 8);
+  L.off_total = up(L.off_base + (size_t)n_seqs * 4);
+  L.bytes = up(L.off_total + 4);
+  return L;
+}
+
+// n_seqs < 0: a fixed-length batch; else a packed batch of n_seqs sequences at cu
+int bwd_impl(const kda_shape* shape, const int* cu, int n_seqs, const BwdPtrs& p, void* stream) {
+  int es = 0;
+  int rc = check_shape(shape, false, &es);
+  if (rc) return rc;
+  const kda_shape& s = *shape;
+  const bool packed = n_seqs >= 0;
+  if (packed) {
+    if (s.B != 1 || n_seqs > (1 << 24)) return KDA_ERR_SHAPE;
+    if (((uintptr_t)cu & 3u) != 0) return KDA_ERR_ALIGN;
+  }
+  const int64_t rows = (int64_t)s.B * s.T * s.H;
+  const int64_t st_bytes = (int64_t)(packed ? n_seqs : s.B) * s.H * s.dk * s.dv * 4;
+  if (rows > 0 && (!p.q || !p.k || !p.v || !p.alpha || !p.beta || !p.d_o || !p.dq || !p.dk || !p.dv || !p.dalpha ||
+                   !p.dbeta))
+    return KDA_ERR_NULL;
+  const BwdVarlenLayout VL = packed ? bwd_varlen_layout(s, n_seqs) : BwdVarlenLayout{};
+  const size_t ws_need = packed ? VL.bytes : kda::bwd_workspace_bytes(s.B, s.T, s.H, s.dk, s.dv);
+  if (ws_need > 0 && !p.ws) return KDA_ERR_NULL;
+  if (p.ws_bytes < ws_need) return KDA_ERR_WORKSPACE;
+  // q, k, v, alpha and d_o move in vectors; beta is read per element
+  const void* in_ptrs[] = {p.q, p.k, p.v, p.alpha, p.d_o};
+  for (const void* x : in_ptrs)
+    if (x && misaligned(x)) return KDA_ERR_ALIGN;
+  if (p.beta && misaligned(p.beta, es)) return KDA_ERR_ALIGN;
+  const void* out_ptrs[] = {p.dq, p.dk, p.dv, p.dalpha, p.ds0, p.s0, p.dsT};
+  for (const void* x : out_ptrs)
+    if (x && misaligned(x)) return KDA_ERR_ALIGN;
+  if (p.dbeta && misaligned(p.dbeta, 4)) return KDA_ERR_ALIGN;
+  if (p.ws && ((uintptr_t)p.ws & 255u) != 0) return KDA_ERR_ALIGN;
+  const Range in[] = {range_of(p.q, rows * s.dk * es),       range_of(p.k, rows * s.dk * es),
+                      range_of(p.v, rows * s.dv * es),       range_of(p.alpha, rows * s.dk * es),
+                      range_of(p.beta, rows * es),           range_of(p.d_o, rows * s.dv * es),
+                      range_of(p.s0, p.s0 ? st_bytes : 0),   range_of(p.dsT, p.dsT ? st_bytes : 0),
+                      range_of(cu, packed ? (int64_t)(n_seqs + 1) * 4 : 0)};
+  const Range out[] = {range_of(p.dq, rows * s.dk * 4),      range_of(p.dk, rows * s.dk * 4),
+                       range_of(p.dv, rows * s.dv * 4),      range_of(p.dalpha, rows * s.dk * 4),
+                       range_of(p.dbeta, rows * 4),          range_of(p.ds0, p.ds0 ? st_bytes : 0),
+                       range_of(p.ws, (int64_t)ws_need)};
+  constexpr int nout = sizeof(out) / sizeof(out[0]);
+  for (int i = 0; i < nout; ++i) {
+    for (const Range& r : in)
+      if (overlap(out[i], r)) return KDA_ERR_ALIAS;
+    for (int j = i + 1; j < nout; ++j)
+      if (overlap(out[i], out[j])) return KDA_ERR_ALIAS;
+  }
+  kda::BwdArgs a{p.q,  p.k,  p.v,      p.alpha, p.beta,           p.d_o, p.s0, p.dsT, p.dq, p.dk, p.dv, p.dalpha,
+                 p.dbeta, p.ds0, (float*)p.ws, s.B, s.T, s.H, s.dk, s.dv, s.dtype == KDA_BF16, stream};
+  if (packed) {
+    if (n_seqs == 0) return KDA_OK;
+    char* ws = (char*)p.ws;
+    kda::ChunkArgs t{};
+    t.T = s.T;
+    t.stream = stream;
+    t.cu = cu;
+    t.n_seqs = n_seqs;
+    t.gmax = (int)VL.gmax;
+    if (kda::launch_varlen_table(t, (int*)(ws + VL.off_cs), (int*)(ws + VL.off_tab), (int*)(ws + VL.off_base),
+                                 (int*)(ws + VL.off_total)) != hipSuccess)
+      return KDA_ERR_HIP;
+    a.cs = (const int*)(ws + VL.off_cs);
+    a.ctab = (const int*)(ws + VL.off_tab);
+    a.cbase = (const int*)(ws + VL.off_base);
+    a.ctotal = (const int*)(ws + VL.off_total);
+    a.n_seqs = n_seqs;
+    a.gmax = (int)VL.gmax;
+  }
+  return kda::launch_bwd(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -442,46 +544,28 @@ int kda_chunk_bwd(const kda_shape* shape, const void* q, const void* k, const vo
                   const void* beta, const float* initial_state, const void* d_o, const float* d_final_state,
                   float* dq, float* dk, float* dv, float* dalpha, float* dbeta, float* d_initial_state,
                   void* workspace, size_t workspace_bytes, void* stream) {
+  const BwdPtrs p{q, k, v, alpha, beta, initial_state, d_o, d_final_state, dq, dk, dv, dalpha, dbeta, d_initial_state,
+                  workspace, workspace_bytes};
+  return bwd_impl(shape, nullptr, -1, p, stream);
+}
+
+size_t kda_chunk_bwd_varlen_workspace_size(const kda_shape* shape, int n_seqs) {
   int es = 0;
-  int rc = check_shape(shape, false, &es);
-  if (rc) return rc;
-  const kda_shape& s = *shape;
-  const int64_t rows = (int64_t)s.B * s.T * s.H;
-  const int64_t st_bytes = (int64_t)s.B * s.H * s.dk * s.dv * 4;
-  if (rows > 0 && (!q || !k || !v || !alpha || !beta || !d_o || !dq || !dk || !dv || !dalpha || !dbeta))
-    return KDA_ERR_NULL;
-  const size_t ws_need = kda::bwd_workspace_bytes(s.B, s.T, s.H, s.dk, s.dv);
-  if (ws_need > 0 && !workspace) return KDA_ERR_NULL;
-  if (workspace_bytes < ws_need) return KDA_ERR_WORKSPACE;
-  // q, k, v, alpha and d_o move in vectors; beta is read per element
-  const void* in_ptrs[] = {q, k, v, alpha, d_o};
-  for (const void* x : in_ptrs)
-    if (x && misaligned(x)) return KDA_ERR_ALIGN;
-  if (beta && misaligned(beta, es)) return KDA_ERR_ALIGN;
-  const void* out_ptrs[] = {dq, dk, dv, dalpha, d_initial_state, initial_state, d_final_state};
-  for (const void* x : out_ptrs)
-    if (x && misaligned(x)) return KDA_ERR_ALIGN;
-  if (dbeta && misaligned(dbeta, 4)) return KDA_ERR_ALIGN;
-  if (workspace && ((uintptr_t)workspace & 255u) != 0) return KDA_ERR_ALIGN;
-  const Range in[] = {range_of(q, rows * s.dk * es),       range_of(k, rows * s.dk * es),
-                      range_of(v, rows * s.dv * es),       range_of(alpha, rows * s.dk * es),
-                      range_of(beta, rows * es),           range_of(d_o, rows * s.dv * es),
-                      range_of(initial_state, initial_state ? st_bytes : 0),
-                      range_of(d_final_state, d_final_state ? st_bytes : 0)};
-  const Range out[] = {range_of(dq, rows * s.dk * 4),      range_of(dk, rows * s.dk * 4),
-                       range_of(dv, rows * s.dv * 4),      range_of(dalpha, rows * s.dk * 4),
-                       range_of(dbeta, rows * 4),          range_of(d_initial_state, d_initial_state ? st_bytes : 0),
-                       range_of(workspace, (int64_t)ws_need)};
-  constexpr int nout = sizeof(out) / sizeof(out[0]);
-  for (int i = 0; i < nout; ++i) {
-    for (const Range& r : in)
-      if (overlap(out[i], r)) return KDA_ERR_ALIAS;
-    for (int j = i + 1; j < nout; ++j)
-      if (overlap(out[i], out[j])) return KDA_ERR_ALIAS;
-  }
-  kda::BwdArgs a{q,  k,  v,      alpha, beta,           d_o, initial_state, d_final_state, dq, dk, dv, dalpha,
-                 dbeta, d_initial_state, (float*)workspace, s.B, s.T, s.H, s.dk, s.dv, s.dtype == KDA_BF16, stream};
-  return kda::launch_bwd(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  if (check_shape(shape, false, &es) != KDA_OK || shape->B != 1 || n_seqs < 0 || n_seqs > (1 << 24)) return 0;
+  return bwd_varlen_layout(*shape, n_seqs).bytes;
+}
+
+int kda_chunk_bwd_varlen(const kda_shape* shape, const int* cu_seqlens, int n_seqs, const void* q, const void* k,
+                         const void* v, const void* alpha, const void* beta, const float* initial_state,
+                         const void* d_o, const float* d_final_state, float* dq, float* dk, float* dv,
+                         float* dalpha, float* dbeta, float* d_initial_state, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!shape) return KDA_ERR_NULL;
+  if (n_seqs < 0) return KDA_ERR_SHAPE;
+  if (!cu_seqlens) return KDA_ERR_NULL;
+  const BwdPtrs p{q, k, v, alpha, beta, initial_state, d_o, d_final_state, dq, dk, dv, dalpha, dbeta, d_initial_state,
+                  workspace, workspace_bytes};
+  return bwd_impl(shape, cu_seqlens, n_seqs, p, stream);
 }
 
 }  // extern "C"

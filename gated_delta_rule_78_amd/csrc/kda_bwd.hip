@@ -111,15 +111,46 @@ struct ChunkGeom {
   int b, h, n, t0, len;
 };
 
-__device__ __forceinline__ ChunkGeom chunk_geom(int g, int NC, int H, int T) {
+// Chunk n of a chain (fixed-length batch: chain = b H + h; packed batch: chain =
+// sequence H + h) and the index of its workspace block (fixed: chain NC + n; packed:
+// h gmax + the sequence's first global chunk + n).
+__device__ __forceinline__ ChunkGeom chain_chunk(const BwdArgs& a, int NC, int chain, int n, size_t* ws) {
   ChunkGeom q;
-  q.n = g % NC;
-  const int bh = g / NC;
-  q.b = bh / H;
-  q.h = bh % H;
-  q.t0 = q.n * C;
-  q.len = min(C, T - q.t0);
+  q.n = n;
+  q.h = chain % a.H;
+  if (!a.ctab) {
+    q.b = chain / a.H;
+    q.t0 = n * C;
+    q.len = min(C, a.T - q.t0);
+    *ws = (size_t)chain * NC + n;
+  } else {
+    const int s = chain / a.H;
+    q.b = 0;
+    q.t0 = a.cs[s] + n * C;
+    q.len = min(C, a.cs[s + 1] - q.t0);
+    *ws = (size_t)q.h * a.gmax + a.cbase[s] + n;
+  }
   return q;
+}
+
+// chunks in a chain
+__device__ __forceinline__ int chain_chunks(const BwdArgs& a, int NC, int chain) {
+  if (!a.ctab) return NC;
+  const int s = chain / a.H;
+  return (a.cs[s + 1] - a.cs[s] + C - 1) / C;
+}
+
+// the chunk of a per-chunk workgroup (fixed: blockIdx = chain NC + n; packed: blockIdx =
+// h gmax + global chunk); false for a packed batch's workgroups past the last chunk
+__device__ __forceinline__ bool block_chunk(const BwdArgs& a, int NC, ChunkGeom* q, size_t* ws) {
+  if (!a.ctab) {
+    *q = chain_chunk(a, NC, blockIdx.x / NC, blockIdx.x % NC, ws);
+    return true;
+  }
+  const int gc = blockIdx.x % a.gmax, h = blockIdx.x / a.gmax;
+  if (gc >= *a.ctotal) return false;
+  *q = chain_chunk(a, NC, a.ctab[2 * gc] * a.H + h, a.ctab[2 * gc + 1], ws);
+  return true;
 }
 
 // element offset of (b, t0, h, 0) in a [B, T, H, d] tensor
@@ -215,9 +246,11 @@ __global__ __launch_bounds__(DK == 128 ? NTG : NT) void bwd_records_kernel(BwdAr
   __shared__ float sPib[NB * DK], sB[C], sY[3][16][17];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, g = lane >> 4;
   const BwdLayout L(DK, a.Dv);
-  const ChunkGeom cg = chunk_geom(blockIdx.x, NC, a.H, a.T);
+  ChunkGeom cg;
+  size_t wsi;
+  if (!block_chunk(a, NC, &cg, &wsi)) return;
   const int len = cg.len;
-  float* ch = a.ws + (size_t)blockIdx.x * L.total;
+  float* ch = a.ws + wsi * L.total;
   const size_t kb = row0(cg, a.T, a.H, DK), ks = (size_t)a.H * DK;
   const size_t bb = ((size_t)cg.b * a.T + cg.t0) * a.H + cg.h;
   float *R0 = sR, *R1 = sR + C * LK, *R2 = sR + 2 * C * LK;
@@ -459,6 +492,7 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC) {
   __shared__ float sM[C * LM], sW[C * LW], sKrT[DK * LM], sV[C * LV], sGl[DK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, g = lane >> 4;
   const int dv = a.Dv, ntile = dv / VTW, bh = blockIdx.x / ntile, v0 = (blockIdx.x % ntile) * VTW;
+  const int nch = chain_chunks(a, NC, bh);  // bh: the chain (b H + h, or sequence H + h)
   const int col = v0 + 16 * wave + n;  // this lane's state column
   const BwdLayout L(DK, dv);
   f32x4_t S[DK / 16];
@@ -471,7 +505,7 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC) {
   // chunk st - 1 while they are in flight.
   float4 pm[NM], pw[NW], pk[NW], pv[NV];
   float pb[NV], pg = 0.f;
-  for (int st = 0; st <= NC; ++st) {
+  for (int st = 0; st <= nch; ++st) {
     if (st > 0) {
       __syncthreads();  // the previous chunk's LDS reads are done
 #pragma unroll
@@ -497,9 +531,10 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC) {
       if (tid < DK) sGl[tid] = pg;
       __syncthreads();
     }
-    if (st < NC) {
-      const ChunkGeom cg = chunk_geom(bh * NC + st, NC, a.H, a.T);
-      const float* cl = a.ws + (size_t)(bh * NC + st) * L.total;
+    if (st < nch) {
+      size_t wsl;
+      const ChunkGeom cg = chain_chunk(a, NC, bh, st, &wsl);
+      const float* cl = a.ws + wsl * L.total;
       const size_t vb = row0(cg, a.T, a.H, dv), vs = (size_t)a.H * dv;
       const size_t bb = ((size_t)cg.b * a.T + cg.t0) * a.H + cg.h;
 #pragma unroll
@@ -524,7 +559,9 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC) {
     }
     if (st == 0) continue;
     const int nc = st - 1;
-    float* ch = a.ws + (size_t)(bh * NC + nc) * L.total;
+    size_t wsc;
+    chain_chunk(a, NC, bh, nc, &wsc);
+    float* ch = a.ws + wsc * L.total;
 #pragma unroll
     for (int I = 0; I < DK / 16; ++I)
 #pragma unroll
@@ -545,7 +582,7 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) ch[L.DL + (16 * I + 4 * g + r) * dv + col] = acc[r];
     }
-    if (nc + 1 < NC) {
+    if (nc + 1 < nch) {
       // S' = gamma_L o S + (K o rho)^T Delta
 #pragma unroll
       for (int I = 0; I < DK / 16; ++I) {
@@ -570,6 +607,7 @@ __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC) {
   __shared__ float sKr[C * LK], sAT[C * LM], sQgT[DK * LM], sWT[DK * LM], sO[C * LV], sGl[DK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, g = lane >> 4;
   const int dv = a.Dv, ntile = dv / VTW, bh = blockIdx.x / ntile, v0 = (blockIdx.x % ntile) * VTW;
+  const int nch = chain_chunks(a, NC, bh);  // bh: the chain (b H + h, or sequence H + h)
   const int col = v0 + 16 * wave + n;
   const BwdLayout L(DK, dv);
   f32x4_t dS[DK / 16];
@@ -578,11 +616,11 @@ __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) dS[I][r] = a.dsT ? a.dsT[((size_t)bh * DK + 16 * I + 4 * g + r) * dv + col] : 0.f;
   // one chunk's operands in registers: K o rho; Q o gamma; W; A; dO; gamma_last.  Step st
-  // moves chunk NC - st from registers to LDS, issues the loads of chunk NC - 1 - st, then
-  // computes chunk NC - st while they are in flight.
+  // moves chunk nch - st from registers to LDS, issues the loads of chunk nch - 1 - st,
+  // then computes chunk nch - st while they are in flight.
   float4 pk[NW], pq[NW], pw[NW], pa[NM], po[NV];
   float pg = 0.f;
-  for (int st = 0; st <= NC; ++st) {
+  for (int st = 0; st <= nch; ++st) {
     if (st > 0) {
       __syncthreads();
 #pragma unroll
@@ -614,10 +652,11 @@ __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC) {
       if (tid < DK) sGl[tid] = pg;
       __syncthreads();
     }
-    if (st < NC) {
-      const int ld = NC - 1 - st;
-      const ChunkGeom cg = chunk_geom(bh * NC + ld, NC, a.H, a.T);
-      const float* cl = a.ws + (size_t)(bh * NC + ld) * L.total;
+    if (st < nch) {
+      const int ld = nch - 1 - st;
+      size_t wsl;
+      const ChunkGeom cg = chain_chunk(a, NC, bh, ld, &wsl);
+      const float* cl = a.ws + wsl * L.total;
       const size_t vb = row0(cg, a.T, a.H, dv), vs = (size_t)a.H * dv;
 #pragma unroll
       for (int it = 0; it < NW; ++it) {
@@ -639,8 +678,10 @@ __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC) {
       if (tid < DK) pg = cl[L.gam + (C - 1) * DK + tid];
     }
     if (st == 0) continue;
-    const int nc = NC - st;
-    float* ch = a.ws + (size_t)(bh * NC + nc) * L.total;
+    const int nc = nch - st;
+    size_t wsc;
+    chain_chunk(a, NC, bh, nc, &wsc);
+    float* ch = a.ws + wsc * L.total;
 #pragma unroll
     for (int I = 0; I < DK / 16; ++I)
 #pragma unroll
@@ -706,9 +747,11 @@ __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
   __shared__ float sB[C], sdB[C], sGl[DK], sPib[NB * DK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, g = lane >> 4;
   const BwdLayout L(DK, DV);
-  const ChunkGeom cg = chunk_geom(blockIdx.x, NC, a.H, a.T);
+  ChunkGeom cg;
+  size_t wsi;
+  if (!block_chunk(a, NC, &cg, &wsi)) return;
   const int len = cg.len;
-  float* ch = a.ws + (size_t)blockIdx.x * L.total;
+  float* ch = a.ws + wsi * L.total;
   const size_t kb = row0(cg, a.T, a.H, DK), ks = (size_t)a.H * DK;
   const size_t vb = row0(cg, a.T, a.H, DV), vs = (size_t)a.H * DV;
   const size_t bb = ((size_t)cg.b * a.T + cg.t0) * a.H + cg.h;
@@ -1132,18 +1175,21 @@ __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
 // ---------------------------------------------------------------------------------------
 template <typename T, int DK>
 static hipError_t launch_bwd_dk(const BwdArgs& a, int NC) {
-  const int BH = a.B * a.H, walks = BH * (a.Dv / VTW);
+  // per-chunk grid: B H NC (fixed) or H gmax (packed; workgroups past the chunk count
+  // exit); walks: one workgroup per (chain, 64 value columns)
+  const int chains = (a.ctab ? a.n_seqs : a.B) * a.H, walks = chains * (a.Dv / VTW);
+  const long per_chunk = a.ctab ? (long)a.H * a.gmax : (long)chains * NC;
   hipStream_t st = (hipStream_t)a.stream;
-  if (NC > 0) {
-    hipLaunchKernelGGL((bwd_records_kernel<T, DK>), dim3(BH * NC), dim3(DK == 128 ? NTG : NT), 0, st, a, NC);
+  if (per_chunk > 0) {
+    hipLaunchKernelGGL((bwd_records_kernel<T, DK>), dim3(per_chunk), dim3(DK == 128 ? NTG : NT), 0, st, a, NC);
     hipLaunchKernelGGL((bwd_state_kernel<T, DK>), dim3(walks), dim3(NT), 0, st, a, NC);
   }
   hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK>), dim3(walks), dim3(NT), 0, st, a, NC);
-  if (NC > 0) {
+  if (per_chunk > 0) {
     if (a.Dv == 64)
-      hipLaunchKernelGGL((bwd_grads_kernel<T, DK, 64>), dim3(BH * NC), dim3(NTG), 0, st, a, NC);
+      hipLaunchKernelGGL((bwd_grads_kernel<T, DK, 64>), dim3(per_chunk), dim3(NTG), 0, st, a, NC);
     else
-      hipLaunchKernelGGL((bwd_grads_kernel<T, DK, 128>), dim3(BH * NC), dim3(NTG), 0, st, a, NC);
+      hipLaunchKernelGGL((bwd_grads_kernel<T, DK, 128>), dim3(per_chunk), dim3(NTG), 0, st, a, NC);
   }
   return hipGetLastError();
 }
@@ -1154,7 +1200,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int NC) {
 }
 
 hipError_t launch_bwd(const BwdArgs& a) {
-  if ((long)a.B * a.H == 0) return hipSuccess;
+  if ((long)(a.ctab ? a.n_seqs : a.B) * a.H == 0) return hipSuccess;
   const int NC = (a.T + C - 1) / C;
   return a.bf16 ? launch_bwd_t<bf16_t>(a, NC) : launch_bwd_t<float>(a, NC);
 }

@@ -70,6 +70,13 @@ struct BwdArgs {
   int B, T, H, Dk, Dv;
   bool bf16;
   void* stream;
+  // packed variable-length batch (B = 1): the chunk table of launch_varlen_table in the
+  // workspace; states are [n_seqs, H, dk, dv]; chunk blocks are laid out [H][gmax]
+  const int* cs = nullptr;      // clamped offsets [n_seqs + 1]
+  const int* ctab = nullptr;    // (sequence, chunk) of every global chunk [gmax][2]
+  const int* cbase = nullptr;   // first global chunk of each sequence [n_seqs]
+  const int* ctotal = nullptr;  // number of chunks [1]
+  int n_seqs = 0, gmax = 0;
 };
 
 // fp32 offsets inside one chunk's workspace block of the backward (C = 64 rows, NB = 4

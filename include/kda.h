@@ -272,6 +272,26 @@ int kda_chunk_bwd(const kda_shape* shape, const void* q, const void* k, const vo
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The backward of a packed variable-length batch (the forward of kda_chunk_fwd_varlen):
+ * shape->B must be 1 and shape->T is the total token count; n_seqs sequences lie back to
+ * back at the device offsets cu_seqlens[0..n_seqs] (int32, non-decreasing, cu[0] = 0,
+ * cu[n_seqs] <= T; out-of-range offsets are clamped).  Each sequence is differentiated on
+ * its own, from its own start state: initial_state, d_final_state and d_initial_state are
+ * [n_seqs, H, dk, dv] fp32 (NULL as for kda_chunk_bwd).  Tokens past cu[n_seqs] get no
+ * gradient written.  workspace: kda_chunk_bwd_varlen_workspace_size(shape, n_seqs) bytes,
+ * 256-byte aligned.  Other arguments, layouts and errors as kda_chunk_bwd; no output may
+ * overlap cu_seqlens (KDA_ERR_ALIAS); a NULL cu_seqlens is KDA_ERR_NULL, B != 1 or
+ * n_seqs < 0 KDA_ERR_SHAPE.
+ */
+size_t kda_chunk_bwd_varlen_workspace_size(const kda_shape* shape, int n_seqs);  /* 0 if invalid */
+int kda_chunk_bwd_varlen(const kda_shape* shape, const int* cu_seqlens, int n_seqs, const void* q,
+                         const void* k, const void* v, const void* alpha, const void* beta,
+                         const float* initial_state, const void* d_o, const float* d_final_state,
+                         float* dq, float* dk, float* dv, float* dalpha, float* dbeta,
+                         float* d_initial_state, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
  * One recurrent decode step for every (b, h), state updated in place:
  *   S <- (I - beta k k^T) Diag(alpha) S + beta k v^T ;  o <- S^T q.
  *   state : [B, H, dk, dv] fp32, read and written in place.

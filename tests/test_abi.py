@@ -334,3 +334,26 @@ def test_bwd_argument_errors(L):
     # nothing to do: no pointers needed, d_initial_state still written (on the device)
     zero = kda.Shape(0, 64, 2, 64, 64, 64, 0)
     assert L.kda_chunk_bwd(ctypes.byref(zero), *([None] * 14), None, sz(0), None) == 0
+
+
+def test_bwd_varlen_argument_errors(L):
+    shape = kda.Shape(1, 300, 2, 64, 64, 64, 0)
+    need = L.kda_chunk_bwd_varlen_workspace_size(ctypes.byref(shape), 4)
+    assert need > 0
+    assert L.kda_chunk_bwd_varlen_workspace_size(ctypes.byref(kda.Shape(2, 300, 2, 64, 64, 64, 0)), 4) == 0
+    assert L.kda_chunk_bwd_varlen_workspace_size(ctypes.byref(shape), -1) == 0
+    sz = ctypes.c_size_t
+
+    def bwd(cu=_p(17), nseq=4, dq=_p(10), ws=_p(16), n=need, sh=shape):
+        return L.kda_chunk_bwd_varlen(ctypes.byref(sh), cu, nseq, _p(0), _p(1), _p(2), _p(3), _p(4), None, _p(5),
+                                      None, dq, _p(11), _p(12), _p(13), _p(14), _p(15), ws, sz(n), None)
+
+    assert bwd(cu=None) == NULL
+    assert bwd(ws=None) == NULL
+    assert bwd(n=need - 1) == WORKSPACE
+    assert bwd(cu=_p(17, off=2)) == ALIGN
+    assert bwd(dq=_p(17)) == ALIAS                 # a gradient over the offsets
+    assert bwd(ws=_p(17)) == ALIAS                 # the workspace over the offsets
+    assert bwd(sh=kda.Shape(2, 300, 2, 64, 64, 64, 0)) == SHAPE
+    assert bwd(nseq=-1) == SHAPE
+    assert bwd(nseq=0) == 0                        # nothing to do
