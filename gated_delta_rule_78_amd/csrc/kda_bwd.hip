@@ -44,11 +44,10 @@ constexpr int NTG = 512;  // threads per workgroup of the gradient kernel and, a
                           // records kernel (two waves per SIMD)
 
 // ---------------------------------------------------------------------------------------
-// One 16x16 fp32 tile: acc[i][j] = sum_k fa(i, k) fb(k, j), K a multiple of 4.  Lane
+// One 16x16 fp32 tile: acc[i][j] = sum_k fa(i, k) fb(k, j), K a multiple of 16.  Lane
 // (n = lane & 15, g = lane >> 4) feeds A[n][k0 + g] and B[k0 + g][n]; the result holds
-// element (4 g + r, n) in acc[r].
-// K a multiple of 16: the operands of the next 16 k are loaded while the current four
-// steps run.
+// element (4 g + r, n) in acc[r].  The operands of the next 16 k are loaded while the
+// current four steps run.
 template <class FA, class FB>
 __device__ __forceinline__ f32x4_t tile_mm(int K, FA fa, FB fb) {
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
@@ -80,32 +79,6 @@ __device__ __forceinline__ f32x4_t tile_mm(int K, FA fa, FB fb) {
   }
   return acc;
 }
-
-// Product over a grid of tm x tn tiles spread over the workgroup's waves:
-// fe(i, j, sum_k fa(i, k) fb(k, j)) for every i < 16 tm, j < 16 tn.
-template <class FA, class FB, class FE>
-__device__ __forceinline__ void wg_mm(int tm, int tn, int K, FA fa, FB fb, FE fe) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n = lane & 15, g = lane >> 4;
-  for (int t = wave; t < tm * tn; t += NT / 64) {
-    const int i0 = (t / tn) * 16, j0 = (t % tn) * 16;
-    const f32x4_t acc = tile_mm(
-        K, [&](int r, int k) { return fa(i0 + r, k); }, [&](int k, int c) { return fb(k, j0 + c); });
-#pragma unroll
-    for (int r = 0; r < 4; ++r) fe(i0 + 4 * g + r, j0 + n, acc[r]);
-  }
-}
-
-// Rows of one (b, h) sequence in a [B, T, H, d] tensor, restricted to one chunk: rows at
-// or past `len` read as `pad` (q, k, v, dO: 0; alpha: 1; beta: 0).
-template <typename T>
-struct Rows {
-  const void* p;
-  size_t base, stride;  // element offset of chunk row 0, elements between rows
-  int len;
-  __device__ __forceinline__ float at(int i, int c, float pad = 0.f) const {
-    return i < len ? Elem<T>::load(p, base + (size_t)i * stride + c) : pad;
-  }
-};
 
 struct ChunkGeom {
   int b, h, n, t0, len;
@@ -156,13 +129,6 @@ __device__ __forceinline__ bool block_chunk(const BwdArgs& a, int NC, ChunkGeom*
 // element offset of (b, t0, h, 0) in a [B, T, H, d] tensor
 __device__ __forceinline__ size_t row0(const ChunkGeom& q, int T, int H, int d) {
   return (((size_t)q.b * T + q.t0) * H + q.h) * (size_t)d;
-}
-
-// prod_{J < x < I} Pib[x][c]: the gates of the whole blocks strictly between J and I
-__device__ __forceinline__ float between(const float* pib, int dk, int J, int I, int c) {
-  float p = 1.f;
-  for (int x = J + 1; x < I; ++x) p *= pib[x * dk + c];
-  return p;
 }
 
 }  // namespace
