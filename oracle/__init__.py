@@ -72,6 +72,8 @@ def load(path: str = _LIB_PATH):
     lib.kda_oracle_decode_sfda.restype = I
     lib.kda_oracle_bwd.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, I, I]
     lib.kda_oracle_bwd.restype = I
+    lib.kda_oracle_bwd_gdn2.argtypes = [I, I, I, I, I, I] + [P] * 17 + [I, I]
+    lib.kda_oracle_bwd_gdn2.restype = I
     if path == _LIB_PATH:
         _lib = lib
     return lib
@@ -207,6 +209,36 @@ def fwd_sfda(q, k, v, lam, beta, S0=None, heads=None, col_block=0, nthreads=0, l
 def decode_sfda(q, k, v, lam, beta, state, heads=None, nthreads=0, lib=None):
     """One SFDA decode step; lam [B, H, dk] complex gates as in fwd_sfda."""
     return _decode_impl("kda_oracle_decode_sfda", q, k, v, lam, beta, state, heads, nthreads, lib)
+
+
+def bwd_gdn2(q, k, v, alpha, erase, write, dO, S0=None, dST=None, heads=None, nthreads=0, lib=None):
+    """Gated DeltaNet-2 backward (GDN-2 page, section 3: the per-channel erase and write
+    gates inside the gradients): as bwd with the erase gate [B, T, H, dk] and the write
+    gate [B, T, H, dv] in place of beta.  Returns dq, dk, dalpha, derase [n_sel, T, dk];
+    dv, dwrite [n_sel, T, dv]; dS0 [n_sel, dk, dv] (fp64)."""
+    lib = lib or load()
+    arrs = [np.ascontiguousarray(x) for x in (q, k, v, alpha, erase, write)]
+    code = _dtype_code(arrs[0])
+    for a in arrs[1:]:
+        if _dtype_code(a) != code:
+            raise TypeError("all oracle inputs must share one dtype")
+    B, T, H, dk = arrs[0].shape
+    dv = arrs[2].shape[-1]
+    sel = None if heads is None else np.ascontiguousarray(np.asarray(heads, dtype=np.int32))
+    n_sel = B * H if sel is None else len(sel)
+    f64 = lambda x, shp: None if x is None else np.ascontiguousarray(np.asarray(x, dtype=np.float64)).reshape(shp)
+    S0d, dSTd = f64(S0, (n_sel, dk, dv)), f64(dST, (n_sel, dk, dv))
+    dOd = f64(dO, (n_sel, T, dv))
+    out = {"dq": np.empty((n_sel, T, dk)), "dk": np.empty((n_sel, T, dk)), "dv": np.empty((n_sel, T, dv)),
+           "dalpha": np.empty((n_sel, T, dk)), "derase": np.empty((n_sel, T, dk)),
+           "dwrite": np.empty((n_sel, T, dv)), "dS0": np.empty((n_sel, dk, dv))}
+    rc = lib.kda_oracle_bwd_gdn2(B, T, H, dk, dv, code, *[_ptr(a) for a in arrs], _ptr(S0d), _ptr(dOd),
+                                 _ptr(dSTd), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                 _ptr(out["dalpha"]), _ptr(out["derase"]), _ptr(out["dwrite"]), _ptr(out["dS0"]),
+                                 _ptr(sel), n_sel, int(nthreads))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_bwd_gdn2 failed")
+    return out
 
 
 def bwd(q, k, v, alpha, beta, dO, S0=None, dST=None, heads=None, nthreads=0, lib=None):

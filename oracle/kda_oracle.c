@@ -469,14 +469,19 @@ int kda_oracle_decode_gdn2(int B, int H, int dk, int dv, int dtype,
  *   dS0   : [n_sel, dk, dv] fp64 or NULL
  * Other arguments as kda_oracle_fwd.  Parallel over heads.
  */
-int kda_oracle_bwd(int B, int T, int H, int dk, int dv, int dtype,
-                   const void* q, const void* k, const void* v,
-                   const void* alpha, const void* beta, const double* S0,
-                   const double* dO, const double* dST,
-                   double* dq, double* dk_out, double* dv_out, double* dalpha, double* dbeta,
-                   double* dS0, const int* sel, int n_sel, int nthreads) {
+/* erase == NULL: KDA / CKDA (beta, dbeta); else Gated DeltaNet-2 (erase, write, derase,
+ * dwrite in their place). */
+static int bwd_common(int B, int T, int H, int dk, int dv, int dtype,
+                      const void* q, const void* k, const void* v,
+                      const void* alpha, const void* beta, const void* erase, const void* write,
+                      const double* S0, const double* dO, const double* dST,
+                      double* dq, double* dk_out, double* dv_out, double* dalpha, double* dbeta,
+                      double* derase, double* dwrite,
+                      double* dS0, const int* sel, int n_sel, int nthreads) {
+    const int g2 = erase != NULL;
     if (B < 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0 || !dO) return -1;
-    if (!dq || !dk_out || !dv_out || !dalpha || !dbeta) return -1;
+    if (!dq || !dk_out || !dv_out || !dalpha) return -1;
+    if (g2 ? (!write || !derase || !dwrite) : !dbeta) return -1;
     if (dtype < ORC_BF16 || dtype > ORC_F64) return -1;
     if (!sel) n_sel = B * H;
     if (n_sel < 0) return -1;
@@ -491,7 +496,7 @@ int kda_oracle_bwd(int B, int T, int H, int dk, int dv, int dtype,
         double* hist = (double*)malloc(sizeof(double) * SS * (size_t)(BLK + 1));
         double* G = (double*)malloc(sizeof(double) * SS);
         double* Sp = (double*)malloc(sizeof(double) * SS);   /* S' of the current token */
-        double* buf = (double*)malloc(sizeof(double) * (size_t)(3 * dk + 5 * dv));
+        double* buf = (double*)malloc(sizeof(double) * (size_t)(5 * dk + 6 * dv));
         if (!ck || !hist || !G || !Sp || !buf) {
 #pragma omp atomic write
             err = 1;
@@ -503,6 +508,7 @@ int kda_oracle_bwd(int B, int T, int H, int dk, int dv, int dtype,
             const int b = bh / H, h = bh % H;
             double *qq = buf, *kk = buf + dk, *aa = buf + 2 * dk;
             double *vv = buf + 3 * dk, *u = vv + dv, *del = u + dv, *dd = del + dv, *tmp = dd + dv;
+            double *bb = tmp + dv, *ee = bb + dk, *ww = ee + dk;  /* GDN-2: erase gate, b o k, write gate */
             /* forward sweep: checkpoint S at the start of every 64-token block */
             double* S = hist;  /* scratch for the sweep */
             for (size_t x = 0; x < SS; ++x) S[x] = S0 ? S0[(size_t)s * SS + x] : 0.0;
@@ -515,7 +521,13 @@ int kda_oracle_bwd(int B, int T, int H, int dk, int dv, int dtype,
                     aa[i] = load_elem(alpha, dtype, row * dk + i);
                 }
                 for (int j = 0; j < dv; ++j) vv[j] = load_elem(v, dtype, row * dv + j);
-                kda_token(S, dk, dv, 0, dv, qq, kk, vv, aa, load_elem(beta, dtype, row), u, NULL, 0);
+                if (g2) {
+                    for (int i = 0; i < dk; ++i) bb[i] = load_elem(erase, dtype, row * dk + i);
+                    for (int j = 0; j < dv; ++j) ww[j] = load_elem(write, dtype, row * dv + j);
+                    gdn2_token(S, dk, dv, 0, dv, qq, kk, vv, aa, bb, ww, u, NULL);
+                } else {
+                    kda_token(S, dk, dv, 0, dv, qq, kk, vv, aa, load_elem(beta, dtype, row), u, NULL, 0);
+                }
             }
             /* backward sweep */
             for (size_t x = 0; x < SS; ++x) G[x] = dST ? dST[(size_t)s * SS + x] : 0.0;
@@ -533,7 +545,13 @@ int kda_oracle_bwd(int B, int T, int H, int dk, int dv, int dtype,
                     for (int j = 0; j < dv; ++j) vv[j] = load_elem(v, dtype, row * dv + j);
                     double* nx = hist + (size_t)(t - t0 + 1) * SS;
                     memcpy(nx, hist + (size_t)(t - t0) * SS, sizeof(double) * SS);
-                    kda_token(nx, dk, dv, 0, dv, qq, kk, vv, aa, load_elem(beta, dtype, row), u, NULL, 0);
+                    if (g2) {
+                        for (int i = 0; i < dk; ++i) bb[i] = load_elem(erase, dtype, row * dk + i);
+                        for (int j = 0; j < dv; ++j) ww[j] = load_elem(write, dtype, row * dv + j);
+                        gdn2_token(nx, dk, dv, 0, dv, qq, kk, vv, aa, bb, ww, u, NULL);
+                    } else {
+                        kda_token(nx, dk, dv, 0, dv, qq, kk, vv, aa, load_elem(beta, dtype, row), u, NULL, 0);
+                    }
                 }
                 for (int t = t1 - 1; t >= t0; --t) {
                     const size_t row = ((size_t)b * T + t) * H + h;
@@ -544,8 +562,67 @@ int kda_oracle_bwd(int B, int T, int H, int dk, int dv, int dtype,
                         aa[i] = load_elem(alpha, dtype, row * dk + i);
                     }
                     for (int j = 0; j < dv; ++j) vv[j] = load_elem(v, dtype, row * dv + j);
-                    const double bt = load_elem(beta, dtype, row);
                     const double* dOt = dO + ((size_t)s * T + t) * dv;
+                    if (g2) {
+                        /* S' = Diag(alpha) S_prev; e = b o k; u = S'^T e; delta = w o v - u;
+                         * S_t = S' + k delta^T */
+                        for (int i = 0; i < dk; ++i) {
+                            bb[i] = load_elem(erase, dtype, row * dk + i);
+                            ee[i] = bb[i] * kk[i];
+                        }
+                        for (int j = 0; j < dv; ++j) ww[j] = load_elem(write, dtype, row * dv + j);
+                        for (int i = 0; i < dk; ++i)
+                            for (int j = 0; j < dv; ++j) Sp[(size_t)i * dv + j] = Sprev[(size_t)i * dv + j] * aa[i];
+                        for (int j = 0; j < dv; ++j) u[j] = 0.0;
+                        for (int i = 0; i < dk; ++i)
+                            for (int j = 0; j < dv; ++j) u[j] += ee[i] * Sp[(size_t)i * dv + j];
+                        for (int j = 0; j < dv; ++j) del[j] = ww[j] * vv[j] - u[j];
+                        /* readout: G += q dO^T ; dq = S_t dO */
+                        for (int i = 0; i < dk; ++i)
+                            for (int j = 0; j < dv; ++j) G[(size_t)i * dv + j] += qq[i] * dOt[j];
+                        double* dqg = dq + ((size_t)s * T + t) * dk;
+                        for (int i = 0; i < dk; ++i) {
+                            double a = 0.0;
+                            for (int j = 0; j < dv; ++j) a += (Sp[(size_t)i * dv + j] + kk[i] * del[j]) * dOt[j];
+                            dqg[i] = a;
+                        }
+                        /* ddelta = G^T k ; d(w o v) = ddelta : dv = w o ddelta, dw = v o ddelta */
+                        for (int j = 0; j < dv; ++j) dd[j] = 0.0;
+                        for (int i = 0; i < dk; ++i)
+                            for (int j = 0; j < dv; ++j) dd[j] += G[(size_t)i * dv + j] * kk[i];
+                        double* dvg = dv_out + ((size_t)s * T + t) * dv;
+                        double* dwg = dwrite + ((size_t)s * T + t) * dv;
+                        for (int j = 0; j < dv; ++j) {
+                            dvg[j] = ww[j] * dd[j];
+                            dwg[j] = vv[j] * dd[j];
+                        }
+                        /* dk = G delta (write side) + b o de, de = -S' ddelta (read side);
+                         * db = k o de */
+                        double* dkg = dk_out + ((size_t)s * T + t) * dk;
+                        double* dbg = derase + ((size_t)s * T + t) * dk;
+                        for (int i = 0; i < dk; ++i) {
+                            double w_side = 0.0, de = 0.0;
+                            for (int j = 0; j < dv; ++j) {
+                                w_side += G[(size_t)i * dv + j] * del[j];
+                                de -= Sp[(size_t)i * dv + j] * dd[j];
+                            }
+                            dkg[i] = w_side + bb[i] * de;
+                            dbg[i] = kk[i] * de;
+                        }
+                        /* dS' = G - e ddelta^T ; dalpha = rowsum(dS' o S_prev) ; G <- Diag(alpha) dS' */
+                        double* dag = dalpha + ((size_t)s * T + t) * dk;
+                        for (int i = 0; i < dk; ++i) {
+                            double a = 0.0;
+                            for (int j = 0; j < dv; ++j) {
+                                const double g = G[(size_t)i * dv + j] - ee[i] * dd[j];
+                                a += Sprev[(size_t)i * dv + j] * g;
+                                G[(size_t)i * dv + j] = g * aa[i];
+                            }
+                            dag[i] = a;
+                        }
+                        continue;
+                    }
+                    const double bt = load_elem(beta, dtype, row);
                     /* recompute S' = Diag(alpha) S_prev, u = S'^T k, delta = v - u */
                     for (int i = 0; i < dk; ++i)
                         for (int j = 0; j < dv; ++j) Sp[(size_t)i * dv + j] = aa[i] * Sprev[(size_t)i * dv + j];
@@ -609,4 +686,31 @@ int kda_oracle_bwd(int B, int T, int H, int dk, int dv, int dtype,
         free(buf);
     }
     return err ? -1 : 0;
+}
+
+int kda_oracle_bwd(int B, int T, int H, int dk, int dv, int dtype,
+                   const void* q, const void* k, const void* v,
+                   const void* alpha, const void* beta, const double* S0,
+                   const double* dO, const double* dST,
+                   double* dq, double* dk_out, double* dv_out, double* dalpha, double* dbeta,
+                   double* dS0, const int* sel, int n_sel, int nthreads) {
+    if (!beta) return -1;
+    return bwd_common(B, T, H, dk, dv, dtype, q, k, v, alpha, beta, NULL, NULL, S0, dO, dST, dq, dk_out, dv_out,
+                      dalpha, dbeta, NULL, NULL, dS0, sel, n_sel, nthreads);
+}
+
+/* Gated DeltaNet-2 backward: the same reverse sweep through gdn2_token (erase gate b per
+ * key channel on the read, write gate w per value channel on the write).  erase [B, T, H,
+ * dk], write [B, T, H, dv] (dtype); derase [n_sel, T, dk], dwrite [n_sel, T, dv] fp64 out,
+ * in place of dbeta.  Other arguments as kda_oracle_bwd. */
+int kda_oracle_bwd_gdn2(int B, int T, int H, int dk, int dv, int dtype,
+                        const void* q, const void* k, const void* v, const void* alpha,
+                        const void* erase, const void* write, const double* S0,
+                        const double* dO, const double* dST,
+                        double* dq, double* dk_out, double* dv_out, double* dalpha,
+                        double* derase, double* dwrite, double* dS0,
+                        const int* sel, int n_sel, int nthreads) {
+    if (!erase || !write) return -1;
+    return bwd_common(B, T, H, dk, dv, dtype, q, k, v, alpha, NULL, erase, write, S0, dO, dST, dq, dk_out, dv_out,
+                      dalpha, NULL, derase, dwrite, dS0, sel, n_sel, nthreads);
 }

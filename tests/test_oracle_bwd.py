@@ -122,3 +122,99 @@ def test_bwd_head_selection_and_no_final_gradient():
     g0 = oracle.bwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"], dO, S0=x["S0"], dST=np.zeros((B * H, dk, dv)))
     for key in g:
         np.testing.assert_array_equal(g0[key], g[key])
+
+
+# ---- Gated DeltaNet-2: erase gate b per key channel (read side), write gate w per value
+# channel (write side): S_t = (I - k (b o k)^T) Diag(alpha) S + k (w o v)^T.
+
+def _gdn2_inputs(rng, B, T, H, dk, dv):
+    x, dO, dST = _inputs(rng, B, T, H, dk, dv)
+    x.pop("beta")
+    x["erase"] = rng.uniform(0.0, 1.0, (B, T, H, dk))
+    x["write"] = rng.uniform(0.0, 1.0, (B, T, H, dv))
+    return x, dO, dST
+
+
+def _gdn2_loss(x, dO, dST):
+    o, S = oracle.fwd_gdn2(x["q"], x["k"], x["v"], x["alpha"], x["erase"], x["write"], S0=x["S0"])
+    return float((o * dO).sum() + (S * dST).sum())
+
+
+def _gdn2_grads(x, dO, dST):
+    return oracle.bwd_gdn2(x["q"], x["k"], x["v"], x["alpha"], x["erase"], x["write"], dO, S0=x["S0"], dST=dST)
+
+
+def _gdn2_entry(g, name, idx, H):
+    if name == "S0":
+        return g["dS0"][idx]
+    key = {"q": "dq", "k": "dk", "v": "dv", "alpha": "dalpha", "erase": "derase", "write": "dwrite"}[name]
+    b, t, h = idx[:3]
+    return g[key][(b * H + h, t) + tuple(idx[3:])]
+
+
+@pytest.mark.parametrize("T", [5, 150])
+def test_gdn2_bwd_exact_secants(T):
+    """L is affine in each single entry of q, v, alpha, the erase gate, the write gate and
+    S0: a secant of any step is the gradient (zero gates included)."""
+    rng = np.random.default_rng(200 + T)
+    B, H, dk, dv = 2, 2, 4, 3
+    x, dO, dST = _gdn2_inputs(rng, B, T, H, dk, dv)
+    x["alpha"][0, 1, 0, 2] = 0.0
+    x["erase"][1, 2, 1, 0] = 0.0
+    g = _gdn2_grads(x, dO, dST)
+    L0 = _gdn2_loss(x, dO, dST)
+    for name in ("q", "v", "alpha", "erase", "write", "S0"):
+        for _ in range(6):
+            idx = tuple(int(rng.integers(0, n)) for n in x[name].shape)
+            y = {kk: vv.copy() for kk, vv in x.items()}
+            y[name][idx] += 0.75
+            sec = (_gdn2_loss(y, dO, dST) - L0) / 0.75
+            ref = _gdn2_entry(g, name, idx, H)
+            assert abs(sec - ref) <= 1e-9 * max(1.0, abs(ref)), (name, idx, sec, ref)
+
+
+def test_gdn2_bwd_key_central_differences():
+    rng = np.random.default_rng(17)
+    B, T, H, dk, dv = 1, 70, 2, 4, 3
+    x, dO, dST = _gdn2_inputs(rng, B, T, H, dk, dv)
+    g = _gdn2_grads(x, dO, dST)
+    h = 1e-5
+    for _ in range(12):
+        idx = tuple(int(rng.integers(0, n)) for n in x["k"].shape)
+        yp = {kk: vv.copy() for kk, vv in x.items()}
+        ym = {kk: vv.copy() for kk, vv in x.items()}
+        yp["k"][idx] += h
+        ym["k"][idx] -= h
+        fd = (_gdn2_loss(yp, dO, dST) - _gdn2_loss(ym, dO, dST)) / (2 * h)
+        ref = _gdn2_entry(g, "k", idx, H)
+        assert abs(fd - ref) <= 1e-6 * max(1.0, abs(ref)), (idx, fd, ref)
+
+
+def test_gdn2_bwd_reduces_to_kda():
+    """Both gates tied to beta (the KDA case of the GDN-2 page's section 1): every gradient
+    equals the KDA backward's, and dbeta = sum_c derase_c + sum_j dwrite_j."""
+    rng = np.random.default_rng(23)
+    B, T, H, dk, dv = 2, 90, 2, 4, 3
+    x, dO, dST = _inputs(rng, B, T, H, dk, dv)
+    b = x["beta"]
+    ga = oracle.bwd(x["q"], x["k"], x["v"], x["alpha"], b, dO, S0=x["S0"], dST=dST)
+    gb = oracle.bwd_gdn2(x["q"], x["k"], x["v"], x["alpha"], np.repeat(b[..., None], dk, -1),
+                         np.repeat(b[..., None], dv, -1), dO, S0=x["S0"], dST=dST)
+    for key in ("dq", "dk", "dv", "dalpha", "dS0"):
+        np.testing.assert_allclose(gb[key], ga[key], rtol=0, atol=1e-12 * max(1.0, np.abs(ga[key]).max()))
+    np.testing.assert_allclose(gb["derase"].sum(-1) + gb["dwrite"].sum(-1), ga["dbeta"], rtol=0, atol=1e-12)
+
+
+def test_gdn2_bwd_scalar_token_by_hand():
+    """d_k = d_v = 1, one token: o = q (a s0 + k (w v - b k a s0)):
+       dq = S1, dv = q k w, dwrite = q k v, derase = -q k^2 a s0, dk = q (w v - 2 b k a s0),
+       dalpha = q s0 (1 - b k^2), dS0 = q a (1 - b k^2)."""
+    q, k, v, a, b, w, s0 = 1.5, 0.5, 2.0, 0.8, 0.6, 0.9, -0.4
+    f = lambda z: np.array(z, dtype=np.float64).reshape(1, 1, 1, 1)
+    g = oracle.bwd_gdn2(f(q), f(k), f(v), f(a), f(b), f(w), np.ones((1, 1, 1)), S0=np.array([[[s0]]]))
+    S1 = a * s0 + k * (w * v - b * k * a * s0)
+    want = {"dq": S1, "dv": q * k * w, "dwrite": q * k * v, "derase": -q * k * k * a * s0,
+            "dk": q * (w * v - 2 * b * k * a * s0), "dalpha": q * s0 * (1 - b * k * k),
+            "dS0": q * a * (1 - b * k * k)}
+    for key, val in want.items():
+        np.testing.assert_allclose(g[key].ravel()[0], val, rtol=0, atol=1e-15)

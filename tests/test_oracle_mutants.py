@@ -278,3 +278,48 @@ def test_bwd_mutant_is_caught(name, src_text, monkeypatch, tmp_path):
     assert src_text.count(old) == 1, f"mutation anchor for {name} not unique"
     lib = _build_variant(src_text.replace(old, new), str(tmp_path), name)
     assert _caught_bwd(lib, monkeypatch), f"mutant {name} passed every backward pin"
+
+
+MUTANTS_BWD_GDN2 = {
+    "gdn2_bwd_dk_read_side_dropped": ("dkg[i] = w_side + bb[i] * de;", "dkg[i] = w_side;"),
+    "gdn2_bwd_dwrite_with_w": ("dwg[j] = vv[j] * dd[j];", "dwg[j] = ww[j] * dd[j];"),
+    "gdn2_bwd_derase_without_k": ("dbg[i] = kk[i] * de;", "dbg[i] = de;"),
+    "gdn2_bwd_erase_adjoint_dropped": ("const double g = G[(size_t)i * dv + j] - ee[i] * dd[j];",
+                                       "const double g = G[(size_t)i * dv + j];"),
+    "gdn2_bwd_read_through_key": ("ee[i] = bb[i] * kk[i];", "ee[i] = kk[i];"),
+}
+
+PIN_TESTS_BWD_GDN2 = [
+    ("secants_short", lambda: bpins.test_gdn2_bwd_exact_secants(5)),
+    ("secants_blocks", lambda: bpins.test_gdn2_bwd_exact_secants(150)),
+    ("key_fd", lambda: bpins.test_gdn2_bwd_key_central_differences()),
+    ("scalar_hand", lambda: bpins.test_gdn2_bwd_scalar_token_by_hand()),
+]
+
+
+def _caught_bwd_gdn2(lib, monkeypatch):
+    """The forward stays the clean library (the pins measure the backward against it)."""
+    failed = []
+    with monkeypatch.context() as m:
+        real = oracle.bwd_gdn2
+        m.setattr(oracle, "bwd_gdn2", lambda *a, **kw: real(*a, lib=lib, **kw))
+        for name, fn in PIN_TESTS_BWD_GDN2:
+            try:
+                with np.errstate(all="ignore"):
+                    fn()
+            except AssertionError:
+                failed.append(name)
+    return failed
+
+
+def test_unmodified_source_passes_gdn2_bwd_pins(src_text, monkeypatch, tmp_path):
+    lib = _build_variant(src_text, str(tmp_path), "clean_bwd_gdn2")
+    assert _caught_bwd_gdn2(lib, monkeypatch) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS_BWD_GDN2))
+def test_gdn2_bwd_mutant_is_caught(name, src_text, monkeypatch, tmp_path):
+    old, new = MUTANTS_BWD_GDN2[name]
+    assert src_text.count(old) == 1, f"mutation anchor for {name} not unique"
+    lib = _build_variant(src_text.replace(old, new), str(tmp_path), name)
+    assert _caught_bwd_gdn2(lib, monkeypatch), f"mutant {name} passed every GDN-2 backward pin"
