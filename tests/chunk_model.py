@@ -358,13 +358,14 @@ def chunk_backward(q, k, v, a, beta, dO, S0=None, dST=None, C=64, check_zero_for
     return out
 
 
-def blocked_decay_grads(dA, dD, q, k, a, av, bv, dgl):
+def blocked_decay_grads(dA, dD, q, k, a, av, bv, dgl, x=None):
     """The decayed sums and the gate gradient of one chunk as the GPU gradient kernel forms
-    them (fp64), from dA (lower, diagonal included), dD (strictly lower), the per-row
-    start-state weights av = d(Q o gamma) o q + d(K o gamma) o k, the final-state weights
-    bv = d(K o rho) o k and dgl = d gamma_last.  Returns Zq, Zr, Zc (the sums
-    sum_j dA_ij k_j r_ij, sum_j dD_ij k_j r_ij, sum_i (dA_ij q_i + dD_ij k_i) r_ij) and
-    dalpha, with no division by a gate:
+    them (fp64), from dA (lower, diagonal included), dD (strictly lower) the gradient of the
+    second decayed product sum_c x_ic k_jc r_ijc (x = k, or the GDN-2 erase vector b o k),
+    the per-row start-state weights av, the final-state weights bv = d(K o rho) o k and
+    dgl = d gamma_last.  Returns Zq, Zr, Zc (the sums sum_j dA_ij k_j r_ij,
+    sum_j dD_ij k_j r_ij, sum_i (dA_ij q_i + dD_ij x_i) r_ij) and dalpha, with no division
+    by a gate:
 
     * block products anchored at the 16-row block edges: PA^M = dA[>= s, < s] Khat^M,
       PD^M likewise (Khat^M_j = k_j r(s-1, j)), F^M_j = sum_{i > e} (dA_ij q_i + dD_ij k_i)
@@ -377,6 +378,7 @@ def blocked_decay_grads(dA, dD, q, k, a, av, bv, dgl):
     """
     C, dk = q.shape
     NB = C // SUB
+    x = k if x is None else x
     pin, sig, pib = np.zeros((C, dk)), np.zeros((C, dk)), np.zeros((NB, dk))
     for I in range(NB):
         p = np.ones(dk)
@@ -404,12 +406,12 @@ def blocked_decay_grads(dA, dD, q, k, a, av, bv, dgl):
     for M in range(NB - 1):
         s, e1 = M * SUB, M * SUB + SUB
         rie = np.stack([pin[i] * between(M, i // SUB) for i in range(e1, C)])
-        F[s:e1] = dA[e1:, s:e1].T @ (q[e1:] * rie) + dD[e1:, s:e1].T @ (k[e1:] * rie)
+        F[s:e1] = dA[e1:, s:e1].T @ (q[e1:] * rie) + dD[e1:, s:e1].T @ (x[e1:] * rie)
 
     Zq, Zr, Zc, dal = np.zeros((C, dk)), np.zeros((C, dk)), np.zeros((C, dk)), np.zeros((C, dk))
     for M in range(NB):
         s = M * SUB
-        al, qv, kv = a[s:s + SUB], q[s:s + SUB], k[s:s + SUB]
+        al, qv, kv, xv = a[s:s + SUB], q[s:s + SUB], k[s:s + SUB], x[s:s + SUB]
         gs = np.prod(pib[:M], axis=0) if M > 0 else np.ones(dk)
         rend = np.prod(pib[M + 1:], axis=0) if M < NB - 1 else np.ones(dk)
         for r in range(SUB):
@@ -425,7 +427,7 @@ def blocked_decay_grads(dA, dD, q, k, a, av, bv, dgl):
             zc, P = dA[i, i] * qv[r], np.ones(dk)
             for ri in range(r + 1, SUB):
                 P = P * al[ri]
-                zc = zc + (dA[s + ri, i] * qv[ri] + dD[s + ri, i] * kv[ri]) * P
+                zc = zc + (dA[s + ri, i] * qv[ri] + dD[s + ri, i] * xv[ri]) * P
             if M < NB - 1:
                 zc = zc + sig[i] * F[i]
             Zq[i], Zr[i], Zc[i] = zq, zr, zc
@@ -434,17 +436,17 @@ def blocked_decay_grads(dA, dD, q, k, a, av, bv, dgl):
         def g_at(i):
             g = av[i] * gs
             if M > 0:
-                g = g + q[i] * PA[M, i] + k[i] * PD[M, i]
+                g = g + q[i] * PA[M, i] + x[i] * PD[M, i]
             if i == C - 1:
                 g = g + bvs + dgl * gs
             return g
 
         u = [g_at(s + r) for r in range(SUB)]
         if M < NB - 1:
-            x = np.zeros(dk)
+            xf = np.zeros(dk)
             for i in range(C - 1, s + SUB - 1, -1):   # sum_{i > e} r(i, e) g_i
-                x = a[i] * (g_at(i) + x)
-            u[SUB - 1] = u[SUB - 1] + x
+                xf = a[i] * (g_at(i) + xf)
+            u[SUB - 1] = u[SUB - 1] + xf
             f = [kv[r] * F[s + r] + bv[s + r] * rend for r in range(SUB)]
         else:
             f = [bv[s + r] for r in range(SUB)]
@@ -454,8 +456,81 @@ def blocked_decay_grads(dA, dD, q, k, a, av, bv, dgl):
                 acc = u[i] + al[i + 1] * acc
             dal[s + m] = acc
             for i in range(m + 1, SUB):
-                E = (qv[i] * dA[s + i, s + m] + kv[i] * dD[s + i, s + m]) * kv[m]
+                E = (qv[i] * dA[s + i, s + m] + xv[i] * dD[s + i, s + m]) * kv[m]
                 if i == SUB - 1:
                     E = E + f[m]
                 u[i] = al[m] * u[i] + E
     return Zq, Zr, Zc, dal
+
+
+def chunk_backward_gdn2(q, k, v, a, erase, write, dO, S0=None, dST=None, C=64, blocked=False):
+    """Gated DeltaNet-2 gradients for one head through the chunk algebra (fp64), as the GPU
+    kernels form them.  erase [T, dk] (b), write [T, dv] (w).  Per chunk, with e = b o k:
+    T = [sum_c e_ic k_jc r_ijc] (j < i), M = (I + T)^-1, W = M (E o gamma), U = M (w o V);
+    then Delta, O, S' as for KDA (which is e = beta k, w = beta).  Returns dq, dk, dv,
+    dalpha, derase, dwrite, dS0.  blocked: decayed sums and gate gradient from
+    blocked_decay_grads with the erase vector as the second product's row operand."""
+    T, dk = q.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if S0 is None else np.asarray(S0, np.float64).copy()
+    low, slow = np.tril(np.ones((C, C))), np.tril(np.ones((C, C)), -1)
+    parts = []
+    for c0 in range(0, T, C):
+        n = min(C, T - c0)
+        pad = lambda x, fill: np.concatenate([x[c0:c0 + n], np.full((C - n,) + x.shape[1:], fill)])[:C]
+        qc, kc, vc, ac = pad(q, 0.0), pad(k, 0.0), pad(v, 0.0), pad(a, 1.0)
+        bc, wc, dOc = pad(erase, 0.0), pad(write, 0.0), pad(dO, 0.0)
+        r = _ranges(ac)
+        gam = np.cumprod(ac, axis=0)
+        rho, gL = r[C - 1], gam[C - 1]
+        ec = bc * kc
+        A = np.einsum("ic,jc,ijc->ij", qc, kc, r) * low
+        Tm = np.einsum("ic,jc,ijc->ij", ec, kc, r) * slow
+        M = np.linalg.inv(np.eye(C) + Tm)
+        Eg, Qg, Kr, WV = ec * gam, qc * gam, kc * rho, wc * vc
+        W = M @ Eg
+        Dl = M @ WV - W @ S
+        parts.append(dict(S=S, q=qc, k=kc, v=vc, a=ac, b=bc, w=wc, e=ec, dO=dOc, r=r, gam=gam, rho=rho, gL=gL,
+                          A=A, T=Tm, M=M, Eg=Eg, Qg=Qg, Kr=Kr, WV=WV, W=W, Dl=Dl, c0=c0, n=n))
+        S = gL[:, None] * S + Kr.T @ Dl
+    out = {x: np.zeros((T, dk)) for x in ("dq", "dk", "dalpha", "derase")}
+    out["dv"], out["dwrite"] = np.zeros((T, dv)), np.zeros((T, dv))
+    dSn = np.zeros((dk, dv)) if dST is None else np.asarray(dST, np.float64).copy()
+    for p in reversed(parts):
+        S, dO_, qc, kc, vc, ac, ec = p["S"], p["dO"], p["q"], p["k"], p["v"], p["a"], p["e"]
+        r, gam, rho, gL, M = p["r"], p["gam"], p["rho"], p["gL"], p["M"]
+        dDl = p["Kr"] @ dSn + p["A"].T @ dO_
+        dS = gL[:, None] * dSn + p["Qg"].T @ dO_ - p["W"].T @ dDl
+        dQg = dO_ @ S.T
+        dA = (dO_ @ p["Dl"].T) * low
+        dKr = p["Dl"] @ dSn.T
+        dgL = (dSn * S).sum(axis=1)
+        dW = -dDl @ S.T
+        dWV = M.T @ dDl                       # d(w o V)
+        dM = (dDl @ p["WV"].T + dW @ p["Eg"].T) * low
+        dEg = M.T @ dW                        # d(E o gamma)
+        dT = -(M.T @ dM @ M.T) * slow
+        av = dQg * qc + dEg * ec
+        bv = dKr * kc
+        if blocked:
+            Zq, Ze, Zc, dal = blocked_decay_grads(dA, dT, qc, kc, ac, av, bv, dgL, x=ec)
+        else:
+            Zq = np.einsum("ij,jc,ijc->ic", dA, kc, r)
+            Ze = np.einsum("ij,jc,ijc->ic", dT, kc, r)
+            Zc = np.einsum("ij,ic,ijc->jc", dA, qc, r) + np.einsum("ij,ic,ijc->jc", dT, ec, r)
+            dG = dQg * p["Qg"] + dEg * p["Eg"] + qc * Zq + ec * Ze - kc * Zc - dKr * p["Kr"]
+            dG[C - 1] += (dKr * p["Kr"]).sum(axis=0) + dgL * gL
+            P = np.cumsum(dG[::-1], axis=0)[::-1]
+            nz = ac != 0.0
+            dal = np.where(nz, P / np.where(nz, ac, 1.0), 0.0)
+        de = dEg * gam + Ze                   # d e, e = b o k
+        n, c0 = p["n"], p["c0"]
+        out["dq"][c0:c0 + n] = (dQg * gam + Zq)[:n]
+        out["dk"][c0:c0 + n] = (dKr * rho + Zc + p["b"] * de)[:n]
+        out["derase"][c0:c0 + n] = (kc * de)[:n]
+        out["dv"][c0:c0 + n] = (p["w"] * dWV)[:n]
+        out["dwrite"][c0:c0 + n] = (vc * dWV)[:n]
+        out["dalpha"][c0:c0 + n] = dal[:n]
+        dSn = dS
+    out["dS0"] = dSn
+    return out
