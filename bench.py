@@ -215,8 +215,8 @@ def bwd_flops(B, T, H, dk, dv, C=64):
 
 
 def bench_backward(steps, warmup, log, name="ckda_prefill_8k"):
-    """Times kda_chunk_bwd on workload `name` (start state and a final-state gradient
-    given).  Returns (workload, ms per call)."""
+    """Times kda_chunk_bwd (kda_gdn2_chunk_bwd for a GDN-2 workload) on workload `name`
+    (start state and a final-state gradient given).  Returns (workload, ms per call)."""
     import torch
     import gated_delta_rule_78_amd as kda
     from gated_delta_rule_78_amd.inputs import make_workload, make_upstream, WORKLOADS, to_torch
@@ -230,9 +230,14 @@ def bench_backward(steps, warmup, log, name="ckda_prefill_8k"):
     ws = torch.empty(kda.bwd_workspace_size(w.B, w.T, w.H, w.dk, w.dv), dtype=torch.uint8, device="cuda")
     log(f"[bench] {name} backward: inputs ready in {time.time() - t0:.1f}s, workspace {ws.numel() / 1e9:.2f} GB")
     stream = torch.cuda.current_stream()
-    ms = timed(lambda: kda.chunk_bwd(q, k, v, a, b, d_o, initial_state=s0, d_final_state=dst, workspace=ws),
-               steps, warmup, stream)
-    del q, k, v, a, b, s0, d_o, dst, ws
+    if w.gates == "gdn2":
+        up = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to("cuda").view(torch.bfloat16)
+        e, g = up(inp.erase), up(inp.write)
+        call = lambda: kda.gdn2_chunk_bwd(q, k, v, a, e, g, d_o, initial_state=s0, d_final_state=dst, workspace=ws)
+    else:
+        call = lambda: kda.chunk_bwd(q, k, v, a, b, d_o, initial_state=s0, d_final_state=dst, workspace=ws)
+    ms = timed(call, steps, warmup, stream)
+    del q, k, v, a, b, s0, d_o, dst, ws, call
     torch.cuda.empty_cache()
     return w, ms
 
@@ -350,6 +355,8 @@ def main():
                     help="only the decode measurement (for profiling the decode kernel)")
     ap.add_argument("--bwd-only", action="store_true",
                     help="only the backward measurement (for profiling the backward kernels)")
+    ap.add_argument("--bwd-workload", default="ckda_prefill_8k", choices=("ckda_prefill_8k", "gdn2_prefill_8k"),
+                    help="workload of --bwd-only")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -381,9 +388,9 @@ def main():
                           "frac": gbs / HBM_PEAK_GBS, "bytes_per_step": db}), flush=True)
         return
     if args.bwd_only:
-        wb, msb = bench_backward(max(1, args.steps // 4), 1, log)
+        wb, msb = bench_backward(max(1, args.steps // 4), 1, log, name=args.bwd_workload)
         fl = bwd_flops(wb.B, wb.T, wb.H, wb.dk, wb.dv)
-        print(json.dumps({"workload": "ckda_prefill_8k backward", "ms_per_call": msb,
+        print(json.dumps({"workload": f"{wb.name} backward", "ms_per_call": msb,
                           "tokens_per_s": wb.B * wb.T / (msb * 1e-3),
                           "tflops_fp32": fl / (msb * 1e-3) / 1e12}), flush=True)
         return
@@ -456,6 +463,10 @@ def main():
                                    "dense_flops_per_call": flb, "tflops_fp32": flb / (msb * 1e-3) / 1e12,
                                    "frac_fp32_mfma": flb / (msb * 1e-3) / 1e12 / MFMA_FP32_PEAK_TFLOPS}
         log(f"[bench] ckda backward 8k: {msb:.3f} ms/call, {flb / (msb * 1e-3) / 1e12:.1f} dense fp32 TFLOP/s")
+        wg, msg = bench_backward(max(2, args.steps // 4), 1, log, name="gdn2_prefill_8k")
+        out["gdn2_backward_8k"] = {"workload": "gdn2_prefill_8k", "ms_per_call": msg,
+                                   "tokens_per_s": wg.B * wg.T / (msg * 1e-3), "dtype": "f32"}
+        log(f"[bench] gdn2 backward 8k: {msg:.3f} ms/call")
         wt, mst, ntk = bench_decode_tokens(4, log)
         bt_ = decode_bytes(wt.B, wt.H, wt.dk, wt.dv, tokens=ntk)
         out["decode_tokens"] = {"workload": "ckda_decode_b256", "tokens_per_call": ntk, "ms_per_call": mst,

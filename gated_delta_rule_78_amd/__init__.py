@@ -17,7 +17,7 @@ import os
 __all__ = ["chunk_fwd", "chunk_records", "chunk_apply_records", "chunk_fwd_debug", "decode_step",
            "gdn2_chunk_fwd", "gdn2_decode_step", "decode_tokens", "gdn2_decode_tokens", "chunk_fwd_varlen",
            "sfda_chunk_fwd", "sfda_decode_step", "sfda_decode_tokens", "chunk_bwd", "chunk_bwd_varlen",
-           "bwd_workspace_size",
+           "gdn2_chunk_bwd", "bwd_workspace_size",
            "workspace_size", "pick_path", "lib", "version", "status_string",
            "LIB_PATH", "KdaError", "Shape", "BF16", "F32"]
 
@@ -94,6 +94,10 @@ def lib() -> ctypes.CDLL:
         L.kda_chunk_bwd_varlen.argtypes = [SP, P, ctypes.c_int, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
                                            ctypes.c_size_t, P]
         L.kda_chunk_bwd_varlen.restype = ctypes.c_int
+        L.kda_gdn2_chunk_bwd.argtypes = [SP] + [P] * 17 + [ctypes.c_size_t, P]
+        L.kda_gdn2_chunk_bwd.restype = ctypes.c_int
+        L.kda_gdn2_chunk_bwd_varlen.argtypes = [SP, P, ctypes.c_int] + [P] * 17 + [ctypes.c_size_t, P]
+        L.kda_gdn2_chunk_bwd_varlen.restype = ctypes.c_int
         L.kda_status_string.argtypes = [ctypes.c_int]
         L.kda_status_string.restype = ctypes.c_char_p
         L.kda_version.argtypes = []
@@ -514,6 +518,63 @@ def bwd_workspace_size(B, T, H, dk, dv, dtype="bf16") -> int:
     return int(lib().kda_chunk_bwd_workspace_size(ctypes.byref(shape)))
 
 
+def _bwd_call(q, k, v, alpha, gates, d_o, cu_seqlens, initial_state, d_final_state, want_d_initial, workspace):
+    """Shared marshalling of the four backward entry points; gates = (beta,) for KDA / CKDA
+    or (erase, write) for Gated DeltaNet-2.  Returns the C call's output tensors."""
+    torch = _torch()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    g2 = len(gates) == 2
+    packed = cu_seqlens is not None
+    if packed and B != 1:
+        raise ValueError("a packed batch has B = 1")
+    code = _dtype_code(q)
+    named = (("k", k), ("alpha", alpha), ("v", v), ("d_o", d_o)) + (
+        (("erase", gates[0]), ("write", gates[1])) if g2 else (("beta", gates[0]),))
+    for nm, t in named:
+        if t.dtype != q.dtype:
+            raise TypeError(f"{nm} must have the dtype of q")
+    if k.shape != q.shape or alpha.shape != q.shape or v.shape != (B, T, H, dv) or d_o.shape != (B, T, H, dv):
+        raise ValueError("shapes: q, k, alpha [B,T,H,dk]; v, d_o [B,T,H,dv]")
+    if g2 and (gates[0].shape != q.shape or gates[1].shape != v.shape):
+        raise ValueError("shapes: erase [B,T,H,dk]; write [B,T,H,dv]")
+    if not g2 and gates[0].shape != (B, T, H):
+        raise ValueError("shape: beta [B,T,H]")
+    if packed and (cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1):
+        raise TypeError("cu_seqlens must be a 1-d int32 tensor")
+    n_states = cu_seqlens.numel() - 1 if packed else B
+    for t, nm in ((initial_state, "initial_state"), (d_final_state, "d_final_state")):
+        if t is not None and (t.dtype != torch.float32 or t.shape != (n_states, H, dk, dv)):
+            raise ValueError(f"{nm} must be float32 [{'n_seqs' if packed else 'B'},H,dk,dv]")
+    dev = q.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    new = torch.zeros if packed else torch.empty  # a packed call leaves tokens past the last offset
+    dq, dkk, dal = (new((B, T, H, dk), **f32) for _ in range(3))
+    dvv = new((B, T, H, dv), **f32)
+    dgates = (new((B, T, H, dk), **f32), new((B, T, H, dv), **f32)) if g2 else (new((B, T, H), **f32),)
+    ds0 = torch.empty((n_states, H, dk, dv), **f32) if want_d_initial else None
+    shape = Shape(B, T, H, dk, dv, 64, code)
+    if packed:
+        need = int(lib().kda_chunk_bwd_varlen_workspace_size(ctypes.byref(shape), n_states))
+    else:
+        need = int(lib().kda_chunk_bwd_workspace_size(ctypes.byref(shape)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check((q, k, v, alpha, d_o, cu_seqlens, initial_state, d_final_state, workspace) + tuple(gates),
+           ("q", "k", "v", "alpha", "d_o", "cu_seqlens", "initial_state", "d_final_state", "workspace")
+           + tuple(nm for nm, _ in named[4:]), dev)
+    nbytes = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+    head = [ctypes.byref(shape)] + ([_ptr(cu_seqlens), n_states] if packed else [])
+    ins = [_ptr(q), _ptr(k), _ptr(v), _ptr(alpha)] + [_ptr(x) for x in gates]
+    outs = [_ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dal)] + [_ptr(x) for x in dgates]
+    entry = ("kda_gdn2_chunk_bwd" if g2 else "kda_chunk_bwd") + ("_varlen" if packed else "")
+    rc = getattr(lib(), entry)(*head, *ins, _ptr(initial_state), _ptr(d_o), _ptr(d_final_state), *outs, _ptr(ds0),
+                               _ptr(workspace), nbytes, _stream(dev))
+    if rc != 0:
+        raise KdaError(rc, entry)
+    return (dq, dkk, dvv, dal) + dgates + (ds0,)
+
+
 def chunk_bwd(q, k, v, alpha, beta, d_o, initial_state=None, d_final_state=None, want_d_initial=True,
               workspace=None):
     """Gradients of L = sum <d_o, o> + <d_final_state, S_T> through chunk_fwd (KDA / CKDA),
@@ -521,39 +582,7 @@ def chunk_bwd(q, k, v, alpha, beta, d_o, initial_state=None, d_final_state=None,
     d_final_state fp32 [B,H,dk,dv] or None (zero).  workspace: optional uint8 device
     tensor of at least bwd_workspace_size(...) bytes (allocated here when omitted).
     Returns (dq, dk, dv, dalpha, dbeta, d_initial_state or None), all fp32."""
-    torch = _torch()
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
-    code = _dtype_code(q)
-    for t, nm in ((k, "k"), (alpha, "alpha"), (v, "v"), (beta, "beta"), (d_o, "d_o")):
-        if t.dtype != q.dtype:
-            raise TypeError(f"{nm} must have the dtype of q")
-    if (k.shape != q.shape or alpha.shape != q.shape or v.shape != (B, T, H, dv) or beta.shape != (B, T, H)
-            or d_o.shape != (B, T, H, dv)):
-        raise ValueError("shapes: q, k, alpha [B,T,H,dk]; v, d_o [B,T,H,dv]; beta [B,T,H]")
-    for t, nm in ((initial_state, "initial_state"), (d_final_state, "d_final_state")):
-        if t is not None and (t.dtype != torch.float32 or t.shape != (B, H, dk, dv)):
-            raise ValueError(f"{nm} must be float32 [B,H,dk,dv]")
-    dev = q.device
-    f32 = dict(dtype=torch.float32, device=dev)
-    dq, dkk, dal = (torch.empty((B, T, H, dk), **f32) for _ in range(3))
-    dvv = torch.empty((B, T, H, dv), **f32)
-    dbeta = torch.empty((B, T, H), **f32)
-    ds0 = torch.empty((B, H, dk, dv), **f32) if want_d_initial else None
-    shape = Shape(B, T, H, dk, dv, 64, code)
-    need = int(lib().kda_chunk_bwd_workspace_size(ctypes.byref(shape)))
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    _check((q, k, v, alpha, beta, d_o, initial_state, d_final_state, workspace),
-           ("q", "k", "v", "alpha", "beta", "d_o", "initial_state", "d_final_state", "workspace"), dev)
-    nbytes = workspace.numel() * workspace.element_size()
-    rc = lib().kda_chunk_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
-                             _ptr(initial_state), _ptr(d_o), _ptr(d_final_state), _ptr(dq), _ptr(dkk), _ptr(dvv),
-                             _ptr(dal), _ptr(dbeta), _ptr(ds0), _ptr(workspace), ctypes.c_size_t(nbytes),
-                             _stream(dev))
-    if rc != 0:
-        raise KdaError(rc, "kda_chunk_bwd")
-    return dq, dkk, dvv, dal, dbeta, ds0
+    return _bwd_call(q, k, v, alpha, (beta,), d_o, None, initial_state, d_final_state, want_d_initial, workspace)
 
 
 def chunk_bwd_varlen(q, k, v, alpha, beta, d_o, cu_seqlens, initial_state=None, d_final_state=None,
@@ -561,42 +590,16 @@ def chunk_bwd_varlen(q, k, v, alpha, beta, d_o, cu_seqlens, initial_state=None, 
     """Backward of chunk_fwd_varlen: a packed batch (B = 1) of len(cu_seqlens) - 1 sequences
     at the int32 device offsets cu_seqlens, each differentiated from its own start state.
     initial_state, d_final_state: fp32 [n_seqs, H, dk, dv] or None.  Returns (dq, dk, dv,
-    dalpha, dbeta, d_initial_state [n_seqs, H, dk, dv] or None), all fp32."""
-    torch = _torch()
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
-    if B != 1:
-        raise ValueError("a packed batch has B = 1")
-    code = _dtype_code(q)
-    for t, nm in ((k, "k"), (alpha, "alpha"), (v, "v"), (beta, "beta"), (d_o, "d_o")):
-        if t.dtype != q.dtype:
-            raise TypeError(f"{nm} must have the dtype of q")
-    if (k.shape != q.shape or alpha.shape != q.shape or v.shape != (B, T, H, dv) or beta.shape != (B, T, H)
-            or d_o.shape != (B, T, H, dv)):
-        raise ValueError("shapes: q, k, alpha [1,T,H,dk]; v, d_o [1,T,H,dv]; beta [1,T,H]")
-    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
-        raise TypeError("cu_seqlens must be a 1-d int32 tensor")
-    n = cu_seqlens.numel() - 1
-    for t, nm in ((initial_state, "initial_state"), (d_final_state, "d_final_state")):
-        if t is not None and (t.dtype != torch.float32 or t.shape != (n, H, dk, dv)):
-            raise ValueError(f"{nm} must be float32 [n_seqs,H,dk,dv]")
-    dev = q.device
-    f32 = dict(dtype=torch.float32, device=dev)
-    dq, dkk, dal = (torch.zeros((B, T, H, dk), **f32) for _ in range(3))
-    dvv = torch.zeros((B, T, H, dv), **f32)
-    dbeta = torch.zeros((B, T, H), **f32)
-    ds0 = torch.empty((n, H, dk, dv), **f32) if want_d_initial else None
-    shape = Shape(B, T, H, dk, dv, 64, code)
-    need = int(lib().kda_chunk_bwd_varlen_workspace_size(ctypes.byref(shape), n))
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    _check((q, k, v, alpha, beta, d_o, cu_seqlens, initial_state, d_final_state, workspace),
-           ("q", "k", "v", "alpha", "beta", "d_o", "cu_seqlens", "initial_state", "d_final_state", "workspace"), dev)
-    nbytes = workspace.numel() * workspace.element_size()
-    rc = lib().kda_chunk_bwd_varlen(ctypes.byref(shape), _ptr(cu_seqlens), n, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
-                                    _ptr(beta), _ptr(initial_state), _ptr(d_o), _ptr(d_final_state), _ptr(dq),
-                                    _ptr(dkk), _ptr(dvv), _ptr(dal), _ptr(dbeta), _ptr(ds0), _ptr(workspace),
-                                    ctypes.c_size_t(nbytes), _stream(dev))
-    if rc != 0:
-        raise KdaError(rc, "kda_chunk_bwd_varlen")
-    return dq, dkk, dvv, dal, dbeta, ds0
+    dalpha, dbeta, d_initial_state [n_seqs, H, dk, dv] or None), all fp32; tokens after the
+    last offset get zeros."""
+    return _bwd_call(q, k, v, alpha, (beta,), d_o, cu_seqlens, initial_state, d_final_state, want_d_initial,
+                     workspace)
+
+
+def gdn2_chunk_bwd(q, k, v, alpha, erase, write, d_o, initial_state=None, d_final_state=None, want_d_initial=True,
+                   workspace=None, cu_seqlens=None):
+    """Gated DeltaNet-2 backward of gdn2_chunk_fwd (or, with cu_seqlens, of its packed form):
+    erase [B,T,H,dk] and write [B,T,H,dv] in the dtype of q in place of beta.  Returns (dq,
+    dk, dv, dalpha, d_erase, d_write, d_initial_state or None), all fp32."""
+    return _bwd_call(q, k, v, alpha, (erase, write), d_o, cu_seqlens, initial_state, d_final_state, want_d_initial,
+                     workspace)

@@ -227,6 +227,11 @@ struct BwdPtrs {
   float *dq, *dk, *dv, *dalpha, *dbeta, *ds0;
   void* ws;
   size_t ws_bytes;
+  // Gated DeltaNet-2 (beta, dbeta NULL): the gates and their gradients
+  const void* erase = nullptr;
+  const void* write = nullptr;
+  float* derase = nullptr;
+  float* dwrite = nullptr;
 };
 
 // Workspace of a packed batch's backward: chunk blocks [H][gmax], then the chunk table
@@ -261,19 +266,21 @@ int bwd_impl(const kda_shape* shape, const int* cu, int n_seqs, const BwdPtrs& p
   }
   const int64_t rows = (int64_t)s.B * s.T * s.H;
   const int64_t st_bytes = (int64_t)(packed ? n_seqs : s.B) * s.H * s.dk * s.dv * 4;
-  if (rows > 0 && (!p.q || !p.k || !p.v || !p.alpha || !p.beta || !p.d_o || !p.dq || !p.dk || !p.dv || !p.dalpha ||
-                   !p.dbeta))
+  const bool g2 = p.erase || p.write || p.derase || p.dwrite;
+  if (rows > 0 && (!p.q || !p.k || !p.v || !p.alpha || !p.d_o || !p.dq || !p.dk || !p.dv || !p.dalpha))
+    return KDA_ERR_NULL;
+  if (rows > 0 && (g2 ? (!p.erase || !p.write || !p.derase || !p.dwrite) : (!p.beta || !p.dbeta)))
     return KDA_ERR_NULL;
   const BwdVarlenLayout VL = packed ? bwd_varlen_layout(s, n_seqs) : BwdVarlenLayout{};
   const size_t ws_need = packed ? VL.bytes : kda::bwd_workspace_bytes(s.B, s.T, s.H, s.dk, s.dv);
   if (ws_need > 0 && !p.ws) return KDA_ERR_NULL;
   if (p.ws_bytes < ws_need) return KDA_ERR_WORKSPACE;
   // q, k, v, alpha and d_o move in vectors; beta is read per element
-  const void* in_ptrs[] = {p.q, p.k, p.v, p.alpha, p.d_o};
+  const void* in_ptrs[] = {p.q, p.k, p.v, p.alpha, p.d_o, p.erase, p.write};
   for (const void* x : in_ptrs)
     if (x && misaligned(x)) return KDA_ERR_ALIGN;
   if (p.beta && misaligned(p.beta, es)) return KDA_ERR_ALIGN;
-  const void* out_ptrs[] = {p.dq, p.dk, p.dv, p.dalpha, p.ds0, p.s0, p.dsT};
+  const void* out_ptrs[] = {p.dq, p.dk, p.dv, p.dalpha, p.ds0, p.s0, p.dsT, p.derase, p.dwrite};
   for (const void* x : out_ptrs)
     if (x && misaligned(x)) return KDA_ERR_ALIGN;
   if (p.dbeta && misaligned(p.dbeta, 4)) return KDA_ERR_ALIGN;
@@ -282,11 +289,15 @@ int bwd_impl(const kda_shape* shape, const int* cu, int n_seqs, const BwdPtrs& p
                       range_of(p.v, rows * s.dv * es),       range_of(p.alpha, rows * s.dk * es),
                       range_of(p.beta, rows * es),           range_of(p.d_o, rows * s.dv * es),
                       range_of(p.s0, p.s0 ? st_bytes : 0),   range_of(p.dsT, p.dsT ? st_bytes : 0),
-                      range_of(cu, packed ? (int64_t)(n_seqs + 1) * 4 : 0)};
+                      range_of(cu, packed ? (int64_t)(n_seqs + 1) * 4 : 0),
+                      range_of(p.erase, p.erase ? rows * s.dk * es : 0),
+                      range_of(p.write, p.write ? rows * s.dv * es : 0)};
   const Range out[] = {range_of(p.dq, rows * s.dk * 4),      range_of(p.dk, rows * s.dk * 4),
                        range_of(p.dv, rows * s.dv * 4),      range_of(p.dalpha, rows * s.dk * 4),
-                       range_of(p.dbeta, rows * 4),          range_of(p.ds0, p.ds0 ? st_bytes : 0),
-                       range_of(p.ws, (int64_t)ws_need)};
+                       range_of(p.dbeta, p.dbeta ? rows * 4 : 0), range_of(p.ds0, p.ds0 ? st_bytes : 0),
+                       range_of(p.ws, (int64_t)ws_need),
+                       range_of(p.derase, p.derase ? rows * s.dk * 4 : 0),
+                       range_of(p.dwrite, p.dwrite ? rows * s.dv * 4 : 0)};
   constexpr int nout = sizeof(out) / sizeof(out[0]);
   for (int i = 0; i < nout; ++i) {
     for (const Range& r : in)
@@ -296,6 +307,12 @@ int bwd_impl(const kda_shape* shape, const int* cu, int n_seqs, const BwdPtrs& p
   }
   kda::BwdArgs a{p.q,  p.k,  p.v,      p.alpha, p.beta,           p.d_o, p.s0, p.dsT, p.dq, p.dk, p.dv, p.dalpha,
                  p.dbeta, p.ds0, (float*)p.ws, s.B, s.T, s.H, s.dk, s.dv, s.dtype == KDA_BF16, stream};
+  if (g2) {
+    a.erase = p.erase;
+    a.write = p.write;
+    a.derase = p.derase;
+    a.dwrite = p.dwrite;
+  }
   if (packed) {
     if (n_seqs == 0) return KDA_OK;
     char* ws = (char*)p.ws;
@@ -565,6 +582,45 @@ int kda_chunk_bwd_varlen(const kda_shape* shape, const int* cu_seqlens, int n_se
   if (!cu_seqlens) return KDA_ERR_NULL;
   const BwdPtrs p{q, k, v, alpha, beta, initial_state, d_o, d_final_state, dq, dk, dv, dalpha, dbeta, d_initial_state,
                   workspace, workspace_bytes};
+  return bwd_impl(shape, cu_seqlens, n_seqs, p, stream);
+}
+
+int kda_gdn2_chunk_bwd(const kda_shape* shape, const void* q, const void* k, const void* v, const void* alpha,
+                       const void* erase_gate, const void* write_gate, const float* initial_state, const void* d_o,
+                       const float* d_final_state, float* dq, float* dk, float* dv, float* dalpha, float* d_erase,
+                       float* d_write, float* d_initial_state, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  BwdPtrs p{q, k, v, alpha, nullptr, initial_state, d_o, d_final_state, dq, dk, dv, dalpha, nullptr, d_initial_state,
+            workspace, workspace_bytes};
+  p.erase = erase_gate;
+  p.write = write_gate;
+  p.derase = d_erase;
+  p.dwrite = d_write;
+  if (!erase_gate || !write_gate || !d_erase || !d_write) {
+    if (!shape) return KDA_ERR_NULL;
+    if ((int64_t)shape->B * shape->T * shape->H > 0) return KDA_ERR_NULL;
+  }
+  return bwd_impl(shape, nullptr, -1, p, stream);
+}
+
+int kda_gdn2_chunk_bwd_varlen(const kda_shape* shape, const int* cu_seqlens, int n_seqs, const void* q,
+                              const void* k, const void* v, const void* alpha, const void* erase_gate,
+                              const void* write_gate, const float* initial_state, const void* d_o,
+                              const float* d_final_state, float* dq, float* dk, float* dv, float* dalpha,
+                              float* d_erase, float* d_write, float* d_initial_state, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (!shape) return KDA_ERR_NULL;
+  if (n_seqs < 0) return KDA_ERR_SHAPE;
+  if (!cu_seqlens) return KDA_ERR_NULL;
+  BwdPtrs p{q, k, v, alpha, nullptr, initial_state, d_o, d_final_state, dq, dk, dv, dalpha, nullptr, d_initial_state,
+            workspace, workspace_bytes};
+  p.erase = erase_gate;
+  p.write = write_gate;
+  p.derase = d_erase;
+  p.dwrite = d_write;
+  if (!erase_gate || !write_gate || !d_erase || !d_write) {
+    if ((int64_t)shape->T * shape->H > 0) return KDA_ERR_NULL;
+  }
   return bwd_impl(shape, cu_seqlens, n_seqs, p, stream);
 }
 

@@ -202,7 +202,7 @@ __device__ __forceinline__ void mfma4(f32x4_t& acc, const float (&av)[4], const 
 //       r_ij = F_i B_j, F the product from the start of i's lam-half through i, B the
 //       product after j through the end of j's lam-half; level 0 gives A's diagonal;
 //   (d) M = (I + diag(beta) D)^-1 by blocks; (e) W = M diag(beta) (K o gamma).
-template <typename T, int DK>
+template <typename T, int DK, bool G2>
 __global__ __launch_bounds__(DK == 128 ? NTG : NT) void bwd_records_kernel(BwdArgs a, int NC) {
   constexpr int NTR = DK == 128 ? NTG : NT;  // one (channel, block) item per thread
   constexpr int LK = DK + 4, LC = C + 1, NI = DK * NB / NTR;  // items per thread
@@ -222,7 +222,9 @@ __global__ __launch_bounds__(DK == 128 ? NTG : NT) void bwd_records_kernel(BwdAr
   float *R0 = sR, *R1 = sR + C * LK, *R2 = sR + 2 * C * LK;
 
   // ---- (a) items (c, I): load, block products
-  float al[NI][SUB], qv[NI][SUB], kv[NI][SUB], pi[NI][SUB], sg[NI][SUB];
+  // xv: the row operand of T and of W: k (KDA, beta applied in the inverse) or the
+  // Gated DeltaNet-2 erase vector b o k
+  float al[NI][SUB], qv[NI][SUB], kv[NI][SUB], xv[NI][SUB], pi[NI][SUB], sg[NI][SUB];
 #pragma unroll
   for (int it = 0; it < NI; ++it) {
     const int item = tid + it * NTR, c = item % DK, I = item / DK;
@@ -233,9 +235,10 @@ __global__ __launch_bounds__(DK == 128 ? NTG : NT) void bwd_records_kernel(BwdAr
       al[it][r] = in ? Elem<T>::load(a.alpha, kb + i * ks + c) : 1.f;
       qv[it][r] = in ? Elem<T>::load(a.q, kb + i * ks + c) : 0.f;
       kv[it][r] = in ? Elem<T>::load(a.k, kb + i * ks + c) : 0.f;
+      xv[it][r] = G2 ? (in ? Elem<T>::load(a.erase, kb + i * ks + c) : 0.f) * kv[it][r] : kv[it][r];
     }
   }
-  for (int i = tid; i < C; i += NTR) sB[i] = i < len ? Elem<T>::load(a.beta, bb + (size_t)i * a.H) : 0.f;
+  for (int i = tid; i < C; i += NTR) sB[i] = G2 ? 1.f : (i < len ? Elem<T>::load(a.beta, bb + (size_t)i * a.H) : 0.f);
 #pragma unroll
   for (int it = 0; it < NI; ++it) {
     const int item = tid + it * NTR, c = item % DK, I = item / DK;
@@ -282,7 +285,7 @@ __global__ __launch_bounds__(DK == 128 ? NTG : NT) void bwd_records_kernel(BwdAr
       ch[L.KR + i * DK + c] = kv[it][r] * (after * sg[it][r]);
       ch[L.QG + i * DK + c] = qv[it][r] * (before * pi[it][r]);
       R0[i * LK + c] = qv[it][r] * pi[it][r];
-      R1[i * LK + c] = kv[it][r] * pi[it][r];
+      R1[i * LK + c] = xv[it][r] * pi[it][r];
       R2[i * LK + c] = kv[it][r] * sg[it][r];
     }
   }
@@ -340,7 +343,7 @@ __global__ __launch_bounds__(DK == 128 ? NTG : NT) void bwd_records_kernel(BwdAr
       for (int r = 0; r < SUB; ++r) {
         const int i = I * SUB + r;
         R0[i * LK + c] = qv[it][r] * Fv[r];
-        R1[i * LK + c] = kv[it][r] * Fv[r];
+        R1[i * LK + c] = xv[it][r] * Fv[r];
         R2[i * LK + c] = kv[it][r] * Bv[r];
       }
     }
@@ -411,7 +414,7 @@ __global__ __launch_bounds__(DK == 128 ? NTG : NT) void bwd_records_kernel(BwdAr
     for (int J = 0; J < NB; ++J)
       if (J < I) before *= sPib[J * DK + c];
 #pragma unroll
-    for (int r = 0; r < SUB; ++r) R0[(I * SUB + r) * LK + c] = kv[it][r] * pi[it][r] * before;
+    for (int r = 0; r < SUB; ++r) R0[(I * SUB + r) * LK + c] = xv[it][r] * pi[it][r] * before;
   }
   __syncthreads();
   for (int job = wave; job < 4 * (DK / 16); job += NTR / 64) {
@@ -451,7 +454,7 @@ __global__ __launch_bounds__(DK == 128 ? NTG : NT) void bwd_records_kernel(BwdAr
 
 // bwd_state_kernel: chunks in order; writes the chunk-start state S_n and Delta_n.  The
 // next chunk's operands are loaded into registers while the current one computes.
-template <typename T, int DK>
+template <typename T, int DK, bool G2>
 __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC) {
   constexpr int LM = C + 4, LW = DK + 4, LV = VTW + 4;
   constexpr int NM = C * C / 4 / NT, NW = C * DK / 4 / NT, NV = C * VTW / 4 / NT;
@@ -466,10 +469,11 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC) {
   for (int I = 0; I < DK / 16; ++I)
 #pragma unroll
     for (int r = 0; r < 4; ++r) S[I][r] = a.s0 ? a.s0[((size_t)bh * DK + 16 * I + 4 * g + r) * dv + col] : 0.f;
-  // one chunk's operands in registers: M; W; K o rho; V and beta; gamma_last.  Step st
+  // one chunk's operands in registers: M; W; K o rho; V and beta (or, Gated DeltaNet-2,
+  // the write gate w: M (w o V)); gamma_last.  Step st
   // moves chunk st - 1 from registers to LDS, issues the loads of chunk st, then computes
   // chunk st - 1 while they are in flight.
-  float4 pm[NM], pw[NW], pk[NW], pv[NV];
+  float4 pm[NM], pw[NW], pk[NW], pv[NV], pwg[G2 ? NV : 1];
   float pb[NV], pg = 0.f;
   for (int st = 0; st <= nch; ++st) {
     if (st > 0) {
@@ -491,8 +495,12 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC) {
 #pragma unroll
       for (int it = 0; it < NV; ++it) {
         const int x = tid + it * NT, j = x / (VTW / 4), c = 4 * (x % (VTW / 4));
-        const float b = pb[it];
-        *(float4*)(sV + j * LV + c) = make_float4(pv[it].x * b, pv[it].y * b, pv[it].z * b, pv[it].w * b);
+        if (G2) {
+          *(float4*)(sV + j * LV + c) = mul4(pv[it], pwg[G2 ? it : 0]);
+        } else {
+          const float b = pb[it];
+          *(float4*)(sV + j * LV + c) = make_float4(pv[it].x * b, pv[it].y * b, pv[it].z * b, pv[it].w * b);
+        }
       }
       if (tid < DK) sGl[tid] = pg;
       __syncthreads();
@@ -519,7 +527,10 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC) {
         const int x = tid + it * NT, j = x / (VTW / 4), c = 4 * (x % (VTW / 4));
         const bool in = j < cg.len;
         pv[it] = in ? ld4<T>(a.v, vb + j * vs + v0 + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-        pb[it] = in ? Elem<T>::load(a.beta, bb + (size_t)j * a.H) : 0.f;
+        if (G2)
+          pwg[G2 ? it : 0] = in ? ld4<T>(a.write, vb + j * vs + v0 + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+        else
+          pb[it] = in ? Elem<T>::load(a.beta, bb + (size_t)j * a.H) : 0.f;
       }
       if (tid < DK) pg = cl[L.gam + (C - 1) * DK + tid];
     }
@@ -703,7 +714,7 @@ __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC) {
 //   D  the block-anchored products PA, PD, F with their B operands staged in LDS;
 //   E  per (channel, block): the in-block decayed sums, dq and dk, the gate gradient.
 
-template <typename T, int DK, int DV>
+template <typename T, int DK, int DV, bool G2>
 __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
   constexpr int LV = DV + 4, LK = DK + 4, LC = C + 1;
   constexpr int RSZ = (3 * C * LV > 3 * C * LK) ? 3 * C * LV : 3 * C * LK;
@@ -751,7 +762,7 @@ __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
     sM[i * LC + j + 2] = m.z;
     sM[i * LC + j + 3] = m.w;
   }
-  for (int i = tid; i < C; i += NTG) sB[i] = i < len ? Elem<T>::load(a.beta, bb + (size_t)i * a.H) : 0.f;
+  for (int i = tid; i < C; i += NTG) sB[i] = G2 ? 1.f : (i < len ? Elem<T>::load(a.beta, bb + (size_t)i * a.H) : 0.f);
   for (int x = tid; x < NB * DK; x += NTG) sPib[x] = ch[L.pib + x];
   __syncthreads();
 
@@ -764,7 +775,7 @@ __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
       sf[u] = *(const float4*)(S + c * DV + 16 * u + 4 * g);
       df[u] = *(const float4*)(DS + c * DV + 16 * u + 4 * g);
     }
-    float gm[4][4], rh[4][4], qq[4][4], kk[4][4];
+    float gm[4][4], rh[4][4], qq[4][4], kk[4][4], eb[4][4];  // eb: erase gate (GDN-2)
 #pragma unroll
     for (int I = 0; I < 4; ++I)
 #pragma unroll
@@ -774,6 +785,7 @@ __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
         rh[I][r] = RHO[i * DK + c];
         qq[I][r] = in1(a.q, i, c);
         kk[I][r] = in1(a.k, i, c);
+        eb[I][r] = G2 ? in1(a.erase, i, c) : 0.f;
       }
     float part = 0.f;
 #pragma unroll
@@ -811,12 +823,20 @@ __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * J + 4 * g + r;
-        AV[i * DK + c] = aq[J][r] * qq[J][r] + kg[r] * kk[J][r];
+        // KDA: kg = d(K o gamma) (beta inside Mt); GDN-2: kg = d(E o gamma), e = b o k
+        const float xk = G2 ? eb[J][r] * kk[J][r] : kk[J][r];
+        AV[i * DK + c] = aq[J][r] * qq[J][r] + kg[r] * xk;
         BV[i * DK + c] = ar[J][r] * kk[J][r];
         DWg[i * DK + c] = aw[J][r];
         if (i < len) {
           a.dq[kb + i * ks + c] = aq[J][r] * gm[J][r];
-          a.dk[kb + i * ks + c] = ar[J][r] * rh[J][r] + kg[r] * gm[J][r];
+          if (G2) {
+            const float de = kg[r] * gm[J][r];
+            a.dk[kb + i * ks + c] = ar[J][r] * rh[J][r] + eb[J][r] * de;
+            a.derase[kb + i * ks + c] = kk[J][r] * de;
+          } else {
+            a.dk[kb + i * ks + c] = ar[J][r] * rh[J][r] + kg[r] * gm[J][r];
+          }
         }
       }
     }
@@ -854,7 +874,15 @@ __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 16 * J + 4 * g + r;
-        if (j < len) a.dv[vb + j * vs + 16 * vt + n] = acc[r];
+        if (j < len) {
+          const size_t o = vb + j * vs + 16 * vt + n;
+          if (G2) {  // acc = d(w o V)
+            a.dv[o] = acc[r] * Elem<T>::load(a.write, o);
+            a.dwrite[o] = acc[r] * Elem<T>::load(a.v, o);
+          } else {
+            a.dv[o] = acc[r];
+          }
+        }
       }
     }
   }
@@ -874,10 +902,15 @@ __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
       if (J <= I) {
         float4 vv[DV / 16], kg[DK / 16];
 #pragma unroll
-        for (int u = 0; u < DV / 16; ++u) vv[u] = j < len ? ld4<T>(a.v, vb + j * vs + 16 * u + 4 * g) : z4;
+        for (int u = 0; u < DV / 16; ++u) {
+          vv[u] = j < len ? ld4<T>(a.v, vb + j * vs + 16 * u + 4 * g) : z4;
+          if (G2) vv[u] = mul4(vv[u], j < len ? ld4<T>(a.write, vb + j * vs + 16 * u + 4 * g) : z4);
+        }
 #pragma unroll
-        for (int u = 0; u < DK / 16; ++u)
+        for (int u = 0; u < DK / 16; ++u) {
           kg[u] = mul4(in4(a.k, j, 16 * u + 4 * g), *(const float4*)(GAM + j * DK + 16 * u + 4 * g));
+          if (G2) kg[u] = mul4(kg[u], in4(a.erase, j, 16 * u + 4 * g));
+        }
         const float *rd = RD + (16 * I + n) * LV, *rw = RW + (16 * I + n) * LK;
 #pragma unroll
         for (int u = 0; u < DV / 16; ++u) mm16(acc, rd, 16 * u, [&](int t) { return f4c(vv[u], t); });
@@ -894,11 +927,12 @@ __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
   __syncthreads();
 
   // ---- C: dbeta = colsum(dMt o M) + rowsum(dT o D);  X = dMt Mt^T;  dT = -(M^T X) o strict-low
-  for (int j = tid; j < C; j += NTG) {
-    float s = 0.f;
-    for (int i = j; i < C; ++i) s += sdT[i * LC + j] * sM[i * LC + j];
-    sdB[j] = s;
-  }
+  if (!G2)
+    for (int j = tid; j < C; j += NTG) {
+      float s = 0.f;
+      for (int i = j; i < C; ++i) s += sdT[i * LC + j] * sM[i * LC + j];
+      sdB[j] = s;
+    }
   float* RX = sR;  // X [C][LC]
   for (int job = wave; job < 16; job += NTG / 64) {
     const int I = job / 4, J = job % 4;
@@ -941,13 +975,14 @@ __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
     }
   }
   __syncthreads();
-  for (int i = tid; i < C; i += NTG) {
-    float s = 0.f;
+  if (!G2)
+    for (int i = tid; i < C; i += NTG) {
+      float s = 0.f;
 #pragma unroll 8
-    for (int j = 0; j < i; ++j) s += sdT[i * LC + j] * ch[L.D + i * C + j];
-    if (i < len) a.dbeta[bb + (size_t)i * a.H] = sdB[i] + s;
-    for (int j = 0; j < i; ++j) sdT[i * LC + j] *= sB[i];
-  }
+      for (int j = 0; j < i; ++j) s += sdT[i * LC + j] * ch[L.D + i * C + j];
+      if (i < len) a.dbeta[bb + (size_t)i * a.H] = sdB[i] + s;
+      for (int j = 0; j < i; ++j) sdT[i * LC + j] *= sB[i];
+    }
   __syncthreads();
   const float* sdD = sdT;
 
@@ -960,9 +995,10 @@ __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
     const int x = tid + it * NTG, i = x / (DK / 4), c = 4 * (x % (DK / 4));
     const float4 kv = in4(a.k, i, c), qv = in4(a.q, i, c);
     const float4 sg = *(const float4*)(SIG + i * DK + c), pn = *(const float4*)(PIN + i * DK + c);
+    const float4 xv = G2 ? mul4(kv, in4(a.erase, i, c)) : kv;  // row operand of the second product
     *(float4*)(RKS + i * LK + c) = mul4(kv, sg);
     *(float4*)(RQP + i * LK + c) = mul4(qv, pn);
-    *(float4*)(RKP + i * LK + c) = mul4(kv, pn);
+    *(float4*)(RKP + i * LK + c) = mul4(xv, pn);
   }
   __syncthreads();
   for (int job = wave; job < 12 * (DK / 16); job += NTG / 64) {
@@ -1025,13 +1061,16 @@ __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
   __syncthreads();
   for (int item = tid; item < DK * NB; item += NTG) {
     const int c = item % DK, Mb = item / DK, s = Mb * SUB;
-    float al[SUB], qv[SUB], kv[SUB], pin[SUB], pa[SUB], pd[SUB];
+    // xv: the row operand of the second product (k, or the GDN-2 erase vector b o k)
+    float al[SUB], qv[SUB], kv[SUB], xv[SUB], eg[SUB], pin[SUB], pa[SUB], pd[SUB];
 #pragma unroll
     for (int r = 0; r < SUB; ++r) {
       const int i = s + r;
       al[r] = RA[i * LK + c];
       qv[r] = RQ[i * LK + c];
       kv[r] = RK[i * LK + c];
+      eg[r] = G2 ? in1(a.erase, i, c) : 1.f;
+      xv[r] = G2 ? eg[r] * kv[r] : kv[r];
       pin[r] = PIN[i * DK + c];
     }
     const float* PAm = PA + (size_t)(Mb > 0 ? Mb - 1 : 0) * C * DK;
@@ -1073,12 +1112,17 @@ __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
 #pragma unroll
       for (int ri = r + 1; ri < SUB; ++ri) {
         P *= al[ri];
-        zc += (sdA[(s + ri) * LC + i] * qv[ri] + sdD[(s + ri) * LC + i] * kv[ri]) * P;
+        zc += (sdA[(s + ri) * LC + i] * qv[ri] + sdD[(s + ri) * LC + i] * xv[ri]) * P;
       }
       zc += sg[r] * fr[r];
       if (i < len) {
         a.dq[kb + i * ks + c] += zq;
-        a.dk[kb + i * ks + c] += zr + zc;
+        if (G2) {  // zr is the row-side sum of T: part of d e, e = b o k
+          a.dk[kb + i * ks + c] += eg[r] * zr + zc;
+          a.derase[kb + i * ks + c] += kv[r] * zr;
+        } else {
+          a.dk[kb + i * ks + c] += zr + zc;
+        }
       }
     }
 
@@ -1096,7 +1140,7 @@ __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
 #pragma unroll
     for (int r = 0; r < SUB; ++r) {
       const int i = s + r;
-      u[r] = AV[i * DK + c] * gs + qv[r] * pa[r] + kv[r] * pd[r];
+      u[r] = AV[i * DK + c] * gs + qv[r] * pa[r] + xv[r] * pd[r];
       if (i == C - 1) u[r] += bvs + dgl * gs;
     }
     float f[SUB];
@@ -1109,7 +1153,10 @@ __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
         for (int r = 0; r < SUB; ++r) {
           const int i = I * SUB + r;
           gv[r] = AV[i * DK + c] * gs;
-          if (Mb > 0) gv[r] += RQ[i * LK + c] * PAm[i * DK + c] + RK[i * LK + c] * PDm[i * DK + c];
+          if (Mb > 0) {
+            const float xi = G2 ? RK[i * LK + c] * in1(a.erase, i, c) : RK[i * LK + c];
+            gv[r] += RQ[i * LK + c] * PAm[i * DK + c] + xi * PDm[i * DK + c];
+          }
           if (i == C - 1) gv[r] += bvs + dgl * gs;
         }
 #pragma unroll
@@ -1130,7 +1177,7 @@ __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
       if (s + m < len) a.dalpha[kb + (s + m) * ks + c] = acc;
 #pragma unroll
       for (int i = m + 1; i < SUB; ++i) {
-        float E = (qv[i] * sdA[(s + i) * LC + s + m] + kv[i] * sdD[(s + i) * LC + s + m]) * kv[m];
+        float E = (qv[i] * sdA[(s + i) * LC + s + m] + xv[i] * sdD[(s + i) * LC + s + m]) * kv[m];
         if (i == SUB - 1) E += f[m];
         u[i] = al[m] * u[i] + E;
       }
@@ -1139,7 +1186,7 @@ __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
 }
 
 // ---------------------------------------------------------------------------------------
-template <typename T, int DK>
+template <typename T, int DK, bool G2>
 static hipError_t launch_bwd_dk(const BwdArgs& a, int NC) {
   // per-chunk grid: B H NC (fixed) or H gmax (packed; workgroups past the chunk count
   // exit); walks: one workgroup per (chain, 64 value columns)
@@ -1147,28 +1194,29 @@ static hipError_t launch_bwd_dk(const BwdArgs& a, int NC) {
   const long per_chunk = a.ctab ? (long)a.H * a.gmax : (long)chains * NC;
   hipStream_t st = (hipStream_t)a.stream;
   if (per_chunk > 0) {
-    hipLaunchKernelGGL((bwd_records_kernel<T, DK>), dim3(per_chunk), dim3(DK == 128 ? NTG : NT), 0, st, a, NC);
-    hipLaunchKernelGGL((bwd_state_kernel<T, DK>), dim3(walks), dim3(NT), 0, st, a, NC);
+    hipLaunchKernelGGL((bwd_records_kernel<T, DK, G2>), dim3(per_chunk), dim3(DK == 128 ? NTG : NT), 0, st, a, NC);
+    hipLaunchKernelGGL((bwd_state_kernel<T, DK, G2>), dim3(walks), dim3(NT), 0, st, a, NC);
   }
   hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK>), dim3(walks), dim3(NT), 0, st, a, NC);
   if (per_chunk > 0) {
     if (a.Dv == 64)
-      hipLaunchKernelGGL((bwd_grads_kernel<T, DK, 64>), dim3(per_chunk), dim3(NTG), 0, st, a, NC);
+      hipLaunchKernelGGL((bwd_grads_kernel<T, DK, 64, G2>), dim3(per_chunk), dim3(NTG), 0, st, a, NC);
     else
-      hipLaunchKernelGGL((bwd_grads_kernel<T, DK, 128>), dim3(per_chunk), dim3(NTG), 0, st, a, NC);
+      hipLaunchKernelGGL((bwd_grads_kernel<T, DK, 128, G2>), dim3(per_chunk), dim3(NTG), 0, st, a, NC);
   }
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool G2>
 static hipError_t launch_bwd_t(const BwdArgs& a, int NC) {
-  return a.Dk == 64 ? launch_bwd_dk<T, 64>(a, NC) : launch_bwd_dk<T, 128>(a, NC);
+  return a.Dk == 64 ? launch_bwd_dk<T, 64, G2>(a, NC) : launch_bwd_dk<T, 128, G2>(a, NC);
 }
 
 hipError_t launch_bwd(const BwdArgs& a) {
   if ((long)(a.ctab ? a.n_seqs : a.B) * a.H == 0) return hipSuccess;
   const int NC = (a.T + C - 1) / C;
-  return a.bf16 ? launch_bwd_t<bf16_t>(a, NC) : launch_bwd_t<float>(a, NC);
+  if (a.erase) return a.bf16 ? launch_bwd_t<bf16_t, true>(a, NC) : launch_bwd_t<float, true>(a, NC);
+  return a.bf16 ? launch_bwd_t<bf16_t, false>(a, NC) : launch_bwd_t<float, false>(a, NC);
 }
 
 }  // namespace kda

@@ -77,6 +77,12 @@ struct BwdArgs {
   const int* cbase = nullptr;   // first global chunk of each sequence [n_seqs]
   const int* ctotal = nullptr;  // number of chunks [1]
   int n_seqs = 0, gmax = 0;
+  // Gated DeltaNet-2 (beta and dbeta unused): erase gate [.., dk], write gate [.., dv] and
+  // their gradients
+  const void* erase = nullptr;
+  const void* write = nullptr;
+  float* derase = nullptr;
+  float* dwrite = nullptr;
 };
 
 // fp32 offsets inside one chunk's workspace block of the backward (C = 64 rows, NB = 4

@@ -52,7 +52,7 @@ class Workload:
     dk: int
     dv: int
     dtype: str          # "bf16" or "f32"
-    gates: str          # "kda" or "ckda"
+    gates: str          # "kda", "ckda", "gdn2" or "sfda"
     zero_s0: bool
     decode_steps: int = 0   # > 0: decode workload, T is ignored
     index: int = 0

@@ -292,6 +292,33 @@ int kda_chunk_bwd_varlen(const kda_shape* shape, const int* cu_seqlens, int n_se
                          void* stream);
 
 /*
+ * Backward of the Gated DeltaNet-2 chunk forward (kda_gdn2_chunk_fwd): the gate-aware
+ * backward of the GDN-2 page (section 3), which keeps the erase gate b_t (per key
+ * channel, on the read) and the write gate w_t (per value channel, on the write) inside
+ * the gradients of the intra-chunk matrices.  With e = b o k per chunk,
+ * T = [sum_c e_ic k_jc r_ijc] (j < i), W = (I + T)^-1 (E o gamma), U = (I + T)^-1 (w o V).
+ *   erase_gate [B, T, H, dk], write_gate [B, T, H, dv] : inputs, dtype of q, 16-byte aligned
+ *   d_erase [B, T, H, dk], d_write [B, T, H, dv] : fp32 outputs in place of dbeta
+ * Everything else (workspace size kda_chunk_bwd_workspace_size / ..._varlen_workspace_size,
+ * layouts, alignment, alias rules, errors, the packed form) as kda_chunk_bwd and
+ * kda_chunk_bwd_varlen.
+ */
+int kda_gdn2_chunk_bwd(const kda_shape* shape, const void* q, const void* k, const void* v,
+                       const void* alpha, const void* erase_gate, const void* write_gate,
+                       const float* initial_state, const void* d_o, const float* d_final_state,
+                       float* dq, float* dk, float* dv, float* dalpha, float* d_erase,
+                       float* d_write, float* d_initial_state, void* workspace,
+                       size_t workspace_bytes, void* stream);
+int kda_gdn2_chunk_bwd_varlen(const kda_shape* shape, const int* cu_seqlens, int n_seqs,
+                              const void* q, const void* k, const void* v, const void* alpha,
+                              const void* erase_gate, const void* write_gate,
+                              const float* initial_state, const void* d_o,
+                              const float* d_final_state, float* dq, float* dk, float* dv,
+                              float* dalpha, float* d_erase, float* d_write,
+                              float* d_initial_state, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
  * One recurrent decode step for every (b, h), state updated in place:
  *   S <- (I - beta k k^T) Diag(alpha) S + beta k v^T ;  o <- S^T q.
  *   state : [B, H, dk, dv] fp32, read and written in place.

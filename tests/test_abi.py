@@ -357,3 +357,31 @@ def test_bwd_varlen_argument_errors(L):
     assert bwd(sh=kda.Shape(2, 300, 2, 64, 64, 64, 0)) == SHAPE
     assert bwd(nseq=-1) == SHAPE
     assert bwd(nseq=0) == 0                        # nothing to do
+
+
+def test_gdn2_bwd_argument_errors(L):
+    shape = kda.Shape(1, 64, 2, 64, 64, 64, 0)
+    need = L.kda_chunk_bwd_workspace_size(ctypes.byref(shape))
+    sz = ctypes.c_size_t
+
+    def bwd(e=_p(18), w=_p(19), de=_p(20), dw=_p(21), dq=_p(10), ws=_p(16), n=need, sh=shape):
+        return L.kda_gdn2_chunk_bwd(ctypes.byref(sh), _p(0), _p(1), _p(2), _p(3), e, w, None, _p(5), None, dq, _p(11),
+                                    _p(12), _p(13), de, dw, _p(15), ws, sz(n), None)
+
+    assert bwd(e=None) == NULL
+    assert bwd(w=None) == NULL
+    assert bwd(de=None) == NULL
+    assert bwd(dw=None) == NULL
+    assert bwd(n=need - 1) == WORKSPACE
+    assert bwd(e=_p(18, off=8)) == ALIGN
+    assert bwd(de=_p(18)) == ALIAS                 # d_erase over the erase gate
+    assert bwd(dw=_p(10, off=64)) == ALIAS         # d_write over dq
+    assert bwd(ws=_p(19)) == ALIAS                 # workspace over the write gate
+    zero = kda.Shape(0, 64, 2, 64, 64, 64, 0)
+    assert L.kda_gdn2_chunk_bwd(ctypes.byref(zero), *([None] * 16), None, sz(0), None) == 0
+    vshape = kda.Shape(1, 300, 2, 64, 64, 64, 0)
+    vneed = L.kda_chunk_bwd_varlen_workspace_size(ctypes.byref(vshape), 4)
+    assert L.kda_gdn2_chunk_bwd_varlen(ctypes.byref(vshape), None, 4, *([_p(0)] * 16), _p(16), sz(vneed),
+                                       None) == NULL
+    assert L.kda_gdn2_chunk_bwd_varlen(ctypes.byref(vshape), _p(17), -1, *([_p(0)] * 16), _p(16), sz(vneed),
+                                       None) == SHAPE
