@@ -359,7 +359,7 @@ def main():
                     help="workload of --bwd-only")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
               "the prefill shards over (b, h) with no exchange, which this single-GPU run does not exercise.",
               file=sys.stderr)
         sys.exit(2)
