@@ -42,10 +42,14 @@ __global__ __launch_bounds__(512) void decode_kernel(const void* __restrict__ q,
   static_assert(RPT * RG == DK && TPR * 4 == DV, "tile split");
   static_assert(!CPX || RPT % 2 == 0, "complex gates: a thread holds whole row pairs");
 
-  __shared__ float s_q[DK], s_k[DK], s_a[DK], s_v[DV];
-  __shared__ float s_e[G2 ? DK : 1];  // read-side key b o k (G2)
-  __shared__ float s_red[NWV][2][DV];
-  __shared__ float s_qk;
+  // token inputs are staged NTK tokens at a time, so that the token loop waits on no
+  // global load; the column sums of u, p and q . k alternate between two buffers, so
+  // that each token needs one barrier
+  constexpr int NTK = 8;
+  __shared__ float s_q[NTK][DK], s_k[NTK][DK], s_a[NTK][DK], s_v[NTK][DV], s_bt[NTK];
+  __shared__ float s_e[G2 ? NTK : 1][G2 ? DK : 1];  // read-side key b o k (G2)
+  __shared__ float s_red[2][NWV][2][DV];
+  __shared__ float s_qk[2][NWV];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -70,97 +74,99 @@ __global__ __launch_bounds__(512) void decode_kernel(const void* __restrict__ q,
 
   // tokens in order, the state staying in registers ([B, ntok, H, .] inputs and outputs;
   // ntok = 1 is the single decode step)
-  for (int tk = 0; tk < ntok; ++tk) {
-    const size_t row = (b * ntok + tk) * H + h;
-    if (tk > 0) __syncthreads();  // the previous token's LDS values are consumed
-    float qk_part = 0.f;
-    if (tid < DK) {
-      const float qq = Elem<T>::load(q, row * DK + tid);
-      const float kk = Elem<T>::load(k, row * DK + tid);
-      s_q[tid] = qq;
-      s_k[tid] = kk;
-      s_a[tid] = Elem<T>::load(alpha, row * DK + tid);
-      if constexpr (G2) s_e[tid] = Elem<T>::load(erase, row * DK + tid) * kk;
-      qk_part = qq * kk;
+  for (int t0 = 0; t0 < ntok; t0 += NTK) {
+    const int nb = min(NTK, ntok - t0);
+    if (t0 > 0) __syncthreads();  // the previous batch's staged inputs are consumed
+    for (int x = tid; x < nb * DK; x += NT) {
+      const int j = x / DK, c = x % DK;
+      const size_t row = (b * ntok + t0 + j) * H + h;
+      const float kk = Elem<T>::load(k, row * DK + c);
+      s_q[j][c] = Elem<T>::load(q, row * DK + c);
+      s_k[j][c] = kk;
+      s_a[j][c] = Elem<T>::load(alpha, row * DK + c);
+      if constexpr (G2) s_e[j][c] = Elem<T>::load(erase, row * DK + c) * kk;
     }
     // the write value: v (KDA, beta applied below) or w o v (G2)
-    if (tid < DV)
-      s_v[tid] = G2 ? Elem<T>::load(write, row * DV + tid) * Elem<T>::load(v, row * DV + tid)
-                    : Elem<T>::load(v, row * DV + tid);
-    const float bt = G2 ? 1.f : Elem<T>::load(beta, row);
-    // q . k: one product per thread (zero beyond DK), reduced per wave, then across waves
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) qk_part += __shfl_xor(qk_part, off);
-    if (lane == 0) s_red[wave][0][0] = qk_part;
-    __syncthreads();
-    if (tid == 0) {
-      float t = 0.f;
-#pragma unroll
-      for (int w = 0; w < NWV; ++w) t += s_red[w][0][0];
-      s_qk = t;
+    for (int x = tid; x < nb * DV; x += NT) {
+      const int j = x / DV, c = x % DV;
+      const size_t row = (b * ntok + t0 + j) * H + h;
+      s_v[j][c] = G2 ? Elem<T>::load(write, row * DV + c) * Elem<T>::load(v, row * DV + c)
+                     : Elem<T>::load(v, row * DV + c);
     }
+    if (tid < nb) s_bt[tid] = G2 ? 1.f : Elem<T>::load(beta, (b * ntok + t0 + tid) * H + h);
+    __syncthreads();
 
-    float u[4] = {0.f, 0.f, 0.f, 0.f}, p[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < nb; ++j) {
+      const int par = (t0 + j) & 1;
+      float u[4] = {0.f, 0.f, 0.f, 0.f}, p[4] = {0.f, 0.f, 0.f, 0.f};
+      float qk = 0.f;  // q . k over this thread's rows, counted once per row (column quad 0)
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int r = row_of(i);
-      const float kk = G2 ? s_e[r] : s_k[r], qq = s_q[r];
-      if constexpr (CPX) {
-        // rows 2p (i even) and 2p+1 (i odd) of this thread: z <- lambda z with
-        // row 2p <- Re s_2p - Im s_2p+1, row 2p+1 <- Im s_2p + Re s_2p+1
-        if ((i & 1) == 0) {
-          const float lr = s_a[r], li = s_a[r + 1];
-          const float4 x = s[i], y = s[i + 1];
-          s[i] = make_float4(lr * x.x - li * y.x, lr * x.y - li * y.y, lr * x.z - li * y.z, lr * x.w - li * y.w);
-          s[i + 1] = make_float4(li * x.x + lr * y.x, li * x.y + lr * y.y, li * x.z + lr * y.z, li * x.w + lr * y.w);
+      for (int i = 0; i < RPT; ++i) {
+        const int r = row_of(i);
+        const float kk = G2 ? s_e[j][r] : s_k[j][r], qq = s_q[j][r];
+        if constexpr (CPX) {
+          // rows 2p (i even) and 2p+1 (i odd) of this thread: z <- lambda z with
+          // row 2p <- Re s_2p - Im s_2p+1, row 2p+1 <- Im s_2p + Re s_2p+1
+          if ((i & 1) == 0) {
+            const float lr = s_a[j][r], li = s_a[j][r + 1];
+            const float4 x = s[i], y = s[i + 1];
+            s[i] = make_float4(lr * x.x - li * y.x, lr * x.y - li * y.y, lr * x.z - li * y.z, lr * x.w - li * y.w);
+            s[i + 1] = make_float4(li * x.x + lr * y.x, li * x.y + lr * y.y, li * x.z + lr * y.z, li * x.w + lr * y.w);
+          }
+        } else {
+          const float a = s_a[j][r];
+          s[i].x *= a; s[i].y *= a; s[i].z *= a; s[i].w *= a;
         }
-      } else {
-        const float a = s_a[r];
-        s[i].x *= a; s[i].y *= a; s[i].z *= a; s[i].w *= a;
+        u[0] += kk * s[i].x; u[1] += kk * s[i].y; u[2] += kk * s[i].z; u[3] += kk * s[i].w;
+        p[0] += qq * s[i].x; p[1] += qq * s[i].y; p[2] += qq * s[i].z; p[3] += qq * s[i].w;
+        if (cq == 0) qk += qq * s_k[j][r];
       }
-      u[0] += kk * s[i].x; u[1] += kk * s[i].y; u[2] += kk * s[i].z; u[3] += kk * s[i].w;
-      p[0] += qq * s[i].x; p[1] += qq * s[i].y; p[2] += qq * s[i].z; p[3] += qq * s[i].w;
-    }
-    // reduce the row groups that share a wave
+      // reduce the row groups that share a wave
 #pragma unroll
-    for (int off = TPR; off < 64; off <<= 1) {
+      for (int off = TPR; off < 64; off <<= 1) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u[j] += __shfl_xor(u[j], off);
-        p[j] += __shfl_xor(p[j], off);
+        for (int jj = 0; jj < 4; ++jj) {
+          u[jj] += __shfl_xor(u[jj], off);
+          p[jj] += __shfl_xor(p[jj], off);
+        }
+        qk += __shfl_xor(qk, off);
       }
-    }
-    __syncthreads();  // s_red reuse (q.k partials consumed by thread 0 above)
-    if (lane < TPR) {
+      if (lane < TPR) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        s_red[wave][0][4 * cq + j] = u[j];
-        s_red[wave][1][4 * cq + j] = p[j];
+        for (int jj = 0; jj < 4; ++jj) {
+          s_red[par][wave][0][4 * cq + jj] = u[jj];
+          s_red[par][wave][1][4 * cq + jj] = p[jj];
+        }
       }
-    }
-    __syncthreads();
-    float d[4];
-    const float qk = s_qk;
+      if (lane == 0) s_qk[par][wave] = qk;
+      __syncthreads();
+      float d[4];
+      float qkt = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = 4 * cq + j;
-      float uu = 0.f, pp = 0.f;
+      for (int w = 0; w < NWV; ++w) qkt += s_qk[par][w];
+      const float bt = s_bt[j];
 #pragma unroll
-      for (int w = 0; w < NWV; ++w) {
-        uu += s_red[w][0][c];
-        pp += s_red[w][1][c];
+      for (int jj = 0; jj < 4; ++jj) {
+        const int c = 4 * cq + jj;
+        float uu = 0.f, pp = 0.f;
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) {
+          uu += s_red[par][w][0][c];
+          pp += s_red[par][w][1][c];
+        }
+        d[jj] = bt * (s_v[j][c] - uu);
+        p[jj] = pp;
       }
-      d[j] = bt * (s_v[c] - uu);
-      p[j] = pp;
-    }
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const float kk = s_k[row_of(i)];
-      s[i].x += kk * d[0]; s[i].y += kk * d[1]; s[i].z += kk * d[2]; s[i].w += kk * d[3];
-    }
-    if (rg == 0) {
+      for (int i = 0; i < RPT; ++i) {
+        const float kk = s_k[j][row_of(i)];
+        s[i].x += kk * d[0]; s[i].y += kk * d[1]; s[i].z += kk * d[2]; s[i].w += kk * d[3];
+      }
+      if (rg == 0) {
+        const size_t row = (b * ntok + t0 + j) * H + h;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) Elem<T>::store(o, row * DV + 4 * cq + j, p[j] + qk * d[j]);
+        for (int jj = 0; jj < 4; ++jj) Elem<T>::store(o, row * DV + 4 * cq + jj, p[jj] + qkt * d[jj]);
+      }
     }
   }
 #pragma unroll
