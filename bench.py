@@ -112,6 +112,34 @@ def stored_traffic(kernel):
     return float(mt.group(1))
 
 
+UTIL_FILES = {  # rocprofv3 MfmaUtil / VALUBusy summaries, per kernel key
+    "chunk_records": os.path.join(ROOT, "profiles", "utilisation_kda_prefill_8k.md"),
+    "chunk_state": os.path.join(ROOT, "profiles", "utilisation_kda_prefill_8k.md"),
+    "decode": os.path.join(ROOT, "profiles", "utilisation_ckda_decode_b256.md"),
+    "bwd_records": os.path.join(ROOT, "profiles", "utilisation_ckda_backward_8k.md"),
+    "bwd_state": os.path.join(ROOT, "profiles", "utilisation_ckda_backward_8k.md"),
+    "bwd_adjoint": os.path.join(ROOT, "profiles", "utilisation_ckda_backward_8k.md"),
+    "bwd_grads": os.path.join(ROOT, "profiles", "utilisation_ckda_backward_8k.md"),
+}
+UTIL_SOURCES = {"bwd_records": ["kda_bwd.hip", "kda_internal.h", "kda_common.h"]}
+for _k in ("bwd_state", "bwd_adjoint", "bwd_grads"):
+    UTIL_SOURCES[_k] = UTIL_SOURCES["bwd_records"]
+
+
+def stored_util(kernel):
+    """rocprofv3 matrix-core and VALU busy percentages of `kernel` ({"mfma_busy_pct",
+    "valu_busy_pct"}), if the counters were taken on the current sources; else None."""
+    path = UTIL_FILES.get(kernel)
+    if not path or not os.path.exists(path):
+        return None
+    files = UTIL_SOURCES.get(kernel) or PMC_FILES[kernel][1]
+    m = re.search(r"^- %s: mfma_busy_pct=([0-9.]+) valu_busy_pct=([0-9.]+) kernel_source_sha256_16=([0-9a-f]+)"
+                  % re.escape(kernel), open(path).read(), re.M)
+    if not m or m.group(3) != kernel_hash(files):
+        return None
+    return {"mfma_busy_pct": float(m.group(1)), "valu_busy_pct": float(m.group(2))}
+
+
 def timed(fn, steps, warmup, stream):
     import torch
     for _ in range(warmup):
@@ -426,6 +454,7 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": stored_traffic(dom),
                      "kernel": dom, "kernel_ms": dom_ms, "algorithmic_bytes_per_launch": dom_bytes,
                      "kernels_ms": res["kernels"],
+                     "rocprof_busy": {k2: stored_util(k2) for k2 in res["kernels"] if k2 in UTIL_FILES},
                      "path": {"algorithmic_bytes_per_step": nbytes, "achieved_gbs": path_gbs,
                               "frac_hbm": path_gbs / HBM_PEAK_GBS,
                               "mfma_tflops_algorithmic": flops / (ms * 1e-3) / 1e12,
@@ -449,7 +478,8 @@ def main():
         out["decode"] = {"workload": "ckda_decode_b256", "B": wd.B, "H": wd.H, "dk": wd.dk, "dv": wd.dv,
                          "steps": wd.decode_steps, "ms_per_step": msd, "value": gbs, "unit": "GB/s",
                          "tokens_per_s": wd.B / (msd * 1e-3), "frac": gbs / HBM_PEAK_GBS,
-                         "bytes_per_step": db, "traffic": stored_traffic("decode")}
+                         "bytes_per_step": db, "traffic": stored_traffic("decode"),
+                         "rocprof_busy": stored_util("decode")}
         log(f"[bench] decode: {msd * 1e3:.1f} us/step, {gbs:.1f} GB/s")
         ws_, mss = bench_decode(3, log, name="sfda_decode_b256")
         gbs_s = db / (mss * 1e-3) / 1e9
@@ -461,7 +491,9 @@ def main():
         out["ckda_backward_8k"] = {"workload": "ckda_prefill_8k", "ms_per_call": msb,
                                    "tokens_per_s": wb.B * wb.T / (msb * 1e-3), "dtype": "f32",
                                    "dense_flops_per_call": flb, "tflops_fp32": flb / (msb * 1e-3) / 1e12,
-                                   "frac_fp32_mfma": flb / (msb * 1e-3) / 1e12 / MFMA_FP32_PEAK_TFLOPS}
+                                   "frac_fp32_mfma": flb / (msb * 1e-3) / 1e12 / MFMA_FP32_PEAK_TFLOPS,
+                                   "rocprof_busy": {k2: stored_util(k2) for k2 in
+                                                    ("bwd_records", "bwd_state", "bwd_adjoint", "bwd_grads")}}
         log(f"[bench] ckda backward 8k: {msb:.3f} ms/call, {flb / (msb * 1e-3) / 1e12:.1f} dense fp32 TFLOP/s")
         wg, msg = bench_backward(max(2, args.steps // 4), 1, log, name="gdn2_prefill_8k")
         out["gdn2_backward_8k"] = {"workload": "gdn2_prefill_8k", "ms_per_call": msg,
