@@ -74,6 +74,8 @@ def load(path: str = _LIB_PATH):
     lib.kda_oracle_bwd.restype = I
     lib.kda_oracle_bwd_gdn2.argtypes = [I, I, I, I, I, I] + [P] * 17 + [I, I]
     lib.kda_oracle_bwd_gdn2.restype = I
+    lib.kda_oracle_bwd_sfda.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, I, I]
+    lib.kda_oracle_bwd_sfda.restype = I
     if path == _LIB_PATH:
         _lib = lib
     return lib
@@ -246,6 +248,17 @@ def bwd(q, k, v, alpha, beta, dO, S0=None, dST=None, heads=None, nthreads=0, lib
     through the token recurrence).  Inputs as fwd; dO [n_sel, T, dv] and dST
     [n_sel, dk, dv] (or None) are widened to fp64.  Returns a dict of fp64 arrays:
     dq, dk, dalpha [n_sel, T, dk]; dv [n_sel, T, dv]; dbeta [n_sel, T]; dS0 [n_sel, dk, dv]."""
+    return _bwd_impl("kda_oracle_bwd", q, k, v, alpha, beta, dO, S0, dST, heads, nthreads, lib)
+
+
+def bwd_sfda(q, k, v, lam, beta, dO, S0=None, dST=None, heads=None, nthreads=0, lib=None):
+    """SFDA backward (SFDA page, "Arquitectura Central": complex rotation-decay gates): as
+    bwd with lam holding (Re, Im) of each key-channel pair's gate in channels (2p, 2p+1);
+    the "dalpha" entry holds d/dRe in channel 2p and d/dIm in channel 2p+1."""
+    return _bwd_impl("kda_oracle_bwd_sfda", q, k, v, lam, beta, dO, S0, dST, heads, nthreads, lib)
+
+
+def _bwd_impl(_entry, q, k, v, alpha, beta, dO, S0, dST, heads, nthreads, lib):
     lib = lib or load()
     arrs = [np.ascontiguousarray(x) for x in (q, k, v, alpha, beta)]
     code = _dtype_code(arrs[0])
@@ -261,9 +274,9 @@ def bwd(q, k, v, alpha, beta, dO, S0=None, dST=None, heads=None, nthreads=0, lib
     dOd = f64(dO, (n_sel, T, dv))
     out = {"dq": np.empty((n_sel, T, dk)), "dk": np.empty((n_sel, T, dk)), "dv": np.empty((n_sel, T, dv)),
            "dalpha": np.empty((n_sel, T, dk)), "dbeta": np.empty((n_sel, T)), "dS0": np.empty((n_sel, dk, dv))}
-    rc = lib.kda_oracle_bwd(B, T, H, dk, dv, code, *[_ptr(a) for a in arrs], _ptr(S0d), _ptr(dOd), _ptr(dSTd),
-                            _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dalpha"]),
-                            _ptr(out["dbeta"]), _ptr(out["dS0"]), _ptr(sel), n_sel, int(nthreads))
+    rc = getattr(lib, _entry)(B, T, H, dk, dv, code, *[_ptr(a) for a in arrs], _ptr(S0d), _ptr(dOd), _ptr(dSTd),
+                              _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dalpha"]),
+                              _ptr(out["dbeta"]), _ptr(out["dS0"]), _ptr(sel), n_sel, int(nthreads))
     if rc != 0:
-        raise RuntimeError("kda_oracle_bwd failed")
+        raise RuntimeError(f"{_entry} failed")
     return out

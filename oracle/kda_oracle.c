@@ -477,8 +477,9 @@ static int bwd_common(int B, int T, int H, int dk, int dv, int dtype,
                       const double* S0, const double* dO, const double* dST,
                       double* dq, double* dk_out, double* dv_out, double* dalpha, double* dbeta,
                       double* derase, double* dwrite,
-                      double* dS0, const int* sel, int n_sel, int nthreads) {
+                      double* dS0, const int* sel, int n_sel, int nthreads, int cpx) {
     const int g2 = erase != NULL;
+    if (cpx && (g2 || dk % 2)) return -1;
     if (B < 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0 || !dO) return -1;
     if (!dq || !dk_out || !dv_out || !dalpha) return -1;
     if (g2 ? (!write || !derase || !dwrite) : !dbeta) return -1;
@@ -526,7 +527,7 @@ static int bwd_common(int B, int T, int H, int dk, int dv, int dtype,
                     for (int j = 0; j < dv; ++j) ww[j] = load_elem(write, dtype, row * dv + j);
                     gdn2_token(S, dk, dv, 0, dv, qq, kk, vv, aa, bb, ww, u, NULL);
                 } else {
-                    kda_token(S, dk, dv, 0, dv, qq, kk, vv, aa, load_elem(beta, dtype, row), u, NULL, 0);
+                    kda_token(S, dk, dv, 0, dv, qq, kk, vv, aa, load_elem(beta, dtype, row), u, NULL, cpx);
                 }
             }
             /* backward sweep */
@@ -550,7 +551,7 @@ static int bwd_common(int B, int T, int H, int dk, int dv, int dtype,
                         for (int j = 0; j < dv; ++j) ww[j] = load_elem(write, dtype, row * dv + j);
                         gdn2_token(nx, dk, dv, 0, dv, qq, kk, vv, aa, bb, ww, u, NULL);
                     } else {
-                        kda_token(nx, dk, dv, 0, dv, qq, kk, vv, aa, load_elem(beta, dtype, row), u, NULL, 0);
+                        kda_token(nx, dk, dv, 0, dv, qq, kk, vv, aa, load_elem(beta, dtype, row), u, NULL, cpx);
                     }
                 }
                 for (int t = t1 - 1; t >= t0; --t) {
@@ -623,9 +624,23 @@ static int bwd_common(int B, int T, int H, int dk, int dv, int dtype,
                         continue;
                     }
                     const double bt = load_elem(beta, dtype, row);
-                    /* recompute S' = Diag(alpha) S_prev, u = S'^T k, delta = v - u */
-                    for (int i = 0; i < dk; ++i)
-                        for (int j = 0; j < dv; ++j) Sp[(size_t)i * dv + j] = aa[i] * Sprev[(size_t)i * dv + j];
+                    /* recompute S' = Diag(alpha) S_prev (SFDA: rows 2p, 2p+1 of every column,
+                     * one complex coordinate, times the complex gate aa[2p] + i aa[2p+1]),
+                     * u = S'^T k, delta = v - u */
+                    if (cpx) {
+                        for (int pp = 0; pp < dk / 2; ++pp) {
+                            const double lr = aa[2 * pp], li = aa[2 * pp + 1];
+                            const double *x0 = Sprev + (size_t)(2 * pp) * dv, *x1 = x0 + dv;
+                            double *y0 = Sp + (size_t)(2 * pp) * dv, *y1 = y0 + dv;
+                            for (int j = 0; j < dv; ++j) {
+                                y0[j] = lr * x0[j] - li * x1[j];
+                                y1[j] = li * x0[j] + lr * x1[j];
+                            }
+                        }
+                    } else {
+                        for (int i = 0; i < dk; ++i)
+                            for (int j = 0; j < dv; ++j) Sp[(size_t)i * dv + j] = aa[i] * Sprev[(size_t)i * dv + j];
+                    }
                     for (int j = 0; j < dv; ++j) u[j] = 0.0;
                     for (int i = 0; i < dk; ++i)
                         for (int j = 0; j < dv; ++j) u[j] += kk[i] * Sp[(size_t)i * dv + j];
@@ -662,8 +677,31 @@ static int bwd_common(int B, int T, int H, int dk, int dv, int dtype,
                         }
                         dkt[i] = bt * a - c;
                     }
-                    /* dS' = G - k ddelta^T ; dalpha = rowsum(dS' o S_prev) ; G <- Diag(alpha) dS' */
                     double* dat = dalpha + ((size_t)s * T + t) * dk;
+                    if (cpx) {
+                        /* dS' = G - k ddelta^T, pair by pair.  S'_0 = lr S_0 - li S_1 and
+                         * S'_1 = li S_0 + lr S_1 give dlr = sum_j (g_0 S_0 + g_1 S_1) and
+                         * dli = sum_j (g_1 S_0 - g_0 S_1); G <- Lambda^T dS' is
+                         * G_0 = lr g_0 + li g_1, G_1 = lr g_1 - li g_0. */
+                        for (int pp = 0; pp < dk / 2; ++pp) {
+                            const int i0 = 2 * pp, i1 = 2 * pp + 1;
+                            const double lr = aa[i0], li = aa[i1];
+                            double dre = 0.0, dim = 0.0;
+                            for (int j = 0; j < dv; ++j) {
+                                const double g0 = G[(size_t)i0 * dv + j] - kk[i0] * dd[j];
+                                const double g1 = G[(size_t)i1 * dv + j] - kk[i1] * dd[j];
+                                const double s0 = Sprev[(size_t)i0 * dv + j], s1 = Sprev[(size_t)i1 * dv + j];
+                                dre += g0 * s0 + g1 * s1;
+                                dim += g1 * s0 - g0 * s1;
+                                G[(size_t)i0 * dv + j] = lr * g0 + li * g1;
+                                G[(size_t)i1 * dv + j] = lr * g1 - li * g0;
+                            }
+                            dat[i0] = dre;
+                            dat[i1] = dim;
+                        }
+                        continue;
+                    }
+                    /* dS' = G - k ddelta^T ; dalpha = rowsum(dS' o S_prev) ; G <- Diag(alpha) dS' */
                     for (int i = 0; i < dk; ++i) {
                         double a = 0.0;
                         for (int j = 0; j < dv; ++j) {
@@ -696,7 +734,7 @@ int kda_oracle_bwd(int B, int T, int H, int dk, int dv, int dtype,
                    double* dS0, const int* sel, int n_sel, int nthreads) {
     if (!beta) return -1;
     return bwd_common(B, T, H, dk, dv, dtype, q, k, v, alpha, beta, NULL, NULL, S0, dO, dST, dq, dk_out, dv_out,
-                      dalpha, dbeta, NULL, NULL, dS0, sel, n_sel, nthreads);
+                      dalpha, dbeta, NULL, NULL, dS0, sel, n_sel, nthreads, 0);
 }
 
 /* Gated DeltaNet-2 backward: the same reverse sweep through gdn2_token (erase gate b per
@@ -712,5 +750,23 @@ int kda_oracle_bwd_gdn2(int B, int T, int H, int dk, int dv, int dtype,
                         const int* sel, int n_sel, int nthreads) {
     if (!erase || !write) return -1;
     return bwd_common(B, T, H, dk, dv, dtype, q, k, v, alpha, NULL, erase, write, S0, dO, dST, dq, dk_out, dv_out,
-                      dalpha, NULL, derase, dwrite, dS0, sel, n_sel, nthreads);
+                      dalpha, NULL, derase, dwrite, dS0, sel, n_sel, nthreads, 0);
+}
+
+/* SFDA backward: the reverse sweep with the rotation-decay step of kda_oracle_fwd_sfda.
+ * lambda [B, T, H, dk] holds the complex gates (real part in channel 2p, imaginary part in
+ * channel 2p+1); dlambda [n_sel, T, dk] returns d/dRe in channel 2p and d/dIm in channel
+ * 2p+1.  Per token, for coordinate p with S' = Lambda S_prev and dS' = G - k ddelta^T:
+ * dRe = sum over columns of (dS'_2p S_prev,2p + dS'_2p+1 S_prev,2p+1), dIm = sum of
+ * (dS'_2p+1 S_prev,2p - dS'_2p S_prev,2p+1), and G <- Lambda^T dS'.  dk must be even;
+ * other arguments as kda_oracle_bwd. */
+int kda_oracle_bwd_sfda(int B, int T, int H, int dk, int dv, int dtype,
+                        const void* q, const void* k, const void* v,
+                        const void* lambda, const void* beta, const double* S0,
+                        const double* dO, const double* dST,
+                        double* dq, double* dk_out, double* dv_out, double* dlambda, double* dbeta,
+                        double* dS0, const int* sel, int n_sel, int nthreads) {
+    if (!beta) return -1;
+    return bwd_common(B, T, H, dk, dv, dtype, q, k, v, lambda, beta, NULL, NULL, S0, dO, dST, dq, dk_out, dv_out,
+                      dlambda, dbeta, NULL, NULL, dS0, sel, n_sel, nthreads, 1);
 }

@@ -323,3 +323,51 @@ def test_gdn2_bwd_mutant_is_caught(name, src_text, monkeypatch, tmp_path):
     assert src_text.count(old) == 1, f"mutation anchor for {name} not unique"
     lib = _build_variant(src_text.replace(old, new), str(tmp_path), name)
     assert _caught_bwd_gdn2(lib, monkeypatch), f"mutant {name} passed every GDN-2 backward pin"
+
+
+# ---- SFDA backward: planted mistakes in the complex-gate branch of the reverse sweep
+MUTANTS_BWD_SFDA = {
+    "sfda_bwd_dim_sign": ("dim += g1 * s0 - g0 * s1;", "dim += g0 * s1 - g1 * s0;"),
+    "sfda_bwd_dre_drops_odd_row": ("dre += g0 * s0 + g1 * s1;", "dre += g0 * s0;"),
+    "sfda_bwd_adjoint_not_transposed": ("G[(size_t)i0 * dv + j] = lr * g0 + li * g1;",
+                                        "G[(size_t)i0 * dv + j] = lr * g0 - li * g1;"),
+    "sfda_bwd_recompute_real_part_only": ("y0[j] = lr * x0[j] - li * x1[j];", "y0[j] = lr * x0[j];"),
+    "sfda_bwd_block_rebuild_real_gates": (
+        "kda_token(nx, dk, dv, 0, dv, qq, kk, vv, aa, load_elem(beta, dtype, row), u, NULL, cpx);",
+        "kda_token(nx, dk, dv, 0, dv, qq, kk, vv, aa, load_elem(beta, dtype, row), u, NULL, 0);"),
+}
+
+PIN_TESTS_BWD_SFDA = [
+    ("secants_short", lambda: bpins.test_sfda_bwd_exact_secants(5)),
+    ("secants_blocks", lambda: bpins.test_sfda_bwd_exact_secants(150)),
+    ("key_fd", lambda: bpins.test_sfda_bwd_key_central_differences()),
+    ("closed_form", lambda: bpins.test_sfda_bwd_pure_rotation_closed_form()),
+]
+
+
+def _caught_bwd_sfda(lib, monkeypatch):
+    """The forward stays the clean library (the pins measure the backward against it)."""
+    failed = []
+    with monkeypatch.context() as m:
+        real = oracle.bwd_sfda
+        m.setattr(oracle, "bwd_sfda", lambda *a, **kw: real(*a, lib=lib, **kw))
+        for name, fn in PIN_TESTS_BWD_SFDA:
+            try:
+                with np.errstate(all="ignore"):
+                    fn()
+            except AssertionError:
+                failed.append(name)
+    return failed
+
+
+def test_unmodified_source_passes_sfda_bwd_pins(src_text, monkeypatch, tmp_path):
+    lib = _build_variant(src_text, str(tmp_path), "clean_bwd_sfda")
+    assert _caught_bwd_sfda(lib, monkeypatch) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS_BWD_SFDA))
+def test_sfda_bwd_mutant_is_caught(name, src_text, monkeypatch, tmp_path):
+    old, new = MUTANTS_BWD_SFDA[name]
+    assert src_text.count(old) == 1, f"mutation anchor for {name} not unique"
+    lib = _build_variant(src_text.replace(old, new), str(tmp_path), name)
+    assert _caught_bwd_sfda(lib, monkeypatch), f"mutant {name} passed every SFDA backward pin"
