@@ -534,3 +534,221 @@ def chunk_backward_gdn2(q, k, v, a, erase, write, dO, S0=None, dST=None, C=64, b
         dSn = dS
     out["dS0"] = dSn
     return out
+
+
+# ---- SFDA (complex rotation-decay gates on key-channel pairs) --------------------------
+# A real d_k-vector x is read as P = d_k / 2 complex numbers x_p = x_2p + i x_2p+1, the
+# state's rows 2p, 2p+1 as one complex row, and the gate of pair p as lam_p, so that the
+# decay is z <- lam z.  Real dot products over channels are sums of Re(conj(x_p) y_p).  For
+# a product y = x c of complex numbers, the gradient (dL/dRe + i dL/dIm) passes as
+# g_x = g_y conj(c); the gate gradient is therefore the conjugate of the real formula's
+# exclusive-product sum, with complex weights.
+
+def cx(x):
+    """[.., 2P] real pairs -> [.., P] complex."""
+    return x[..., 0::2] + 1j * x[..., 1::2]
+
+
+def pairs(z):
+    """[.., P] complex -> [.., 2P] real pairs."""
+    out = np.empty(z.shape[:-1] + (2 * z.shape[-1],))
+    out[..., 0::2], out[..., 1::2] = z.real, z.imag
+    return out
+
+
+def _rot_rows(g, S):
+    """Rows (2p, 2p+1) of S times the complex g_p (g [P], S [2P, dv])."""
+    Z = g[:, None] * (S[0::2] + 1j * S[1::2])
+    out = np.empty_like(S)
+    out[0::2], out[1::2] = Z.real, Z.imag
+    return out
+
+
+def _ranges_cpx(lam):
+    C, P = lam.shape
+    r = np.zeros((C, C, P), complex)
+    for j in range(C):
+        run = np.ones(P, complex)
+        r[j, j] = 1.0
+        for i in range(j + 1, C):
+            run = run * lam[i]
+            r[i, j] = run
+    return r
+
+
+def blocked_decay_grads_cpx(dA, dD, q, k, lam, av, bv, dgl):
+    """Complex form of blocked_decay_grads (q, k, lam, av, bv [C, P] complex; dgl [P]):
+    the same block anchoring, with conj(r) on the key side (Zc and its fold term F) and
+    conj(q), conj(k) in the pair weights.  Returns Zq, Zr, Zc and the gate gradient as
+    dL/dRe + i dL/dIm per pair."""
+    C, P = q.shape
+    NB = C // SUB
+    pin, sig, pib = np.zeros((C, P), complex), np.zeros((C, P), complex), np.zeros((NB, P), complex)
+    for I in range(NB):
+        p = np.ones(P, complex)
+        for r in range(SUB):
+            p = p * lam[I * SUB + r]
+            pin[I * SUB + r] = p
+        pib[I] = p
+        sf = np.ones(P, complex)
+        for r in range(SUB - 1, -1, -1):
+            sig[I * SUB + r] = sf
+            sf = sf * lam[I * SUB + r]
+
+    def between(J, I):
+        p = np.ones(P, complex)
+        for y in range(J + 1, I):
+            p = p * pib[y]
+        return p
+
+    PA, PD, F = np.zeros((NB, C, P), complex), np.zeros((NB, C, P), complex), np.zeros((C, P), complex)
+    for M in range(1, NB):
+        s = M * SUB
+        khat = np.stack([k[j] * sig[j] * between(j // SUB, M) for j in range(s)])
+        PA[M, s:] = dA[s:, :s] @ khat
+        PD[M, s:] = dD[s:, :s] @ khat
+    for M in range(NB - 1):
+        s, e1 = M * SUB, M * SUB + SUB
+        rie = np.conj(np.stack([pin[i] * between(M, i // SUB) for i in range(e1, C)]))
+        F[s:e1] = dA[e1:, s:e1].T @ (q[e1:] * rie) + dD[e1:, s:e1].T @ (k[e1:] * rie)
+
+    Zq, Zr, Zc = np.zeros((C, P), complex), np.zeros((C, P), complex), np.zeros((C, P), complex)
+    dal = np.zeros((C, P), complex)
+    for M in range(NB):
+        s = M * SUB
+        al, qv, kv = lam[s:s + SUB], q[s:s + SUB], k[s:s + SUB]
+        gs = np.prod(pib[:M], axis=0) if M > 0 else np.ones(P, complex)
+        rend = np.prod(pib[M + 1:], axis=0) if M < NB - 1 else np.ones(P, complex)
+        for r in range(SUB):
+            i = s + r
+            zq, zr, Pr = dA[i, i] * kv[r], np.zeros(P, complex), np.ones(P, complex)
+            for rj in range(r - 1, -1, -1):
+                Pr = Pr * al[rj + 1]
+                zq = zq + dA[i, s + rj] * kv[rj] * Pr
+                zr = zr + dD[i, s + rj] * kv[rj] * Pr
+            if M > 0:
+                zq = zq + pin[i] * PA[M, i]
+                zr = zr + pin[i] * PD[M, i]
+            zc, Pr = dA[i, i] * qv[r], np.ones(P, complex)
+            for ri in range(r + 1, SUB):
+                Pr = Pr * al[ri]
+                zc = zc + (dA[s + ri, i] * qv[ri] + dD[s + ri, i] * kv[ri]) * np.conj(Pr)
+            if M < NB - 1:
+                zc = zc + np.conj(sig[i]) * F[i]
+            Zq[i], Zr[i], Zc[i] = zq, zr, zc
+        bvs = sum((bv[j] * sig[j] * between(j // SUB, M) for j in range(s)), np.zeros(P, complex))
+
+        def g_at(i):
+            g = av[i] * gs
+            if M > 0:
+                g = g + np.conj(q[i]) * PA[M, i] + np.conj(k[i]) * PD[M, i]
+            if i == C - 1:
+                g = g + bvs + dgl * gs
+            return g
+
+        u = [g_at(s + r) for r in range(SUB)]
+        if M < NB - 1:
+            xf = np.zeros(P, complex)
+            for i in range(C - 1, s + SUB - 1, -1):
+                xf = lam[i] * (g_at(i) + xf)
+            u[SUB - 1] = u[SUB - 1] + xf
+            f = [kv[r] * np.conj(F[s + r]) + bv[s + r] * rend for r in range(SUB)]
+        else:
+            f = [bv[s + r] for r in range(SUB)]
+        for m in range(SUB):
+            acc = u[SUB - 1]
+            for i in range(SUB - 2, m - 1, -1):
+                acc = u[i] + al[i + 1] * acc
+            dal[s + m] = acc
+            for i in range(m + 1, SUB):
+                E = (np.conj(qv[i]) * dA[s + i, s + m] + np.conj(kv[i]) * dD[s + i, s + m]) * kv[m]
+                if i == SUB - 1:
+                    E = E + f[m]
+                u[i] = al[m] * u[i] + E
+    return Zq, Zr, Zc, np.conj(dal)
+
+
+def chunk_backward_sfda(q, k, v, lam, beta, dO, S0=None, dST=None, C=64, blocked=False):
+    """SFDA gradients for one head through the chunk algebra (fp64).  lam [T, dk] holds
+    (Re, Im) of each pair's gate.  Per chunk, with complex ranges r_ij = prod_{j<l<=i} lam_l,
+    gamma_i = r_(i,-1), rho_j = r_(C-1,j): Q~ = q conj(gamma), K~g = k conj(gamma),
+    K~r = rho k (pairs), A_ij = sum_p Re(conj(q_ip) r_ijp k_jp), D likewise with k_i, and the
+    chunk-end decay multiplies the state's row pairs by gamma_last.  Returns dq, dk, dv,
+    dalpha (d/dRe, d/dIm in channels 2p, 2p+1), dbeta, dS0.  blocked: decayed sums and
+    gate gradient from blocked_decay_grads_cpx."""
+    T, dk = q.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if S0 is None else np.asarray(S0, np.float64).copy()
+    low, slow = np.tril(np.ones((C, C))), np.tril(np.ones((C, C)), -1)
+    parts = []
+    for c0 in range(0, T, C):
+        n = min(C, T - c0)
+        pad = lambda x, fill: np.concatenate([x[c0:c0 + n], np.full((C - n,) + x.shape[1:], fill)])[:C]
+        qc, kc, vc, bc, dOc = pad(q, 0.0), pad(k, 0.0), pad(v, 0.0), pad(beta, 0.0), pad(dO, 0.0)
+        lc = np.concatenate([cx(lam[c0:c0 + n]), np.ones((C - n, dk // 2), complex)])
+        qh, kh = cx(qc), cx(kc)
+        r = _ranges_cpx(lc)
+        gam = np.cumprod(lc, axis=0)
+        rho, gL = r[C - 1], gam[C - 1]
+        A = np.einsum("ip,ijp,jp->ij", np.conj(qh), r, kh).real * low
+        D = np.einsum("ip,ijp,jp->ij", np.conj(kh), r, kh).real * slow
+        M = np.linalg.inv(np.eye(C) + bc[:, None] * D)
+        Mt = M * bc[None, :]
+        Qg, Kg, Kr = pairs(qh * np.conj(gam)), pairs(kh * np.conj(gam)), pairs(rho * kh)
+        W = Mt @ Kg
+        Dl = Mt @ vc - W @ S
+        Sn = _rot_rows(gL, S) + Kr.T @ Dl
+        parts.append(dict(S=S, q=qh, k=kh, v=vc, lam=lc, beta=bc, dO=dOc, r=r, gam=gam, rho=rho, gL=gL, A=A,
+                          D=D, M=M, Mt=Mt, Qg=Qg, Kg=Kg, Kr=Kr, W=W, Dl=Dl, c0=c0, n=n))
+        S = Sn
+    out = {x: np.zeros((T, dk)) for x in ("dq", "dk", "dalpha")}
+    out["dv"], out["dbeta"] = np.zeros((T, dv)), np.zeros(T)
+    dSn = np.zeros((dk, dv)) if dST is None else np.asarray(dST, np.float64).copy()
+    for p in reversed(parts):
+        S, dO_, qh, kh, lc = p["S"], p["dO"], p["q"], p["k"], p["lam"]
+        r, gam, rho, gL = p["r"], p["gam"], p["rho"], p["gL"]
+        dDl = p["Kr"] @ dSn + p["A"].T @ dO_
+        dS = _rot_rows(np.conj(gL), dSn) + p["Qg"].T @ dO_ - p["W"].T @ dDl
+        dQg, dKr, dW = dO_ @ S.T, p["Dl"] @ dSn.T, -dDl @ S.T
+        dA = (dO_ @ p["Dl"].T) * low
+        dV = p["Mt"].T @ dDl
+        dMt = (dDl @ p["v"].T + dW @ p["Kg"].T) * low
+        dKg = p["Mt"].T @ dW
+        dbeta = (dMt * p["M"]).sum(axis=0)
+        dT = -(p["M"].T @ (dMt * p["beta"][None, :]) @ p["M"].T) * slow
+        dbeta = dbeta + (dT * p["D"]).sum(axis=1)
+        dD = p["beta"][:, None] * dT
+        dQh, dKgh, dKrh = cx(dQg), cx(dKg), cx(dKr)
+        av = dQh * np.conj(qh) + dKgh * np.conj(kh)
+        bv = np.conj(dKrh) * kh
+        dgl = (np.conj(cx(dSn.T)) * cx(S.T)).sum(axis=0)            # sum_j conj(dS'_j) S_j
+        if blocked:
+            Zq, Zr, Zc, dlam = blocked_decay_grads_cpx(dA, dD, qh, kh, lc, av, bv, dgl)
+        else:
+            Zq = np.einsum("ij,ijp,jp->ip", dA, r, kh)
+            Zr = np.einsum("ij,ijp,jp->ip", dD, r, kh)
+            Zc = np.einsum("ij,ijp,ip->jp", dA, np.conj(r), qh) + np.einsum("ij,ijp,ip->jp", dD, np.conj(r), kh)
+            E = np.einsum("ij,ip,jp->ijp", dA, np.conj(qh), kh) + np.einsum("ij,ip,jp->ijp", dD, np.conj(kh), kh)
+            dlam = np.zeros((C, dk // 2), complex)
+            for m in range(C):
+                gm1 = np.prod(lc[:m], axis=0)                                         # gamma_(m-1)
+                left = np.stack([np.prod(lc[j + 1:m], axis=0) for j in range(m)]) if m else None
+                tot = np.zeros(dk // 2, complex)
+                for i in range(m, C):
+                    right = np.prod(lc[m + 1:i + 1], axis=0)                           # r_(i, m)
+                    inner = av[i] * gm1 + ((E[i, :m] * left).sum(axis=0) if m else 0.0)
+                    tot = tot + right * inner
+                tail = dgl * gm1 + ((bv[:m] * left).sum(axis=0) if m else 0.0)
+                tot = tot + np.prod(lc[m + 1:], axis=0) * tail
+                dlam[m] = np.conj(tot)
+        dq = pairs(dQh * gam + Zq)
+        dk_ = pairs(dKgh * gam + dKrh * np.conj(rho) + Zr + Zc)
+        n, c0 = p["n"], p["c0"]
+        out["dq"][c0:c0 + n] = dq[:n]
+        out["dk"][c0:c0 + n] = dk_[:n]
+        out["dv"][c0:c0 + n] = dV[:n]
+        out["dalpha"][c0:c0 + n] = pairs(dlam)[:n]
+        out["dbeta"][c0:c0 + n] = dbeta[:n]
+        dSn = dS
+    out["dS0"] = dSn
+    return out

@@ -155,3 +155,30 @@ def test_gdn2_chunk_backward_matches_oracle(T, dk, dv, blocked):
     for key in ("dq", "dk", "dv", "dalpha", "derase", "dwrite", "dS0"):
         y = r[key][0]
         assert np.abs(g[key] - y).max() <= 1e-10 * max(1.0, np.abs(y).max()), key
+
+
+@pytest.mark.parametrize("T,dk,dv,blocked", [(100, 8, 4, False), (130, 8, 4, True), (64, 4, 3, True)])
+def test_sfda_chunk_backward_matches_oracle(T, dk, dv, blocked):
+    """The SFDA chunk backward in complex pair arithmetic, directly and in the GPU kernel's
+    blocked decomposition (conj(r) on the key side, conjugated pair weights), equals the
+    oracle's SFDA backward; gates include an exact zero and quarter and half turns."""
+    import oracle
+    rng = np.random.default_rng(11 * T + dk)
+    q = rng.standard_normal((T, dk))
+    k = rng.standard_normal((T, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    v = rng.standard_normal((T, dv))
+    mag, th = rng.uniform(0.0, 1.0, (T, dk // 2)), rng.uniform(-np.pi, np.pi, (T, dk // 2))
+    lam = np.empty((T, dk))
+    lam[:, 0::2], lam[:, 1::2] = mag * np.cos(th), mag * np.sin(th)
+    lam[3, 0:2], lam[20, 2:4], lam[40, 0:2] = (0.0, 0.0), (0.0, 1.0), (-1.0, 0.0)
+    b = rng.uniform(0.0, 2.0, T)
+    S0 = rng.standard_normal((dk, dv))
+    dO = rng.standard_normal((T, dv))
+    dST = rng.standard_normal((dk, dv))
+    g = cm.chunk_backward_sfda(q, k, v, lam, b, dO, S0, dST, C=64, blocked=blocked)
+    r = oracle.bwd_sfda(q[None, :, None], k[None, :, None], v[None, :, None], lam[None, :, None], b[None, :, None],
+                        dO[None], S0=S0[None], dST=dST[None])
+    for key in ("dq", "dk", "dv", "dalpha", "dbeta", "dS0"):
+        y = r[key][0]
+        assert np.abs(g[key] - y).max() <= 1e-10 * max(1.0, np.abs(y).max()), key
