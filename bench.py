@@ -243,7 +243,7 @@ def bwd_flops(B, T, H, dk, dv, C=64):
 
 
 def bench_backward(steps, warmup, log, name="ckda_prefill_8k"):
-    """Times kda_chunk_bwd (kda_gdn2_chunk_bwd for a GDN-2 workload) on workload `name`
+    """Times kda_chunk_bwd (kda_gdn2_chunk_bwd, kda_sfda_chunk_bwd for those gates) on workload `name`
     (start state and a final-state gradient given).  Returns (workload, ms per call)."""
     import torch
     import gated_delta_rule_78_amd as kda
@@ -262,6 +262,8 @@ def bench_backward(steps, warmup, log, name="ckda_prefill_8k"):
         up = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to("cuda").view(torch.bfloat16)
         e, g = up(inp.erase), up(inp.write)
         call = lambda: kda.gdn2_chunk_bwd(q, k, v, a, e, g, d_o, initial_state=s0, d_final_state=dst, workspace=ws)
+    elif w.gates == "sfda":
+        call = lambda: kda.sfda_chunk_bwd(q, k, v, a, b, d_o, initial_state=s0, d_final_state=dst, workspace=ws)
     else:
         call = lambda: kda.chunk_bwd(q, k, v, a, b, d_o, initial_state=s0, d_final_state=dst, workspace=ws)
     ms = timed(call, steps, warmup, stream)
@@ -383,7 +385,7 @@ def main():
                     help="only the decode measurement (for profiling the decode kernel)")
     ap.add_argument("--bwd-only", action="store_true",
                     help="only the backward measurement (for profiling the backward kernels)")
-    ap.add_argument("--bwd-workload", default="ckda_prefill_8k", choices=("ckda_prefill_8k", "gdn2_prefill_8k"),
+    ap.add_argument("--bwd-workload", default="ckda_prefill_8k", choices=("ckda_prefill_8k", "gdn2_prefill_8k", "sfda_prefill_8k"),
                     help="workload of --bwd-only")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -499,6 +501,10 @@ def main():
         out["gdn2_backward_8k"] = {"workload": "gdn2_prefill_8k", "ms_per_call": msg,
                                    "tokens_per_s": wg.B * wg.T / (msg * 1e-3), "dtype": "f32"}
         log(f"[bench] gdn2 backward 8k: {msg:.3f} ms/call")
+        wsf, mss_ = bench_backward(max(2, args.steps // 4), 1, log, name="sfda_prefill_8k")
+        out["sfda_backward_8k"] = {"workload": "sfda_prefill_8k", "ms_per_call": mss_,
+                                   "tokens_per_s": wsf.B * wsf.T / (mss_ * 1e-3), "dtype": "f32"}
+        log(f"[bench] sfda backward 8k: {mss_:.3f} ms/call")
         wt, mst, ntk = bench_decode_tokens(4, log)
         bt_ = decode_bytes(wt.B, wt.H, wt.dk, wt.dv, tokens=ntk)
         out["decode_tokens"] = {"workload": "ckda_decode_b256", "tokens_per_call": ntk, "ms_per_call": mst,

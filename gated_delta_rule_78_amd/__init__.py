@@ -98,6 +98,11 @@ def lib() -> ctypes.CDLL:
         L.kda_gdn2_chunk_bwd.restype = ctypes.c_int
         L.kda_gdn2_chunk_bwd_varlen.argtypes = [SP, P, ctypes.c_int] + [P] * 17 + [ctypes.c_size_t, P]
         L.kda_gdn2_chunk_bwd_varlen.restype = ctypes.c_int
+        L.kda_sfda_chunk_bwd.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.kda_sfda_chunk_bwd.restype = ctypes.c_int
+        L.kda_sfda_chunk_bwd_varlen.argtypes = [SP, P, ctypes.c_int, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                                ctypes.c_size_t, P]
+        L.kda_sfda_chunk_bwd_varlen.restype = ctypes.c_int
         L.kda_status_string.argtypes = [ctypes.c_int]
         L.kda_status_string.restype = ctypes.c_char_p
         L.kda_version.argtypes = []
@@ -518,9 +523,11 @@ def bwd_workspace_size(B, T, H, dk, dv, dtype="bf16") -> int:
     return int(lib().kda_chunk_bwd_workspace_size(ctypes.byref(shape)))
 
 
-def _bwd_call(q, k, v, alpha, gates, d_o, cu_seqlens, initial_state, d_final_state, want_d_initial, workspace):
-    """Shared marshalling of the four backward entry points; gates = (beta,) for KDA / CKDA
-    or (erase, write) for Gated DeltaNet-2.  Returns the C call's output tensors."""
+def _bwd_call(q, k, v, alpha, gates, d_o, cu_seqlens, initial_state, d_final_state, want_d_initial, workspace,
+              family="kda"):
+    """Shared marshalling of the backward entry points; gates = (beta,) for KDA / CKDA and
+    SFDA (family "sfda": complex gates in alpha) or (erase, write) for Gated DeltaNet-2.
+    Returns the C call's output tensors."""
     torch = _torch()
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -567,7 +574,10 @@ def _bwd_call(q, k, v, alpha, gates, d_o, cu_seqlens, initial_state, d_final_sta
     head = [ctypes.byref(shape)] + ([_ptr(cu_seqlens), n_states] if packed else [])
     ins = [_ptr(q), _ptr(k), _ptr(v), _ptr(alpha)] + [_ptr(x) for x in gates]
     outs = [_ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dal)] + [_ptr(x) for x in dgates]
-    entry = ("kda_gdn2_chunk_bwd" if g2 else "kda_chunk_bwd") + ("_varlen" if packed else "")
+    if family == "sfda" and dk % 2:
+        raise ValueError("SFDA gates pair the key channels: dk must be even")
+    entry = ("kda_gdn2_chunk_bwd" if g2 else ("kda_sfda_chunk_bwd" if family == "sfda" else "kda_chunk_bwd")) + (
+        "_varlen" if packed else "")
     rc = getattr(lib(), entry)(*head, *ins, _ptr(initial_state), _ptr(d_o), _ptr(d_final_state), *outs, _ptr(ds0),
                                _ptr(workspace), nbytes, _stream(dev))
     if rc != 0:
@@ -603,3 +613,13 @@ def gdn2_chunk_bwd(q, k, v, alpha, erase, write, d_o, initial_state=None, d_fina
     dk, dv, dalpha, d_erase, d_write, d_initial_state or None), all fp32."""
     return _bwd_call(q, k, v, alpha, (erase, write), d_o, cu_seqlens, initial_state, d_final_state, want_d_initial,
                      workspace)
+
+
+def sfda_chunk_bwd(q, k, v, lam, beta, d_o, initial_state=None, d_final_state=None, want_d_initial=True,
+                   workspace=None, cu_seqlens=None):
+    """SFDA backward of sfda_chunk_fwd (or, with cu_seqlens, of its packed form): lam
+    [B,T,H,dk] holds (Re, Im) of each key-channel pair's gate.  Returns (dq, dk, dv, dlam,
+    dbeta, d_initial_state or None), all fp32; dlam holds d/dRe and d/dIm in the pair's
+    channels."""
+    return _bwd_call(q, k, v, lam, (beta,), d_o, cu_seqlens, initial_state, d_final_state, want_d_initial,
+                     workspace, family="sfda")

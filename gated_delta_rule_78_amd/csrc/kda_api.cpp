@@ -232,6 +232,8 @@ struct BwdPtrs {
   const void* write = nullptr;
   float* derase = nullptr;
   float* dwrite = nullptr;
+  // SFDA: alpha / dalpha hold complex gates and their gradients, (Re, Im) per channel pair
+  bool cpx = false;
 };
 
 // Workspace of a packed batch's backward: chunk blocks [H][gmax], then the chunk table
@@ -312,6 +314,10 @@ int bwd_impl(const kda_shape* shape, const int* cu, int n_seqs, const BwdPtrs& p
     a.write = p.write;
     a.derase = p.derase;
     a.dwrite = p.dwrite;
+  }
+  if (p.cpx) {
+    if (g2) return KDA_ERR_UNSUPPORTED;
+    a.cpx = true;
   }
   if (packed) {
     if (n_seqs == 0) return KDA_OK;
@@ -621,6 +627,30 @@ int kda_gdn2_chunk_bwd_varlen(const kda_shape* shape, const int* cu_seqlens, int
   if (!erase_gate || !write_gate || !d_erase || !d_write) {
     if ((int64_t)shape->T * shape->H > 0) return KDA_ERR_NULL;
   }
+  return bwd_impl(shape, cu_seqlens, n_seqs, p, stream);
+}
+
+int kda_sfda_chunk_bwd(const kda_shape* shape, const void* q, const void* k, const void* v, const void* lambda,
+                       const void* beta, const float* initial_state, const void* d_o, const float* d_final_state,
+                       float* dq, float* dk, float* dv, float* dlambda, float* dbeta, float* d_initial_state,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  BwdPtrs p{q, k, v, lambda, beta, initial_state, d_o, d_final_state, dq, dk, dv, dlambda, dbeta, d_initial_state,
+            workspace, workspace_bytes};
+  p.cpx = true;
+  return bwd_impl(shape, nullptr, -1, p, stream);
+}
+
+int kda_sfda_chunk_bwd_varlen(const kda_shape* shape, const int* cu_seqlens, int n_seqs, const void* q,
+                              const void* k, const void* v, const void* lambda, const void* beta,
+                              const float* initial_state, const void* d_o, const float* d_final_state, float* dq,
+                              float* dk, float* dv, float* dlambda, float* dbeta, float* d_initial_state,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!shape) return KDA_ERR_NULL;
+  if (n_seqs < 0) return KDA_ERR_SHAPE;
+  if (!cu_seqlens) return KDA_ERR_NULL;
+  BwdPtrs p{q, k, v, lambda, beta, initial_state, d_o, d_final_state, dq, dk, dv, dlambda, dbeta, d_initial_state,
+            workspace, workspace_bytes};
+  p.cpx = true;
   return bwd_impl(shape, cu_seqlens, n_seqs, p, stream);
 }
 

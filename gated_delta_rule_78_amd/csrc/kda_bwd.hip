@@ -187,7 +187,93 @@ __device__ __forceinline__ void mfma4(f32x4_t& acc, const float (&av)[4], const 
   for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[t], bv[t], acc, 0, 0, 0);
 #endif
 }
+
+// SFDA complex gates: key channels 2p, 2p+1 hold one complex coordinate (x = channel 2p,
+// y = channel 2p+1); the gate of coordinate p multiplies it.  A real dot product over the
+// channels is sum_p Re(conj(a_p) b_p), so the anchored operands of a decayed product carry
+// conj() of the factor on the row side.
+struct cf {
+  float x, y;
+};
+__device__ __forceinline__ cf cmul(cf a, cf b) { return {a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x}; }
+__device__ __forceinline__ cf cmulc(cf a, cf b) { return {a.x * b.x + a.y * b.y, a.y * b.x - a.x * b.y}; }  // a conj(b)
+__device__ __forceinline__ cf cadd(cf a, cf b) { return {a.x + b.x, a.y + b.y}; }
+__device__ __forceinline__ cf cscale(cf a, float s) { return {a.x * s, a.y * s}; }
+__device__ __forceinline__ cf cconj(cf a) { return {a.x, -a.y}; }
+__device__ __forceinline__ float comp(cf a, int e) { return e ? a.y : a.x; }
+// the complex number of the pair holding channel c, from a per-channel array
+__device__ __forceinline__ cf cpair(const float* p, int c) { return {p[c & ~1], p[c | 1]}; }
 }  // namespace
+
+// ---------------------------------------------------------------------------------------
+// (d) of the records kernels: M = (I + diag(beta) D)^-1, diagonal blocks by substitution,
+// then block rows I = 1..3: M_IJ = -M_II sum_{J <= K < I} (beta D)_IK M_KJ
+template <int NTR>
+__device__ __forceinline__ void records_inverse(const float* sD, float* sM, const float* sB, float (*sY)[16][17]) {
+  constexpr int LC = C + 1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, g = lane >> 4;
+  if (tid < 4 * SUB) {
+    const int s = (tid / SUB) * SUB, col = tid % SUB;
+    for (int r = 0; r < SUB; ++r) {
+      float acc = 0.f;
+      for (int j = 0; j < r; ++j) acc += sD[(s + r) * LC + s + j] * sM[(s + j) * LC + s + col];
+      sM[(s + r) * LC + s + col] = (r == col ? 1.f : 0.f) - sB[s + r] * acc;
+    }
+  }
+  __syncthreads();
+  for (int I = 1; I < NB; ++I) {
+    const int si = I * SUB;
+    for (int J = wave; J < I; J += NTR / 64) {
+      const int sj = J * SUB;
+      const f32x4_t y = tile_mm(
+          si - sj, [&](int r, int kk) { return sB[si + r] * sD[(si + r) * LC + sj + kk]; },
+          [&](int kk, int col) { return sM[(sj + kk) * LC + sj + col]; });
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sY[J][4 * g + r][n] = y[r];
+    }
+    __syncthreads();
+    for (int J = wave; J < I; J += NTR / 64) {
+      const int sj = J * SUB;
+      const f32x4_t m = tile_mm(
+          SUB, [&](int r, int kk) { return sM[(si + r) * LC + si + kk]; }, [&](int kk, int col) { return sY[J][kk][col]; });
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sM[(si + 4 * g + r) * LC + sj + n] = -m[r];
+    }
+    __syncthreads();
+  }
+}
+
+// (e) of the records kernels, after K o gamma (its complex form for SFDA) is staged in R0:
+// W = M diag(beta) R0, then A, D, M to the workspace
+template <int DK, int NTR>
+__device__ __forceinline__ void records_w_out(float* ch, const BwdLayout& L, const float* R0, const float* sA,
+                                              const float* sD, const float* sM, const float* sB) {
+  constexpr int LK = DK + 4, LC = C + 1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, g = lane >> 4;
+  for (int job = wave; job < 4 * (DK / 16); job += NTR / 64) {
+    const int I = job / (DK / 16), ct = job % (DK / 16), c = 16 * ct + n;
+    f32x4_t acc = zero4f();
+#pragma unroll
+    for (int k0 = 0; k0 < C; k0 += 16) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int j = k0 + 4 * g + t;
+        av[t] = sM[(16 * I + n) * LC + j] * sB[j];
+        bv[t] = R0[j * LK + c];
+      }
+      mfma4(acc, av, bv);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ch[L.W + (16 * I + 4 * g + r) * DK + c] = acc[r];
+  }
+  for (int x = tid; x < C * C; x += NTR) {
+    const int i = x / C, j = x % C;
+    ch[L.A + x] = sA[i * LC + j];
+    ch[L.D + x] = sD[i * LC + j];
+    ch[L.M + x] = sM[i * LC + j];
+  }
+}
 
 // ---------------------------------------------------------------------------------------
 // bwd_records_kernel: one workgroup per (b, h, chunk).  A (channel, block) item keeps the
@@ -373,37 +459,7 @@ __global__ __launch_bounds__(DK == 128 ? NTG : NT) void bwd_records_kernel(BwdAr
   }
   __syncthreads();
 
-  // ---- (d) M = (I + diag(beta) D)^-1: diagonal blocks by substitution, then block rows
-  // I = 1..3: M_IJ = -M_II sum_{J <= K < I} (beta D)_IK M_KJ
-  if (tid < 4 * SUB) {
-    const int s = (tid / SUB) * SUB, col = tid % SUB;
-    for (int r = 0; r < SUB; ++r) {
-      float acc = 0.f;
-      for (int j = 0; j < r; ++j) acc += sD[(s + r) * LC + s + j] * sM[(s + j) * LC + s + col];
-      sM[(s + r) * LC + s + col] = (r == col ? 1.f : 0.f) - sB[s + r] * acc;
-    }
-  }
-  __syncthreads();
-  for (int I = 1; I < NB; ++I) {
-    const int si = I * SUB;
-    for (int J = wave; J < I; J += NTR / 64) {
-      const int sj = J * SUB;
-      const f32x4_t y = tile_mm(
-          si - sj, [&](int r, int kk) { return sB[si + r] * sD[(si + r) * LC + sj + kk]; },
-          [&](int kk, int col) { return sM[(sj + kk) * LC + sj + col]; });
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sY[J][4 * g + r][n] = y[r];
-    }
-    __syncthreads();
-    for (int J = wave; J < I; J += NTR / 64) {
-      const int sj = J * SUB;
-      const f32x4_t m = tile_mm(
-          SUB, [&](int r, int kk) { return sM[(si + r) * LC + si + kk]; }, [&](int kk, int col) { return sY[J][kk][col]; });
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sM[(si + 4 * g + r) * LC + sj + n] = -m[r];
-    }
-    __syncthreads();
-  }
+  records_inverse<NTR>(sD, sM, sB, sY);
 
   // ---- (e) K o gamma into the staging region; W = M diag(beta) (K o gamma); A, D, M out
 #pragma unroll
@@ -417,29 +473,213 @@ __global__ __launch_bounds__(DK == 128 ? NTG : NT) void bwd_records_kernel(BwdAr
     for (int r = 0; r < SUB; ++r) R0[(I * SUB + r) * LK + c] = xv[it][r] * pi[it][r] * before;
   }
   __syncthreads();
-  for (int job = wave; job < 4 * (DK / 16); job += NTR / 64) {
-    const int I = job / (DK / 16), ct = job % (DK / 16), c = 16 * ct + n;
-    f32x4_t acc = zero4f();
+  records_w_out<DK, NTR>(ch, L, R0, sA, sD, sM, sB);
+}
+
+// ---------------------------------------------------------------------------------------
+// bwd_records_cpx_kernel: the records for SFDA complex gates (SFDA page, "Arquitectura
+// Central").  Same items, anchors and levels as bwd_records_kernel, with every gate product
+// complex per key-channel pair: a thread keeps its pair's gate, q and k (both channels,
+// so the two threads of a pair do the same complex arithmetic) and writes its own channel's
+// component.  For i in block I and j in block J < I, r_ij = pi_i (blocks between) sigma_j,
+// and A_ij = sum_p Re(conj(q_ip) r_ijp k_jp) = sum over channels of (q conj(pi))_i times
+// ((blocks between) sigma k)_j; gamma, rho, pi, sigma and the block totals are stored as
+// (Re, Im) in the pair's channels; Q o gamma becomes q conj(gamma), K o gamma k conj(gamma)
+// and K o rho rho k.
+template <typename T, int DK>
+__global__ __launch_bounds__(DK == 128 ? NTG : NT) void bwd_records_cpx_kernel(BwdArgs a, int NC) {
+  constexpr int NTR = DK == 128 ? NTG : NT;
+  constexpr int LK = DK + 4, LC = C + 1, NI = DK * NB / NTR;
+  static_assert(NI >= 1 && DK * NB % NTR == 0, "items");
+  __shared__ float sR[3 * C * LK];
+  __shared__ float sA[C * LC], sD[C * LC], sM[C * LC];
+  __shared__ float sPib[NB * DK], sB[C], sY[3][16][17];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, g = lane >> 4;
+  const BwdLayout L(DK, a.Dv);
+  ChunkGeom cg;
+  size_t wsi;
+  if (!block_chunk(a, NC, &cg, &wsi)) return;
+  const int len = cg.len;
+  float* ch = a.ws + wsi * L.total;
+  const size_t kb = row0(cg, a.T, a.H, DK), ks = (size_t)a.H * DK;
+  const size_t bb = ((size_t)cg.b * a.T + cg.t0) * a.H + cg.h;
+  float *R0 = sR, *R1 = sR + C * LK, *R2 = sR + 2 * C * LK;
+
+  // ---- (a) items (c, I): the pair's gate, q, k; pi, sigma and the block total
+  cf al[NI][SUB], qv[NI][SUB], kv[NI][SUB];
 #pragma unroll
-    for (int k0 = 0; k0 < C; k0 += 16) {
-      float av[4], bv[4];
+  for (int it = 0; it < NI; ++it) {
+    const int item = tid + it * NTR, c0 = (item % DK) & ~1, I = item / DK;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int j = k0 + 4 * g + t;
-        av[t] = sM[(16 * I + n) * LC + j] * sB[j];
-        bv[t] = R0[j * LK + c];
-      }
-      mfma4(acc, av, bv);
+    for (int r = 0; r < SUB; ++r) {
+      const int i = I * SUB + r;
+      const bool in = i < len;
+      const size_t o = kb + i * ks + c0;
+      al[it][r] = in ? cf{Elem<T>::load(a.alpha, o), Elem<T>::load(a.alpha, o + 1)} : cf{1.f, 0.f};
+      qv[it][r] = in ? cf{Elem<T>::load(a.q, o), Elem<T>::load(a.q, o + 1)} : cf{0.f, 0.f};
+      kv[it][r] = in ? cf{Elem<T>::load(a.k, o), Elem<T>::load(a.k, o + 1)} : cf{0.f, 0.f};
     }
+  }
+  for (int i = tid; i < C; i += NTR) sB[i] = i < len ? Elem<T>::load(a.beta, bb + (size_t)i * a.H) : 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) ch[L.W + (16 * I + 4 * g + r) * DK + c] = acc[r];
+  for (int it = 0; it < NI; ++it) {
+    const int item = tid + it * NTR, c = item % DK, I = item / DK, e = c & 1;
+    cf p = {1.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < SUB; ++r) {
+      p = cmul(p, al[it][r]);
+      ch[L.pin + (I * SUB + r) * DK + c] = comp(p, e);
+    }
+    sPib[I * DK + c] = comp(p, e);
+    ch[L.pib + I * DK + c] = comp(p, e);
+    cf sf = {1.f, 0.f};
+#pragma unroll
+    for (int r = SUB - 1; r >= 0; --r) {
+      ch[L.sig + (I * SUB + r) * DK + c] = comp(sf, e);
+      sf = cmul(sf, al[it][r]);
+    }
   }
   for (int x = tid; x < C * C; x += NTR) {
     const int i = x / C, j = x % C;
-    ch[L.A + x] = sA[i * LC + j];
-    ch[L.D + x] = sD[i * LC + j];
-    ch[L.M + x] = sM[i * LC + j];
+    if (j / SUB > i / SUB) sA[i * LC + j] = sD[i * LC + j] = sM[i * LC + j] = 0.f;
   }
+  __syncthreads();
+  // gamma, rho, Q o gamma, K o rho; the anchored operands of (b): q conj(pi), k conj(pi), sigma k
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    const int item = tid + it * NTR, c = item % DK, I = item / DK, e = c & 1;
+    cf before = {1.f, 0.f}, after = {1.f, 0.f};
+#pragma unroll
+    for (int J = 0; J < NB; ++J) {
+      if (J < I) before = cmul(before, cpair(sPib + J * DK, c));
+      if (J > I) after = cmul(after, cpair(sPib + J * DK, c));
+    }
+    cf sgl[SUB];
+    cf sf = {1.f, 0.f};
+#pragma unroll
+    for (int r = SUB - 1; r >= 0; --r) {
+      sgl[r] = sf;
+      sf = cmul(sf, al[it][r]);
+    }
+    cf p = {1.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < SUB; ++r) {
+      const int i = I * SUB + r;
+      p = cmul(p, al[it][r]);
+      const cf gam = cmul(before, p), rho = cmul(after, sgl[r]);
+      ch[L.gam + i * DK + c] = comp(gam, e);
+      ch[L.rho + i * DK + c] = comp(rho, e);
+      ch[L.KR + i * DK + c] = comp(cmul(rho, kv[it][r]), e);
+      ch[L.QG + i * DK + c] = comp(cmulc(qv[it][r], gam), e);
+      R0[i * LK + c] = comp(cmulc(qv[it][r], p), e);
+      R1[i * LK + c] = comp(cmulc(kv[it][r], p), e);
+      R2[i * LK + c] = comp(cmul(sgl[r], kv[it][r]), e);
+    }
+  }
+  __syncthreads();
+
+  // ---- (b) off-diagonal tiles; the blocks between J and I multiply the column operand's pairs
+  for (int job = wave; job < 12; job += NTR / 64) {
+    const int mat = job / 6, p = job % 6, I = p < 1 ? 1 : (p < 3 ? 2 : 3), J = p - I * (I - 1) / 2;
+    const float* xrow = (mat ? R1 : R0) + (16 * I + n) * LK;
+    const float* yrow = R2 + (16 * J + n) * LK;
+    f32x4_t acc = zero4f();
+#pragma unroll
+    for (int k0 = 0; k0 < DK; k0 += 16) {
+      const float4 y4 = *(const float4*)(yrow + k0 + 4 * g);
+      const int cb = k0 + 4 * g;  // channels cb .. cb + 3: pairs (cb, cb + 1), (cb + 2, cb + 3)
+      cf w0 = {1.f, 0.f}, w1 = {1.f, 0.f};
+      for (int x = J + 1; x < I; ++x) {
+        w0 = cmul(w0, cpair(sPib + x * DK, cb));
+        w1 = cmul(w1, cpair(sPib + x * DK, cb + 2));
+      }
+      const cf y0 = cmul(cf{y4.x, y4.y}, w0), y1 = cmul(cf{y4.z, y4.w}, w1);
+      const float yv[4] = {y0.x, y0.y, y1.x, y1.y};
+      mm16(acc, xrow, k0, [&](int t) { return yv[t]; });
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) (mat ? sD : sA)[(16 * I + 4 * g + r) * LC + 16 * J + n] = acc[r];
+  }
+
+  // ---- (c) diagonal tiles by levels lam = 8, 4, 2, 1, then 0 (A's diagonal)
+  for (int lam = 8; lam >= 0; lam = lam > 1 ? lam / 2 : lam - 1) {
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      const int item = tid + it * NTR, c = item % DK, I = item / DK, e = c & 1;
+      cf Fv[SUB], Bv[SUB];
+      if (lam > 0) {
+        cf p = {1.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < SUB; ++r) {
+          if ((r & (lam - 1)) == 0) p = cf{1.f, 0.f};
+          p = cmul(p, al[it][r]);
+          Fv[r] = p;
+        }
+        p = cf{1.f, 0.f};
+#pragma unroll
+        for (int r = SUB - 1; r >= 0; --r) {
+          if (((r + 1) & (lam - 1)) == 0) p = cf{1.f, 0.f};
+          Bv[r] = p;
+          p = cmul(p, al[it][r]);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < SUB; ++r) Fv[r] = Bv[r] = cf{1.f, 0.f};
+      }
+#pragma unroll
+      for (int r = 0; r < SUB; ++r) {
+        const int i = I * SUB + r;
+        R0[i * LK + c] = comp(cmulc(qv[it][r], Fv[r]), e);
+        R1[i * LK + c] = comp(cmulc(kv[it][r], Fv[r]), e);
+        R2[i * LK + c] = comp(cmul(Bv[r], kv[it][r]), e);
+      }
+    }
+    __syncthreads();
+    for (int job = wave; job < 8; job += NTR / 64) {
+      const int I = job % NB, mat = job / NB, si = 16 * I;
+      const float* xrow = (mat ? R1 : R0) + (si + n) * LK;
+      const float* yrow = R2 + (si + n) * LK;
+      f32x4_t acc = zero4f();
+#pragma unroll
+      for (int k0 = 0; k0 < DK; k0 += 16) {
+        const float4 y4 = *(const float4*)(yrow + k0 + 4 * g);
+        mm16(acc, xrow, k0, [&](int t) { return f4c(y4, t); });
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int il = 4 * g + r, jl = n;
+        bool keep;
+        if (lam > 0)
+          keep = (il & lam) && !(jl & lam) && ((il & ~(2 * lam - 1)) == (jl & ~(2 * lam - 1)));
+        else
+          keep = il == jl && !mat;
+        if (keep) (mat ? sD : sA)[(si + il) * LC + si + jl] = acc[r];
+        else if (lam == 0 && jl >= il) (mat ? sD : sA)[(si + il) * LC + si + jl] = 0.f;
+      }
+    }
+  }
+  __syncthreads();
+
+  records_inverse<NTR>(sD, sM, sB, sY);
+
+  // ---- (e) k conj(gamma) into the staging region; W = M diag(beta) (K o gamma); A, D, M out
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    const int item = tid + it * NTR, c = item % DK, I = item / DK, e = c & 1;
+    cf before = {1.f, 0.f};
+#pragma unroll
+    for (int J = 0; J < NB; ++J)
+      if (J < I) before = cmul(before, cpair(sPib + J * DK, c));
+    cf p = {1.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < SUB; ++r) {
+      p = cmul(p, al[it][r]);
+      R0[(I * SUB + r) * LK + c] = comp(cmulc(kv[it][r], cmul(before, p)), e);
+    }
+  }
+  __syncthreads();
+  records_w_out<DK, NTR>(ch, L, R0, sA, sD, sM, sB);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -454,7 +694,9 @@ __global__ __launch_bounds__(DK == 128 ? NTG : NT) void bwd_records_kernel(BwdAr
 
 // bwd_state_kernel: chunks in order; writes the chunk-start state S_n and Delta_n.  The
 // next chunk's operands are loaded into registers while the current one computes.
-template <typename T, int DK, bool G2>
+// CPX: SFDA complex gates -- gamma_L multiplies the state's row pairs (2p, 2p+1), which
+// are registers r, r + 1 (r even) of one lane.
+template <typename T, int DK, bool G2, bool CPX>
 __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC) {
   constexpr int LM = C + 4, LW = DK + 4, LV = VTW + 4;
   constexpr int NM = C * C / 4 / NT, NW = C * DK / 4 / NT, NV = C * VTW / 4 / NT;
@@ -567,8 +809,18 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC) {
         const float* krow = sKrT + (16 * I + n) * LM;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) mm16(acc, krow, 16 * kt, [&](int t) { return Dl[kt][t]; });
+        if constexpr (CPX) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) S[I][r] = sGl[16 * I + 4 * g + r] * S[I][r] + acc[r];
+          for (int r = 0; r < 4; r += 2) {
+            const cf gl = {sGl[16 * I + 4 * g + r], sGl[16 * I + 4 * g + r + 1]};
+            const cf z = cmul(gl, cf{S[I][r], S[I][r + 1]});
+            S[I][r] = z.x + acc[r];
+            S[I][r + 1] = z.y + acc[r + 1];
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) S[I][r] = sGl[16 * I + 4 * g + r] * S[I][r] + acc[r];
+        }
       }
     }
   }
@@ -577,7 +829,9 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC) {
 // bwd_adjoint_kernel: chunks in reverse; writes the end-state adjoint dS'_n and dDelta_n
 // of every chunk, and dS_0.  The next chunk's operands are loaded into registers while
 // the current one computes.
-template <typename T, int DK>
+// CPX: SFDA complex gates -- the transpose of the chunk-end rotation-decay is conj(gamma_L)
+// on the row pairs.
+template <typename T, int DK, bool CPX>
 __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC) {
   constexpr int LK = DK + 4, LM = C + 4, LV = VTW + 4;
   constexpr int NM = C * C / 4 / NT, NW = C * DK / 4 / NT, NV = C * VTW / 4 / NT;
@@ -690,8 +944,18 @@ __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC) {
       const float* wrow = sWT + (16 * I + n) * LM;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) mm16(acc, wrow, 16 * kt, [&](int t) { return dD[kt][t]; }, -1.f);
+      if constexpr (CPX) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dS[I][r] = sGl[16 * I + 4 * g + r] * dS[I][r] + acc[r];
+        for (int r = 0; r < 4; r += 2) {
+          const cf gl = {sGl[16 * I + 4 * g + r], sGl[16 * I + 4 * g + r + 1]};
+          const cf z = cmulc(cf{dS[I][r], dS[I][r + 1]}, gl);
+          dS[I][r] = z.x + acc[r];
+          dS[I][r + 1] = z.y + acc[r + 1];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dS[I][r] = sGl[16 * I + 4 * g + r] * dS[I][r] + acc[r];
+      }
     }
   }
   if (a.ds0) {
@@ -714,7 +978,11 @@ __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC) {
 //   D  the block-anchored products PA, PD, F with their B operands staged in LDS;
 //   E  per (channel, block): the in-block decayed sums, dq and dk, the gate gradient.
 
-template <typename T, int DK, int DV, bool G2>
+//   CPX (SFDA complex gates): the per-channel products of A become complex products of a
+//   lane's pair with its neighbour lane's (the pair's other channel, lane ^ 1); D forms
+//   the anchored operands with complex factors; E takes one (pair, block) item per
+//   thread, in complex arithmetic.
+template <typename T, int DK, int DV, bool G2, bool CPX>
 __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
   constexpr int LV = DV + 4, LK = DK + 4, LC = C + 1;
   constexpr int RSZ = (3 * C * LV > 3 * C * LK) ? 3 * C * LV : 3 * C * LK;
@@ -793,7 +1061,21 @@ __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
       part += sf[u].x * df[u].x + sf[u].y * df[u].y + sf[u].z * df[u].z + sf[u].w * df[u].w;
     part += __shfl_xor(part, 16);
     part += __shfl_xor(part, 32);
-    if (g == 0) sGl[c] = part;
+    if constexpr (CPX) {
+      // dgl_p = sum_j conj(dS'_pj) S_pj: Re = sum (d0 s0 + d1 s1), Im = sum (d0 s1 - d1 s0);
+      // cross = sum_j s_c d_(c^1), from the neighbour lane's dS' row
+      float cross = 0.f;
+#pragma unroll
+      for (int u = 0; u < DV / 16; ++u)
+        cross += sf[u].x * __shfl_xor(df[u].x, 1) + sf[u].y * __shfl_xor(df[u].y, 1) +
+                 sf[u].z * __shfl_xor(df[u].z, 1) + sf[u].w * __shfl_xor(df[u].w, 1);
+      cross += __shfl_xor(cross, 16);
+      cross += __shfl_xor(cross, 32);
+      const float part_o = __shfl_xor(part, 1), cross_o = __shfl_xor(cross, 1);
+      if (g == 0) sGl[c] = (c & 1) ? cross - cross_o : part + part_o;
+    } else {
+      if (g == 0) sGl[c] = part;
+    }
     f32x4_t aq[4], aw[4], ar[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
@@ -819,6 +1101,30 @@ __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
           bv[t] = aw[kt][t];
         }
         mfma4(kg, av, bv);
+      }
+      if constexpr (CPX) {
+        // complex pairs in channel order (this lane's channel and its neighbour's):
+        // av = d(Q~) conj(q) + d(K~g) conj(k), bv = conj(d(K~r)) k, dq = d(Q~) gamma,
+        // dk = d(K~g) gamma + d(K~r) conj(rho)
+        const int e = c & 1;
+        auto pr = [&](float own) {
+          const float oth = __shfl_xor(own, 1);
+          return e ? cf{oth, own} : cf{own, oth};
+        };
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * J + 4 * g + r;
+          const cf dq_ = pr(aq[J][r]), dkg = pr(kg[r]), dkr = pr(ar[J][r]);
+          const cf qc = pr(qq[J][r]), kc = pr(kk[J][r]), gc = pr(gm[J][r]), rc = pr(rh[J][r]);
+          AV[i * DK + c] = comp(cadd(cmulc(dq_, qc), cmulc(dkg, kc)), e);
+          BV[i * DK + c] = comp(cmulc(kc, dkr), e);
+          DWg[i * DK + c] = aw[J][r];
+          if (i < len) {
+            a.dq[kb + i * ks + c] = comp(cmul(dq_, gc), e);
+            a.dk[kb + i * ks + c] = comp(cadd(cmul(dkg, gc), cmulc(dkr, rc)), e);
+          }
+        }
+        continue;
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -908,7 +1214,13 @@ __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
         }
 #pragma unroll
         for (int u = 0; u < DK / 16; ++u) {
-          kg[u] = mul4(in4(a.k, j, 16 * u + 4 * g), *(const float4*)(GAM + j * DK + 16 * u + 4 * g));
+          const float4 k4 = in4(a.k, j, 16 * u + 4 * g), g4 = *(const float4*)(GAM + j * DK + 16 * u + 4 * g);
+          if constexpr (CPX) {  // k conj(gamma) on the two pairs of the four channels
+            const cf z0 = cmulc(cf{k4.x, k4.y}, cf{g4.x, g4.y}), z1 = cmulc(cf{k4.z, k4.w}, cf{g4.z, g4.w});
+            kg[u] = make_float4(z0.x, z0.y, z1.x, z1.y);
+          } else {
+            kg[u] = mul4(k4, g4);
+          }
           if (G2) kg[u] = mul4(kg[u], in4(a.erase, j, 16 * u + 4 * g));
         }
         const float *rd = RD + (16 * I + n) * LV, *rw = RW + (16 * I + n) * LK;
@@ -996,10 +1308,27 @@ __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
     const float4 kv = in4(a.k, i, c), qv = in4(a.q, i, c);
     const float4 sg = *(const float4*)(SIG + i * DK + c), pn = *(const float4*)(PIN + i * DK + c);
     const float4 xv = G2 ? mul4(kv, in4(a.erase, i, c)) : kv;  // row operand of the second product
-    *(float4*)(RKS + i * LK + c) = mul4(kv, sg);
-    *(float4*)(RQP + i * LK + c) = mul4(qv, pn);
-    *(float4*)(RKP + i * LK + c) = mul4(xv, pn);
+    if constexpr (CPX) {  // k sigma; q conj(pi), k conj(pi) (the key side of F takes conj(r))
+      const cf k0 = {kv.x, kv.y}, k1 = {kv.z, kv.w}, q0 = {qv.x, qv.y}, q1 = {qv.z, qv.w};
+      const cf s0 = {sg.x, sg.y}, s1 = {sg.z, sg.w}, p0 = {pn.x, pn.y}, p1 = {pn.z, pn.w};
+      cf a0 = cmul(k0, s0), a1 = cmul(k1, s1);
+      *(float4*)(RKS + i * LK + c) = make_float4(a0.x, a0.y, a1.x, a1.y);
+      a0 = cmulc(q0, p0), a1 = cmulc(q1, p1);
+      *(float4*)(RQP + i * LK + c) = make_float4(a0.x, a0.y, a1.x, a1.y);
+      a0 = cmulc(k0, p0), a1 = cmulc(k1, p1);
+      *(float4*)(RKP + i * LK + c) = make_float4(a0.x, a0.y, a1.x, a1.y);
+    } else {
+      *(float4*)(RKS + i * LK + c) = mul4(kv, sg);
+      *(float4*)(RQP + i * LK + c) = mul4(qv, pn);
+      *(float4*)(RKP + i * LK + c) = mul4(xv, pn);
+    }
   }
+  // complex product of the whole blocks between J and I for the pair of channel c
+  auto between_c = [&](int J, int I, int c) {
+    cf w = {1.f, 0.f};
+    for (int x = J + 1; x < I; ++x) w = cmul(w, cpair(sPib + x * DK, c));
+    return w;
+  };
   __syncthreads();
   for (int job = wave; job < 12 * (DK / 16); job += NTG / 64) {
     const int ct = job % (DK / 16), p6 = (job / (DK / 16)) % 6, mat = job / (DK / 16) / 6;
@@ -1009,13 +1338,23 @@ __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
     const float* src = mat ? sdD : sdA;
     f32x4_t acc = zero4f();
     for (int J = 0; J < Mb; ++J) {
-      const float w = between(J, Mb, c);
       float av[4], bv[4];
+      if constexpr (CPX) {
+        const cf w = between_c(J, Mb, c);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int jx = 16 * J + 4 * g + t;
-        av[t] = src[(16 * I + n) * LC + jx];
-        bv[t] = RKS[jx * LK + c] * w;
+        for (int t = 0; t < 4; ++t) {
+          const int jx = 16 * J + 4 * g + t;
+          av[t] = src[(16 * I + n) * LC + jx];
+          bv[t] = comp(cmul(cpair(RKS + jx * LK, c), w), c & 1);
+        }
+      } else {
+        const float w = between(J, Mb, c);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int jx = 16 * J + 4 * g + t;
+          av[t] = src[(16 * I + n) * LC + jx];
+          bv[t] = RKS[jx * LK + c] * w;
+        }
       }
       mfma4(acc, av, bv);
     }
@@ -1027,22 +1366,40 @@ __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
     const int Mb = job / (DK / 16), ct = job % (DK / 16), s = 16 * Mb, c = 16 * ct + n;
     f32x4_t acc = zero4f();
     for (int I = Mb + 1; I < NB; ++I) {
-      const float w = between(Mb, I, c);
       float av[4], bv[4];
+      if constexpr (CPX) {  // conj(r(i, e)) = conj(pi_i) conj(blocks between)
+        const cf w = between_c(Mb, I, c);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int ix = 16 * I + 4 * g + t;
-        av[t] = sdA[ix * LC + s + n];
-        bv[t] = RQP[ix * LK + c] * w;
-      }
-      mfma4(acc, av, bv);
+        for (int t = 0; t < 4; ++t) {
+          const int ix = 16 * I + 4 * g + t;
+          av[t] = sdA[ix * LC + s + n];
+          bv[t] = comp(cmulc(cpair(RQP + ix * LK, c), w), c & 1);
+        }
+        mfma4(acc, av, bv);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int ix = 16 * I + 4 * g + t;
-        av[t] = sdD[ix * LC + s + n];
-        bv[t] = RKP[ix * LK + c] * w;
+        for (int t = 0; t < 4; ++t) {
+          const int ix = 16 * I + 4 * g + t;
+          av[t] = sdD[ix * LC + s + n];
+          bv[t] = comp(cmulc(cpair(RKP + ix * LK, c), w), c & 1);
+        }
+        mfma4(acc, av, bv);
+      } else {
+        const float w = between(Mb, I, c);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int ix = 16 * I + 4 * g + t;
+          av[t] = sdA[ix * LC + s + n];
+          bv[t] = RQP[ix * LK + c] * w;
+        }
+        mfma4(acc, av, bv);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int ix = 16 * I + 4 * g + t;
+          av[t] = sdD[ix * LC + s + n];
+          bv[t] = RKP[ix * LK + c] * w;
+        }
+        mfma4(acc, av, bv);
       }
-      mfma4(acc, av, bv);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) F[(s + 4 * g + r) * DK + c] = acc[r];
@@ -1056,9 +1413,123 @@ __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
     const int x = tid + it * NTG, i = x / (DK / 4), c = 4 * (x % (DK / 4));
     *(float4*)(RQ + i * LK + c) = in4(a.q, i, c);
     *(float4*)(RK + i * LK + c) = in4(a.k, i, c);
-    *(float4*)(RA + i * LK + c) = i < len ? ld4<T>(a.alpha, kb + i * ks + c) : make_float4(1.f, 1.f, 1.f, 1.f);
+    // rows past the end decay by the identity: 1 per channel, or 1 + 0i per complex pair
+    *(float4*)(RA + i * LK + c) = i < len   ? ld4<T>(a.alpha, kb + i * ks + c)
+                                  : CPX ? make_float4(1.f, 0.f, 1.f, 0.f)
+                                        : make_float4(1.f, 1.f, 1.f, 1.f);
   }
   __syncthreads();
+  if constexpr (CPX) {
+    // SFDA: one (pair, block) item per thread, the real item's sums and recursion in complex
+    // arithmetic: Zq_i = sum_j dA_ij r_ij k_j, Zc_j = sum_i (dA_ij q_i + dD_ij k_i) conj(r_ij);
+    // pair weights E_ij = (dA_ij conj(q_i) + dD_ij conj(k_i)) k_j; the recursion's result
+    // is the conjugate of the gate gradient (dL/dRe + i dL/dIm)
+    for (int item = tid; item < (DK / 2) * NB; item += NTG) {
+      const int c0 = 2 * (item % (DK / 2)), Mb = item / (DK / 2), s = Mb * SUB;
+      auto lds = [&](const float* base, int i) { return cf{base[i * LK + c0], base[i * LK + c0 + 1]}; };
+      auto wsc = [&](const float* base, int i) { return cf{base[i * DK + c0], base[i * DK + c0 + 1]}; };
+      cf al[SUB], qv[SUB], kv[SUB];
+#pragma unroll
+      for (int r = 0; r < SUB; ++r) {
+        al[r] = lds(RA, s + r);
+        qv[r] = lds(RQ, s + r);
+        kv[r] = lds(RK, s + r);
+      }
+      const float* PAm = PA + (size_t)(Mb > 0 ? Mb - 1 : 0) * C * DK;
+      const float* PDm = PD + (size_t)(Mb > 0 ? Mb - 1 : 0) * C * DK;
+      cf gs = {1.f, 0.f}, rend = {1.f, 0.f};
+#pragma unroll
+      for (int J = 0; J < NB; ++J) {
+        if (J < Mb) gs = cmul(gs, cpair(sPib + J * DK, c0));
+        if (J > Mb) rend = cmul(rend, cpair(sPib + J * DK, c0));
+      }
+#pragma unroll
+      for (int r = 0; r < SUB; ++r) {
+        const int i = s + r;
+        cf zq = cscale(kv[r], sdA[i * LC + i]), zr = {0.f, 0.f}, P = {1.f, 0.f};
+#pragma unroll
+        for (int rj = r - 1; rj >= 0; --rj) {
+          P = cmul(P, al[rj + 1]);
+          const cf kp = cmul(kv[rj], P);
+          zq = cadd(zq, cscale(kp, sdA[i * LC + s + rj]));
+          zr = cadd(zr, cscale(kp, sdD[i * LC + s + rj]));
+        }
+        if (Mb > 0) {
+          const cf pin = wsc(PIN, i);
+          zq = cadd(zq, cmul(pin, wsc(PAm, i)));
+          zr = cadd(zr, cmul(pin, wsc(PDm, i)));
+        }
+        cf zc = cscale(qv[r], sdA[i * LC + i]);
+        P = cf{1.f, 0.f};
+#pragma unroll
+        for (int ri = r + 1; ri < SUB; ++ri) {
+          P = cmul(P, al[ri]);
+          const cf w = cadd(cscale(qv[ri], sdA[(s + ri) * LC + i]), cscale(kv[ri], sdD[(s + ri) * LC + i]));
+          zc = cadd(zc, cmulc(w, P));
+        }
+        if (Mb < NB - 1) zc = cadd(zc, cmulc(wsc(F, i), wsc(SIG, i)));
+        if (i < len) {
+          const size_t o = kb + i * ks + c0;
+          a.dq[o] += zq.x;
+          a.dq[o + 1] += zq.y;
+          a.dk[o] += zr.x + zc.x;
+          a.dk[o + 1] += zr.y + zc.y;
+        }
+      }
+
+      cf bvs = {0.f, 0.f};  // sum_{j < s} bv_j r(s-1, j)
+      for (int J = 0; J < Mb; ++J) {
+        cf part = {0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < SUB; ++r) part = cadd(part, cmul(wsc(BV, J * SUB + r), wsc(SIG, J * SUB + r)));
+        bvs = cadd(bvs, cmul(part, between_c(J, Mb, c0)));
+      }
+      const cf dgl = cpair(sGl, c0);
+      const cf tail = cadd(bvs, cmul(dgl, gs));  // the final-state terms of row C - 1
+      cf u[SUB];
+#pragma unroll
+      for (int r = 0; r < SUB; ++r) {
+        const int i = s + r;
+        u[r] = cmul(wsc(AV, i), gs);
+        if (Mb > 0) u[r] = cadd(u[r], cadd(cmulc(wsc(PAm, i), qv[r]), cmulc(wsc(PDm, i), kv[r])));
+        if (i == C - 1) u[r] = cadd(u[r], tail);
+      }
+      cf f[SUB];
+      if (Mb < NB - 1) {
+        cf x = {0.f, 0.f};  // sum_{i > e} r(i, e) g_i
+        for (int i = C - 1; i >= s + SUB; --i) {
+          cf gv = cmul(wsc(AV, i), gs);
+          if (Mb > 0) gv = cadd(gv, cadd(cmulc(wsc(PAm, i), lds(RQ, i)), cmulc(wsc(PDm, i), lds(RK, i))));
+          if (i == C - 1) gv = cadd(gv, tail);
+          x = cmul(lds(RA, i), cadd(gv, x));
+        }
+        u[SUB - 1] = cadd(u[SUB - 1], x);
+#pragma unroll
+        for (int r = 0; r < SUB; ++r) f[r] = cadd(cmulc(kv[r], wsc(F, s + r)), cmul(wsc(BV, s + r), rend));
+      } else {
+#pragma unroll
+        for (int r = 0; r < SUB; ++r) f[r] = wsc(BV, s + r);
+      }
+#pragma unroll
+      for (int m = 0; m < SUB; ++m) {
+        cf acc = u[SUB - 1];
+#pragma unroll
+        for (int i = SUB - 2; i >= m; --i) acc = cadd(u[i], cmul(al[i + 1], acc));
+        if (s + m < len) {
+          a.dalpha[kb + (s + m) * ks + c0] = acc.x;
+          a.dalpha[kb + (s + m) * ks + c0 + 1] = -acc.y;
+        }
+#pragma unroll
+        for (int i = m + 1; i < SUB; ++i) {
+          cf E = cmul(cadd(cscale(cconj(qv[i]), sdA[(s + i) * LC + s + m]), cscale(cconj(kv[i]), sdD[(s + i) * LC + s + m])),
+                      kv[m]);
+          if (i == SUB - 1) E = cadd(E, f[m]);
+          u[i] = cadd(cmul(al[m], u[i]), E);
+        }
+      }
+    }
+    return;
+  }
   for (int item = tid; item < DK * NB; item += NTG) {
     const int c = item % DK, Mb = item / DK, s = Mb * SUB;
     // xv: the row operand of the second product (k, or the GDN-2 erase vector b o k)
@@ -1186,7 +1657,7 @@ __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
 }
 
 // ---------------------------------------------------------------------------------------
-template <typename T, int DK, bool G2>
+template <typename T, int DK, bool G2, bool CPX>
 static hipError_t launch_bwd_dk(const BwdArgs& a, int NC) {
   // per-chunk grid: B H NC (fixed) or H gmax (packed; workgroups past the chunk count
   // exit); walks: one workgroup per (chain, 64 value columns)
@@ -1194,29 +1665,36 @@ static hipError_t launch_bwd_dk(const BwdArgs& a, int NC) {
   const long per_chunk = a.ctab ? (long)a.H * a.gmax : (long)chains * NC;
   hipStream_t st = (hipStream_t)a.stream;
   if (per_chunk > 0) {
-    hipLaunchKernelGGL((bwd_records_kernel<T, DK, G2>), dim3(per_chunk), dim3(DK == 128 ? NTG : NT), 0, st, a, NC);
-    hipLaunchKernelGGL((bwd_state_kernel<T, DK, G2>), dim3(walks), dim3(NT), 0, st, a, NC);
+    if constexpr (CPX)
+      hipLaunchKernelGGL((bwd_records_cpx_kernel<T, DK>), dim3(per_chunk), dim3(DK == 128 ? NTG : NT), 0, st, a, NC);
+    else
+      hipLaunchKernelGGL((bwd_records_kernel<T, DK, G2>), dim3(per_chunk), dim3(DK == 128 ? NTG : NT), 0, st, a, NC);
+    hipLaunchKernelGGL((bwd_state_kernel<T, DK, G2, CPX>), dim3(walks), dim3(NT), 0, st, a, NC);
   }
-  hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK>), dim3(walks), dim3(NT), 0, st, a, NC);
+  hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX>), dim3(walks), dim3(NT), 0, st, a, NC);
   if (per_chunk > 0) {
     if (a.Dv == 64)
-      hipLaunchKernelGGL((bwd_grads_kernel<T, DK, 64, G2>), dim3(per_chunk), dim3(NTG), 0, st, a, NC);
+      hipLaunchKernelGGL((bwd_grads_kernel<T, DK, 64, G2, CPX>), dim3(per_chunk), dim3(NTG), 0, st, a, NC);
     else
-      hipLaunchKernelGGL((bwd_grads_kernel<T, DK, 128, G2>), dim3(per_chunk), dim3(NTG), 0, st, a, NC);
+      hipLaunchKernelGGL((bwd_grads_kernel<T, DK, 128, G2, CPX>), dim3(per_chunk), dim3(NTG), 0, st, a, NC);
   }
   return hipGetLastError();
 }
 
-template <typename T, bool G2>
+template <typename T, bool G2, bool CPX>
 static hipError_t launch_bwd_t(const BwdArgs& a, int NC) {
-  return a.Dk == 64 ? launch_bwd_dk<T, 64, G2>(a, NC) : launch_bwd_dk<T, 128, G2>(a, NC);
+  return a.Dk == 64 ? launch_bwd_dk<T, 64, G2, CPX>(a, NC) : launch_bwd_dk<T, 128, G2, CPX>(a, NC);
 }
 
 hipError_t launch_bwd(const BwdArgs& a) {
   if ((long)(a.ctab ? a.n_seqs : a.B) * a.H == 0) return hipSuccess;
   const int NC = (a.T + C - 1) / C;
-  if (a.erase) return a.bf16 ? launch_bwd_t<bf16_t, true>(a, NC) : launch_bwd_t<float, true>(a, NC);
-  return a.bf16 ? launch_bwd_t<bf16_t, false>(a, NC) : launch_bwd_t<float, false>(a, NC);
+  if (a.cpx) {
+    if (a.erase) return hipErrorInvalidValue;
+    return a.bf16 ? launch_bwd_t<bf16_t, false, true>(a, NC) : launch_bwd_t<float, false, true>(a, NC);
+  }
+  if (a.erase) return a.bf16 ? launch_bwd_t<bf16_t, true, false>(a, NC) : launch_bwd_t<float, true, false>(a, NC);
+  return a.bf16 ? launch_bwd_t<bf16_t, false, false>(a, NC) : launch_bwd_t<float, false, false>(a, NC);
 }
 
 }  // namespace kda

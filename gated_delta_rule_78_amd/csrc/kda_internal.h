@@ -83,6 +83,9 @@ struct BwdArgs {
   const void* write = nullptr;
   float* derase = nullptr;
   float* dwrite = nullptr;
+  // SFDA (complex gates in alpha's place, (Re, Im) per key-channel pair; dalpha returns
+  // d/dRe, d/dIm in the same channels)
+  bool cpx = false;
 };
 
 // fp32 offsets inside one chunk's workspace block of the backward (C = 64 rows, NB = 4

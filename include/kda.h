@@ -29,7 +29,7 @@
  *                      with its workspace query further down.
  * Variants further down: the two-pass forward with a caller workspace, packed
  * variable-length batches, multi-token decode, Gated DeltaNet-2 gates and SFDA
- * complex gates.
+ * complex gates, each with its backward.
  *
  * Conventions shared by all entry points
  *   - Every pointer except `shape` is a DEVICE pointer on the current HIP
@@ -317,6 +317,30 @@ int kda_gdn2_chunk_bwd_varlen(const kda_shape* shape, const int* cu_seqlens, int
                               float* dalpha, float* d_erase, float* d_write,
                               float* d_initial_state, void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/*
+ * Backward of the SFDA chunk forward (kda_sfda_chunk_fwd; SFDA page, "Arquitectura
+ * Central": complex rotation-decay gates).  lambda holds the gate of key-channel pair p as
+ * (Re, Im) in channels (2p, 2p+1), as for the forward; dlambda [B, T, H, dk] fp32 returns
+ * dL/dRe in channel 2p and dL/dIm in channel 2p+1.  The chunk form is kda_chunk_bwd's with
+ * complex gate products per pair (r_ij = prod of lambda_l, j < l <= i): Q o gamma becomes
+ * q conj(gamma), K o gamma k conj(gamma), K o rho rho k, the chunk-end decay rotates the
+ * state's row pairs, and the gate gradient is the conjugate of the exclusive-product sum of
+ * kda_chunk_bwd in complex arithmetic (no division by a gate).  Both dtypes; every other
+ * argument, the workspace (kda_chunk_bwd_workspace_size / ..._varlen_workspace_size),
+ * layouts, alignment, alias rules and errors as kda_chunk_bwd and kda_chunk_bwd_varlen.
+ */
+int kda_sfda_chunk_bwd(const kda_shape* shape, const void* q, const void* k, const void* v,
+                       const void* lambda, const void* beta, const float* initial_state,
+                       const void* d_o, const float* d_final_state, float* dq, float* dk,
+                       float* dv, float* dlambda, float* dbeta, float* d_initial_state,
+                       void* workspace, size_t workspace_bytes, void* stream);
+int kda_sfda_chunk_bwd_varlen(const kda_shape* shape, const int* cu_seqlens, int n_seqs,
+                              const void* q, const void* k, const void* v, const void* lambda,
+                              const void* beta, const float* initial_state, const void* d_o,
+                              const float* d_final_state, float* dq, float* dk, float* dv,
+                              float* dlambda, float* dbeta, float* d_initial_state,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * One recurrent decode step for every (b, h), state updated in place:

@@ -385,3 +385,30 @@ def test_gdn2_bwd_argument_errors(L):
                                        None) == NULL
     assert L.kda_gdn2_chunk_bwd_varlen(ctypes.byref(vshape), _p(17), -1, *([_p(0)] * 16), _p(16), sz(vneed),
                                        None) == SHAPE
+
+
+def test_sfda_bwd_argument_errors(L):
+    """The SFDA backward shares kda_chunk_bwd's checks (no compute without a GPU)."""
+    shape = kda.Shape(1, 64, 2, 64, 64, 64, 0)
+    need = L.kda_chunk_bwd_workspace_size(ctypes.byref(shape))
+    sz = ctypes.c_size_t
+
+    def bwd(q=_p(0), lam=_p(3), dq=_p(10), dlam=_p(13), ws=_p(16), n=need, sh=shape):
+        return L.kda_sfda_chunk_bwd(ctypes.byref(sh), q, _p(1), _p(2), lam, _p(4), None, _p(5), None, dq, _p(11),
+                                    _p(12), dlam, _p(14), _p(15), ws, sz(n), None)
+
+    assert L.kda_sfda_chunk_bwd(None, *([None] * 15), sz(0), None) == NULL
+    assert bwd(lam=None) == NULL
+    assert bwd(dlam=None) == NULL
+    assert bwd(n=need - 1) == WORKSPACE
+    assert bwd(lam=_p(3, off=8)) == ALIGN
+    assert bwd(dlam=_p(3)) == ALIAS                # the gate gradient over the gates
+    assert bwd(sh=kda.Shape(1, 64, 2, 96, 64, 64, 0)) == UNSUP
+    zero = kda.Shape(0, 64, 2, 64, 64, 64, 0)
+    assert L.kda_sfda_chunk_bwd(ctypes.byref(zero), *([None] * 15), sz(0), None) == 0
+    vshape = kda.Shape(1, 300, 2, 64, 64, 64, 0)
+    vneed = L.kda_chunk_bwd_varlen_workspace_size(ctypes.byref(vshape), 4)
+    assert L.kda_sfda_chunk_bwd_varlen(ctypes.byref(vshape), None, 4, *([_p(0)] * 14), _p(16), sz(vneed),
+                                       None) == NULL
+    assert L.kda_sfda_chunk_bwd_varlen(ctypes.byref(vshape), _p(17), -1, *([_p(0)] * 14), _p(16), sz(vneed),
+                                       None) == SHAPE
