@@ -62,7 +62,9 @@ int prep_cpw_override() {
 
 size_t workspace_bytes_for(const kda_shape& s) {
   const size_t nchunks = ((size_t)s.T + 63) / 64;
-  return (size_t)s.B * s.H * nchunks * kda::record_bytes(s.dtype == KDA_BF16, s.dk);
+  const bool bf16 = s.dtype == KDA_BF16;
+  return (size_t)s.B * s.H * nchunks * kda::record_bytes(bf16, s.dk) +
+         kda::state_split_bytes(s.B, s.T, s.H, s.dk, s.dv, bf16);
 }
 
 // Pointers of one chunk-forward call; the members a given entry point does not take are NULL.

@@ -55,6 +55,10 @@ hipError_t launch_prep(const ChunkArgs& a, void* ws, int cpw);
 // the same records from the bf16 kernel sized for two workgroups per compute unit
 hipError_t launch_records(const ChunkArgs& a, void* ws, int cpw);
 hipError_t launch_state(const ChunkArgs& a, const void* ws);
+// Few (b, h) chains over a long sequence: the state pass splits each chain into this many
+// segments (1: one walk per chain) and needs state_split_bytes of scratch after the records.
+int state_segments(int B, int T, int H, int dk, int dv, bool bf16);
+size_t state_split_bytes(int B, int T, int H, int dk, int dv, bool bf16);
 size_t record_bytes(bool bf16, int dk);
 // varlen: clamped offsets and the chunk table from a.cu (one workgroup)
 hipError_t launch_varlen_table(const ChunkArgs& a, int* cs, int* ctab, int* cbase, int* ctotal);

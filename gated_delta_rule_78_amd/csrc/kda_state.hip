@@ -60,6 +60,10 @@ struct SCfg {
   static_assert(NBUF * (RL::IMG + NTILE * V_BYTES) <= 160 * 1024, "LDS budget");
 };
 
+// flags of a split walk (launch_state_split): no output stores; v read as zero; start from
+// the identity; only the last segment writes the end state, indexed by (b, h)
+enum : int { kSegNoOut = 1, kSegZeroV = 2, kSegIdentity = 4, kSegLastOnly = 8 };
+
 }  // namespace
 
 // Keeps the compiler's scheduler from moving instructions across this point: the
@@ -233,7 +237,8 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
                                                                          float* sT, int Tlen, int H, int DV, int BH,
                                                                          const void* __restrict__ gw,
                                                                          const int* __restrict__ cu,
-                                                                         const int* __restrict__ cbase, int gmax) {
+                                                                         const int* __restrict__ cbase, int gmax,
+                                                                         int nseg, int segc, int flags) {
   using K = SCfg<T, DK, VT, G2>;
   constexpr int NP = K::NP;
   using RL = typename K::RL;
@@ -256,18 +261,22 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
   const int g = lane >> 4;
   const int n = lane & 15;
   const int NVT = DV / VT;
-  int bh, vt;
+  // chains: (b, h) pairs, times nseg segments of segc chunks each when the walk is split;
+  // the value tiles of one chain (or segment) read the same records and share an XCD
+  const int BHs = BH * nseg;
+  int bhs, vt;
   {
     const int bid = blockIdx.x;
-    if (NVT > 1 && (BH & 7) == 0) {
+    if (NVT > 1 && (BHs & 7) == 0) {
       const int r = bid >> 3;
       vt = r % NVT;
-      bh = (r / NVT) * 8 + (bid & 7);
+      bhs = (r / NVT) * 8 + (bid & 7);
     } else {
-      bh = bid / NVT;
+      bhs = bid / NVT;
       vt = bid % NVT;
     }
   }
+  const int bh = bhs / nseg, seg = bhs - bh * nseg;
   // the sequence this workgroup walks: batch row b of length Tlen, or (packed varlen
   // batch, cu != NULL) sequence b = bh / H of length cu[b + 1] - cu[b]
   const int b = bh / H, h = bh % H;
@@ -284,17 +293,30 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
     slen = Tlen;
     rec0 = ws + (size_t)bh * ((Tlen + C - 1) / C) * RL::BYTES;
   }
+  if (nseg > 1) {  // this workgroup's segment: chunks [seg segc, (seg + 1) segc)
+    const int cb = seg * segc;
+    rec0 += (size_t)cb * RL::BYTES;
+    sbase += (size_t)cb * C;
+    slen = max(0, min(slen - cb * C, segc * C));
+  }
   const int nchunks = (slen + C - 1) / C;
+  const size_t sidx = (size_t)bhs;  // start / end state index: (b, h), or (b, h, segment)
 
   f32x4_t S[DK / 16];
 #pragma unroll
   for (int r = 0; r < DK / 16; ++r) S[r] = zero4();
-  if (s0 && !producer) {
+  if ((flags & kSegIdentity) && !producer) {  // S = I (the walk then yields the transfer P)
 #pragma unroll
     for (int r = 0; r < DK / 16; ++r)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) S[r][e] = s0[((size_t)bh * DK + 16 * r + 4 * g + e) * DV + v0 + 16 * wave + n];
+      for (int e = 0; e < 4; ++e) S[r][e] = 16 * r + 4 * g + e == v0 + 16 * wave + n ? 1.f : 0.f;
+  } else if (s0 && !producer) {
+#pragma unroll
+    for (int r = 0; r < DK / 16; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[r][e] = s0[(sidx * DK + 16 * r + 4 * g + e) * DV + v0 + 16 * wave + n];
   }
+  const bool zero_v = (flags & kSegZeroV) != 0, no_out = (flags & kSegNoOut) != 0;
 
   // (producer waves) chunk c's record and v tile -> LDS; v rows past the end are clamped
   // to the last row here and zeroed once they have landed
@@ -302,7 +324,7 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
     const char* rec = rec0 + (size_t)c * RL::BYTES;
     const int t0 = c * C;
 #pragma nounroll
-    for (int x = pw; x < K::N_DMA_V; x += NP) {
+    for (int x = zero_v ? K::N_DMA_V : pw; x < K::N_DMA_V; x += NP) {
       const int sl = x * 64 + lane;
       const int row = sl / K::UPR, u = sl % K::UPR;
       const size_t gr = (sbase + min(t0 + row, slen - 1)) * H + h;
@@ -318,6 +340,7 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
   };
   // the staged outputs of chunk c (in the consumed v tile `vv`) -> o
   auto store_o = [&](int c, const char* vv) {
+    if (no_out) return;
     const int t0 = c * C;
     const int nv = min(C, slen - t0);
     for (int j = tid; j < C * K::UPR; j += NT) {
@@ -329,7 +352,7 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
   };
   // v rows past the end of the sequence read as zero
   auto pad_rows = [&](int c, char* vv) {
-    const int nv = slen - c * C;
+    const int nv = zero_v ? 0 : slen - c * C;
     if (nv < C) {
       for (int j = nv * K::UPR + tid; j < C * K::UPR; j += NT) *(uint4*)(vv + j * 16) = make_uint4(0, 0, 0, 0);
       lds_barrier();
@@ -376,12 +399,63 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
     }
   }
 
-  if (sT && !producer) {
+  const bool last_only = (flags & kSegLastOnly) != 0;
+  if (sT && !producer && (!last_only || seg == nseg - 1)) {
+    const size_t oi = last_only ? (size_t)bh : sidx;
 #pragma unroll
     for (int r = 0; r < DK / 16; ++r)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        sT[((size_t)bh * DK + 16 * r + 4 * g + e) * DV + v0 + 16 * wave + n] = S[r][e];
+      for (int e = 0; e < 4; ++e) sT[(oi * DK + 16 * r + 4 * g + e) * DV + v0 + 16 * wave + n] = S[r][e];
+  }
+}
+
+// Start states of the segments of a split walk: Sst[b, h, 0] = S_0 (or zero) and
+// Sst[b, h, g + 1] = P_g Sst[b, h, g] + B_g, where B_g is segment g's end state from a zero
+// start and P_g (d_k x d_k) its end state from the identity with v = 0 -- the affine
+// transfer of a block of the SFDA page ("Principales Contribuciones", item 3), applied
+// segment by segment.  One workgroup per (b, h, 16 state columns), fp32.
+template <int DK>
+__global__ __launch_bounds__(256) void seg_scan_kernel(const float* __restrict__ s0, const float* __restrict__ P,
+                                                     const float* __restrict__ Bst, float* __restrict__ Sst, int G,
+                                                     int DV) {
+  __shared__ float sS[DK][17];
+  const int nsl = DV / 16, bh = blockIdx.x / nsl, c0 = (blockIdx.x % nsl) * 16;
+  const int tid = threadIdx.x, c = tid & 15, r0 = tid >> 4;  // rows r0 + 16 j
+  constexpr int RJ = DK / 16;
+  const size_t SS = (size_t)DK * DV;
+  float* out0 = Sst + (size_t)bh * G * SS;
+#pragma unroll
+  for (int j = 0; j < RJ; ++j) {
+    const int r = r0 + 16 * j;
+    const float x = s0 ? s0[((size_t)bh * DK + r) * DV + c0 + c] : 0.f;
+    sS[r][c] = x;
+    out0[(size_t)r * DV + c0 + c] = x;
+  }
+  for (int gi = 0; gi + 1 < G; ++gi) {
+    __syncthreads();
+    const float* Pg = P + ((size_t)bh * G + gi) * DK * DK;
+    const float* Bg = Bst + ((size_t)bh * G + gi) * SS;
+    float acc[RJ];
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) {
+      const int r = r0 + 16 * j;
+      float a = Bg[(size_t)r * DV + c0 + c];
+      const float4* prow = (const float4*)(Pg + (size_t)r * DK);
+#pragma unroll 4
+      for (int k4 = 0; k4 < DK / 4; ++k4) {
+        const float4 p = prow[k4];
+        a += p.x * sS[4 * k4][c] + p.y * sS[4 * k4 + 1][c] + p.z * sS[4 * k4 + 2][c] + p.w * sS[4 * k4 + 3][c];
+      }
+      acc[j] = a;
+    }
+    __syncthreads();
+    float* outg = Sst + ((size_t)bh * G + gi + 1) * SS;
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) {
+      const int r = r0 + 16 * j;
+      sS[r][c] = acc[j];
+      outg[(size_t)r * DV + c0 + c] = acc[j];
+    }
   }
 }
 
@@ -393,8 +467,61 @@ static hipError_t launch_state_t(const ChunkArgs& a, const void* ws) {
   // varlen: one chain per (sequence, head): BH = n_seqs * H
   const int BHc = a.cu ? a.n_seqs * a.H : BH;
   hipLaunchKernelGGL(kern, dim3(BHc * (a.dv / VT)), dim3(K::NT), 0, (hipStream_t)a.stream, (const char*)ws, a.v,
-                     a.s0, a.o, a.sT, a.T, a.H, a.dv, BHc, a.write, a.cu, a.ctab_base, a.gmax);
+                     a.s0, a.o, a.sT, a.T, a.H, a.dv, BHc, a.write, a.cu, a.ctab_base, a.gmax, 1, 0, 0);
   return hipGetLastError();
+}
+
+// The split walk (fixed-length bf16 batches at d_k = 128, few (b, h) chains): four launches
+// over G segments per chain, 64 value columns per workgroup, scratch after the records:
+// B [BH G][d_k][d_v], P [BH G][d_k][d_k], segment start states [BH G][d_k][d_v].
+static hipError_t launch_state_split(const ChunkArgs& a, const void* ws, int G) {
+  using K = SCfg<bf16_t, 128, 64, false>;
+  const int BH = a.B * a.H, NC = (a.T + C - 1) / C, segc = (NC + G - 1) / G;
+  const size_t rec = (size_t)BH * NC * K::RL::BYTES;
+  float* Bst = (float*)((char*)ws + rec);
+  float* P = Bst + (size_t)BH * G * 128 * a.dv;
+  float* Sst = P + (size_t)BH * G * 128 * 128;
+  hipStream_t st = (hipStream_t)a.stream;
+  auto kern = chunk_state_kernel<bf16_t, 128, 64, false, false>;
+  const char* w = (const char*)ws;
+  hipLaunchKernelGGL(kern, dim3(BH * G * (a.dv / 64)), dim3(K::NT), 0, st, w, a.v, (const float*)nullptr, a.o, Bst,
+                     a.T, a.H, a.dv, BH, nullptr, nullptr, nullptr, 0, G, segc, (int)kSegNoOut);
+  hipLaunchKernelGGL(kern, dim3(BH * G * 2), dim3(K::NT), 0, st, w, a.v, (const float*)nullptr, a.o, P, a.T, a.H,
+                     128, BH, nullptr, nullptr, nullptr, 0, G, segc, (int)(kSegNoOut | kSegZeroV | kSegIdentity));
+  hipLaunchKernelGGL(seg_scan_kernel<128>, dim3(BH * (a.dv / 16)), dim3(256), 0, st, a.s0, P, Bst, Sst, G, a.dv);
+  hipLaunchKernelGGL(kern, dim3(BH * G * (a.dv / 64)), dim3(K::NT), 0, st, w, a.v, (const float*)Sst, a.o, a.sT,
+                     a.T, a.H, a.dv, BH, nullptr, nullptr, nullptr, 0, G, segc, (int)kSegLastOnly);
+  return hipGetLastError();
+}
+
+// KDA_STATE_SEG=0 keeps the single walk per chain, =G forces G segments (tuning aid)
+static int state_seg_override() {
+  static const int v = [] {
+    const char* e = getenv("KDA_STATE_SEG");
+    return e ? atoi(e) : -1;
+  }();
+  return v;
+}
+
+int state_segments(int B, int T, int H, int dk, int dv, bool bf16) {
+  if (!bf16 || dk != 128 || (dv != 64 && dv != 128)) return 1;
+  const int NC = (T + C - 1) / C, o = state_seg_override();
+  int G;
+  if (o >= 0) {
+    G = o;
+  } else {
+    const long tiles = (long)B * H * (dv / 64);  // 64-column tiles of the plain walk
+    if (tiles >= 256) return 1;
+    G = (int)((256 + tiles - 1) / tiles);
+  }
+  G = min(G, NC / 16);  // at least 16 chunks per segment
+  return G >= 2 ? G : 1;
+}
+
+size_t state_split_bytes(int B, int T, int H, int dk, int dv, bool bf16) {
+  const int G = state_segments(B, T, H, dk, dv, bf16);
+  if (G < 2) return 0;
+  return (size_t)B * H * G * dk * (2 * (size_t)dv + dk) * sizeof(float);
 }
 
 // KDA_STATE_VT=16|32|64 pins the state pass's value-tile width (tuning aid)
@@ -442,6 +569,10 @@ static hipError_t launch_state_g(const ChunkArgs& a, const void* ws) {
 
 hipError_t launch_state(const ChunkArgs& a, const void* ws) {
   if ((a.cu ? a.n_seqs : a.B) * a.H == 0) return hipSuccess;
+  if (!a.cu && !a.write && !a.cpx) {
+    const int G = state_segments(a.B, a.T, a.H, a.dk, a.dv, a.bf16);
+    if (G >= 2) return launch_state_split(a, ws, G);
+  }
   if (a.cpx) return a.write ? hipErrorInvalidValue : launch_state_g<false, true>(a, ws);
   return a.write ? launch_state_g<true>(a, ws) : launch_state_g<false>(a, ws);
 }

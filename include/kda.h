@@ -113,6 +113,14 @@ int kda_chunk_fwd(const kda_shape* shape, const void* q, const void* k, const vo
  *          (-W, Q o gamma, (K o rho)^T, A, (I + T)^-1 diag(beta), gamma of the last
  *          row: the data of the chunk's affine block transfer) into the workspace;
  *   pass 2 walks the chunks of each (b, h) in order and carries the fp32 state.
+ *          With few (b, h) chains over a long sequence (bf16, dk = 128, fewer than 256
+ *          64-column tiles), each chain is split into segments of at least 16 chunks
+ *          that are walked in parallel: once from a zero state (end state B_g), once
+ *          from the identity with v = 0 (the segment's transfer P_g), then the start
+ *          states S_(g+1) = P_g S_g + B_g are scanned and every segment is walked from
+ *          its own start state (the affine block transfer of the SFDA page,
+ *          "Principales Contribuciones" item 3); the scratch for this follows the
+ *          records in the workspace and is counted by kda_chunk_fwd_workspace_size.
  * This trades extra HBM traffic (each record is written once and read once) for
  * parallelism over chunks; on MI355X it is the faster forward whenever T > 64 (about
  * twice the single-pass kernel of kda_chunk_fwd at d = 128, measured from 128 to
