@@ -113,8 +113,8 @@ int kda_chunk_fwd(const kda_shape* shape, const void* q, const void* k, const vo
  *          (-W, Q o gamma, (K o rho)^T, A, (I + T)^-1 diag(beta), gamma of the last
  *          row: the data of the chunk's affine block transfer) into the workspace;
  *   pass 2 walks the chunks of each (b, h) in order and carries the fp32 state.
- *          With few (b, h) chains over a long sequence (bf16, dk = 128, fewer than 256
- *          64-column tiles), each chain is split into segments of at least 16 chunks
+ *          With few (b, h) chains over a long sequence (bf16, dk = 128, at most 32
+ *          64-column tiles), each chain is split into 8 or more segments of at least 16 chunks
  *          that are walked in parallel: once from a zero state (end state B_g), once
  *          from the identity with v = 0 (the segment's transfer P_g), then the start
  *          states S_(g+1) = P_g S_g + B_g are scanned and every segment is walked from

@@ -260,19 +260,19 @@ def test_full_ckda_prefill_128k_sampled():
 @pytest.mark.parametrize("dv,zero_s0,in_place", [(128, False, False), (64, False, True), (128, True, False)])
 def test_split_state_walk(dv, zero_s0, in_place):
     """Few (b, h) chains over a long sequence: the state pass splits each chain into
-    segments (B1 H2 T4485: 4 segments of 18, 18, 18 and 17 chunks), walks them from zero and
-    from the identity, scans the segment start states and walks them again; every output
-    and the final state against the oracle, all heads."""
+    segments (B1 H2 T8325: 8 segments, seven of 17 chunks and one of 12), walks them from
+    zero and from the identity, scans the segment start states and walks them again; every
+    output and the final state against the oracle, all heads."""
     import gated_delta_rule_78_amd as kda
     from gated_delta_rule_78_amd import lib
     import ctypes
-    T = 64 * 70 + 5
+    T = 64 * 130 + 5
     sh = kda.Shape(1, T, 2, 128, dv, 64, 0)
     plain = kda.Shape(1, 64 * 15, 2, 128, dv, 64, 0)
     # the workspace grows by the split walk's scratch exactly when the split is taken
     rec = lambda s: (s.T + 63) // 64 * s.B * s.H
     one = lib().kda_chunk_fwd_workspace_size(ctypes.byref(plain)) // rec(plain)
-    assert lib().kda_chunk_fwd_workspace_size(ctypes.byref(sh)) == rec(sh) * one + 2 * 4 * 128 * (2 * dv + 128) * 4
+    assert lib().kda_chunk_fwd_workspace_size(ctypes.byref(sh)) == rec(sh) * one + 2 * 8 * 128 * (2 * dv + 128) * 4
     inp = make(1, T, 2, 128, dv, "bf16", "ckda", zero_s0, seed=61 + dv)
     _check(inp, inp.S0, in_place=in_place and not zero_s0, label=f"split dv{dv}", path="twopass")
 
@@ -282,7 +282,7 @@ def test_split_state_walk_long_memory():
     beta <= 0.05, S0 ~ N(0, 1)): the segment transfers P and the scan of start states carry
     most of every output, so an error in either shows at O(1)."""
     from gated_delta_rule_78_amd.inputs import bf16_bits
-    T = 64 * 70 + 5
+    T = 64 * 130 + 5
     inp = make(1, T, 2, 128, 128, "bf16", "kda", False, seed=67)
     rng = np.random.default_rng(67)
     inp.alpha = bf16_bits(np.where(rng.random(inp.alpha.shape) < 0.5, 1.0, 1.0 - 2.0 ** -8).astype(np.float32))
