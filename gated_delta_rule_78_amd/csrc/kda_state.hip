@@ -38,8 +38,9 @@ __device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
 // chunk's record and v tile global -> LDS with 16-byte DMA.  A wave stalled issuing
 // DMA cannot issue matrix work, and one wave's DMA issue rate is well below a CU's
 // share of HBM bandwidth, hence several producers beside the compute waves.
-// G2: Gated DeltaNet-2 -- a write-gate tile (same layout as v) streams beside v and
-// U = M (w o v).
+// G2: Gated DeltaNet-2 -- U = M (w o v); each compute wave loads the write gate of its own
+// rows and columns into registers one chunk ahead, so the LDS holds only v tiles and the
+// value tiles can be as wide as KDA's.
 template <typename T, int DK, int VT, bool G2 = false>
 struct SCfg {
   using RL = RecordLayout<T, DK>;
@@ -53,7 +54,7 @@ struct SCfg {
   static constexpr int N_DMA_REC = (RL::IMG + 1023) / 1024;  // wave-wide DMA steps per record
   static constexpr int N_DMA_V = C * UPR / 64;
   static constexpr int V_BYTES = C * RS_V;
-  static constexpr int NTILE = G2 ? 2 : 1;   // v (and write-gate) tiles per buffer
+  static constexpr int NTILE = 1;            // v tiles per buffer
   // two record and v buffers when they fit: the next chunk streams in during this one
   static constexpr int NBUF = 2 * (RL::IMG + NTILE * V_BYTES) <= 160 * 1024 ? 2 : 1;
   static_assert(N_DMA_V * 64 == C * UPR, "v tile split");
@@ -83,7 +84,7 @@ __device__ __forceinline__ void fence_sched() {
 // CPX: SFDA complex gates -- gamma_last holds (Re, Im) per key-channel pair and turns the
 // state's row pairs (rows 2p, 2p+1 = one complex coordinate, same lane) by that product.
 template <typename T, int DK, int VT, bool G2 = false, bool CPX = false>
-__device__ __forceinline__ void state_chunk(const char* rec, char* vv, const char* wv, f32x4_t (&S)[DK / 16],
+__device__ __forceinline__ void state_chunk(const char* rec, char* vv, const Frag<T>* wf, f32x4_t (&S)[DK / 16],
                                             int wave, int g, int n) {
   using K = SCfg<T, DK, VT, G2>;
   using RL = typename K::RL;
@@ -116,11 +117,9 @@ __device__ __forceinline__ void state_chunk(const char* rec, char* vv, const cha
   if constexpr (G2) {  // the write side: z = w o v, rounded once to the operand type
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      Frag<T> bw;
-      bw.load_col8(wv + (32 * ks + 8 * g) * K::RS_V + (16 * wave + n) * ES, K::RS_V);
       float z[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) z[e] = bv[ks].get(e) * bw.get(e);
+      for (int e = 0; e < 8; ++e) z[e] = bv[ks].get(e) * wf[ks].get(e);
 #pragma unroll
       for (int e = 0; e < 8; ++e) bv[ks].set(e, z[e]);
     }
@@ -251,8 +250,6 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
   __shared__ __align__(16) char v_a[K::V_BYTES];
   __shared__ __align__(16) char rec_b[K::NBUF == 2 ? RL::IMG : 16];
   __shared__ __align__(16) char v_b[K::NBUF == 2 ? K::V_BYTES : 16];
-  __shared__ __align__(16) char w_a[G2 ? K::V_BYTES : 16];  // write-gate tiles (G2)
-  __shared__ __align__(16) char w_b[G2 && K::NBUF == 2 ? K::V_BYTES : 16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -320,7 +317,7 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
 
   // (producer waves) chunk c's record and v tile -> LDS; v rows past the end are clamped
   // to the last row here and zeroed once they have landed
-  auto issue = [&](int c, char* rec_dst, char* v_dst, char* w_dst) {
+  auto issue = [&](int c, char* rec_dst, char* v_dst) {
     const char* rec = rec0 + (size_t)c * RL::BYTES;
     const int t0 = c * C;
 #pragma nounroll
@@ -330,7 +327,6 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
       const size_t gr = (sbase + min(t0 + row, slen - 1)) * H + h;
       const size_t off = (gr * DV + v0) * ES + (size_t)u * 16;
       dma16((const char*)gv + off, v_dst + x * 1024);
-      if constexpr (G2) dma16((const char*)gw + off, w_dst + x * 1024);
     }
 #pragma nounroll
     for (int x = pw; x < K::N_DMA_REC; x += NP) {
@@ -359,11 +355,25 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
     }
   };
 
-  if (nchunks > 0 && producer) issue(0, rec_a, v_a, w_a);
+  // (compute waves, G2) the write gate of this lane's rows 32 ks + 8 g + e and column of
+  // chunk c, rows past the end clamped to the last row (their v rows are zero)
+  Frag<T> wf[G2 ? 2 : 1];
+  auto load_w = [&](int c) {
+    const int t0 = c * C, col = v0 + 16 * wave + n;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const size_t row = sbase + min(t0 + 32 * ks + 8 * g + e, slen - 1);
+        wf[ks].set(e, Elem<T>::load(gw, (row * H + h) * DV + col));
+      }
+  };
+  if (G2 && nchunks > 0 && !producer) load_w(0);
+  if (nchunks > 0 && producer) issue(0, rec_a, v_a);
   if constexpr (K::NBUF == 2) {
     // chunk c computes from buffers P while the producer streams chunk c + 1 into
     // buffers Q; the outputs of chunk c - 1, staged in Q's v tile, are stored first
-    auto step = [&](int c, const char* recP, char* vP, const char* wP, char* recQ, char* vQ, char* wQ) {
+    auto step = [&](int c, const char* recP, char* vP, char* recQ, char* vQ) {
       full_barrier();  // chunk c landed; chunk c - 1 finished everywhere
       if (c > 0) {
         store_o(c - 1, vQ);
@@ -371,15 +381,16 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
       }
       pad_rows(c, vP);
       if (producer) {
-        if (c + 1 < nchunks) issue(c + 1, recQ, vQ, wQ);
+        if (c + 1 < nchunks) issue(c + 1, recQ, vQ);
       } else {
-        state_chunk<T, DK, VT, G2, CPX>(recP, vP, wP, S, wave, g, n);
+        state_chunk<T, DK, VT, G2, CPX>(recP, vP, wf, S, wave, g, n);
+        if (G2 && c + 1 < nchunks) load_w(c + 1);
       }
     };
     for (int chunk = 0; chunk < nchunks; chunk += 2) {
-      step(chunk, rec_a, v_a, w_a, rec_b, v_b, w_b);
+      step(chunk, rec_a, v_a, rec_b, v_b);
       if (chunk + 1 >= nchunks) break;
-      step(chunk + 1, rec_b, v_b, w_b, rec_a, v_a, w_a);
+      step(chunk + 1, rec_b, v_b, rec_a, v_a);
     }
     if (nchunks > 0) {
       lds_barrier();
@@ -389,12 +400,15 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
     for (int chunk = 0; chunk < nchunks; ++chunk) {
       full_barrier();
       pad_rows(chunk, v_a);
-      if (!producer) state_chunk<T, DK, VT, G2, CPX>(rec_a, v_a, w_a, S, wave, g, n);
+      if (!producer) {
+        state_chunk<T, DK, VT, G2, CPX>(rec_a, v_a, wf, S, wave, g, n);
+        if (G2 && chunk + 1 < nchunks) load_w(chunk + 1);
+      }
       lds_barrier();
       store_o(chunk, v_a);
       if (chunk + 1 < nchunks) {
         lds_barrier();  // every output read out of v_a before the next chunk lands there
-        if (producer) issue(chunk + 1, rec_a, v_a, w_a);
+        if (producer) issue(chunk + 1, rec_a, v_a);
       }
     }
   }
@@ -537,10 +551,10 @@ static int state_vt_override() {
 
 // Value-tile width of the state pass: each workgroup walks the whole chunk chain of one
 // (b, h, tile), so with few (b, h) pairs narrower tiles put more compute units on the
-// chains (every tile reads the whole record; the extra reads hit in L2).  The
-// Gated DeltaNet-2 write-gate tiles need LDS: at d_k = 128 the tiles are at most 32 wide.
+// chains (every tile reads the whole record; the extra reads hit in L2).  The Gated
+// DeltaNet-2 write gate rides in registers, so every gate family takes the same widths.
 static int pick_state_vt(const ChunkArgs& a) {
-  const int cap = (a.write && a.bf16 && a.dk == 128) ? 32 : 64;
+  const int cap = 64;
   const int o = state_vt_override();
   int vt;
   if (o == 16 || o == 32 || o == 64) {
@@ -557,9 +571,7 @@ static hipError_t launch_state_vt(const ChunkArgs& a, const void* ws) {
   switch (pick_state_vt(a)) {
     case 16: return launch_state_t<T, DK, 16, G2, CPX>(a, ws);
     case 32: return launch_state_t<T, DK, 32, G2, CPX>(a, ws);
-    default:
-      if constexpr (G2 && DK == 128 && sizeof(T) == 2) return hipErrorInvalidValue;  // capped at 32 above
-      else return launch_state_t<T, DK, 64, G2, CPX>(a, ws);
+    default: return launch_state_t<T, DK, 64, G2, CPX>(a, ws);
   }
 }
 
