@@ -692,25 +692,50 @@ __global__ __launch_bounds__(DK == 128 ? NTG : NT) void bwd_records_cpx_kernel(B
 // Only the chunk's shared operands are staged in LDS (row strides padded by four floats),
 // with vector loads issued together.
 
+// A split walk (few chains over long sequences): each chain is cut into nseg segments of
+// segc chunks that are walked in parallel -- from a zero start with the real inputs (end
+// states B_g), from the identity with the inputs read as zero (the d_k x d_k transfers
+// P_g, cols = d_k), then, after a scan of the segment start states, from those start
+// states with the per-chunk writes.  nseg = 1 is the plain walk.
+struct WalkSplit {
+  int nseg = 1, segc = 0, cols = 0, flags = 0;
+  const float* start = nullptr;  // [chains nseg][d_k][cols], NULL: zero (nseg > 1)
+  float* end = nullptr;          // [chains nseg][d_k][cols], or NULL
+};
+enum : int { kWNoWrite = 1, kWZeroIn = 2, kWIdentity = 4 };
+
 // bwd_state_kernel: chunks in order; writes the chunk-start state S_n and Delta_n.  The
 // next chunk's operands are loaded into registers while the current one computes.
 // CPX: SFDA complex gates -- gamma_L multiplies the state's row pairs (2p, 2p+1), which
 // are registers r, r + 1 (r even) of one lane.
 template <typename T, int DK, bool G2, bool CPX>
-__global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC) {
+__global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC, WalkSplit sp) {
   constexpr int LM = C + 4, LW = DK + 4, LV = VTW + 4;
   constexpr int NM = C * C / 4 / NT, NW = C * DK / 4 / NT, NV = C * VTW / 4 / NT;
   __shared__ float sM[C * LM], sW[C * LW], sKrT[DK * LM], sV[C * LV], sGl[DK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, g = lane >> 4;
-  const int dv = a.Dv, ntile = dv / VTW, bh = blockIdx.x / ntile, v0 = (blockIdx.x % ntile) * VTW;
-  const int nch = chain_chunks(a, NC, bh);  // bh: the chain (b H + h, or sequence H + h)
+  const bool split = sp.nseg > 1;
+  const int dv = a.Dv, cols = split ? sp.cols : dv, ntile = cols / VTW;
+  const int cs = blockIdx.x / ntile, v0 = (blockIdx.x % ntile) * VTW;  // cs: chain (and segment)
+  const int bh = cs / sp.nseg, seg = cs % sp.nseg;  // bh: the chain (b H + h, or sequence H + h)
+  const int c0 = seg * sp.segc, nall = chain_chunks(a, NC, bh);
+  const int nch = split ? max(0, min(sp.segc, nall - c0)) : nall;
+  const bool zero_in = sp.flags & kWZeroIn, no_write = sp.flags & kWNoWrite;
   const int col = v0 + 16 * wave + n;  // this lane's state column
   const BwdLayout L(DK, dv);
   f32x4_t S[DK / 16];
 #pragma unroll
   for (int I = 0; I < DK / 16; ++I)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) S[I][r] = a.s0 ? a.s0[((size_t)bh * DK + 16 * I + 4 * g + r) * dv + col] : 0.f;
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * I + 4 * g + r;
+      if (sp.flags & kWIdentity)
+        S[I][r] = row == col ? 1.f : 0.f;
+      else if (split)
+        S[I][r] = sp.start ? sp.start[((size_t)cs * DK + row) * cols + col] : 0.f;
+      else
+        S[I][r] = a.s0 ? a.s0[((size_t)bh * DK + row) * dv + col] : 0.f;
+    }
   // one chunk's operands in registers: M; W; K o rho; V and beta (or, Gated DeltaNet-2,
   // the write gate w: M (w o V)); gamma_last.  Step st
   // moves chunk st - 1 from registers to LDS, issues the loads of chunk st, then computes
@@ -749,10 +774,11 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC) {
     }
     if (st < nch) {
       size_t wsl;
-      const ChunkGeom cg = chain_chunk(a, NC, bh, st, &wsl);
+      const ChunkGeom cg = chain_chunk(a, NC, bh, c0 + st, &wsl);
       const float* cl = a.ws + wsl * L.total;
       const size_t vb = row0(cg, a.T, a.H, dv), vs = (size_t)a.H * dv;
       const size_t bb = ((size_t)cg.b * a.T + cg.t0) * a.H + cg.h;
+      const int vlen = zero_in ? 0 : cg.len;  // the transfer walk reads v as zero
 #pragma unroll
       for (int it = 0; it < NM; ++it) {
         const int x = tid + it * NT, i = x / (C / 4), j = 4 * (x % (C / 4));
@@ -767,7 +793,7 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC) {
 #pragma unroll
       for (int it = 0; it < NV; ++it) {
         const int x = tid + it * NT, j = x / (VTW / 4), c = 4 * (x % (VTW / 4));
-        const bool in = j < cg.len;
+        const bool in = j < vlen;
         pv[it] = in ? ld4<T>(a.v, vb + j * vs + v0 + c) : make_float4(0.f, 0.f, 0.f, 0.f);
         if (G2)
           pwg[G2 ? it : 0] = in ? ld4<T>(a.write, vb + j * vs + v0 + c) : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -779,12 +805,14 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC) {
     if (st == 0) continue;
     const int nc = st - 1;
     size_t wsc;
-    chain_chunk(a, NC, bh, nc, &wsc);
+    chain_chunk(a, NC, bh, c0 + nc, &wsc);
     float* ch = a.ws + wsc * L.total;
+    if (!no_write) {
 #pragma unroll
-    for (int I = 0; I < DK / 16; ++I)
+      for (int I = 0; I < DK / 16; ++I)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ch[L.S + (16 * I + 4 * g + r) * dv + col] = S[I][r];
+        for (int r = 0; r < 4; ++r) ch[L.S + (16 * I + 4 * g + r) * dv + col] = S[I][r];
+    }
     // Delta = M (beta o V) - W S
     f32x4_t Dl[4];
 #pragma unroll
@@ -798,10 +826,12 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC) {
 #pragma unroll
       for (int kt = 0; kt < DK / 16; ++kt) mm16(acc, wrow, 16 * kt, [&](int t) { return S[kt][t]; }, -1.f);
       Dl[I] = acc;
+      if (!no_write) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ch[L.DL + (16 * I + 4 * g + r) * dv + col] = acc[r];
+        for (int r = 0; r < 4; ++r) ch[L.DL + (16 * I + 4 * g + r) * dv + col] = acc[r];
+      }
     }
-    if (nc + 1 < nch) {
+    if (nc + 1 < nch || sp.end) {
       // S' = gamma_L o S + (K o rho)^T Delta
 #pragma unroll
       for (int I = 0; I < DK / 16; ++I) {
@@ -824,6 +854,12 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC) {
       }
     }
   }
+  if (sp.end) {
+#pragma unroll
+    for (int I = 0; I < DK / 16; ++I)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sp.end[((size_t)cs * DK + 16 * I + 4 * g + r) * cols + col] = S[I][r];
+  }
 }
 
 // bwd_adjoint_kernel: chunks in reverse; writes the end-state adjoint dS'_n and dDelta_n
@@ -832,20 +868,33 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC) {
 // CPX: SFDA complex gates -- the transpose of the chunk-end rotation-decay is conj(gamma_L)
 // on the row pairs.
 template <typename T, int DK, bool CPX>
-__global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC) {
+__global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC, WalkSplit sp) {
   constexpr int LK = DK + 4, LM = C + 4, LV = VTW + 4;
   constexpr int NM = C * C / 4 / NT, NW = C * DK / 4 / NT, NV = C * VTW / 4 / NT;
   __shared__ float sKr[C * LK], sAT[C * LM], sQgT[DK * LM], sWT[DK * LM], sO[C * LV], sGl[DK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, g = lane >> 4;
-  const int dv = a.Dv, ntile = dv / VTW, bh = blockIdx.x / ntile, v0 = (blockIdx.x % ntile) * VTW;
-  const int nch = chain_chunks(a, NC, bh);  // bh: the chain (b H + h, or sequence H + h)
+  const bool split = sp.nseg > 1;
+  const int dv = a.Dv, cols = split ? sp.cols : dv, ntile = cols / VTW;
+  const int cs = blockIdx.x / ntile, v0 = (blockIdx.x % ntile) * VTW;  // cs: chain (and segment)
+  const int bh = cs / sp.nseg, seg = cs % sp.nseg;  // bh: the chain (b H + h, or sequence H + h)
+  const int c0 = seg * sp.segc, nall = chain_chunks(a, NC, bh);
+  const int nch = split ? max(0, min(sp.segc, nall - c0)) : nall;  // chunks c0 .. c0 + nch - 1, in reverse
+  const bool zero_in = sp.flags & kWZeroIn, no_write = sp.flags & kWNoWrite;
   const int col = v0 + 16 * wave + n;
   const BwdLayout L(DK, dv);
   f32x4_t dS[DK / 16];
 #pragma unroll
   for (int I = 0; I < DK / 16; ++I)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dS[I][r] = a.dsT ? a.dsT[((size_t)bh * DK + 16 * I + 4 * g + r) * dv + col] : 0.f;
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * I + 4 * g + r;
+      if (sp.flags & kWIdentity)
+        dS[I][r] = row == col ? 1.f : 0.f;
+      else if (split)
+        dS[I][r] = sp.start ? sp.start[((size_t)cs * DK + row) * cols + col] : 0.f;
+      else
+        dS[I][r] = a.dsT ? a.dsT[((size_t)bh * DK + row) * dv + col] : 0.f;
+    }
   // one chunk's operands in registers: K o rho; Q o gamma; W; A; dO; gamma_last.  Step st
   // moves chunk nch - st from registers to LDS, issues the loads of chunk nch - 1 - st,
   // then computes chunk nch - st while they are in flight.
@@ -884,7 +933,7 @@ __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC) {
       __syncthreads();
     }
     if (st < nch) {
-      const int ld = nch - 1 - st;
+      const int ld = c0 + nch - 1 - st;
       size_t wsl;
       const ChunkGeom cg = chain_chunk(a, NC, bh, ld, &wsl);
       const float* cl = a.ws + wsl * L.total;
@@ -904,19 +953,21 @@ __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC) {
 #pragma unroll
       for (int it = 0; it < NV; ++it) {
         const int x = tid + it * NT, i = x / (VTW / 4), c = 4 * (x % (VTW / 4));
-        po[it] = i < cg.len ? ld4<T>(a.dO, vb + i * vs + v0 + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+        po[it] = i < cg.len && !zero_in ? ld4<T>(a.dO, vb + i * vs + v0 + c) : make_float4(0.f, 0.f, 0.f, 0.f);
       }
       if (tid < DK) pg = cl[L.gam + (C - 1) * DK + tid];
     }
     if (st == 0) continue;
-    const int nc = nch - st;
+    const int nc = c0 + nch - st;
     size_t wsc;
     chain_chunk(a, NC, bh, nc, &wsc);
     float* ch = a.ws + wsc * L.total;
+    if (!no_write) {
 #pragma unroll
-    for (int I = 0; I < DK / 16; ++I)
+      for (int I = 0; I < DK / 16; ++I)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ch[L.DS + (16 * I + 4 * g + r) * dv + col] = dS[I][r];
+        for (int r = 0; r < 4; ++r) ch[L.DS + (16 * I + 4 * g + r) * dv + col] = dS[I][r];
+    }
     // dDelta = (K o rho) dS' + A^T dO
     f32x4_t dD[4];
 #pragma unroll
@@ -930,8 +981,10 @@ __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC) {
       for (int k0 = 0; k0 < C; k0 += 16)
         mm16(acc, arow, k0, [&](int t) { return sO[(k0 + 4 * g + t) * LV + 16 * wave + n]; });
       dD[I] = acc;
+      if (!no_write) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ch[L.DDL + (16 * I + 4 * g + r) * dv + col] = acc[r];
+        for (int r = 0; r < 4; ++r) ch[L.DDL + (16 * I + 4 * g + r) * dv + col] = acc[r];
+      }
     }
     // dS = gamma_L o dS' + (Q o gamma)^T dO - W^T dDelta
 #pragma unroll
@@ -958,11 +1011,64 @@ __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC) {
       }
     }
   }
-  if (a.ds0) {
+  if (sp.end) {
+#pragma unroll
+    for (int I = 0; I < DK / 16; ++I)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sp.end[((size_t)cs * DK + 16 * I + 4 * g + r) * cols + col] = dS[I][r];
+  } else if (a.ds0 && seg == 0) {  // the chain's first segment ends at S_0
 #pragma unroll
     for (int I = 0; I < DK / 16; ++I)
 #pragma unroll
       for (int r = 0; r < 4; ++r) a.ds0[((size_t)bh * DK + 16 * I + 4 * g + r) * dv + col] = dS[I][r];
+  }
+}
+
+// Segment start states of a split walk, fp32, one workgroup per (chain, 16 columns):
+// forward (the state walk) X_0 = init, X_(g+1) = P_g X_g + B_g; reverse (the adjoint walk,
+// whose segments run backwards) X_(G-1) = init, X_(g-1) = P_g X_g + B_g.  init may be NULL.
+template <int DK>
+__global__ __launch_bounds__(256) void walk_scan_kernel(const float* __restrict__ init, const float* __restrict__ P,
+                                                      const float* __restrict__ Bst, float* __restrict__ X, int G,
+                                                      int dv, int reverse) {
+  __shared__ float sX[DK][17];
+  const int nsl = dv / 16, ch = blockIdx.x / nsl, c0 = (blockIdx.x % nsl) * 16;
+  const int tid = threadIdx.x, c = tid & 15, r0 = tid >> 4;
+  constexpr int RJ = DK / 16;
+  const size_t SS = (size_t)DK * dv;
+  const int g0 = reverse ? G - 1 : 0;
+#pragma unroll
+  for (int j = 0; j < RJ; ++j) {
+    const int r = r0 + 16 * j;
+    const float x = init ? init[((size_t)ch * DK + r) * dv + c0 + c] : 0.f;
+    sX[r][c] = x;
+    X[((size_t)ch * G + g0) * SS + (size_t)r * dv + c0 + c] = x;
+  }
+  for (int step = 0; step + 1 < G; ++step) {
+    const int gi = reverse ? G - 1 - step : step, gn = reverse ? gi - 1 : gi + 1;
+    __syncthreads();
+    const float* Pg = P + ((size_t)ch * G + gi) * DK * DK;
+    const float* Bg = Bst + ((size_t)ch * G + gi) * SS;
+    float acc[RJ];
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) {
+      const int r = r0 + 16 * j;
+      float s = Bg[(size_t)r * dv + c0 + c];
+      const float4* prow = (const float4*)(Pg + (size_t)r * DK);
+#pragma unroll 4
+      for (int k4 = 0; k4 < DK / 4; ++k4) {
+        const float4 p = prow[k4];
+        s += p.x * sX[4 * k4][c] + p.y * sX[4 * k4 + 1][c] + p.z * sX[4 * k4 + 2][c] + p.w * sX[4 * k4 + 3][c];
+      }
+      acc[j] = s;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) {
+      const int r = r0 + 16 * j;
+      sX[r][c] = acc[j];
+      X[((size_t)ch * G + gn) * SS + (size_t)r * dv + c0 + c] = acc[j];
+    }
   }
 }
 
@@ -1669,9 +1775,30 @@ static hipError_t launch_bwd_dk(const BwdArgs& a, int NC) {
       hipLaunchKernelGGL((bwd_records_cpx_kernel<T, DK>), dim3(per_chunk), dim3(DK == 128 ? NTG : NT), 0, st, a, NC);
     else
       hipLaunchKernelGGL((bwd_records_kernel<T, DK, G2>), dim3(per_chunk), dim3(DK == 128 ? NTG : NT), 0, st, a, NC);
-    hipLaunchKernelGGL((bwd_state_kernel<T, DK, G2, CPX>), dim3(walks), dim3(NT), 0, st, a, NC);
   }
-  hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX>), dim3(walks), dim3(NT), 0, st, a, NC);
+  const int G = a.ctab ? 1 : bwd_walk_segments(a.B, a.T, a.H, a.Dk, a.Dv);
+  if (G < 2) {
+    if (per_chunk > 0) hipLaunchKernelGGL((bwd_state_kernel<T, DK, G2, CPX>), dim3(walks), dim3(NT), 0, st, a, NC, WalkSplit{});
+    hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX>), dim3(walks), dim3(NT), 0, st, a, NC, WalkSplit{});
+  } else {
+    // split walks: scratch after the chunk blocks; B [chains G][d_k][d_v], P [chains G][d_k][d_k],
+    // start states [chains G][d_k][d_v], used by the state walk and then by the adjoint walk
+    float* Bst = a.ws + (size_t)chains * NC * BwdLayout(DK, a.Dv).total;
+    float* P = Bst + (size_t)chains * G * DK * a.Dv;
+    float* X = P + (size_t)chains * G * DK * DK;
+    const int segc = (NC + G - 1) / G, wv = chains * G * (a.Dv / VTW), wk = chains * G * (DK / VTW);
+    const WalkSplit wb{G, segc, a.Dv, kWNoWrite, nullptr, Bst};
+    const WalkSplit wp{G, segc, DK, kWNoWrite | kWZeroIn | kWIdentity, nullptr, P};
+    const WalkSplit wf{G, segc, a.Dv, 0, X, nullptr};
+    hipLaunchKernelGGL((bwd_state_kernel<T, DK, G2, CPX>), dim3(wv), dim3(NT), 0, st, a, NC, wb);
+    hipLaunchKernelGGL((bwd_state_kernel<T, DK, G2, CPX>), dim3(wk), dim3(NT), 0, st, a, NC, wp);
+    hipLaunchKernelGGL(walk_scan_kernel<DK>, dim3(chains * (a.Dv / 16)), dim3(256), 0, st, a.s0, P, Bst, X, G, a.Dv, 0);
+    hipLaunchKernelGGL((bwd_state_kernel<T, DK, G2, CPX>), dim3(wv), dim3(NT), 0, st, a, NC, wf);
+    hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX>), dim3(wv), dim3(NT), 0, st, a, NC, wb);
+    hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX>), dim3(wk), dim3(NT), 0, st, a, NC, wp);
+    hipLaunchKernelGGL(walk_scan_kernel<DK>, dim3(chains * (a.Dv / 16)), dim3(256), 0, st, a.dsT, P, Bst, X, G, a.Dv, 1);
+    hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX>), dim3(wv), dim3(NT), 0, st, a, NC, wf);
+  }
   if (per_chunk > 0) {
     if (a.Dv == 64)
       hipLaunchKernelGGL((bwd_grads_kernel<T, DK, 64, G2, CPX>), dim3(per_chunk), dim3(NTG), 0, st, a, NC);
@@ -1684,6 +1811,31 @@ static hipError_t launch_bwd_dk(const BwdArgs& a, int NC) {
 template <typename T, bool G2, bool CPX>
 static hipError_t launch_bwd_t(const BwdArgs& a, int NC) {
   return a.Dk == 64 ? launch_bwd_dk<T, 64, G2, CPX>(a, NC) : launch_bwd_dk<T, 128, G2, CPX>(a, NC);
+}
+
+// Segments per chain of the split walks (1: one walk per chain): taken, as in the forward's
+// state pass, when fewer than 256 walk tiles of 64 columns would run and at least 8
+// segments of 16 or more chunks fit (three walks of NC / G chunks on 256 workgroups beat one
+// walk of NC chunks on few).  KDA_BWD_SEG=0 keeps one walk, =G forces G segments.
+int bwd_walk_segments(int B, int T, int H, int dk, int dv) {
+  static const int o = [] {
+    const char* e = getenv("KDA_BWD_SEG");
+    return e ? atoi(e) : -1;
+  }();
+  const int NC = (T + C - 1) / C;
+  if (o >= 0) {
+    const int G = min(o, NC / 16);
+    return G >= 2 ? G : 1;
+  }
+  const long tiles = (long)B * H * (dv / VTW);
+  if (tiles >= 256) return 1;
+  const int G = min((int)((256 + tiles - 1) / tiles), NC / 16);
+  return G >= 8 ? G : 1;
+}
+
+size_t bwd_split_bytes(int B, int T, int H, int dk, int dv) {
+  const int G = bwd_walk_segments(B, T, H, dk, dv);
+  return G < 2 ? 0 : (size_t)B * H * G * dk * (2 * (size_t)dv + dk) * sizeof(float);
 }
 
 hipError_t launch_bwd(const BwdArgs& a) {

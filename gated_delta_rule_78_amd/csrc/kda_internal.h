@@ -125,9 +125,14 @@ struct BwdLayout {
   }
 };
 
+// Few chains over long sequences: the backward walks split each chain into this many
+// segments (1: one walk per chain), with bwd_split_bytes of scratch after the chunk blocks.
+int bwd_walk_segments(int B, int T, int H, int dk, int dv);
+size_t bwd_split_bytes(int B, int T, int H, int dk, int dv);
+
 inline size_t bwd_workspace_bytes(int B, int T, int H, int dk, int dv) {
   const size_t nchunks = ((size_t)T + 63) / 64;
-  return (size_t)B * H * nchunks * BwdLayout(dk, dv).total * sizeof(float);
+  return (size_t)B * H * nchunks * BwdLayout(dk, dv).total * sizeof(float) + bwd_split_bytes(B, T, H, dk, dv);
 }
 
 hipError_t launch_bwd(const BwdArgs& a);

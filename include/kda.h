@@ -264,7 +264,10 @@ int kda_sfda_decode_tokens(const kda_shape* shape, const void* q, const void* k,
  *   d_initial_state : [B, H, dk, dv] fp32 output, or NULL when not wanted
  *   workspace       : kda_chunk_bwd_workspace_size(shape) bytes of device memory,
  *                     256-byte aligned (about 805 KB per chunk of 64 tokens and head at
- *                     dk = dv = 128); its contents on entry do not matter.
+ *                     dk = dv = 128, plus, for few (b, h) over long sequences, the
+ *                     scratch of the split walks: each chain's state and adjoint walks run
+ *                     as 8 or more parallel segments joined by their affine transfers);
+ *                     its contents on entry do not matter.
  * Supported: dk, dv in {64, 128}, bf16 or fp32 inputs, chunk 0 or 64.  q, k, v, alpha,
  * d_o, the outputs and the states need 16-byte alignment, beta that of its element type
  * (KDA_ERR_ALIGN otherwise).  No output may

@@ -170,3 +170,59 @@ def test_bwd_varlen_single_sequence_equals_fixed():
     torch.cuda.synchronize()
     for x, y in zip(fixed, packed):
         np.testing.assert_array_equal(x.cpu().numpy(), y.cpu().numpy())
+
+
+def _split_inputs(gates, seed, long_memory=False):
+    from gated_delta_rule_78_amd.inputs import bf16_bits
+    T = 64 * 130 + 5   # B1 H2: 8 segments per chain (seven of 17 chunks, one of 12)
+    inp = make(1, T, 2, 128, 128, "bf16", gates, False, seed=seed)
+    dO, dST = make_upstream(1, T, 2, 128, 128, "bf16", seed=seed)
+    S0 = inp.S0
+    if long_memory:   # gates in {1, 1 - 2^-8}, beta <= 0.05: states and adjoints cross segments
+        rng = np.random.default_rng(seed)
+        inp.alpha = bf16_bits(np.where(rng.random(inp.alpha.shape) < 0.5, 1.0, 1.0 - 2.0 ** -8).astype(np.float32))
+        inp.beta = bf16_bits((0.05 * rng.random(inp.beta.shape)).astype(np.float32))
+        S0 = rng.standard_normal(S0.shape).astype(np.float32)
+        dST = rng.standard_normal(dST.shape).astype(np.float32)
+    return inp, dO, dST, S0
+
+
+@pytest.mark.parametrize("long_memory", [False, True])
+def test_bwd_split_walks(long_memory):
+    """Few chains over a long sequence: both walks split each chain into segments (zero
+    start, identity transfer, scan, final walk; the adjoint in reverse), every gradient
+    against the oracle on all heads; the workspace grows by the split's scratch."""
+    import gated_delta_rule_78_amd as kda
+    T = 64 * 130 + 5
+    plain = kda.bwd_workspace_size(1, 64 * 15, 2, 128, 128) // (15 * 2)      # one chunk block
+    assert kda.bwd_workspace_size(1, T, 2, 128, 128) == 131 * 2 * plain + 2 * 8 * 128 * (2 * 128 + 128) * 4
+    inp, dO, dST, S0 = _split_inputs("ckda", 95 + long_memory, long_memory)
+    _check(inp, dO, dST, S0, label="split long memory" if long_memory else "split")
+
+
+def test_bwd_split_walks_gdn2_and_sfda():
+    """The split walks under the Gated DeltaNet-2 write gate and the SFDA rotation."""
+    import gated_delta_rule_78_amd as kda
+    import torch
+    for gates, seed in (("gdn2", 97), ("sfda", 98)):
+        inp, dO, dST, S0 = _split_inputs(gates, seed)
+        q, k, v, a, b = inputs_to_dev(inp)
+        d_o, s0, dst = to_dev(dO, "bf16"), state_to_dev(S0), state_to_dev(dST)
+        print(f"bwd split {gates} T={inp.meta['T']}", flush=True)
+        if gates == "gdn2":
+            out = kda.gdn2_chunk_bwd(q, k, v, a, to_dev(inp.erase, "bf16"), to_dev(inp.write, "bf16"), d_o,
+                                     initial_state=s0, d_final_state=dst)
+            keys = ("dq", "dk", "dv", "dalpha", "derase", "dwrite", "dS0")
+            ref = oracle.bwd_gdn2(inp.q, inp.k, inp.v, inp.alpha, inp.erase, inp.write,
+                                  as_float(dO, "bf16")[0].transpose(1, 0, 2), S0=S0[0], dST=dST[0])
+        else:
+            out = kda.sfda_chunk_bwd(q, k, v, a, b, d_o, initial_state=s0, d_final_state=dst)
+            keys = ("dq", "dk", "dv", "dalpha", "dbeta", "dS0")
+            ref = oracle.bwd_sfda(inp.q, inp.k, inp.v, inp.alpha, inp.beta,
+                                  as_float(dO, "bf16")[0].transpose(1, 0, 2), S0=S0[0], dST=dST[0])
+        torch.cuda.synchronize()
+        for key, x in zip(keys, out):
+            x = x.cpu().numpy()
+            got = x[0] if key == "dS0" else (x[0].transpose(1, 0) if x.ndim == 3 else x[0].transpose(1, 0, 2))
+            e = rel_err_slices(got, ref[key], 2)
+            assert e <= GATE, (gates, key, e)
