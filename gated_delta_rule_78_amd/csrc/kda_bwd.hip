@@ -1828,7 +1828,7 @@ int bwd_walk_segments(int B, int T, int H, int dk, int dv) {
     return G >= 2 ? G : 1;
   }
   const long tiles = (long)B * H * (dv / VTW);
-  if (tiles >= 256) return 1;
+  if (tiles <= 0 || tiles >= 256) return 1;
   const int G = min((int)((256 + tiles - 1) / tiles), NC / 16);
   return G >= 8 ? G : 1;
 }

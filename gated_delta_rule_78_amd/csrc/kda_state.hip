@@ -529,7 +529,7 @@ int state_segments(int B, int T, int H, int dk, int dv, bool bf16) {
     return G >= 2 ? G : 1;
   }
   const long tiles = (long)B * H * (dv / 64);  // 64-column tiles of one walk per chain
-  if (tiles >= 256) return 1;
+  if (tiles <= 0 || tiles >= 256) return 1;
   const int G = min((int)((256 + tiles - 1) / tiles), NC / 16);  // at least 16 chunks per segment
   return G >= 8 ? G : 1;
 }

@@ -114,6 +114,8 @@ def test_workspace_size_and_errors(L):
     assert size(1, 64, 1, 64, 64) < one
     assert size(1, 64, 1, 64, 64, dtype=1) > size(1, 64, 1, 64, 64)
     assert size(1, 0, 3, 128, 128) == 0
+    assert size(0, 8192, 3, 128, 128) == 0            # no (b, h): no records, no split scratch
+    assert L.kda_chunk_bwd_workspace_size(ctypes.byref(kda.Shape(0, 8192, 3, 128, 128, 64, 0))) == 0
     assert size(1, 64, 1, 96, 128) == 0               # unsupported shape
     assert size(1, 64, 1, 128, 128, dtype=1) == 0
     assert L.kda_chunk_fwd_workspace_size(None) == 0
