@@ -358,6 +358,8 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
   // (compute waves, G2) the write gate of this lane's rows 32 ks + 8 g + e and column of
   // chunk c, rows past the end clamped to the last row (their v rows are zero)
   Frag<T> wf[G2 ? 2 : 1];
+#pragma unroll
+  for (int ks = 0; ks < (G2 ? 2 : 1); ++ks) wf[ks].zero();  // stays zero where v reads as zero
   auto load_w = [&](int c) {
     const int t0 = c * C, col = v0 + 16 * wave + n;
 #pragma unroll
@@ -368,7 +370,7 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
         wf[ks].set(e, Elem<T>::load(gw, (row * H + h) * DV + col));
       }
   };
-  if (G2 && nchunks > 0 && !producer) load_w(0);
+  if (G2 && !zero_v && nchunks > 0 && !producer) load_w(0);
   if (nchunks > 0 && producer) issue(0, rec_a, v_a);
   if constexpr (K::NBUF == 2) {
     // chunk c computes from buffers P while the producer streams chunk c + 1 into
@@ -384,7 +386,7 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
         if (c + 1 < nchunks) issue(c + 1, recQ, vQ);
       } else {
         state_chunk<T, DK, VT, G2, CPX>(recP, vP, wf, S, wave, g, n);
-        if (G2 && c + 1 < nchunks) load_w(c + 1);
+        if (G2 && !zero_v && c + 1 < nchunks) load_w(c + 1);
       }
     };
     for (int chunk = 0; chunk < nchunks; chunk += 2) {
@@ -402,7 +404,7 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
       pad_rows(chunk, v_a);
       if (!producer) {
         state_chunk<T, DK, VT, G2, CPX>(rec_a, v_a, wf, S, wave, g, n);
-        if (G2 && chunk + 1 < nchunks) load_w(chunk + 1);
+        if (G2 && !zero_v && chunk + 1 < nchunks) load_w(chunk + 1);
       }
       lds_barrier();
       store_o(chunk, v_a);
@@ -488,23 +490,25 @@ static hipError_t launch_state_t(const ChunkArgs& a, const void* ws) {
 // The split walk (fixed-length bf16 batches at d_k = 128, few (b, h) chains): four launches
 // over G segments per chain, 64 value columns per workgroup, scratch after the records:
 // B [BH G][d_k][d_v], P [BH G][d_k][d_k], segment start states [BH G][d_k][d_v].
+template <bool G2, bool CPX>
 static hipError_t launch_state_split(const ChunkArgs& a, const void* ws, int G) {
-  using K = SCfg<bf16_t, 128, 64, false>;
+  using K = SCfg<bf16_t, 128, 64, G2>;
   const int BH = a.B * a.H, NC = (a.T + C - 1) / C, segc = (NC + G - 1) / G;
   const size_t rec = (size_t)BH * NC * K::RL::BYTES;
   float* Bst = (float*)((char*)ws + rec);
   float* P = Bst + (size_t)BH * G * 128 * a.dv;
   float* Sst = P + (size_t)BH * G * 128 * 128;
   hipStream_t st = (hipStream_t)a.stream;
-  auto kern = chunk_state_kernel<bf16_t, 128, 64, false, false>;
+  auto kern = chunk_state_kernel<bf16_t, 128, 64, G2, CPX>;
   const char* w = (const char*)ws;
+  // (the transfer walk reads neither v nor the write gate: U = M (w o v) = 0)
   hipLaunchKernelGGL(kern, dim3(BH * G * (a.dv / 64)), dim3(K::NT), 0, st, w, a.v, (const float*)nullptr, a.o, Bst,
-                     a.T, a.H, a.dv, BH, nullptr, nullptr, nullptr, 0, G, segc, (int)kSegNoOut);
+                     a.T, a.H, a.dv, BH, a.write, nullptr, nullptr, 0, G, segc, (int)kSegNoOut);
   hipLaunchKernelGGL(kern, dim3(BH * G * 2), dim3(K::NT), 0, st, w, a.v, (const float*)nullptr, a.o, P, a.T, a.H,
-                     128, BH, nullptr, nullptr, nullptr, 0, G, segc, (int)(kSegNoOut | kSegZeroV | kSegIdentity));
+                     128, BH, a.write, nullptr, nullptr, 0, G, segc, (int)(kSegNoOut | kSegZeroV | kSegIdentity));
   hipLaunchKernelGGL(seg_scan_kernel<128>, dim3(BH * (a.dv / 16)), dim3(256), 0, st, a.s0, P, Bst, Sst, G, a.dv);
   hipLaunchKernelGGL(kern, dim3(BH * G * (a.dv / 64)), dim3(K::NT), 0, st, w, a.v, (const float*)Sst, a.o, a.sT,
-                     a.T, a.H, a.dv, BH, nullptr, nullptr, nullptr, 0, G, segc, (int)kSegLastOnly);
+                     a.T, a.H, a.dv, BH, a.write, nullptr, nullptr, 0, G, segc, (int)kSegLastOnly);
   return hipGetLastError();
 }
 
@@ -583,9 +587,12 @@ static hipError_t launch_state_g(const ChunkArgs& a, const void* ws) {
 
 hipError_t launch_state(const ChunkArgs& a, const void* ws) {
   if ((a.cu ? a.n_seqs : a.B) * a.H == 0) return hipSuccess;
-  if (!a.cu && !a.write && !a.cpx) {
+  if (!a.cu) {
     const int G = state_segments(a.B, a.T, a.H, a.dk, a.dv, a.bf16);
-    if (G >= 2) return launch_state_split(a, ws, G);
+    if (G >= 2) {
+      if (a.cpx) return a.write ? hipErrorInvalidValue : launch_state_split<false, true>(a, ws, G);
+      return a.write ? launch_state_split<true, false>(a, ws, G) : launch_state_split<false, false>(a, ws, G);
+    }
   }
   if (a.cpx) return a.write ? hipErrorInvalidValue : launch_state_g<false, true>(a, ws);
   return a.write ? launch_state_g<true>(a, ws) : launch_state_g<false>(a, ws);

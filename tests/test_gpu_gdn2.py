@@ -149,3 +149,11 @@ def test_gdn2_decode_steps_match_chunk_forward():
     f = lambda x: x.float().cpu().numpy().transpose(0, 2, 1, 3).reshape(6, -1)
     assert rel_err_slices(f(od), f(o), 6) <= TOL["bf16"]
     assert rel_err_slices(S.cpu().numpy().reshape(6, -1), sT.cpu().numpy().reshape(6, -1), 6) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dv", [64, 128])
+def test_gdn2_split_state_walk(dv):
+    """B1 H2 T8325: the state pass splits each chain into 8 segments (the transfer walk
+    reads neither v nor the write gate); all heads against the oracle."""
+    inp = make(1, 64 * 130 + 5, 2, 128, dv, "bf16", "gdn2", False, seed=71 + dv)
+    _check(inp, inp.S0, label=f"split dv{dv}")

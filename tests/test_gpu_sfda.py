@@ -171,3 +171,10 @@ def test_sfda_decode_matches_chunk_forward_and_multi_token():
     assert rel_err_slices(S.cpu().numpy().reshape(6, -1), sT.cpu().numpy().reshape(6, -1), 6) <= TOL["bf16"]
     assert rel_err_slices(f(om), f(od), 6) <= 1e-5
     assert rel_err_slices(S2.cpu().numpy().reshape(6, -1), S.cpu().numpy().reshape(6, -1), 6) <= 1e-5
+
+
+def test_sfda_split_state_walk():
+    """B1 H2 T8325: the state pass splits each chain into 8 segments under the complex
+    rotation-decay gates; all heads against the oracle."""
+    inp = make(1, 64 * 130 + 5, 2, 128, 128, "bf16", "sfda", False, seed=73)
+    _check(inp, inp.S0, label="split")
