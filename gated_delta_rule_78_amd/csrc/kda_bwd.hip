@@ -155,6 +155,54 @@ __device__ __forceinline__ f32x4_t zero4f() {
   f32x4_t z = {0.f, 0.f, 0.f, 0.f};
   return z;
 }
+// Raw input words held in registers between a load and its use one step later: widening
+// bf16 at the load would make the load's wait come at once, ahead of the matrix work.
+template <typename T>
+struct RawIn;
+template <>
+struct RawIn<bf16_t> {
+  using v4 = uint2;
+  using s1 = uint32_t;
+  static __device__ __forceinline__ v4 load4(const void* p, size_t i) { return *(const uint2*)((const uint16_t*)p + i); }
+  static __device__ __forceinline__ s1 load1(const void* p, size_t i) { return ((const uint16_t*)p)[i]; }
+  static __device__ __forceinline__ f32x4_t widen(v4 w) {
+    f32x4_t r = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u), __uint_as_float(w.y << 16),
+                 __uint_as_float(w.y & 0xFFFF0000u)};
+    return r;
+  }
+  static __device__ __forceinline__ float widen(s1 b) { return __uint_as_float(b << 16); }
+};
+template <>
+struct RawIn<float> {
+  using v4 = f32x4_t;
+  using s1 = float;
+  static __device__ __forceinline__ v4 load4(const void* p, size_t i) { return *(const f32x4_t*)((const float*)p + i); }
+  static __device__ __forceinline__ s1 load1(const void* p, size_t i) { return ((const float*)p)[i]; }
+  static __device__ __forceinline__ f32x4_t widen(v4 w) { return w; }
+  static __device__ __forceinline__ float widen(s1 b) { return b; }
+};
+
+// Keeps the scheduler from moving instructions across this point: LDS reads issued before it
+// stay ahead of the matrix-core work after it.
+__device__ __forceinline__ void sched_fence() {
+#ifndef KDA_HOST_PASS
+  __builtin_amdgcn_sched_barrier(0);
+#endif
+}
+// acc += sum_t A[4 slots] B[4 slots] over one 16-wide slice of the contraction
+__device__ __forceinline__ void mfma4v(f32x4_t& acc, const f32x4_t& av, const float* bv) {
+#ifndef KDA_HOST_PASS
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[t], bv[t], acc, 0, 0, 0);
+#endif
+}
+__device__ __forceinline__ void mfma4v(f32x4_t& acc, const f32x4_t& av, const f32x4_t& bv) {
+#ifndef KDA_HOST_PASS
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[t], bv[t], acc, 0, 0, 0);
+#endif
+}
+
 
 // acc += sgn * A[row][k0 .. k0 + 15] B[k0 .. k0 + 15][n], this lane's A row in LDS at `arow`,
 // fb(t) = B[k0 + 4 g + t][n]
@@ -712,7 +760,7 @@ template <typename T, int DK, bool G2, bool CPX>
 __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC, WalkSplit sp) {
   constexpr int LM = C + 4, LW = DK + 4, LV = VTW + 4;
   constexpr int NM = C * C / 4 / NT, NW = C * DK / 4 / NT, NV = C * VTW / 4 / NT;
-  __shared__ float sM[C * LM], sW[C * LW], sKrT[DK * LM], sV[C * LV], sGl[DK];
+  __shared__ __attribute__((aligned(16))) float sM[C * LM], sW[C * LW], sKrT[DK * LM], sV[C * LV], sGl[DK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, g = lane >> 4;
   const bool split = sp.nseg > 1;
   const int dv = a.Dv, cols = split ? sp.cols : dv, ntile = cols / VTW;
@@ -736,24 +784,35 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC, WalkSp
       else
         S[I][r] = a.s0 ? a.s0[((size_t)bh * DK + row) * dv + col] : 0.f;
     }
+#ifndef KDA_HOST_PASS
+  // the start values are in registers before the walk: otherwise the compiler keeps their
+  // loads pending into the loop and waits on every outstanding load at the first store
+  __builtin_amdgcn_s_waitcnt(0);
+#endif
   // one chunk's operands in registers: M; W; K o rho; V and beta (or, Gated DeltaNet-2,
   // the write gate w: M (w o V)); gamma_last.  Step st
   // moves chunk st - 1 from registers to LDS, issues the loads of chunk st, then computes
   // chunk st - 1 while they are in flight.
-  float4 pm[NM], pw[NW], pk[NW], pv[NV], pwg[G2 ? NV : 1];
-  float pb[NV], pg = 0.f;
+  using RI = RawIn<T>;
+  f32x4_t pm[NM], pw[NW], pk[NW];
+  typename RI::v4 pv[NV], pwg[G2 ? NV : 1];
+  typename RI::s1 pb[NV];
+  float pg = 0.f;
+  int plen = 0;  // rows of the loaded v tile that are inside the chunk (0: v read as zero)
+  size_t wnext = 0;  // workspace slot of the chunk loaded last (chunk tables are read once)
   for (int st = 0; st <= nch; ++st) {
+    const size_t wcur = wnext;
     if (st > 0) {
       __syncthreads();  // the previous chunk's LDS reads are done
 #pragma unroll
       for (int it = 0; it < NM; ++it) {
         const int x = tid + it * NT, i = x / (C / 4), j = 4 * (x % (C / 4));
-        *(float4*)(sM + i * LM + j) = pm[it];
+        *(f32x4_t*)(sM + i * LM + j) = pm[it];
       }
 #pragma unroll
       for (int it = 0; it < NW; ++it) {
         const int x = tid + it * NT, i = x / (DK / 4), c = 4 * (x % (DK / 4));
-        *(float4*)(sW + i * LW + c) = pw[it];
+        *(f32x4_t*)(sW + i * LW + c) = pw[it];
         sKrT[(c + 0) * LM + i] = pk[it].x;
         sKrT[(c + 1) * LM + i] = pk[it].y;
         sKrT[(c + 2) * LM + i] = pk[it].z;
@@ -762,11 +821,12 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC, WalkSp
 #pragma unroll
       for (int it = 0; it < NV; ++it) {
         const int x = tid + it * NT, j = x / (VTW / 4), c = 4 * (x % (VTW / 4));
+        const bool in = j < plen;
         if (G2) {
-          *(float4*)(sV + j * LV + c) = mul4(pv[it], pwg[G2 ? it : 0]);
+          *(f32x4_t*)(sV + j * LV + c) = in ? RI::widen(pv[it]) * RI::widen(pwg[G2 ? it : 0]) : zero4f();
         } else {
-          const float b = pb[it];
-          *(float4*)(sV + j * LV + c) = make_float4(pv[it].x * b, pv[it].y * b, pv[it].z * b, pv[it].w * b);
+          const float b = RI::widen(pb[it]);
+          *(f32x4_t*)(sV + j * LV + c) = in ? RI::widen(pv[it]) * b : zero4f();
         }
       }
       if (tid < DK) sGl[tid] = pg;
@@ -775,82 +835,112 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC, WalkSp
     if (st < nch) {
       size_t wsl;
       const ChunkGeom cg = chain_chunk(a, NC, bh, c0 + st, &wsl);
+      wnext = wsl;
       const float* cl = a.ws + wsl * L.total;
       const size_t vb = row0(cg, a.T, a.H, dv), vs = (size_t)a.H * dv;
       const size_t bb = ((size_t)cg.b * a.T + cg.t0) * a.H + cg.h;
-      const int vlen = zero_in ? 0 : cg.len;  // the transfer walk reads v as zero
+      // loads are unconditional (rows past the chunk clamped to its last row, masked when
+      // staged), so that no wait on them is forced before the chunk's products
+      plen = zero_in ? 0 : cg.len;  // the transfer walk reads v as zero
+      const int lastr = max(cg.len - 1, 0);
 #pragma unroll
       for (int it = 0; it < NM; ++it) {
         const int x = tid + it * NT, i = x / (C / 4), j = 4 * (x % (C / 4));
-        pm[it] = *(const float4*)(cl + L.M + i * C + j);
+        pm[it] = *(const f32x4_t*)(cl + L.M + i * C + j);
       }
 #pragma unroll
       for (int it = 0; it < NW; ++it) {
         const int x = tid + it * NT, i = x / (DK / 4), c = 4 * (x % (DK / 4));
-        pw[it] = *(const float4*)(cl + L.W + i * DK + c);
-        pk[it] = *(const float4*)(cl + L.KR + i * DK + c);
+        pw[it] = *(const f32x4_t*)(cl + L.W + i * DK + c);
+        pk[it] = *(const f32x4_t*)(cl + L.KR + i * DK + c);
       }
 #pragma unroll
       for (int it = 0; it < NV; ++it) {
         const int x = tid + it * NT, j = x / (VTW / 4), c = 4 * (x % (VTW / 4));
-        const bool in = j < vlen;
-        pv[it] = in ? ld4<T>(a.v, vb + j * vs + v0 + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const int jr = min(j, lastr);
+        pv[it] = RI::load4(a.v, vb + jr * vs + v0 + c);
         if (G2)
-          pwg[G2 ? it : 0] = in ? ld4<T>(a.write, vb + j * vs + v0 + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+          pwg[G2 ? it : 0] = RI::load4(a.write, vb + jr * vs + v0 + c);
         else
-          pb[it] = in ? Elem<T>::load(a.beta, bb + (size_t)j * a.H) : 0.f;
+          pb[it] = RI::load1(a.beta, bb + (size_t)jr * a.H);
       }
-      if (tid < DK) pg = cl[L.gam + (C - 1) * DK + tid];
+      pg = cl[L.gam + (C - 1) * DK + min(tid, DK - 1)];  // unconditional: no branch around the load
     }
     if (st == 0) continue;
     const int nc = st - 1;
-    size_t wsc;
-    chain_chunk(a, NC, bh, c0 + nc, &wsc);
-    float* ch = a.ws + wsc * L.total;
+    float* ch = a.ws + wcur * L.total;
     if (!no_write) {
 #pragma unroll
       for (int I = 0; I < DK / 16; ++I)
 #pragma unroll
         for (int r = 0; r < 4; ++r) ch[L.S + (16 * I + 4 * g + r) * dv + col] = S[I][r];
     }
-    // Delta = M (beta o V) - W S
+    // Delta = M (beta o V) - W S, then S' = gamma_L o S + (K o rho)^T Delta, one row block
+    // at a time.  With one wave per SIMD nothing else hides the LDS latency, so the A
+    // operands of the next block are read while the current one multiplies.
+    float bvv[4][4];  // B operands shared by every row block: this wave's columns of beta o V
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) bvv[q][t] = sV[(16 * q + 4 * g + t) * LV + 16 * wave + n];
+    f32x4_t am[2][4], aw[2][DK / 16], ak[2][4], agl[2];
+    auto load_d = [&](int b, int I) {
+      const float* mrow = sM + (16 * I + n) * LM + 4 * g;
+      const float* wrow = sW + (16 * I + n) * LW + 4 * g;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) am[b][q] = *(const f32x4_t*)(mrow + 16 * q);
+#pragma unroll
+      for (int kt = 0; kt < DK / 16; ++kt) aw[b][kt] = *(const f32x4_t*)(wrow + 16 * kt);
+    };
+    auto load_s = [&](int b, int I) {
+      const float* krow = sKrT + (16 * I + n) * LM + 4 * g;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) ak[b][kt] = *(const f32x4_t*)(krow + 16 * kt);
+      agl[b] = *(const f32x4_t*)(sGl + 16 * I + 4 * g);
+    };
+    load_d(0, 0);
+    sched_fence();
     f32x4_t Dl[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-      f32x4_t acc = zero4f();
-      const float* mrow = sM + (16 * I + n) * LM;
+      if (I + 1 < 4)
+        load_d((I + 1) & 1, I + 1);
+      else
+        load_s(0, 0);
+      sched_fence();
+      f32x4_t acc = zero4f(), accw = zero4f();
 #pragma unroll
-      for (int k0 = 0; k0 < C; k0 += 16)
-        mm16(acc, mrow, k0, [&](int t) { return sV[(k0 + 4 * g + t) * LV + 16 * wave + n]; });
-      const float* wrow = sW + (16 * I + n) * LW;
+      for (int q = 0; q < 4; ++q) mfma4v(acc, am[I & 1][q], bvv[q]);
 #pragma unroll
-      for (int kt = 0; kt < DK / 16; ++kt) mm16(acc, wrow, 16 * kt, [&](int t) { return S[kt][t]; }, -1.f);
-      Dl[I] = acc;
+      for (int kt = 0; kt < DK / 16; ++kt) mfma4v(accw, aw[I & 1][kt], S[kt]);
+      Dl[I] = acc - accw;
+      sched_fence();
       if (!no_write) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ch[L.DL + (16 * I + 4 * g + r) * dv + col] = acc[r];
+        for (int r = 0; r < 4; ++r) ch[L.DL + (16 * I + 4 * g + r) * dv + col] = Dl[I][r];
       }
     }
     if (nc + 1 < nch || sp.end) {
-      // S' = gamma_L o S + (K o rho)^T Delta
 #pragma unroll
       for (int I = 0; I < DK / 16; ++I) {
+        if (I + 1 < DK / 16) load_s((I + 1) & 1, I + 1);
+        sched_fence();
         f32x4_t acc = zero4f();
-        const float* krow = sKrT + (16 * I + n) * LM;
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) mm16(acc, krow, 16 * kt, [&](int t) { return Dl[kt][t]; });
+        for (int kt = 0; kt < 4; ++kt) mfma4v(acc, ak[I & 1][kt], Dl[kt]);
+        const f32x4_t gl = agl[I & 1];
         if constexpr (CPX) {
 #pragma unroll
           for (int r = 0; r < 4; r += 2) {
-            const cf gl = {sGl[16 * I + 4 * g + r], sGl[16 * I + 4 * g + r + 1]};
-            const cf z = cmul(gl, cf{S[I][r], S[I][r + 1]});
+            const cf z = cmul(cf{gl[r], gl[r + 1]}, cf{S[I][r], S[I][r + 1]});
             S[I][r] = z.x + acc[r];
             S[I][r + 1] = z.y + acc[r + 1];
           }
         } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) S[I][r] = sGl[16 * I + 4 * g + r] * S[I][r] + acc[r];
+          for (int r = 0; r < 4; ++r) S[I][r] = gl[r] * S[I][r] + acc[r];
         }
+        sched_fence();
       }
     }
   }
@@ -871,7 +961,7 @@ template <typename T, int DK, bool CPX>
 __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC, WalkSplit sp) {
   constexpr int LK = DK + 4, LM = C + 4, LV = VTW + 4;
   constexpr int NM = C * C / 4 / NT, NW = C * DK / 4 / NT, NV = C * VTW / 4 / NT;
-  __shared__ float sKr[C * LK], sAT[C * LM], sQgT[DK * LM], sWT[DK * LM], sO[C * LV], sGl[DK];
+  __shared__ __attribute__((aligned(16))) float sKr[C * LK], sAT[C * LM], sQgT[DK * LM], sWT[DK * LM], sO[C * LV], sGl[DK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, g = lane >> 4;
   const bool split = sp.nseg > 1;
   const int dv = a.Dv, cols = split ? sp.cols : dv, ntile = cols / VTW;
@@ -895,18 +985,28 @@ __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC, Walk
       else
         dS[I][r] = a.dsT ? a.dsT[((size_t)bh * DK + row) * dv + col] : 0.f;
     }
+#ifndef KDA_HOST_PASS
+  // the start values are in registers before the walk: otherwise the compiler keeps their
+  // loads pending into the loop and waits on every outstanding load at the first store
+  __builtin_amdgcn_s_waitcnt(0);
+#endif
   // one chunk's operands in registers: K o rho; Q o gamma; W; A; dO; gamma_last.  Step st
   // moves chunk nch - st from registers to LDS, issues the loads of chunk nch - 1 - st,
   // then computes chunk nch - st while they are in flight.
-  float4 pk[NW], pq[NW], pw[NW], pa[NM], po[NV];
+  using RI = RawIn<T>;
+  f32x4_t pk[NW], pq[NW], pw[NW], pa[NM];
+  typename RI::v4 po[NV];
   float pg = 0.f;
+  int plen = 0;  // rows of the loaded dO tile that are inside the chunk (0: dO read as zero)
+  size_t wnext = 0;  // workspace slot of the chunk loaded last (chunk tables are read once)
   for (int st = 0; st <= nch; ++st) {
+    const size_t wcur = wnext;
     if (st > 0) {
       __syncthreads();
 #pragma unroll
       for (int it = 0; it < NW; ++it) {
         const int x = tid + it * NT, i = x / (DK / 4), c = 4 * (x % (DK / 4));
-        *(float4*)(sKr + i * LK + c) = pk[it];
+        *(f32x4_t*)(sKr + i * LK + c) = pk[it];
         sQgT[(c + 0) * LM + i] = pq[it].x;
         sQgT[(c + 1) * LM + i] = pq[it].y;
         sQgT[(c + 2) * LM + i] = pq[it].z;
@@ -927,7 +1027,7 @@ __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC, Walk
 #pragma unroll
       for (int it = 0; it < NV; ++it) {
         const int x = tid + it * NT, i = x / (VTW / 4), c = 4 * (x % (VTW / 4));
-        *(float4*)(sO + i * LV + c) = po[it];
+        *(f32x4_t*)(sO + i * LV + c) = i < plen ? RI::widen(po[it]) : zero4f();
       }
       if (tid < DK) sGl[tid] = pg;
       __syncthreads();
@@ -936,79 +1036,109 @@ __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC, Walk
       const int ld = c0 + nch - 1 - st;
       size_t wsl;
       const ChunkGeom cg = chain_chunk(a, NC, bh, ld, &wsl);
+      wnext = wsl;
       const float* cl = a.ws + wsl * L.total;
       const size_t vb = row0(cg, a.T, a.H, dv), vs = (size_t)a.H * dv;
+      plen = zero_in ? 0 : cg.len;  // unconditional loads, rows past the chunk clamped and masked when staged
+      const int lastr = max(cg.len - 1, 0);
 #pragma unroll
       for (int it = 0; it < NW; ++it) {
         const int x = tid + it * NT, i = x / (DK / 4), c = 4 * (x % (DK / 4));
-        pk[it] = *(const float4*)(cl + L.KR + i * DK + c);
-        pq[it] = *(const float4*)(cl + L.QG + i * DK + c);
-        pw[it] = *(const float4*)(cl + L.W + i * DK + c);
+        pk[it] = *(const f32x4_t*)(cl + L.KR + i * DK + c);
+        pq[it] = *(const f32x4_t*)(cl + L.QG + i * DK + c);
+        pw[it] = *(const f32x4_t*)(cl + L.W + i * DK + c);
       }
 #pragma unroll
       for (int it = 0; it < NM; ++it) {
         const int x = tid + it * NT, j = x / (C / 4), i = 4 * (x % (C / 4));
-        pa[it] = *(const float4*)(cl + L.A + j * C + i);
+        pa[it] = *(const f32x4_t*)(cl + L.A + j * C + i);
       }
 #pragma unroll
       for (int it = 0; it < NV; ++it) {
         const int x = tid + it * NT, i = x / (VTW / 4), c = 4 * (x % (VTW / 4));
-        po[it] = i < cg.len && !zero_in ? ld4<T>(a.dO, vb + i * vs + v0 + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+        po[it] = RI::load4(a.dO, vb + min(i, lastr) * vs + v0 + c);
       }
-      if (tid < DK) pg = cl[L.gam + (C - 1) * DK + tid];
+      pg = cl[L.gam + (C - 1) * DK + min(tid, DK - 1)];  // unconditional: no branch around the load
     }
     if (st == 0) continue;
-    const int nc = c0 + nch - st;
-    size_t wsc;
-    chain_chunk(a, NC, bh, nc, &wsc);
-    float* ch = a.ws + wsc * L.total;
+    float* ch = a.ws + wcur * L.total;  // chunk c0 + nch - st
     if (!no_write) {
 #pragma unroll
       for (int I = 0; I < DK / 16; ++I)
 #pragma unroll
         for (int r = 0; r < 4; ++r) ch[L.DS + (16 * I + 4 * g + r) * dv + col] = dS[I][r];
     }
-    // dDelta = (K o rho) dS' + A^T dO
+    // dDelta = (K o rho) dS' + A^T dO, then dS = gamma_L o dS' + (Q o gamma)^T dO - W^T dDelta,
+    // one row block at a time, the A operands of the next block read while the current
+    // one multiplies (one wave per SIMD: nothing else hides the LDS latency).
+    float bo[4][4];  // B operands shared by every row block: this wave's columns of dO
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) bo[q][t] = sO[(16 * q + 4 * g + t) * LV + 16 * wave + n];
+    f32x4_t akr[2][DK / 16], aat[2][4], aq[2][4], awt[2][4], agl[2];
+    auto load_a = [&](int b, int I) {
+      const float* krow = sKr + (16 * I + n) * LK + 4 * g;
+      const float* arow = sAT + (16 * I + n) * LM + 4 * g;
+#pragma unroll
+      for (int kt = 0; kt < DK / 16; ++kt) akr[b][kt] = *(const f32x4_t*)(krow + 16 * kt);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) aat[b][q] = *(const f32x4_t*)(arow + 16 * q);
+    };
+    auto load_b = [&](int b, int I) {
+      const float* qrow = sQgT + (16 * I + n) * LM + 4 * g;
+      const float* wrow = sWT + (16 * I + n) * LM + 4 * g;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) aq[b][q] = *(const f32x4_t*)(qrow + 16 * q);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) awt[b][kt] = *(const f32x4_t*)(wrow + 16 * kt);
+      agl[b] = *(const f32x4_t*)(sGl + 16 * I + 4 * g);
+    };
+    load_a(0, 0);
+    sched_fence();
     f32x4_t dD[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
+      if (I + 1 < 4)
+        load_a((I + 1) & 1, I + 1);
+      else
+        load_b(0, 0);
+      sched_fence();
       f32x4_t acc = zero4f();
-      const float* krow = sKr + (16 * I + n) * LK;
 #pragma unroll
-      for (int kt = 0; kt < DK / 16; ++kt) mm16(acc, krow, 16 * kt, [&](int t) { return dS[kt][t]; });
-      const float* arow = sAT + (16 * I + n) * LM;
+      for (int kt = 0; kt < DK / 16; ++kt) mfma4v(acc, akr[I & 1][kt], dS[kt]);
 #pragma unroll
-      for (int k0 = 0; k0 < C; k0 += 16)
-        mm16(acc, arow, k0, [&](int t) { return sO[(k0 + 4 * g + t) * LV + 16 * wave + n]; });
+      for (int q = 0; q < 4; ++q) mfma4v(acc, aat[I & 1][q], bo[q]);
       dD[I] = acc;
+      sched_fence();
       if (!no_write) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) ch[L.DDL + (16 * I + 4 * g + r) * dv + col] = acc[r];
       }
     }
-    // dS = gamma_L o dS' + (Q o gamma)^T dO - W^T dDelta
 #pragma unroll
     for (int I = 0; I < DK / 16; ++I) {
-      f32x4_t acc = zero4f();
-      const float* qrow = sQgT + (16 * I + n) * LM;
+      if (I + 1 < DK / 16) load_b((I + 1) & 1, I + 1);
+      sched_fence();
+      f32x4_t acc = zero4f(), accw = zero4f();
 #pragma unroll
-      for (int k0 = 0; k0 < C; k0 += 16)
-        mm16(acc, qrow, k0, [&](int t) { return sO[(k0 + 4 * g + t) * LV + 16 * wave + n]; });
-      const float* wrow = sWT + (16 * I + n) * LM;
+      for (int q = 0; q < 4; ++q) mfma4v(acc, aq[I & 1][q], bo[q]);
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) mm16(acc, wrow, 16 * kt, [&](int t) { return dD[kt][t]; }, -1.f);
+      for (int kt = 0; kt < 4; ++kt) mfma4v(accw, awt[I & 1][kt], dD[kt]);
+      acc -= accw;
+      const f32x4_t gl = agl[I & 1];
       if constexpr (CPX) {
 #pragma unroll
         for (int r = 0; r < 4; r += 2) {
-          const cf gl = {sGl[16 * I + 4 * g + r], sGl[16 * I + 4 * g + r + 1]};
-          const cf z = cmulc(cf{dS[I][r], dS[I][r + 1]}, gl);
+          const cf z = cmulc(cf{dS[I][r], dS[I][r + 1]}, cf{gl[r], gl[r + 1]});
           dS[I][r] = z.x + acc[r];
           dS[I][r + 1] = z.y + acc[r + 1];
         }
       } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dS[I][r] = sGl[16 * I + 4 * g + r] * dS[I][r] + acc[r];
+        for (int r = 0; r < 4; ++r) dS[I][r] = gl[r] * dS[I][r] + acc[r];
       }
+      sched_fence();
     }
   }
   if (sp.end) {
