@@ -40,6 +40,7 @@ namespace kda {
 namespace {
 
 constexpr int NT = 256;   // threads per workgroup of the walks
+constexpr int NTW = 512;  // threads per workgroup of the state walk (two waves per 16 columns)
 constexpr int NTG = 512;  // threads per workgroup of the gradient kernel and, at d_k = 128, of the
                           // records kernel (two waves per SIMD)
 
@@ -757,11 +758,14 @@ enum : int { kWNoWrite = 1, kWZeroIn = 2, kWIdentity = 4 };
 // CPX: SFDA complex gates -- gamma_L multiplies the state's row pairs (2p, 2p+1), which
 // are registers r, r + 1 (r even) of one lane.
 template <typename T, int DK, bool G2, bool CPX>
-__global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC, WalkSplit sp) {
+__global__ __launch_bounds__(NTW) void bwd_state_kernel(BwdArgs a, int NC, WalkSplit sp) {
   constexpr int LM = C + 4, LW = DK + 4, LV = VTW + 4;
-  constexpr int NM = C * C / 4 / NT, NW = C * DK / 4 / NT, NV = C * VTW / 4 / NT;
+  constexpr int NM = C * C / 4 / NTW, NW = C * DK / 4 / NTW, NV = C * VTW / 4 / NTW;
+  constexpr int NH = DK / 32;  // state row blocks per wave: two waves share 16 columns
   __shared__ __attribute__((aligned(16))) float sM[C * LM], sW[C * LW], sKrT[DK * LM], sV[C * LV], sGl[DK];
+  __shared__ __attribute__((aligned(16))) f32x4_t sX[8 * 4 * 64];  // partial Delta of each wave
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, g = lane >> 4;
+  const int cw = wave & 3, hh = wave >> 2;  // column slice; half of the state rows (blocks hh NH ..)
   const bool split = sp.nseg > 1;
   const int dv = a.Dv, cols = split ? sp.cols : dv, ntile = cols / VTW;
   const int cs = blockIdx.x / ntile, v0 = (blockIdx.x % ntile) * VTW;  // cs: chain (and segment)
@@ -769,14 +773,14 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC, WalkSp
   const int c0 = seg * sp.segc, nall = chain_chunks(a, NC, bh);
   const int nch = split ? max(0, min(sp.segc, nall - c0)) : nall;
   const bool zero_in = sp.flags & kWZeroIn, no_write = sp.flags & kWNoWrite;
-  const int col = v0 + 16 * wave + n;  // this lane's state column
+  const int col = v0 + 16 * cw + n;  // this lane's state column
   const BwdLayout L(DK, dv);
-  f32x4_t S[DK / 16];
+  f32x4_t S[NH];  // rows of blocks hh NH + I
 #pragma unroll
-  for (int I = 0; I < DK / 16; ++I)
+  for (int I = 0; I < NH; ++I)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = 16 * I + 4 * g + r;
+      const int row = 16 * (hh * NH + I) + 4 * g + r;
       if (sp.flags & kWIdentity)
         S[I][r] = row == col ? 1.f : 0.f;
       else if (split)
@@ -806,12 +810,12 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC, WalkSp
       __syncthreads();  // the previous chunk's LDS reads are done
 #pragma unroll
       for (int it = 0; it < NM; ++it) {
-        const int x = tid + it * NT, i = x / (C / 4), j = 4 * (x % (C / 4));
+        const int x = tid + it * NTW, i = x / (C / 4), j = 4 * (x % (C / 4));
         *(f32x4_t*)(sM + i * LM + j) = pm[it];
       }
 #pragma unroll
       for (int it = 0; it < NW; ++it) {
-        const int x = tid + it * NT, i = x / (DK / 4), c = 4 * (x % (DK / 4));
+        const int x = tid + it * NTW, i = x / (DK / 4), c = 4 * (x % (DK / 4));
         *(f32x4_t*)(sW + i * LW + c) = pw[it];
         sKrT[(c + 0) * LM + i] = pk[it].x;
         sKrT[(c + 1) * LM + i] = pk[it].y;
@@ -820,7 +824,7 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC, WalkSp
       }
 #pragma unroll
       for (int it = 0; it < NV; ++it) {
-        const int x = tid + it * NT, j = x / (VTW / 4), c = 4 * (x % (VTW / 4));
+        const int x = tid + it * NTW, j = x / (VTW / 4), c = 4 * (x % (VTW / 4));
         const bool in = j < plen;
         if (G2) {
           *(f32x4_t*)(sV + j * LV + c) = in ? RI::widen(pv[it]) * RI::widen(pwg[G2 ? it : 0]) : zero4f();
@@ -845,18 +849,18 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC, WalkSp
       const int lastr = max(cg.len - 1, 0);
 #pragma unroll
       for (int it = 0; it < NM; ++it) {
-        const int x = tid + it * NT, i = x / (C / 4), j = 4 * (x % (C / 4));
+        const int x = tid + it * NTW, i = x / (C / 4), j = 4 * (x % (C / 4));
         pm[it] = *(const f32x4_t*)(cl + L.M + i * C + j);
       }
 #pragma unroll
       for (int it = 0; it < NW; ++it) {
-        const int x = tid + it * NT, i = x / (DK / 4), c = 4 * (x % (DK / 4));
+        const int x = tid + it * NTW, i = x / (DK / 4), c = 4 * (x % (DK / 4));
         pw[it] = *(const f32x4_t*)(cl + L.W + i * DK + c);
         pk[it] = *(const f32x4_t*)(cl + L.KR + i * DK + c);
       }
 #pragma unroll
       for (int it = 0; it < NV; ++it) {
-        const int x = tid + it * NT, j = x / (VTW / 4), c = 4 * (x % (VTW / 4));
+        const int x = tid + it * NTW, j = x / (VTW / 4), c = 4 * (x % (VTW / 4));
         const int jr = min(j, lastr);
         pv[it] = RI::load4(a.v, vb + jr * vs + v0 + c);
         if (G2)
@@ -871,32 +875,34 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC, WalkSp
     float* ch = a.ws + wcur * L.total;
     if (!no_write) {
 #pragma unroll
-      for (int I = 0; I < DK / 16; ++I)
+      for (int I = 0; I < NH; ++I)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ch[L.S + (16 * I + 4 * g + r) * dv + col] = S[I][r];
+        for (int r = 0; r < 4; ++r) ch[L.S + (16 * (hh * NH + I) + 4 * g + r) * dv + col] = S[I][r];
     }
-    // Delta = M (beta o V) - W S, then S' = gamma_L o S + (K o rho)^T Delta, one row block
-    // at a time.  With one wave per SIMD nothing else hides the LDS latency, so the A
-    // operands of the next block are read while the current one multiplies.
-    float bvv[4][4];  // B operands shared by every row block: this wave's columns of beta o V
+    // Delta = M (beta o V) - W S, then S' = gamma_L o S + (K o rho)^T Delta.  The two waves
+    // of a column slice each hold half of the state rows: each forms the part of Delta
+    // over its rows (and half of M (beta o V)), the parts meet through LDS, and each
+    // advances its own rows.  The A operands of the next row block are read from LDS while
+    // the current one multiplies.
+    float bvv[2][4];  // B operands shared by every row block: this wave's columns of beta o V
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < 2; ++q)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) bvv[q][t] = sV[(16 * q + 4 * g + t) * LV + 16 * wave + n];
-    f32x4_t am[2][4], aw[2][DK / 16], ak[2][4], agl[2];
+      for (int t = 0; t < 4; ++t) bvv[q][t] = sV[(16 * (2 * hh + q) + 4 * g + t) * LV + 16 * cw + n];
+    f32x4_t am[2][2], aw[2][NH], ak[2][4], agl[2];
     auto load_d = [&](int b, int I) {
-      const float* mrow = sM + (16 * I + n) * LM + 4 * g;
-      const float* wrow = sW + (16 * I + n) * LW + 4 * g;
+      const float* mrow = sM + (16 * I + n) * LM + 4 * g + 32 * hh;
+      const float* wrow = sW + (16 * I + n) * LW + 4 * g + 16 * NH * hh;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) am[b][q] = *(const f32x4_t*)(mrow + 16 * q);
+      for (int q = 0; q < 2; ++q) am[b][q] = *(const f32x4_t*)(mrow + 16 * q);
 #pragma unroll
-      for (int kt = 0; kt < DK / 16; ++kt) aw[b][kt] = *(const f32x4_t*)(wrow + 16 * kt);
+      for (int kt = 0; kt < NH; ++kt) aw[b][kt] = *(const f32x4_t*)(wrow + 16 * kt);
     };
-    auto load_s = [&](int b, int I) {
-      const float* krow = sKrT + (16 * I + n) * LM + 4 * g;
+    auto load_s = [&](int b, int I) {  // I: this wave's row block (global block hh NH + I)
+      const float* krow = sKrT + (16 * (hh * NH + I) + n) * LM + 4 * g;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) ak[b][kt] = *(const f32x4_t*)(krow + 16 * kt);
-      agl[b] = *(const f32x4_t*)(sGl + 16 * I + 4 * g);
+      agl[b] = *(const f32x4_t*)(sGl + 16 * (hh * NH + I) + 4 * g);
     };
     load_d(0, 0);
     sched_fence();
@@ -910,20 +916,31 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC, WalkSp
       sched_fence();
       f32x4_t acc = zero4f(), accw = zero4f();
 #pragma unroll
-      for (int q = 0; q < 4; ++q) mfma4v(acc, am[I & 1][q], bvv[q]);
+      for (int q = 0; q < 2; ++q) mfma4v(acc, am[I & 1][q], bvv[q]);
 #pragma unroll
-      for (int kt = 0; kt < DK / 16; ++kt) mfma4v(accw, aw[I & 1][kt], S[kt]);
+      for (int kt = 0; kt < NH; ++kt) mfma4v(accw, aw[I & 1][kt], S[kt]);
       Dl[I] = acc - accw;
+      sX[(wave * 4 + I) * 64 + lane] = Dl[I];
       sched_fence();
-      if (!no_write) {
+    }
+    __syncthreads();  // both halves' parts of Delta are in LDS
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ch[L.DL + (16 * I + 4 * g + r) * dv + col] = Dl[I][r];
-      }
+    for (int I = 0; I < 4; ++I) {
+      const f32x4_t o = sX[((wave ^ 4) * 4 + I) * 64 + lane];
+      Dl[I] = hh == 0 ? Dl[I] + o : o + Dl[I];  // the same sum, in the same order, in both halves
+    }
+    if (!no_write) {
+#pragma unroll
+      for (int I = 0; I < 4; ++I)
+        if ((I >> 1) == hh) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ch[L.DL + (16 * I + 4 * g + r) * dv + col] = Dl[I][r];
+        }
     }
     if (nc + 1 < nch || sp.end) {
 #pragma unroll
-      for (int I = 0; I < DK / 16; ++I) {
-        if (I + 1 < DK / 16) load_s((I + 1) & 1, I + 1);
+      for (int I = 0; I < NH; ++I) {
+        if (I + 1 < NH) load_s((I + 1) & 1, I + 1);
         sched_fence();
         f32x4_t acc = zero4f();
 #pragma unroll
@@ -946,9 +963,9 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(BwdArgs a, int NC, WalkSp
   }
   if (sp.end) {
 #pragma unroll
-    for (int I = 0; I < DK / 16; ++I)
+    for (int I = 0; I < NH; ++I)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sp.end[((size_t)cs * DK + 16 * I + 4 * g + r) * cols + col] = S[I][r];
+      for (int r = 0; r < 4; ++r) sp.end[((size_t)cs * DK + 16 * (hh * NH + I) + 4 * g + r) * cols + col] = S[I][r];
   }
 }
 
@@ -1908,7 +1925,7 @@ static hipError_t launch_bwd_dk(const BwdArgs& a, int NC) {
   }
   const int G = a.ctab ? 1 : bwd_walk_segments(a.B, a.T, a.H, a.Dk, a.Dv);
   if (G < 2) {
-    if (per_chunk > 0) hipLaunchKernelGGL((bwd_state_kernel<T, DK, G2, CPX>), dim3(walks), dim3(NT), 0, st, a, NC, WalkSplit{});
+    if (per_chunk > 0) hipLaunchKernelGGL((bwd_state_kernel<T, DK, G2, CPX>), dim3(walks), dim3(NTW), 0, st, a, NC, WalkSplit{});
     hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX>), dim3(walks), dim3(NT), 0, st, a, NC, WalkSplit{});
   } else {
     // split walks: scratch after the chunk blocks; B [chains G][d_k][d_v], P [chains G][d_k][d_k],
@@ -1920,10 +1937,10 @@ static hipError_t launch_bwd_dk(const BwdArgs& a, int NC) {
     const WalkSplit wb{G, segc, a.Dv, kWNoWrite, nullptr, Bst};
     const WalkSplit wp{G, segc, DK, kWNoWrite | kWZeroIn | kWIdentity, nullptr, P};
     const WalkSplit wf{G, segc, a.Dv, 0, X, nullptr};
-    hipLaunchKernelGGL((bwd_state_kernel<T, DK, G2, CPX>), dim3(wv), dim3(NT), 0, st, a, NC, wb);
-    hipLaunchKernelGGL((bwd_state_kernel<T, DK, G2, CPX>), dim3(wk), dim3(NT), 0, st, a, NC, wp);
+    hipLaunchKernelGGL((bwd_state_kernel<T, DK, G2, CPX>), dim3(wv), dim3(NTW), 0, st, a, NC, wb);
+    hipLaunchKernelGGL((bwd_state_kernel<T, DK, G2, CPX>), dim3(wk), dim3(NTW), 0, st, a, NC, wp);
     hipLaunchKernelGGL(walk_scan_kernel<DK>, dim3(chains * (a.Dv / 16)), dim3(256), 0, st, a.s0, P, Bst, X, G, a.Dv, 0);
-    hipLaunchKernelGGL((bwd_state_kernel<T, DK, G2, CPX>), dim3(wv), dim3(NT), 0, st, a, NC, wf);
+    hipLaunchKernelGGL((bwd_state_kernel<T, DK, G2, CPX>), dim3(wv), dim3(NTW), 0, st, a, NC, wf);
     hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX>), dim3(wv), dim3(NT), 0, st, a, NC, wb);
     hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX>), dim3(wk), dim3(NT), 0, st, a, NC, wp);
     hipLaunchKernelGGL(walk_scan_kernel<DK>, dim3(chains * (a.Dv / 16)), dim3(256), 0, st, a.dsT, P, Bst, X, G, a.Dv, 1);
