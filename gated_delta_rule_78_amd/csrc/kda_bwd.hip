@@ -816,11 +816,12 @@ __global__ __launch_bounds__(NTW) void bwd_state_kernel(BwdArgs a, int NC, WalkS
 #pragma unroll
       for (int it = 0; it < NW; ++it) {
         const int x = tid + it * NTW, i = x / (DK / 4), c = 4 * (x % (DK / 4));
+        const int ti = x % C, tc = 4 * (x / C);  // transposed tiles: a wave's lanes take consecutive rows
         *(f32x4_t*)(sW + i * LW + c) = pw[it];
-        sKrT[(c + 0) * LM + i] = pk[it].x;
-        sKrT[(c + 1) * LM + i] = pk[it].y;
-        sKrT[(c + 2) * LM + i] = pk[it].z;
-        sKrT[(c + 3) * LM + i] = pk[it].w;
+        sKrT[(tc + 0) * LM + ti] = pk[it].x;
+        sKrT[(tc + 1) * LM + ti] = pk[it].y;
+        sKrT[(tc + 2) * LM + ti] = pk[it].z;
+        sKrT[(tc + 3) * LM + ti] = pk[it].w;
       }
 #pragma unroll
       for (int it = 0; it < NV; ++it) {
@@ -855,8 +856,9 @@ __global__ __launch_bounds__(NTW) void bwd_state_kernel(BwdArgs a, int NC, WalkS
 #pragma unroll
       for (int it = 0; it < NW; ++it) {
         const int x = tid + it * NTW, i = x / (DK / 4), c = 4 * (x % (DK / 4));
+        const int ti = x % C, tc = 4 * (x / C);
         pw[it] = *(const f32x4_t*)(cl + L.W + i * DK + c);
-        pk[it] = *(const f32x4_t*)(cl + L.KR + i * DK + c);
+        pk[it] = *(const f32x4_t*)(cl + L.KR + ti * DK + tc);
       }
 #pragma unroll
       for (int it = 0; it < NV; ++it) {
@@ -1023,19 +1025,20 @@ __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC, Walk
 #pragma unroll
       for (int it = 0; it < NW; ++it) {
         const int x = tid + it * NT, i = x / (DK / 4), c = 4 * (x % (DK / 4));
+        const int ti = x % C, tc = 4 * (x / C);  // transposed tiles: a wave's lanes take consecutive rows
         *(f32x4_t*)(sKr + i * LK + c) = pk[it];
-        sQgT[(c + 0) * LM + i] = pq[it].x;
-        sQgT[(c + 1) * LM + i] = pq[it].y;
-        sQgT[(c + 2) * LM + i] = pq[it].z;
-        sQgT[(c + 3) * LM + i] = pq[it].w;
-        sWT[(c + 0) * LM + i] = pw[it].x;
-        sWT[(c + 1) * LM + i] = pw[it].y;
-        sWT[(c + 2) * LM + i] = pw[it].z;
-        sWT[(c + 3) * LM + i] = pw[it].w;
+        sQgT[(tc + 0) * LM + ti] = pq[it].x;
+        sQgT[(tc + 1) * LM + ti] = pq[it].y;
+        sQgT[(tc + 2) * LM + ti] = pq[it].z;
+        sQgT[(tc + 3) * LM + ti] = pq[it].w;
+        sWT[(tc + 0) * LM + ti] = pw[it].x;
+        sWT[(tc + 1) * LM + ti] = pw[it].y;
+        sWT[(tc + 2) * LM + ti] = pw[it].z;
+        sWT[(tc + 3) * LM + ti] = pw[it].w;
       }
 #pragma unroll
       for (int it = 0; it < NM; ++it) {
-        const int x = tid + it * NT, j = x / (C / 4), i = 4 * (x % (C / 4));
+        const int x = tid + it * NT, j = x % C, i = 4 * (x / C);  // consecutive rows j per wave
         sAT[(i + 0) * LM + j] = pa[it].x;
         sAT[(i + 1) * LM + j] = pa[it].y;
         sAT[(i + 2) * LM + j] = pa[it].z;
@@ -1061,13 +1064,14 @@ __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC, Walk
 #pragma unroll
       for (int it = 0; it < NW; ++it) {
         const int x = tid + it * NT, i = x / (DK / 4), c = 4 * (x % (DK / 4));
+        const int ti = x % C, tc = 4 * (x / C);
         pk[it] = *(const f32x4_t*)(cl + L.KR + i * DK + c);
-        pq[it] = *(const f32x4_t*)(cl + L.QG + i * DK + c);
-        pw[it] = *(const f32x4_t*)(cl + L.W + i * DK + c);
+        pq[it] = *(const f32x4_t*)(cl + L.QG + ti * DK + tc);
+        pw[it] = *(const f32x4_t*)(cl + L.W + ti * DK + tc);
       }
 #pragma unroll
       for (int it = 0; it < NM; ++it) {
-        const int x = tid + it * NT, j = x / (C / 4), i = 4 * (x % (C / 4));
+        const int x = tid + it * NT, j = x % C, i = 4 * (x / C);
         pa[it] = *(const f32x4_t*)(cl + L.A + j * C + i);
       }
 #pragma unroll
