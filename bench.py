@@ -212,7 +212,7 @@ def bench_prefill(name, steps, warmup, log):
     elif path == "twopass":
         ws = torch.empty(kda.workspace_size(w.B, w.T, w.H, w.dk, w.dv), dtype=torch.uint8, device="cuda")
         ms, t1, t2 = timed_split(lambda: kda.chunk_records(q, k, a, b, workspace=ws, dv=w.dv),
-                                 lambda: kda.chunk_apply_records(ws, v, s0, out=o, final_state=sT, dk=w.dk),
+                                 lambda: kda.chunk_apply_records(ws, q, k, a, v, s0, out=o, final_state=sT),
                                  steps, warmup, stream)
         res.update(ms=ms, kernels={"chunk_records": t1, "chunk_state": t2},
                    workspace_bytes=ws.numel())

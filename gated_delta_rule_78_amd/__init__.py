@@ -58,7 +58,7 @@ def lib() -> ctypes.CDLL:
         L.kda_chunk_fwd_workspace_size.restype = ctypes.c_size_t
         L.kda_chunk_records.argtypes = [SP, P, P, P, P, P, ctypes.c_size_t, P]
         L.kda_chunk_records.restype = ctypes.c_int
-        L.kda_chunk_apply_records.argtypes = [SP, P, ctypes.c_size_t, P, P, P, P, P]
+        L.kda_chunk_apply_records.argtypes = [SP, P, P, P, P, ctypes.c_size_t, P, P, P, P, P]
         L.kda_chunk_apply_records.restype = ctypes.c_int
         L.kda_decode_step.argtypes = [SP, P, P, P, P, P, P, P, P]
         L.kda_decode_step.restype = ctypes.c_int
@@ -257,14 +257,19 @@ def chunk_records(q, k, alpha, beta, workspace=None, dv=None):
     return workspace
 
 
-def chunk_apply_records(workspace, v, initial_state=None, out=None, final_state=None, want_final=True, dk=128,
-                        dtype=None):
-    """Second pass alone: applies the records in `workspace` to v [B,T,H,dv] and the
-    start state.  dk is the key width the records were made with.  Returns
-    (o [B,T,H,dv], final_state or None)."""
+def chunk_apply_records(workspace, q, k, alpha, v, initial_state=None, out=None, final_state=None, want_final=True):
+    """Second pass alone: applies the records in `workspace` (made from q, k, alpha and
+    beta by chunk_records) to v [B,T,H,dv] and the start state; q, k, alpha are the
+    tensors the records were made from.  Returns (o [B,T,H,dv], final_state or None)."""
     torch = _torch()
     B, T, H, dv = v.shape
+    dk = q.shape[-1]
     code = _dtype_code(v)
+    for t, nm in ((q, "q"), (k, "k"), (alpha, "alpha")):
+        if t.dtype != v.dtype:
+            raise TypeError(f"{nm} must have the dtype of v")
+        if t.shape != (B, T, H, dk):
+            raise ValueError("shapes: q, k, alpha [B,T,H,dk]; v [B,T,H,dv]")
     dev = v.device
     if out is None:
         out = torch.empty((B, T, H, dv), dtype=v.dtype, device=dev)
@@ -273,12 +278,13 @@ def chunk_apply_records(workspace, v, initial_state=None, out=None, final_state=
     for t, nm in ((initial_state, "initial_state"), (final_state, "final_state")):
         if t is not None and (t.dtype != torch.float32 or t.shape != (B, H, dk, dv)):
             raise ValueError(f"{nm} must be float32 [B,H,dk,dv]")
-    _check((workspace, v, initial_state, out, final_state),
-           ("workspace", "v", "initial_state", "out", "final_state"), dev)
+    _check((workspace, q, k, alpha, v, initial_state, out, final_state),
+           ("workspace", "q", "k", "alpha", "v", "initial_state", "out", "final_state"), dev)
     shape = Shape(B, T, H, dk, dv, 64, code)
     nbytes = workspace.numel() * workspace.element_size()
-    rc = lib().kda_chunk_apply_records(ctypes.byref(shape), _ptr(workspace), ctypes.c_size_t(nbytes), _ptr(v),
-                                       _ptr(initial_state), _ptr(out), _ptr(final_state), _stream(dev))
+    rc = lib().kda_chunk_apply_records(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(alpha), _ptr(workspace),
+                                       ctypes.c_size_t(nbytes), _ptr(v), _ptr(initial_state), _ptr(out),
+                                       _ptr(final_state), _stream(dev))
     if rc != 0:
         raise KdaError(rc, "kda_chunk_apply_records")
     return out, final_state

@@ -81,8 +81,9 @@ struct ChunkPtrs {
   bool cpx = false;             // SFDA complex gates in alpha (two-pass, bf16 only)
 };
 
-// kNeedQKAB: q, k, alpha and beta (or, with kNeedG2, the erase gate in beta's place)
-enum : int { kNeedQKAB = 1, kNeedVO = 2, kNeedWS = 4, kNeedG2 = 8 };
+// kNeedQKAB: q, k, alpha and beta (or, with kNeedG2, the erase gate in beta's place);
+// kNeedQKA: q, k and alpha only
+enum : int { kNeedQKAB = 1, kNeedVO = 2, kNeedWS = 4, kNeedG2 = 8, kNeedQKA = 16 };
 
 // Host-side checks shared by the chunk entry points (nothing touches the device).
 // n_states: state tiles per head (B, or the number of sequences of a varlen batch);
@@ -100,6 +101,7 @@ int validate_chunk(const kda_shape* shape, const ChunkPtrs& p, int need, int64_t
   const bool g2 = (need & kNeedG2) != 0;
   if (rows > 0) {
     if ((need & kNeedQKAB) && (!p.q || !p.k || !p.alpha || (g2 ? !p.erase : !p.beta))) return KDA_ERR_NULL;
+    if ((need & kNeedQKA) && (!p.q || !p.k || !p.alpha)) return KDA_ERR_NULL;
     if ((need & kNeedVO) && (!p.v || !p.o || (g2 && !p.write))) return KDA_ERR_NULL;
   }
   // q, k, v, alpha, o, the gate tiles and the states move in 16-byte vectors; beta is
@@ -427,11 +429,12 @@ int kda_chunk_records(const kda_shape* shape, const void* q, const void* k, cons
   return rc ? rc : run_records(*shape, p, stream);
 }
 
-int kda_chunk_apply_records(const kda_shape* shape, const void* workspace, size_t workspace_bytes, const void* v,
+int kda_chunk_apply_records(const kda_shape* shape, const void* q, const void* k, const void* alpha,
+                            const void* workspace, size_t workspace_bytes, const void* v,
                             const float* initial_state, void* o, float* final_state, void* stream) {
-  const ChunkPtrs p{nullptr, nullptr, v, nullptr, nullptr, initial_state, o, final_state, nullptr,
+  const ChunkPtrs p{q, k, v, alpha, nullptr, initial_state, o, final_state, nullptr,
                     const_cast<void*>(workspace), workspace_bytes};
-  int rc = validate_chunk(shape, p, kNeedVO | kNeedWS);
+  int rc = validate_chunk(shape, p, kNeedQKA | kNeedVO | kNeedWS);
   return rc ? rc : run_apply(*shape, p, stream);
 }
 

@@ -1028,25 +1028,20 @@ static hipError_t launch_prep_t(const ChunkArgs& a, char* ws, int cpw) {
 
 template <bool G2>
 static hipError_t launch_prep_g(const ChunkArgs& a, void* ws, int cpw) {
-  if (!a.bf16) return a.dk == 64 ? launch_prep_t<float, 64, G2>(a, (char*)ws, cpw) : hipErrorInvalidValue;
-  return a.dk == 64 ? launch_prep_t<bf16_t, 64, G2>(a, (char*)ws, cpw)
-                    : launch_prep_t<bf16_t, 128, G2>(a, (char*)ws, cpw);
+  return a.dk == 64 && a.dv == 64 ? launch_prep_t<float, 64, G2>(a, (char*)ws, cpw) : hipErrorInvalidValue;
 }
 
-// bf16 records come from the kernel sized for two workgroups per compute unit; the
-// first half of the fused kernel writes the fp32 ones (and the bf16 ones when
-// KDA_RECORDS_FUSED is set in the environment, for comparison)
+// bf16 records (WalkRecord) come from the kernel sized for two workgroups per compute
+// unit; the first half of the fused kernel writes the fp32 ones (RecordLayout)
 hipError_t launch_prep(const ChunkArgs& a, void* ws, int cpw) {
-  if (a.cpx) return launch_records(a, ws, cpw);  // complex gates: that kernel only
-  if (a.bf16 && (a.dk == 64 || a.dk == 128) && (long)C * a.H * a.dk * 2 < (1L << 32) &&
-      !getenv("KDA_RECORDS_FUSED"))
-    return launch_records(a, ws, cpw);
+  if (a.bf16) return launch_records(a, ws, cpw);
+  if (a.cpx) return hipErrorInvalidValue;
   return a.erase ? launch_prep_g<true>(a, ws, cpw) : launch_prep_g<false>(a, ws, cpw);
 }
 
 size_t record_bytes(bool bf16, int dk) {
   if (!bf16) return RecordLayout<float, 64>::BYTES;
-  return dk == 64 ? RecordLayout<bf16_t, 64>::BYTES : RecordLayout<bf16_t, 128>::BYTES;
+  return dk == 64 ? WalkRecord<64>::BYTES : WalkRecord<128>::BYTES;
 }
 
 }  // namespace kda

@@ -55,6 +55,8 @@ hipError_t launch_prep(const ChunkArgs& a, void* ws, int cpw);
 // the same records from the bf16 kernel sized for two workgroups per compute unit
 hipError_t launch_records(const ChunkArgs& a, void* ws, int cpw);
 hipError_t launch_state(const ChunkArgs& a, const void* ws);
+// the bf16 walk over WalkRecord records (kda_walk.hip; launch_state forwards bf16 calls)
+hipError_t launch_walk(const ChunkArgs& a, const void* ws);
 // Few (b, h) chains over a long sequence: the state pass splits each chain into this many
 // segments (1: one walk per chain) and needs state_split_bytes of scratch after the records.
 int state_segments(int B, int T, int H, int dk, int dv, bool bf16);

@@ -1,7 +1,8 @@
-// kda_record.h -- per-chunk record passed from the parallel first pass of the two-pass
-// chunk forward to the state pass.  A record is the byte image of the LDS tiles the
-// state pass reads, padded rows included, so that the state pass moves it into LDS with
-// plain 16-byte DMA and reads it there without bank conflicts:
+// kda_record.h -- per-chunk records passed from the parallel first pass of the two-pass
+// chunk forward to the state pass.
+//
+// RecordLayout<T, DK> (fp32 inputs, d_k = d_v = 64): the byte image of the LDS tiles the
+// fp32 state pass reads, padded rows included, so that it moves with plain 16-byte DMA:
 //   WW  [64][DK]  -W           (W = M diag(beta) (K o gamma)),  rows of DK*ES + 16 bytes
 //   QG  [64][DK]  Q o gamma,                                    rows of DK*ES + 16 bytes
 //   KRT [DK][64]  (K o rho)^T,                                  rows of 64*ES + 16 bytes
@@ -9,6 +10,22 @@
 //   MT  [64][64]  M diag(beta), zero above the diagonal,        rows of 64*ES + 16 bytes
 //   GC  [DK]      gamma of the chunk's last row, fp32
 // (element type T unless noted; the 16 pad bytes of a row hold no data).
+//
+// WalkRecord<DK> (bf16 inputs): only what the key and query sides cannot rebuild cheaply.
+// The state pass re-reads q, k and alpha and forms Q o gamma, K o gamma and K o rho itself
+// from the gate products stored here, so the record carries the two 64 x 64 chunk matrices
+// and the block products:
+//   A    lower 64 x 64, bf16      A_ij = sum_c q_ic k_jc r_ijc (j <= i)
+//   MH   lower 64 x 64, bf16      M~ = (I + T)^-1 diag(beta) rounded to bf16
+//   ML   lower 64 x 64, bf16      M~ - MH rounded to bf16 (MH + ML carries M~ to ~2^-17)
+//   GP   [3][DK] fp32             product of the gates of the 16-row blocks before block I = 1..3
+//   RP   [3][DK] fp32             product of the gates of the blocks after block I = 0..2
+//   G63  [DK] fp32                gamma of the chunk's last row (product of all 64 gates)
+// A lower matrix is stored as two row-major images: rows 0..31 with columns 0..31 (rows of
+// 80 bytes) and rows 32..63 with columns 0..63 (rows of 144 bytes); the 16 pad bytes per
+// row keep the state pass's LDS reads free of bank conflicts.  The first DMA bytes (A, MH,
+// ML) are moved into LDS as one image; the gate products are read into registers.
+// For complex (SFDA) gates the gate products hold (Re, Im) in each key-channel pair.
 #pragma once
 #include <stddef.h>
 
@@ -30,6 +47,28 @@ struct RecordLayout {
   static constexpr int IMG = GC + DK * 4;                       // bytes that carry the image
   static constexpr size_t BYTES = ((size_t)IMG + 255) / 256 * 256;  // stride between records
   static_assert(IMG % 16 == 0, "16-byte units");
+};
+
+template <int DK>
+struct WalkRecord {
+  static constexpr int RS_TOP = 32 * 2 + 16;  // rows 0..31, columns 0..31
+  static constexpr int RS_BOT = 64 * 2 + 16;  // rows 32..63, columns 0..63
+  static constexpr int BOT = 32 * RS_TOP;
+  static constexpr int MAT = BOT + 32 * RS_BOT;  // one lower matrix
+  static constexpr int A = 0;
+  static constexpr int MH = MAT;
+  static constexpr int ML = 2 * MAT;
+  static constexpr int DMA = 3 * MAT;  // moved into LDS by the state pass
+  static constexpr int GP = DMA;
+  static constexpr int RP = GP + 3 * DK * 4;
+  static constexpr int G63 = RP + 3 * DK * 4;
+  static constexpr int IMG = G63 + DK * 4;
+  static constexpr size_t BYTES = ((size_t)IMG + 255) / 256 * 256;
+  static_assert(DMA % 1024 == 0, "whole wave-wide DMA steps");
+  // byte offset of element (i, j), j <= 31 for i <= 31, of a lower matrix image
+  __host__ __device__ static constexpr int at(int i, int j) {
+    return i < 32 ? i * RS_TOP + 2 * j : BOT + (i - 32) * RS_BOT + 2 * j;
+  }
 };
 
 }  // namespace kda

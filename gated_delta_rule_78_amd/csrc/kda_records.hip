@@ -44,33 +44,37 @@ struct RCfg {
   static constexpr int LVL_ROWS = 24;         // per block: 8 q rows, 8 key rows (upper ranks), 8 k rows
   static constexpr int SZ_LV = NB * LVL_ROWS * RS_DK;
   static constexpr int mx(int a, int b) { return a > b ? a : b; }
-  // region X: Xq, Xk of blocks 1..3 and Y of blocks 0..2 -> level buffer 1 -> (K o gamma)^T, M (fp32)
+  // region X.  Level path: Xq, Xk of blocks 1..3 and Y of blocks 0..2, then level buffer 1.
+  // Ratio path: the row operands Q o gamma and E o gamma (E: the erase-side key).  Both:
+  // M (fp32) for the inverse.
   static constexpr int OFF_XQ = 0;
   static constexpr int OFF_XK = OFF_XQ + 3 * SUB * RS_DK;
   static constexpr int OFF_Y = OFF_XK + 3 * SUB * RS_DK;
   static constexpr int SZ_X_A = OFF_Y + 3 * SUB * RS_DK;
-  static constexpr int OFF_KGT = 0;
-  static constexpr int OFF_MM = OFF_KGT + DK * RS_C;
-  static constexpr int SZ_X_B = OFF_MM + C * RS_F;
-  static constexpr int SZ_X = mx(mx(SZ_X_A, SZ_LV), SZ_X_B);
-  // region L: level buffer 0 -> D (fp32: T before its beta row scale), the transposed
-  // inverse blocks (MB), later M~ over MB; -W over D once the inverse is done.  A~ lies
-  // past the level buffer, so its zero entries (upper tiles, upper triangles of the
-  // diagonal tiles) are written once and never overwritten.
+  static constexpr int OFF_FQ = 0;
+  static constexpr int OFF_FE = C * RS_DK;
+  static constexpr int SZ_X_F = 2 * C * RS_DK;
+  static constexpr int OFF_MM = 0;
+  static constexpr int SZ_X_B = C * RS_F;
+  static constexpr int SZ_X = mx(mx(SZ_X_A, SZ_LV), mx(SZ_X_F, SZ_X_B));
+  // region L.  Level path: level buffer 0; ratio path: the column operand K o rho / gamma_last.
+  // Then D (fp32: T before its beta row scale) and the transposed inverse blocks (MB).  A~
+  // lies past all of them, so its zero entries (upper tiles, upper triangles of the diagonal
+  // tiles) are written once and never overwritten.
   static constexpr int NMB = 5;
   static constexpr int OFF_TT = 0;
+  static constexpr int OFF_FK = 0;
   static constexpr int OFF_MB = OFF_TT + C * RS_F;
-  static constexpr int OFF_AT = OFF_MB + mx(NMB * SUB * RS_MB, C * RS_C);
+  static constexpr int OFF_AT = mx(OFF_MB + NMB * SUB * RS_MB, SZ_LV);
   static constexpr int SZ_L = OFF_AT + C * RS_C;
-  static_assert(SZ_LV <= OFF_AT, "level buffer 0 stays clear of A~");
+  static_assert(C * RS_DK <= OFF_AT, "the ratio path's column operand stays clear of A~");
   static constexpr int BASE_X = 0;
   static constexpr int BASE_L = BASE_X + SZ_X;
-  static constexpr int BASE_GT = BASE_L + SZ_L;         // block totals g[4][DK]
-  static constexpr int BASE_GC = BASE_GT + NB * DK * 4;  // gamma of the last row [DK]
-  static constexpr int BASE_BETA = BASE_GC + DK * 4;     // beta [C]
-  static constexpr int LDS = BASE_BETA + C * 4;
+  static constexpr int BASE_GT = BASE_L + SZ_L;          // block totals g[4][DK]
+  static constexpr int BASE_BETA = BASE_GT + NB * DK * 4;  // beta [C]
+  static constexpr int BASE_OK = BASE_BETA + C * 4;      // per-wave votes of the path choice
+  static constexpr int LDS = BASE_OK + 16;
   static_assert(LDS <= 80 * 1024, "two workgroups per compute unit");
-  static_assert(C * RS_DK <= C * RS_F, "-W fits over D");
   // gate items: (block, channel pair); GRP items (lanes) per block
   static constexpr int GRP = DK / 2;
   static constexpr int NITEM = NB * GRP;
@@ -139,44 +143,6 @@ __device__ __forceinline__ void put_level(const f32x4_t& acc, int I, int g, int 
   }
 }
 
-// Running gate products on an item's channel pair (2c, 2c+1).  Real gates (KDA / CKDA /
-// Gated DeltaNet-2): two independent channels, (x, y) their products.  Complex gates
-// (SFDA page, "Arquitectura Central": the pair is one complex coordinate and its gate the
-// complex number lambda = (Re, Im) in channels (2c, 2c+1)): (x, y) = (Re, Im) of the
-// product.  The row side of a decayed product takes the conjugate (the transpose of a
-// rotation-decay block), the column side the product itself:
-//   r_ij = F_i B_j,  x_i^T R_ij y_j = (conj(F_i) x_i) . (B_j y_j)  over real channel pairs.
-template <bool CPX>
-struct Gp2 {
-  float x, y;
-  __device__ __forceinline__ static Gp2 one() { return Gp2{1.f, CPX ? 0.f : 1.f}; }
-  __device__ __forceinline__ Gp2 operator*(const Gp2& o) const {
-    if constexpr (CPX) return Gp2{x * o.x - y * o.y, x * o.y + y * o.x};
-    else return Gp2{x * o.x, y * o.y};
-  }
-  __device__ __forceinline__ void operator*=(const Gp2& o) { *this = *this * o; }
-  // row-side operand of the pair (v0, v1): conj(F) v (complex) or (F0 v0, F1 v1)
-  __device__ __forceinline__ void row(float v0, float v1, float& r0, float& r1) const {
-    if constexpr (CPX) {
-      r0 = x * v0 + y * v1;
-      r1 = x * v1 - y * v0;
-    } else {
-      r0 = v0 * x;
-      r1 = v1 * y;
-    }
-  }
-  // column-side operand: B v (complex) or (B0 v0, B1 v1)
-  __device__ __forceinline__ void col(float v0, float v1, float& r0, float& r1) const {
-    if constexpr (CPX) {
-      r0 = x * v0 - y * v1;
-      r1 = x * v1 + y * v0;
-    } else {
-      r0 = v0 * x;
-      r1 = v1 * y;
-    }
-  }
-};
-
 // Column-side scale of eight consecutive channels of a bf16 fragment by the gate products p
 // (channel pairs (2i, 2i+1) of p: complex numbers when CPX)
 template <bool CPX>
@@ -206,11 +172,10 @@ __global__ __launch_bounds__(256, 2) void chunk_records_kernel(
   // cu != NULL: packed variable-length batch; chunk indices are global (ctab[c] =
   // (sequence, chunk of that sequence)) and records are [H][gmax]
   using K = RCfg<DK>;
-  using RL = RecordLayout<bf16_t, DK>;
+  using RL = WalkRecord<DK>;
   using R = Raw<bf16_t>;
   using G = Gp2<CPX>;
   static_assert(!(G2 && CPX), "complex gates take the KDA erase/write form");
-  static_assert(RL::RS_DK == K::RS_DK && RL::RS_C == K::RS_C, "record rows match the LDS tiles");
   constexpr int NT = K::NT;
   constexpr int LDF = K::RS_F / 4;
   constexpr int GRP = K::GRP;
@@ -218,8 +183,8 @@ __global__ __launch_bounds__(256, 2) void chunk_records_kernel(
   char* const R_X = smem + K::BASE_X;
   char* const R_L = smem + K::BASE_L;
   float* const GT = (float*)(smem + K::BASE_GT);
-  float* const GC = (float*)(smem + K::BASE_GC);
   float* const BETA = (float*)(smem + K::BASE_BETA);
+  int* const OKW = (int*)(smem + K::BASE_OK);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -264,9 +229,16 @@ __global__ __launch_bounds__(256, 2) void chunk_records_kernel(
     const uint32_t rs = (uint32_t)H * DK * 2;
     const int last = gn.len - 1 - gn.t0;
     if (has_item) {
+      // the item's first row and column byte, from an opaque copy of the thread index:
+      // otherwise the sixteen row offsets are hoisted out of the chunk loop and spilled,
+      // and each reload waits for every load in flight
+      int t = threadIdx.x;
+      asm volatile("" : "+v"(t));
+      const int row0 = SUB * (t / GRP);
+      const uint32_t col = 4 * (t % GRP);
 #pragma unroll
       for (int m = 0; m < SUB; ++m) {
-        const uint32_t off = (uint32_t)min(SUB * iI + m, last) * rs + 4 * icp;
+        const uint32_t off = (uint32_t)min(row0 + m, last) * rs + col;
         pq[m] = *(const uint32_t*)((const char*)gq + base + off);
         pk[m] = *(const uint32_t*)((const char*)gk + base + off);
         pa[m] = *(const uint32_t*)((const char*)galpha + base + off);
@@ -310,8 +282,8 @@ __global__ __launch_bounds__(256, 2) void chunk_records_kernel(
     // ---------------- item registers, fp32 (rows past the end: q = k = 0, alpha = 1)
     // Rows past the end keep the clamped copies of the last row's q and k: their beta is 0,
     // so their rows of T and of M~ are zero, they add nothing to any state, and their
-    // outputs are never stored.  Only their gate must be the identity (it enters gamma_last
-    // and rho): (1, 1) for real gates, 1 + 0i for complex ones.
+    // outputs are never stored.  Only their gate must be the identity (it enters the gate
+    // products): (1, 1) for real gates, 1 + 0i for complex ones.
     float qf[SUB][2], kf[SUB][2];
     G al[SUB];
     constexpr uint32_t kOne = CPX ? 0x00003F80u : R::kOneWord;
@@ -340,56 +312,175 @@ __global__ __launch_bounds__(256, 2) void chunk_records_kernel(
       }
     };
     if (tid < C) BETA[tid] = (t0 + tid < gm.len) ? (G2 ? 1.f : __uint_as_float(pb << 16)) : 0.f;
-    // level-lam operands of the item's block into level buffer `buf`: rows u (q) and
-    // 8 + u (erase-side key) of the upper-half ranks, prefix products from the upper
-    // half's start; rows 16 + v (k) of the lower-half ranks, suffix products to its end
-    auto write_level = [&](char* buf, int lam) {
-      char* LA = buf + iI * K::LVL_ROWS * K::RS_DK + 4 * icp;
-      char* LB = LA + 16 * K::RS_DK;
+
+    // ================= phase B0: block totals, and the choice of path.  The ratio path
+    // factors r_ij = gamma_i * (rho_j / gamma_last) with gamma_i the running product from
+    // the chunk start and rho_j the one from j + 1 to the chunk end: one product per matrix
+    // instead of the block and level split.  It is taken only when every channel's
+    // product over the whole chunk has magnitude >= 2^-64: gamma_last divides nothing
+    // smaller, no factor leaves the fp32 / bf16 range (|gamma_i| >= |gamma_last| when
+    // |alpha| <= 1), and each decayed product keeps its relative rounding.  A zero gate,
+    // or a run of tiny ones, sends the chunk down the level path, which never divides.
+    if (has_item) {
       G f = G::one();
 #pragma unroll
-      for (int m = 0; m < SUB; ++m) {
-        if (m & lam) {
-          if ((m & (lam - 1)) == 0)
-            f = al[m];
-          else
-            f *= al[m];
-          const int u = (m / (2 * lam)) * lam + (m & (lam - 1));
-          float k0, k1, r0, r1;
-          read_key(m, k0, k1);
-          f.row(qf[m][0], qf[m][1], r0, r1);
-          R::st(LA + u * K::RS_DK, r0, r1);
-          f.row(k0, k1, r0, r1);
-          R::st(LA + (8 + u) * K::RS_DK, r0, r1);
-        }
-      }
-      G bb = G::one();
-#pragma unroll
-      for (int m = SUB - 1; m >= 0; --m) {
-        if (!(m & lam)) {
-          if ((m & (lam - 1)) == lam - 1)
-            bb = G::one();
-          else
-            bb *= al[m + 1];
-          const int v = (m / (2 * lam)) * lam + (m & (lam - 1));
-          float r0, r1;
-          bb.col(kf[m][0], kf[m][1], r0, r1);
-          R::st(LB + v * K::RS_DK, r0, r1);
-        }
-      }
-    };
-
-    // ================= phase B: block-anchored operands, block totals, diagonal of A, level 8
-    float adiag = 0.f;
+      for (int m = 0; m < SUB; ++m) f *= al[m];
+      *(float2*)(GT + iI * DK + 2 * icp) = make_float2(f.x, f.y);
+    }
+    lds_barrier();
+    G t0v = G::one(), t1v = G::one(), t2v = G::one(), t3v = G::one();
     if (has_item) {
-      {
-        char* xq = R_X + K::OFF_XQ + (SUB * (iI - 1)) * K::RS_DK + 4 * icp;
-        char* xk = R_X + K::OFF_XK + (SUB * (iI - 1)) * K::RS_DK + 4 * icp;
-        G f = G::one();
+      const float2 a0 = *(const float2*)(GT + 2 * icp), a1 = *(const float2*)(GT + DK + 2 * icp);
+      const float2 a2 = *(const float2*)(GT + 2 * DK + 2 * icp), a3 = *(const float2*)(GT + 3 * DK + 2 * icp);
+      t0v = G{a0.x, a0.y};
+      t1v = G{a1.x, a1.y};
+      t2v = G{a2.x, a2.y};
+      t3v = G{a3.x, a3.y};
+    }
+    bool ratio = false;
+    if constexpr (!CPX) {
+      const G gl = t0v * t1v * t2v * t3v;
+      const bool ok = !has_item || (fabsf(gl.x) >= 0x1p-64f && fabsf(gl.y) >= 0x1p-64f);
+      const bool wave_ok = __ballot(!ok) == 0;
+      if (lane == 0) OKW[wave] = wave_ok ? 1 : 0;
+      lds_barrier();
+      ratio = (OKW[0] & OKW[1] & OKW[2] & OKW[3]) != 0;
+    }
+    // the record's gate products: GP[I - 1] = prod of blocks < I, RP[I] = prod of blocks > I,
+    // G63 = all four (one channel pair per thread)
+    if (tid < DK / 2) {
+      float* GP = (float*)(rec + RL::GP);
+      float* RP = (float*)(rec + RL::RP);
+      float* GL = (float*)(rec + RL::G63);
+      const int c2 = 2 * tid;
+      // (this thread's item is (block 0, pair tid): t0v..t3v are its pair's block totals)
+      const G p01 = t0v * t1v, p23 = t2v * t3v;
+      const G gp[3] = {t0v, p01, p01 * t2v};
+      const G rp[3] = {t1v * p23, p23, t3v};
+#pragma unroll
+      for (int I = 0; I < 3; ++I) {
+        *(float2*)(GP + I * DK + c2) = make_float2(gp[I].x, gp[I].y);
+        *(float2*)(RP + I * DK + c2) = make_float2(rp[I].x, rp[I].y);
+      }
+      const G gl = p01 * p23;
+      *(float2*)(GL + c2) = make_float2(gl.x, gl.y);
+    }
+    float* const TT = (float*)(R_L + K::OFF_TT);
+    char* const AT = R_L + K::OFF_AT;
+
+    if (ratio) {
+      // ================= ratio path, phase F1: row operands Q o gamma, E o gamma and the
+      // column operand K o rho / gamma_last, each as [pos][channel] bf16
+      if (has_item) {
+        const G gp = iI == 0 ? G::one() : iI == 1 ? t0v : iI == 2 ? t0v * t1v : t0v * t1v * t2v;
+        const G rp = iI == 3 ? G::one() : iI == 2 ? t3v : iI == 1 ? t2v * t3v : t1v * t2v * t3v;
+        const G gl = t0v * t1v * t2v * t3v;
+        char* fq = R_X + K::OFF_FQ + (SUB * iI) * K::RS_DK + 4 * icp;
+        char* fe = R_X + K::OFF_FE + (SUB * iI) * K::RS_DK + 4 * icp;
+        char* fk = R_L + K::OFF_FK + (SUB * iI) * K::RS_DK + 4 * icp;
+        G f = gp;
 #pragma unroll
         for (int m = 0; m < SUB; ++m) {
           f *= al[m];
-          if (iI >= 1) {
+          float e0, e1;
+          read_key(m, e0, e1);
+          R::st(fq + m * K::RS_DK, qf[m][0] * f.x, qf[m][1] * f.y);
+          R::st(fe + m * K::RS_DK, e0 * f.x, e1 * f.y);
+        }
+        G bb{rp.x / gl.x, rp.y / gl.y};
+#pragma unroll
+        for (int m = SUB - 1; m >= 0; --m) {
+          R::st(fk + m * K::RS_DK, kf[m][0] * bb.x, kf[m][1] * bb.y);
+          bb *= al[m];
+        }
+      }
+      if (chunk + 1 < c_end) issue(chunk + 1);
+      lds_barrier();
+      // ================= phase F2: the ten lower 16 x 16 tiles of A (Q o gamma rows) and of
+      // D (E o gamma rows) against the column operand; five jobs per wave
+      f32x4_t acc[5];
+#pragma unroll
+      for (int s = 0; s < 5; ++s) {
+        const int j = wave + 4 * s, t = j % 10;
+        const int I = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+        const int J = t - (I * (I + 1)) / 2;
+        const char* arow = R_X + (j < 10 ? K::OFF_FQ : K::OFF_FE) + (16 * I + n) * K::RS_DK;
+        const char* brow = R_L + K::OFF_FK + (16 * J + n) * K::RS_DK;
+        Frag<bf16_t> fa[K::KS], fb[K::KS];
+#pragma unroll
+        for (int ks = 0; ks < K::KS; ++ks) {
+          fa[ks].load8(arow + (32 * ks + 8 * g) * 2);
+          fb[ks].load8(brow + (32 * ks + 8 * g) * 2);
+        }
+        acc[s] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < K::KS; ++ks) mma(acc[s], fa[ks], fb[ks]);
+      }
+      lds_barrier();  // the column operand is read out before D lands over it
+#pragma unroll
+      for (int s = 0; s < 5; ++s) {
+        const int j = wave + 4 * s, t = j % 10;
+        const int I = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+        const int J = t - (I * (I + 1)) / 2;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int li = 4 * g + e, gi = 16 * I + li, gj = 16 * J + n;
+          if (j < 10)
+            *(uint16_t*)(AT + gi * K::RS_C + gj * 2) = f32_to_bf16(I > J || n <= li ? acc[s][e] : 0.f);
+          else
+            TT[gi * LDF + gj] = acc[s][e];
+        }
+      }
+    } else {
+      // ================= level path, phase B: block-anchored operands, diagonal of A, level 8
+      // level-lam operands of the item's block into level buffer `buf`: rows u (q) and
+      // 8 + u (erase-side key) of the upper-half ranks, prefix products from the upper
+      // half's start; rows 16 + v (k) of the lower-half ranks, suffix products to its end
+      auto write_level = [&](char* buf, int lam) {
+        char* LA = buf + iI * K::LVL_ROWS * K::RS_DK + 4 * icp;
+        char* LB = LA + 16 * K::RS_DK;
+        G f = G::one();
+#pragma unroll
+        for (int m = 0; m < SUB; ++m) {
+          if (m & lam) {
+            if ((m & (lam - 1)) == 0)
+              f = al[m];
+            else
+              f *= al[m];
+            const int u = (m / (2 * lam)) * lam + (m & (lam - 1));
+            float k0, k1, r0, r1;
+            read_key(m, k0, k1);
+            f.row(qf[m][0], qf[m][1], r0, r1);
+            R::st(LA + u * K::RS_DK, r0, r1);
+            f.row(k0, k1, r0, r1);
+            R::st(LA + (8 + u) * K::RS_DK, r0, r1);
+          }
+        }
+        G bb = G::one();
+#pragma unroll
+        for (int m = SUB - 1; m >= 0; --m) {
+          if (!(m & lam)) {
+            if ((m & (lam - 1)) == lam - 1)
+              bb = G::one();
+            else
+              bb *= al[m + 1];
+            const int v = (m / (2 * lam)) * lam + (m & (lam - 1));
+            float r0, r1;
+            bb.col(kf[m][0], kf[m][1], r0, r1);
+            R::st(LB + v * K::RS_DK, r0, r1);
+          }
+        }
+      };
+
+      float adiag = 0.f;
+      if (has_item) {
+        if (iI >= 1) {
+          char* xq = R_X + K::OFF_XQ + (SUB * (iI - 1)) * K::RS_DK + 4 * icp;
+          char* xk = R_X + K::OFF_XK + (SUB * (iI - 1)) * K::RS_DK + 4 * icp;
+          G f = G::one();
+#pragma unroll
+          for (int m = 0; m < SUB; ++m) {
+            f *= al[m];
             float k0, k1, r0, r1;
             read_key(m, k0, k1);
             f.row(qf[m][0], qf[m][1], r0, r1);
@@ -398,205 +489,142 @@ __global__ __launch_bounds__(256, 2) void chunk_records_kernel(
             R::st(xk + m * K::RS_DK, r0, r1);
           }
         }
-        *(float2*)(GT + iI * DK + 2 * icp) = make_float2(f.x, f.y);
-      }
-      if (iI <= 2) {
-        char* y = R_X + K::OFF_Y + (SUB * iI) * K::RS_DK + 4 * icp;
-        G bb = G::one();
+        if (iI <= 2) {
+          char* y = R_X + K::OFF_Y + (SUB * iI) * K::RS_DK + 4 * icp;
+          G bb = G::one();
 #pragma unroll
-        for (int m = SUB - 1; m >= 0; --m) {
-          float r0, r1;
-          bb.col(kf[m][0], kf[m][1], r0, r1);
-          R::st(y + m * K::RS_DK, r0, r1);
-          bb *= al[m];
-        }
-      }
-      float d[SUB];
-#pragma unroll
-      for (int m = 0; m < SUB; ++m) {
-        const float q0 = qf[m][0], q1 = qf[m][1];
-        const float k0 = kf[m][0], k1 = kf[m][1];
-        d[m] = fmaf(q1, k1, q0 * k0);
-      }
-      adiag = reduce16<GRP>(d, lane);
-      write_level(R_L, 8);
-    }
-    lds_barrier();
-
-    // ================= phase M1: the six off-diagonal tiles of A and T, level 8 tiles.
-    // Waves 0, 1: two off-diagonal jobs; waves 2, 3: one off-diagonal job and two
-    // level-8 blocks.  Job j: (I, J) = (1,0) (2,1) (3,2) (2,0) (3,1) (3,0).
-    auto lvl_job = [&](const char* buf, int I, f32x4_t& acc) {
-      const char* LA = buf + I * K::LVL_ROWS * K::RS_DK;
-      const char* LB = LA + 16 * K::RS_DK;
-      Frag<bf16_t> fa[K::KS], fb[K::KS];
-#pragma unroll
-      for (int ks = 0; ks < K::KS; ++ks) {
-        const int c0 = 32 * ks + 8 * g;
-        fa[ks].load8(LA + n * K::RS_DK + c0 * 2);
-        if (n < 8)
-          fb[ks].load8(LB + n * K::RS_DK + c0 * 2);
-        else
-          fb[ks].zero();
-      }
-      acc = zero4();
-#pragma unroll
-      for (int ks = 0; ks < K::KS; ++ks) mma(acc, fa[ks], fb[ks]);
-    };
-    auto off_job = [&](int j, f32x4_t& ra, f32x4_t& rt) {
-      const int I = kOffI[j], J = kOffJ[j], pi = kOffPi[j];
-      const char* xq = R_X + K::OFF_XQ + (SUB * (I - 1) + n) * K::RS_DK;
-      const char* xk = R_X + K::OFF_XK + (SUB * (I - 1) + n) * K::RS_DK;
-      const char* y = R_X + K::OFF_Y + (SUB * J + n) * K::RS_DK;
-      Frag<bf16_t> fa[K::KS], fk[K::KS], fb[K::KS];
-#pragma unroll
-      for (int ks = 0; ks < K::KS; ++ks) {
-        const int c0 = 32 * ks + 8 * g;
-        fb[ks].load8(y + c0 * 2);
-        fa[ks].load8(xq + c0 * 2);
-        fk[ks].load8(xk + c0 * 2);
-      }
-      ra = zero4();
-      rt = zero4();
-#pragma unroll
-      for (int ks = 0; ks < K::KS; ++ks) {
-        if (pi >= 0) {
-          // whole blocks between J and I: g1 (pi 0), g1 g2 (pi 1), g2 (pi 2)
-          const int c0 = 32 * ks + 8 * g;
-          const float* G1 = GT + (pi == 2 ? 2 : 1) * DK + c0;
-          float4 p0 = *(const float4*)G1, p1 = *(const float4*)(G1 + 4);
-          if (pi == 1) {
-            const float4 e0 = *(const float4*)(GT + 2 * DK + c0), e1 = *(const float4*)(GT + 2 * DK + c0 + 4);
-            const G a0 = G{p0.x, p0.y} * G{e0.x, e0.y}, a1 = G{p0.z, p0.w} * G{e0.z, e0.w};
-            const G a2 = G{p1.x, p1.y} * G{e1.x, e1.y}, a3 = G{p1.z, p1.w} * G{e1.z, e1.w};
-            p0 = make_float4(a0.x, a0.y, a1.x, a1.y);
-            p1 = make_float4(a2.x, a2.y, a3.x, a3.y);
-          }
-          const float pv8[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-          scale_col<CPX>(fb[ks], pv8);
-        }
-        mma(ra, fa[ks], fb[ks]);
-        mma(rt, fk[ks], fb[ks]);
-      }
-    };
-    f32x4_t acc1[4];
-    off_job(wave, acc1[0], acc1[1]);
-    if (wave < 2) {
-      off_job(wave + 4, acc1[2], acc1[3]);
-    } else {
-      lvl_job(R_L, 2 * (wave - 2), acc1[2]);
-      lvl_job(R_L, 2 * (wave - 2) + 1, acc1[3]);
-    }
-    lds_barrier();
-
-    // ================= phase C: Q o gamma and (K o rho)^T into the record, gamma_last,
-    // level 4 (buffer 1) and level 2 (buffer 0) operands
-    G Gp = G::one();  // gate product of the blocks before the item's block
-    if (has_item) {
-      const float2 t0f = *(const float2*)(GT + 2 * icp), t1f = *(const float2*)(GT + DK + 2 * icp);
-      const float2 t2f = *(const float2*)(GT + 2 * DK + 2 * icp), t3f = *(const float2*)(GT + 3 * DK + 2 * icp);
-      const G t0v{t0f.x, t0f.y}, t1v{t1f.x, t1f.y}, t2v{t2f.x, t2f.y}, t3v{t3f.x, t3f.y};
-      Gp = iI == 0 ? G::one() : iI == 1 ? t0v : iI == 2 ? t0v * t1v : t0v * t1v * t2v;
-      const G Rp = iI == 3 ? G::one() : iI == 2 ? t3v : iI == 1 ? t2v * t3v : t1v * t2v * t3v;
-      if (iI == 3) {  // gamma_last
-        const G gl = Gp * t3v;
-        *(float2*)(GC + 2 * icp) = make_float2(gl.x, gl.y);
-      }
-      {
-        char* qg = rec + RL::QG + (SUB * iI) * K::RS_DK + 4 * icp;
-        G f = Gp;
-#pragma unroll
-        for (int m = 0; m < SUB; ++m) {
-          f *= al[m];
-          float r0, r1;
-          f.row(qf[m][0], qf[m][1], r0, r1);
-          R::st(qg + m * K::RS_DK, r0, r1);
-        }
-      }
-      {
-        char* pr0 = rec + RL::KRT + (2 * icp) * K::RS_C + (SUB * iI) * 2;
-        G bb = Rp;
-#pragma unroll
-        for (int h8 = SUB - 8; h8 >= 0; h8 -= 8) {
-          float r8a[8], r8b[8];
-#pragma unroll
-          for (int mm = 7; mm >= 0; --mm) {
-            const int m = h8 + mm;
-            bb.col(kf[m][0], kf[m][1], r8a[mm], r8b[mm]);
+          for (int m = SUB - 1; m >= 0; --m) {
+            float r0, r1;
+            bb.col(kf[m][0], kf[m][1], r0, r1);
+            R::st(y + m * K::RS_DK, r0, r1);
             bb *= al[m];
           }
-          st_row8<bf16_t>(pr0 + h8 * 2, r8a);
-          st_row8<bf16_t>(pr0 + K::RS_C + h8 * 2, r8b);
         }
-      }
-      write_level(R_X, 4);
-      write_level(R_L, 2);
-    }
-    // the record's pad bytes of Q o gamma and (K o rho)^T rows (whole lines reach memory)
-    if (tid < C) *(uint4*)(rec + RL::QG + tid * K::RS_DK + DK * 2) = make_uint4(0, 0, 0, 0);
-    if (tid < DK) *(uint4*)(rec + RL::KRT + tid * K::RS_C + C * 2) = make_uint4(0, 0, 0, 0);
-    lds_barrier();
-
-    // ================= phase M2: level 4 and level 2 tiles of block `wave`
-    f32x4_t acc2[2];
-    lvl_job(R_X, wave, acc2[0]);
-    lvl_job(R_L, wave, acc2[1]);
-    lds_barrier();
-
-    // ================= phase C2: level 1 operands (buffer 0), (K o gamma)^T with the
-    // erase-side key, then the next chunk's inputs
-    if (has_item) {
-      write_level(R_L, 1);
-      char* pg0 = R_X + K::OFF_KGT + (2 * icp) * K::RS_C + (SUB * iI) * 2;
-      G f = Gp;
+        float d[SUB];
 #pragma unroll
-      for (int h8 = 0; h8 < SUB; h8 += 8) {
-        float g8a[8], g8b[8];
-#pragma unroll
-        for (int mm = 0; mm < 8; ++mm) {
-          const int m = h8 + mm;
-          f *= al[m];
-          float k0, k1;
-          read_key(m, k0, k1);
-          f.row(k0, k1, g8a[mm], g8b[mm]);
+        for (int m = 0; m < SUB; ++m) {
+          const float q0 = qf[m][0], q1 = qf[m][1];
+          const float k0 = kf[m][0], k1 = kf[m][1];
+          d[m] = fmaf(q1, k1, q0 * k0);
         }
-        st_row8<bf16_t>(pg0 + h8 * 2, g8a);
-        st_row8<bf16_t>(pg0 + K::RS_C + h8 * 2, g8b);
+        adiag = reduce16<GRP>(d, lane);
+        write_level(R_L, 8);
       }
-    }
-    if (chunk + 1 < c_end) issue(chunk + 1);
-    lds_barrier();
+      lds_barrier();
 
-    // ================= phase M3: level 1 tile of block `wave`
-    f32x4_t acc3;
-    lvl_job(R_L, wave, acc3);
-    lds_barrier();
-
-    // ================= phase D: every product into D (fp32) and A~ (bf16)
-    float* const TT = (float*)(R_L + K::OFF_TT);
-    char* const AT = R_L + K::OFF_AT;
-    auto put_off = [&](int j, const f32x4_t& ra, const f32x4_t& rt) {
-      const int I = kOffI[j], J = kOffJ[j];
+      // ================= phase M1: the six off-diagonal tiles of A and T, level 8 tiles.
+      // Waves 0, 1: two off-diagonal jobs; waves 2, 3: one off-diagonal job and two
+      // level-8 blocks.  Job j: (I, J) = (1,0) (2,1) (3,2) (2,0) (3,1) (3,0).
+      auto lvl_job = [&](const char* buf, int I, f32x4_t& acc) {
+        const char* LA = buf + I * K::LVL_ROWS * K::RS_DK;
+        const char* LB = LA + 16 * K::RS_DK;
+        Frag<bf16_t> fa[K::KS], fb[K::KS];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int gi = 16 * I + 4 * g + e, gj = 16 * J + n;
-        *(uint16_t*)(AT + gi * K::RS_C + gj * 2) = f32_to_bf16(ra[e]);
-        TT[gi * LDF + gj] = rt[e];
+        for (int ks = 0; ks < K::KS; ++ks) {
+          const int c0 = 32 * ks + 8 * g;
+          fa[ks].load8(LA + n * K::RS_DK + c0 * 2);
+          if (n < 8)
+            fb[ks].load8(LB + n * K::RS_DK + c0 * 2);
+          else
+            fb[ks].zero();
+        }
+        acc = zero4();
+#pragma unroll
+        for (int ks = 0; ks < K::KS; ++ks) mma(acc, fa[ks], fb[ks]);
+      };
+      auto off_job = [&](int j, f32x4_t& ra, f32x4_t& rt) {
+        const int I = kOffI[j], J = kOffJ[j], pi = kOffPi[j];
+        const char* xq = R_X + K::OFF_XQ + (SUB * (I - 1) + n) * K::RS_DK;
+        const char* xk = R_X + K::OFF_XK + (SUB * (I - 1) + n) * K::RS_DK;
+        const char* y = R_X + K::OFF_Y + (SUB * J + n) * K::RS_DK;
+        Frag<bf16_t> fa[K::KS], fk[K::KS], fb[K::KS];
+#pragma unroll
+        for (int ks = 0; ks < K::KS; ++ks) {
+          const int c0 = 32 * ks + 8 * g;
+          fb[ks].load8(y + c0 * 2);
+          fa[ks].load8(xq + c0 * 2);
+          fk[ks].load8(xk + c0 * 2);
+        }
+        ra = zero4();
+        rt = zero4();
+#pragma unroll
+        for (int ks = 0; ks < K::KS; ++ks) {
+          if (pi >= 0) {
+            // whole blocks between J and I: g1 (pi 0), g1 g2 (pi 1), g2 (pi 2)
+            const int c0 = 32 * ks + 8 * g;
+            const float* G1 = GT + (pi == 2 ? 2 : 1) * DK + c0;
+            float4 p0 = *(const float4*)G1, p1 = *(const float4*)(G1 + 4);
+            if (pi == 1) {
+              const float4 e0 = *(const float4*)(GT + 2 * DK + c0), e1 = *(const float4*)(GT + 2 * DK + c0 + 4);
+              const G a0 = G{p0.x, p0.y} * G{e0.x, e0.y}, a1 = G{p0.z, p0.w} * G{e0.z, e0.w};
+              const G a2 = G{p1.x, p1.y} * G{e1.x, e1.y}, a3 = G{p1.z, p1.w} * G{e1.z, e1.w};
+              p0 = make_float4(a0.x, a0.y, a1.x, a1.y);
+              p1 = make_float4(a2.x, a2.y, a3.x, a3.y);
+            }
+            const float pv8[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+            scale_col<CPX>(fb[ks], pv8);
+          }
+          mma(ra, fa[ks], fb[ks]);
+          mma(rt, fk[ks], fb[ks]);
+        }
+      };
+      f32x4_t acc1[4];
+      off_job(wave, acc1[0], acc1[1]);
+      if (wave < 2) {
+        off_job(wave + 4, acc1[2], acc1[3]);
+      } else {
+        lvl_job(R_L, 2 * (wave - 2), acc1[2]);
+        lvl_job(R_L, 2 * (wave - 2) + 1, acc1[3]);
       }
-    };
-    put_off(wave, acc1[0], acc1[1]);
-    if (wave < 2) {
-      put_off(wave + 4, acc1[2], acc1[3]);
-    } else {
-      put_level<8, K::RS_C, LDF>(acc1[2], 2 * (wave - 2), g, n, AT, TT);
-      put_level<8, K::RS_C, LDF>(acc1[3], 2 * (wave - 2) + 1, g, n, AT, TT);
-    }
-    put_level<4, K::RS_C, LDF>(acc2[0], wave, g, n, AT, TT);
-    put_level<2, K::RS_C, LDF>(acc2[1], wave, g, n, AT, TT);
-    put_level<1, K::RS_C, LDF>(acc3, wave, g, n, AT, TT);
-    if (has_item && (tid % (GRP / 16)) == 0) {
-      const int i = SUB * iI + (tid % GRP) / (GRP / 16);
-      *(uint16_t*)(AT + i * K::RS_C + i * 2) = f32_to_bf16(adiag);
+      lds_barrier();
+
+      // ================= phase C: level 4 (buffer 1) and level 2 (buffer 0) operands
+      if (has_item) {
+        write_level(R_X, 4);
+        write_level(R_L, 2);
+      }
+      lds_barrier();
+
+      // ================= phase M2: level 4 and level 2 tiles of block `wave`
+      f32x4_t acc2[2];
+      lvl_job(R_X, wave, acc2[0]);
+      lvl_job(R_L, wave, acc2[1]);
+      lds_barrier();
+
+      // ================= phase C2: level 1 operands (buffer 0), then the next chunk's inputs
+      if (has_item) write_level(R_L, 1);
+      if (chunk + 1 < c_end) issue(chunk + 1);
+      lds_barrier();
+
+      // ================= phase M3: level 1 tile of block `wave`
+      f32x4_t acc3;
+      lvl_job(R_L, wave, acc3);
+      lds_barrier();
+
+      // ================= phase D: every product into D (fp32) and A~ (bf16)
+      auto put_off = [&](int j, const f32x4_t& ra, const f32x4_t& rt) {
+        const int I = kOffI[j], J = kOffJ[j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int gi = 16 * I + 4 * g + e, gj = 16 * J + n;
+          *(uint16_t*)(AT + gi * K::RS_C + gj * 2) = f32_to_bf16(ra[e]);
+          TT[gi * LDF + gj] = rt[e];
+        }
+      };
+      put_off(wave, acc1[0], acc1[1]);
+      if (wave < 2) {
+        put_off(wave + 4, acc1[2], acc1[3]);
+      } else {
+        put_level<8, K::RS_C, LDF>(acc1[2], 2 * (wave - 2), g, n, AT, TT);
+        put_level<8, K::RS_C, LDF>(acc1[3], 2 * (wave - 2) + 1, g, n, AT, TT);
+      }
+      put_level<4, K::RS_C, LDF>(acc2[0], wave, g, n, AT, TT);
+      put_level<2, K::RS_C, LDF>(acc2[1], wave, g, n, AT, TT);
+      put_level<1, K::RS_C, LDF>(acc3, wave, g, n, AT, TT);
+      if (has_item && (tid % (GRP / 16)) == 0) {
+        const int i = SUB * iI + (tid % GRP) / (GRP / 16);
+        *(uint16_t*)(AT + i * K::RS_C + i * 2) = f32_to_bf16(adiag);
+      }
     }
     lds_barrier();
 
@@ -734,10 +762,24 @@ __global__ __launch_bounds__(256, 2) void chunk_records_kernel(
       put_M(3, 0, neg_N_times(3, keep), -1);
     }
     lds_barrier();
-    // M~ = M diag(beta), lower incl. diagonal, as matrix-core operand (over MB)
-    char* const MT = R_L + K::OFF_MB;
-    for (int x = tid; x < C * C / 8; x += NT) {
-      const int i = x / (C / 8), j0 = 8 * (x % (C / 8));
+    // ================= the record: M~ = M diag(beta) as a bf16 pair (hi, and the rounding
+    // residual lo), straight from registers; A~ copied from LDS.  Both lower matrices are
+    // stored as their rows 0..31 x columns 0..31 and rows 32..63 x columns 0..63 (pad
+    // bytes written as zeros, so whole lines reach memory).
+    for (int x = tid; x < 32 * 5 + 32 * 9; x += NT) {
+      const bool top = x < 32 * 5;
+      const int i = top ? x / 5 : 32 + (x - 160) / 9, u = top ? x % 5 : (x - 160) % 9;
+      const int ncol = top ? 4 : 8;  // 16-byte data units per row
+      char* mh = rec + RL::MH + (top ? i * RL::RS_TOP : RL::BOT + (i - 32) * RL::RS_BOT) + 16 * u;
+      char* ml = mh + (RL::ML - RL::MH);
+      char* ar = rec + RL::A + (mh - (rec + RL::MH));
+      if (u == ncol) {  // the row's pad unit
+        *(uint4*)mh = make_uint4(0, 0, 0, 0);
+        *(uint4*)ml = make_uint4(0, 0, 0, 0);
+        *(uint4*)ar = make_uint4(0, 0, 0, 0);
+        continue;
+      }
+      const int j0 = 8 * u;
       const float4 m0 = *(const float4*)(MM + i * LDF + j0), m1 = *(const float4*)(MM + i * LDF + j0 + 4);
       const float4 b0 = *(const float4*)(BETA + j0), b1 = *(const float4*)(BETA + j0 + 4);
       float v8[8] = {m0.x * b0.x, m0.y * b0.y, m0.z * b0.z, m0.w * b0.w,
@@ -745,46 +787,16 @@ __global__ __launch_bounds__(256, 2) void chunk_records_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (j0 + e > i) v8[e] = 0.f;
-      st_row8<bf16_t>(MT + i * K::RS_C + j0 * 2, v8);
-    }
-    lds_barrier();
-
-    // ================= phase W: -W = -M~ (K o gamma) over D
-    char* const WW = R_L + K::OFF_TT;
-    {
-      Frag<bf16_t> am[NB][2];
+      uint32_t hw[4], lw[4];
 #pragma unroll
-      for (int I = 0; I < NB; ++I)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          if (ks == 0 || I >= 2)
-            am[I][ks].load8(MT + (16 * I + n) * K::RS_C + (32 * ks + 8 * g) * 2);
-          else
-            am[I][ks].zero();
-        }
-      constexpr int NCT = DK / 16;
-      for (int cn = wave; cn < NCT; cn += 4) {
-        Frag<bf16_t> bk[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          bk[ks].load8(R_X + K::OFF_KGT + (16 * cn + n) * K::RS_C + (32 * ks + 8 * g) * 2);
-#pragma unroll
-        for (int I = 0; I < NB; ++I) {
-          f32x4_t acc = zero4();
-          mma(acc, am[I][0], bk[0]);
-          if (I >= 2) mma(acc, am[I][1], bk[1]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            *(uint16_t*)(WW + (16 * I + 4 * g + e) * K::RS_DK + (16 * cn + n) * 2) = f32_to_bf16(-acc[e]);
-        }
+      for (int e = 0; e < 4; ++e) {
+        hw[e] = pack_bf16x2(v8[2 * e], v8[2 * e + 1]);
+        lw[e] = pack_bf16x2(v8[2 * e] - __uint_as_float(hw[e] << 16), v8[2 * e + 1] - __uint_as_float(hw[e] & 0xFFFF0000u));
       }
+      *(uint4*)mh = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      *(uint4*)ml = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      *(uint4*)ar = *(const uint4*)(AT + i * K::RS_C + j0 * 2);
     }
-    lds_barrier();
-    // ================= the LDS part of the record: -W, A~, M~, gamma_last
-    copy_flat<NT>(rec + RL::WW, WW, RL::QG - RL::WW, tid);
-    copy_flat<NT>(rec + RL::AT, AT, RL::MT - RL::AT, tid);
-    copy_flat<NT>(rec + RL::MT, MT, RL::GC - RL::MT, tid);
-    copy_flat<NT>(rec + RL::GC, (const char*)GC, RL::IMG - RL::GC, tid);
   }
 }
 

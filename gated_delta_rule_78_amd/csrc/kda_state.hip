@@ -1,4 +1,6 @@
-// kda_state.hip -- second pass of the two-pass chunk forward: inter-chunk state propagation.
+// kda_state.hip -- second pass of the two-pass chunk forward for fp32 inputs (d_k = d_v = 64):
+// inter-chunk state propagation over the fp32 records of the fused kernel's first half.
+// (bf16 inputs take the walk of kda_walk.hip.)
 //
 // For every (b, h, value tile) the workgroup walks the chunks in order, carrying the
 // fp32 state S [d_k x VT] in registers (matrix-core accumulator layout), and applies
@@ -425,56 +427,6 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_state_kernel(const c
   }
 }
 
-// Start states of the segments of a split walk: Sst[b, h, 0] = S_0 (or zero) and
-// Sst[b, h, g + 1] = P_g Sst[b, h, g] + B_g, where B_g is segment g's end state from a zero
-// start and P_g (d_k x d_k) its end state from the identity with v = 0 -- the affine
-// transfer of a block of the SFDA page ("Principales Contribuciones", item 3), applied
-// segment by segment.  One workgroup per (b, h, 16 state columns), fp32.
-template <int DK>
-__global__ __launch_bounds__(256) void seg_scan_kernel(const float* __restrict__ s0, const float* __restrict__ P,
-                                                     const float* __restrict__ Bst, float* __restrict__ Sst, int G,
-                                                     int DV) {
-  __shared__ float sS[DK][17];
-  const int nsl = DV / 16, bh = blockIdx.x / nsl, c0 = (blockIdx.x % nsl) * 16;
-  const int tid = threadIdx.x, c = tid & 15, r0 = tid >> 4;  // rows r0 + 16 j
-  constexpr int RJ = DK / 16;
-  const size_t SS = (size_t)DK * DV;
-  float* out0 = Sst + (size_t)bh * G * SS;
-#pragma unroll
-  for (int j = 0; j < RJ; ++j) {
-    const int r = r0 + 16 * j;
-    const float x = s0 ? s0[((size_t)bh * DK + r) * DV + c0 + c] : 0.f;
-    sS[r][c] = x;
-    out0[(size_t)r * DV + c0 + c] = x;
-  }
-  for (int gi = 0; gi + 1 < G; ++gi) {
-    __syncthreads();
-    const float* Pg = P + ((size_t)bh * G + gi) * DK * DK;
-    const float* Bg = Bst + ((size_t)bh * G + gi) * SS;
-    float acc[RJ];
-#pragma unroll
-    for (int j = 0; j < RJ; ++j) {
-      const int r = r0 + 16 * j;
-      float a = Bg[(size_t)r * DV + c0 + c];
-      const float4* prow = (const float4*)(Pg + (size_t)r * DK);
-#pragma unroll 4
-      for (int k4 = 0; k4 < DK / 4; ++k4) {
-        const float4 p = prow[k4];
-        a += p.x * sS[4 * k4][c] + p.y * sS[4 * k4 + 1][c] + p.z * sS[4 * k4 + 2][c] + p.w * sS[4 * k4 + 3][c];
-      }
-      acc[j] = a;
-    }
-    __syncthreads();
-    float* outg = Sst + ((size_t)bh * G + gi + 1) * SS;
-#pragma unroll
-    for (int j = 0; j < RJ; ++j) {
-      const int r = r0 + 16 * j;
-      sS[r][c] = acc[j];
-      outg[(size_t)r * DV + c0 + c] = acc[j];
-    }
-  }
-}
-
 template <typename T, int DK, int VT, bool G2, bool CPX>
 static hipError_t launch_state_t(const ChunkArgs& a, const void* ws) {
   using K = SCfg<T, DK, VT, G2>;
@@ -485,63 +437,6 @@ static hipError_t launch_state_t(const ChunkArgs& a, const void* ws) {
   hipLaunchKernelGGL(kern, dim3(BHc * (a.dv / VT)), dim3(K::NT), 0, (hipStream_t)a.stream, (const char*)ws, a.v,
                      a.s0, a.o, a.sT, a.T, a.H, a.dv, BHc, a.write, a.cu, a.ctab_base, a.gmax, 1, 0, 0);
   return hipGetLastError();
-}
-
-// The split walk (fixed-length bf16 batches at d_k = 128, few (b, h) chains): four launches
-// over G segments per chain, 64 value columns per workgroup, scratch after the records:
-// B [BH G][d_k][d_v], P [BH G][d_k][d_k], segment start states [BH G][d_k][d_v].
-template <bool G2, bool CPX>
-static hipError_t launch_state_split(const ChunkArgs& a, const void* ws, int G) {
-  using K = SCfg<bf16_t, 128, 64, G2>;
-  const int BH = a.B * a.H, NC = (a.T + C - 1) / C, segc = (NC + G - 1) / G;
-  const size_t rec = (size_t)BH * NC * K::RL::BYTES;
-  float* Bst = (float*)((char*)ws + rec);
-  float* P = Bst + (size_t)BH * G * 128 * a.dv;
-  float* Sst = P + (size_t)BH * G * 128 * 128;
-  hipStream_t st = (hipStream_t)a.stream;
-  auto kern = chunk_state_kernel<bf16_t, 128, 64, G2, CPX>;
-  const char* w = (const char*)ws;
-  // (the transfer walk reads neither v nor the write gate: U = M (w o v) = 0)
-  hipLaunchKernelGGL(kern, dim3(BH * G * (a.dv / 64)), dim3(K::NT), 0, st, w, a.v, (const float*)nullptr, a.o, Bst,
-                     a.T, a.H, a.dv, BH, a.write, nullptr, nullptr, 0, G, segc, (int)kSegNoOut);
-  hipLaunchKernelGGL(kern, dim3(BH * G * 2), dim3(K::NT), 0, st, w, a.v, (const float*)nullptr, a.o, P, a.T, a.H,
-                     128, BH, a.write, nullptr, nullptr, 0, G, segc, (int)(kSegNoOut | kSegZeroV | kSegIdentity));
-  hipLaunchKernelGGL(seg_scan_kernel<128>, dim3(BH * (a.dv / 16)), dim3(256), 0, st, a.s0, P, Bst, Sst, G, a.dv);
-  hipLaunchKernelGGL(kern, dim3(BH * G * (a.dv / 64)), dim3(K::NT), 0, st, w, a.v, (const float*)Sst, a.o, a.sT,
-                     a.T, a.H, a.dv, BH, a.write, nullptr, nullptr, 0, G, segc, (int)kSegLastOnly);
-  return hipGetLastError();
-}
-
-// KDA_STATE_SEG=0 keeps the single walk per chain, =G forces G segments (tuning aid)
-static int state_seg_override() {
-  static const int v = [] {
-    const char* e = getenv("KDA_STATE_SEG");
-    return e ? atoi(e) : -1;
-  }();
-  return v;
-}
-
-// The split costs three walks of NC / G chunks at 64 columns per workgroup (about 3.1 us
-// per chunk) against one walk of NC chunks on narrower tiles (about 1.9 us per chunk at 16
-// columns, with half the compute units idle or fewer): it pays from about G = 5 on, and is
-// taken from G = 8 (the measured B1 H16 T128K case: 3.93 -> 2.12 ms).
-int state_segments(int B, int T, int H, int dk, int dv, bool bf16) {
-  if (!bf16 || dk != 128 || (dv != 64 && dv != 128)) return 1;
-  const int NC = (T + C - 1) / C, o = state_seg_override();
-  if (o >= 0) {
-    const int G = min(o, NC / 16);
-    return G >= 2 ? G : 1;
-  }
-  const long tiles = (long)B * H * (dv / 64);  // 64-column tiles of one walk per chain
-  if (tiles <= 0 || tiles >= 256) return 1;
-  const int G = min((int)((256 + tiles - 1) / tiles), NC / 16);  // at least 16 chunks per segment
-  return G >= 8 ? G : 1;
-}
-
-size_t state_split_bytes(int B, int T, int H, int dk, int dv, bool bf16) {
-  const int G = state_segments(B, T, H, dk, dv, bf16);
-  if (G < 2) return 0;
-  return (size_t)B * H * G * dk * (2 * (size_t)dv + dk) * sizeof(float);
 }
 
 // KDA_STATE_VT=16|32|64 pins the state pass's value-tile width (tuning aid)
@@ -579,22 +474,16 @@ static hipError_t launch_state_vt(const ChunkArgs& a, const void* ws) {
   }
 }
 
-template <bool G2, bool CPX = false>
+template <bool G2>
 static hipError_t launch_state_g(const ChunkArgs& a, const void* ws) {
-  if (!a.bf16) return a.dk == 64 && a.dv == 64 ? launch_state_vt<float, 64, G2, CPX>(a, ws) : hipErrorInvalidValue;
-  return a.dk == 64 ? launch_state_vt<bf16_t, 64, G2, CPX>(a, ws) : launch_state_vt<bf16_t, 128, G2, CPX>(a, ws);
+  return a.dk == 64 && a.dv == 64 ? launch_state_vt<float, 64, G2, false>(a, ws) : hipErrorInvalidValue;
 }
 
+// fp32 records (RecordLayout) are walked here; bf16 ones by launch_walk (kda_walk.hip)
 hipError_t launch_state(const ChunkArgs& a, const void* ws) {
   if ((a.cu ? a.n_seqs : a.B) * a.H == 0) return hipSuccess;
-  if (!a.cu) {
-    const int G = state_segments(a.B, a.T, a.H, a.dk, a.dv, a.bf16);
-    if (G >= 2) {
-      if (a.cpx) return a.write ? hipErrorInvalidValue : launch_state_split<false, true>(a, ws, G);
-      return a.write ? launch_state_split<true, false>(a, ws, G) : launch_state_split<false, false>(a, ws, G);
-    }
-  }
-  if (a.cpx) return a.write ? hipErrorInvalidValue : launch_state_g<false, true>(a, ws);
+  if (a.bf16) return launch_walk(a, ws);
+  if (a.cpx) return hipErrorInvalidValue;
   return a.write ? launch_state_g<true>(a, ws) : launch_state_g<false>(a, ws);
 }
 

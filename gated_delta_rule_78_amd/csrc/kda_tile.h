@@ -111,6 +111,44 @@ __device__ __forceinline__ void full_barrier() {
 #endif
 }
 
+// Running gate products on an item's channel pair (2c, 2c+1).  Real gates (KDA / CKDA /
+// Gated DeltaNet-2): two independent channels, (x, y) their products.  Complex gates
+// (SFDA page, "Arquitectura Central": the pair is one complex coordinate and its gate the
+// complex number lambda = (Re, Im) in channels (2c, 2c+1)): (x, y) = (Re, Im) of the
+// product.  The row side of a decayed product takes the conjugate (the transpose of a
+// rotation-decay block), the column side the product itself:
+//   r_ij = F_i B_j,  x_i^T R_ij y_j = (conj(F_i) x_i) . (B_j y_j)  over real channel pairs.
+template <bool CPX>
+struct Gp2 {
+  float x, y;
+  __device__ __forceinline__ static Gp2 one() { return Gp2{1.f, CPX ? 0.f : 1.f}; }
+  __device__ __forceinline__ Gp2 operator*(const Gp2& o) const {
+    if constexpr (CPX) return Gp2{x * o.x - y * o.y, x * o.y + y * o.x};
+    else return Gp2{x * o.x, y * o.y};
+  }
+  __device__ __forceinline__ void operator*=(const Gp2& o) { *this = *this * o; }
+  // row-side operand of the pair (v0, v1): conj(F) v (complex) or (F0 v0, F1 v1)
+  __device__ __forceinline__ void row(float v0, float v1, float& r0, float& r1) const {
+    if constexpr (CPX) {
+      r0 = x * v0 + y * v1;
+      r1 = x * v1 - y * v0;
+    } else {
+      r0 = v0 * x;
+      r1 = v1 * y;
+    }
+  }
+  // column-side operand: B v (complex) or (B0 v0, B1 v1)
+  __device__ __forceinline__ void col(float v0, float v1, float& r0, float& r1) const {
+    if constexpr (CPX) {
+      r0 = x * v0 - y * v1;
+      r1 = x * v1 + y * v0;
+    } else {
+      r0 = v0 * x;
+      r1 = v1 * y;
+    }
+  }
+};
+
 }  // namespace
 
 }  // namespace kda

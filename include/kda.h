@@ -139,23 +139,26 @@ int kda_chunk_fwd_ws(const kda_shape* shape, const void* q, const void* k, const
 
 /*
  * The two passes of kda_chunk_fwd_ws as separate calls (same workspace rules).
- * A chunk's record depends only on q, k, alpha and beta: it is the chunk's exact
- * affine block transfer (SFDA page, "Principales Contribuciones" item 3) less the
- * part that v and the state enter linearly, so one set of records can be applied
- * to several v / start-state pairs of the same shape.
+ * A chunk's record depends only on q, k, alpha and beta: with the chunk's q, k and
+ * alpha it fixes the chunk's exact affine block transfer (SFDA page, "Principales
+ * Contribuciones" item 3) less the part that v and the state enter linearly, so one
+ * set of records can be applied to several v / start-state pairs of the same shape.
  *   kda_chunk_records       : reads q, k, alpha, beta [layouts as kda_chunk_fwd];
  *                             writes the records of every (b, h, chunk).
- *   kda_chunk_apply_records : reads the records, v and initial_state (NULL = zero);
- *                             writes o and final_state (NULL = not written; may equal
- *                             initial_state).  The workspace is only read.
+ *   kda_chunk_apply_records : reads the records, q, k, alpha (the same tensors the
+ *                             records were made from: the walk rebuilds Q o gamma,
+ *                             K o gamma and K o rho from them), v and initial_state
+ *                             (NULL = zero); writes o and final_state (NULL = not
+ *                             written; may equal initial_state).  The workspace is only
+ *                             read.
  * shape->dv is checked but does not change the records.  Errors as kda_chunk_fwd_ws;
  * a NULL workspace is KDA_ERR_NULL unless the shape needs none (B*T == 0).
  */
 int kda_chunk_records(const kda_shape* shape, const void* q, const void* k, const void* alpha,
                       const void* beta, void* workspace, size_t workspace_bytes, void* stream);
-int kda_chunk_apply_records(const kda_shape* shape, const void* workspace, size_t workspace_bytes,
-                            const void* v, const float* initial_state, void* o, float* final_state,
-                            void* stream);
+int kda_chunk_apply_records(const kda_shape* shape, const void* q, const void* k, const void* alpha,
+                            const void* workspace, size_t workspace_bytes, const void* v,
+                            const float* initial_state, void* o, float* final_state, void* stream);
 
 /*
  * Packed variable-length batch (two-pass forward): n_seqs sequences lie back to back

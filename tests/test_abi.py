@@ -135,8 +135,8 @@ def test_records_and_apply_argument_errors(L):
     def rec(q=_p(0), k=_p(1), a=_p(3), b=_p(4), ws=_p(9), n=need, sh=shape):
         return L.kda_chunk_records(ctypes.byref(sh), q, k, a, b, ws, sz(n), None)
 
-    def app(ws=_p(9), n=need, v=_p(2), s0=None, o=_p(5), sT=None):
-        return L.kda_chunk_apply_records(ctypes.byref(shape), ws, sz(n), v, s0, o, sT, None)
+    def app(ws=_p(9), n=need, v=_p(2), s0=None, o=_p(5), sT=None, q=_p(0), k=_p(1), a=_p(3)):
+        return L.kda_chunk_apply_records(ctypes.byref(shape), q, k, a, ws, sz(n), v, s0, o, sT, None)
 
     assert rec(q=None) == NULL
     assert rec(b=None) == NULL
@@ -146,6 +146,9 @@ def test_records_and_apply_argument_errors(L):
     assert rec(ws=_p(3)) == ALIAS                        # workspace over alpha
     assert rec(sh=kda.Shape(1, 64, 2, 64, 64, 64, 1), n=need) == WORKSPACE   # fp32 records are larger
     assert app(v=None) == NULL
+    assert app(q=None) == NULL                           # the walk rebuilds its key operands
+    assert app(a=None) == NULL
+    assert app(o=_p(1)) == ALIAS                         # output over k
     assert app(o=None) == NULL
     assert app(ws=None) == NULL
     assert app(n=0) == WORKSPACE

@@ -16,29 +16,22 @@ from kda_testutil import TOL, heads_of, inputs_to_dev, rel_err_slices, state_to_
 pytestmark = pytest.mark.gpu
 
 
-def _gpu(inp, S0, fused_records=False):
-    import os
+def _gpu(inp, S0):
     import gated_delta_rule_78_amd as kda
     import torch
     q, k, v, a, _ = inputs_to_dev(inp)
     e, w = to_dev(inp.erase, inp.dtype), to_dev(inp.write, inp.dtype)
     s0 = None if S0 is None else state_to_dev(S0)
-    if fused_records:  # bf16 records from the first half of the fused kernel
-        os.environ["KDA_RECORDS_FUSED"] = "1"
-    try:
-        o, sT = kda.gdn2_chunk_fwd(q, k, v, a, e, w, initial_state=s0)
-        torch.cuda.synchronize()
-    finally:
-        os.environ.pop("KDA_RECORDS_FUSED", None)
+    o, sT = kda.gdn2_chunk_fwd(q, k, v, a, e, w, initial_state=s0)
+    torch.cuda.synchronize()
     return o.float().cpu().numpy(), sT.cpu().numpy()
 
 
-def _check(inp, S0, heads=None, label="", fused_records=False):
+def _check(inp, S0, heads=None, label=""):
     m = inp.meta
     B, T, H, dk, dv = m["B"], m["T"], m["H"], m["dk"], m["dv"]
-    print(f"gdn2 {label} B={B} T={T} H={H} dk={dk} dv={dv} {inp.dtype} fused_records={fused_records}",
-          flush=True)
-    o_gpu, s_gpu = _gpu(inp, S0, fused_records)
+    print(f"gdn2 {label} B={B} T={T} H={H} dk={dk} dv={dv} {inp.dtype}", flush=True)
+    o_gpu, s_gpu = _gpu(inp, S0)
     sel = list(range(B * H)) if heads is None else list(heads)
     s0_ref = None if S0 is None else S0.reshape(B * H, dk, dv)[sel]
     o_ref, s_ref = oracle.fwd_gdn2(inp.q, inp.k, inp.v, inp.alpha, inp.erase, inp.write, S0=s0_ref, heads=sel,
@@ -56,11 +49,10 @@ def test_gdn2_lengths(T):
     _check(inp, inp.S0, label=f"T{T}")
 
 
-@pytest.mark.parametrize("fused_records", [False, True])
 @pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64)])
-def test_gdn2_head_widths(dk, dv, fused_records):
+def test_gdn2_head_widths(dk, dv):
     inp = make(2, 150, 3, dk, dv, "bf16", "gdn2", False, seed=17 + dk + dv)
-    _check(inp, inp.S0, label=f"d{dk}x{dv}", fused_records=fused_records)
+    _check(inp, inp.S0, label=f"d{dk}x{dv}")
 
 
 def test_gdn2_fp32():

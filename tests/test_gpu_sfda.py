@@ -75,14 +75,20 @@ def test_sfda_quarter_turns_zeros_and_unit_gates():
     _check(inp, inp.S0, label="special gates")
 
 
-def test_sfda_zero_phases_match_kda_path():
+@pytest.mark.parametrize("zero_per_chunk", [True, False])
+def test_sfda_zero_phases_match_kda_path(zero_per_chunk):
     """Im lambda = 0 with both channels of a pair decayed by Re lambda is KDA: the SFDA
-    path and the KDA two-pass path agree to rounding."""
+    path and the KDA two-pass path agree.  With one zero gate pair in every chunk both
+    take the first pass's level products (the complex gates always do), the same
+    arithmetic: agreement to 1e-3.  Without it the KDA gates take the ratio products,
+    which round differently: agreement within the bf16 bar."""
     import gated_delta_rule_78_amd as kda
     import torch
     inp = make(2, 200, 3, 128, 128, "bf16", "kda", False, seed=67)
     a = as_float(inp.alpha, "bf16")
     tied = np.repeat(a[..., 0::2], 2, axis=-1)
+    if zero_per_chunk:
+        tied[:, [37, 101, 165, 195], :, 10:12] = 0.0  # one in each of the four chunks
     lam = tied.copy()
     lam[..., 1::2] = 0.0
     inp.alpha = bf16_bits(tied)
@@ -94,8 +100,9 @@ def test_sfda_zero_phases_match_kda_path():
     o2, s2 = kda.chunk_fwd(q, k, v, at, b, initial_state=s0, path="twopass")
     torch.cuda.synchronize()
     f = lambda x: x.float().cpu().numpy().transpose(0, 2, 1, 3).reshape(6, -1)
-    assert rel_err_slices(f(o1), f(o2), 6) < 1e-3
-    assert rel_err_slices(s1.cpu().numpy().reshape(6, -1), s2.cpu().numpy().reshape(6, -1), 6) < 1e-3
+    tol = 1e-3 if zero_per_chunk else TOL["bf16"]
+    assert rel_err_slices(f(o1), f(o2), 6) < tol
+    assert rel_err_slices(s1.cpu().numpy().reshape(6, -1), s2.cpu().numpy().reshape(6, -1), 6) < tol
 
 
 def test_sfda_full_prefill_8k_sampled():
