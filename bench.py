@@ -45,14 +45,16 @@ PMC_FILES = {
     "chunk_records": (os.path.join(ROOT, "profiles", "chunk_records_kda_prefill_8k_counters.md"),
                       ["kda_records.hip", "kda_tile.h", "kda_record.h", "kda_common.h"]),
     "chunk_state": (os.path.join(ROOT, "profiles", "chunk_state_kda_prefill_8k_counters.md"),
-                    ["kda_state.hip", "kda_tile.h", "kda_record.h", "kda_common.h"]),
+                    ["kda_walk.hip", "kda_tile.h", "kda_record.h", "kda_common.h"]),
     "chunk_fused": (os.path.join(ROOT, "profiles", "chunk_fused_kda_prefill_8k_counters.md"),
                     ["kda_chunk.hip", "kda_tile.h", "kda_common.h"]),
     "decode": (os.path.join(ROOT, "profiles", "decode_ckda_decode_b256_counters.md"),
                ["kda_decode.hip", "kda_common.h"]),
 }
-RECORD_PAYLOAD = {128: 3 * 64 * 128 * 2 + 2 * 64 * 64 * 2 + 128 * 4,   # -W, QG, KRT, A, M~ (bf16), gamma (fp32)
-                  64: 3 * 64 * 64 * 2 + 2 * 64 * 64 * 2 + 64 * 4}
+# the bf16 walk record of one (b, h, chunk): A, M~ hi and M~ lo, three lower 64 x 64 bf16
+# matrices stored as row-major blocks with 16 pad bytes per row (the image the state pass
+# moves into LDS as it is)
+RECORD_BYTES = {128: 21504, 64: 21504}
 
 
 def chunk_bytes(B, T, H, dk, dv, es=2):
@@ -70,18 +72,18 @@ def chunk_flops(B, T, H, dk, dv, C=64):
 
 
 def records_bytes(B, T, H, dk, es=2):
-    """Algorithmic bytes of one kda_chunk_records launch: q, k, alpha, beta read once,
-    one record per (b, h, chunk) written (its data: the padding of the LDS-image rows
-    is not counted)."""
+    """Own bytes of one kda_chunk_records launch: q, k, alpha, beta read once, one record
+    per (b, h, chunk) written."""
     nch = (T + 63) // 64
-    return B * T * H * es * (3 * dk + 1) + B * H * nch * RECORD_PAYLOAD[dk]
+    return B * T * H * es * (3 * dk + 1) + B * H * nch * RECORD_BYTES[dk]
 
 
 def state_bytes(B, T, H, dk, dv, es=2):
-    """Algorithmic bytes of one kda_chunk_apply_records launch: every record read once,
-    v read and o written once, start state read and final state written."""
+    """Own bytes of one kda_chunk_apply_records launch: every record read once, q, k,
+    alpha, v read and o written once, start state read and final state written."""
     nch = (T + 63) // 64
-    return B * H * nch * RECORD_PAYLOAD[dk] + B * T * H * es * 2 * dv + 2 * B * H * dk * dv * 4
+    return (B * H * nch * RECORD_BYTES[dk] + B * T * H * es * (3 * dk + 2 * dv)
+            + 2 * B * H * dk * dv * 4)
 
 
 def decode_bytes(B, H, dk, dv, es=2, tokens=1):
@@ -344,14 +346,38 @@ def bench_decode_tokens(ntok, log, reps=3):
     return w, float(np.median(times)), ntok
 
 
+def host_cpus():
+    """(threads to use, description): the CPUs this process may run on, bounded by the
+    cgroup CPU quota where one is set (more threads than the quota only time-slice)."""
+    n = len(os.sched_getaffinity(0))
+    note = f"{n} CPUs in the affinity mask"
+    try:
+        quota, period = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        if quota != "max":
+            lim = max(1, int(-(-int(quota) // int(period))))
+            note += f", cgroup quota {int(quota) / int(period):g} CPUs"
+            n = min(n, lim)
+    except (OSError, ValueError):
+        pass
+    model = "unknown CPU"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return n, f"{model}; {note}"
+
+
 def cpu_baseline(inp, budget_s, log):
     """The fp64 oracle on whole sequences of a sample of heads of the prefill
-    workload; value scaled to the metric's unit (tokens/s across all H heads)."""
+    workload, on every CPU this process may use; value scaled to the metric's unit
+    (tokens/s across all H heads)."""
     import oracle
     m = inp.meta
     B, T, H = m["B"], m["T"], m["H"]
-    cores = len(os.sched_getaffinity(0))
-    cores = min(cores, 16)
+    cores, cpu = host_cpus()
     t0 = time.time()
     oracle.fwd(inp.q, inp.k, inp.v, inp.alpha, inp.beta, S0=inp.S0.reshape(B * H, m["dk"], m["dv"])[:1],
                heads=[0], col_block=max(1, m["dv"] // cores), nthreads=cores, want_o=True)
@@ -364,9 +390,10 @@ def cpu_baseline(inp, budget_s, log):
                col_block=max(1, (m["dv"] * n) // (4 * cores)) if n < 4 * cores else m["dv"],
                nthreads=cores, want_o=True)
     dt = time.time() - t0
-    log(f"[bench] cpu oracle: {n} heads x T={T} in {dt:.1f}s on {cores} threads")
+    log(f"[bench] cpu oracle: {n} heads x T={T} in {dt:.1f}s on {cores} threads ({cpu})")
     head_tokens_per_s = n * T / dt
     return {"value": head_tokens_per_s / H, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu": cpu,
             "sample": f"{n} of {B * H} (b,h) heads of the B={B} H={H} T={T} d=128 KDA prefill, whole "
                       f"sequences, fp64, {dt:.1f}s wall"}
 
@@ -431,11 +458,15 @@ def main():
     nbytes = chunk_bytes(w.B, w.T, w.H, w.dk, w.dv)
     path_gbs = nbytes / (ms * 1e-3) / 1e9
     flops = chunk_flops(w.B, w.T, w.H, w.dk, w.dv)
-    # roofline of the dominant kernel: its algorithmic bytes over its own mean duration
+    # roofline of the dominant kernel: the path's algorithmic bytes per launch (each launch
+    # of the path covers all B*T*H head-tokens: 1,282 B each plus the two states) over that
+    # kernel's own mean duration; beside it the whole path against the same floor
     dom = max(res["kernels"], key=res["kernels"].get)
     dom_ms = res["kernels"][dom]
-    dom_bytes = kernel_bytes(dom, w)
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    achieved = nbytes / (dom_ms * 1e-3) / 1e9
+    roof_tokens_per_s = tokens / (nbytes / (HBM_PEAK_GBS * 1e9))
+    own = {k2: {"ms": t2, "own_bytes": kernel_bytes(k2, w), "own_gbs": kernel_bytes(k2, w) / (t2 * 1e-3) / 1e9}
+           for k2, t2 in res["kernels"].items()}
     out = {
         "metric": "chunk-fwd tokens/s (H=32,d=128,T=8K bf16) + decode state GB/s, % of roofline",
         "value": value,
@@ -454,13 +485,13 @@ def main():
                    "chunk": 64, "state": "fp32", "tokens_per_step": tokens, "path": res["path"]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": stored_traffic(dom),
-                     "kernel": dom, "kernel_ms": dom_ms, "algorithmic_bytes_per_launch": dom_bytes,
-                     "kernels_ms": res["kernels"],
+                     "kernel": dom, "kernel_ms": dom_ms, "algorithmic_bytes_per_launch": nbytes,
+                     "algorithmic_bytes_per_head_token": chunk_bytes(1, 1, 1, w.dk, w.dv) - 2 * w.dk * w.dv * 4,
+                     "path_frac": value / roof_tokens_per_s, "path_roofline_tokens_per_s": roof_tokens_per_s,
+                     "path_ms": ms, "kernel_own_traffic": own,
                      "rocprof_busy": {k2: stored_util(k2) for k2 in res["kernels"] if k2 in UTIL_FILES},
-                     "path": {"algorithmic_bytes_per_step": nbytes, "achieved_gbs": path_gbs,
-                              "frac_hbm": path_gbs / HBM_PEAK_GBS,
-                              "mfma_tflops_algorithmic": flops / (ms * 1e-3) / 1e12,
-                              "mfma_frac_algorithmic": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}},
+                     "mfma": {"tflops_algorithmic": flops / (ms * 1e-3) / 1e12,
+                              "frac_bf16_peak": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}},
     }
     log(f"[bench] kda prefill ({res['path']}): {ms:.3f} ms/step, {value:.4g} tokens/s; "
         + ", ".join(f"{k2} {v2:.3f} ms" for k2, v2 in res["kernels"].items()))

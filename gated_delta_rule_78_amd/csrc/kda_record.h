@@ -13,19 +13,15 @@
 //
 // WalkRecord<DK> (bf16 inputs): only what the key and query sides cannot rebuild cheaply.
 // The state pass re-reads q, k and alpha and forms Q o gamma, K o gamma and K o rho itself
-// from the gate products stored here, so the record carries the two 64 x 64 chunk matrices
-// and the block products:
+// (the gate products are running products of alpha inside the chunk), so the record
+// carries the two 64 x 64 chunk matrices:
 //   A    lower 64 x 64, bf16      A_ij = sum_c q_ic k_jc r_ijc (j <= i)
 //   MH   lower 64 x 64, bf16      M~ = (I + T)^-1 diag(beta) rounded to bf16
 //   ML   lower 64 x 64, bf16      M~ - MH rounded to bf16 (MH + ML carries M~ to ~2^-17)
-//   GP   [3][DK] fp32             product of the gates of the 16-row blocks before block I = 1..3
-//   RP   [3][DK] fp32             product of the gates of the blocks after block I = 0..2
-//   G63  [DK] fp32                gamma of the chunk's last row (product of all 64 gates)
 // A lower matrix is stored as two row-major images: rows 0..31 with columns 0..31 (rows of
 // 80 bytes) and rows 32..63 with columns 0..63 (rows of 144 bytes); the 16 pad bytes per
-// row keep the state pass's LDS reads free of bank conflicts.  The first DMA bytes (A, MH,
-// ML) are moved into LDS as one image; the gate products are read into registers.
-// For complex (SFDA) gates the gate products hold (Re, Im) in each key-channel pair.
+// row keep the state pass's LDS reads free of bank conflicts.  The state pass moves the
+// whole record into LDS as one image.
 #pragma once
 #include <stddef.h>
 
@@ -59,11 +55,7 @@ struct WalkRecord {
   static constexpr int MH = MAT;
   static constexpr int ML = 2 * MAT;
   static constexpr int DMA = 3 * MAT;  // moved into LDS by the state pass
-  static constexpr int GP = DMA;
-  static constexpr int RP = GP + 3 * DK * 4;
-  static constexpr int G63 = RP + 3 * DK * 4;
-  static constexpr int IMG = G63 + DK * 4;
-  static constexpr size_t BYTES = ((size_t)IMG + 255) / 256 * 256;
+  static constexpr size_t BYTES = ((size_t)DMA + 255) / 256 * 256;
   static_assert(DMA % 1024 == 0, "whole wave-wide DMA steps");
   // byte offset of element (i, j), j <= 31 for i <= 31, of a lower matrix image
   __host__ __device__ static constexpr int at(int i, int j) {

@@ -346,25 +346,6 @@ __global__ __launch_bounds__(256, 2) void chunk_records_kernel(
       lds_barrier();
       ratio = (OKW[0] & OKW[1] & OKW[2] & OKW[3]) != 0;
     }
-    // the record's gate products: GP[I - 1] = prod of blocks < I, RP[I] = prod of blocks > I,
-    // G63 = all four (one channel pair per thread)
-    if (tid < DK / 2) {
-      float* GP = (float*)(rec + RL::GP);
-      float* RP = (float*)(rec + RL::RP);
-      float* GL = (float*)(rec + RL::G63);
-      const int c2 = 2 * tid;
-      // (this thread's item is (block 0, pair tid): t0v..t3v are its pair's block totals)
-      const G p01 = t0v * t1v, p23 = t2v * t3v;
-      const G gp[3] = {t0v, p01, p01 * t2v};
-      const G rp[3] = {t1v * p23, p23, t3v};
-#pragma unroll
-      for (int I = 0; I < 3; ++I) {
-        *(float2*)(GP + I * DK + c2) = make_float2(gp[I].x, gp[I].y);
-        *(float2*)(RP + I * DK + c2) = make_float2(rp[I].x, rp[I].y);
-      }
-      const G gl = p01 * p23;
-      *(float2*)(GL + c2) = make_float2(gl.x, gl.y);
-    }
     float* const TT = (float*)(R_L + K::OFF_TT);
     char* const AT = R_L + K::OFF_AT;
 

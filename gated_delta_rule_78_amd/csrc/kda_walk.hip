@@ -54,6 +54,140 @@ __device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
 #endif
 }
 
+// LDS stores of the producer waves' operands, written as instructions the compiler does
+// not analyse: it cannot tell the operand tiles from the destination of the DMA still in
+// flight and would otherwise wait for that DMA (and every load issued after it) before the
+// first operand store.  The stores complete before the step barrier (lgkmcnt(0) there).
+__device__ __forceinline__ uint32_t lds_off(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void lds_st32(void* p, uint32_t v) {
+#ifndef KDA_HOST_PASS
+  asm volatile("ds_write_b32 %0, %1" ::"v"(lds_off(p)), "v"(v) : "memory");
+#endif
+}
+__device__ __forceinline__ void lds_st64(void* p, float x, float y) {
+#ifndef KDA_HOST_PASS
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  f2 v = {x, y};
+  asm volatile("ds_write_b64 %0, %1" ::"v"(lds_off(p)), "v"(v) : "memory");
+#endif
+}
+__device__ __forceinline__ void lds_st128(void* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+#ifndef KDA_HOST_PASS
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  u4 v = {a, b, c, d};
+  asm volatile("ds_write_b128 %0, %1" ::"v"(lds_off(p)), "v"(v) : "memory");
+#endif
+}
+
+// The gate product v of the lane CTRL's DPP row shift points at (row_shr:d = 0x110 + d,
+// row_shl:d = 0x100 + d), or the identity where that lane lies outside the 16-lane row.
+template <typename G, int CTRL>
+__device__ __forceinline__ G dpp_fill(const G& v) {
+  const G one = G::one();
+  auto f = [](float old, float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                                 __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+  };
+  return G{f(one.x, v.x), f(one.y, v.y)};
+}
+
+// Inclusive products along each 16-lane DPP row of eight values: I over the lanes up to
+// this one, J over the lanes from this one on (lane i multiplies in lane i -+ d for
+// d = 1, 2, 4, 8; a lane whose partner lies outside the row is left as it is).  The 16
+// chains are interleaved, so no cross-lane read follows the write of its source closely
+// (the leading s_nop covers the inputs' writes).
+__device__ __forceinline__ void row_scan16(float (&I)[8], float (&J)[8]) {
+#ifndef KDA_HOST_PASS
+  asm volatile(
+      "s_nop 1\n"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %1, %1, %1 row_shr:1 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %2, %2, %2 row_shr:1 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %3, %3, %3 row_shr:1 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %4, %4, %4 row_shr:1 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %5, %5, %5 row_shr:1 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %6, %6, %6 row_shr:1 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %7, %7, %7 row_shr:1 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %8, %8, %8 row_shl:1 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %9, %9, %9 row_shl:1 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %10, %10, %10 row_shl:1 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %11, %11, %11 row_shl:1 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %12, %12, %12 row_shl:1 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %13, %13, %13 row_shl:1 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %14, %14, %14 row_shl:1 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %15, %15, %15 row_shl:1 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %1, %1, %1 row_shr:2 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %2, %2, %2 row_shr:2 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %3, %3, %3 row_shr:2 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %4, %4, %4 row_shr:2 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %5, %5, %5 row_shr:2 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %6, %6, %6 row_shr:2 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %7, %7, %7 row_shr:2 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %8, %8, %8 row_shl:2 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %9, %9, %9 row_shl:2 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %10, %10, %10 row_shl:2 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %11, %11, %11 row_shl:2 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %12, %12, %12 row_shl:2 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %13, %13, %13 row_shl:2 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %14, %14, %14 row_shl:2 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %15, %15, %15 row_shl:2 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %1, %1, %1 row_shr:4 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %2, %2, %2 row_shr:4 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %3, %3, %3 row_shr:4 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %4, %4, %4 row_shr:4 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %5, %5, %5 row_shr:4 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %6, %6, %6 row_shr:4 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %7, %7, %7 row_shr:4 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %8, %8, %8 row_shl:4 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %9, %9, %9 row_shl:4 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %10, %10, %10 row_shl:4 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %11, %11, %11 row_shl:4 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %12, %12, %12 row_shl:4 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %13, %13, %13 row_shl:4 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %14, %14, %14 row_shl:4 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %15, %15, %15 row_shl:4 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %1, %1, %1 row_shr:8 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %2, %2, %2 row_shr:8 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %3, %3, %3 row_shr:8 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %4, %4, %4 row_shr:8 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %5, %5, %5 row_shr:8 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %6, %6, %6 row_shr:8 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %7, %7, %7 row_shr:8 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %8, %8, %8 row_shl:8 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %9, %9, %9 row_shl:8 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %10, %10, %10 row_shl:8 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %11, %11, %11 row_shl:8 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %12, %12, %12 row_shl:8 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %13, %13, %13 row_shl:8 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %14, %14, %14 row_shl:8 row_mask:0xf bank_mask:0xf\n"
+      "v_mul_f32_dpp %15, %15, %15 row_shl:8 row_mask:0xf bank_mask:0xf\n"
+      : "+v"(I[0]), "+v"(I[1]), "+v"(I[2]), "+v"(I[3]), "+v"(I[4]), "+v"(I[5]), "+v"(I[6]), "+v"(I[7]), "+v"(J[0]), "+v"(J[1]), "+v"(J[2]), "+v"(J[3]), "+v"(J[4]), "+v"(J[5]), "+v"(J[6]), "+v"(J[7]));
+#endif
+}
+
+// The producers' workgroup barrier: their LDS writes are complete and every vector-memory
+// operation but the last N they issued (the vector-memory counter retires in issue order).
+template <int N>
+__device__ __forceinline__ void producer_barrier() {
+#ifndef KDA_HOST_PASS
+  static_assert(N >= 0 && N < 64, "6-bit vmcnt");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);  // vmcnt(N) expcnt(7) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+#endif
+}
+
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
 // fp32 pair -> bf16 pair hi = bf16(x) and the rounding residual lo = bf16(x - hi)
 __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
   hi = pack_bf16x2(x0, x1);
@@ -89,8 +223,7 @@ struct WCfg {
   static constexpr int V_BYTES = C * RS_V;
   static constexpr int N_DMA_REC = RL::DMA / 1024;
   static constexpr int N_DMA_V = C * UPR / 64;
-  static constexpr int GRP = DK / 2;  // gate items per 16-row block
-  static constexpr int NITEM = NB * GRP;
+  static constexpr int NITEM = 2 * DK;  // gate items: 16 row groups x DK / 8 channel groups
   static_assert(NITEM <= NP * 64, "one gate item per producer lane");
   static_assert(N_DMA_V * 64 == C * UPR, "v tile split");
   static_assert(2 * (OPS + RL::DMA + V_BYTES) <= 160 * 1024, "LDS budget");
@@ -98,6 +231,10 @@ struct WCfg {
   // bits 1..3 of the row, so the sixteen rows a matrix-core fragment load touches (and
   // the two rows a gate item writes) spread over all LDS banks without row padding
   __device__ static constexpr int kt_unit(int c, int u) { return c * RS_KT + 16 * (u ^ ((c >> 1) & 7)); }
+  // v tile: LDS unit u of row r holds the tile's 16-byte unit u ^ vsw(r) (the DMA and the
+  // output store apply the same permutation), so the four row groups 4g + e that a
+  // fragment's lanes read fall on different banks
+  __device__ static constexpr int vsw(int r) { return ((r >> 2) & 3) * 2 & (UPR - 1); }
 };
 
 // flags of a split walk (launch_walk_split): no output stores; v read as zero; start from
@@ -126,12 +263,45 @@ __device__ __forceinline__ void walk_chunk(const char* ops, const char* rec, cha
   const float* OG = (const float*)(ops + K::OFF_G);
   const int col = 16 * wave + n;
 
-  // R = V - (K o gamma) (S_hi + S_lo)  (the operand tile holds -(K o gamma)); O = (Q o gamma) S_hi
-  // (one base address, rows at immediate offsets; the tile is read whole and the rows past
-  // the end masked, so no per-row address or branch)
-  char* const vb = vv + 4 * g * K::RS_V + col * 2;
+  // (one base address for this lane's column of the v tile, rows at immediate offsets; the
+  // tile is read whole and the rows past the end masked, so no per-row address or branch).
+  // Rows 16 I + 4g + e share the unit permutation of row 4g (vsw depends on bits 2, 3).
+  char* const vb = vv + 4 * g * K::RS_V + 16 * ((col >> 3) ^ K::vsw(4 * g)) + (col & 7) * 2;
   const int nvl = zero_v ? 0 : nv - 4 * g;  // rows 16 I + e of this lane that exist: 16 I + e < nvl
+  // The operand fragments of each group of products are loaded one group ahead and the
+  // scheduling fences keep them there: with one compute wave per SIMD little else hides
+  // the LDS latency.
+  auto ld_kq = [&](int ks, Frag<bf16_t> (&fk)[NB], Frag<bf16_t> (&fq)[NB]) __attribute__((always_inline)) {
+    const int c0 = 32 * ks + 4 * g;
+#pragma unroll
+    for (int I = 0; I < NB; ++I) {
+      const char* krow = OK + (16 * I + n) * K::RS_Q;
+      const char* qrow = OQ + (16 * I + n) * K::RS_Q;
+      fk[I].load4x2(krow + c0 * 2, krow + (c0 + 16) * 2);
+      fq[I].load4x2(qrow + c0 * 2, qrow + (c0 + 16) * 2);
+    }
+  };
+  // (I, s2) of the six lower 16 x 32 blocks of a 64 x 64 record matrix
+  auto blk_I = [](int j) { return j < 2 ? j : 2 + (j - 2) / 2; };
+  auto blk_s = [](int j) { return j < 2 ? 0 : (j - 2) % 2; };
+  auto ld_rec = [&](int mat, int j, Frag<bf16_t>& f) __attribute__((always_inline)) {
+    const int I = blk_I(j), s2 = blk_s(j);
+    f.load4x2(rec + mat + RL::at(16 * I + n, 32 * s2 + 4 * g), rec + mat + RL::at(16 * I + n, 32 * s2 + 16 + 4 * g));
+  };
+  auto ld_kt = [&](int r, Frag<bf16_t> (&fk)[2]) __attribute__((always_inline)) {
+    const int kc = 16 * r + n;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      // positions 32 s2 + 4g .. +3 and 32 s2 + 16 + 4g .. +3: units 4 s2 + g / 2 and + 2, half g & 1
+      const int u = 4 * s2 + (g >> 1), h8 = 8 * (g & 1);
+      fk[s2].load4x2(OKT + K::kt_unit(kc, u) + h8, OKT + K::kt_unit(kc, u + 2) + h8);
+    }
+  };
+
+  // R = V - (K o gamma) (S_hi + S_lo)  (the operand tile holds -(K o gamma)); O = (Q o gamma) S_hi
   f32x4_t Rr[NB], O[NB];
+  Frag<bf16_t> fk[2][NB], fq[2][NB];
+  ld_kq(0, fk[0], fq[0]);
 #pragma unroll
   for (int I = 0; I < NB; ++I) {
 #pragma unroll
@@ -142,27 +312,32 @@ __device__ __forceinline__ void walk_chunk(const char* ops, const char* rec, cha
     }
     O[I] = zero4();
   }
+  fence_sched();
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
+    if (ks + 1 < KS) ld_kq(ks + 1, fk[(ks + 1) & 1], fq[(ks + 1) & 1]);
+    fence_sched();
     // S as hi / lo B fragments (k-slots: rows 32 ks + 4g + e and 32 ks + 16 + 4g + e)
     Frag<bf16_t> bsh, bsl;
     split_acc(S[2 * ks], S[2 * ks + 1], bsh, bsl);
-    const int c0 = 32 * ks + 4 * g;
 #pragma unroll
     for (int I = 0; I < NB; ++I) {
-      Frag<bf16_t> fk, fq;
-      const char* krow = OK + (16 * I + n) * K::RS_Q;
-      const char* qrow = OQ + (16 * I + n) * K::RS_Q;
-      fk.load4x2(krow + c0 * 2, krow + (c0 + 16) * 2);
-      fq.load4x2(qrow + c0 * 2, qrow + (c0 + 16) * 2);
-      mma(Rr[I], fk, bsh);
-      mma(Rr[I], fk, bsl);
-      mma(O[I], fq, bsh);
+      mma(Rr[I], fk[ks & 1][I], bsh);
+      mma(O[I], fq[ks & 1][I], bsh);
+      mma(Rr[I], fk[ks & 1][I], bsl);
     }
+    fence_sched();
   }
 
   // Delta = M~ R over the lower blocks (I, s2) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1):
   // M~_hi R_hi + M~_hi R_lo + M~_lo R_hi
+  Frag<bf16_t> fh[6], fl[6];
+#pragma unroll
+  for (int j = 0; j < 6; ++j) {
+    ld_rec(RL::MH, j, fh[j]);
+    ld_rec(RL::ML, j, fl[j]);
+  }
+  fence_sched();
   Frag<bf16_t> brh[2], brl[2];
   split_acc(Rr[0], Rr[1], brh[0], brl[0]);
   split_acc(Rr[2], Rr[3], brh[1], brl[1]);
@@ -171,33 +346,36 @@ __device__ __forceinline__ void walk_chunk(const char* ops, const char* rec, cha
   for (int I = 0; I < NB; ++I) D[I] = zero4();
 #pragma unroll
   for (int j = 0; j < 6; ++j) {
-    const int I = j < 2 ? j : 2 + (j - 2) / 2, s2 = j < 2 ? 0 : (j - 2) % 2;
-    const int o1 = RL::at(16 * I + n, 32 * s2 + 4 * g), o2 = RL::at(16 * I + n, 32 * s2 + 16 + 4 * g);
-    Frag<bf16_t> fh, fl;
-    fh.load4x2(rec + RL::MH + o1, rec + RL::MH + o2);
-    fl.load4x2(rec + RL::ML + o1, rec + RL::ML + o2);
-    mma(D[I], fh, brh[s2]);
-    mma(D[I], fh, brl[s2]);
-    mma(D[I], fl, brh[s2]);
+    const int I = blk_I(j), s2 = blk_s(j);
+    mma(D[I], fh[j], brh[s2]);
+    mma(D[I], fh[j], brl[s2]);
+    mma(D[I], fl[j], brh[s2]);
   }
+  // the readout block's and the first state row block's operands, in flight meanwhile
+  Frag<bf16_t> fa[6], ft[2][2];
+#pragma unroll
+  for (int j = 0; j < 6; ++j) ld_rec(RL::A, j, fa[j]);
+  ld_kt(0, ft[0]);
+  fence_sched();
 
   // O += A Delta_hi
   Frag<bf16_t> bdh[2], bdl[2];
   split_acc(D[0], D[1], bdh[0], bdl[0]);
   split_acc(D[2], D[3], bdh[1], bdl[1]);
 #pragma unroll
-  for (int j = 0; j < 6; ++j) {
-    const int I = j < 2 ? j : 2 + (j - 2) / 2, s2 = j < 2 ? 0 : (j - 2) % 2;
-    const int o1 = RL::at(16 * I + n, 32 * s2 + 4 * g), o2 = RL::at(16 * I + n, 32 * s2 + 16 + 4 * g);
-    Frag<bf16_t> fa;
-    fa.load4x2(rec + RL::A + o1, rec + RL::A + o2);
-    mma(O[I], fa, bdh[s2]);
-  }
+  for (int j = 0; j < 6; ++j) mma(O[blk_I(j)], fa[j], bdh[blk_s(j)]);
 
   // S <- diag(gamma_last) S + (K o rho)^T (Delta_hi + Delta_lo)
+  float4 gl[2];
+  gl[0] = *(const float4*)(OG + 4 * g);
 #pragma unroll
   for (int r = 0; r < DK / 16; ++r) {
-    const float4 c = *(const float4*)(OG + 16 * r + 4 * g);
+    if (r + 1 < DK / 16) {
+      gl[(r + 1) & 1] = *(const float4*)(OG + 16 * (r + 1) + 4 * g);
+      ld_kt(r + 1, ft[(r + 1) & 1]);
+    }
+    const float4 c = gl[r & 1];
+    fence_sched();
     if constexpr (CPX) {  // rows (2p, 2p+1) are one complex coordinate, turned by gamma_last
       const float s0 = S[r][0], s1 = S[r][1], s2 = S[r][2], s3 = S[r][3];
       S[r][0] = c.x * s0 - c.y * s1;
@@ -210,16 +388,12 @@ __device__ __forceinline__ void walk_chunk(const char* ops, const char* rec, cha
       S[r][2] *= c.z;
       S[r][3] *= c.w;
     }
-    const int kc = 16 * r + n;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
-      // positions 32 s2 + 4g .. +3 and 32 s2 + 16 + 4g .. +3: units 4 s2 + g / 2 and + 2, half g & 1
-      const int u = 4 * s2 + (g >> 1), h8 = 8 * (g & 1);
-      Frag<bf16_t> fk;
-      fk.load4x2(OKT + K::kt_unit(kc, u) + h8, OKT + K::kt_unit(kc, u + 2) + h8);
-      mma(S[r], fk, bdh[s2]);
-      mma(S[r], fk, bdl[s2]);
+      mma(S[r], ft[r & 1][s2], bdh[s2]);
+      mma(S[r], ft[r & 1][s2], bdl[s2]);
     }
+    fence_sched();
   }
 
   // O over this wave's own (already consumed) v columns
@@ -244,7 +418,6 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
   constexpr int NW = K::NW;
   constexpr int NP = K::NP;
   constexpr int NT = K::NT;
-  constexpr int GRP = K::GRP;
   // separate LDS objects per buffer, so that reads of one buffer are not ordered
   // behind the DMA (or the operand stores) still filling the other
   __shared__ __align__(16) char ops_a[K::OPS];
@@ -318,125 +491,241 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
       for (int e = 0; e < 4; ++e) S[r][e] = s0[(sidx * DK + 16 * r + 4 * g + e) * DV + v0 + 16 * wave + n];
   }
 
-  // ---- producer side: gate item of lane pt = (block iI, channel pair icp)
+  // ---- producer side: lane pt holds one gate item (4 rows x 8 channels) when pt < NITEM
   const int pt = tid - NW * 64;
   const bool has_item = producer && pt < K::NITEM;
-  // (producer wave pw) the outputs of chunk c staged in `vv` -> o, for the 1 KiB units of
-  // the v tile this wave fills by DMA; then chunk c + 2's record matrices and v tile into
-  // the same buffers.  Each wave reads out exactly the LDS bytes it overwrites next, so no
-  // workgroup barrier sits between the two.
-  auto store_o = [&](int c, const char* vv) __attribute__((always_inline)) {
-    const int t0 = c * C;
+  // Transfers of producer wave pw per step: ND DMA instructions (1 KiB each) and NS output
+  // stores.  DMA index i < N_DMA_V is v unit i, the rest are record units; indices past
+  // the last repeat the last record unit (the same bytes to the same place).  Output unit
+  // j of the wave is v unit pw + NP j, which this wave reads out before its own DMA
+  // overwrites it, so no workgroup barrier sits between the two.  The counts are the same
+  // on every step: the tail repeats the last chunk's transfers into buffers nobody reads,
+  // and the stores of a step with nothing to write are dropped by the buffer range check.
+  // The vector-memory counter, which retires in issue order, then holds a known number of
+  // operations at every wait (the barrier's and the compiler's).
+  constexpr int NU = K::N_DMA_V + K::N_DMA_REC;
+  constexpr int ND = (NU + NP - 1) / NP;
+  constexpr int NS = (K::N_DMA_V + NP - 1) / NP;
+  static_assert(NS >= 1 && NS <= 2, "one or two output units per producer wave");
+  typedef uint32_t u32x4o __attribute__((ext_vector_type(4)));
+  u32x4o ov0 = {0u, 0u, 0u, 0u}, ov1 = ov0;
+  // the wave's output units of the tile staged in `vv` into registers (then lgkmcnt(0):
+  // the DMA that follows may overwrite them)
+  auto read_o = [&](const char* vv) __attribute__((always_inline)) {
+    ov0 = *(const u32x4o*)(vv + (min(pw, K::N_DMA_V - 1) * 64 + lane) * 16);
+    if constexpr (NS > 1) ov1 = *(const u32x4o*)(vv + (min(pw + NP, K::N_DMA_V - 1) * 64 + lane) * 16);
+#ifndef KDA_HOST_PASS
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+#endif
+  };
+  // ... and out to o rows of chunk c (when `any`): rows past the end fall outside the
+  // buffer range and are dropped
+  auto write_o = [&](int c, bool any) __attribute__((always_inline)) {
+    const int t0 = max(c, 0) * C;
     const int nv = min(C, slen - t0);
-    for (int x = pw; x < K::N_DMA_V; x += NP) {
-      const int sl = x * 64 + lane;
-      const int row = sl / K::UPR, u = sl % K::UPR;
-      if (row < nv)
-        *(uint4*)((char*)go + ((sbase + t0 + row) * H + h) * DV * 2 + (size_t)v0 * 2 + (size_t)u * 16) =
-            *(const uint4*)(vv + sl * 16);
+    const uint32_t rs = (uint32_t)H * DV * 2;
+    // (the descriptor fields are wave-uniform: made explicit, or the compiler loops over
+    // lanes to build a scalar descriptor)
+    const uint64_t ba = (uint64_t)((char*)go + ((sbase + t0) * H + h) * DV * 2 + (size_t)v0 * 2);
+    char* base = (char*)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(ba >> 32)) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ba));
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int x = pw + NP * j;
+      const int num = __builtin_amdgcn_readfirstlane(any && x < K::N_DMA_V && nv > 0 ? (int)((nv - 1) * rs) + VT * 2 : 0);
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, num, 0x00020000);
+      const int sl = min(x, K::N_DMA_V - 1) * 64 + lane;
+      const int row = sl / K::UPR, u = (sl % K::UPR) ^ K::vsw(row);
+      __builtin_amdgcn_raw_buffer_store_b128(j == 0 ? ov0 : ov1, rsrc, (int)(row * rs) + u * 16, 0, 0);
     }
   };
-  auto issue_dma = [&](int c, char* rec_dst, char* v_dst) __attribute__((always_inline)) {
+  // chunk c's v tile and record matrices into v_dst, rec_dst (v tile from the record
+  // itself when v is read as zero: the bytes go unused)
+  constexpr int NDP = (ND + 3) / 4;  // DMA instructions per part (four parts)
+  auto issue_dma = [&](int c, char* rec_dst, char* v_dst, int part = -1) __attribute__((always_inline)) {
     const char* rc = rec0 + (size_t)c * RL::BYTES;
     const int t0 = c * C;
-    if (!zero_v) {
-#pragma nounroll
-      for (int x = pw; x < K::N_DMA_V; x += NP) {
-        const int sl = x * 64 + lane;
-        const int row = sl / K::UPR, u = sl % K::UPR;
-        const size_t gr = (sbase + min(t0 + row, slen - 1)) * H + h;
-        const size_t off = (gr * DV + v0) * 2 + (size_t)u * 16;
-        dma16((const char*)gv + off, v_dst + x * 1024);
-      }
+#pragma unroll
+    for (int j = 0; j < ND; ++j) {
+      if (part >= 0 && j / NDP != part) continue;
+      const int i = min(pw + NP * j, NU - 1);
+      const bool isv = i < K::N_DMA_V;
+      const int sl = min(i, K::N_DMA_V - 1) * 64 + lane;
+      const int row = sl / K::UPR, u = (sl % K::UPR) ^ K::vsw(row);
+      const size_t gr = (sbase + min(t0 + row, slen - 1)) * H + h;
+      const char* vsrc = zero_v ? rc + lane * 16 : (const char*)gv + (gr * DV + v0) * 2 + (size_t)u * 16;
+      const char* src = isv ? vsrc : rc + (i - K::N_DMA_V) * 1024 + lane * 16;
+      dma16(src, isv ? v_dst + i * 1024 : rec_dst + (i - K::N_DMA_V) * 1024);
     }
-#pragma nounroll
-    for (int x = pw; x < K::N_DMA_REC; x += NP) dma16(rc + x * 1024 + lane * 16, rec_dst + x * 1024);
   };
-  // one chunk ahead: the item's 16 rows of q, k, alpha (and the erase gate) and its block's
-  // gate products, raw.  Rows past the end are clamped to the last row (unconditional
-  // loads) and given gate 1 when used.
-  // (native vectors, not arrays: arrays captured by the lambdas stay in scratch memory)
+  // Gate items: lane (rg, cg) = (lane & 15, lane >> 4) of producer wave pw holds rows
+  // 4 rg .. 4 rg + 3 of channels c0 = 32 pw + 8 cg .. c0 + 7 (one 16-byte vector per row
+  // and tensor: few, wide loads).  The 16 row groups of a channel group are the 16 lanes of
+  // one DPP row, so the gate products across row groups are 4-step scans along that row.
+  // The raw rows sit in two register sets that alternate by chunk: chunk c + 2's inputs
+  // load into the set chunk c vacated while chunk c + 1's are turned into operands, so a
+  // load has a whole step to land.  Rows past the end are clamped to the last row
+  // (unconditional loads) and given gate 1 when used.  (Native vectors, not arrays: arrays
+  // captured by the lambdas stay in scratch memory.)
   typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
-  typedef float f32x2v __attribute__((ext_vector_type(2)));
-  u32x16 pq, pk, pa, pe;
-  f32x2v pgp = {1.f, CPX ? 0.f : 1.f}, prp = pgp, pgl = pgp;
-  int plim = 0;  // rows of the loaded chunk that exist in this item's block
-  auto issue_in = [&](int c) __attribute__((always_inline)) {
-    // the item's first row and column byte from an opaque copy of the thread index: the
-    // row offsets are then recomputed per chunk instead of hoisted out of the loop and
-    // spilled (a reload would wait for every load in flight)
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  struct PSet {
+    u32x16 q, k, a, e;  // dword 4 j + p: row 4 rg + j, channels c0 + 2p, c0 + 2p + 1
+    int nrow;           // rows of the loaded chunk that exist
+  };
+  PSet ps0, ps1;
+  ps0.nrow = ps1.nrow = 0;
+  // row j of the lane's row group (4 rg + j) of chunk c into `ps`
+  auto load_row = [&](int c, PSet& ps, int j) __attribute__((always_inline)) {
+    // the lane's row group and channels from an opaque copy of the thread index: the row
+    // offsets are then recomputed per chunk instead of hoisted out of the loop and spilled
+    // (a reload would wait for every load in flight)
     int t = threadIdx.x - NW * 64;
     asm volatile("" : "+v"(t));
-    const int blk = t / GRP, cp = t % GRP;
+    const int rg = t & 15, c0 = 32 * (t >> 6) + 8 * ((t >> 4) & 3);
     const int t0 = c * C;
     const size_t base = ((sbase + t0) * H + h) * DK * 2;
     const uint32_t rs = (uint32_t)H * DK * 2;
-    const int last = slen - 1 - t0;
-    plim = slen - t0 - SUB * blk;
+    ps.nrow = slen - t0;
+    const uint32_t off = (uint32_t)min(4 * rg + j, ps.nrow - 1) * rs + 2 * c0;
+    const u32x4v q4 = *(const u32x4v*)((const char*)gq + base + off);
+    const u32x4v k4 = *(const u32x4v*)((const char*)gk + base + off);
+    const u32x4v a4 = *(const u32x4v*)((const char*)galpha + base + off);
 #pragma unroll
-    for (int m = 0; m < SUB; ++m) {
-      const uint32_t off = (uint32_t)min(SUB * blk + m, last) * rs + 4 * cp;
-      pq[m] = *(const uint32_t*)((const char*)gq + base + off);
-      pk[m] = *(const uint32_t*)((const char*)gk + base + off);
-      pa[m] = *(const uint32_t*)((const char*)galpha + base + off);
-      if constexpr (G2) pe[m] = *(const uint32_t*)((const char*)gerase + base + off);
+    for (int p = 0; p < 4; ++p) {
+      ps.q[4 * j + p] = q4[p];
+      ps.k[4 * j + p] = k4[p];
+      ps.a[4 * j + p] = a4[p];
     }
-    const char* rc = rec0 + (size_t)c * RL::BYTES;
-    if (blk > 0) pgp = *(const f32x2v*)(rc + RL::GP + ((blk - 1) * DK + 2 * cp) * 4);
-    if (blk < NB - 1) prp = *(const f32x2v*)(rc + RL::RP + (blk * DK + 2 * cp) * 4);
-    if (blk == 0) pgl = *(const f32x2v*)(rc + RL::G63 + 8 * cp);
+    if constexpr (G2) {
+      const u32x4v e4 = *(const u32x4v*)((const char*)gerase + base + off);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) ps.e[4 * j + p] = e4[p];
+    }
   };
-  // the operands of the loaded chunk into `ops`, bf16: Q o gamma and -(E o gamma) rows (E:
-  // k, or b o k for Gated DeltaNet-2), (K o rho)^T columns, gamma_last
-  auto form = [&](char* ops) __attribute__((always_inline)) {
+  auto load_rows = [&](int c, PSet& ps) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) load_row(c, ps, j);
+  };
+  // the operands of the chunk loaded in `ps` into `ops`, bf16: Q o gamma and -(E o gamma)
+  // rows (E: k, or b o k for Gated DeltaNet-2), (K o rho)^T columns, gamma_last
+  // hook(j), j = 0..3, runs at four points spread over the work (the step's transfers,
+  // issued in parts between the arithmetic)
+  auto form = [&](const PSet& ps, char* ops, auto&& hook) __attribute__((always_inline)) {
+    hook(0);
     int t = threadIdx.x - NW * 64;
     asm volatile("" : "+v"(t));
-    const int blk = t / GRP, cp = t % GRP;
+    const int rg = t & 15, c0 = 32 * (t >> 6) + 8 * ((t >> 4) & 3);
     constexpr uint32_t kOne = CPX ? 0x00003F80u : R::kOneWord;
-    G al[SUB];
+    // gates (channel pair p of row j), the products inside the row group: prefix P (rows
+    // up to j) and exclusive suffix B (rows after j), then across the groups
+    G al[4][4], P[4][4], B[4][4], X[4], Y[4], tot[4];
 #pragma unroll
-    for (int m = 0; m < SUB; ++m) R::unpack(m < plim ? pa[m] : kOne, al[m].x, al[m].y);
-    char* oq = ops + K::OFF_Q + (SUB * blk) * K::RS_Q + 4 * cp;
-    char* ok = ops + K::OFF_K + (SUB * blk) * K::RS_Q + 4 * cp;
-    G f{pgp[0], pgp[1]};
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int m = 0; m < SUB; ++m) {
-      f *= al[m];
-      float q0, q1, e0, e1, r0, r1;
-      R::unpack(pq[m], q0, q1);
-      R::unpack(pk[m], e0, e1);
-      if constexpr (G2) {
-        float b0, b1;
-        R::unpack(pe[m], b0, b1);
-        e0 *= b0;
-        e1 *= b1;
+      for (int p = 0; p < 4; ++p) R::unpack(4 * rg + j < ps.nrow ? ps.a[4 * j + p] : kOne, al[j][p].x, al[j][p].y);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      P[0][p] = al[0][p];
+      P[1][p] = P[0][p] * al[1][p];
+      P[2][p] = P[1][p] * al[2][p];
+      P[3][p] = P[2][p] * al[3][p];
+      B[3][p] = G::one();
+      B[2][p] = al[3][p];
+      B[1][p] = al[2][p] * al[3][p];
+      B[0][p] = al[1][p] * B[1][p];
+    }
+    // inclusive scans of the group totals along the DPP row: I (groups up to rg), J
+    // (groups from rg on); X, Y their exclusive forms
+    if constexpr (!CPX) {
+      float I[8], J[8];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        I[2 * p] = J[2 * p] = P[3][p].x;
+        I[2 * p + 1] = J[2 * p + 1] = P[3][p].y;
       }
-      f.row(q0, q1, r0, r1);
-      *(uint32_t*)(oq + m * K::RS_Q) = pack_bf16x2(r0, r1);
-      f.row(e0, e1, r0, r1);
-      *(uint32_t*)(ok + m * K::RS_Q) = pack_bf16x2(-r0, -r1);
-    }
-    G bb{prp[0], prp[1]};
-    typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
-    u32x8 w0, w1;
+      row_scan16(I, J);
 #pragma unroll
-    for (int m = SUB - 1; m >= 0; m -= 2) {
-      float k0, k1, a0, a1, c0, c1;
-      R::unpack(pk[m], k0, k1);
-      bb.col(k0, k1, a0, a1);
-      bb *= al[m];
-      R::unpack(pk[m - 1], k0, k1);
-      bb.col(k0, k1, c0, c1);
-      bb *= al[m - 1];
-      w0[m / 2] = pack_bf16x2(c0, a0);
-      w1[m / 2] = pack_bf16x2(c1, a1);
+      for (int p = 0; p < 4; ++p) {
+        tot[p] = G{I[2 * p], I[2 * p + 1]};
+        X[p] = dpp_fill<G, 0x111>(tot[p]);
+        Y[p] = dpp_fill<G, 0x101>(G{J[2 * p], J[2 * p + 1]});
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        G I = P[3][p], J = P[3][p];
+        I = I * dpp_fill<G, 0x111>(I);
+        J = J * dpp_fill<G, 0x101>(J);
+        I = I * dpp_fill<G, 0x112>(I);
+        J = J * dpp_fill<G, 0x102>(J);
+        I = I * dpp_fill<G, 0x114>(I);
+        J = J * dpp_fill<G, 0x104>(J);
+        I = I * dpp_fill<G, 0x118>(I);
+        J = J * dpp_fill<G, 0x108>(J);
+        X[p] = dpp_fill<G, 0x111>(I);
+        Y[p] = dpp_fill<G, 0x101>(J);
+        tot[p] = I;
+      }
     }
-    char* kt = ops + K::OFF_KT;
-    *(uint4*)(kt + K::kt_unit(2 * cp, 2 * blk)) = make_uint4(w0[0], w0[1], w0[2], w0[3]);
-    *(uint4*)(kt + K::kt_unit(2 * cp, 2 * blk + 1)) = make_uint4(w0[4], w0[5], w0[6], w0[7]);
-    *(uint4*)(kt + K::kt_unit(2 * cp + 1, 2 * blk)) = make_uint4(w1[0], w1[1], w1[2], w1[3]);
-    *(uint4*)(kt + K::kt_unit(2 * cp + 1, 2 * blk + 1)) = make_uint4(w1[4], w1[5], w1[6], w1[7]);
-    if (blk == 0) *(f32x2v*)(ops + K::OFF_G + 8 * cp) = pgl;
+    typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+    u32x2v kt[4][2];  // (K o rho)^T: channel 2p + c2, rows (4rg, 4rg+1), (4rg+2, 4rg+3)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j > 0) hook(j);
+      uint32_t wq[4], wk[4];
+      float kr[4][2];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const G gm = X[p] * P[j][p], rh = Y[p] * B[j][p];
+        float q0, q1, k0, k1, e0, e1, r0, r1;
+        R::unpack(ps.q[4 * j + p], q0, q1);
+        R::unpack(ps.k[4 * j + p], k0, k1);
+        e0 = k0;
+        e1 = k1;
+        if constexpr (G2) {
+          float b0, b1;
+          R::unpack(ps.e[4 * j + p], b0, b1);
+          e0 *= b0;
+          e1 *= b1;
+        }
+        gm.row(q0, q1, r0, r1);
+        wq[p] = pack_bf16x2(r0, r1);
+        gm.row(e0, e1, r0, r1);
+        wk[p] = pack_bf16x2(-r0, -r1);
+        rh.col(k0, k1, kr[p][0], kr[p][1]);
+      }
+      const int row = 4 * rg + j;
+      lds_st128(ops + K::OFF_Q + row * K::RS_Q + 2 * c0, wq[0], wq[1], wq[2], wq[3]);
+      lds_st128(ops + K::OFF_K + row * K::RS_Q + 2 * c0, wk[0], wk[1], wk[2], wk[3]);
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          const float v = kr[p][c2];
+          if (j == 0) kt[p][c2][0] = __float_as_uint(v);
+          if (j == 1) kt[p][c2][0] = pack_bf16x2(__uint_as_float(kt[p][c2][0]), v);
+          if (j == 2) kt[p][c2][1] = __float_as_uint(v);
+          if (j == 3) kt[p][c2][1] = pack_bf16x2(__uint_as_float(kt[p][c2][1]), v);
+        }
+    }
+    char* ktb = ops + K::OFF_KT;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const int ch = c0 + 2 * p + c2;
+        lds_st64(ktb + K::kt_unit(ch, rg >> 1) + 8 * (rg & 1), __uint_as_float(kt[p][c2][0]),
+                 __uint_as_float(kt[p][c2][1]));
+      }
+    if (rg == 15) {  // gamma_last: the inclusive product over every row group
+      float* og = (float*)(ops + K::OFF_G) + c0;
+      lds_st128(og, __float_as_uint(tot[0].x), __float_as_uint(tot[0].y), __float_as_uint(tot[1].x),
+                __float_as_uint(tot[1].y));
+      lds_st128(og + 4, __float_as_uint(tot[2].x), __float_as_uint(tot[2].y), __float_as_uint(tot[3].x),
+                __float_as_uint(tot[3].y));
+    }
   };
 
   // (compute waves, G2) the write gate of this lane's rows 16 I + 4 g + e and column of
@@ -455,48 +744,81 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
       }
   };
 
-  if (nchunks > 0) {
-    if (producer) issue_dma(0, rec_a, v_a);
-    if (has_item) {
-      issue_in(0);
-      form(ops_a);
-      if (nchunks > 1) issue_in(1);
-    }
-    if (G2 && !zero_v && !producer) load_w(0);
-  }
+  // The two roles run separate loops (so the compiler sees their registers as never live
+  // at once); both pass the same barriers: one per chunk, and one at the end.
   // Step c: the compute waves walk chunk c from buffers P (operands, record, v tile); the
   // producers store chunk c - 1's outputs out of buffers Q, stream chunk c + 1's record and v
-  // tile into Q and build its operands there, and load chunk c + 2's inputs.  One barrier.
-  auto step = [&](int c, const char* opsP, const char* recP, char* vP, char* opsQ, char* recQ, char* vQ) __attribute__((always_inline)) {
-    full_barrier();  // chunk c landed and its operands are in place; chunk c - 1 finished
-    if (producer) {
-      if (c > 0 && !no_out) {
-        store_o(c - 1, vQ);
-#ifndef KDA_HOST_PASS
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the outputs are read out of vQ
+  // tile into Q, build its operands there, and load chunk c + 2's inputs.
+  if (producer) {
+    // (items: whether the wave holds gate items, a compile-time constant so that no
+    // branch around a transfer blurs the counts)
+    auto run = [&](auto items) __attribute__((always_inline)) {
+      constexpr bool kItems = decltype(items)::value;
+#ifndef KDA_PRODUCER_WAIT
+      constexpr int kWait = 0;
+#else
+      constexpr int kWait = KDA_PRODUCER_WAIT * (kItems ? 1 : 0);
 #endif
+      const int last = nchunks - 1;
+      issue_dma(0, rec_a, v_a);
+      write_o(0, false);  // (issues the step's store count; writes nothing)
+      if constexpr (kItems) {
+        load_rows(0, ps0);
+        load_rows(min(1, last), ps1);
+        form(ps0, ops_a, [](int) {});
       }
-      if (c + 1 < nchunks) {
-        issue_dma(c + 1, recQ, vQ);
-        if (has_item) {
-          form(opsQ);
-          if (c + 2 < nchunks) issue_in(c + 2);
+      // step c: the outputs of chunk c - 1 out of buffers Q, chunk c + 1's record and v
+      // tile into Q, chunk c + 2's rows into the set chunk c vacated (psN), and chunk
+      // c + 1's operands from psP (rows loaded a step ago) into Q.  Everything a step
+      // issues lands before the next step's barrier.
+      auto pstep = [&](int c, PSet& psP, PSet& psN, char* opsQ, char* recQ, char* vQ) __attribute__((always_inline)) {
+        producer_barrier<kWait>();
+        read_o(vQ);
+        write_o(c - 1, c > 0 && !no_out);
+        fence_sched();
+        if constexpr (kItems) {
+          // chunk c + 1's transfers in four parts between the arithmetic: a wave blocked
+          // issuing a transfer (memory pipeline full) then still has arithmetic between
+          // the blocks
+          const int cd = min(c + 1, last), cl = min(c + 2, last);
+          form(psP, opsQ, [&](int j) __attribute__((always_inline)) {
+            fence_sched();
+            issue_dma(cd, recQ, vQ, j);
+            load_row(cl, psN, j);
+            fence_sched();
+          });
+        } else {
+          issue_dma(min(c + 1, last), recQ, vQ);
         }
+      };
+      for (int chunk = 0; chunk < nchunks; chunk += 2) {
+        pstep(chunk, ps1, ps0, ops_b, rec_b, v_b);
+        if (chunk + 1 >= nchunks) break;
+        pstep(chunk + 1, ps0, ps1, ops_a, rec_a, v_a);
       }
-    } else {
+      full_barrier();
+      read_o((last & 1) ? v_b : v_a);
+      write_o(last, !no_out);
+    };
+    if (nchunks > 0) {
+      if (has_item)
+        run(BoolC<true>{});
+      else
+        run(BoolC<false>{});
+    }
+  } else {
+    if (G2 && !zero_v && nchunks > 0) load_w(0);
+    auto cstep = [&](int c, const char* opsP, const char* recP, char* vP) __attribute__((always_inline)) {
+      full_barrier();  // chunk c landed and its operands are in place
       walk_chunk<DK, VT, G2, CPX>(opsP, recP, vP, wf, zero_v, slen - c * C, S, wave, g, n);
       if (G2 && !zero_v && c + 1 < nchunks) load_w(c + 1);
+    };
+    for (int chunk = 0; chunk < nchunks; chunk += 2) {
+      cstep(chunk, ops_a, rec_a, v_a);
+      if (chunk + 1 >= nchunks) break;
+      cstep(chunk + 1, ops_b, rec_b, v_b);
     }
-  };
-  for (int chunk = 0; chunk < nchunks; chunk += 2) {
-    step(chunk, ops_a, rec_a, v_a, ops_b, rec_b, v_b);
-    if (chunk + 1 >= nchunks) break;
-    step(chunk + 1, ops_b, rec_b, v_b, ops_a, rec_a, v_a);
-  }
-  if (nchunks > 0) {
-    full_barrier();
-    if (producer && !no_out) store_o(nchunks - 1, ((nchunks - 1) & 1) ? v_b : v_a);
+    if (nchunks > 0) full_barrier();  // the last outputs are staged
   }
 
   const bool last_only = (flags & kSegLastOnly) != 0;
