@@ -204,14 +204,16 @@ def _chunk_call(debug, q, k, v, alpha, beta, initial_state, out, final_state, wa
         if rc != 0:
             raise KdaError(rc, "kda_chunk_fwd_ws")
         return out, final_state, None
-    if path not in ("fused", "twopass"):
+    if path not in ("fused", "twopass", "capi"):
         raise ValueError(f"unknown path {path!r}")
     if debug:
         nch = (T + 63) // 64
         dbg = torch.zeros((B * H, nch, 4, 64, 64), dtype=torch.float32, device=dev)
         rc = lib().kda_chunk_fwd_debug(*args, _ptr(dbg), _stream(dev))
-    else:
+    elif path == "capi":  # kda_chunk_fwd: the library picks the path and its workspace
         rc = lib().kda_chunk_fwd(*args, _stream(dev))
+    else:  # the single-pass kernel (kda_chunk_fwd_ws without a workspace)
+        rc = lib().kda_chunk_fwd_ws(*args, None, ctypes.c_size_t(0), _stream(dev))
     if rc != 0:
         raise KdaError(rc, "kda_chunk_fwd")
     return out, final_state, dbg
@@ -222,7 +224,8 @@ def chunk_fwd(q, k, v, alpha, beta, initial_state=None, out=None, final_state=No
     """Chunkwise WY forward.  q, k, alpha [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H]
     (all bf16 or all fp32, contiguous, on one GPU); initial_state fp32 [B,H,dk,dv]
     or None.  path: "fused" (single pass), "twopass" (parallel per-chunk records in a
-    workspace, then the state pass) or "auto".  workspace: optional uint8 device
+    workspace, then the state pass), "capi" (kda_chunk_fwd's own choice, with its
+    workspace from the stream-ordered pool) or "auto".  workspace: optional uint8 device
     tensor of at least workspace_size(...) bytes for the two-pass path (allocated
     here when omitted).  Returns (o [B,T,H,dv], final_state fp32 [B,H,dk,dv] or None)."""
     o, s, _ = _chunk_call(False, q, k, v, alpha, beta, initial_state, out, final_state, want_final, path,

@@ -370,10 +370,22 @@ int kda_version(void) { return kVersion; }
 int kda_chunk_fwd(const kda_shape* shape, const void* q, const void* k, const void* v,
                   const void* alpha, const void* beta, const float* initial_state, void* o,
                   float* final_state, void* stream) {
-  const ChunkPtrs p{q, k, v, alpha, beta, initial_state, o, final_state, nullptr, nullptr, 0};
+  ChunkPtrs p{q, k, v, alpha, beta, initial_state, o, final_state, nullptr, nullptr, 0};
   int rc = validate_chunk(shape, p, kNeedQKAB | kNeedVO);
   if (rc) return rc;
-  return kda::launch_chunk(chunk_args(*shape, p, stream)) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  if (shape->T <= 64 || (int64_t)shape->B * shape->H == 0)
+    return kda::launch_chunk(chunk_args(*shape, p, stream)) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  // more than one chunk: the two-pass forward on a workspace taken from the device's
+  // stream-ordered memory pool and given back in stream order after the second pass
+  const size_t need = kda_chunk_fwd_workspace_size(shape);
+  void* ws = nullptr;
+  if (hipMallocAsync(&ws, need, (hipStream_t)stream) != hipSuccess || !ws) return KDA_ERR_HIP;
+  p.ws = ws;
+  p.ws_bytes = need;
+  rc = run_records(*shape, p, stream);
+  if (!rc) rc = run_apply(*shape, p, stream);
+  if (hipFreeAsync(ws, (hipStream_t)stream) != hipSuccess && !rc) rc = KDA_ERR_HIP;
+  return rc;
 }
 
 size_t kda_chunk_fwd_workspace_size(const kda_shape* shape) {
@@ -386,7 +398,12 @@ size_t kda_chunk_fwd_workspace_size(const kda_shape* shape) {
 int kda_chunk_fwd_ws(const kda_shape* shape, const void* q, const void* k, const void* v, const void* alpha,
                      const void* beta, const float* initial_state, void* o, float* final_state, void* workspace,
                      size_t workspace_bytes, void* stream) {
-  if (!workspace) return kda_chunk_fwd(shape, q, k, v, alpha, beta, initial_state, o, final_state, stream);
+  if (!workspace) {  // the single-pass kernel
+    const ChunkPtrs p{q, k, v, alpha, beta, initial_state, o, final_state, nullptr, nullptr, 0};
+    const int rc = validate_chunk(shape, p, kNeedQKAB | kNeedVO);
+    if (rc) return rc;
+    return kda::launch_chunk(chunk_args(*shape, p, stream)) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  }
   const ChunkPtrs p{q, k, v, alpha, beta, initial_state, o, final_state, nullptr, workspace, workspace_bytes};
   int rc = validate_chunk(shape, p, kNeedQKAB | kNeedVO | kNeedWS);
   if (rc) return rc;

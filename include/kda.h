@@ -101,6 +101,12 @@ typedef enum {
  * Supported: dk in {64, 128}, dv in {64, 128}; KDA_F32 requires dk == dv == 64.
  * T need not be a multiple of 64 (the last chunk is masked); B*T == 0 only
  * copies initial_state to final_state (or zeroes it).
+ * Path: one chunk (T <= 64) runs the single-pass kernel; more than one chunk runs the
+ * two-pass forward of kda_chunk_fwd_ws on a workspace of kda_chunk_fwd_workspace_size()
+ * bytes that this call takes from the device's stream-ordered memory pool
+ * (hipMallocAsync on `stream`) and hands back in stream order after the second pass
+ * (hipFreeAsync); a pool failure is KDA_ERR_HIP.  Callers that manage their own memory
+ * pass a workspace to kda_chunk_fwd_ws.
  */
 int kda_chunk_fwd(const kda_shape* shape, const void* q, const void* k, const void* v,
                   const void* alpha, const void* beta, const float* initial_state,
@@ -109,10 +115,13 @@ int kda_chunk_fwd(const kda_shape* shape, const void* q, const void* k, const vo
 /*
  * Two-pass chunk forward.  Same operation, arguments and errors as kda_chunk_fwd,
  * plus a caller-owned device workspace:
- *   pass 1 computes, for every (b, h, chunk) in parallel, the chunk's WY record
- *          (-W, Q o gamma, (K o rho)^T, A, (I + T)^-1 diag(beta), gamma of the last
- *          row: the data of the chunk's affine block transfer) into the workspace;
- *   pass 2 walks the chunks of each (b, h) in order and carries the fp32 state.
+ *   pass 1 computes, for every (b, h, chunk) in parallel, the chunk's WY record into
+ *          the workspace: for bf16 inputs A (the decay-weighted causal q.k products) and
+ *          (I + T)^-1 diag(beta) as a bf16 pair (value and rounding residual); for
+ *          fp32 inputs also -W, Q o gamma, (K o rho)^T and the last row's gamma;
+ *   pass 2 walks the chunks of each (b, h) in order and carries the fp32 state
+ *          (for bf16 it re-reads q, k, alpha and rebuilds the gate-scaled operands
+ *          itself).
  *          With few (b, h) chains over a long sequence (bf16, dk = 128, at most 32
  *          64-column tiles), each chain is split into 8 or more segments of at least 16 chunks
  *          that are walked in parallel: once from a zero state (end state B_g), once
@@ -123,10 +132,13 @@ int kda_chunk_fwd(const kda_shape* shape, const void* q, const void* k, const vo
  *          records in the workspace and is counted by kda_chunk_fwd_workspace_size.
  * This trades extra HBM traffic (each record is written once and read once) for
  * parallelism over chunks; on MI355X it is the faster forward whenever T > 64 (about
- * twice the single-pass kernel of kda_chunk_fwd at d = 128, measured from 128 to
- * 2,048 heads).
+ * twice the single-pass kernel at d = 128, measured from 128 to 2,048 heads), and for
+ * bf16 the more exact one: its state chain carries the state, the residuals and
+ * (I + T)^-1 diag(beta) as bf16 pairs, which keeps the norm-preserving regime (alpha
+ * in {-1, +1}, beta in {0, 2}) within the 2e-2 bar at T = 65,536, where the
+ * single-pass kernel's single bf16 operands drift past it from T of about 8,192.
  *   workspace       : device memory, 256-byte aligned, not overlapping any argument;
- *                     NULL selects the single-pass kernel (same as kda_chunk_fwd).
+ *                     NULL selects the single-pass kernel.
  *   workspace_bytes : at least kda_chunk_fwd_workspace_size(shape), else
  *                     KDA_ERR_WORKSPACE.
  * The workspace contents on return are unspecified.

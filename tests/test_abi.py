@@ -111,7 +111,7 @@ def test_workspace_size_and_errors(L):
     assert size(4, 8192, 32, 128, 128) == 4 * 32 * 128 * one
     assert size(1, 65, 1, 128, 128) == 2 * one
     assert size(1, 64, 1, 128, 64) == one            # the record does not depend on dv
-    assert size(1, 64, 1, 64, 64) < one
+    assert size(1, 64, 1, 64, 64) == one             # bf16: the chunk matrices only, any d_k
     assert size(1, 64, 1, 64, 64, dtype=1) > size(1, 64, 1, 64, 64)
     assert size(1, 0, 3, 128, 128) == 0
     assert size(0, 8192, 3, 128, 128) == 0            # no (b, h): no records, no split scratch
