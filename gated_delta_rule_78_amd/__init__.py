@@ -18,7 +18,7 @@ __all__ = ["chunk_fwd", "chunk_records", "chunk_apply_records", "chunk_fwd_debug
            "gdn2_chunk_fwd", "gdn2_decode_step", "decode_tokens", "gdn2_decode_tokens", "chunk_fwd_varlen",
            "sfda_chunk_fwd", "sfda_decode_step", "sfda_decode_tokens", "chunk_bwd", "chunk_bwd_varlen",
            "gdn2_chunk_bwd", "bwd_workspace_size",
-           "workspace_size", "pick_path", "lib", "version", "status_string",
+           "workspace_size", "pick_path", "chunk_fwd_noalloc", "lib", "version", "status_string",
            "LIB_PATH", "KdaError", "Shape", "BF16", "F32"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -54,6 +54,8 @@ def lib() -> ctypes.CDLL:
         L.kda_chunk_fwd_debug.restype = ctypes.c_int
         L.kda_chunk_fwd_ws.argtypes = [SP, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.kda_chunk_fwd_ws.restype = ctypes.c_int
+        L.kda_chunk_fwd_noalloc.argtypes = [SP, P, P, P, P, P, P, P, P, P]
+        L.kda_chunk_fwd_noalloc.restype = ctypes.c_int
         L.kda_chunk_fwd_workspace_size.argtypes = [SP]
         L.kda_chunk_fwd_workspace_size.restype = ctypes.c_size_t
         L.kda_chunk_records.argtypes = [SP, P, P, P, P, P, ctypes.c_size_t, P]
@@ -231,6 +233,33 @@ def chunk_fwd(q, k, v, alpha, beta, initial_state=None, out=None, final_state=No
     o, s, _ = _chunk_call(False, q, k, v, alpha, beta, initial_state, out, final_state, want_final, path,
                           workspace)
     return o, s
+
+
+def chunk_fwd_noalloc(q, k, v, alpha, beta, out, initial_state=None, final_state=None):
+    """The two-pass chunk forward on the library's fixed per-GPU scratch (no device memory
+    is allocated here or in the library): for callers that cannot allocate.  Layouts as
+    chunk_fwd; `out` [B,T,H,dv] is required, `final_state` fp32 [B,H,dk,dv] is written
+    when given.  Raises KdaError (KDA_ERR_SCRATCH) when the shape's workspace exceeds
+    KDA_NOALLOC_SCRATCH_BYTES.  Calls that overlap in time on one GPU race on the scratch.
+    Returns (out, final_state)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    code = _dtype_code(q)
+    for t, nm in ((k, "k"), (alpha, "alpha"), (v, "v"), (beta, "beta"), (out, "out")):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{nm} must have the dtype of q")
+    if k.shape != q.shape or alpha.shape != q.shape or v.shape != (B, T, H, dv) or beta.shape != (B, T, H) \
+            or out.shape != (B, T, H, dv):
+        raise ValueError("shapes: q, k, alpha [B,T,H,dk]; v, out [B,T,H,dv]; beta [B,T,H]")
+    dev = q.device
+    _check((q, k, v, alpha, beta, initial_state, out, final_state),
+           ("q", "k", "v", "alpha", "beta", "initial_state", "out", "final_state"), dev)
+    shape = Shape(B, T, H, dk, dv, 64, code)
+    rc = lib().kda_chunk_fwd_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                     _ptr(initial_state), _ptr(out), _ptr(final_state), _stream(dev))
+    if rc != 0:
+        raise KdaError(rc, "kda_chunk_fwd_noalloc")
+    return out, final_state
 
 
 def chunk_records(q, k, alpha, beta, workspace=None, dv=None):

@@ -21,7 +21,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # device pass honours it; the host pass only warns that it does not know it).
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_chunk.hip", "kda_state.hip", "kda_varlen.hip", "kda_records.hip", "kda_walk.hip", "kda_bwd.hip"]
+SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_chunk.hip", "kda_state.hip", "kda_varlen.hip", "kda_records.hip", "kda_walk.hip", "kda_bwd.hip",
+           "kda_noalloc.hip"]
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -360,6 +360,7 @@ const char* kda_status_string(int status) {
     case KDA_ERR_UNSUPPORTED: return "unsupported configuration (dk/dv, chunk or dtype)";
     case KDA_ERR_HIP: return "HIP runtime error on launch";
     case KDA_ERR_WORKSPACE: return "workspace smaller than kda_chunk_fwd_workspace_size()";
+    case KDA_ERR_SCRATCH: return "shape needs more workspace than the fixed no-alloc scratch (KDA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

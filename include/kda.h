@@ -87,7 +87,9 @@ typedef enum {
     KDA_ERR_ALIAS = -5,       /* the output overlaps an input it must not alias */
     KDA_ERR_UNSUPPORTED = -6, /* valid but unsupported (dk/dv, chunk, dtype x dk) */
     KDA_ERR_HIP = -7,         /* the HIP runtime reported an error on launch */
-    KDA_ERR_WORKSPACE = -8    /* workspace smaller than kda_chunk_fwd_workspace_size() */
+    KDA_ERR_WORKSPACE = -8,   /* workspace smaller than kda_chunk_fwd_workspace_size() */
+    KDA_ERR_SCRATCH = -9      /* kda_chunk_fwd_noalloc: the shape needs more workspace than
+                                 KDA_NOALLOC_SCRATCH_BYTES */
 } kda_status;
 
 /*
@@ -106,7 +108,8 @@ typedef enum {
  * bytes that this call takes from the device's stream-ordered memory pool
  * (hipMallocAsync on `stream`) and hands back in stream order after the second pass
  * (hipFreeAsync); a pool failure is KDA_ERR_HIP.  Callers that manage their own memory
- * pass a workspace to kda_chunk_fwd_ws.
+ * pass a workspace to kda_chunk_fwd_ws; callers that cannot allocate at all use
+ * kda_chunk_fwd_noalloc.
  */
 int kda_chunk_fwd(const kda_shape* shape, const void* q, const void* k, const void* v,
                   const void* alpha, const void* beta, const float* initial_state,
@@ -148,6 +151,27 @@ int kda_chunk_fwd_ws(const kda_shape* shape, const void* q, const void* k, const
                      const void* alpha, const void* beta, const float* initial_state,
                      void* o, float* final_state, void* workspace, size_t workspace_bytes,
                      void* stream);
+
+/*
+ * kda_chunk_fwd_ws without a workspace argument and without any device allocation, for
+ * callers that cannot allocate: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same operation, arguments and errors as
+ * kda_chunk_fwd_ws; the workspace is a fixed array of KDA_NOALLOC_SCRATCH_BYTES in device
+ * memory that each GPU the library runs on holds from load until the process ends.
+ *   limit : kda_chunk_fwd_workspace_size(shape) > KDA_NOALLOC_SCRATCH_BYTES is rejected
+ *           with KDA_ERR_SCRATCH before anything runs (64 MiB holds about 3,100 (b, h,
+ *           chunk) records: B*H = 32 heads up to T = 6,144 at d = 128, for instance).
+ *   races : every call on one GPU uses that GPU's one array, so calls that overlap in
+ *           time on the same GPU (different streams or host threads) must not be made;
+ *           calls in one stream order are safe.  The array needs no clearing: a call reads
+ *           only what it wrote itself.
+ * The first call on a device (with that device current) looks up the array's device
+ * address with hipGetSymbolAddress; a failure there is KDA_ERR_HIP.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int kda_chunk_fwd_noalloc(const kda_shape* shape, const void* q, const void* k, const void* v,
+                          const void* alpha, const void* beta, const float* initial_state,
+                          void* o, float* final_state, void* stream);
 
 /*
  * The two passes of kda_chunk_fwd_ws as separate calls (same workspace rules).
