@@ -412,6 +412,10 @@ def main():
                     help="only the decode measurement (for profiling the decode kernel)")
     ap.add_argument("--bwd-only", action="store_true",
                     help="only the backward measurement (for profiling the backward kernels)")
+    ap.add_argument("--prefill", default=None,
+                    choices=("kda_prefill_8k", "ckda_prefill_8k", "ckda_prefill_128k", "gdn2_prefill_8k",
+                             "sfda_prefill_8k"),
+                    help="only this prefill workload (for profiling its kernels); prints its own line")
     ap.add_argument("--bwd-workload", default="ckda_prefill_8k", choices=("ckda_prefill_8k", "gdn2_prefill_8k", "sfda_prefill_8k"),
                     help="workload of --bwd-only")
     args = ap.parse_args()
@@ -443,6 +447,11 @@ def main():
         gbs = db / (msd * 1e-3) / 1e9
         print(json.dumps({"workload": "ckda_decode_b256", "ms_per_step": msd, "value": gbs, "unit": "GB/s",
                           "frac": gbs / HBM_PEAK_GBS, "bytes_per_step": db}), flush=True)
+        return
+    if args.prefill:
+        wp, rp, _ = bench_prefill(args.prefill, args.steps, args.warmup, log)
+        print(json.dumps({"workload": args.prefill, "path": rp["path"], "ms_per_step": rp["ms"],
+                          "tokens_per_s": wp.B * wp.T / (rp["ms"] * 1e-3), "kernels_ms": rp["kernels"]}), flush=True)
         return
     if args.bwd_only:
         wb, msb = bench_backward(max(1, args.steps // 4), 1, log, name=args.bwd_workload)
