@@ -240,6 +240,10 @@ struct WCfg {
 // flags of a split walk (launch_walk_split): no output stores; v read as zero; start from
 // the identity; only the last segment writes the end state, indexed by (b, h)
 enum : int { kSegNoOut = 1, kSegZeroV = 2, kSegIdentity = 4, kSegLastOnly = 8 };
+// what a walk computes (a compile-time choice: the split walk's first two passes skip the
+// work they would discard): everything; the state only (outputs neither formed nor
+// stored, no Q o gamma); the state only with v = 0 (no v tile either)
+enum : int { kWalkFull = 0, kWalkState = 1, kWalkTransfer = 2 };
 
 __device__ __forceinline__ void fence_sched() {
 #ifndef KDA_HOST_PASS
@@ -251,9 +255,11 @@ __device__ __forceinline__ void fence_sched() {
 // operands in `ops`, record (A, MH, ML) in `rec`, v tile in `vv` (rows nv.. of the chunk lie
 // past the end of the sequence and read as zero); S advances one chunk and the outputs are
 // staged over this wave's own (consumed) columns of `vv`.
-template <int DK, int VT, bool G2, bool CPX>
+template <int DK, int VT, bool G2, bool CPX, int MODE>
 __device__ __forceinline__ void walk_chunk(const char* ops, const char* rec, char* vv, const float (&wf)[16],
                                            bool zero_v, int nv, f32x4_t (&S)[DK / 16], int wave, int g, int n) {
+  constexpr bool kOut = MODE == kWalkFull;    // outputs formed and staged
+  constexpr bool kV = MODE != kWalkTransfer;  // v read
   using K = WCfg<DK, VT>;
   using RL = typename K::RL;
   constexpr int KS = K::KS;
@@ -278,7 +284,7 @@ __device__ __forceinline__ void walk_chunk(const char* ops, const char* rec, cha
       const char* krow = OK + (16 * I + n) * K::RS_Q;
       const char* qrow = OQ + (16 * I + n) * K::RS_Q;
       fk[I].load4x2(krow + c0 * 2, krow + (c0 + 16) * 2);
-      fq[I].load4x2(qrow + c0 * 2, qrow + (c0 + 16) * 2);
+      if constexpr (kOut) fq[I].load4x2(qrow + c0 * 2, qrow + (c0 + 16) * 2);
     }
   };
   // (I, s2) of the six lower 16 x 32 blocks of a 64 x 64 record matrix
@@ -306,9 +312,13 @@ __device__ __forceinline__ void walk_chunk(const char* ops, const char* rec, cha
   for (int I = 0; I < NB; ++I) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      float x = bf16_to_f32(*(const uint16_t*)(vb + (16 * I + e) * K::RS_V));
-      if constexpr (G2) x *= wf[4 * I + e];
-      Rr[I][e] = 16 * I + e < nvl ? x : 0.f;
+      if constexpr (kV) {
+        float x = bf16_to_f32(*(const uint16_t*)(vb + (16 * I + e) * K::RS_V));
+        if constexpr (G2) x *= wf[4 * I + e];
+        Rr[I][e] = 16 * I + e < nvl ? x : 0.f;
+      } else {
+        Rr[I][e] = 0.f;
+      }
     }
     O[I] = zero4();
   }
@@ -323,7 +333,7 @@ __device__ __forceinline__ void walk_chunk(const char* ops, const char* rec, cha
 #pragma unroll
     for (int I = 0; I < NB; ++I) {
       mma(Rr[I], fk[ks & 1][I], bsh);
-      mma(O[I], fq[ks & 1][I], bsh);
+      if constexpr (kOut) mma(O[I], fq[ks & 1][I], bsh);
       mma(Rr[I], fk[ks & 1][I], bsl);
     }
     fence_sched();
@@ -353,8 +363,10 @@ __device__ __forceinline__ void walk_chunk(const char* ops, const char* rec, cha
   }
   // the readout block's and the first state row block's operands, in flight meanwhile
   Frag<bf16_t> fa[6], ft[2][2];
+  if constexpr (kOut) {
 #pragma unroll
-  for (int j = 0; j < 6; ++j) ld_rec(RL::A, j, fa[j]);
+    for (int j = 0; j < 6; ++j) ld_rec(RL::A, j, fa[j]);
+  }
   ld_kt(0, ft[0]);
   fence_sched();
 
@@ -362,8 +374,10 @@ __device__ __forceinline__ void walk_chunk(const char* ops, const char* rec, cha
   Frag<bf16_t> bdh[2], bdl[2];
   split_acc(D[0], D[1], bdh[0], bdl[0]);
   split_acc(D[2], D[3], bdh[1], bdl[1]);
+  if constexpr (kOut) {
 #pragma unroll
-  for (int j = 0; j < 6; ++j) mma(O[blk_I(j)], fa[j], bdh[blk_s(j)]);
+    for (int j = 0; j < 6; ++j) mma(O[blk_I(j)], fa[j], bdh[blk_s(j)]);
+  }
 
   // S <- diag(gamma_last) S + (K o rho)^T (Delta_hi + Delta_lo)
   float4 gl[2];
@@ -397,15 +411,17 @@ __device__ __forceinline__ void walk_chunk(const char* ops, const char* rec, cha
   }
 
   // O over this wave's own (already consumed) v columns
+  if constexpr (kOut) {
 #pragma unroll
-  for (int I = 0; I < NB; ++I)
+    for (int I = 0; I < NB; ++I)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) *(uint16_t*)(vb + (16 * I + e) * K::RS_V) = f32_to_bf16(O[I][e]);
+      for (int e = 0; e < 4; ++e) *(uint16_t*)(vb + (16 * I + e) * K::RS_V) = f32_to_bf16(O[I][e]);
+  }
 }
 
 }  // namespace
 
-template <int DK, int VT, bool G2, bool CPX>
+template <int DK, int VT, bool G2, bool CPX, int MODE>
 __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
     const char* __restrict__ ws, const void* __restrict__ gq, const void* __restrict__ gk,
     const void* __restrict__ galpha, const void* __restrict__ gerase, const void* __restrict__ gv,
@@ -474,7 +490,9 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
   }
   const int nchunks = (slen + C - 1) / C;
   const size_t sidx = (size_t)bhs;  // start / end state index: (b, h), or (b, h, segment)
-  const bool zero_v = (flags & kSegZeroV) != 0, no_out = (flags & kSegNoOut) != 0;
+  constexpr bool kOut = MODE == kWalkFull;    // outputs formed and stored
+  constexpr bool kV = MODE != kWalkTransfer;  // v read
+  const bool zero_v = !kV || (flags & kSegZeroV) != 0, no_out = !kOut || (flags & kSegNoOut) != 0;
 
   f32x4_t S[DK / 16];
 #pragma unroll
@@ -503,7 +521,8 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
   // and the stores of a step with nothing to write are dropped by the buffer range check.
   // The vector-memory counter, which retires in issue order, then holds a known number of
   // operations at every wait (the barrier's and the compiler's).
-  constexpr int NU = K::N_DMA_V + K::N_DMA_REC;
+  constexpr int NVU = kV ? K::N_DMA_V : 0;  // v units moved per step
+  constexpr int NU = NVU + K::N_DMA_REC;
   constexpr int ND = (NU + NP - 1) / NP;
   constexpr int NS = (K::N_DMA_V + NP - 1) / NP;
   static_assert(NS >= 1 && NS <= 2, "one or two output units per producer wave");
@@ -550,13 +569,17 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
     for (int j = 0; j < ND; ++j) {
       if (part >= 0 && j / NDP != part) continue;
       const int i = min(pw + NP * j, NU - 1);
-      const bool isv = i < K::N_DMA_V;
-      const int sl = min(i, K::N_DMA_V - 1) * 64 + lane;
-      const int row = sl / K::UPR, u = (sl % K::UPR) ^ K::vsw(row);
-      const size_t gr = (sbase + min(t0 + row, slen - 1)) * H + h;
-      const char* vsrc = zero_v ? rc + lane * 16 : (const char*)gv + (gr * DV + v0) * 2 + (size_t)u * 16;
-      const char* src = isv ? vsrc : rc + (i - K::N_DMA_V) * 1024 + lane * 16;
-      dma16(src, isv ? v_dst + i * 1024 : rec_dst + (i - K::N_DMA_V) * 1024);
+      if constexpr (kV) {
+        const bool isv = i < NVU;
+        const int sl = min(i, K::N_DMA_V - 1) * 64 + lane;
+        const int row = sl / K::UPR, u = (sl % K::UPR) ^ K::vsw(row);
+        const size_t gr = (sbase + min(t0 + row, slen - 1)) * H + h;
+        const char* vsrc = zero_v ? rc + lane * 16 : (const char*)gv + (gr * DV + v0) * 2 + (size_t)u * 16;
+        const char* src = isv ? vsrc : rc + (i - NVU) * 1024 + lane * 16;
+        dma16(src, isv ? v_dst + i * 1024 : rec_dst + (i - NVU) * 1024);
+      } else {
+        dma16(rc + i * 1024 + lane * 16, rec_dst + i * 1024);
+      }
     }
   };
   // Gate items: lane (rg, cg) = (lane & 15, lane >> 4) of producer wave pw holds rows
@@ -589,12 +612,15 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
     const uint32_t rs = (uint32_t)H * DK * 2;
     ps.nrow = slen - t0;
     const uint32_t off = (uint32_t)min(4 * rg + j, ps.nrow - 1) * rs + 2 * c0;
-    const u32x4v q4 = *(const u32x4v*)((const char*)gq + base + off);
+    if constexpr (kOut) {
+      const u32x4v q4 = *(const u32x4v*)((const char*)gq + base + off);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) ps.q[4 * j + p] = q4[p];
+    }
     const u32x4v k4 = *(const u32x4v*)((const char*)gk + base + off);
     const u32x4v a4 = *(const u32x4v*)((const char*)galpha + base + off);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      ps.q[4 * j + p] = q4[p];
       ps.k[4 * j + p] = k4[p];
       ps.a[4 * j + p] = a4[p];
     }
@@ -679,8 +705,7 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const G gm = X[p] * P[j][p], rh = Y[p] * B[j][p];
-        float q0, q1, k0, k1, e0, e1, r0, r1;
-        R::unpack(ps.q[4 * j + p], q0, q1);
+        float k0, k1, e0, e1, r0, r1;
         R::unpack(ps.k[4 * j + p], k0, k1);
         e0 = k0;
         e1 = k1;
@@ -690,14 +715,18 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
           e0 *= b0;
           e1 *= b1;
         }
-        gm.row(q0, q1, r0, r1);
-        wq[p] = pack_bf16x2(r0, r1);
+        if constexpr (kOut) {
+          float q0, q1;
+          R::unpack(ps.q[4 * j + p], q0, q1);
+          gm.row(q0, q1, r0, r1);
+          wq[p] = pack_bf16x2(r0, r1);
+        }
         gm.row(e0, e1, r0, r1);
         wk[p] = pack_bf16x2(-r0, -r1);
         rh.col(k0, k1, kr[p][0], kr[p][1]);
       }
       const int row = 4 * rg + j;
-      lds_st128(ops + K::OFF_Q + row * K::RS_Q + 2 * c0, wq[0], wq[1], wq[2], wq[3]);
+      if constexpr (kOut) lds_st128(ops + K::OFF_Q + row * K::RS_Q + 2 * c0, wq[0], wq[1], wq[2], wq[3]);
       lds_st128(ops + K::OFF_K + row * K::RS_Q + 2 * c0, wk[0], wk[1], wk[2], wk[3]);
 #pragma unroll
       for (int p = 0; p < 4; ++p)
@@ -761,7 +790,7 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
 #endif
       const int last = nchunks - 1;
       issue_dma(0, rec_a, v_a);
-      write_o(0, false);  // (issues the step's store count; writes nothing)
+      if constexpr (kOut) write_o(0, false);  // (issues the step's store count; writes nothing)
       if constexpr (kItems) {
         load_rows(0, ps0);
         load_rows(min(1, last), ps1);
@@ -773,8 +802,10 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
       // issues lands before the next step's barrier.
       auto pstep = [&](int c, PSet& psP, PSet& psN, char* opsQ, char* recQ, char* vQ) __attribute__((always_inline)) {
         producer_barrier<kWait>();
-        read_o(vQ);
-        write_o(c - 1, c > 0 && !no_out);
+        if constexpr (kOut) {
+          read_o(vQ);
+          write_o(c - 1, c > 0 && !no_out);
+        }
         fence_sched();
         if constexpr (kItems) {
           // chunk c + 1's transfers in four parts between the arithmetic: a wave blocked
@@ -797,8 +828,10 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
         pstep(chunk + 1, ps0, ps1, ops_a, rec_a, v_a);
       }
       full_barrier();
-      read_o((last & 1) ? v_b : v_a);
-      write_o(last, !no_out);
+      if constexpr (kOut) {
+        read_o((last & 1) ? v_b : v_a);
+        write_o(last, !no_out);
+      }
     };
     if (nchunks > 0) {
       if (has_item)
@@ -810,7 +843,7 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
     if (G2 && !zero_v && nchunks > 0) load_w(0);
     auto cstep = [&](int c, const char* opsP, const char* recP, char* vP) __attribute__((always_inline)) {
       full_barrier();  // chunk c landed and its operands are in place
-      walk_chunk<DK, VT, G2, CPX>(opsP, recP, vP, wf, zero_v, slen - c * C, S, wave, g, n);
+      walk_chunk<DK, VT, G2, CPX, MODE>(opsP, recP, vP, wf, zero_v, slen - c * C, S, wave, g, n);
       if (G2 && !zero_v && c + 1 < nchunks) load_w(c + 1);
     };
     for (int chunk = 0; chunk < nchunks; chunk += 2) {
@@ -881,11 +914,11 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(const float* __restrict__
   }
 }
 
-template <int DK, int VT, bool G2, bool CPX>
+template <int DK, int VT, bool G2, bool CPX, int MODE = kWalkFull>
 static void walk_launch(const ChunkArgs& a, const void* ws, int nblocks, int BH, int DV, const float* s0, float* sT,
                         int nseg, int segc, int flags) {
   using K = WCfg<DK, VT>;
-  hipLaunchKernelGGL((chunk_walk_kernel<DK, VT, G2, CPX>), dim3(nblocks), dim3(K::NT), 0, (hipStream_t)a.stream,
+  hipLaunchKernelGGL((chunk_walk_kernel<DK, VT, G2, CPX, MODE>), dim3(nblocks), dim3(K::NT), 0, (hipStream_t)a.stream,
                      (const char*)ws, a.q, a.k, a.alpha, a.erase, a.v, a.write, s0, a.o, sT, a.T, a.H, DV, BH, a.cu,
                      a.ctab_base, a.gmax, nseg, segc, flags);
 }
@@ -909,10 +942,11 @@ static hipError_t launch_walk_split(const ChunkArgs& a, const void* ws, int G) {
   float* P = Bst + (size_t)BH * G * 128 * a.dv;
   float* Sst = P + (size_t)BH * G * 128 * 128;
   // the end states from a zero start (outputs not stored)
-  walk_launch<128, 64, G2, CPX>(a, ws, BH * G * (a.dv / 64), BH, a.dv, nullptr, Bst, G, segc, kSegNoOut);
+  walk_launch<128, 64, G2, CPX, kWalkState>(a, ws, BH * G * (a.dv / 64), BH, a.dv, nullptr, Bst, G, segc,
+                                            kSegNoOut);
   // the transfers: the identity walked with v = 0 (the write gate is then irrelevant)
-  walk_launch<128, 64, G2, CPX>(a, ws, BH * G * 2, BH, 128, nullptr, P, G, segc,
-                                kSegNoOut | kSegZeroV | kSegIdentity);
+  walk_launch<128, 64, G2, CPX, kWalkTransfer>(a, ws, BH * G * 2, BH, 128, nullptr, P, G, segc,
+                                               kSegNoOut | kSegZeroV | kSegIdentity);
   hipLaunchKernelGGL(seg_scan_kernel<128>, dim3(BH * (a.dv / 16)), dim3(256), 0, (hipStream_t)a.stream, a.s0, P,
                      Bst, Sst, G, a.dv);
   walk_launch<128, 64, G2, CPX>(a, ws, BH * G * (a.dv / 64), BH, a.dv, Sst, a.sT, G, segc, kSegLastOnly);
