@@ -165,7 +165,7 @@ __device__ __forceinline__ void scale_col(Frag<bf16_t>& f, const float (&p)[8]) 
 
 // CPX: SFDA complex gates (the alpha tensor holds (Re, Im) of each channel pair's gate).
 template <int DK, bool G2, bool CPX>
-__global__ __launch_bounds__(256, 2) void chunk_records_kernel(
+__global__ __launch_bounds__(256, G2 ? 1 : 2) void chunk_records_kernel(
     const void* __restrict__ gq, const void* __restrict__ gk, const void* __restrict__ galpha,
     const void* __restrict__ gbeta, const void* __restrict__ gerase, int Tlen, int H, char* __restrict__ ws,
     int cpw, const int* __restrict__ cu, const int* __restrict__ ctab, const int* __restrict__ ctotal, int gmax) {

@@ -170,6 +170,16 @@ __device__ __forceinline__ void row_scan16(float (&I)[8], float (&J)[8]) {
 #endif
 }
 
+// A workgroup barrier that waits for this wave's LDS operations only.
+__device__ __forceinline__ void lds_barrier_only() {
+#ifndef KDA_HOST_PASS
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+#endif
+}
+
 // The producers' workgroup barrier: their LDS writes are complete and every vector-memory
 // operation but the last N they issued (the vector-memory counter retires in issue order).
 template <int N>
@@ -312,12 +322,11 @@ __device__ __forceinline__ void walk_chunk(const char* ops, const char* rec, cha
   for (int I = 0; I < NB; ++I) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if constexpr (kV) {
-        float x = bf16_to_f32(*(const uint16_t*)(vb + (16 * I + e) * K::RS_V));
-        if constexpr (G2) x *= wf[4 * I + e];
+      if constexpr (kV && !G2) {
+        const float x = bf16_to_f32(*(const uint16_t*)(vb + (16 * I + e) * K::RS_V));
         Rr[I][e] = 16 * I + e < nvl ? x : 0.f;
       } else {
-        Rr[I][e] = 0.f;
+        Rr[I][e] = 0.f;  // (Gated DeltaNet-2: w o V is added after the products below)
       }
     }
     O[I] = zero4();
@@ -337,6 +346,16 @@ __device__ __forceinline__ void walk_chunk(const char* ops, const char* rec, cha
       mma(Rr[I], fk[ks & 1][I], bsl);
     }
     fence_sched();
+  }
+
+  if constexpr (kV && G2) {  // R += w o V: the write gates' loads have had the products' time
+#pragma unroll
+    for (int I = 0; I < NB; ++I)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = bf16_to_f32(*(const uint16_t*)(vb + (16 * I + e) * K::RS_V)) * wf[4 * I + e];
+        Rr[I][e] += 16 * I + e < nvl ? x : 0.f;
+      }
   }
 
   // Delta = M~ R over the lower blocks (I, s2) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1):
@@ -842,7 +861,10 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
   } else {
     if (G2 && !zero_v && nchunks > 0) load_w(0);
     auto cstep = [&](int c, const char* opsP, const char* recP, char* vP) __attribute__((always_inline)) {
-      full_barrier();  // chunk c landed and its operands are in place
+      // chunk c landed and its operands are in place.  (The compute waves' own memory
+      // operations are only the write-gate loads, which the walk waits for where it uses
+      // them, after the state products: the barrier does not wait for them.)
+      lds_barrier_only();
       walk_chunk<DK, VT, G2, CPX, MODE>(opsP, recP, vP, wf, zero_v, slen - c * C, S, wave, g, n);
       if (G2 && !zero_v && c + 1 < nchunks) load_w(c + 1);
     };
@@ -851,7 +873,7 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
       if (chunk + 1 >= nchunks) break;
       cstep(chunk + 1, ops_b, rec_b, v_b);
     }
-    if (nchunks > 0) full_barrier();  // the last outputs are staged
+    if (nchunks > 0) lds_barrier_only();  // the last outputs are staged
   }
 
   const bool last_only = (flags & kSegLastOnly) != 0;
