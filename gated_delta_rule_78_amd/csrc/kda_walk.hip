@@ -578,27 +578,53 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
       __builtin_amdgcn_raw_buffer_store_b128(j == 0 ? ov0 : ov1, rsrc, (int)(row * rs) + u * 16, 0, 0);
     }
   };
-  // chunk c's v tile and record matrices into v_dst, rec_dst (v tile from the record
-  // itself when v is read as zero: the bytes go unused)
-  constexpr int NDP = (ND + 3) / 4;  // DMA instructions per part (four parts)
-  auto issue_dma = [&](int c, char* rec_dst, char* v_dst, int part = -1) __attribute__((always_inline)) {
+  // The record and v tile of a chunk move through the producers' registers: unit j of
+  // wave pw (16 bytes per lane, 1 KiB per wave) is loaded two steps before use and written
+  // to LDS one step before use, so a load has a whole step to land and the step barrier
+  // waits for LDS writes only.  (With DMA into LDS the barrier must wait for the DMA, and
+  // with it every load issued before it.)  Unit i < NVU is v unit i, the rest record
+  // units; the v tile comes from the record itself when v is read as zero (the bytes go
+  // unused).
+  static_assert(ND <= 8, "unit registers");
+  typedef uint32_t u32x16u __attribute__((ext_vector_type(16)));
+  struct USet {
+    u32x16u lo, hi;  // units 0..3, 4..7
+  };
+  USet us0, us1;
+  auto load_units = [&](int c, USet& us) __attribute__((always_inline)) {
     const char* rc = rec0 + (size_t)c * RL::BYTES;
     const int t0 = c * C;
 #pragma unroll
     for (int j = 0; j < ND; ++j) {
-      if (part >= 0 && j / NDP != part) continue;
       const int i = min(pw + NP * j, NU - 1);
+      const char* src;
       if constexpr (kV) {
         const bool isv = i < NVU;
         const int sl = min(i, K::N_DMA_V - 1) * 64 + lane;
         const int row = sl / K::UPR, u = (sl % K::UPR) ^ K::vsw(row);
         const size_t gr = (sbase + min(t0 + row, slen - 1)) * H + h;
         const char* vsrc = zero_v ? rc + lane * 16 : (const char*)gv + (gr * DV + v0) * 2 + (size_t)u * 16;
-        const char* src = isv ? vsrc : rc + (i - NVU) * 1024 + lane * 16;
-        dma16(src, isv ? v_dst + i * 1024 : rec_dst + (i - NVU) * 1024);
+        src = isv ? vsrc : rc + (i - NVU) * 1024 + lane * 16;
       } else {
-        dma16(rc + i * 1024 + lane * 16, rec_dst + i * 1024);
+        src = rc + i * 1024 + lane * 16;
       }
+      const uint4 x = *(const uint4*)src;
+      u32x16u& d = j < 4 ? us.lo : us.hi;
+      const int o = 4 * (j & 3);
+      d[o] = x.x;
+      d[o + 1] = x.y;
+      d[o + 2] = x.z;
+      d[o + 3] = x.w;
+    }
+  };
+  auto store_units = [&](const USet& us, char* rec_dst, char* v_dst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < ND; ++j) {
+      const int i = min(pw + NP * j, NU - 1);
+      char* dst = (kV && i < NVU) ? v_dst + i * 1024 : rec_dst + (i - NVU) * 1024;
+      const u32x16u& d = j < 4 ? us.lo : us.hi;
+      const int o = 4 * (j & 3);
+      lds_st128(dst + lane * 16, d[o], d[o + 1], d[o + 2], d[o + 3]);
     }
   };
   // Gate items: lane (rg, cg) = (lane & 15, lane >> 4) of producer wave pw holds rows
@@ -802,49 +828,44 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
     // branch around a transfer blurs the counts)
     auto run = [&](auto items) __attribute__((always_inline)) {
       constexpr bool kItems = decltype(items)::value;
-#ifndef KDA_PRODUCER_WAIT
-      constexpr int kWait = 0;
-#else
-      constexpr int kWait = KDA_PRODUCER_WAIT * (kItems ? 1 : 0);
-#endif
       const int last = nchunks - 1;
-      issue_dma(0, rec_a, v_a);
+      load_units(0, us0);
+      if constexpr (kItems) load_rows(0, ps0);
+      load_units(min(1, last), us1);
+      if constexpr (kItems) load_rows(min(1, last), ps1);
       if constexpr (kOut) write_o(0, false);  // (issues the step's store count; writes nothing)
-      if constexpr (kItems) {
-        load_rows(0, ps0);
-        load_rows(min(1, last), ps1);
-        form(ps0, ops_a, [](int) {});
-      }
-      // step c: the outputs of chunk c - 1 out of buffers Q, chunk c + 1's record and v
-      // tile into Q, chunk c + 2's rows into the set chunk c vacated (psN), and chunk
-      // c + 1's operands from psP (rows loaded a step ago) into Q.  Everything a step
-      // issues lands before the next step's barrier.
-      auto pstep = [&](int c, PSet& psP, PSet& psN, char* opsQ, char* recQ, char* vQ) __attribute__((always_inline)) {
-        producer_barrier<kWait>();
-        if constexpr (kOut) {
-          read_o(vQ);
-          write_o(c - 1, c > 0 && !no_out);
-        }
+      store_units(us0, rec_a, v_a);
+      if constexpr (kItems) form(ps0, ops_a, [](int) {});
+      // step c: the outputs of chunk c - 1 out of buffers Q, chunk c + 2's rows into the
+      // register set chunk c vacated (psN) while chunk c + 1's operands are formed from
+      // psP into Q, then chunk c + 1's record and v tile (loaded a step ago) into Q, and
+      // chunk c + 2's units into usN.  The barrier waits for the LDS writes only: a load
+      // issued in step c is first needed in step c + 1, and the compute waves never wait
+      // for one.
+      auto pstep = [&](int c, PSet& psP, PSet& psN, USet& usP, USet& usN, char* opsQ, char* recQ, char* vQ)
+          __attribute__((always_inline)) {
+        lds_barrier_only();
+        if constexpr (kOut) read_o(vQ);
+        fence_sched();
+        if constexpr (kOut) write_o(c - 1, c > 0 && !no_out);
         fence_sched();
         if constexpr (kItems) {
-          // chunk c + 1's transfers in four parts between the arithmetic: a wave blocked
-          // issuing a transfer (memory pipeline full) then still has arithmetic between
-          // the blocks
-          const int cd = min(c + 1, last), cl = min(c + 2, last);
+          const int cl = min(c + 2, last);
           form(psP, opsQ, [&](int j) __attribute__((always_inline)) {
             fence_sched();
-            issue_dma(cd, recQ, vQ, j);
             load_row(cl, psN, j);
             fence_sched();
           });
-        } else {
-          issue_dma(min(c + 1, last), recQ, vQ);
         }
+        fence_sched();
+        store_units(usP, recQ, vQ);
+        fence_sched();
+        load_units(min(c + 2, last), usN);
       };
       for (int chunk = 0; chunk < nchunks; chunk += 2) {
-        pstep(chunk, ps1, ps0, ops_b, rec_b, v_b);
+        pstep(chunk, ps1, ps0, us1, us0, ops_b, rec_b, v_b);
         if (chunk + 1 >= nchunks) break;
-        pstep(chunk + 1, ps0, ps1, ops_a, rec_a, v_a);
+        pstep(chunk + 1, ps0, ps1, us0, us1, ops_a, rec_a, v_a);
       }
       full_barrier();
       if constexpr (kOut) {
