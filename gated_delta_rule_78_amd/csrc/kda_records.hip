@@ -348,6 +348,10 @@ __global__ __launch_bounds__(256, G2 ? 1 : 2) void chunk_records_kernel(
     }
     float* const TT = (float*)(R_L + K::OFF_TT);
     char* const AT = R_L + K::OFF_AT;
+    // the next chunk's inputs, from one place and unconditionally (the last chunk loads
+    // itself again): loads issued on both sides of the path choice would meet in
+    // register copies, which wait for every load in flight
+    issue(min(chunk + 1, c_end - 1));
 
     if (ratio) {
       // ================= ratio path, phase F1: row operands Q o gamma, E o gamma and the
@@ -375,7 +379,6 @@ __global__ __launch_bounds__(256, G2 ? 1 : 2) void chunk_records_kernel(
           bb *= al[m];
         }
       }
-      if (chunk + 1 < c_end) issue(chunk + 1);
       lds_barrier();
       // ================= phase F2: the ten lower 16 x 16 tiles of A (Q o gamma rows) and of
       // D (E o gamma rows) against the column operand; five jobs per wave
@@ -574,7 +577,6 @@ __global__ __launch_bounds__(256, G2 ? 1 : 2) void chunk_records_kernel(
 
       // ================= phase C2: level 1 operands (buffer 0), then the next chunk's inputs
       if (has_item) write_level(R_L, 1);
-      if (chunk + 1 < c_end) issue(chunk + 1);
       lds_barrier();
 
       // ================= phase M3: level 1 tile of block `wave`
@@ -747,27 +749,29 @@ __global__ __launch_bounds__(256, G2 ? 1 : 2) void chunk_records_kernel(
     // residual lo), straight from registers; A~ copied from LDS.  Both lower matrices are
     // stored as their rows 0..31 x columns 0..31 and rows 32..63 x columns 0..63 (pad
     // bytes written as zeros, so whole lines reach memory).
-    for (int x = tid; x < 32 * 5 + 32 * 9; x += NT) {
+    // Every thread stores exactly two units (the second repeating the first where the
+    // 448 units run out: the same bytes to the same place), so the number of stores in
+    // flight is the same in every wave and the next chunk's wait for its prefetched inputs
+    // (loaded before these stores) need not wait for the stores as well.
+    static_assert(32 * 5 + 32 * 9 <= 2 * NT, "two units per thread");
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int x = it == 0 || tid + NT >= 32 * 5 + 32 * 9 ? tid : tid + NT;
       const bool top = x < 32 * 5;
       const int i = top ? x / 5 : 32 + (x - 160) / 9, u = top ? x % 5 : (x - 160) % 9;
       const int ncol = top ? 4 : 8;  // 16-byte data units per row
       char* mh = rec + RL::MH + (top ? i * RL::RS_TOP : RL::BOT + (i - 32) * RL::RS_BOT) + 16 * u;
       char* ml = mh + (RL::ML - RL::MH);
       char* ar = rec + RL::A + (mh - (rec + RL::MH));
-      if (u == ncol) {  // the row's pad unit
-        *(uint4*)mh = make_uint4(0, 0, 0, 0);
-        *(uint4*)ml = make_uint4(0, 0, 0, 0);
-        *(uint4*)ar = make_uint4(0, 0, 0, 0);
-        continue;
-      }
-      const int j0 = 8 * u;
+      const bool pad = u == ncol;  // the row's pad unit: zeros
+      const int j0 = pad ? 0 : 8 * u;
       const float4 m0 = *(const float4*)(MM + i * LDF + j0), m1 = *(const float4*)(MM + i * LDF + j0 + 4);
       const float4 b0 = *(const float4*)(BETA + j0), b1 = *(const float4*)(BETA + j0 + 4);
       float v8[8] = {m0.x * b0.x, m0.y * b0.y, m0.z * b0.z, m0.w * b0.w,
                      m1.x * b1.x, m1.y * b1.y, m1.z * b1.z, m1.w * b1.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        if (j0 + e > i) v8[e] = 0.f;
+        if (pad || j0 + e > i) v8[e] = 0.f;
       uint32_t hw[4], lw[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -776,7 +780,8 @@ __global__ __launch_bounds__(256, G2 ? 1 : 2) void chunk_records_kernel(
       }
       *(uint4*)mh = make_uint4(hw[0], hw[1], hw[2], hw[3]);
       *(uint4*)ml = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-      *(uint4*)ar = *(const uint4*)(AT + i * K::RS_C + j0 * 2);
+      const uint4 av = *(const uint4*)(AT + i * K::RS_C + j0 * 2);
+      *(uint4*)ar = pad ? make_uint4(0, 0, 0, 0) : av;
     }
   }
 }
