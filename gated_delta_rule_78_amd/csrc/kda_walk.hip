@@ -542,7 +542,11 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
   // operations at every wait (the barrier's and the compiler's).
   constexpr int NVU = kV ? K::N_DMA_V : 0;  // v units moved per step
   constexpr int NU = NVU + K::N_DMA_REC;
-  constexpr int ND = (NU + NP - 1) / NP;
+  // a wave's unit slots: NVJ v slots (unit pw + NP j), then NRJ record slots (unit
+  // pw + NP j' of the record, the last one repeated past the end)
+  constexpr int NVJ = (NVU + NP - 1) / NP;
+  constexpr int NRJ = (K::N_DMA_REC + NP - 1) / NP;
+  constexpr int ND = NVJ + NRJ;
   constexpr int NS = (K::N_DMA_V + NP - 1) / NP;
   static_assert(NS >= 1 && NS <= 2, "one or two output units per producer wave");
   typedef uint32_t u32x4o __attribute__((ext_vector_type(4)));
@@ -596,17 +600,17 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
     const int t0 = c * C;
 #pragma unroll
     for (int j = 0; j < ND; ++j) {
-      const int i = min(pw + NP * j, NU - 1);
       const char* src;
-      if constexpr (kV) {
-        const bool isv = i < NVU;
+      if (j < NVJ) {  // v slot (when the wave has no unit there, a record unit again)
+        const int i = pw + NP * j;
         const int sl = min(i, K::N_DMA_V - 1) * 64 + lane;
         const int row = sl / K::UPR, u = (sl % K::UPR) ^ K::vsw(row);
         const size_t gr = (sbase + min(t0 + row, slen - 1)) * H + h;
-        const char* vsrc = zero_v ? rc + lane * 16 : (const char*)gv + (gr * DV + v0) * 2 + (size_t)u * 16;
-        src = isv ? vsrc : rc + (i - NVU) * 1024 + lane * 16;
+        src = zero_v ? rc + lane * 16 : (const char*)gv + (gr * DV + v0) * 2 + (size_t)u * 16;
+        if (NVU % NP != 0 && i >= NVU) src = rc + lane * 16;
       } else {
-        src = rc + i * 1024 + lane * 16;
+        const int r = min(pw + NP * (j - NVJ), K::N_DMA_REC - 1);
+        src = rc + r * 1024 + lane * 16;
       }
       const uint4 x = *(const uint4*)src;
       u32x16u& d = j < 4 ? us.lo : us.hi;
@@ -620,8 +624,14 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
   auto store_units = [&](const USet& us, char* rec_dst, char* v_dst) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < ND; ++j) {
-      const int i = min(pw + NP * j, NU - 1);
-      char* dst = (kV && i < NVU) ? v_dst + i * 1024 : rec_dst + (i - NVU) * 1024;
+      char* dst;
+      if (j < NVJ) {
+        const int i = pw + NP * j;
+        dst = v_dst + i * 1024;
+        if (NVU % NP != 0 && i >= NVU) dst = rec_dst;  // (the record's first unit again)
+      } else {
+        dst = rec_dst + min(pw + NP * (j - NVJ), K::N_DMA_REC - 1) * 1024;
+      }
       const u32x16u& d = j < 4 ? us.lo : us.hi;
       const int o = 4 * (j & 3);
       lds_st128(dst + lane * 16, d[o], d[o + 1], d[o + 2], d[o + 3]);
