@@ -2,8 +2,8 @@
 // the state along the chunks of each (b, h, value tile).
 //
 // Per chunk, with the fp32 state S [d_k x VT] in registers (matrix-core accumulator
-// layout), the chunk's record (A, M~ = (I + T)^-1 diag(beta), the gate block products) and
-// the chunk's q, k, alpha, v:
+// layout), the chunk's record (A, M~ = (I + T)^-1 diag(beta) as a bf16 pair) and the
+// chunk's q, k, alpha, v:
 //   R     = V - (K o gamma) S
 //   Delta = M~ R                              (= M~ V - M~ (K o gamma) S = U - W S)
 //   O     = (Q o gamma) S + A Delta
@@ -25,11 +25,12 @@
 // operands: their errors end in the output, not in the state.
 //
 // Work split in a workgroup: VT / 16 compute waves (16 value columns each) and four
-// producer waves.  The producers move the chunk's record (A, M~ hi, M~ lo) and v tile
-// global -> LDS with 16-byte DMA (two buffers: the next chunk streams in while the
-// current one computes), and rebuild the chunk's operands Q o gamma, -(K o gamma) and
-// (K o rho)^T from q, k, alpha and the record's block products (one gate item = 16 rows x
-// one channel pair per lane, loaded one chunk ahead).
+// producer waves.  The producers load the chunk's record (A, M~ hi, M~ lo) and v tile into
+// registers a step ahead and write them to the second of two LDS buffer sets (the next
+// chunk is assembled while the current one computes), and rebuild the chunk's operands
+// Q o gamma, -(K o gamma) and (K o rho)^T and gamma_last from q, k, alpha alone (one gate
+// item = 4 rows x 8 channels per lane, loaded a step ahead; the running products across
+// row groups are DPP scans).
 #include <stdlib.h>
 
 #include "kda_common.h"
@@ -41,23 +42,9 @@ namespace kda {
 
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void global_void;
-
-// 16 bytes per lane from global memory straight into LDS: lane l of the wave writes
-// lds_wave_base + 16 l (the LDS base is wave-uniform).  Completion is tracked by the
-// vector-memory counter; the data is visible to the workgroup after a vmcnt(0) wait
-// and a barrier.
-__device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
-#ifndef KDA_HOST_PASS
-  __builtin_amdgcn_global_load_lds((global_void*)g, (lds_void*)lds_wave_base, 16, 0, 0);
-#endif
-}
-
-// LDS stores of the producer waves' operands, written as instructions the compiler does
-// not analyse: it cannot tell the operand tiles from the destination of the DMA still in
-// flight and would otherwise wait for that DMA (and every load issued after it) before the
-// first operand store.  The stores complete before the step barrier (lgkmcnt(0) there).
+// LDS stores of the producer waves (operands, record, v tile), written as instructions the
+// compiler does not analyse, so that it neither orders them behind the compute waves'
+// buffer reads nor waits on them; they complete before the step barrier (lgkmcnt(0)).
 __device__ __forceinline__ uint32_t lds_off(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -175,19 +162,6 @@ __device__ __forceinline__ void lds_barrier_only() {
 #ifndef KDA_HOST_PASS
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-#endif
-}
-
-// The producers' workgroup barrier: their LDS writes are complete and every vector-memory
-// operation but the last N they issued (the vector-memory counter retires in issue order).
-template <int N>
-__device__ __forceinline__ void producer_barrier() {
-#ifndef KDA_HOST_PASS
-  static_assert(N >= 0 && N < 64, "6-bit vmcnt");
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);  // vmcnt(N) expcnt(7) lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 #endif
