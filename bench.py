@@ -52,9 +52,9 @@ PMC_FILES = {
                ["kda_decode.hip", "kda_common.h"]),
 }
 # the bf16 walk record of one (b, h, chunk): A, M~ hi and M~ lo, three lower 64 x 64 bf16
-# matrices stored as row-major blocks with 16 pad bytes per row (the image the state pass
-# moves into LDS as it is)
-RECORD_BYTES = {128: 21504, 64: 21504}
+# matrices stored as row-major blocks (rows 0..31 x 32 columns, rows 32..63 x 64 columns;
+# the image the state pass moves into LDS as it is)
+RECORD_BYTES = {128: 18432, 64: 18432}
 
 
 def chunk_bytes(B, T, H, dk, dv, es=2):

@@ -18,10 +18,13 @@
 //   A    lower 64 x 64, bf16      A_ij = sum_c q_ic k_jc r_ijc (j <= i)
 //   MH   lower 64 x 64, bf16      M~ = (I + T)^-1 diag(beta) rounded to bf16
 //   ML   lower 64 x 64, bf16      M~ - MH rounded to bf16 (MH + ML carries M~ to ~2^-17)
-// A lower matrix is stored as two row-major images: rows 0..31 with columns 0..31 (rows of
-// 80 bytes) and rows 32..63 with columns 0..63 (rows of 144 bytes); the 16 pad bytes per
-// row keep the state pass's LDS reads free of bank conflicts.  The state pass moves the
-// whole record into LDS as one image.
+// A lower matrix is stored as two row-major blocks: rows 0..31 with columns 0..31 (rows of
+// 64 bytes) and rows 32..63 with columns 0..63 (rows of 128 bytes); the upper-right 32 x 32
+// block, all zeros, is not stored.  There is no padding: the 16-byte units of a row are
+// permuted instead (unit u of row i sits at u ^ ((i >> 2) & 3) in the top block and at
+// u ^ ((i >> 1) & 7) in the bottom one), so that the sixteen rows a matrix-core fragment
+// read touches land on distinct LDS banks.  The state pass moves the whole record into LDS
+// as one image.
 #pragma once
 #include <stddef.h>
 
@@ -47,8 +50,8 @@ struct RecordLayout {
 
 template <int DK>
 struct WalkRecord {
-  static constexpr int RS_TOP = 32 * 2 + 16;  // rows 0..31, columns 0..31
-  static constexpr int RS_BOT = 64 * 2 + 16;  // rows 32..63, columns 0..63
+  static constexpr int RS_TOP = 32 * 2;  // rows 0..31, columns 0..31
+  static constexpr int RS_BOT = 64 * 2;  // rows 32..63, columns 0..63
   static constexpr int BOT = 32 * RS_TOP;
   static constexpr int MAT = BOT + 32 * RS_BOT;  // one lower matrix
   static constexpr int A = 0;
@@ -56,10 +59,12 @@ struct WalkRecord {
   static constexpr int ML = 2 * MAT;
   static constexpr int DMA = 3 * MAT;  // moved into LDS by the state pass
   static constexpr size_t BYTES = ((size_t)DMA + 255) / 256 * 256;
-  static_assert(DMA % 1024 == 0, "whole wave-wide DMA steps");
+  static_assert(DMA % 1024 == 0, "whole 1 KiB transfer units");
+  // the stored position of 16-byte unit u of row i
+  __host__ __device__ static constexpr int unit(int i, int u) { return i < 32 ? u ^ ((i >> 2) & 3) : u ^ ((i >> 1) & 7); }
   // byte offset of element (i, j), j <= 31 for i <= 31, of a lower matrix image
   __host__ __device__ static constexpr int at(int i, int j) {
-    return i < 32 ? i * RS_TOP + 2 * j : BOT + (i - 32) * RS_BOT + 2 * j;
+    return (i < 32 ? i * RS_TOP : BOT + (i - 32) * RS_BOT) + 16 * unit(i, j >> 3) + 2 * (j & 7);
   }
 };
 

@@ -747,41 +747,37 @@ __global__ __launch_bounds__(256, G2 ? 1 : 2) void chunk_records_kernel(
     lds_barrier();
     // ================= the record: M~ = M diag(beta) as a bf16 pair (hi, and the rounding
     // residual lo), straight from registers; A~ copied from LDS.  Both lower matrices are
-    // stored as their rows 0..31 x columns 0..31 and rows 32..63 x columns 0..63 (pad
-    // bytes written as zeros, so whole lines reach memory).
+    // stored as their rows 0..31 x columns 0..31 and rows 32..63 x columns 0..63, in
+    // 16-byte units permuted per row (WalkRecord::unit).
     // Every thread stores exactly two units (the second repeating the first where the
-    // 448 units run out: the same bytes to the same place), so the number of stores in
+    // 384 units run out: the same bytes to the same place), so the number of stores in
     // flight is the same in every wave and the next chunk's wait for its prefetched inputs
     // (loaded before these stores) need not wait for the stores as well.
-    static_assert(32 * 5 + 32 * 9 <= 2 * NT, "two units per thread");
+    constexpr int NU_TOP = 32 * 4, NU_ALL = NU_TOP + 32 * 8;
+    static_assert(NU_ALL <= 2 * NT, "two units per thread");
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
-      const int x = it == 0 || tid + NT >= 32 * 5 + 32 * 9 ? tid : tid + NT;
-      const bool top = x < 32 * 5;
-      const int i = top ? x / 5 : 32 + (x - 160) / 9, u = top ? x % 5 : (x - 160) % 9;
-      const int ncol = top ? 4 : 8;  // 16-byte data units per row
-      char* mh = rec + RL::MH + (top ? i * RL::RS_TOP : RL::BOT + (i - 32) * RL::RS_BOT) + 16 * u;
-      char* ml = mh + (RL::ML - RL::MH);
-      char* ar = rec + RL::A + (mh - (rec + RL::MH));
-      const bool pad = u == ncol;  // the row's pad unit: zeros
-      const int j0 = pad ? 0 : 8 * u;
+      const int x = it == 0 || tid + NT >= NU_ALL ? tid : tid + NT;
+      const bool top = x < NU_TOP;
+      const int i = top ? x / 4 : 32 + (x - NU_TOP) / 8, u = top ? x % 4 : (x - NU_TOP) % 8;
+      const int off = (top ? i * RL::RS_TOP : RL::BOT + (i - 32) * RL::RS_BOT) + 16 * RL::unit(i, u);
+      const int j0 = 8 * u;
       const float4 m0 = *(const float4*)(MM + i * LDF + j0), m1 = *(const float4*)(MM + i * LDF + j0 + 4);
       const float4 b0 = *(const float4*)(BETA + j0), b1 = *(const float4*)(BETA + j0 + 4);
       float v8[8] = {m0.x * b0.x, m0.y * b0.y, m0.z * b0.z, m0.w * b0.w,
                      m1.x * b1.x, m1.y * b1.y, m1.z * b1.z, m1.w * b1.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        if (pad || j0 + e > i) v8[e] = 0.f;
+        if (j0 + e > i) v8[e] = 0.f;
       uint32_t hw[4], lw[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         hw[e] = pack_bf16x2(v8[2 * e], v8[2 * e + 1]);
         lw[e] = pack_bf16x2(v8[2 * e] - __uint_as_float(hw[e] << 16), v8[2 * e + 1] - __uint_as_float(hw[e] & 0xFFFF0000u));
       }
-      *(uint4*)mh = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      *(uint4*)ml = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-      const uint4 av = *(const uint4*)(AT + i * K::RS_C + j0 * 2);
-      *(uint4*)ar = pad ? make_uint4(0, 0, 0, 0) : av;
+      *(uint4*)(rec + RL::MH + off) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      *(uint4*)(rec + RL::ML + off) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      *(uint4*)(rec + RL::A + off) = *(const uint4*)(AT + i * K::RS_C + j0 * 2);
     }
   }
 }

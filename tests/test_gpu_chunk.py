@@ -222,19 +222,25 @@ def test_intermediates_match_chunk_model():
 
 def _walk_records(ws, B, H, T, dk):
     """Parse the bf16 records of kda_chunk_records: per (b*H + h, chunk) the lower matrices
-    A and M~ = MH + ML (two row-major images: rows 0..31 x columns 0..31 in rows of 80 bytes,
-    rows 32..63 x columns 0..63 in rows of 144 bytes)."""
-    mat = 32 * 80 + 32 * 144
+    A and M~ = MH + ML, each two row-major blocks (rows 0..31 x columns 0..31 in rows of 64
+    bytes, rows 32..63 x columns 0..63 in rows of 128 bytes) whose 16-byte units are
+    permuted per row: unit u of row i is stored at u ^ ((i >> 2) & 3) (top) or
+    u ^ ((i >> 1) & 7) (bottom)."""
+    mat = 32 * 64 + 32 * 128
     nbytes = (3 * mat + 255) // 256 * 256
     nc = (T + 63) // 64
     raw = ws[: B * H * nc * nbytes].cpu().numpy().reshape(B * H, nc, nbytes)
 
     def lower(buf, off):
         m = np.zeros((64, 64), np.float64)
-        top = buf[off: off + 32 * 80].reshape(32, 80)[:, :64].copy().view(np.uint16)
-        bot = buf[off + 32 * 80: off + mat].reshape(32, 144)[:, :128].copy().view(np.uint16)
-        m[:32, :32] = as_float(top, "bf16")
-        m[32:, :] = as_float(bot, "bf16")
+        top = buf[off: off + 32 * 64].reshape(32, 4, 16)
+        bot = buf[off + 32 * 64: off + mat].reshape(32, 8, 16)
+        for i in range(32):
+            t = np.stack([top[i, u ^ ((i >> 2) & 3)] for u in range(4)]).reshape(-1).copy().view(np.uint16)
+            m[i, :32] = as_float(t, "bf16")
+            r = 32 + i
+            b = np.stack([bot[i, u ^ ((r >> 1) & 7)] for u in range(8)]).reshape(-1).copy().view(np.uint16)
+            m[r, :] = as_float(b, "bf16")
         return m
 
     out = []
