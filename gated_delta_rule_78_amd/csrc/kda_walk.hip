@@ -623,7 +623,7 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
   typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
   typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
   struct PSet {
-    u32x16 q, k, a, e;  // dword 4 j + p: row 4 rg + j, channels c0 + 2p, c0 + 2p + 1
+    u32x16 q, k, a;  // dword 4 j + p: row 4 rg + j, channels c0 + 2p, c0 + 2p + 1
     int nrow;           // rows of the loaded chunk that exist
   };
   PSet ps0, ps1;
@@ -653,11 +653,6 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
       ps.k[4 * j + p] = k4[p];
       ps.a[4 * j + p] = a4[p];
     }
-    if constexpr (G2) {
-      const u32x4v e4 = *(const u32x4v*)((const char*)gerase + base + off);
-#pragma unroll
-      for (int p = 0; p < 4; ++p) ps.e[4 * j + p] = e4[p];
-    }
   };
   auto load_rows = [&](int c, PSet& ps) __attribute__((always_inline)) {
 #pragma unroll
@@ -667,11 +662,25 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
   // rows (E: k, or b o k for Gated DeltaNet-2), (K o rho)^T columns, gamma_last
   // hook(j), j = 0..3, runs at four points spread over the work (the step's transfers,
   // issued in parts between the arithmetic)
-  auto form = [&](const PSet& ps, char* ops, auto&& hook) __attribute__((always_inline)) {
-    hook(0);
+  auto form = [&](const PSet& ps, char* ops, int cf, auto&& hook) __attribute__((always_inline)) {
     int t = threadIdx.x - NW * 64;
     asm volatile("" : "+v"(t));
     const int rg = t & 15, c0 = 32 * (t >> 6) + 8 * ((t >> 4) & 3);
+    // (Gated DeltaNet-2) the erase gates of chunk cf, the one being formed: one register
+    // set, loaded here and first used after the gate scans
+    u32x16 ev;
+    if constexpr (G2) {
+      const size_t base = ((sbase + cf * C) * H + h) * DK * 2;
+      const uint32_t rs = (uint32_t)H * DK * 2;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t off = (uint32_t)min(4 * rg + j, slen - cf * C - 1) * rs + 2 * c0;
+        const u32x4v e4 = *(const u32x4v*)((const char*)gerase + base + off);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) ev[4 * j + p] = e4[p];
+      }
+    }
+    hook(0);
     constexpr uint32_t kOne = CPX ? 0x00003F80u : R::kOneWord;
     // gates (channel pair p of row j), the products inside the row group: prefix P (rows
     // up to j) and exclusive suffix B (rows after j), then across the groups
@@ -740,7 +749,7 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
         e1 = k1;
         if constexpr (G2) {
           float b0, b1;
-          R::unpack(ps.e[4 * j + p], b0, b1);
+          R::unpack(ev[4 * j + p], b0, b1);
           e0 *= b0;
           e1 *= b1;
         }
@@ -819,7 +828,7 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
       if constexpr (kItems) load_rows(min(1, last), ps1);
       if constexpr (kOut) write_o(0, false);  // (issues the step's store count; writes nothing)
       store_units(us0, rec_a, v_a);
-      if constexpr (kItems) form(ps0, ops_a, [](int) {});
+      if constexpr (kItems) form(ps0, ops_a, 0, [](int) {});
       // step c: the outputs of chunk c - 1 out of buffers Q, chunk c + 2's rows into the
       // register set chunk c vacated (psN) while chunk c + 1's operands are formed from
       // psP into Q, then chunk c + 1's record and v tile (loaded a step ago) into Q, and
@@ -835,7 +844,7 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
         fence_sched();
         if constexpr (kItems) {
           const int cl = min(c + 2, last);
-          form(psP, opsQ, [&](int j) __attribute__((always_inline)) {
+          form(psP, opsQ, min(c + 1, last), [&](int j) __attribute__((always_inline)) {
             fence_sched();
             load_row(cl, psN, j);
             fence_sched();
