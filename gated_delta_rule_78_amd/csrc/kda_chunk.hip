@@ -55,6 +55,16 @@
 
 namespace kda {
 
+// The rounding residual of Frag::from_acc(a, b) (bf16): the fragment of x - bf16(x) for
+// the same eight values, given the rounded fragment h.
+template <typename T>
+__device__ __forceinline__ void residual_frag(const Frag<T>& h, const f32x4_t& a, const f32x4_t& b, Frag<T>& r) {
+  const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    r.w[e] = pack_bf16x2(x[2 * e] - __uint_as_float(h.w[e] << 16), x[2 * e + 1] - __uint_as_float(h.w[e] & 0xFFFF0000u));
+}
+
 namespace {
 
 template <typename T, int DK, int VT>
@@ -891,10 +901,17 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
     }
 
     // ================= phase S: Delta = U - W S ; O = (Q o gamma) S + A Delta ; S update
+    // (bf16: S in W S and Delta in the state update enter as a bf16 pair, value and
+    // rounding residual, so that their roundings do not accumulate along the chain where the
+    // transitions are orthogonal; the readout A Delta takes the single bf16 value)
     {
-      Frag<T> bs[K::KS];
+      constexpr bool kPair = std::is_same<T, bf16_t>::value;
+      Frag<T> bs[K::KS], bsl[K::KS];
 #pragma unroll
-      for (int ks = 0; ks < K::KS; ++ks) bs[ks].from_acc(S[2 * ks], S[2 * ks + 1]);
+      for (int ks = 0; ks < K::KS; ++ks) {
+        bs[ks].from_acc(S[2 * ks], S[2 * ks + 1]);
+        if constexpr (kPair) residual_frag(bs[ks], S[2 * ks], S[2 * ks + 1], bsl[ks]);
+      }
 #pragma unroll
       for (int I = 0; I < NB; ++I) {
         const char* wrow = WW + (16 * I + n) * K::RS_DK;
@@ -905,11 +922,18 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
           fw[ks].load4x2(wrow + c0 * ES, wrow + (c0 + 16) * ES);
         }
 #pragma unroll
-        for (int ks = 0; ks < K::KS; ++ks) mma(Dl[I], fw[ks], bs[ks]);
+        for (int ks = 0; ks < K::KS; ++ks) {
+          mma(Dl[I], fw[ks], bs[ks]);
+          if constexpr (kPair) mma(Dl[I], fw[ks], bsl[ks]);
+        }
       }
-      Frag<T> bd[2];
+      Frag<T> bd[2], bdl[2];
       bd[0].from_acc(Dl[0], Dl[1]);
       bd[1].from_acc(Dl[2], Dl[3]);
+      if constexpr (kPair) {
+        residual_frag(bd[0], Dl[0], Dl[1], bdl[0]);
+        residual_frag(bd[1], Dl[2], Dl[3], bdl[1]);
+      }
 #pragma unroll
       for (int I = 0; I < NB; ++I) {
         const char* arow = AT + (16 * I + n) * K::RS_C;
@@ -938,7 +962,10 @@ __global__ __launch_bounds__((VT / 16) * 64) void chunk_fwd_kernel(
           fa[s2].load4x2(krow + p0 * ES, krow + (p0 + 16) * ES);
         }
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) mma(S[r], fa[s2], bd[s2]);
+        for (int s2 = 0; s2 < 2; ++s2) {
+          mma(S[r], fa[s2], bd[s2]);
+          if constexpr (kPair) mma(S[r], fa[s2], bdl[s2]);
+        }
       }
       // stage O (over the consumed v tile)
 #pragma unroll

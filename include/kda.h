@@ -138,8 +138,9 @@ int kda_chunk_fwd(const kda_shape* shape, const void* q, const void* k, const vo
  * twice the single-pass kernel at d = 128, measured from 128 to 2,048 heads), and for
  * bf16 the more exact one: its state chain carries the state, the residuals and
  * (I + T)^-1 diag(beta) as bf16 pairs, which keeps the norm-preserving regime (alpha
- * in {-1, +1}, beta in {0, 2}) within the 2e-2 bar at T = 65,536, where the
- * single-pass kernel's single bf16 operands drift past it from T of about 8,192.
+ * in {-1, +1}, beta in {0, 2}) at about 4e-3 at T = 65,536; the single-pass kernel pairs
+ * the state and Delta only (W = (I + T)^-1 diag(beta) (K o gamma) stays single bf16) and
+ * reaches about 1.9e-2 there at T = 8,192, near the 2e-2 bar, more beyond.
  *   workspace       : device memory, 256-byte aligned, not overlapping any argument;
  *                     NULL selects the single-pass kernel.
  *   workspace_bytes : at least kda_chunk_fwd_workspace_size(shape), else
