@@ -904,16 +904,42 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
 // Sst[b, h, g + 1] = P_g Sst[b, h, g] + B_g, where B_g is segment g's end state from a zero
 // start and P_g (d_k x d_k) its end state from the identity with v = 0 -- the affine
 // transfer of a block of the SFDA page ("Principales Contribuciones", item 3), applied
-// segment by segment.  One workgroup per (b, h, 16 state columns), fp32.
+// segment by segment.  One workgroup per (b, h, 16 state columns), fp32: P_g is staged in
+// LDS (P_(g+1) loads into registers while segment g is applied) and each thread carries
+// eight rows of the product as independent sums.
 template <int DK>
 __global__ __launch_bounds__(256) void seg_scan_kernel(const float* __restrict__ s0, const float* __restrict__ P,
                                                      const float* __restrict__ Bst, float* __restrict__ Sst, int G,
                                                      int DV) {
+  constexpr int LP = DK + 4;  // P rows in LDS: four rows a wave reads at once on distinct banks
+  __shared__ float sP[DK * LP];
   __shared__ float sS[DK][17];
   const int nsl = DV / 16, bh = blockIdx.x / nsl, c0 = (blockIdx.x % nsl) * 16;
   const int tid = threadIdx.x, c = tid & 15, r0 = tid >> 4;  // rows r0 + 16 j
   constexpr int RJ = DK / 16;
+  constexpr int NV4 = DK * DK / 4 / 256;  // float4 of P per thread
   const size_t SS = (size_t)DK * DV;
+  // (a native vector, not an array: an array carried across the loop stays in scratch)
+  typedef float pvec __attribute__((ext_vector_type(4 * NV4)));
+  pvec pf;
+  auto load_p = [&](int gi) __attribute__((always_inline)) {
+    const float4* src = (const float4*)(P + ((size_t)bh * G + gi) * DK * DK);
+#pragma unroll
+    for (int i = 0; i < NV4; ++i) {
+      const float4 v = src[tid + 256 * i];
+      pf[4 * i] = v.x;
+      pf[4 * i + 1] = v.y;
+      pf[4 * i + 2] = v.z;
+      pf[4 * i + 3] = v.w;
+    }
+  };
+  auto store_p = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NV4; ++i) {
+      const int x = tid + 256 * i, row = x / (DK / 4), col = 4 * (x % (DK / 4));
+      *(float4*)(sP + row * LP + col) = make_float4(pf[4 * i], pf[4 * i + 1], pf[4 * i + 2], pf[4 * i + 3]);
+    }
+  };
   float* out0 = Sst + (size_t)bh * G * SS;
 #pragma unroll
   for (int j = 0; j < RJ; ++j) {
@@ -922,24 +948,25 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(const float* __restrict__
     sS[r][c] = x;
     out0[(size_t)r * DV + c0 + c] = x;
   }
+  if (G > 1) {
+    load_p(0);
+    store_p();
+  }
   for (int gi = 0; gi + 1 < G; ++gi) {
-    __syncthreads();
-    const float* Pg = P + ((size_t)bh * G + gi) * DK * DK;
+    __syncthreads();  // sP = P_gi, sS = the start state of segment gi
+    if (gi + 2 < G) load_p(gi + 1);
     const float* Bg = Bst + ((size_t)bh * G + gi) * SS;
     float acc[RJ];
 #pragma unroll
-    for (int j = 0; j < RJ; ++j) {
-      const int r = r0 + 16 * j;
-      float a = Bg[(size_t)r * DV + c0 + c];
-      const float4* prow = (const float4*)(Pg + (size_t)r * DK);
+    for (int j = 0; j < RJ; ++j) acc[j] = Bg[(size_t)(r0 + 16 * j) * DV + c0 + c];
 #pragma unroll 4
-      for (int k4 = 0; k4 < DK / 4; ++k4) {
-        const float4 p = prow[k4];
-        a += p.x * sS[4 * k4][c] + p.y * sS[4 * k4 + 1][c] + p.z * sS[4 * k4 + 2][c] + p.w * sS[4 * k4 + 3][c];
-      }
-      acc[j] = a;
+    for (int k = 0; k < DK; ++k) {
+      const float xk = sS[k][c];
+#pragma unroll
+      for (int j = 0; j < RJ; ++j) acc[j] += sP[(r0 + 16 * j) * LP + k] * xk;
     }
     __syncthreads();
+    if (gi + 2 < G) store_p();
     float* outg = Sst + ((size_t)bh * G + gi + 1) * SS;
 #pragma unroll
     for (int j = 0; j < RJ; ++j) {
