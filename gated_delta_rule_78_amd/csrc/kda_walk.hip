@@ -906,18 +906,21 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
 // transfer of a block of the SFDA page ("Principales Contribuciones", item 3), applied
 // segment by segment.  One workgroup per (b, h, 16 state columns), fp32: P_g is staged in
 // LDS (P_(g+1) loads into registers while segment g is applied) and each thread carries
-// eight rows of the product as independent sums.
+// DK / 32 rows of the product as independent sums.
+constexpr int kScanThreads = 512;
+
 template <int DK>
-__global__ __launch_bounds__(256) void seg_scan_kernel(const float* __restrict__ s0, const float* __restrict__ P,
+__global__ __launch_bounds__(kScanThreads) void seg_scan_kernel(const float* __restrict__ s0, const float* __restrict__ P,
                                                      const float* __restrict__ Bst, float* __restrict__ Sst, int G,
                                                      int DV) {
   constexpr int LP = DK + 4;  // P rows in LDS: four rows a wave reads at once on distinct banks
   __shared__ float sP[DK * LP];
   __shared__ float sS[DK][17];
   const int nsl = DV / 16, bh = blockIdx.x / nsl, c0 = (blockIdx.x % nsl) * 16;
-  const int tid = threadIdx.x, c = tid & 15, r0 = tid >> 4;  // rows r0 + 16 j
-  constexpr int RJ = DK / 16;
-  constexpr int NV4 = DK * DK / 4 / 256;  // float4 of P per thread
+  constexpr int NR = kScanThreads / 16;  // row groups
+  const int tid = threadIdx.x, c = tid & 15, r0 = tid >> 4;  // rows r0 + NR j
+  constexpr int RJ = DK / NR;
+  constexpr int NV4 = DK * DK / 4 / kScanThreads;  // float4 of P per thread
   const size_t SS = (size_t)DK * DV;
   // (a native vector, not an array: an array carried across the loop stays in scratch)
   typedef float pvec __attribute__((ext_vector_type(4 * NV4)));
@@ -926,7 +929,7 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(const float* __restrict__
     const float4* src = (const float4*)(P + ((size_t)bh * G + gi) * DK * DK);
 #pragma unroll
     for (int i = 0; i < NV4; ++i) {
-      const float4 v = src[tid + 256 * i];
+      const float4 v = src[tid + kScanThreads * i];
       pf[4 * i] = v.x;
       pf[4 * i + 1] = v.y;
       pf[4 * i + 2] = v.z;
@@ -936,14 +939,14 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(const float* __restrict__
   auto store_p = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NV4; ++i) {
-      const int x = tid + 256 * i, row = x / (DK / 4), col = 4 * (x % (DK / 4));
+      const int x = tid + kScanThreads * i, row = x / (DK / 4), col = 4 * (x % (DK / 4));
       *(float4*)(sP + row * LP + col) = make_float4(pf[4 * i], pf[4 * i + 1], pf[4 * i + 2], pf[4 * i + 3]);
     }
   };
   float* out0 = Sst + (size_t)bh * G * SS;
 #pragma unroll
   for (int j = 0; j < RJ; ++j) {
-    const int r = r0 + 16 * j;
+    const int r = r0 + NR * j;
     const float x = s0 ? s0[((size_t)bh * DK + r) * DV + c0 + c] : 0.f;
     sS[r][c] = x;
     out0[(size_t)r * DV + c0 + c] = x;
@@ -958,19 +961,19 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(const float* __restrict__
     const float* Bg = Bst + ((size_t)bh * G + gi) * SS;
     float acc[RJ];
 #pragma unroll
-    for (int j = 0; j < RJ; ++j) acc[j] = Bg[(size_t)(r0 + 16 * j) * DV + c0 + c];
+    for (int j = 0; j < RJ; ++j) acc[j] = Bg[(size_t)(r0 + NR * j) * DV + c0 + c];
 #pragma unroll 4
     for (int k = 0; k < DK; ++k) {
       const float xk = sS[k][c];
 #pragma unroll
-      for (int j = 0; j < RJ; ++j) acc[j] += sP[(r0 + 16 * j) * LP + k] * xk;
+      for (int j = 0; j < RJ; ++j) acc[j] += sP[(r0 + NR * j) * LP + k] * xk;
     }
     __syncthreads();
     if (gi + 2 < G) store_p();
     float* outg = Sst + ((size_t)bh * G + gi + 1) * SS;
 #pragma unroll
     for (int j = 0; j < RJ; ++j) {
-      const int r = r0 + 16 * j;
+      const int r = r0 + NR * j;
       sS[r][c] = acc[j];
       outg[(size_t)r * DV + c0 + c] = acc[j];
     }
@@ -1010,7 +1013,7 @@ static hipError_t launch_walk_split(const ChunkArgs& a, const void* ws, int G) {
   // the transfers: the identity walked with v = 0 (the write gate is then irrelevant)
   walk_launch<128, 64, G2, CPX, kWalkTransfer>(a, ws, BH * G * 2, BH, 128, nullptr, P, G, segc,
                                                kSegNoOut | kSegZeroV | kSegIdentity);
-  hipLaunchKernelGGL(seg_scan_kernel<128>, dim3(BH * (a.dv / 16)), dim3(256), 0, (hipStream_t)a.stream, a.s0, P,
+  hipLaunchKernelGGL(seg_scan_kernel<128>, dim3(BH * (a.dv / 16)), dim3(kScanThreads), 0, (hipStream_t)a.stream, a.s0, P,
                      Bst, Sst, G, a.dv);
   walk_launch<128, 64, G2, CPX>(a, ws, BH * G * (a.dv / 64), BH, a.dv, Sst, a.sT, G, segc, kSegLastOnly);
   return hipGetLastError();
