@@ -241,10 +241,11 @@ struct BwdPtrs {
 };
 
 // Workspace of a packed batch's backward: chunk blocks [H][gmax], then the chunk table
-// (clamped offsets, (sequence, chunk) pairs, first chunk of each sequence, chunk count).
+// (clamped offsets, (sequence, chunk) pairs, first chunk of each sequence, chunk count),
+// then the gradient kernel's slots.
 struct BwdVarlenLayout {
   int64_t gmax;
-  size_t off_cs, off_tab, off_base, off_total, bytes;
+  size_t off_cs, off_tab, off_base, off_total, off_gs, bytes;
 };
 
 BwdVarlenLayout bwd_varlen_layout(const kda_shape& s, int n_seqs) {
@@ -255,7 +256,8 @@ BwdVarlenLayout bwd_varlen_layout(const kda_shape& s, int n_seqs) {
   L.off_tab = up(L.off_cs + (size_t)(n_seqs + 1) * 4);
   L.off_base = up(L.off_tab + (size_t)L.gmax * 8);
   L.off_total = up(L.off_base + (size_t)n_seqs * 4);
-  L.bytes = up(L.off_total + 4);
+  L.off_gs = up(L.off_total + 4);
+  L.bytes = up(L.off_gs + kda::grad_scratch_bytes((long)s.H * L.gmax, s.dk));
   return L;
 }
 
@@ -341,6 +343,7 @@ int bwd_impl(const kda_shape* shape, const int* cu, int n_seqs, const BwdPtrs& p
     a.ctotal = (const int*)(ws + VL.off_total);
     a.n_seqs = n_seqs;
     a.gmax = (int)VL.gmax;
+    a.gscr = (float*)(ws + VL.off_gs);
   }
   return kda::launch_bwd(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

@@ -116,12 +116,13 @@ __device__ __forceinline__ int chain_chunks(const BwdArgs& a, int NC, int chain)
 
 // the chunk of a per-chunk workgroup (fixed: blockIdx = chain NC + n; packed: blockIdx =
 // h gmax + global chunk); false for a packed batch's workgroups past the last chunk
-__device__ __forceinline__ bool block_chunk(const BwdArgs& a, int NC, ChunkGeom* q, size_t* ws) {
+__device__ __forceinline__ bool block_chunk(const BwdArgs& a, int NC, ChunkGeom* q, size_t* ws,
+                                            int blk = blockIdx.x) {
   if (!a.ctab) {
-    *q = chain_chunk(a, NC, blockIdx.x / NC, blockIdx.x % NC, ws);
+    *q = chain_chunk(a, NC, blk / NC, blk % NC, ws);
     return true;
   }
-  const int gc = blockIdx.x % a.gmax, h = blockIdx.x / a.gmax;
+  const int gc = blk % a.gmax, h = blk / a.gmax;
   if (gc >= *a.ctotal) return false;
   *q = chain_chunk(a, NC, a.ctab[2 * gc] * a.H + h, a.ctab[2 * gc + 1], ws);
   return true;
@@ -1224,7 +1225,37 @@ __global__ __launch_bounds__(256) void walk_scan_kernel(const float* __restrict_
 }
 
 // ---------------------------------------------------------------------------------------
-// bwd_grads_kernel: one workgroup per (b, h, chunk), in five phases:
+// Scratch slots of the gradient kernel: n slots of GradScratch (n a multiple of 8), then
+// the lock words (zero: free; cleared before every launch), [8][GradScratch::lock_row(n)]
+// so that each XCD's words fill cache lines of their own.  Slot s belongs to XCD s % 8: a
+// workgroup takes a free slot of the XCD it runs on and frees it at its end, so a slot's
+// lines only ever sit in that XCD's L2 and the lock needs no cache maintenance (the
+// workgroup's own accesses to the slot have completed when it frees it).  An XCD holds
+// fewer resident workgroups than its n / 8 slots, or waits for one of its own workgroups
+// to free one; a holder never waits for anything before it frees its slot.
+__device__ inline int* grad_slot_lock(float* base, int n, int slot_floats, int s) {
+  return (int*)(base + (size_t)n * slot_floats) + (s & 7) * GradScratch::lock_row(n) + (s >> 3);
+}
+__device__ inline int xcc_id() {
+  int x;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+  return x & 7;
+}
+__device__ inline int grad_slot_acquire(float* base, int n, int slot_floats) {
+  const int per = n / 8, x = xcc_id();
+  int j = (int)(blockIdx.x / 8) % per;
+  while (atomicCAS(grad_slot_lock(base, n, slot_floats, x + 8 * j), 0, 1) != 0) j = j + 1 == per ? 0 : j + 1;
+  return x + 8 * j;
+}
+__device__ inline void grad_slot_release(float* base, int n, int slot_floats, int s) {
+  atomicExch(grad_slot_lock(base, n, slot_floats, s), 0);
+}
+__global__ void clear_words_kernel(int* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+}
+
+// ---------------------------------------------------------------------------------------
+// bwd_grads_kernel: per (b, h, chunk), in five phases:
 //   A  products over the value dimension, by key-channel tile: a wave holds its 16
 //      channels' rows of S and dS' as B fragments in registers and runs d(Q o gamma),
 //      dW and d(K o rho) against dO, dDelta and Delta staged in LDS, then
@@ -1259,7 +1290,13 @@ __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
   const size_t bb = ((size_t)cg.b * a.T + cg.t0) * a.H + cg.h;
   const float *GAM = ch + L.gam, *RHO = ch + L.rho, *PIN = ch + L.pin, *SIG = ch + L.sig;
   const float *S = ch + L.S, *DS = ch + L.DS;
-  float *AV = ch + L.AV, *BV = ch + L.BV, *DWg = ch + L.DW, *F = ch + L.F, *PA = ch + L.PA, *PD = ch + L.PD;
+  // this workgroup's scratch slot, held until the kernel's last use of it
+  __shared__ int sSlot;
+  const GradScratch GS(DK);
+  if (tid == 0) sSlot = grad_slot_acquire(a.gscr, a.gslots, GS.total);
+  __syncthreads();
+  float* gs = a.gscr + (size_t)sSlot * GS.total;
+  float *AV = gs + GS.AV, *BV = gs + GS.BV, *DWg = gs + GS.DW, *F = gs + GS.F, *PA = gs + GS.PA, *PD = gs + GS.PD;
   const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
   auto in4 = [&](const void* p, int i, int c) { return i < len ? ld4<T>(p, kb + i * ks + c) : z4; };
   auto in1 = [&](const void* p, int i, int c) { return i < len ? Elem<T>::load(p, kb + i * ks + c) : 0.f; };
@@ -1785,132 +1822,136 @@ __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
         }
       }
     }
-    return;
-  }
-  for (int item = tid; item < DK * NB; item += NTG) {
-    const int c = item % DK, Mb = item / DK, s = Mb * SUB;
-    // xv: the row operand of the second product (k, or the GDN-2 erase vector b o k)
-    float al[SUB], qv[SUB], kv[SUB], xv[SUB], eg[SUB], pin[SUB], pa[SUB], pd[SUB];
+  } else {
+    for (int item = tid; item < DK * NB; item += NTG) {
+      const int c = item % DK, Mb = item / DK, s = Mb * SUB;
+      // xv: the row operand of the second product (k, or the GDN-2 erase vector b o k)
+      float al[SUB], qv[SUB], kv[SUB], xv[SUB], eg[SUB], pin[SUB], pa[SUB], pd[SUB];
 #pragma unroll
-    for (int r = 0; r < SUB; ++r) {
-      const int i = s + r;
-      al[r] = RA[i * LK + c];
-      qv[r] = RQ[i * LK + c];
-      kv[r] = RK[i * LK + c];
-      eg[r] = G2 ? in1(a.erase, i, c) : 1.f;
-      xv[r] = G2 ? eg[r] * kv[r] : kv[r];
-      pin[r] = PIN[i * DK + c];
-    }
-    const float* PAm = PA + (size_t)(Mb > 0 ? Mb - 1 : 0) * C * DK;
-    const float* PDm = PD + (size_t)(Mb > 0 ? Mb - 1 : 0) * C * DK;
+      for (int r = 0; r < SUB; ++r) {
+        const int i = s + r;
+        al[r] = RA[i * LK + c];
+        qv[r] = RQ[i * LK + c];
+        kv[r] = RK[i * LK + c];
+        eg[r] = G2 ? in1(a.erase, i, c) : 1.f;
+        xv[r] = G2 ? eg[r] * kv[r] : kv[r];
+        pin[r] = PIN[i * DK + c];
+      }
+      const float* PAm = PA + (size_t)(Mb > 0 ? Mb - 1 : 0) * C * DK;
+      const float* PDm = PD + (size_t)(Mb > 0 ? Mb - 1 : 0) * C * DK;
 #pragma unroll
-    for (int r = 0; r < SUB; ++r) {
-      pa[r] = Mb > 0 ? PAm[(s + r) * DK + c] : 0.f;
-      pd[r] = Mb > 0 ? PDm[(s + r) * DK + c] : 0.f;
-    }
-    float gs = 1.f, rend = 1.f;  // gamma_(s-1); r(C-1, e)
+      for (int r = 0; r < SUB; ++r) {
+        pa[r] = Mb > 0 ? PAm[(s + r) * DK + c] : 0.f;
+        pd[r] = Mb > 0 ? PDm[(s + r) * DK + c] : 0.f;
+      }
+      float gs = 1.f, rend = 1.f;  // gamma_(s-1); r(C-1, e)
 #pragma unroll
-    for (int J = 0; J < NB; ++J) {
-      if (J < Mb) gs *= sPib[J * DK + c];
-      if (J > Mb) rend *= sPib[J * DK + c];
-    }
+      for (int J = 0; J < NB; ++J) {
+        if (J < Mb) gs *= sPib[J * DK + c];
+        if (J > Mb) rend *= sPib[J * DK + c];
+      }
 
-    // Zq_i = sum_{j <= i} dA_ij k_j r_ij, Zr_i = sum_{j < i} dD_ij k_j r_ij,
-    // Zc_j = sum_{i >= j} (dA_ij q_i + dD_ij k_i) r_ij
-    float fr[SUB], sg[SUB];
+      // Zq_i = sum_{j <= i} dA_ij k_j r_ij, Zr_i = sum_{j < i} dD_ij k_j r_ij,
+      // Zc_j = sum_{i >= j} (dA_ij q_i + dD_ij k_i) r_ij
+      float fr[SUB], sg[SUB];
 #pragma unroll
-    for (int r = 0; r < SUB; ++r) {
-      fr[r] = Mb < NB - 1 ? F[(s + r) * DK + c] : 0.f;
-      sg[r] = SIG[(s + r) * DK + c];
-    }
-#pragma unroll
-    for (int r = 0; r < SUB; ++r) {
-      const int i = s + r;
-      float zq = sdA[i * LC + i] * kv[r], zr = 0.f, P = 1.f;
-#pragma unroll
-      for (int rj = r - 1; rj >= 0; --rj) {
-        P *= al[rj + 1];
-        zq += sdA[i * LC + s + rj] * kv[rj] * P;
-        zr += sdD[i * LC + s + rj] * kv[rj] * P;
+      for (int r = 0; r < SUB; ++r) {
+        fr[r] = Mb < NB - 1 ? F[(s + r) * DK + c] : 0.f;
+        sg[r] = SIG[(s + r) * DK + c];
       }
-      zq += pin[r] * pa[r];
-      zr += pin[r] * pd[r];
-      float zc = sdA[i * LC + i] * qv[r];
-      P = 1.f;
 #pragma unroll
-      for (int ri = r + 1; ri < SUB; ++ri) {
-        P *= al[ri];
-        zc += (sdA[(s + ri) * LC + i] * qv[ri] + sdD[(s + ri) * LC + i] * xv[ri]) * P;
-      }
-      zc += sg[r] * fr[r];
-      if (i < len) {
-        a.dq[kb + i * ks + c] += zq;
-        if (G2) {  // zr is the row-side sum of T: part of d e, e = b o k
-          a.dk[kb + i * ks + c] += eg[r] * zr + zc;
-          a.derase[kb + i * ks + c] += kv[r] * zr;
-        } else {
-          a.dk[kb + i * ks + c] += zr + zc;
+      for (int r = 0; r < SUB; ++r) {
+        const int i = s + r;
+        float zq = sdA[i * LC + i] * kv[r], zr = 0.f, P = 1.f;
+#pragma unroll
+        for (int rj = r - 1; rj >= 0; --rj) {
+          P *= al[rj + 1];
+          zq += sdA[i * LC + s + rj] * kv[rj] * P;
+          zr += sdD[i * LC + s + rj] * kv[rj] * P;
         }
-      }
-    }
-
-    // gate gradient.  g_i = sum over j < s (and the start-state column j = -1) of the
-    // pair weights times r(s-1, j), for rows i >= s.
-    float bvs = 0.f;  // sum_{j < s} bv_j r(s-1, j)
-    for (int J = 0; J < Mb; ++J) {
-      float part = 0.f;
+        zq += pin[r] * pa[r];
+        zr += pin[r] * pd[r];
+        float zc = sdA[i * LC + i] * qv[r];
+        P = 1.f;
 #pragma unroll
-      for (int r = 0; r < SUB; ++r) part += BV[(J * SUB + r) * DK + c] * SIG[(J * SUB + r) * DK + c];
-      bvs += part * between(J, Mb, c);
-    }
-    const float dgl = sGl[c];
-    float u[SUB];
-#pragma unroll
-    for (int r = 0; r < SUB; ++r) {
-      const int i = s + r;
-      u[r] = AV[i * DK + c] * gs + qv[r] * pa[r] + xv[r] * pd[r];
-      if (i == C - 1) u[r] += bvs + dgl * gs;
-    }
-    float f[SUB];
-    if (Mb < NB - 1) {
-      // rows below the block fold into its last row: X = sum_{i > e} r(i, e) g_i
-      float x = 0.f;
-      for (int I = NB - 1; I > Mb; --I) {
-        float gv[SUB];
-#pragma unroll
-        for (int r = 0; r < SUB; ++r) {
-          const int i = I * SUB + r;
-          gv[r] = AV[i * DK + c] * gs;
-          if (Mb > 0) {
-            const float xi = G2 ? RK[i * LK + c] * in1(a.erase, i, c) : RK[i * LK + c];
-            gv[r] += RQ[i * LK + c] * PAm[i * DK + c] + xi * PDm[i * DK + c];
+        for (int ri = r + 1; ri < SUB; ++ri) {
+          P *= al[ri];
+          zc += (sdA[(s + ri) * LC + i] * qv[ri] + sdD[(s + ri) * LC + i] * xv[ri]) * P;
+        }
+        zc += sg[r] * fr[r];
+        if (i < len) {
+          a.dq[kb + i * ks + c] += zq;
+          if (G2) {  // zr is the row-side sum of T: part of d e, e = b o k
+            a.dk[kb + i * ks + c] += eg[r] * zr + zc;
+            a.derase[kb + i * ks + c] += kv[r] * zr;
+          } else {
+            a.dk[kb + i * ks + c] += zr + zc;
           }
-          if (i == C - 1) gv[r] += bvs + dgl * gs;
         }
-#pragma unroll
-        for (int r = SUB - 1; r >= 0; --r) x = RA[(I * SUB + r) * LK + c] * (gv[r] + x);
       }
-      u[SUB - 1] += x;
+
+      // gate gradient.  g_i = sum over j < s (and the start-state column j = -1) of the
+      // pair weights times r(s-1, j), for rows i >= s.
+      float bvs = 0.f;  // sum_{j < s} bv_j r(s-1, j)
+      for (int J = 0; J < Mb; ++J) {
+        float part = 0.f;
 #pragma unroll
-      for (int r = 0; r < SUB; ++r) f[r] = kv[r] * fr[r] + BV[(s + r) * DK + c] * rend;
-    } else {
+        for (int r = 0; r < SUB; ++r) part += BV[(J * SUB + r) * DK + c] * SIG[(J * SUB + r) * DK + c];
+        bvs += part * between(J, Mb, c);
+      }
+      const float dgl = sGl[c];
+      float u[SUB];
 #pragma unroll
-      for (int r = 0; r < SUB; ++r) f[r] = BV[(s + r) * DK + c];  // the final-state row C - 1
-    }
+      for (int r = 0; r < SUB; ++r) {
+        const int i = s + r;
+        u[r] = AV[i * DK + c] * gs + qv[r] * pa[r] + xv[r] * pd[r];
+        if (i == C - 1) u[r] += bvs + dgl * gs;
+      }
+      float f[SUB];
+      if (Mb < NB - 1) {
+        // rows below the block fold into its last row: X = sum_{i > e} r(i, e) g_i
+        float x = 0.f;
+        for (int I = NB - 1; I > Mb; --I) {
+          float gv[SUB];
 #pragma unroll
-    for (int m = 0; m < SUB; ++m) {
-      float acc = u[SUB - 1];
+          for (int r = 0; r < SUB; ++r) {
+            const int i = I * SUB + r;
+            gv[r] = AV[i * DK + c] * gs;
+            if (Mb > 0) {
+              const float xi = G2 ? RK[i * LK + c] * in1(a.erase, i, c) : RK[i * LK + c];
+              gv[r] += RQ[i * LK + c] * PAm[i * DK + c] + xi * PDm[i * DK + c];
+            }
+            if (i == C - 1) gv[r] += bvs + dgl * gs;
+          }
 #pragma unroll
-      for (int i = SUB - 2; i >= m; --i) acc = u[i] + al[i + 1] * acc;
-      if (s + m < len) a.dalpha[kb + (s + m) * ks + c] = acc;
+          for (int r = SUB - 1; r >= 0; --r) x = RA[(I * SUB + r) * LK + c] * (gv[r] + x);
+        }
+        u[SUB - 1] += x;
 #pragma unroll
-      for (int i = m + 1; i < SUB; ++i) {
-        float E = (qv[i] * sdA[(s + i) * LC + s + m] + xv[i] * sdD[(s + i) * LC + s + m]) * kv[m];
-        if (i == SUB - 1) E += f[m];
-        u[i] = al[m] * u[i] + E;
+        for (int r = 0; r < SUB; ++r) f[r] = kv[r] * fr[r] + BV[(s + r) * DK + c] * rend;
+      } else {
+#pragma unroll
+        for (int r = 0; r < SUB; ++r) f[r] = BV[(s + r) * DK + c];  // the final-state row C - 1
+      }
+#pragma unroll
+      for (int m = 0; m < SUB; ++m) {
+        float acc = u[SUB - 1];
+#pragma unroll
+        for (int i = SUB - 2; i >= m; --i) acc = u[i] + al[i + 1] * acc;
+        if (s + m < len) a.dalpha[kb + (s + m) * ks + c] = acc;
+#pragma unroll
+        for (int i = m + 1; i < SUB; ++i) {
+          float E = (qv[i] * sdA[(s + i) * LC + s + m] + xv[i] * sdD[(s + i) * LC + s + m]) * kv[m];
+          if (i == SUB - 1) E += f[m];
+          u[i] = al[m] * u[i] + E;
+        }
       }
     }
   }
+  // the slot is free again once every wave's accesses to it have completed
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) grad_slot_release(a.gscr, a.gslots, GS.total, sSlot);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1951,10 +1992,17 @@ static hipError_t launch_bwd_dk(const BwdArgs& a, int NC) {
     hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX>), dim3(wv), dim3(NT), 0, st, a, NC, wf);
   }
   if (per_chunk > 0) {
+    BwdArgs ag = a;
+    if (!ag.gscr)  // fixed-length batch: after the chunk blocks and the split walks' scratch
+      ag.gscr = a.ws + (size_t)chains * NC * BwdLayout(DK, a.Dv).total +
+                bwd_split_bytes(a.B, a.T, a.H, a.Dk, a.Dv) / sizeof(float);
+    ag.gslots = (int)grad_slots(per_chunk);
+    hipLaunchKernelGGL(clear_words_kernel, dim3(1), dim3(256), 0, st,
+                       (int*)(ag.gscr + (size_t)ag.gslots * GradScratch(DK).total), 8 * GradScratch::lock_row(ag.gslots));
     if (a.Dv == 64)
-      hipLaunchKernelGGL((bwd_grads_kernel<T, DK, 64, G2, CPX>), dim3(per_chunk), dim3(NTG), 0, st, a, NC);
+      hipLaunchKernelGGL((bwd_grads_kernel<T, DK, 64, G2, CPX>), dim3(per_chunk), dim3(NTG), 0, st, ag, NC);
     else
-      hipLaunchKernelGGL((bwd_grads_kernel<T, DK, 128, G2, CPX>), dim3(per_chunk), dim3(NTG), 0, st, a, NC);
+      hipLaunchKernelGGL((bwd_grads_kernel<T, DK, 128, G2, CPX>), dim3(per_chunk), dim3(NTG), 0, st, ag, NC);
   }
   return hipGetLastError();
 }

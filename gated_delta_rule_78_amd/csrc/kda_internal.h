@@ -92,14 +92,17 @@ struct BwdArgs {
   // SFDA (complex gates in alpha's place, (Re, Im) per key-channel pair; dalpha returns
   // d/dRe, d/dIm in the same channels)
   bool cpx = false;
+  // the gradient kernel's slots (grad_scratch_bytes); NULL: right after the split walks'
+  // scratch of a fixed-length batch
+  float* gscr = nullptr;
+  int gslots = 0;
 };
 
 // fp32 offsets inside one chunk's workspace block of the backward (C = 64 rows, NB = 4
 // blocks of 16): gate products, A, D, M, W, K o rho, Q o gamma (records); S_n, Delta_n
-// (forward walk);
-// dS'_n, dDelta_n (adjoint walk); scratch of the gradient kernel.
+// (forward walk); dS'_n, dDelta_n (adjoint walk).
 struct BwdLayout {
-  int gam, rho, pin, sig, pib, A, D, M, W, KR, QG, S, DL, DS, DDL, AV, BV, DW, F, PA, PD, total;
+  int gam, rho, pin, sig, pib, A, D, M, W, KR, QG, S, DL, DS, DDL, total;
   __host__ __device__ BwdLayout(int dk, int dv) {
     const int C = 64, CK = C * dk;
     gam = 0;
@@ -117,24 +120,52 @@ struct BwdLayout {
     DL = S + dk * dv;
     DS = DL + C * dv;
     DDL = DS + dk * dv;
-    AV = DDL + C * dv;
+    total = (DDL + C * dv + 63) / 64 * 64;
+  }
+};
+
+// The gradient kernel's own scratch, one slot per resident workgroup (fp32 offsets in a
+// slot): AV, BV, dW, F [C][dk] and the anchored products PA, PD [3][C][dk].  A workgroup
+// holds a slot while it runs, so the slots are rewritten chunk after chunk and the ones in
+// use at once are few enough to stay in the chip's caches.  A lock word per slot follows
+// the slots.
+struct GradScratch {
+  int AV, BV, DW, F, PA, PD, total;
+  __host__ __device__ GradScratch(int dk) {
+    const int CK = 64 * dk;
+    AV = 0;
     BV = AV + CK;
     DW = BV + CK;
     F = DW + CK;
     PA = F + CK;
     PD = PA + 3 * CK;
-    total = (PD + 3 * CK + 63) / 64 * 64;
+    total = PD + 3 * CK;
   }
+  // lock words per XCD for n slots (n / 8 of them, in whole 128-byte lines)
+  __host__ __device__ static int lock_row(long n) { return (int)((n / 8 + 31) / 32 * 32); }
 };
+// (64 per XCD, more than the 32 gradient workgroups an XCD holds at once)
+constexpr long kGradSlots = 512;
+inline long grad_slots(long chunk_blocks) {  // a multiple of 8: the slots are split by XCD
+  const long n = (chunk_blocks + 7) / 8 * 8;
+  return n < kGradSlots ? n : kGradSlots;
+}
+inline size_t grad_scratch_bytes(long chunk_blocks, int dk) {
+  const size_t n = (size_t)grad_slots(chunk_blocks);
+  return n * GradScratch(dk).total * sizeof(float) + ((size_t)8 * GradScratch::lock_row((long)n) * 4 + 255) / 256 * 256;
+}
 
 // Few chains over long sequences: the backward walks split each chain into this many
 // segments (1: one walk per chain), with bwd_split_bytes of scratch after the chunk blocks.
 int bwd_walk_segments(int B, int T, int H, int dk, int dv);
 size_t bwd_split_bytes(int B, int T, int H, int dk, int dv);
 
+// chunk blocks [B H NC], the split walks' scratch, the gradient kernel's slots
 inline size_t bwd_workspace_bytes(int B, int T, int H, int dk, int dv) {
   const size_t nchunks = ((size_t)T + 63) / 64;
-  return (size_t)B * H * nchunks * BwdLayout(dk, dv).total * sizeof(float) + bwd_split_bytes(B, T, H, dk, dv);
+  const size_t blocks = (size_t)B * H * nchunks;
+  return blocks * BwdLayout(dk, dv).total * sizeof(float) + bwd_split_bytes(B, T, H, dk, dv) +
+         grad_scratch_bytes((long)blocks, dk);
 }
 
 hipError_t launch_bwd(const BwdArgs& a);

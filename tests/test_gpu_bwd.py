@@ -194,8 +194,14 @@ def test_bwd_split_walks(long_memory):
     against the oracle on all heads; the workspace grows by the split's scratch."""
     import gated_delta_rule_78_amd as kda
     T = 64 * 130 + 5
-    plain = kda.bwd_workspace_size(1, 64 * 15, 2, 128, 128) // (15 * 2)      # one chunk block
-    assert kda.bwd_workspace_size(1, T, 2, 128, 128) == 131 * 2 * plain + 2 * 8 * 128 * (2 * 128 + 128) * 4
+
+    def slots(n):  # the gradient pass's slots: n rounded up to 8, at most 512, of 10 x 64 x 128
+        m = min((n + 7) // 8 * 8, 512)  # fp32, then 8 rows of lock words in whole 128-byte lines
+        return m * 10 * 64 * 128 * 4 + (8 * ((m // 8 + 31) // 32 * 32) * 4 + 255) // 256 * 256
+
+    plain = (kda.bwd_workspace_size(1, 64 * 15, 2, 128, 128) - slots(30)) // (15 * 2)  # one chunk block
+    assert kda.bwd_workspace_size(1, T, 2, 128, 128) == (131 * 2 * plain + 2 * 8 * 128 * (2 * 128 + 128) * 4
+                                                         + slots(262))
     inp, dO, dST, S0 = _split_inputs("ckda", 95 + long_memory, long_memory)
     _check(inp, dO, dST, S0, label="split long memory" if long_memory else "split")
 
