@@ -236,12 +236,12 @@ __device__ __forceinline__ void fence_sched() {
 }
 
 // One chunk of the walk for compute wave `wave` (value columns 16 wave + n of the tile):
-// operands in `ops`, record (A, MH, ML) in `rec`, v tile in `vv` (rows nv.. of the chunk lie
-// past the end of the sequence and read as zero); S advances one chunk and the outputs are
-// staged over this wave's own (consumed) columns of `vv`.
+// operands in `ops`, record (A, MH, ML) in `rec`, v tile in `vv` (rows past the end of the
+// sequence hold zeros); S advances one chunk and the outputs are staged over this wave's
+// own (consumed) columns of `vv`.
 template <int DK, int VT, bool G2, bool CPX, int MODE>
 __device__ __forceinline__ void walk_chunk(const char* ops, const char* rec, char* vv, const float (&wf)[16],
-                                           bool zero_v, int nv, f32x4_t (&S)[DK / 16], int wave, int g, int n) {
+                                           f32x4_t (&S)[DK / 16], int wave, int g, int n) {
   constexpr bool kOut = MODE == kWalkFull;    // outputs formed and staged
   constexpr bool kV = MODE != kWalkTransfer;  // v read
   using K = WCfg<DK, VT>;
@@ -254,10 +254,10 @@ __device__ __forceinline__ void walk_chunk(const char* ops, const char* rec, cha
   const int col = 16 * wave + n;
 
   // (one base address for this lane's column of the v tile, rows at immediate offsets; the
-  // tile is read whole and the rows past the end masked, so no per-row address or branch).
+  // tile is read whole: the producers store the rows past the end, and the whole tile when
+  // v is read as zero, as zeros, so no per-row address, mask or branch).
   // Rows 16 I + 4g + e share the unit permutation of row 4g (vsw depends on bits 2, 3).
   char* const vb = vv + 4 * g * K::RS_V + 16 * ((col >> 3) ^ K::vsw(4 * g)) + (col & 7) * 2;
-  const int nvl = zero_v ? 0 : nv - 4 * g;  // rows 16 I + e of this lane that exist: 16 I + e < nvl
   // The operand fragments of each group of products are loaded one group ahead and the
   // scheduling fences keep them there: with one compute wave per SIMD little else hides
   // the LDS latency.
@@ -297,8 +297,7 @@ __device__ __forceinline__ void walk_chunk(const char* ops, const char* rec, cha
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if constexpr (kV && !G2) {
-        const float x = bf16_to_f32(*(const uint16_t*)(vb + (16 * I + e) * K::RS_V));
-        Rr[I][e] = 16 * I + e < nvl ? x : 0.f;
+        Rr[I][e] = bf16_to_f32(*(const uint16_t*)(vb + (16 * I + e) * K::RS_V));
       } else {
         Rr[I][e] = 0.f;  // (Gated DeltaNet-2: w o V is added after the products below)
       }
@@ -327,8 +326,7 @@ __device__ __forceinline__ void walk_chunk(const char* ops, const char* rec, cha
     for (int I = 0; I < NB; ++I)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float x = bf16_to_f32(*(const uint16_t*)(vb + (16 * I + e) * K::RS_V)) * wf[4 * I + e];
-        Rr[I][e] += 16 * I + e < nvl ? x : 0.f;
+        Rr[I][e] += bf16_to_f32(*(const uint16_t*)(vb + (16 * I + e) * K::RS_V)) * wf[4 * I + e];
       }
   }
 
@@ -408,7 +406,11 @@ __device__ __forceinline__ void walk_chunk(const char* ops, const char* rec, cha
 #pragma unroll
     for (int I = 0; I < NB; ++I)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) *(uint16_t*)(vb + (16 * I + e) * K::RS_V) = f32_to_bf16(O[I][e]);
+      for (int e = 0; e < 4; e += 2) {  // rows e and e + 1 rounded by one conversion
+        const uint32_t w = pack_bf16x2(O[I][e], O[I][e + 1]);
+        *(uint16_t*)(vb + (16 * I + e) * K::RS_V) = (uint16_t)w;
+        *(uint16_t*)(vb + (16 * I + e + 1) * K::RS_V) = (uint16_t)(w >> 16);
+      }
   }
 }
 
@@ -562,7 +564,7 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
   // waits for LDS writes only.  (With DMA into LDS the barrier must wait for the DMA, and
   // with it every load issued before it.)  Unit i < NVU is v unit i, the rest record
   // units; the v tile comes from the record itself when v is read as zero (the bytes go
-  // unused).
+  // unused, the stores write zeros).
   static_assert(ND <= 8, "unit registers");
   typedef uint32_t u32x16u __attribute__((ext_vector_type(16)));
   struct USet {
@@ -595,22 +597,31 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
       d[o + 3] = x.w;
     }
   };
-  auto store_units = [&](const USet& us, char* rec_dst, char* v_dst) __attribute__((always_inline)) {
+  // (v rows at or past `nvrow`, the rows of the chunk that exist, or all of them when v is
+  // read as zero, are stored as zeros: the compute waves read the tile unmasked)
+  auto store_units = [&](const USet& us, char* rec_dst, char* v_dst, int nvrow) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < ND; ++j) {
       char* dst;
+      bool zero = false;
       if (j < NVJ) {
         const int i = pw + NP * j;
         dst = v_dst + i * 1024;
-        if (NVU % NP != 0 && i >= NVU) dst = rec_dst;  // (the record's first unit again)
+        const int row = (min(i, K::N_DMA_V - 1) * 64 + lane) / K::UPR;
+        zero = row >= nvrow;
+        if (NVU % NP != 0 && i >= NVU) {  // (the record's first unit again)
+          dst = rec_dst;
+          zero = false;
+        }
       } else {
         dst = rec_dst + min(pw + NP * (j - NVJ), K::N_DMA_REC - 1) * 1024;
       }
       const u32x16u& d = j < 4 ? us.lo : us.hi;
       const int o = 4 * (j & 3);
-      lds_st128(dst + lane * 16, d[o], d[o + 1], d[o + 2], d[o + 3]);
+      lds_st128(dst + lane * 16, zero ? 0u : d[o], zero ? 0u : d[o + 1], zero ? 0u : d[o + 2], zero ? 0u : d[o + 3]);
     }
   };
+  auto v_rows = [&](int c) { return zero_v ? 0 : slen - c * C; };
   // Gate items: lane (rg, cg) = (lane & 15, lane >> 4) of producer wave pw holds rows
   // 4 rg .. 4 rg + 3 of channels c0 = 32 pw + 8 cg .. c0 + 7 (one 16-byte vector per row
   // and tensor: few, wide loads).  The 16 row groups of a channel group are the 16 lanes of
@@ -827,7 +838,7 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
       load_units(min(1, last), us1);
       if constexpr (kItems) load_rows(min(1, last), ps1);
       if constexpr (kOut) write_o(0, false);  // (issues the step's store count; writes nothing)
-      store_units(us0, rec_a, v_a);
+      store_units(us0, rec_a, v_a, v_rows(0));
       if constexpr (kItems) form(ps0, ops_a, 0, [](int) {});
       // step c: the outputs of chunk c - 1 out of buffers Q, chunk c + 2's rows into the
       // register set chunk c vacated (psN) while chunk c + 1's operands are formed from
@@ -851,7 +862,7 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
           });
         }
         fence_sched();
-        store_units(usP, recQ, vQ);
+        store_units(usP, recQ, vQ, v_rows(min(c + 1, last)));
         fence_sched();
         load_units(min(c + 2, last), usN);
       };
@@ -879,7 +890,7 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
       // operations are only the write-gate loads, which the walk waits for where it uses
       // them, after the state products: the barrier does not wait for them.)
       lds_barrier_only();
-      walk_chunk<DK, VT, G2, CPX, MODE>(opsP, recP, vP, wf, zero_v, slen - c * C, S, wave, g, n);
+      walk_chunk<DK, VT, G2, CPX, MODE>(opsP, recP, vP, wf, S, wave, g, n);
       if (G2 && !zero_v && c + 1 < nchunks) load_w(c + 1);
     };
     for (int chunk = 0; chunk < nchunks; chunk += 2) {
