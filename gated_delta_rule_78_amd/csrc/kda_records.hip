@@ -632,13 +632,14 @@ __global__ __launch_bounds__(256, G2 ? 1 : 2) void chunk_records_kernel(
       }
 #pragma unroll
       for (int p = 0; p < SUB; ++p) tr[p] = p < col ? bcol * tr[p] : 0.f;
+      dpp_sources_ready(tr);
       float x[SUB], nx[SUB];  // column of N_II and its negation
-#define KDA_FS_ROW(i)                                                                        \
-  {                                                                                          \
-    float acc = (col == i) ? 1.f : 0.f;                                                      \
-    _Pragma("unroll") for (int p = 0; p < i; ++p) acc = fmaf(row_bcast<i>(tr[p]), nx[p], acc); \
-    x[i] = acc;                                                                              \
-    nx[i] = -acc;                                                                            \
+#define KDA_FS_ROW(i)                                                                     \
+  {                                                                                       \
+    float acc = (col == i) ? 1.f : 0.f;                                                   \
+    _Pragma("unroll") for (int p = 0; p < i; ++p) acc = fmac_bcast<i>(acc, tr[p], nx[p]); \
+    x[i] = acc;                                                                           \
+    nx[i] = -acc;                                                                         \
   }
       KDA_FS_ROW(0) KDA_FS_ROW(1) KDA_FS_ROW(2) KDA_FS_ROW(3) KDA_FS_ROW(4) KDA_FS_ROW(5) KDA_FS_ROW(6)
       KDA_FS_ROW(7) KDA_FS_ROW(8) KDA_FS_ROW(9) KDA_FS_ROW(10) KDA_FS_ROW(11) KDA_FS_ROW(12) KDA_FS_ROW(13)

@@ -81,6 +81,28 @@ __device__ __forceinline__ float row_bcast(float x) {
                                                                0xF, true));
 }
 
+// acc + (x of lane `src` of this lane's 16-lane DPP row) * y in one v_fmac_f32 with a
+// row_newbcast source, one rounding as fmaf.  x must have been written at least two
+// wait states before (dpp_sources_ready): the compiler does not see the DPP read inside
+// the asm.
+template <int src>
+__device__ __forceinline__ float fmac_bcast(float acc, float x, float y) {
+#ifndef KDA_HOST_PASS
+  asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf" : "+v"(acc) : "v"(x), "v"(y), "n"(src));
+#endif
+  return acc;
+}
+
+// Two wait states after the writes of the sixteen values read by fmac_bcast (ordered
+// after them: they are the asm's operands, left in place).
+__device__ __forceinline__ void dpp_sources_ready(float (&t)[16]) {
+#ifndef KDA_HOST_PASS
+  asm volatile("s_nop 1"
+               : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]), "+v"(t[4]), "+v"(t[5]), "+v"(t[6]), "+v"(t[7]),
+                 "+v"(t[8]), "+v"(t[9]), "+v"(t[10]), "+v"(t[11]), "+v"(t[12]), "+v"(t[13]), "+v"(t[14]), "+v"(t[15]));
+#endif
+}
+
 // 16x16 fp32 product step: acc += A B with A[row n][k-slot 4 g + s], B[k-slot 4 g + s][col n]
 __device__ __forceinline__ void mm4(f32x4_t& acc, const float (&a)[4], const float (&b)[4]) {
 #ifndef KDA_HOST_PASS
