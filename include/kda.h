@@ -33,7 +33,9 @@
  *
  * Conventions shared by all entry points
  *   - Every pointer except `shape` is a DEVICE pointer on the current HIP
- *     device; the caller owns every buffer.  The library allocates nothing.
+ *     device; the caller owns every buffer.  The library allocates nothing,
+ *     except the two-pass workspace that kda_chunk_fwd takes from the
+ *     stream-ordered pool (see there).
  *   - Layouts are dense, row-major, contiguous:
  *       q, k, alpha : [B, T, H, dk]      (decode: [B, H, dk])
  *       v           : [B, T, H, dv]      (decode: [B, H, dv])
@@ -45,8 +47,10 @@
  *     16-byte aligned q, k, v, alpha and o (they move in 16-byte vectors).
  *     Every other pointer needs only the alignment of its element type.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = default
- *     stream).  The library keeps no mutable global state; concurrent calls
- *     on different streams with disjoint outputs are safe.
+ *     stream).  The library keeps no mutable global state apart from
+ *     kda_chunk_fwd_noalloc's per-GPU scratch array (calls of that entry point
+ *     that overlap in time on one GPU race); concurrent calls of the others on
+ *     different streams with disjoint outputs and workspaces are safe.
  *   - Return value: KDA_OK (0), or a negative kda_status.  Argument errors are
  *     detected on the host before anything is launched; KDA_ERR_HIP reports a
  *     launch failure (hipGetLastError).  No C++ exception crosses the ABI.
