@@ -288,6 +288,29 @@ def test_records_match_chunk_model(gates):
 
 
 @pytest.mark.parametrize("path", PATHS)
+def test_gate_products_at_the_ratio_threshold(path):
+    """The record pass forms the decay ratios as products with 1 / gamma_last only where
+    every channel's gate product over the chunk keeps |gamma_last| >= 2^-64.  Chunk 0 sits
+    exactly on that bound (|alpha| = 1/2 on every row and channel, signs mixed: the largest
+    factors, 2^64, the ratio products allow); chunk 1 falls just below it (alpha = 63/128,
+    products near 2^-66: the level products); chunk 2 is on the bound again with one zero
+    gate in one channel (level products: exact zero ratios across it); then a ragged
+    random tail.  Every head against the oracle."""
+    from gated_delta_rule_78_amd.inputs import bf16_bits
+    T = 3 * 64 + 10
+    inp = make(1, T, 2, 128, 128, "bf16", "kda", False, seed=77)
+    a = as_float(inp.alpha, "bf16").copy()
+    sign = np.random.default_rng(78).choice(np.array([-1.0, 1.0], np.float32), size=a[:, :64].shape)
+    a[:, 0:64] = 0.5 * sign
+    a[:, 64:128] = 63.0 / 128.0
+    a[:, 128:192] = 0.5
+    a[0, 150, 1, 17] = 0.0
+    inp.alpha = bf16_bits(a)
+    assert np.array_equal(as_float(inp.alpha, "bf16"), a)  # every gate exact in bf16
+    _check(inp, inp.S0, label="ratio-threshold", path=path)
+
+
+@pytest.mark.parametrize("path", PATHS)
 def test_full_kda_prefill_8k(path):
     """The B4 H32 T8192 KDA workload in the launch configuration the benchmark times,
     every head against the oracle."""
