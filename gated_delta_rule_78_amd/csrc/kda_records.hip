@@ -1,7 +1,8 @@
 // kda_records.hip -- first pass of the two-pass chunk forward (bf16): the record of every
-// chunk (-W, Q o gamma, (K o rho)^T, A~, M~, gamma_last), sized so that two workgroups
-// share a compute unit (<= 80 KiB of LDS, <= 256 registers per lane): while one
-// workgroup waits on a dependent LDS read or a barrier, the other issues.
+// chunk (A~ and M~ = (I + T)^-1 diag(beta) as a bf16 pair; the walk rebuilds the
+// gate-scaled q and k itself), sized so that two workgroups share a compute unit
+// (<= 80 KiB of LDS, <= 256 registers per lane): while one workgroup waits on a dependent
+// LDS read or a barrier, the other issues.
 //
 // The math is that of the chunk-WY product form on the SFDA page ("El Teorema de
 // Chunk-WY Constructivo"; "Principales Contribuciones" item 3) and the decay-absorbed WY
@@ -20,8 +21,9 @@
 //     across the block's lanes, not a matrix-core pass over the raw q, k tiles;
 //   * the four levels run as three passes through two level buffers, their results
 //     stay in registers until every product is done;
-//   * Q o gamma and (K o rho)^T go from the items' registers straight to the record;
-//     only -W, A~, M~ and gamma_last are assembled in LDS and copied out.
+//   * where every channel's gate product over the chunk stays >= 2^-64 in magnitude the
+//     decay ratios are formed as one product per matrix (the ratio path) instead;
+//   * A~ is assembled in LDS and copied out, M~ goes from registers to the record.
 #include "kda_common.h"
 #include "kda_internal.h"
 #include "kda_record.h"
@@ -342,9 +344,15 @@ __global__ __launch_bounds__(256, G2 ? 1 : 2) void chunk_records_kernel(
       const G gl = t0v * t1v * t2v * t3v;
       const bool ok = !has_item || (fabsf(gl.x) >= 0x1p-64f && fabsf(gl.y) >= 0x1p-64f);
       const bool wave_ok = __ballot(!ok) == 0;
-      if (lane == 0) OKW[wave] = wave_ok ? 1 : 0;
-      lds_barrier();
-      ratio = (OKW[0] & OKW[1] & OKW[2] & OKW[3]) != 0;
+      if constexpr (K::NITEM == NT) {
+        // every wave holds the items of one block over all channel pairs, so its own vote
+        // is the chunk's: no exchange
+        ratio = wave_ok;
+      } else {
+        if (lane == 0) OKW[wave] = wave_ok ? 1 : 0;
+        lds_barrier();
+        ratio = (OKW[0] & OKW[1] & OKW[2] & OKW[3]) != 0;
+      }
     }
     float* const TT = (float*)(R_L + K::OFF_TT);
     char* const AT = R_L + K::OFF_AT;
