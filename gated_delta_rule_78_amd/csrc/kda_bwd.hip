@@ -262,13 +262,18 @@ template <int NTR>
 __device__ __forceinline__ void records_inverse(const float* sD, float* sM, const float* sB, float (*sY)[16][17]) {
   constexpr int LC = C + 1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, g = lane >> 4;
-  if (tid < 4 * SUB) {
+  if (tid < 4 * SUB) {  // (the thread's column stays in registers until it is complete)
     const int s = (tid / SUB) * SUB, col = tid % SUB;
+    float x[SUB];
+#pragma unroll
     for (int r = 0; r < SUB; ++r) {
       float acc = 0.f;
-      for (int j = 0; j < r; ++j) acc += sD[(s + r) * LC + s + j] * sM[(s + j) * LC + s + col];
-      sM[(s + r) * LC + s + col] = (r == col ? 1.f : 0.f) - sB[s + r] * acc;
+#pragma unroll
+      for (int j = 0; j < r; ++j) acc += sD[(s + r) * LC + s + j] * x[j];
+      x[r] = (r == col ? 1.f : 0.f) - sB[s + r] * acc;
     }
+#pragma unroll
+    for (int r = 0; r < SUB; ++r) sM[(s + r) * LC + s + col] = x[r];
   }
   __syncthreads();
   for (int I = 1; I < NB; ++I) {
@@ -1533,12 +1538,16 @@ __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
   __syncthreads();
 
   // ---- C: dbeta = colsum(dMt o M) + rowsum(dT o D);  X = dMt Mt^T;  dT = -(M^T X) o strict-low
-  if (!G2)
-    for (int j = tid; j < C; j += NTG) {
-      float s = 0.f;
-      for (int i = j; i < C; ++i) s += sdT[i * LC + j] * sM[i * LC + j];
-      sdB[j] = s;
-    }
+  if (!G2) {  // (eight threads per column, rows interleaved, the sum by lane exchanges)
+    static_assert(NTG == 8 * C, "eight threads per column");
+    const int j = tid >> 3;
+    float s = 0.f;
+    for (int i = j + (tid & 7); i < C; i += 8) s += sdT[i * LC + j] * sM[i * LC + j];
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 4);
+    if ((tid & 7) == 0) sdB[j] = s;
+  }
   float* RX = sR;  // X [C][LC]
   for (int job = wave; job < 16; job += NTG / 64) {
     const int I = job / 4, J = job % 4;
@@ -1581,14 +1590,27 @@ __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
     }
   }
   __syncthreads();
-  if (!G2)
-    for (int i = tid; i < C; i += NTG) {
-      float s = 0.f;
-#pragma unroll 8
-      for (int j = 0; j < i; ++j) s += sdT[i * LC + j] * ch[L.D + i * C + j];
-      if (i < len) a.dbeta[bb + (size_t)i * a.H] = sdB[i] + s;
-      for (int j = 0; j < i; ++j) sdT[i * LC + j] *= sB[i];
-    }
+  if (!G2) {
+    // dbeta_i = sdB_i + sum_{j < i} dT_ij D_ij, then dT <- diag(beta) dT: eight threads per
+    // row, eight columns each (D's row read as two 16-byte vectors, all rows at once), the
+    // row sum by lane exchanges
+    static_assert(NTG == 8 * C, "eight threads per row");
+    const int i = tid >> 3, j0 = 8 * (tid & 7);
+    const float4 d0 = *(const float4*)(ch + L.D + i * C + j0), d1 = *(const float4*)(ch + L.D + i * C + j0 + 4);
+    const float dv8[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (j0 + e < i) s += sdT[i * LC + j0 + e] * dv8[e];
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 4);
+    if ((tid & 7) == 0 && i < len) a.dbeta[bb + (size_t)i * a.H] = sdB[i] + s;
+    const float bi = sB[i];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (j0 + e < i) sdT[i * LC + j0 + e] *= bi;
+  }
   __syncthreads();
   const float* sdD = sdT;
 
