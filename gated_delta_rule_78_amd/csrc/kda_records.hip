@@ -73,8 +73,8 @@ struct RCfg {
   static constexpr int BASE_X = 0;
   static constexpr int BASE_L = BASE_X + SZ_X;
   static constexpr int BASE_GT = BASE_L + SZ_L;          // block totals g[4][DK]
-  static constexpr int BASE_BETA = BASE_GT + NB * DK * 4;  // beta [C]
-  static constexpr int BASE_OK = BASE_BETA + C * 4;      // per-wave votes of the path choice
+  static constexpr int BASE_BETA = BASE_GT + NB * DK * 4;  // beta [2][C], by chunk parity
+  static constexpr int BASE_OK = BASE_BETA + 2 * C * 4;  // per-wave votes of the path choice
   static constexpr int LDS = BASE_OK + 16;
   static_assert(LDS <= 80 * 1024, "two workgroups per compute unit");
   // gate items: (block, channel pair); GRP items (lanes) per block
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256, G2 ? 1 : 2) void chunk_records_kernel(
   char* const R_X = smem + K::BASE_X;
   char* const R_L = smem + K::BASE_L;
   float* const GT = (float*)(smem + K::BASE_GT);
-  float* const BETA = (float*)(smem + K::BASE_BETA);
+  float* const BETA2 = (float*)(smem + K::BASE_BETA);
   int* const OKW = (int*)(smem + K::BASE_OK);
 
   const int tid = threadIdx.x;
@@ -269,7 +269,11 @@ __global__ __launch_bounds__(256, G2 ? 1 : 2) void chunk_records_kernel(
     const Geo gm = geo(chunk);
     const int t0 = gm.t0;
     char* const rec = ws + gm.rec * RL::BYTES;
-    lds_barrier();  // the previous chunk's record is out of LDS
+    // (no barrier here: every LDS region this chunk writes before its first barrier -- beta,
+    // in the buffer of this chunk's parity, and the block totals -- is one the previous
+    // chunk no longer reads; the regions its record stores read are rewritten only after
+    // that first barrier, which every wave reaches after its record stores)
+    float* const BETA = BETA2 + ((chunk - c_begin) & 1) * C;
     // lane-dependent indices, recomputed per chunk from an opaque copy of the thread
     // index: otherwise every LDS address derived from them is hoisted out of the loop
     // and held (spilled) across it
