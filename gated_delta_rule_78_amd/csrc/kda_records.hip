@@ -384,7 +384,9 @@ __global__ __launch_bounds__(256, G2 ? 1 : 2) void chunk_records_kernel(
           R::st(fq + m * K::RS_DK, qf[m][0] * f.x, qf[m][1] * f.y);
           R::st(fe + m * K::RS_DK, e0 * f.x, e1 * f.y);
         }
-        G bb{rp.x / gl.x, rp.y / gl.y};
+        // (|gamma_last| >= 2^-64 here: the hardware reciprocal, about one ulp, is ample for
+        // operands that are rounded to bf16)
+        G bb{rp.x * __builtin_amdgcn_rcpf(gl.x), rp.y * __builtin_amdgcn_rcpf(gl.y)};
 #pragma unroll
         for (int m = SUB - 1; m >= 0; --m) {
           R::st(fk + m * K::RS_DK, kf[m][0] * bb.x, kf[m][1] * bb.y);
