@@ -222,8 +222,9 @@ struct WCfg {
 };
 
 // flags of a split walk (launch_walk_split): no output stores; v read as zero; start from
-// the identity; only the last segment writes the end state, indexed by (b, h)
-enum : int { kSegNoOut = 1, kSegZeroV = 2, kSegIdentity = 4, kSegLastOnly = 8 };
+// the identity; only the last segment writes the end state, indexed by (b, h); the start
+// state indexed by (b, h) (S_0 itself); the end state written as the next segment's start
+enum : int { kSegNoOut = 1, kSegZeroV = 2, kSegIdentity = 4, kSegLastOnly = 8, kSegS0Head = 16, kSegEndNext = 32 };
 // what a walk computes (a compile-time choice: the split walk's first two passes skip the
 // work they would discard): everything; the state only (outputs neither formed nor
 // stored, no Q o gamma); the state only with v = 0 (no v tile either)
@@ -416,12 +417,18 @@ __device__ __forceinline__ void walk_chunk(const char* ops, const char* rec, cha
 
 }  // namespace
 
+// The walk of one workgroup: `bid` numbers it among the launch's workgroups of this mode;
+// ops_a ... v_b are its LDS buffers (distinct __shared__ arrays of the calling kernel).
+// Chains: the (b, h) pairs, times nsub segments seg_lo ... seg_lo + nsub - 1 of the nseg
+// segments of segc chunks each when the walk is split.
 template <int DK, int VT, bool G2, bool CPX, int MODE>
-__global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
+__device__ __forceinline__ void walk_body(
+    char* ops_a, char* ops_b, char* rec_a, char* rec_b, char* v_a, char* v_b, const int bid,
     const char* __restrict__ ws, const void* __restrict__ gq, const void* __restrict__ gk,
     const void* __restrict__ galpha, const void* __restrict__ gerase, const void* __restrict__ gv,
     const void* __restrict__ gw, const float* s0, void* __restrict__ go, float* sT, int Tlen, int H, int DV,
-    int BH, const int* __restrict__ cu, const int* __restrict__ cbase, int gmax, int nseg, int segc, int flags) {
+    int BH, const int* __restrict__ cu, const int* __restrict__ cbase, int gmax, int nseg, int segc, int flags,
+    int nsub, int seg_lo) {
   using K = WCfg<DK, VT>;
   using RL = typename K::RL;
   using R = Raw<bf16_t>;
@@ -429,14 +436,6 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
   constexpr int NW = K::NW;
   constexpr int NP = K::NP;
   constexpr int NT = K::NT;
-  // separate LDS objects per buffer, so that reads of one buffer are not ordered
-  // behind the DMA (or the operand stores) still filling the other
-  __shared__ __align__(16) char ops_a[K::OPS];
-  __shared__ __align__(16) char ops_b[K::OPS];
-  __shared__ __align__(16) char rec_a[RL::DMA];
-  __shared__ __align__(16) char rec_b[RL::DMA];
-  __shared__ __align__(16) char v_a[K::V_BYTES];
-  __shared__ __align__(16) char v_b[K::V_BYTES];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -445,12 +444,10 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
   const int g = lane >> 4;
   const int n = lane & 15;
   const int NVT = DV / VT;
-  // chains: (b, h) pairs, times nseg segments of segc chunks each when the walk is split;
   // the value tiles of one chain (or segment) read the same records and share an XCD
-  const int BHs = BH * nseg;
+  const int BHs = BH * nsub;
   int bhs, vt;
   {
-    const int bid = blockIdx.x;
     if (NVT > 1 && (BHs & 7) == 0) {
       const int r = bid >> 3;
       vt = r % NVT;
@@ -460,7 +457,7 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
       vt = bid % NVT;
     }
   }
-  const int bh = bhs / nseg, seg = bhs - bh * nseg;
+  const int bh = bhs / nsub, seg = seg_lo + (bhs - bh * nsub);
   // the sequence this workgroup walks: batch row b of length Tlen, or (packed varlen
   // batch, cu != NULL) sequence b = bh / H of length cu[b + 1] - cu[b]
   const int b = bh / H, h = bh % H;
@@ -484,7 +481,7 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
     slen = max(0, min(slen - cb * C, segc * C));
   }
   const int nchunks = (slen + C - 1) / C;
-  const size_t sidx = (size_t)bhs;  // start / end state index: (b, h), or (b, h, segment)
+  const size_t sidx = (size_t)bh * nseg + seg;  // start / end state index: (b, h), or (b, h, segment)
   constexpr bool kOut = MODE == kWalkFull;    // outputs formed and stored
   constexpr bool kV = MODE != kWalkTransfer;  // v read
   const bool zero_v = !kV || (flags & kSegZeroV) != 0, no_out = !kOut || (flags & kSegNoOut) != 0;
@@ -498,10 +495,11 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) S[r][e] = 16 * r + 4 * g + e == v0 + 16 * wave + n ? 1.f : 0.f;
   } else if (s0 && !producer) {
+    const size_t si0 = (flags & kSegS0Head) ? (size_t)bh : sidx;
 #pragma unroll
     for (int r = 0; r < DK / 16; ++r)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) S[r][e] = s0[(sidx * DK + 16 * r + 4 * g + e) * DV + v0 + 16 * wave + n];
+      for (int e = 0; e < 4; ++e) S[r][e] = s0[(si0 * DK + 16 * r + 4 * g + e) * DV + v0 + 16 * wave + n];
   }
 
   // ---- producer side: lane pt holds one gate item (4 rows x 8 channels) when pt < NITEM
@@ -903,7 +901,7 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
 
   const bool last_only = (flags & kSegLastOnly) != 0;
   if (sT && !producer && (!last_only || seg == nseg - 1)) {
-    const size_t oi = last_only ? (size_t)bh : sidx;
+    const size_t oi = last_only ? (size_t)bh : (flags & kSegEndNext) ? sidx + 1 : sidx;
 #pragma unroll
     for (int r = 0; r < DK / 16; ++r)
 #pragma unroll
@@ -911,8 +909,60 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
   }
 }
 
-// Start states of the segments of a split walk: Sst[b, h, 0] = S_0 (or zero) and
-// Sst[b, h, g + 1] = P_g Sst[b, h, g] + B_g, where B_g is segment g's end state from a zero
+#define KDA_WALK_LDS(K, RL)                              \
+  __shared__ __align__(16) char ops_a[K::OPS];           \
+  __shared__ __align__(16) char ops_b[K::OPS];           \
+  __shared__ __align__(16) char rec_a[RL::DMA];          \
+  __shared__ __align__(16) char rec_b[RL::DMA];          \
+  __shared__ __align__(16) char v_a[K::V_BYTES];         \
+  __shared__ __align__(16) char v_b[K::V_BYTES];
+
+// One walk per workgroup.  Separate LDS objects per buffer, so that reads of one buffer
+// are not ordered behind the loads (or the operand stores) still filling the other.
+template <int DK, int VT, bool G2, bool CPX, int MODE>
+__global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
+    const char* __restrict__ ws, const void* __restrict__ gq, const void* __restrict__ gk,
+    const void* __restrict__ galpha, const void* __restrict__ gerase, const void* __restrict__ gv,
+    const void* __restrict__ gw, const float* s0, void* __restrict__ go, float* sT, int Tlen, int H, int DV,
+    int BH, const int* __restrict__ cu, const int* __restrict__ cbase, int gmax, int nseg, int segc, int flags,
+    int nsub, int seg_lo) {
+  using K = WCfg<DK, VT>;
+  using RL = typename K::RL;
+  KDA_WALK_LDS(K, RL)
+  walk_body<DK, VT, G2, CPX, MODE>(ops_a, ops_b, rec_a, rec_b, v_a, v_b, blockIdx.x, ws, gq, gk, galpha, gerase, gv,
+                                   gw, s0, go, sT, Tlen, H, DV, BH, cu, cbase, gmax, nseg, segc, flags, nsub, seg_lo);
+}
+
+// The first launch of a split walk over nseg >= 2 segments (d_k = 128, 64 columns):
+// the first `nfirst` workgroups walk segment 0 in full from S_0 (outputs stored; the end
+// state is segment 1's start, written to Sst), the others walk segments 1 ... nseg - 2
+// from a zero start without outputs (their end states B_g, written to Bst).  Segment 0
+// thus needs neither an end state from zero nor a transfer, and the last segment needs
+// neither either, so the three walk launches each cover nseg - 1 segments.
+template <bool G2, bool CPX>
+__global__ __launch_bounds__((64 / 16 + 4) * 64) void chunk_walk_head_kernel(
+    const char* __restrict__ ws, const void* __restrict__ gq, const void* __restrict__ gk,
+    const void* __restrict__ galpha, const void* __restrict__ gerase, const void* __restrict__ gv,
+    const void* __restrict__ gw, const float* s0, void* __restrict__ go, float* Sst, float* Bst, int Tlen, int H,
+    int DV, int BH, int nseg, int segc, int nfirst) {
+  using K = WCfg<128, 64>;
+  using RL = typename K::RL;
+  KDA_WALK_LDS(K, RL)
+  const int bid = blockIdx.x;
+  if (bid < nfirst)
+    walk_body<128, 64, G2, CPX, kWalkFull>(ops_a, ops_b, rec_a, rec_b, v_a, v_b, bid, ws, gq, gk, galpha, gerase,
+                                           gv, gw, s0, go, Sst, Tlen, H, DV, BH, nullptr, nullptr, 0, nseg, segc,
+                                           kSegS0Head | kSegEndNext, 1, 0);
+  else
+    walk_body<128, 64, G2, CPX, kWalkState>(ops_a, ops_b, rec_a, rec_b, v_a, v_b, bid - nfirst, ws, gq, gk, galpha,
+                                            gerase, gv, gw, nullptr, go, Bst, Tlen, H, DV, BH, nullptr, nullptr, 0,
+                                            nseg, segc, kSegNoOut, nseg - 2, 1);
+}
+#undef KDA_WALK_LDS
+
+// Start states of the segments of a split walk: Sst[b, h, g + 1] = P_g Sst[b, h, g] + B_g
+// for g = g0 ... G - 2, from Sst[b, h, g0] (g0 = 1: segment 1's start, already written by
+// the walk of segment 0; g0 = 0: S_0 or zero, copied there), where B_g is segment g's end state from a zero
 // start and P_g (d_k x d_k) its end state from the identity with v = 0 -- the affine
 // transfer of a block of the SFDA page ("Principales Contribuciones", item 3), applied
 // segment by segment.  One workgroup per (b, h, 16 state columns), fp32: P_g is staged in
@@ -923,7 +973,7 @@ constexpr int kScanThreads = 512;
 template <int DK>
 __global__ __launch_bounds__(kScanThreads) void seg_scan_kernel(const float* __restrict__ s0, const float* __restrict__ P,
                                                      const float* __restrict__ Bst, float* __restrict__ Sst, int G,
-                                                     int DV) {
+                                                     int DV, int g0) {
   constexpr int LP = DK + 4;  // P rows in LDS: four rows a wave reads at once on distinct banks
   __shared__ float sP[DK * LP];
   __shared__ float sS[DK][17];
@@ -954,19 +1004,23 @@ __global__ __launch_bounds__(kScanThreads) void seg_scan_kernel(const float* __r
       *(float4*)(sP + row * LP + col) = make_float4(pf[4 * i], pf[4 * i + 1], pf[4 * i + 2], pf[4 * i + 3]);
     }
   };
-  float* out0 = Sst + (size_t)bh * G * SS;
+  float* out0 = Sst + ((size_t)bh * G + g0) * SS;
 #pragma unroll
   for (int j = 0; j < RJ; ++j) {
     const int r = r0 + NR * j;
-    const float x = s0 ? s0[((size_t)bh * DK + r) * DV + c0 + c] : 0.f;
-    sS[r][c] = x;
-    out0[(size_t)r * DV + c0 + c] = x;
+    if (g0) {
+      sS[r][c] = out0[(size_t)r * DV + c0 + c];
+    } else {
+      const float x = s0 ? s0[((size_t)bh * DK + r) * DV + c0 + c] : 0.f;
+      sS[r][c] = x;
+      out0[(size_t)r * DV + c0 + c] = x;
+    }
   }
-  if (G > 1) {
-    load_p(0);
+  if (G > g0 + 1) {
+    load_p(g0);
     store_p();
   }
-  for (int gi = 0; gi + 1 < G; ++gi) {
+  for (int gi = g0; gi + 1 < G; ++gi) {
     __syncthreads();  // sP = P_gi, sS = the start state of segment gi
     if (gi + 2 < G) load_p(gi + 1);
     const float* Bg = Bst + ((size_t)bh * G + gi) * SS;
@@ -993,40 +1047,50 @@ __global__ __launch_bounds__(kScanThreads) void seg_scan_kernel(const float* __r
 
 template <int DK, int VT, bool G2, bool CPX, int MODE = kWalkFull>
 static void walk_launch(const ChunkArgs& a, const void* ws, int nblocks, int BH, int DV, const float* s0, float* sT,
-                        int nseg, int segc, int flags) {
+                        int nseg, int segc, int flags, int nsub, int seg_lo) {
   using K = WCfg<DK, VT>;
+  if (nblocks <= 0) return;
   hipLaunchKernelGGL((chunk_walk_kernel<DK, VT, G2, CPX, MODE>), dim3(nblocks), dim3(K::NT), 0, (hipStream_t)a.stream,
                      (const char*)ws, a.q, a.k, a.alpha, a.erase, a.v, a.write, s0, a.o, sT, a.T, a.H, DV, BH, a.cu,
-                     a.ctab_base, a.gmax, nseg, segc, flags);
+                     a.ctab_base, a.gmax, nseg, segc, flags, nsub, seg_lo);
 }
 
 template <int DK, int VT, bool G2, bool CPX>
 static hipError_t launch_walk_t(const ChunkArgs& a, const void* ws) {
   // varlen: one chain per (sequence, head): BH = n_seqs * H
   const int BHc = a.cu ? a.n_seqs * a.H : a.B * a.H;
-  walk_launch<DK, VT, G2, CPX>(a, ws, BHc * (a.dv / VT), BHc, a.dv, a.s0, a.sT, 1, 0, 0);
+  walk_launch<DK, VT, G2, CPX>(a, ws, BHc * (a.dv / VT), BHc, a.dv, a.s0, a.sT, 1, 0, 0, 1, 0);
   return hipGetLastError();
 }
 
-// The split walk (fixed-length batches at d_k = 128, few (b, h) chains): four launches
-// over G segments per chain, 64 value columns per workgroup, scratch after the records:
-// B [BH G][d_k][d_v], P [BH G][d_k][d_k], segment start states [BH G][d_k][d_v].
+// The split walk (fixed-length batches at d_k = 128, few (b, h) chains, G >= 2 segments
+// per chain): four launches, 64 value columns per workgroup, scratch after the records:
+// B [BH G][d_k][d_v], P [BH G][d_k][d_k], segment start states [BH G][d_k][d_v] (index 0
+// unused).  Segment 0 starts from S_0 and the last segment's transfer is never applied, so
+// the end states and transfers are walked for segments 1 ... G - 2 only; segment 0's full
+// walk runs beside the end-state walks and writes segment 1's start.
 template <bool G2, bool CPX>
 static hipError_t launch_walk_split(const ChunkArgs& a, const void* ws, int G) {
-  const int BH = a.B * a.H, NC = (a.T + C - 1) / C, segc = (NC + G - 1) / G;
+  const int BH = a.B * a.H, NC = (a.T + C - 1) / C, segc = (NC + G - 1) / G, tv = a.dv / 64;
   const size_t rec = (size_t)BH * NC * WalkRecord<128>::BYTES;
   float* Bst = (float*)((char*)ws + rec);
   float* P = Bst + (size_t)BH * G * 128 * a.dv;
   float* Sst = P + (size_t)BH * G * 128 * 128;
-  // the end states from a zero start (outputs not stored)
-  walk_launch<128, 64, G2, CPX, kWalkState>(a, ws, BH * G * (a.dv / 64), BH, a.dv, nullptr, Bst, G, segc,
-                                            kSegNoOut);
-  // the transfers: the identity walked with v = 0 (the write gate is then irrelevant)
-  walk_launch<128, 64, G2, CPX, kWalkTransfer>(a, ws, BH * G * 2, BH, 128, nullptr, P, G, segc,
-                                               kSegNoOut | kSegZeroV | kSegIdentity);
-  hipLaunchKernelGGL(seg_scan_kernel<128>, dim3(BH * (a.dv / 16)), dim3(kScanThreads), 0, (hipStream_t)a.stream, a.s0, P,
-                     Bst, Sst, G, a.dv);
-  walk_launch<128, 64, G2, CPX>(a, ws, BH * G * (a.dv / 64), BH, a.dv, Sst, a.sT, G, segc, kSegLastOnly);
+  // segment 0 in full from S_0, and the end states of segments 1 ... G - 2 from a zero start
+  const int nfirst = BH * tv;
+  hipLaunchKernelGGL((chunk_walk_head_kernel<G2, CPX>), dim3(nfirst + BH * (G - 2) * tv), dim3(WCfg<128, 64>::NT), 0,
+                     (hipStream_t)a.stream, (const char*)ws, a.q, a.k, a.alpha, a.erase, a.v, a.write, a.s0, a.o, Sst,
+                     Bst, a.T, a.H, a.dv, BH, G, segc, nfirst);
+  if (G > 2) {
+    // the transfers of segments 1 ... G - 2: the identity walked with v = 0 (the write gate
+    // is then irrelevant)
+    walk_launch<128, 64, G2, CPX, kWalkTransfer>(a, ws, BH * (G - 2) * 2, BH, 128, nullptr, P, G, segc,
+                                                 kSegNoOut | kSegZeroV | kSegIdentity, G - 2, 1);
+    hipLaunchKernelGGL(seg_scan_kernel<128>, dim3(BH * (a.dv / 16)), dim3(kScanThreads), 0, (hipStream_t)a.stream,
+                       a.s0, P, Bst, Sst, G, a.dv, 1);
+  }
+  // segments 1 ... G - 1 from their start states (the last one writes the final state)
+  walk_launch<128, 64, G2, CPX>(a, ws, BH * (G - 1) * tv, BH, a.dv, Sst, a.sT, G, segc, kSegLastOnly, G - 1, 1);
   return hipGetLastError();
 }
 
@@ -1039,9 +1103,10 @@ static int state_seg_override() {
   return v;
 }
 
-// The split costs three walks of NC / G chunks at 64 columns per workgroup against one
-// walk of NC chunks on narrower tiles (with half the compute units idle or fewer): it is
-// taken from G = 8 segments of at least 16 chunks.
+// The split costs three walks of G - 1 segments of NC / G chunks at 64 columns per
+// workgroup against one walk of NC chunks on narrower tiles (with half the compute units
+// idle or fewer): G - 1 segments fill the compute units once per walk; the split is taken
+// from G = 8 segments of at least 16 chunks.
 int state_segments(int B, int T, int H, int dk, int dv, bool bf16) {
   if (!bf16 || dk != 128 || (dv != 64 && dv != 128)) return 1;
   const int NC = (T + C - 1) / C, o = state_seg_override();
@@ -1051,7 +1116,7 @@ int state_segments(int B, int T, int H, int dk, int dv, bool bf16) {
   }
   const long tiles = (long)B * H * (dv / 64);  // 64-column tiles of one walk per chain
   if (tiles <= 0 || tiles >= 256) return 1;
-  const int G = min((int)((256 + tiles - 1) / tiles), NC / 16);  // at least 16 chunks per segment
+  const int G = min((int)((256 + tiles - 1) / tiles) + 1, NC / 16);  // at least 16 chunks per segment
   return G >= 8 ? G : 1;
 }
 
