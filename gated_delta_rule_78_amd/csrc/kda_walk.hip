@@ -428,7 +428,7 @@ __device__ __forceinline__ void walk_body(
     const void* __restrict__ galpha, const void* __restrict__ gerase, const void* __restrict__ gv,
     const void* __restrict__ gw, const float* s0, void* __restrict__ go, float* sT, int Tlen, int H, int DV,
     int BH, const int* __restrict__ cu, const int* __restrict__ cbase, int gmax, int nseg, int segc, int flags,
-    int nsub, int seg_lo) {
+    int nsub, int seg_lo, int c0, int c1) {
   using K = WCfg<DK, VT>;
   using RL = typename K::RL;
   using R = Raw<bf16_t>;
@@ -474,11 +474,12 @@ __device__ __forceinline__ void walk_body(
     slen = Tlen;
     rec0 = ws + (size_t)bh * ((Tlen + C - 1) / C) * RL::BYTES;
   }
-  if (nseg > 1) {  // this workgroup's segment: chunks [seg segc, (seg + 1) segc)
-    const int cb = seg * segc;
+  if (nseg > 1) {  // this workgroup's segment: c0 chunks, c1 chunks, then segc chunks each
+    const int cb = seg == 0 ? 0 : seg == 1 ? c0 : c0 + c1 + (seg - 2) * segc;
+    const int cl = seg == 0 ? c0 : seg == 1 ? c1 : segc;
     rec0 += (size_t)cb * RL::BYTES;
     sbase += (size_t)cb * C;
-    slen = max(0, min(slen - cb * C, segc * C));
+    slen = max(0, min(slen - cb * C, cl * C));
   }
   const int nchunks = (slen + C - 1) / C;
   const size_t sidx = (size_t)bh * nseg + seg;  // start / end state index: (b, h), or (b, h, segment)
@@ -925,44 +926,47 @@ __global__ __launch_bounds__((VT / 16 + 4) * 64) void chunk_walk_kernel(
     const void* __restrict__ galpha, const void* __restrict__ gerase, const void* __restrict__ gv,
     const void* __restrict__ gw, const float* s0, void* __restrict__ go, float* sT, int Tlen, int H, int DV,
     int BH, const int* __restrict__ cu, const int* __restrict__ cbase, int gmax, int nseg, int segc, int flags,
-    int nsub, int seg_lo) {
+    int nsub, int seg_lo, int c0, int c1) {
   using K = WCfg<DK, VT>;
   using RL = typename K::RL;
   KDA_WALK_LDS(K, RL)
   walk_body<DK, VT, G2, CPX, MODE>(ops_a, ops_b, rec_a, rec_b, v_a, v_b, blockIdx.x, ws, gq, gk, galpha, gerase, gv,
-                                   gw, s0, go, sT, Tlen, H, DV, BH, cu, cbase, gmax, nseg, segc, flags, nsub, seg_lo);
+                                   gw, s0, go, sT, Tlen, H, DV, BH, cu, cbase, gmax, nseg, segc, flags, nsub, seg_lo,
+                                   c0, c1);
 }
 
-// The first launch of a split walk over nseg >= 2 segments (d_k = 128, 64 columns):
-// the first `nfirst` workgroups walk segment 0 in full from S_0 (outputs stored; the end
-// state is segment 1's start, written to Sst), the others walk segments 1 ... nseg - 2
-// from a zero start without outputs (their end states B_g, written to Bst).  Segment 0
-// thus needs neither an end state from zero nor a transfer, and the last segment needs
-// neither either, so the three walk launches each cover nseg - 1 segments.
-template <bool G2, bool CPX>
-__global__ __launch_bounds__((64 / 16 + 4) * 64) void chunk_walk_head_kernel(
+// A launch of a split walk over nseg segments (d_k = 128, 64 columns) that runs two walks
+// side by side: the first `nfirst` workgroups walk segment seg_first in full (outputs
+// stored) from its start state (S_0 indexed by (b, h) for segment 0, else Sst), writing
+// the end state to Sst as segment seg_first + 1's start; the others run MODE2 (end states
+// from zero, or transfers from the identity) over segments seg_lo ... seg_lo + nsub - 1,
+// writing to out2 (d_v2 columns per state).  Segments 0 and 1 are walked this way, one in
+// each of the first two launches, so neither needs an end state from zero nor a transfer.
+template <bool G2, bool CPX, int MODE2>
+__global__ __launch_bounds__((64 / 16 + 4) * 64) void chunk_walk_pair_kernel(
     const char* __restrict__ ws, const void* __restrict__ gq, const void* __restrict__ gk,
     const void* __restrict__ galpha, const void* __restrict__ gerase, const void* __restrict__ gv,
-    const void* __restrict__ gw, const float* s0, void* __restrict__ go, float* Sst, float* Bst, int Tlen, int H,
-    int DV, int BH, int nseg, int segc, int nfirst) {
+    const void* __restrict__ gw, const float* s_first, void* __restrict__ go, float* Sst, float* out2, int Tlen,
+    int H, int DV, int DV2, int BH, int nseg, int segc, int c0, int c1, int nfirst, int seg_first, int flags2,
+    int nsub, int seg_lo) {
   using K = WCfg<128, 64>;
   using RL = typename K::RL;
   KDA_WALK_LDS(K, RL)
   const int bid = blockIdx.x;
   if (bid < nfirst)
     walk_body<128, 64, G2, CPX, kWalkFull>(ops_a, ops_b, rec_a, rec_b, v_a, v_b, bid, ws, gq, gk, galpha, gerase,
-                                           gv, gw, s0, go, Sst, Tlen, H, DV, BH, nullptr, nullptr, 0, nseg, segc,
-                                           kSegS0Head | kSegEndNext, 1, 0);
+                                           gv, gw, s_first, go, Sst, Tlen, H, DV, BH, nullptr, nullptr, 0, nseg, segc,
+                                           (seg_first == 0 ? kSegS0Head : 0) | kSegEndNext, 1, seg_first, c0, c1);
   else
-    walk_body<128, 64, G2, CPX, kWalkState>(ops_a, ops_b, rec_a, rec_b, v_a, v_b, bid - nfirst, ws, gq, gk, galpha,
-                                            gerase, gv, gw, nullptr, go, Bst, Tlen, H, DV, BH, nullptr, nullptr, 0,
-                                            nseg, segc, kSegNoOut, nseg - 2, 1);
+    walk_body<128, 64, G2, CPX, MODE2>(ops_a, ops_b, rec_a, rec_b, v_a, v_b, bid - nfirst, ws, gq, gk, galpha, gerase,
+                                       gv, gw, nullptr, go, out2, Tlen, H, DV2, BH, nullptr, nullptr, 0, nseg, segc,
+                                       flags2, nsub, seg_lo, c0, c1);
 }
 #undef KDA_WALK_LDS
 
 // Start states of the segments of a split walk: Sst[b, h, g + 1] = P_g Sst[b, h, g] + B_g
-// for g = g0 ... G - 2, from Sst[b, h, g0] (g0 = 1: segment 1's start, already written by
-// the walk of segment 0; g0 = 0: S_0 or zero, copied there), where B_g is segment g's end state from a zero
+// for g = g0 ... G - 2, from Sst[b, h, g0] (g0 > 0: segment g0's start, already written by
+// the full walk of segment g0 - 1; g0 = 0: S_0 or zero, copied there), where B_g is segment g's end state from a zero
 // start and P_g (d_k x d_k) its end state from the identity with v = 0 -- the affine
 // transfer of a block of the SFDA page ("Principales Contribuciones", item 3), applied
 // segment by segment.  One workgroup per (b, h, 16 state columns), fp32: P_g is staged in
@@ -1047,12 +1051,12 @@ __global__ __launch_bounds__(kScanThreads) void seg_scan_kernel(const float* __r
 
 template <int DK, int VT, bool G2, bool CPX, int MODE = kWalkFull>
 static void walk_launch(const ChunkArgs& a, const void* ws, int nblocks, int BH, int DV, const float* s0, float* sT,
-                        int nseg, int segc, int flags, int nsub, int seg_lo) {
+                        int nseg, int segc, int flags, int nsub, int seg_lo, int c0 = 0, int c1 = 0) {
   using K = WCfg<DK, VT>;
   if (nblocks <= 0) return;
   hipLaunchKernelGGL((chunk_walk_kernel<DK, VT, G2, CPX, MODE>), dim3(nblocks), dim3(K::NT), 0, (hipStream_t)a.stream,
                      (const char*)ws, a.q, a.k, a.alpha, a.erase, a.v, a.write, s0, a.o, sT, a.T, a.H, DV, BH, a.cu,
-                     a.ctab_base, a.gmax, nseg, segc, flags, nsub, seg_lo);
+                     a.ctab_base, a.gmax, nseg, segc, flags, nsub, seg_lo, c0, c1);
 }
 
 template <int DK, int VT, bool G2, bool CPX>
@@ -1066,31 +1070,60 @@ static hipError_t launch_walk_t(const ChunkArgs& a, const void* ws) {
 // The split walk (fixed-length batches at d_k = 128, few (b, h) chains, G >= 2 segments
 // per chain): four launches, 64 value columns per workgroup, scratch after the records:
 // B [BH G][d_k][d_v], P [BH G][d_k][d_k], segment start states [BH G][d_k][d_v] (index 0
-// unused).  Segment 0 starts from S_0 and the last segment's transfer is never applied, so
-// the end states and transfers are walked for segments 1 ... G - 2 only; segment 0's full
-// walk runs beside the end-state walks and writes segment 1's start.
+// unused).  Segment 0 is walked in full from S_0 beside the end states of segments
+// 2 ... G - 2, segment 1 in full from the start that gives beside their transfers; the
+// scan then forms the starts of segments 3 ... G - 1 (the last segment's end state and
+// transfer are never needed), and the last launch walks segments 2 ... G - 1 in full.
+// Segment lengths of a split walk over NC chunks: segments 0 and 1 take c0 and c1 chunks,
+// the others segc each (the last one what remains).  From G = 4 on, segment 0's full walk
+// shares a launch with end-state walks and segment 1's with transfer walks, which take
+// about 0.79 and 0.65 of a full walk's time per chunk (2.96 and 2.43 against 3.75 us per
+// chunk at B1 H16 T128K), so segments 0 and 1 get 51/64 and 42/64 of segc and the
+// workgroups of each launch end together.
+static void split_lengths(int NC, int G, int& segc, int& c0, int& c1) {
+  if (G <= 3) {
+    segc = c0 = c1 = (NC + G - 1) / G;
+    return;
+  }
+  segc = max(1, (int)((long)NC * 64 / ((long)(G - 2) * 64 + 51 + 42)));
+  for (;; ++segc) {
+    c0 = segc * 51 / 64;
+    c1 = segc * 42 / 64;
+    if (c0 + c1 + (long)(G - 2) * segc >= NC) break;
+  }
+}
+
 template <bool G2, bool CPX>
 static hipError_t launch_walk_split(const ChunkArgs& a, const void* ws, int G) {
-  const int BH = a.B * a.H, NC = (a.T + C - 1) / C, segc = (NC + G - 1) / G, tv = a.dv / 64;
+  const int BH = a.B * a.H, NC = (a.T + C - 1) / C, tv = a.dv / 64;
+  int segc, c0, c1;
+  split_lengths(NC, G, segc, c0, c1);
   const size_t rec = (size_t)BH * NC * WalkRecord<128>::BYTES;
   float* Bst = (float*)((char*)ws + rec);
   float* P = Bst + (size_t)BH * G * 128 * a.dv;
   float* Sst = P + (size_t)BH * G * 128 * 128;
-  // segment 0 in full from S_0, and the end states of segments 1 ... G - 2 from a zero start
-  const int nfirst = BH * tv;
-  hipLaunchKernelGGL((chunk_walk_head_kernel<G2, CPX>), dim3(nfirst + BH * (G - 2) * tv), dim3(WCfg<128, 64>::NT), 0,
-                     (hipStream_t)a.stream, (const char*)ws, a.q, a.k, a.alpha, a.erase, a.v, a.write, a.s0, a.o, Sst,
-                     Bst, a.T, a.H, a.dv, BH, G, segc, nfirst);
+  const hipStream_t st = (hipStream_t)a.stream;
+  const int nfirst = BH * tv, nmid = G > 3 ? G - 3 : 0;  // segments 2 ... G - 2
+  // segment 0 in full; the end states of segments 2 ... G - 2 from a zero start
+  hipLaunchKernelGGL((chunk_walk_pair_kernel<G2, CPX, kWalkState>), dim3(nfirst + BH * nmid * tv),
+                     dim3(WCfg<128, 64>::NT), 0, st, (const char*)ws, a.q, a.k, a.alpha, a.erase, a.v, a.write, a.s0,
+                     a.o, Sst, Bst, a.T, a.H, a.dv, a.dv, BH, G, segc, c0, c1, nfirst, 0, kSegNoOut, nmid, 2);
   if (G > 2) {
-    // the transfers of segments 1 ... G - 2: the identity walked with v = 0 (the write gate
-    // is then irrelevant)
-    walk_launch<128, 64, G2, CPX, kWalkTransfer>(a, ws, BH * (G - 2) * 2, BH, 128, nullptr, P, G, segc,
-                                                 kSegNoOut | kSegZeroV | kSegIdentity, G - 2, 1);
-    hipLaunchKernelGGL(seg_scan_kernel<128>, dim3(BH * (a.dv / 16)), dim3(kScanThreads), 0, (hipStream_t)a.stream,
-                       a.s0, P, Bst, Sst, G, a.dv, 1);
+    // segment 1 in full; the transfers of segments 2 ... G - 2: the identity walked with
+    // v = 0 (the write gate is then irrelevant)
+    hipLaunchKernelGGL((chunk_walk_pair_kernel<G2, CPX, kWalkTransfer>), dim3(nfirst + BH * nmid * 2),
+                       dim3(WCfg<128, 64>::NT), 0, st, (const char*)ws, a.q, a.k, a.alpha, a.erase, a.v, a.write, Sst,
+                       a.o, Sst, P, a.T, a.H, a.dv, 128, BH, G, segc, c0, c1, nfirst, 1,
+                       kSegNoOut | kSegZeroV | kSegIdentity, nmid, 2);
   }
-  // segments 1 ... G - 1 from their start states (the last one writes the final state)
-  walk_launch<128, 64, G2, CPX>(a, ws, BH * (G - 1) * tv, BH, a.dv, Sst, a.sT, G, segc, kSegLastOnly, G - 1, 1);
+  if (nmid > 0)
+    hipLaunchKernelGGL(seg_scan_kernel<128>, dim3(BH * (a.dv / 16)), dim3(kScanThreads), 0, st, a.s0, P, Bst, Sst, G,
+                       a.dv, 2);
+  // segments 2 ... G - 1 from their start states (the last one writes the final state);
+  // with G = 2, segment 1
+  const int lo = G > 2 ? 2 : 1;
+  walk_launch<128, 64, G2, CPX>(a, ws, BH * (G - lo) * tv, BH, a.dv, Sst, a.sT, G, segc, kSegLastOnly, G - lo, lo,
+                                c0, c1);
   return hipGetLastError();
 }
 
@@ -1103,10 +1136,10 @@ static int state_seg_override() {
   return v;
 }
 
-// The split costs three walks of G - 1 segments of NC / G chunks at 64 columns per
-// workgroup against one walk of NC chunks on narrower tiles (with half the compute units
-// idle or fewer): G - 1 segments fill the compute units once per walk; the split is taken
-// from G = 8 segments of at least 16 chunks.
+// The split costs three launches of G - 2 segments' walks of NC / G chunks at 64 columns
+// per workgroup against one walk of NC chunks on narrower tiles (with half the compute
+// units idle or fewer): G - 2 segments fill the compute units once per launch; the split
+// is taken from G = 8 segments of at least 16 chunks.
 int state_segments(int B, int T, int H, int dk, int dv, bool bf16) {
   if (!bf16 || dk != 128 || (dv != 64 && dv != 128)) return 1;
   const int NC = (T + C - 1) / C, o = state_seg_override();
@@ -1116,7 +1149,7 @@ int state_segments(int B, int T, int H, int dk, int dv, bool bf16) {
   }
   const long tiles = (long)B * H * (dv / 64);  // 64-column tiles of one walk per chain
   if (tiles <= 0 || tiles >= 256) return 1;
-  const int G = min((int)((256 + tiles - 1) / tiles) + 1, NC / 16);  // at least 16 chunks per segment
+  const int G = min((int)((256 + tiles - 1) / tiles) + 2, NC / 16);  // at least 16 chunks per segment
   return G >= 8 ? G : 1;
 }
 
