@@ -45,6 +45,11 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m gated_delta_rule_78_amd.build` "
                                "(there is no CPU fallback)")
+        # torch first: it carries its own HIP runtime, and libkda.so must bind to that
+        # one.  Loaded before torch, the library would pull in the system runtime and
+        # torch's the second one, and a launch on a torch stream then fails in the
+        # library's runtime.
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         P = ctypes.c_void_p
         SP = ctypes.POINTER(Shape)
