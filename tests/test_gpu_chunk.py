@@ -369,9 +369,10 @@ def test_orthogonal_regime_64k():
 @pytest.mark.parametrize("dv,zero_s0,in_place", [(128, False, False), (64, False, True), (128, True, False)])
 def test_split_state_walk(dv, zero_s0, in_place):
     """Few (b, h) chains over a long sequence: the state pass splits each chain into
-    segments (B1 H2 T8325: 8 segments, seven of 17 chunks and one of 12), walks them from
-    zero and from the identity, scans the segment start states and walks them again; every
-    output and the final state against the oracle, all heads."""
+    segments (B1 H2 T8325: 8 segments of 14, 11, then 18 chunks, the last of 16), walks
+    segments 0 and 1 in full beside the end states from zero and the transfers from the
+    identity of segments 2-6, scans the segment start states and walks segments 2-7 again;
+    every output and the final state against the oracle, all heads."""
     import gated_delta_rule_78_amd as kda
     from gated_delta_rule_78_amd import lib
     import ctypes
