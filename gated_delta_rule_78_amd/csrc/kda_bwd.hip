@@ -752,19 +752,66 @@ __global__ __launch_bounds__(DK == 128 ? NTG : NT) void bwd_records_cpx_kernel(B
 // states B_g), from the identity with the inputs read as zero (the d_k x d_k transfers
 // P_g, cols = d_k), then, after a scan of the segment start states, from those start
 // states with the per-chunk writes.  nseg = 1 is the plain walk.
+// A launch covers segments seg_lo ... seg_lo + nsub - 1.  Segment lengths: c0, c1, then
+// segc each (the last one what remains), counted from the sequence's start, or (mirror)
+// from its end, so that the two short segments are the last two.
 struct WalkSplit {
   int nseg = 1, segc = 0, cols = 0, flags = 0;
   const float* start = nullptr;  // [chains nseg][d_k][cols], NULL: zero (nseg > 1)
   float* end = nullptr;          // [chains nseg][d_k][cols], or NULL
+  int nsub = 1, seg_lo = 0, c0 = 0, c1 = 0, mirror = 0;
 };
-enum : int { kWNoWrite = 1, kWZeroIn = 2, kWIdentity = 4 };
+// no per-chunk writes; inputs read as zero; start from the identity; start from the
+// chain's own start (S_0, or dS_T for the adjoint walk) instead of `start`; end state
+// written as the start of the next (kWEndNext) or previous (kWEndPrev) segment
+enum : int { kWNoWrite = 1, kWZeroIn = 2, kWIdentity = 4, kWHead = 8, kWEndNext = 16, kWEndPrev = 32 };
+
+// the descriptor of this workgroup's walk, picked field by field (a select of the whole
+// struct is kept in scratch memory)
+__device__ __forceinline__ WalkSplit pick_split(const WalkSplit& x, const WalkSplit& y, bool second) {
+  WalkSplit w;
+  w.nseg = second ? y.nseg : x.nseg;
+  w.segc = second ? y.segc : x.segc;
+  w.cols = second ? y.cols : x.cols;
+  w.flags = second ? y.flags : x.flags;
+  w.start = second ? y.start : x.start;
+  w.end = second ? y.end : x.end;
+  w.nsub = second ? y.nsub : x.nsub;
+  w.seg_lo = second ? y.seg_lo : x.seg_lo;
+  w.c0 = second ? y.c0 : x.c0;
+  w.c1 = second ? y.c1 : x.c1;
+  w.mirror = second ? y.mirror : x.mirror;
+  return w;
+}
+
+// chunks [c0, c0 + nch) of segment `seg` of a chain of nall chunks
+__device__ __forceinline__ void walk_seg_range(const WalkSplit& sp, int seg, int nall, int& c0, int& nch) {
+  const int g = sp.mirror ? sp.nseg - 1 - seg : seg;
+  const int st = g == 0 ? 0 : g == 1 ? sp.c0 : sp.c0 + sp.c1 + (g - 2) * sp.segc;
+  const int ln = g == 0 ? sp.c0 : g == 1 ? sp.c1 : sp.segc;
+  if (!sp.mirror) {
+    c0 = st;
+    nch = max(0, min(ln, nall - st));
+  } else {
+    const int hi = max(0, nall - st), lo = max(0, nall - st - ln);
+    c0 = lo;
+    nch = hi - lo;
+  }
+}
 
 // bwd_state_kernel: chunks in order; writes the chunk-start state S_n and Delta_n.  The
 // next chunk's operands are loaded into registers while the current one computes.
 // CPX: SFDA complex gates -- gamma_L multiplies the state's row pairs (2p, 2p+1), which
 // are registers r, r + 1 (r even) of one lane.
-template <typename T, int DK, bool G2, bool CPX>
-__global__ __launch_bounds__(NTW) void bwd_state_kernel(BwdArgs a, int NC, WalkSplit sp) {
+template <typename T, int DK, bool G2, bool CPX, int WMODE = 0>
+__global__ __launch_bounds__(NTW) void bwd_state_kernel(BwdArgs a, int NC, WalkSplit sp0, WalkSplit sp1,
+                                                        int nfirst) {
+  // WMODE 0: one walk per chain (the descriptors are ignored, none of the split logic is
+  // compiled); 1: one segment walk per workgroup (sp0); 2: a paired launch, workgroups from
+  // nfirst on run the second walk (sp1).  The plain walk keeps its registers.
+  const bool second = WMODE == 2 && (int)blockIdx.x >= nfirst;
+  const WalkSplit sp = WMODE == 2 ? pick_split(sp0, sp1, second) : WMODE == 1 ? sp0 : WalkSplit{};
+  const int bid = second ? (int)blockIdx.x - nfirst : (int)blockIdx.x;
   constexpr int LM = C + 4, LW = DK + 4, LV = VTW + 4;
   constexpr int NM = C * C / 4 / NTW, NW = C * DK / 4 / NTW, NV = C * VTW / 4 / NTW;
   constexpr int NH = DK / 32;  // state row blocks per wave: two waves share 16 columns
@@ -774,10 +821,12 @@ __global__ __launch_bounds__(NTW) void bwd_state_kernel(BwdArgs a, int NC, WalkS
   const int cw = wave & 3, hh = wave >> 2;  // column slice; half of the state rows (blocks hh NH ..)
   const bool split = sp.nseg > 1;
   const int dv = a.Dv, cols = split ? sp.cols : dv, ntile = cols / VTW;
-  const int cs = blockIdx.x / ntile, v0 = (blockIdx.x % ntile) * VTW;  // cs: chain (and segment)
-  const int bh = cs / sp.nseg, seg = cs % sp.nseg;  // bh: the chain (b H + h, or sequence H + h)
-  const int c0 = seg * sp.segc, nall = chain_chunks(a, NC, bh);
-  const int nch = split ? max(0, min(sp.segc, nall - c0)) : nall;
+  const int cl = bid / ntile, v0 = (bid % ntile) * VTW;  // cl: chain (and segment) of this launch
+  const int bh = cl / sp.nsub, seg = sp.seg_lo + cl % sp.nsub;  // bh: the chain (b H + h, or sequence H + h)
+  const int cs = bh * sp.nseg + seg;  // index of the segment's start and end states
+  const int nall = chain_chunks(a, NC, bh);
+  int c0 = 0, nch = nall;
+  if (split) walk_seg_range(sp, seg, nall, c0, nch);
   const bool zero_in = sp.flags & kWZeroIn, no_write = sp.flags & kWNoWrite;
   const int col = v0 + 16 * cw + n;  // this lane's state column
   const BwdLayout L(DK, dv);
@@ -789,7 +838,7 @@ __global__ __launch_bounds__(NTW) void bwd_state_kernel(BwdArgs a, int NC, WalkS
       const int row = 16 * (hh * NH + I) + 4 * g + r;
       if (sp.flags & kWIdentity)
         S[I][r] = row == col ? 1.f : 0.f;
-      else if (split)
+      else if (split && !(sp.flags & kWHead))
         S[I][r] = sp.start ? sp.start[((size_t)cs * DK + row) * cols + col] : 0.f;
       else
         S[I][r] = a.s0 ? a.s0[((size_t)bh * DK + row) * dv + col] : 0.f;
@@ -970,10 +1019,11 @@ __global__ __launch_bounds__(NTW) void bwd_state_kernel(BwdArgs a, int NC, WalkS
     }
   }
   if (sp.end) {
+    const int ce = cs + ((sp.flags & kWEndNext) ? 1 : (sp.flags & kWEndPrev) ? -1 : 0);
 #pragma unroll
     for (int I = 0; I < NH; ++I)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sp.end[((size_t)cs * DK + 16 * (hh * NH + I) + 4 * g + r) * cols + col] = S[I][r];
+      for (int r = 0; r < 4; ++r) sp.end[((size_t)ce * DK + 16 * (hh * NH + I) + 4 * g + r) * cols + col] = S[I][r];
   }
 }
 
@@ -983,17 +1033,24 @@ __global__ __launch_bounds__(NTW) void bwd_state_kernel(BwdArgs a, int NC, WalkS
 // CPX: SFDA complex gates -- the transpose of the chunk-end rotation-decay is conj(gamma_L)
 // on the row pairs.
 template <typename T, int DK, bool CPX>
-__global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC, WalkSplit sp) {
+__global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC, WalkSplit sp0, WalkSplit sp1,
+                                                         int nfirst) {
+  // workgroups from nfirst on run the second walk of a paired launch
+  const bool second = (int)blockIdx.x >= nfirst;
+  const WalkSplit sp = pick_split(sp0, sp1, second);
+  const int bid = second ? (int)blockIdx.x - nfirst : (int)blockIdx.x;
   constexpr int LK = DK + 4, LM = C + 4, LV = VTW + 4;
   constexpr int NM = C * C / 4 / NT, NW = C * DK / 4 / NT, NV = C * VTW / 4 / NT;
   __shared__ __attribute__((aligned(16))) float sKr[C * LK], sAT[C * LM], sQgT[DK * LM], sWT[DK * LM], sO[C * LV], sGl[DK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, g = lane >> 4;
   const bool split = sp.nseg > 1;
   const int dv = a.Dv, cols = split ? sp.cols : dv, ntile = cols / VTW;
-  const int cs = blockIdx.x / ntile, v0 = (blockIdx.x % ntile) * VTW;  // cs: chain (and segment)
-  const int bh = cs / sp.nseg, seg = cs % sp.nseg;  // bh: the chain (b H + h, or sequence H + h)
-  const int c0 = seg * sp.segc, nall = chain_chunks(a, NC, bh);
-  const int nch = split ? max(0, min(sp.segc, nall - c0)) : nall;  // chunks c0 .. c0 + nch - 1, in reverse
+  const int cl = bid / ntile, v0 = (bid % ntile) * VTW;  // cl: chain (and segment) of this launch
+  const int bh = cl / sp.nsub, seg = sp.seg_lo + cl % sp.nsub;  // bh: the chain (b H + h, or sequence H + h)
+  const int cs = bh * sp.nseg + seg;  // index of the segment's start and end adjoints
+  const int nall = chain_chunks(a, NC, bh);
+  int c0 = 0, nch = nall;  // chunks c0 .. c0 + nch - 1, in reverse
+  if (split) walk_seg_range(sp, seg, nall, c0, nch);
   const bool zero_in = sp.flags & kWZeroIn, no_write = sp.flags & kWNoWrite;
   const int col = v0 + 16 * wave + n;
   const BwdLayout L(DK, dv);
@@ -1005,7 +1062,7 @@ __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC, Walk
       const int row = 16 * I + 4 * g + r;
       if (sp.flags & kWIdentity)
         dS[I][r] = row == col ? 1.f : 0.f;
-      else if (split)
+      else if (split && !(sp.flags & kWHead))
         dS[I][r] = sp.start ? sp.start[((size_t)cs * DK + row) * cols + col] : 0.f;
       else
         dS[I][r] = a.dsT ? a.dsT[((size_t)bh * DK + row) * dv + col] : 0.f;
@@ -1169,10 +1226,11 @@ __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC, Walk
     }
   }
   if (sp.end) {
+    const int ce = cs + ((sp.flags & kWEndNext) ? 1 : (sp.flags & kWEndPrev) ? -1 : 0);
 #pragma unroll
     for (int I = 0; I < DK / 16; ++I)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sp.end[((size_t)cs * DK + 16 * I + 4 * g + r) * cols + col] = dS[I][r];
+      for (int r = 0; r < 4; ++r) sp.end[((size_t)ce * DK + 16 * I + 4 * g + r) * cols + col] = dS[I][r];
   } else if (a.ds0 && seg == 0) {  // the chain's first segment ends at S_0
 #pragma unroll
     for (int I = 0; I < DK / 16; ++I)
@@ -1184,25 +1242,33 @@ __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC, Walk
 // Segment start states of a split walk, fp32, one workgroup per (chain, 16 columns):
 // forward (the state walk) X_0 = init, X_(g+1) = P_g X_g + B_g; reverse (the adjoint walk,
 // whose segments run backwards) X_(G-1) = init, X_(g-1) = P_g X_g + B_g.  init may be NULL.
+// g_first >= 0: the scan starts from X_(g_first), already written (by the full walk of the
+// segment before it).
 template <int DK>
 __global__ __launch_bounds__(256) void walk_scan_kernel(const float* __restrict__ init, const float* __restrict__ P,
                                                       const float* __restrict__ Bst, float* __restrict__ X, int G,
-                                                      int dv, int reverse) {
+                                                      int dv, int reverse, int g_first) {
   __shared__ float sX[DK][17];
   const int nsl = dv / 16, ch = blockIdx.x / nsl, c0 = (blockIdx.x % nsl) * 16;
   const int tid = threadIdx.x, c = tid & 15, r0 = tid >> 4;
   constexpr int RJ = DK / 16;
   const size_t SS = (size_t)DK * dv;
-  const int g0 = reverse ? G - 1 : 0;
+  const int g0 = g_first >= 0 ? g_first : reverse ? G - 1 : 0;
 #pragma unroll
   for (int j = 0; j < RJ; ++j) {
     const int r = r0 + 16 * j;
-    const float x = init ? init[((size_t)ch * DK + r) * dv + c0 + c] : 0.f;
-    sX[r][c] = x;
-    X[((size_t)ch * G + g0) * SS + (size_t)r * dv + c0 + c] = x;
+    float* xg = X + ((size_t)ch * G + g0) * SS + (size_t)r * dv + c0 + c;
+    if (g_first >= 0) {
+      sX[r][c] = *xg;
+    } else {
+      const float x = init ? init[((size_t)ch * DK + r) * dv + c0 + c] : 0.f;
+      sX[r][c] = x;
+      *xg = x;
+    }
   }
-  for (int step = 0; step + 1 < G; ++step) {
-    const int gi = reverse ? G - 1 - step : step, gn = reverse ? gi - 1 : gi + 1;
+  const int nsteps = reverse ? g0 : G - 1 - g0;
+  for (int step = 0; step < nsteps; ++step) {
+    const int gi = reverse ? g0 - step : g0 + step, gn = reverse ? gi - 1 : gi + 1;
     __syncthreads();
     const float* Pg = P + ((size_t)ch * G + gi) * DK * DK;
     const float* Bg = Bst + ((size_t)ch * G + gi) * SS;
@@ -1977,6 +2043,22 @@ __global__ __launch_bounds__(NTG) void bwd_grads_kernel(BwdArgs a, int NC) {
 }
 
 // ---------------------------------------------------------------------------------------
+// Segment lengths of the split walks over NC chunks: c0, c1, then segc each (the last one
+// what remains), as in the forward's split walk: from G = 4 on, the two short segments are
+// walked in full beside the end-state and the transfer walks of the middle segments.
+static void bwd_split_lengths(int NC, int G, int& segc, int& c0, int& c1) {
+  if (G < 4) {
+    segc = c0 = c1 = (NC + G - 1) / G;
+    return;
+  }
+  segc = max(1, (int)((long)NC * 64 / ((long)(G - 2) * 64 + 51 + 42)));
+  for (;; ++segc) {
+    c0 = segc * 51 / 64;
+    c1 = segc * 42 / 64;
+    if (c0 + c1 + (long)(G - 2) * segc >= NC) break;
+  }
+}
+
 template <typename T, int DK, bool G2, bool CPX>
 static hipError_t launch_bwd_dk(const BwdArgs& a, int NC) {
   // per-chunk grid: B H NC (fixed) or H gmax (packed; workgroups past the chunk count
@@ -1992,26 +2074,80 @@ static hipError_t launch_bwd_dk(const BwdArgs& a, int NC) {
   }
   const int G = a.ctab ? 1 : bwd_walk_segments(a.B, a.T, a.H, a.Dk, a.Dv);
   if (G < 2) {
-    if (per_chunk > 0) hipLaunchKernelGGL((bwd_state_kernel<T, DK, G2, CPX>), dim3(walks), dim3(NTW), 0, st, a, NC, WalkSplit{});
-    hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX>), dim3(walks), dim3(NT), 0, st, a, NC, WalkSplit{});
+    if (per_chunk > 0)
+      hipLaunchKernelGGL((bwd_state_kernel<T, DK, G2, CPX>), dim3(walks), dim3(NTW), 0, st, a, NC, WalkSplit{},
+                         WalkSplit{}, 1 << 30);
+    hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX>), dim3(walks), dim3(NT), 0, st, a, NC, WalkSplit{}, WalkSplit{},
+                       1 << 30);
   } else {
     // split walks: scratch after the chunk blocks; B [chains G][d_k][d_v], P [chains G][d_k][d_k],
     // start states [chains G][d_k][d_v], used by the state walk and then by the adjoint walk
     float* Bst = a.ws + (size_t)chains * NC * BwdLayout(DK, a.Dv).total;
     float* P = Bst + (size_t)chains * G * DK * a.Dv;
     float* X = P + (size_t)chains * G * DK * DK;
-    const int segc = (NC + G - 1) / G, wv = chains * G * (a.Dv / VTW), wk = chains * G * (DK / VTW);
-    const WalkSplit wb{G, segc, a.Dv, kWNoWrite, nullptr, Bst};
-    const WalkSplit wp{G, segc, DK, kWNoWrite | kWZeroIn | kWIdentity, nullptr, P};
-    const WalkSplit wf{G, segc, a.Dv, 0, X, nullptr};
-    hipLaunchKernelGGL((bwd_state_kernel<T, DK, G2, CPX>), dim3(wv), dim3(NTW), 0, st, a, NC, wb);
-    hipLaunchKernelGGL((bwd_state_kernel<T, DK, G2, CPX>), dim3(wk), dim3(NTW), 0, st, a, NC, wp);
-    hipLaunchKernelGGL(walk_scan_kernel<DK>, dim3(chains * (a.Dv / 16)), dim3(256), 0, st, a.s0, P, Bst, X, G, a.Dv, 0);
-    hipLaunchKernelGGL((bwd_state_kernel<T, DK, G2, CPX>), dim3(wv), dim3(NTW), 0, st, a, NC, wf);
-    hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX>), dim3(wv), dim3(NT), 0, st, a, NC, wb);
-    hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX>), dim3(wk), dim3(NT), 0, st, a, NC, wp);
-    hipLaunchKernelGGL(walk_scan_kernel<DK>, dim3(chains * (a.Dv / 16)), dim3(256), 0, st, a.dsT, P, Bst, X, G, a.Dv, 1);
-    hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX>), dim3(wv), dim3(NT), 0, st, a, NC, wf);
+    int segc, sc0, sc1;
+    bwd_split_lengths(NC, G, segc, sc0, sc1);
+    auto wsp = [&](int nsub, int seg_lo, int cols, int flags, const float* start, float* end, int mirror) {
+      WalkSplit w;
+      w.nseg = G;
+      w.segc = segc;
+      w.cols = cols;
+      w.flags = flags;
+      w.start = start;
+      w.end = end;
+      w.nsub = nsub;
+      w.seg_lo = seg_lo;
+      w.c0 = sc0;
+      w.c1 = sc1;
+      w.mirror = mirror;
+      return w;
+    };
+    const int tv = a.Dv / VTW, tk = DK / VTW, all = 1 << 30;
+    const WalkSplit none;
+    if (G < 4) {  // every segment through the end-state and transfer walks, equal lengths
+      const int wv = chains * G * tv, wk = chains * G * tk;
+      const WalkSplit wb = wsp(G, 0, a.Dv, kWNoWrite, nullptr, Bst, 0);
+      const WalkSplit wp = wsp(G, 0, DK, kWNoWrite | kWZeroIn | kWIdentity, nullptr, P, 0);
+      const WalkSplit wf = wsp(G, 0, a.Dv, 0, X, nullptr, 0);
+      hipLaunchKernelGGL((bwd_state_kernel<T, DK, G2, CPX, 1>), dim3(wv), dim3(NTW), 0, st, a, NC, wb, none, all);
+      hipLaunchKernelGGL((bwd_state_kernel<T, DK, G2, CPX, 1>), dim3(wk), dim3(NTW), 0, st, a, NC, wp, none, all);
+      hipLaunchKernelGGL(walk_scan_kernel<DK>, dim3(chains * (a.Dv / 16)), dim3(256), 0, st, a.s0, P, Bst, X, G, a.Dv, 0,
+                         -1);
+      hipLaunchKernelGGL((bwd_state_kernel<T, DK, G2, CPX, 1>), dim3(wv), dim3(NTW), 0, st, a, NC, wf, none, all);
+      hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX>), dim3(wv), dim3(NT), 0, st, a, NC, wb, none, all);
+      hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX>), dim3(wk), dim3(NT), 0, st, a, NC, wp, none, all);
+      hipLaunchKernelGGL(walk_scan_kernel<DK>, dim3(chains * (a.Dv / 16)), dim3(256), 0, st, a.dsT, P, Bst, X, G, a.Dv,
+                         1, -1);
+      hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX>), dim3(wv), dim3(NT), 0, st, a, NC, wf, none, all);
+    } else {
+      // The state walk: segment 0 in full from S_0 beside the end states of segments
+      // 2 ... G - 2 from zero, segment 1 in full beside their transfers, the scan of the
+      // starts of segments 3 ... G - 1, then segments 2 ... G - 1 in full.  The adjoint
+      // walk runs the mirror image: segments G - 1 and G - 2 (the two short ones at the
+      // sequence's end) in full from dS_T, the middle ones through end states and
+      // transfers, the reverse scan, then segments G - 3 ... 0 in full.
+      const int nmid = G - 3, nf = chains * tv;
+      hipLaunchKernelGGL((bwd_state_kernel<T, DK, G2, CPX, 2>), dim3(nf + chains * nmid * tv), dim3(NTW), 0, st, a, NC,
+                         wsp(1, 0, a.Dv, kWHead | kWEndNext, nullptr, X, 0),
+                         wsp(nmid, 2, a.Dv, kWNoWrite, nullptr, Bst, 0), nf);
+      hipLaunchKernelGGL((bwd_state_kernel<T, DK, G2, CPX, 2>), dim3(nf + chains * nmid * tk), dim3(NTW), 0, st, a, NC,
+                         wsp(1, 1, a.Dv, kWEndNext, X, X, 0),
+                         wsp(nmid, 2, DK, kWNoWrite | kWZeroIn | kWIdentity, nullptr, P, 0), nf);
+      hipLaunchKernelGGL(walk_scan_kernel<DK>, dim3(chains * (a.Dv / 16)), dim3(256), 0, st, a.s0, P, Bst, X, G, a.Dv, 0,
+                         2);
+      hipLaunchKernelGGL((bwd_state_kernel<T, DK, G2, CPX, 1>), dim3(chains * (G - 2) * tv), dim3(NTW), 0, st, a, NC,
+                         wsp(G - 2, 2, a.Dv, 0, X, nullptr, 0), none, all);
+      hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX>), dim3(nf + chains * nmid * tv), dim3(NT), 0, st, a, NC,
+                         wsp(1, G - 1, a.Dv, kWHead | kWEndPrev, nullptr, X, 1),
+                         wsp(nmid, 1, a.Dv, kWNoWrite, nullptr, Bst, 1), nf);
+      hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX>), dim3(nf + chains * nmid * tk), dim3(NT), 0, st, a, NC,
+                         wsp(1, G - 2, a.Dv, kWEndPrev, X, X, 1),
+                         wsp(nmid, 1, DK, kWNoWrite | kWZeroIn | kWIdentity, nullptr, P, 1), nf);
+      hipLaunchKernelGGL(walk_scan_kernel<DK>, dim3(chains * (a.Dv / 16)), dim3(256), 0, st, a.dsT, P, Bst, X, G, a.Dv,
+                         1, G - 3);
+      hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX>), dim3(chains * (G - 2) * tv), dim3(NT), 0, st, a, NC,
+                         wsp(G - 2, 0, a.Dv, 0, X, nullptr, 1), none, all);
+    }
   }
   if (per_chunk > 0) {
     BwdArgs ag = a;
@@ -2036,8 +2172,9 @@ static hipError_t launch_bwd_t(const BwdArgs& a, int NC) {
 
 // Segments per chain of the split walks (1: one walk per chain): taken, as in the forward's
 // state pass, when fewer than 256 walk tiles of 64 columns would run and at least 8
-// segments of 16 or more chunks fit (three walks of NC / G chunks on 256 workgroups beat one
-// walk of NC chunks on few).  KDA_BWD_SEG=0 keeps one walk, =G forces G segments.
+// segments of 16 or more chunks fit (three launches of G - 2 segments each on 256
+// workgroups beat one walk of NC chunks on few).  KDA_BWD_SEG=0 keeps one walk, =G forces
+// G segments.
 int bwd_walk_segments(int B, int T, int H, int dk, int dv) {
   static const int o = [] {
     const char* e = getenv("KDA_BWD_SEG");
@@ -2050,7 +2187,7 @@ int bwd_walk_segments(int B, int T, int H, int dk, int dv) {
   }
   const long tiles = (long)B * H * (dv / VTW);
   if (tiles <= 0 || tiles >= 256) return 1;
-  const int G = min((int)((256 + tiles - 1) / tiles), NC / 16);
+  const int G = min((int)((256 + tiles - 1) / tiles) + 2, NC / 16);
   return G >= 8 ? G : 1;
 }
 
