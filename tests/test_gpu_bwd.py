@@ -174,7 +174,7 @@ def test_bwd_varlen_single_sequence_equals_fixed():
 
 def _split_inputs(gates, seed, long_memory=False):
     from gated_delta_rule_78_amd.inputs import bf16_bits
-    T = 64 * 130 + 5   # B1 H2: 8 segments per chain (seven of 17 chunks, one of 12)
+    T = 64 * 130 + 5   # B1 H2: 8 segments per chain (14, 11, then 18 chunks, the last of 16)
     inp = make(1, T, 2, 128, 128, "bf16", gates, False, seed=seed)
     dO, dST = make_upstream(1, T, 2, 128, 128, "bf16", seed=seed)
     S0 = inp.S0

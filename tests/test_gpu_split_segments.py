@@ -1,4 +1,4 @@
-"""The forward's split state walk at forced segment counts, against the fp64 oracle (gpu).
+"""The split walks at forced segment counts, against the fp64 oracle (gpu).
 
 The library takes the split from 8 segments on; KDA_STATE_SEG forces G segments for
 tuning, which reaches the degenerate launch layouts: G = 2 (segment 0 walked in full, then
@@ -7,7 +7,10 @@ transfer walks, no scan), G = 4 and 5 (one and two middle segments through the e
 and transfer walks and the scan).  The setting is read once per process, so each count
 runs in a child process of its own (one at a time).  Inputs follow the long-memory recipe
 (gates in {1, 1 - 2^-8}, beta <= 0.05, S0 ~ N(0, 1)), where the start state carries into
-every output, so a wrong segment start shows at O(1).
+every output, so a wrong segment start shows at O(1).  The backward's state and adjoint
+walks (KDA_BWD_SEG) take the same counts: below 4 every segment goes through the end-state
+and transfer walks, from 4 on the first two (the adjoint: the last two) are walked in full
+beside them.
 """
 import os
 import subprocess
@@ -52,6 +55,27 @@ def test_split_walk_forced_segments(G):
     print(f"split walk with KDA_STATE_SEG={G} (child process)", flush=True)
     env = dict(os.environ, KDA_STATE_SEG=str(G))
     r = subprocess.run([sys.executable, "-c", CHILD.format(root=ROOT, here=HERE, G=G)], env=env, cwd=ROOT,
+                       capture_output=True, text=True, timeout=110)
+    print(r.stdout[-3000:], r.stderr[-3000:], flush=True)
+    assert r.returncode == 0 and r.stdout.rstrip().endswith("ok")
+
+
+CHILD_BWD = r"""
+import sys
+sys.path[:0] = [{root!r}, {here!r}]
+from test_gpu_bwd import _split_inputs, _check
+G = {G}
+inp, dO, dST, S0 = _split_inputs("ckda", 80 + G, long_memory=True)
+_check(inp, dO, dST, S0, label="bwd split G=%d" % G)
+print("ok", flush=True)
+"""
+
+
+@pytest.mark.parametrize("G", [2, 3, 4, 5])
+def test_bwd_split_walks_forced_segments(G):
+    print(f"backward split walks with KDA_BWD_SEG={G} (child process)", flush=True)
+    env = dict(os.environ, KDA_BWD_SEG=str(G))
+    r = subprocess.run([sys.executable, "-c", CHILD_BWD.format(root=ROOT, here=HERE, G=G)], env=env, cwd=ROOT,
                        capture_output=True, text=True, timeout=110)
     print(r.stdout[-3000:], r.stderr[-3000:], flush=True)
     assert r.returncode == 0 and r.stdout.rstrip().endswith("ok")
