@@ -416,7 +416,8 @@ def main():
                     choices=("kda_prefill_8k", "ckda_prefill_8k", "ckda_prefill_128k", "gdn2_prefill_8k",
                              "sfda_prefill_8k"),
                     help="only this prefill workload (for profiling its kernels); prints its own line")
-    ap.add_argument("--bwd-workload", default="ckda_prefill_8k", choices=("ckda_prefill_8k", "gdn2_prefill_8k", "sfda_prefill_8k"),
+    ap.add_argument("--bwd-workload", default="ckda_prefill_8k",
+                    choices=("ckda_prefill_8k", "gdn2_prefill_8k", "sfda_prefill_8k", "ckda_prefill_128k"),
                     help="workload of --bwd-only")
     args = ap.parse_args()
     if args.gpus != 1:
