@@ -1032,12 +1032,13 @@ __global__ __launch_bounds__(NTW) void bwd_state_kernel(BwdArgs a, int NC, WalkS
 // the current one computes.
 // CPX: SFDA complex gates -- the transpose of the chunk-end rotation-decay is conj(gamma_L)
 // on the row pairs.
-template <typename T, int DK, bool CPX>
+template <typename T, int DK, bool CPX, int WMODE = 0>
 __global__ __launch_bounds__(NT) void bwd_adjoint_kernel(BwdArgs a, int NC, WalkSplit sp0, WalkSplit sp1,
                                                          int nfirst) {
-  // workgroups from nfirst on run the second walk of a paired launch
-  const bool second = (int)blockIdx.x >= nfirst;
-  const WalkSplit sp = pick_split(sp0, sp1, second);
+  // WMODE as in bwd_state_kernel: 0 one walk per chain, 1 one segment walk per workgroup,
+  // 2 a paired launch (workgroups from nfirst on run the second walk)
+  const bool second = WMODE == 2 && (int)blockIdx.x >= nfirst;
+  const WalkSplit sp = WMODE == 2 ? pick_split(sp0, sp1, second) : WMODE == 1 ? sp0 : WalkSplit{};
   const int bid = second ? (int)blockIdx.x - nfirst : (int)blockIdx.x;
   constexpr int LK = DK + 4, LM = C + 4, LV = VTW + 4;
   constexpr int NM = C * C / 4 / NT, NW = C * DK / 4 / NT, NV = C * VTW / 4 / NT;
@@ -2114,11 +2115,11 @@ static hipError_t launch_bwd_dk(const BwdArgs& a, int NC) {
       hipLaunchKernelGGL(walk_scan_kernel<DK>, dim3(chains * (a.Dv / 16)), dim3(256), 0, st, a.s0, P, Bst, X, G, a.Dv, 0,
                          -1);
       hipLaunchKernelGGL((bwd_state_kernel<T, DK, G2, CPX, 1>), dim3(wv), dim3(NTW), 0, st, a, NC, wf, none, all);
-      hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX>), dim3(wv), dim3(NT), 0, st, a, NC, wb, none, all);
-      hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX>), dim3(wk), dim3(NT), 0, st, a, NC, wp, none, all);
+      hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX, 1>), dim3(wv), dim3(NT), 0, st, a, NC, wb, none, all);
+      hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX, 1>), dim3(wk), dim3(NT), 0, st, a, NC, wp, none, all);
       hipLaunchKernelGGL(walk_scan_kernel<DK>, dim3(chains * (a.Dv / 16)), dim3(256), 0, st, a.dsT, P, Bst, X, G, a.Dv,
                          1, -1);
-      hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX>), dim3(wv), dim3(NT), 0, st, a, NC, wf, none, all);
+      hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX, 1>), dim3(wv), dim3(NT), 0, st, a, NC, wf, none, all);
     } else {
       // The state walk: segment 0 in full from S_0 beside the end states of segments
       // 2 ... G - 2 from zero, segment 1 in full beside their transfers, the scan of the
@@ -2137,15 +2138,15 @@ static hipError_t launch_bwd_dk(const BwdArgs& a, int NC) {
                          2);
       hipLaunchKernelGGL((bwd_state_kernel<T, DK, G2, CPX, 1>), dim3(chains * (G - 2) * tv), dim3(NTW), 0, st, a, NC,
                          wsp(G - 2, 2, a.Dv, 0, X, nullptr, 0), none, all);
-      hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX>), dim3(nf + chains * nmid * tv), dim3(NT), 0, st, a, NC,
+      hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX, 2>), dim3(nf + chains * nmid * tv), dim3(NT), 0, st, a, NC,
                          wsp(1, G - 1, a.Dv, kWHead | kWEndPrev, nullptr, X, 1),
                          wsp(nmid, 1, a.Dv, kWNoWrite, nullptr, Bst, 1), nf);
-      hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX>), dim3(nf + chains * nmid * tk), dim3(NT), 0, st, a, NC,
+      hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX, 2>), dim3(nf + chains * nmid * tk), dim3(NT), 0, st, a, NC,
                          wsp(1, G - 2, a.Dv, kWEndPrev, X, X, 1),
                          wsp(nmid, 1, DK, kWNoWrite | kWZeroIn | kWIdentity, nullptr, P, 1), nf);
       hipLaunchKernelGGL(walk_scan_kernel<DK>, dim3(chains * (a.Dv / 16)), dim3(256), 0, st, a.dsT, P, Bst, X, G, a.Dv,
                          1, G - 3);
-      hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX>), dim3(chains * (G - 2) * tv), dim3(NT), 0, st, a, NC,
+      hipLaunchKernelGGL((bwd_adjoint_kernel<T, DK, CPX, 1>), dim3(chains * (G - 2) * tv), dim3(NT), 0, st, a, NC,
                          wsp(G - 2, 0, a.Dv, 0, X, nullptr, 1), none, all);
     }
   }
